@@ -1,0 +1,238 @@
+/*
+ * csa2.h -- C ABI of the CSA2 layer-step library for AMD Instinct MI355X (gfx950).
+ *
+ * One CSA2 (Compressed Sparse Attention 2) layer step is
+ *   (1) an indexer that scores every causally visible compressed main-KV entry
+ *       with FP4 indexer Q/K,
+ *   (2) a Top-K (K = 512) selection per query, and
+ *   (3) sparse attention over the selected entries, dequantised from the FP4 main-KV
+ *       cache, merged in one softmax with the layer's own FP8 sliding window.
+ * Full layers run (1)-(3); Reindex layers run (1)-(3) on a borrowed cache, optionally
+ * inside a candidate pool; Reuse layers borrow the index set and run (3) only.
+ *
+ * Sources, cited by page and section:
+ *   [W] shibing624.github.io walkthrough "一个 token 只花 890 字节：DeepSeek-V4.1-Flash 把
+ *       KV 缓存压到了什么程度": "CSA2：跨层复用，能借就不自己算" (Figure 4),
+ *       "分层稀疏索引器" (Figure 5), "FP4 与 SWA Bounded Replay".
+ *   [J] jdon.com article "557亿参数只唤醒80亿！DeepSeek把AI记忆砍掉437倍还拿了第一！":
+ *       "缓存压缩真的是越大越好吗".
+ *   [L] m.lsln.cn summary of the report: "4.3 消融实验", "五、相关工作".
+ *   [MX] OCP Microscaling Formats v1.0; [FP8] OCP 8-bit floating point (E4M3, no inf).
+ *
+ * Conventions (all calls):
+ *   - Every data pointer is caller-owned DEVICE memory; the library never allocates or
+ *     frees on these calls.  Scratch space comes in through `workspace`, sized by the
+ *     matching *_workspace_bytes() helper.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous,
+ *     stream-ordered, stateless and re-entrant; overlapping calls on different streams
+ *     must not share a workspace.
+ *   - Arguments are validated on the host before anything is launched; on failure the
+ *     call returns a negative csa2 status and launches nothing.  CSA2_ERR_HIP means the
+ *     runtime rejected a launch; csa2_last_error() then holds its text (per thread).
+ *   - Values read from device arrays (positions, counts, indices) are clamped or skipped
+ *     in-kernel so that no access leaves the buffers the sizes describe.
+ *   - Inputs are finite; NaN/Inf inputs are outside the contract.
+ *
+ * Layouts (row-major, contiguous):
+ *   main-KV cache   kv_codes  [n_seq, seq_cap, D/2]  E2M1 pairs, channel 2i in the low
+ *                                                     nibble of byte i
+ *                   kv_scales [n_seq, seq_cap, D/16] E4M3, one per 16 channels
+ *   indexer-K cache k_codes   [n_seq, seq_cap, d/2]  E2M1 pairs
+ *                   k_scales  [n_seq, seq_cap, d/32] E8M0, one per 32 channels
+ *   indexer Q       q_codes   [n_q, H_I, d/2], q_scales [n_q, H_I, d/32] (MXFP4)
+ *   SWA cache       swa       [n_seq, swa_cap, D]    E4M3; the row of token p of sequence
+ *                                                     b is (p - swa_base[b]) mod swa_cap
+ *   index sets      idx       [n_q, k] int32 positions, ascending, -1 padded
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define CSA2_OK 0
+#define CSA2_ERR_NULL (-1)         /* a required pointer is NULL */
+#define CSA2_ERR_SHAPE (-2)        /* a size, count or shape argument is out of range */
+#define CSA2_ERR_UNSUPPORTED (-3)  /* argument combination not supported (format, dtype, device) */
+#define CSA2_ERR_HIP (-4)          /* the HIP runtime reported an error */
+#define CSA2_ERR_WORKSPACE (-5)    /* workspace missing or smaller than required */
+
+/* ---- storage formats ---- */
+#define CSA2_FMT_NVFP4 0  /* main KV: E2M1 + one E4M3 scale per 16 channels, no global scale
+                             ([W] "FP4 与 SWA Bounded Replay"; [L] 4.3, 5) */
+#define CSA2_FMT_MXFP4 1  /* indexer Q/K: E2M1 + one E8M0 scale per 32 channels ([MX];
+                             [W] "FP4 与 SWA Bounded Replay": indexer Q/K in FP4) */
+#define CSA2_FMT_FP8 2    /* sliding-window KV: unscaled E4M3 ([J] "缓存压缩真的是越大越好吗") */
+
+/* ---- element types of dense inputs / outputs ---- */
+#define CSA2_DT_F32 0
+#define CSA2_DT_BF16 1
+
+/* ---- fixed limits ---- */
+#define CSA2_MAX_TOPK 2048         /* k of csa2_topk, max_blocks of csa2_build_pool */
+#define CSA2_MAX_INDEX_HEADS 16    /* H_I of csa2_index_score */
+#define CSA2_INDEX_DIM 128         /* d of csa2_index_score */
+#define CSA2_MAIN_DIM 512          /* D of csa2_sparse_attn */
+#define CSA2_MAX_WINDOW 1024       /* window of csa2_sparse_attn */
+
+/* Library version (major*10000 + minor*100 + patch). */
+int csa2_version(void);
+
+/* Checks that the current HIP device is a gfx950 (MI355X) and that the library's code
+ * objects load on it.  Returns CSA2_OK, CSA2_ERR_UNSUPPORTED (other device) or
+ * CSA2_ERR_HIP (no device / runtime error). */
+int csa2_init(void);
+
+/* Static text for a status code; never NULL. */
+const char* csa2_status_string(int status);
+
+/* Text of the last HIP error seen by a csa2 call on this thread ("" if none). */
+const char* csa2_last_error(void);
+
+/*
+ * csa2_quantize_kv -- quantise rows and scatter them into a cache.
+ * [W] "FP4 与 SWA Bounded Replay" (main KV: E2M1 with an E4M3 scale per 16 channels,
+ * quantised after RoPE); [L] 4.3 and 5 (no second-level global scale, after RoPE);
+ * [MX] (indexer Q/K); [J] "缓存压缩真的是越大越好吗" (SWA KV in FP8).
+ *
+ *   src        [rows, dim] f32 or bf16 (src_dtype), the post-RoPE latents
+ *   fmt        CSA2_FMT_NVFP4: per 16 channels, scale = E4M3 nearest to amax/6
+ *                (saturating at 448); element = E2M1 nearest to x/scale (saturating at
+ *                6), sign kept; a scale of 0 stores signed zeros.
+ *              CSA2_FMT_MXFP4: per 32 channels, scale = 2^E, E = floor(log2 amax) - 2
+ *                clamped to [-127, 127], code E+127 (0 for an all-zero group); element =
+ *                E2M1 nearest to x/2^E, saturating at 6.
+ *              CSA2_FMT_FP8: element = E4M3 nearest to x, saturating at +-448.
+ *              Nearest = round to nearest, ties to the even code (bit-exact).
+ *   dst_row    [rows] int64 destination row of each source row (NULL: row r -> r);
+ *              rows whose destination is outside [0, dst_rows) are skipped
+ *   codes      [dst_rows, dim/2] (FP4) or [dst_rows, dim] (FP8) bytes
+ *   scales     [dst_rows, dim/16] (NVFP4) or [dst_rows, dim/32] (MXFP4); unused for FP8
+ * Errors: NULL src/codes (or scales for FP4) -> CSA2_ERR_NULL; rows < 0, dim <= 0, dim not
+ * a multiple of the group (16 / 32 / 8 for FP8) or dim > 8192 -> CSA2_ERR_SHAPE; unknown
+ * fmt or src_dtype -> CSA2_ERR_UNSUPPORTED.  rows == 0 launches nothing.
+ */
+int csa2_quantize_kv(const void* src, int src_dtype, int64_t rows, int dim, int fmt,
+                     const int64_t* dst_row, int64_t dst_rows, uint8_t* codes, uint8_t* scales,
+                     void* stream);
+
+/*
+ * csa2_index_score -- indexer scores of each query over its sequence's entries.
+ * [W] "CSA2：跨层复用，能借就不自己算" (a lightweight indexer scores the global main KV with
+ * indexer Q/K), "分层稀疏索引器" (later layers score only inside the pool);
+ * [W] "FP4 与 SWA Bounded Replay" (indexer Q/K in FP4).
+ *
+ *   score(q, j) = sum_h w[q,h] * max(0, sum_c Q[q,h,c] K[seq(q), j, c])
+ * with Q and K the exact MXFP4 values; products are exact, sums are fp32.
+ *
+ *   q_codes/q_scales  [n_q, n_heads, dim/2] / [n_q, n_heads, dim/32], MXFP4
+ *   w                 [n_q, n_heads] f32
+ *   n_heads           1..16;  dim == 128
+ *   k_codes/k_scales  indexer-K cache, [n_seq, seq_cap, dim/2] / [.., dim/32]
+ *   q_seq             [n_q] int32 sequence of each query (queries with q_seq outside
+ *                     [0, n_seq) get no scores)
+ *   n_vis             [n_q] int64 visible entries of each query (clamped to seq_cap)
+ *   cand_blocks       NULL: score positions j in [0, n_vis), written to scores[q, j];
+ *                     positions past n_vis are not written.
+ *                     else [n_q, max_cand_blocks] int32 block ids with n_cand_blocks [n_q]
+ *                     valid ones: slot s in [0, max_cand_blocks*block) holds position
+ *                     cand_blocks[q, s/block]*block + s%block and is written to
+ *                     scores[q, s]; slots past n_cand_blocks*block, with a negative block
+ *                     id or with an invisible position get -inf.
+ *   block             positions per pool block (1..64) when cand_blocks is given
+ *   scores            [n_q, scores_stride] f32
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (n_q < 0, n_heads not in 1..16, dim != 128,
+ * seq_cap < 0, n_seq < 1, scores_stride too small for seq_cap or max_cand_blocks*block).
+ */
+int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                     int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                     int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                     const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                     int max_cand_blocks, float* scores, int64_t scores_stride, void* stream);
+
+/*
+ * csa2_topk -- the k highest-scoring candidates of each query.
+ * [W] "CSA2：跨层复用，能借就不自己算" (Top-K, K = 512).
+ *
+ * Candidates are ranked by (score descending, position ascending); the first min(k, n)
+ * are returned as ascending positions, padded with -1; count_out[q] = their number.
+ *   cand_blocks NULL: candidates are positions [0, min(n_vis[q], max_vis)), score of
+ *                     position j at scores[q, j].
+ *   cand_blocks given: the slot layout of csa2_index_score (slots whose position is
+ *                     invalid or invisible are not candidates).
+ *   k in 1..2048.  Workspace: csa2_topk_workspace_bytes(n_q, n_slots, k) bytes, where
+ *   n_slots = max_vis (no pool) or max_cand_blocks*block.
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_WORKSPACE.
+ */
+int csa2_topk(const float* scores, int64_t scores_stride, int n_q, const int64_t* n_vis,
+              int64_t max_vis, const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+              int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out, void* workspace,
+              size_t workspace_bytes, void* stream);
+size_t csa2_topk_workspace_bytes(int n_q, int64_t n_slots, int k);
+
+/*
+ * csa2_build_pool -- the hierarchical sparse indexer's candidate pool.
+ * [W] "分层稀疏索引器" and Figure 5: the decoder's first Full layer keeps at most
+ * max_blocks (2,048) aligned blocks of `block` (8) positions, chosen by the block's
+ * maximum indexer score; later Reindex layers choose their Top-K inside it.
+ *
+ *   block score b = max of scores[q, j] over visible j in [b*block, b*block+block)
+ *   blocks ranked by (block score descending, block id ascending); the first
+ *   min(max_blocks, ceil(n_vis/block)) are returned ascending in blocks_out[q, :],
+ *   padded with -1, with count_out[q] their number.
+ *   block 1..64, max_blocks 1..2048.
+ *   Workspace: csa2_pool_workspace_bytes(n_q, max_vis, block, max_blocks).
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_WORKSPACE.
+ */
+int csa2_build_pool(const float* scores, int64_t scores_stride, int n_q, const int64_t* n_vis,
+                    int64_t max_vis, int block, int max_blocks, int32_t* blocks_out,
+                    int32_t* count_out, void* workspace, size_t workspace_bytes, void* stream);
+size_t csa2_pool_workspace_bytes(int n_q, int64_t max_vis, int block, int max_blocks);
+
+/*
+ * csa2_sparse_attn -- attention over the selected main-KV entries and the window.
+ * [W] "CSA2：跨层复用，能借就不自己算" (Top-K entries plus the layer's own sliding-window
+ * KV; each mode keeps its own Q and window), "FP4 与 SWA Bounded Replay" (FP4 values are
+ * dequantised before attention; after a replay from token s, query i sees the window keys
+ * [max(s, i-W+1), i]); [J] "缓存压缩真的是越大越好吗" (window KV in FP8).
+ *
+ * For query row q at token t = q_pos[q] with replay start s = replay_start[q]:
+ *   keys  = { main entry idx[q, i] : 0 <= idx < seq_cap }  (others are skipped)
+ *         u { window token p : max(s, t-window+1) <= p <= t }   (no de-duplication)
+ *   logit = sm_scale * (Q[q,h,:] . key)    with key the exact dequantised value
+ *   out[q,h,:] = sum softmax(logit) * key   (V = K: the shared entry)
+ *   lse[q,h]   = ln sum exp(logit)           (natural log)
+ * A query with no key (only possible when s > t) gets out = 0 and lse = -inf.
+ *
+ *   q         [n_q, n_heads, dim] bf16;  n_heads a multiple of 16 (<= 256); dim == 512
+ *   kv_codes/kv_scales  main-KV cache (NVFP4), [n_seq, seq_cap, ...]
+ *   q_seq     [n_q] int32 (queries with q_seq outside [0, n_seq) get out = 0, lse = -inf)
+ *   idx       [n_q, k] int32 positions, any order, -1 (or any value outside
+ *             [0, seq_cap)) = empty;  k in 0..2048
+ *   swa       [n_seq, swa_cap, dim] E4M3; swa_base [n_seq] int64; window in 1..1024 and
+ *             window <= swa_cap
+ *   out       [n_q, n_heads, dim] f32 or bf16 (out_dtype); lse [n_q, n_heads] f32 or NULL
+ *   Workspace: csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window).
+ * Arithmetic: Q.K on bf16 matrix cores with fp32 accumulation (K is exact in bf16);
+ * softmax in fp32; P.V with P rounded to fp16 and V exact in fp16, fp32 accumulation.
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED (out_dtype),
+ * CSA2_ERR_WORKSPACE.
+ */
+int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
+                     const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                     const int32_t* idx, int k, const uint8_t* swa, int64_t swa_cap,
+                     const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
+                     int window, float sm_scale, void* out, int out_dtype, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+size_t csa2_attn_workspace_bytes(int n_q, int n_heads, int dim, int k, int window);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -1,0 +1,150 @@
+"""Shapes of the CSA2 workloads and the seeded tensors that feed them.
+
+Every workload is a set of sequences with a compressed main-KV cache
+(``seq_cap`` entries each, compression ratio ``m``), an indexer-K cache on the
+same entries, a per-layer FP8 sliding-window cache, and a set of query rows
+(one per decoding sequence, or every token of a prefill chunk).
+
+Value recipe (all seeded, see ``synth.c``):
+  main-KV latent   N(0,1)^512 -> RMS norm (unit weight) -> rotary embedding on
+                   the last 64 channels at position entry*m, fp32
+  indexer-K latent N(0,1)^128, fp32 (a stand-in for the learned projection of
+                   the main latent; such a projection of an isotropic Gaussian
+                   is again a Gaussian of about unit variance per channel)
+  SWA latent       as the main latent, one row per token position, per layer
+  indexer Q        N(0,1)^(H_I*128), fp32, per layer and query row
+  indexer weight   U(0,1)^H_I, fp32, per layer and query row
+  attention Q      N(0,1)^(H*512) rounded to bf16, per layer and query row
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import (ATTN_Q, INDEX_K_LATENT, INDEX_Q, INDEX_W, MAIN_LATENT, SWA_LATENT,
+               latent_rows, normal_bf16_bits, normal_f32, tensor_id, uniform_f32)
+
+DIM = 512          # main-KV latent channels
+IDX_DIM = 128      # indexer head dimension
+TOPK = 512         # entries kept per query
+WINDOW = 128       # sliding-window length
+BLOCK = 8          # pool block size (positions)
+MAX_BLOCKS = 2048  # pool capacity in blocks
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    n_seq: int
+    seq_cap: int                 # main-KV entries allocated per sequence
+    m: int                       # tokens per compressed entry
+    heads: int                   # attention heads
+    idx_heads: int               # indexer heads
+    q_seq: np.ndarray            # [n_q] int32 sequence of each query row
+    q_pos: np.ndarray            # [n_q] int64 absolute token position of each query
+    replay_start: np.ndarray     # [n_q] int64 replay start s of each query
+    layers: tuple                # layer modes in order: full, full_pool, reuse, reindex, reindex_pool
+    new_entries: tuple           # (first, count) entries quantized inside the step
+    swa_cap: int = WINDOW        # SWA ring rows per sequence (row = (pos - base) mod cap)
+    swa_base: int = 0
+    description: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def n_q(self) -> int:
+        return int(self.q_seq.shape[0])
+
+    @property
+    def n_vis(self) -> np.ndarray:
+        """Visible compressed entries per query: only complete blocks of m tokens."""
+        return ((self.q_pos + 1) // self.m).astype(np.int64)
+
+    # ----- seeded tensors (host numpy) -----
+    def main_latents(self, seq: int, row0: int, rows: int) -> np.ndarray:
+        return latent_rows(self.seed, tensor_id(MAIN_LATENT, 0, seq), row0, rows, DIM, 64, self.m)
+
+    def index_k_latents(self, seq: int, row0: int, rows: int) -> np.ndarray:
+        t = tensor_id(INDEX_K_LATENT, 0, seq)
+        return normal_f32(self.seed, t, row0 * IDX_DIM, rows * IDX_DIM).reshape(rows, IDX_DIM)
+
+    def swa_latents(self, layer: int, seq: int, pos0: int, count: int) -> np.ndarray:
+        return latent_rows(self.seed, tensor_id(SWA_LATENT, layer, seq), pos0, count, DIM, 64, 1)
+
+    def index_q(self, layer: int, q0: int = 0, nq: int | None = None) -> np.ndarray:
+        nq = self.n_q - q0 if nq is None else nq
+        n = self.idx_heads * IDX_DIM
+        return normal_f32(self.seed, tensor_id(INDEX_Q, layer), q0 * n, nq * n).reshape(
+            nq, self.idx_heads, IDX_DIM)
+
+    def index_w(self, layer: int, q0: int = 0, nq: int | None = None) -> np.ndarray:
+        nq = self.n_q - q0 if nq is None else nq
+        h = self.idx_heads
+        return uniform_f32(self.seed, tensor_id(INDEX_W, layer), q0 * h, nq * h).reshape(nq, h)
+
+    def attn_q_bits(self, layer: int, q0: int = 0, nq: int | None = None) -> np.ndarray:
+        nq = self.n_q - q0 if nq is None else nq
+        n = self.heads * DIM
+        return normal_bf16_bits(self.seed, tensor_id(ATTN_Q, layer), q0 * n, nq * n).reshape(
+            nq, self.heads, DIM)
+
+    def swa_positions_needed(self, seq: int) -> tuple:
+        """Token positions whose SWA rows any query of `seq` can read: [lo, hi]."""
+        sel = self.q_seq == seq
+        t = self.q_pos[sel]
+        s = self.replay_start[sel]
+        lo = int(np.maximum(s, t - WINDOW + 1).min())
+        return lo, int(t.max())
+
+
+def decode(name: str, seed: int, batch: int, n_entries: int, heads: int, idx_heads: int,
+           layers=("full",), description: str = "") -> Workload:
+    """Batched decode at m=1: query b is the newest token of sequence b, which sees all entries."""
+    q_pos = np.full(batch, n_entries - 1, dtype=np.int64)
+    return Workload(name=name, seed=seed, n_seq=batch, seq_cap=n_entries, m=1, heads=heads,
+                    idx_heads=idx_heads, q_seq=np.arange(batch, dtype=np.int32), q_pos=q_pos,
+                    replay_start=np.zeros(batch, dtype=np.int64), layers=tuple(layers),
+                    new_entries=(n_entries - 1, 1), description=description)
+
+
+def prefill(name: str, seed: int, prefix_tokens: int, chunk_tokens: int, m: int, heads: int,
+            idx_heads: int, description: str = "") -> Workload:
+    """One sequence: a cached prefix, then a chunk of new tokens.  The query rows are the
+    last WINDOW prefix tokens (bounded replay from s = prefix - WINDOW) and the new tokens."""
+    s = prefix_tokens - WINDOW
+    q_pos = np.arange(s, prefix_tokens + chunk_tokens, dtype=np.int64)
+    total_entries = (prefix_tokens + chunk_tokens) // m
+    first_new = prefix_tokens // m
+    wl = Workload(name=name, seed=seed, n_seq=1, seq_cap=total_entries, m=m, heads=heads,
+                  idx_heads=idx_heads, q_seq=np.zeros(q_pos.shape[0], dtype=np.int32), q_pos=q_pos,
+                  replay_start=np.full(q_pos.shape[0], s, dtype=np.int64), layers=("full",),
+                  new_entries=(first_new, total_entries - first_new),
+                  swa_cap=chunk_tokens + WINDOW, swa_base=s, description=description)
+    wl.extra["counted_rows"] = chunk_tokens
+    return wl
+
+
+def config(name: str) -> Workload:
+    """The five workloads: tiny decode, 128K batched decode, one layer group at 128K,
+    1M decode with the candidate pool, and an m=2 encoder prefill chunk."""
+    if name == "c1":
+        return decode("c1", 0, 1, 4096, 16, 8, ("full",),
+                      "tiny Full decode: 1 query, 16 heads, 4,096 entries, 8 indexer heads")
+    if name == "c2":
+        return decode("c2", 1, 64, 131072, 64, 16, ("full",),
+                      "batched Full decode: 64 queries x 128K entries, 64 heads, 16 indexer heads")
+    if name == "c3":
+        return decode("c3", 2, 32, 131072, 64, 16, ("full", "reuse", "reuse", "reuse", "reindex"),
+                      "layer group: Full + 3 Reuse + Reindex, 32 queries x 128K entries")
+    if name == "c4":
+        return decode("c4", 3, 8, 1048576, 64, 16,
+                      ("full_pool", "reindex_pool", "reindex_pool", "reindex_pool", "reindex_pool"),
+                      "1M decode: Full + pool, then 4 Reindex inside the 16,384-position pool")
+    if name == "c5":
+        return prefill("c5", 4, 262144, 4096, 2, 64, 16,
+                       "encoder prefill chunk: 4,096 tokens after a 262,144-token prefix, m=2")
+    raise KeyError(name)
+
+
+CONFIG_NAMES = ("c1", "c2", "c3", "c4", "c5")
