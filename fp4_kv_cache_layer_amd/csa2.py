@@ -1,0 +1,252 @@
+"""Python binding of the CSA2 C ABI (include/csa2.h): argument marshalling only.
+
+Each function has the C entry point's name, takes torch tensors (device memory and the
+current stream are torch's), checks shapes and dtypes, passes raw pointers to
+libcsa2.so and raises Csa2Error on a non-zero status.  Every step runs in the HIP
+kernels; there is no other code path.  If the library is missing or cannot load, the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported before libcsa2.so so that the process holds a single HIP runtime
+
+from .build import LIB_PATH
+
+FMT_NVFP4, FMT_MXFP4, FMT_FP8 = 0, 1, 2
+DT_F32, DT_BF16 = 0, 1
+MAX_TOPK = 2048
+
+_lib = None
+
+
+class Csa2Error(RuntimeError):
+    pass
+
+
+def _hip_runtimes_mapped() -> set:
+    try:
+        with open("/proc/self/maps") as f:
+            return {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    except OSError:
+        return set()
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcsa2.so (built by __graft_entry__.build()); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise Csa2Error(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise Csa2Error(f"two HIP runtimes are mapped into this process: {sorted(runtimes)}")
+    vp, i64, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "csa2_version": ([], i32),
+        "csa2_init": ([], i32),
+        "csa2_status_string": ([i32], ctypes.c_char_p),
+        "csa2_last_error": ([], ctypes.c_char_p),
+        "csa2_quantize_kv": ([vp, i32, i64, i32, i32, vp, i64, vp, vp, vp], i32),
+        "csa2_index_score": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64, vp],
+                             i32),
+        "csa2_topk": ([vp, i64, i32, vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp], i32),
+        "csa2_topk_workspace_bytes": ([i32, i64, i32], sz),
+        "csa2_build_pool": ([vp, i64, i32, vp, i64, i32, i32, vp, vp, vp, sz, vp], i32),
+        "csa2_pool_workspace_bytes": ([i32, i64, i32, i32], sz),
+        "csa2_sparse_attn": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp, vp, vp, i32, f32, vp,
+                              i32, vp, vp, sz, vp], i32),
+        "csa2_attn_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        L = lib()
+        msg = L.csa2_status_string(rc).decode()
+        last = L.csa2_last_error().decode()
+        raise Csa2Error(f"{name} failed ({rc}): {msg}" + (f" [{last}]" if last else ""))
+
+
+def _need(t, dtype, ndim, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous device tensor")
+
+
+def csa2_version() -> int:
+    return int(lib().csa2_version())
+
+
+def csa2_init():
+    _check(lib().csa2_init(), "csa2_init")
+
+
+def csa2_quantize_kv(src, fmt: int, codes, scales=None, dst_row=None):
+    """src [rows, dim] f32/bf16; codes [dst_rows, dim/2] (FP4) or [dst_rows, dim] (FP8) u8;
+    scales [dst_rows, dim/16 | dim/32] u8; dst_row [rows] int64 or None."""
+    if src.dtype not in (torch.float32, torch.bfloat16) or src.dim() != 2 or not src.is_cuda:
+        raise TypeError("src must be a 2-D f32/bf16 device tensor")
+    src = src.contiguous()
+    rows, dim = src.shape
+    _need(codes, torch.uint8, 2, "codes")
+    per = dim if fmt == FMT_FP8 else dim // 2
+    if codes.shape[1] != per:
+        raise ValueError("codes row size does not match dim")
+    if fmt != FMT_FP8:
+        _need(scales, torch.uint8, 2, "scales")
+        g = 16 if fmt == FMT_NVFP4 else 32
+        if scales.shape != (codes.shape[0], dim // g):
+            raise ValueError("scales shape does not match codes / dim")
+    if dst_row is not None:
+        _need(dst_row, torch.int64, 1, "dst_row")
+        if dst_row.shape[0] != rows:
+            raise ValueError("dst_row length != rows")
+    dt = DT_F32 if src.dtype == torch.float32 else DT_BF16
+    rc = lib().csa2_quantize_kv(_p(src), dt, rows, dim, fmt, _p(dst_row), codes.shape[0], _p(codes),
+                                _p(scales) if fmt != FMT_FP8 else None, _stream())
+    _check(rc, "csa2_quantize_kv")
+
+
+def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
+                     cand_blocks=None, n_cand_blocks=None, block: int = 8):
+    """q_codes [n_q, H_I, 64], q_scales [n_q, H_I, 4], w [n_q, H_I] f32;
+    k_codes [n_seq, seq_cap, 64], k_scales [n_seq, seq_cap, 4]; q_seq [n_q] int32,
+    n_vis [n_q] int64; scores [n_q, stride] f32; cand_blocks [n_q, max_blocks] int32."""
+    _need(q_codes, torch.uint8, 3, "q_codes")
+    _need(q_scales, torch.uint8, 3, "q_scales")
+    _need(w, torch.float32, 2, "w")
+    _need(k_codes, torch.uint8, 3, "k_codes")
+    _need(k_scales, torch.uint8, 3, "k_scales")
+    _need(q_seq, torch.int32, 1, "q_seq")
+    _need(n_vis, torch.int64, 1, "n_vis")
+    _need(scores, torch.float32, 2, "scores")
+    n_q, h, half = q_codes.shape
+    n_seq, seq_cap, kh = k_codes.shape
+    if q_scales.shape != (n_q, h, half // 16) or w.shape != (n_q, h) or kh != half or \
+            k_scales.shape != (n_seq, seq_cap, half // 16) or q_seq.shape[0] != n_q or n_vis.shape[0] != n_q or \
+            scores.shape[0] != n_q:
+        raise ValueError("index_score: inconsistent shapes")
+    max_blocks = 0
+    if cand_blocks is not None:
+        _need(cand_blocks, torch.int32, 2, "cand_blocks")
+        _need(n_cand_blocks, torch.int32, 1, "n_cand_blocks")
+        max_blocks = cand_blocks.shape[1]
+        if cand_blocks.shape[0] != n_q or n_cand_blocks.shape[0] != n_q:
+            raise ValueError("index_score: inconsistent pool shapes")
+    rc = lib().csa2_index_score(_p(q_codes), _p(q_scales), _p(w), n_q, h, 2 * half, _p(k_codes), _p(k_scales),
+                                seq_cap, n_seq, _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks), block,
+                                max_blocks, _p(scores), scores.stride(0), _stream())
+    _check(rc, "csa2_index_score")
+
+
+def csa2_topk_workspace_bytes(n_q: int, n_slots: int, k: int) -> int:
+    return int(lib().csa2_topk_workspace_bytes(n_q, n_slots, k))
+
+
+def csa2_topk(scores, n_vis, max_vis: int, k: int, idx_out, count_out, workspace=None,
+              cand_blocks=None, n_cand_blocks=None, block: int = 8):
+    """scores [n_q, stride] f32 -> idx_out [n_q, k] int32 ascending, -1 padded; count_out [n_q] int32."""
+    _need(scores, torch.float32, 2, "scores")
+    _need(n_vis, torch.int64, 1, "n_vis")
+    _need(idx_out, torch.int32, 2, "idx_out")
+    _need(count_out, torch.int32, 1, "count_out")
+    n_q = scores.shape[0]
+    if idx_out.shape != (n_q, k) or count_out.shape[0] != n_q or n_vis.shape[0] != n_q:
+        raise ValueError("topk: inconsistent shapes")
+    max_blocks = 0
+    if cand_blocks is not None:
+        _need(cand_blocks, torch.int32, 2, "cand_blocks")
+        _need(n_cand_blocks, torch.int32, 1, "n_cand_blocks")
+        max_blocks = cand_blocks.shape[1]
+    n_slots = max_blocks * block if cand_blocks is not None else max_vis
+    need = csa2_topk_workspace_bytes(n_q, max(n_slots, 1), k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    rc = lib().csa2_topk(_p(scores), scores.stride(0), n_q, _p(n_vis), max_vis, _p(cand_blocks),
+                         _p(n_cand_blocks), block, max_blocks, k, _p(idx_out), _p(count_out), _p(workspace),
+                         ws_bytes, _stream())
+    _check(rc, "csa2_topk")
+
+
+def csa2_pool_workspace_bytes(n_q: int, max_vis: int, block: int, max_blocks: int) -> int:
+    return int(lib().csa2_pool_workspace_bytes(n_q, max_vis, block, max_blocks))
+
+
+def csa2_build_pool(scores, n_vis, max_vis: int, blocks_out, count_out, block: int = 8, workspace=None):
+    """scores [n_q, stride] f32 -> blocks_out [n_q, max_blocks] int32 ascending, -1 padded."""
+    _need(scores, torch.float32, 2, "scores")
+    _need(n_vis, torch.int64, 1, "n_vis")
+    _need(blocks_out, torch.int32, 2, "blocks_out")
+    _need(count_out, torch.int32, 1, "count_out")
+    n_q, max_blocks = blocks_out.shape
+    need = csa2_pool_workspace_bytes(n_q, max(max_vis, 1), block, max_blocks)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    rc = lib().csa2_build_pool(_p(scores), scores.stride(0), n_q, _p(n_vis), max_vis, block, max_blocks,
+                               _p(blocks_out), _p(count_out), _p(workspace), ws_bytes, _stream())
+    _check(rc, "csa2_build_pool")
+
+
+def csa2_attn_workspace_bytes(n_q: int, n_heads: int, dim: int, k: int, window: int) -> int:
+    return int(lib().csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window))
+
+
+def csa2_sparse_attn(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, replay_start, window: int,
+                     sm_scale: float, out, lse=None, workspace=None):
+    """q [n_q, H, 512] bf16; kv_codes [n_seq, seq_cap, 256], kv_scales [n_seq, seq_cap, 32];
+    idx [n_q, k] int32; swa [n_seq, swa_cap, 512] u8; swa_base [n_seq] int64;
+    q_pos, replay_start [n_q] int64; out [n_q, H, 512] f32/bf16; lse [n_q, H] f32."""
+    _need(q, torch.bfloat16, 3, "q")
+    _need(kv_codes, torch.uint8, 3, "kv_codes")
+    _need(kv_scales, torch.uint8, 3, "kv_scales")
+    _need(q_seq, torch.int32, 1, "q_seq")
+    _need(idx, torch.int32, 2, "idx")
+    _need(swa, torch.uint8, 3, "swa")
+    _need(swa_base, torch.int64, 1, "swa_base")
+    _need(q_pos, torch.int64, 1, "q_pos")
+    _need(replay_start, torch.int64, 1, "replay_start")
+    n_q, H, D = q.shape
+    n_seq, seq_cap, _ = kv_codes.shape
+    k = idx.shape[1]
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (n_q, H, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [n_q, H, D] f32/bf16 tensor")
+    if kv_codes.shape[2] != D // 2 or kv_scales.shape != (n_seq, seq_cap, D // 16) or swa.shape[0] != n_seq or \
+            swa.shape[2] != D or swa_base.shape[0] != n_seq or idx.shape[0] != n_q:
+        raise ValueError("sparse_attn: inconsistent shapes")
+    if lse is not None:
+        _need(lse, torch.float32, 2, "lse")
+        if tuple(lse.shape) != (n_q, H):
+            raise ValueError("lse shape")
+    need = csa2_attn_workspace_bytes(n_q, H, D, k, window)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
+    rc = lib().csa2_sparse_attn(_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq), _p(idx), k,
+                                _p(swa), swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), window,
+                                float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes, _stream())
+    _check(rc, "csa2_sparse_attn")

@@ -1,0 +1,52 @@
+// Internal device helpers shared by the CSA2 HIP kernels (gfx950 only).
+//
+// FP4/FP8 encodings follow the OCP MX v1.0 (E2M1, E8M0) and OCP FP8 (E4M3, no
+// infinities) definitions: E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; E4M3 bias 7
+// with subnormals m*2^-9 and max 448; E8M0 = 2^(c-127).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+
+namespace csa2 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// vector loads/stores assume 16-byte aligned bases
+__host__ __device__ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// magnitude of a finite non-negative E4M3 code (0..126), exact in fp32
+__device__ __forceinline__ float e4m3_mag(int c) {
+  int e = c >> 3, m = c & 7;
+  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((uint32_t)(e + 120) << 23) | ((uint32_t)m << 20));
+}
+
+// signed value of any non-NaN E4M3 byte
+__device__ __forceinline__ float e4m3_val(uint32_t c) {
+  float v = e4m3_mag((int)(c & 0x7f));
+  return (c & 0x80) ? -v : v;
+}
+
+// signed value of an E2M1 nibble, as fp32 bits (exact)
+__device__ __forceinline__ float e2m1_val(uint32_t c) {
+  uint32_t m = c & 7;
+  uint32_t bits = m >= 2 ? (((m >> 1) + 126u) << 23) | ((m & 1u) << 22) : (m ? 0x3F000000u : 0u);
+  return __uint_as_float(bits | ((c & 8u) << 28));
+}
+
+// fp32 holding a value exactly representable in bf16 -> bf16 bits (truncation is exact)
+__device__ __forceinline__ uint16_t exact_bf16_bits(float f) { return (uint16_t)(__float_as_uint(f) >> 16); }
+
+}  // namespace csa2
+
+// Launch-error bookkeeping used by every entry point (defined in abi.hip).
+int csa2_record_hip_error(hipError_t e);
+int csa2_check_launch();

@@ -1,0 +1,205 @@
+// csa2_quantize_kv: quantise post-RoPE rows to NVFP4 / MXFP4 / FP8 and scatter them
+// into a cache ([W] "FP4 与 SWA Bounded Replay"; [L] 4.3 and 5; OCP MX v1.0).
+//
+// Rounding is decided without division: "x rounds to a code >= c" is the comparison of
+// x against the exact midpoint between codes c-1 and c (ties go to the even code).  All
+// midpoints and their products with the scale carry at most 7 significant bits, so every
+// comparison is exact in fp32 and the codes are bit-exact.
+//
+// One thread quantises one scale group (16 / 32 channels) or, for FP8, 8 channels.
+// Consecutive threads take consecutive groups of a row, so a wave reads a contiguous
+// stretch of the source.  This runs once per new cache row (one row per sequence per
+// decode step), so it is far from any roofline; it is written for exactness first.
+#include "device.h"
+
+namespace csa2 {
+
+// E4M3 code nearest to a/6 (a >= 0), ties to even, saturating at 448 (code 126).
+// Binary search for the largest c with "a/6 rounds to >= c", i.e. a > 6*mid(c-1,c) or
+// (a == 6*mid(c-1,c) and c even); 6*mid = 3*(v(c-1)+v(c)) is exact.
+__device__ __forceinline__ int nvfp4_scale_code(float a) {
+  int lo = 0, hi = 126;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    float t = 3.0f * (e4m3_mag(mid - 1) + e4m3_mag(mid));
+    bool up = a > t || (a == t && !(mid & 1));
+    lo = up ? mid : lo;
+    hi = up ? hi : mid - 1;
+  }
+  return lo;
+}
+
+// E4M3 code (0..126) nearest to a >= 0, ties to even, saturating at 448.
+__device__ __forceinline__ int fp8_mag_code(float a) {
+  int lo = 0, hi = 126;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    float t = 0.5f * (e4m3_mag(mid - 1) + e4m3_mag(mid));
+    bool up = a > t || (a == t && !(mid & 1));
+    lo = up ? mid : lo;
+    hi = up ? hi : mid - 1;
+  }
+  return lo;
+}
+
+// E2M1 magnitude code of a/s (a >= 0, s > 0), ties to even, saturating at 6.
+// Midpoints between the E2M1 magnitudes: .25 .75 1.25 1.75 2.5 3.5 5.
+__device__ __forceinline__ uint32_t e2m1_code(float a, float s) {
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    float t = s * mids[i];
+    // code >= i+1 iff a > t, or a == t and i+1 is even
+    c += (a > t) || (a == t && (i & 1));
+  }
+  return c;
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t load_bits(const T* p, int64_t i);
+
+template <>
+__device__ __forceinline__ uint32_t load_bits<float>(const float* p, int64_t i) {
+  return __float_as_uint(p[i]);
+}
+template <>
+__device__ __forceinline__ uint32_t load_bits<uint16_t>(const uint16_t* p, int64_t i) {
+  return (uint32_t)p[i] << 16;
+}
+
+// ---- NVFP4: one thread per 16-channel group ----
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_nvfp4(const T* __restrict__ src, int64_t rows, int dim,
+                                                     const int64_t* __restrict__ dst_row, int64_t dst_rows,
+                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int gpr = dim / 16;
+  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * gpr) return;
+  int64_t r = gid / gpr;
+  int g = (int)(gid % gpr);
+  int64_t d = dst_row ? dst_row[r] : r;
+  if (d < 0 || d >= dst_rows) return;
+  uint32_t bits[16];
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    bits[i] = load_bits(src, r * dim + g * 16 + i);
+    uint32_t ab = bits[i] & 0x7fffffffu;  // |x|; integer order == float order for x >= 0
+    amax_bits = ab > amax_bits ? ab : amax_bits;
+  }
+  int sc = nvfp4_scale_code(__uint_as_float(amax_bits));
+  float s = e4m3_mag(sc);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t mag = s > 0.0f ? e2m1_code(__uint_as_float(bits[i] & 0x7fffffffu), s) : 0u;
+    uint32_t c = mag | ((bits[i] >> 28) & 8u);
+    if (i < 8) lo |= c << (4 * i);
+    else hi |= c << (4 * (i - 8));
+  }
+  uint2* out = reinterpret_cast<uint2*>(codes + d * (dim / 2) + g * 8);
+  *out = make_uint2(lo, hi);
+  scales[d * gpr + g] = (uint8_t)sc;
+}
+
+// ---- MXFP4: one thread per 32-channel group ----
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_mxfp4(const T* __restrict__ src, int64_t rows, int dim,
+                                                     const int64_t* __restrict__ dst_row, int64_t dst_rows,
+                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int gpr = dim / 32;
+  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * gpr) return;
+  int64_t r = gid / gpr;
+  int g = (int)(gid % gpr);
+  int64_t d = dst_row ? dst_row[r] : r;
+  if (d < 0 || d >= dst_rows) return;
+  uint32_t bits[32];
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    bits[i] = load_bits(src, r * dim + g * 32 + i);
+    uint32_t ab = bits[i] & 0x7fffffffu;
+    amax_bits = ab > amax_bits ? ab : amax_bits;
+  }
+  // E = floor(log2 amax) - 2, clamped to [-127, 127]; subnormal amax gives -127
+  int code;
+  int e_field = (int)(amax_bits >> 23);
+  if (amax_bits == 0) code = 0;
+  else if (e_field == 0) code = 0;  // floor(log2 amax) <= -127 -> E clamps to -127
+  else {
+    int E = e_field - 127 - 2;
+    E = E < -127 ? -127 : E;
+    code = E + 127;
+  }
+  int E = code - 127;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float a = __uint_as_float(bits[i] & 0x7fffffffu);
+    // compare a with mid*2^E instead of a*2^-E with mid; both exact
+    uint32_t mag = e2m1_code(a, ldexpf(1.0f, E));
+    uint32_t c = mag | ((bits[i] >> 28) & 8u);
+    w[i >> 3] |= c << (4 * (i & 7));
+  }
+  uint4* out = reinterpret_cast<uint4*>(codes + d * (dim / 2) + g * 16);
+  *out = make_uint4(w[0], w[1], w[2], w[3]);
+  scales[d * gpr + g] = (uint8_t)code;
+}
+
+// ---- FP8 (E4M3, unscaled): one thread per 8 channels ----
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_fp8(const T* __restrict__ src, int64_t rows, int dim,
+                                                   const int64_t* __restrict__ dst_row, int64_t dst_rows,
+                                                   uint8_t* __restrict__ codes) {
+  const int gpr = dim / 8;
+  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * gpr) return;
+  int64_t r = gid / gpr;
+  int g = (int)(gid % gpr);
+  int64_t d = dst_row ? dst_row[r] : r;
+  if (d < 0 || d >= dst_rows) return;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t b = load_bits(src, r * dim + g * 8 + i);
+    uint32_t c = (uint32_t)fp8_mag_code(__uint_as_float(b & 0x7fffffffu)) | ((b >> 24) & 0x80u);
+    if (i < 4) lo |= c << (8 * i);
+    else hi |= c << (8 * (i - 4));
+  }
+  *reinterpret_cast<uint2*>(codes + d * dim + g * 8) = make_uint2(lo, hi);
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" int csa2_quantize_kv(const void* src, int src_dtype, int64_t rows, int dim, int fmt,
+                                const int64_t* dst_row, int64_t dst_rows, uint8_t* codes,
+                                uint8_t* scales, void* stream) {
+  if (!src || !codes) return CSA2_ERR_NULL;
+  if (fmt != CSA2_FMT_NVFP4 && fmt != CSA2_FMT_MXFP4 && fmt != CSA2_FMT_FP8) return CSA2_ERR_UNSUPPORTED;
+  if (src_dtype != CSA2_DT_F32 && src_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
+  if (fmt != CSA2_FMT_FP8 && !scales) return CSA2_ERR_NULL;
+  int group = fmt == CSA2_FMT_NVFP4 ? 16 : (fmt == CSA2_FMT_MXFP4 ? 32 : 8);
+  if (rows < 0 || dim <= 0 || dim > 8192 || dim % group || dst_rows < 0) return CSA2_ERR_SHAPE;
+  if (!aligned16(codes)) return CSA2_ERR_SHAPE;
+  if (rows == 0) return CSA2_OK;
+  hipStream_t st = (hipStream_t)stream;
+  int64_t work = rows * (dim / group);
+  dim3 grid((unsigned)((work + 255) / 256)), block(256);
+  if (grid.x == 0 || (work + 255) / 256 > 0x7fffffff) return CSA2_ERR_SHAPE;
+  bool bf = src_dtype == CSA2_DT_BF16;
+  if (fmt == CSA2_FMT_NVFP4) {
+    if (bf) hipLaunchKernelGGL(k_quant_nvfp4<uint16_t>, grid, block, 0, st, (const uint16_t*)src, rows, dim, dst_row, dst_rows, codes, scales);
+    else hipLaunchKernelGGL(k_quant_nvfp4<float>, grid, block, 0, st, (const float*)src, rows, dim, dst_row, dst_rows, codes, scales);
+  } else if (fmt == CSA2_FMT_MXFP4) {
+    if (bf) hipLaunchKernelGGL(k_quant_mxfp4<uint16_t>, grid, block, 0, st, (const uint16_t*)src, rows, dim, dst_row, dst_rows, codes, scales);
+    else hipLaunchKernelGGL(k_quant_mxfp4<float>, grid, block, 0, st, (const float*)src, rows, dim, dst_row, dst_rows, codes, scales);
+  } else {
+    if (bf) hipLaunchKernelGGL(k_quant_fp8<uint16_t>, grid, block, 0, st, (const uint16_t*)src, rows, dim, dst_row, dst_rows, codes);
+    else hipLaunchKernelGGL(k_quant_fp8<float>, grid, block, 0, st, (const float*)src, rows, dim, dst_row, dst_rows, codes);
+  }
+  return csa2_check_launch();
+}

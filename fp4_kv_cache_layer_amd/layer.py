@@ -1,0 +1,124 @@
+"""Layer-mode driver for the CSA2 layer step (host orchestration only).
+
+[W] "CSA2：跨层复用，能借就不自己算" and Figure 4: every CSA2 layer is statically one of
+  Full    -- its own global KV and indexer K, fresh Top-K indices,
+  Reindex -- the previous layer's global KV, its own indexer Q re-scoring it,
+  Reuse   -- the previous layer's KV and Top-K indices; attention only,
+and every layer keeps its own global Q and its own sliding-window KV.
+[W] "分层稀疏索引器" and Figure 5: the decoder's first Full layer builds a pool of at
+most 2,048 blocks x 8 positions by max indexer score; later Reindex layers pick their
+Top-K inside it.
+
+This module only allocates buffers and sequences calls into the C ABI; it moves no
+data itself.  One `Csa2Step` holds the buffers of a batch of query rows; `full`,
+`reindex` and `reuse` run one layer each on the caller's stream.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import csa2 as C
+
+
+class Caches:
+    """Device caches of a layer group: main KV (NVFP4), indexer K (MXFP4), and the
+    per-layer FP8 window caches with their ring bases."""
+
+    def __init__(self, kv_codes, kv_scales, ik_codes, ik_scales, swa: dict, swa_base):
+        self.kv_codes, self.kv_scales = kv_codes, kv_scales
+        self.ik_codes, self.ik_scales = ik_codes, ik_scales
+        self.swa = swa              # layer -> [n_seq, swa_cap, 512] uint8
+        self.swa_base = swa_base    # [n_seq] int64
+
+    @property
+    def seq_cap(self) -> int:
+        return self.kv_codes.shape[1]
+
+    @staticmethod
+    def empty(n_seq: int, seq_cap: int, swa_layers, swa_cap: int, dim: int = 512, idx_dim: int = 128,
+              device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        return Caches(torch.zeros(n_seq, seq_cap, dim // 2, **u8), torch.zeros(n_seq, seq_cap, dim // 16, **u8),
+                      torch.zeros(n_seq, seq_cap, idx_dim // 2, **u8), torch.zeros(n_seq, seq_cap, idx_dim // 32, **u8),
+                      {L: torch.zeros(n_seq, swa_cap, dim, **u8) for L in swa_layers},
+                      torch.zeros(n_seq, dtype=torch.int64, device=device))
+
+
+class Csa2Step:
+    """Buffers and calls for one batch of query rows through the layers of a group."""
+
+    def __init__(self, n_q: int, n_heads: int, idx_heads: int, seq_cap: int, k: int = 512, window: int = 128,
+                 block: int = 8, max_blocks: int = 2048, idx_dim: int = 128, dim: int = 512,
+                 out_dtype=torch.float32, device="cuda"):
+        self.n_q, self.n_heads, self.idx_heads = n_q, n_heads, idx_heads
+        self.seq_cap, self.k, self.window = seq_cap, k, window
+        self.block, self.max_blocks, self.dim = block, max_blocks, dim
+        dev = dict(device=device)
+        self.qi_codes = torch.empty(n_q, idx_heads, idx_dim // 2, dtype=torch.uint8, **dev)
+        self.qi_scales = torch.empty(n_q, idx_heads, idx_dim // 32, dtype=torch.uint8, **dev)
+        self.scores = torch.empty(n_q, max(seq_cap, max_blocks * block), dtype=torch.float32, **dev)
+        self.idx = torch.empty(n_q, k, dtype=torch.int32, **dev)
+        self.count = torch.empty(n_q, dtype=torch.int32, **dev)
+        self.pool = torch.empty(n_q, max_blocks, dtype=torch.int32, **dev)
+        self.pool_count = torch.empty(n_q, dtype=torch.int32, **dev)
+        self.out = torch.empty(n_q, n_heads, dim, dtype=out_dtype, **dev)
+        self.lse = torch.empty(n_q, n_heads, dtype=torch.float32, **dev)
+        n_slots = max(seq_cap, max_blocks * block, 1)
+        self.ws_topk = torch.empty(max(C.csa2_topk_workspace_bytes(n_q, n_slots, k), 1), dtype=torch.uint8, **dev)
+        self.ws_pool = torch.empty(max(C.csa2_pool_workspace_bytes(n_q, max(seq_cap, 1), block, max_blocks), 1),
+                                   dtype=torch.uint8, **dev)
+        self.ws_attn = torch.empty(max(C.csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window), 1),
+                                   dtype=torch.uint8, **dev)
+        self.sm_scale = 1.0 / math.sqrt(dim)
+
+    # ---- steps ----
+    def quantize_index_q(self, q_f32):
+        """indexer Q [n_q, H_I, d] f32 -> MXFP4 (per query, per head, per 32 channels)."""
+        n_q, h, d = q_f32.shape
+        C.csa2_quantize_kv(q_f32.reshape(n_q * h, d), C.FMT_MXFP4, self.qi_codes.view(n_q * h, d // 2),
+                           self.qi_scales.view(n_q * h, d // 32))
+
+    def score(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False):
+        if in_pool:
+            C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
+                               self.scores, self.pool, self.pool_count, self.block)
+        else:
+            C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
+                               self.scores)
+
+    def select(self, n_vis, in_pool: bool = False):
+        if in_pool:
+            C.csa2_topk(self.scores, n_vis, self.seq_cap, self.k, self.idx, self.count, self.ws_topk,
+                        self.pool, self.pool_count, self.block)
+        else:
+            C.csa2_topk(self.scores, n_vis, self.seq_cap, self.k, self.idx, self.count, self.ws_topk)
+
+    def build_pool(self, n_vis):
+        C.csa2_build_pool(self.scores, n_vis, self.seq_cap, self.pool, self.pool_count, self.block, self.ws_pool)
+
+    def attend(self, caches: Caches, layer: int, q_attn, q_seq, q_pos, replay_start, out=None, lse=None):
+        C.csa2_sparse_attn(q_attn, caches.kv_codes, caches.kv_scales, q_seq, self.idx, caches.swa[layer],
+                           caches.swa_base, q_pos, replay_start, self.window, self.sm_scale,
+                           self.out if out is None else out, self.lse if lse is None else lse, self.ws_attn)
+
+    # ---- layer modes ----
+    def full(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, make_pool=False,
+             out=None, lse=None):
+        self.quantize_index_q(q_index_f32)
+        self.score(caches, w, q_seq, n_vis)
+        self.select(n_vis)
+        if make_pool:
+            self.build_pool(n_vis)
+        self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse)
+
+    def reindex(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, in_pool=False,
+                out=None, lse=None):
+        self.quantize_index_q(q_index_f32)
+        self.score(caches, w, q_seq, n_vis, in_pool)
+        self.select(n_vis, in_pool)
+        self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse)
+
+    def reuse(self, caches, layer, q_attn, q_seq, q_pos, replay_start, out=None, lse=None):
+        self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse)

@@ -32,6 +32,8 @@
  *   - Values read from device arrays (positions, counts, indices) are clamped or skipped
  *     in-kernel so that no access leaves the buffers the sizes describe.
  *   - Inputs are finite; NaN/Inf inputs are outside the contract.
+ *   - Code arrays (codes, q_codes, k_codes, kv_codes, swa), q and out must start on a
+ *     16-byte boundary (CSA2_ERR_SHAPE otherwise); row sizes keep every row aligned.
  *
  * Layouts (row-major, contiguous):
  *   main-KV cache   kv_codes  [n_seq, seq_cap, D/2]  E2M1 pairs, channel 2i in the low

@@ -91,6 +91,8 @@ void synth_normal_bf16(uint64_t seed, uint64_t tensor, uint64_t first, int64_t c
 void synth_latent_rows(uint64_t seed, uint64_t tensor, int64_t row0, int64_t rows, int dim,
                        int rope_dims, int64_t pos_mult, float* out) {
   const double base = 10000.0;
+  double inv_freq[2048];
+  for (int p = 0; p < rope_dims / 2; ++p) inv_freq[p] = pow(base, -2.0 * p / rope_dims);
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < rows; ++i) {
     double x[4096];
@@ -105,7 +107,7 @@ void synth_latent_rows(uint64_t seed, uint64_t tensor, int64_t row0, int64_t row
     double pos = (double)(r * pos_mult);
     int off = dim - rope_dims;
     for (int p = 0; p < rope_dims / 2; ++p) {
-      double theta = pos * pow(base, -2.0 * p / rope_dims);
+      double theta = pos * inv_freq[p];
       double cs = cos(theta), sn = sin(theta);
       double a = x[off + 2 * p], b = x[off + 2 * p + 1];
       x[off + 2 * p] = a * cs - b * sn;

@@ -1,0 +1,78 @@
+"""The C-ABI library loads and exports every symbol include/csa2.h declares; argument
+validation rejects bad calls on the host, before anything reaches the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import torch  # noqa: F401  (the binding always loads torch's HIP runtime first)
+    from fp4_kv_cache_layer_amd.build import LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        pytest.fail("libcsa2.so is not built; run __graft_entry__.build()")
+    return ctypes.CDLL(LIB_PATH)
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ("csa2_quantize_kv", "csa2_index_score", "csa2_topk", "csa2_build_pool", "csa2_sparse_attn"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version(L):
+    L.csa2_status_string.restype = ctypes.c_char_p
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.csa2_status_string(code)
+    assert L.csa2_status_string(-99) == b"unknown status"
+    assert L.csa2_version() >= 100
+
+
+def test_validation_before_launch(L):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.csa2_quantize_kv.argtypes = [vp, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp]
+    fake = vp(0x1000)   # never dereferenced: every call below fails validation first
+    assert L.csa2_quantize_kv(None, 0, 4, 512, 0, None, 4, fake, fake, None) == -1
+    assert L.csa2_quantize_kv(fake, 0, 4, 500, 0, None, 4, fake, fake, None) == -2     # dim % 16
+    assert L.csa2_quantize_kv(fake, 0, 4, 512, 9, None, 4, fake, fake, None) == -3     # fmt
+    assert L.csa2_quantize_kv(fake, 0, 4, 512, 0, None, 4, vp(0x1001), fake, None) == -2  # misaligned
+    assert L.csa2_quantize_kv(fake, 0, 0, 512, 0, None, 4, fake, fake, None) == 0      # empty: no launch
+    L.csa2_topk.argtypes = [vp, i64, ctypes.c_int, vp, i64, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp,
+                            vp, ctypes.c_size_t, vp]
+    assert L.csa2_topk(fake, 100, 2, fake, 100, None, None, 8, 0, 4096, fake, fake, None, 0, None) == -2  # k > 2048
+    assert L.csa2_topk(fake, 10, 2, fake, 100, None, None, 8, 0, 16, fake, fake, None, 0, None) == -2   # stride
+    assert L.csa2_topk(fake, 1 << 20, 2, fake, 1 << 20, None, None, 8, 0, 512, fake, fake, None, 0, None) == -5
+    L.csa2_topk_workspace_bytes.restype = ctypes.c_size_t
+    L.csa2_topk_workspace_bytes.argtypes = [ctypes.c_int, i64, ctypes.c_int]
+    assert L.csa2_topk_workspace_bytes(2, 8192, 512) == 0           # one segment: no scratch
+    assert L.csa2_topk_workspace_bytes(2, 1 << 20, 512) > 0
+    L.csa2_sparse_attn.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, i64, ctypes.c_int, vp, vp,
+                                   ctypes.c_int, vp, i64, vp, vp, vp, ctypes.c_int, ctypes.c_float, vp, ctypes.c_int,
+                                   vp, vp, ctypes.c_size_t, vp]
+    args = [fake, 4, 64, 512, fake, fake, 100, 1, fake, fake, 512, fake, 128, fake, fake, fake, 128, 0.05, fake, 0,
+            None, None, 0, None]
+    a = list(args); a[2] = 40                       # heads not a multiple of 16
+    assert L.csa2_sparse_attn(*a) == -2
+    a = list(args); a[16] = 256                     # window > swa_cap
+    assert L.csa2_sparse_attn(*a) == -2
+    a = list(args); a[19] = 7                       # out dtype
+    assert L.csa2_sparse_attn(*a) == -3
+    a = list(args); a[9] = None                     # idx NULL with k > 0
+    assert L.csa2_sparse_attn(*a) == -1
+    assert L.csa2_sparse_attn(*args) == -5          # split over workgroups needs a workspace

@@ -1,0 +1,310 @@
+"""GPU parity of each C-ABI call against the oracle, at sizes the oracle finishes in
+seconds that still span several tiles / segments and a ragged tail."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa2_oracle as O
+from tests import gpu_cases as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def C():
+    from fp4_kv_cache_layer_amd import csa2
+    csa2.csa2_init()
+    return csa2
+
+
+def _adversarial_rows(rng, rows, dim, group):
+    """Rows whose group maxima and elements sit on and 1 ulp beside rounding midpoints."""
+    mids = [(O.E4M3[c] + O.E4M3[c + 1]) / 2 for c in range(0x7E)]
+    t = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    x = np.zeros((rows, dim), np.float32)
+    for r in range(rows):
+        for g in range(dim // group):
+            m = mids[rng.integers(len(mids))]
+            a = np.float32(6 * m)
+            s = O.E4M3[O.nearest_code(np.array([a / 6.0]), O.E4M3[:0x7F], np.arange(0x7F))[0]]
+            v = (s * t[rng.integers(len(t), size=group)]).astype(np.float32)
+            v[0] = a
+            nudge = rng.integers(3, size=group)
+            v = np.where(nudge == 1, np.nextafter(v, np.float32(0)), v)
+            v = np.where(nudge == 2, np.nextafter(v, np.float32(1e9)), v)
+            v *= rng.choice([-1, 1], size=group).astype(np.float32)
+            x[r, g * group:(g + 1) * group] = rng.permutation(v)
+    return x
+
+
+def _special_rows(dim):
+    rows = [np.zeros(dim), -np.zeros(dim), np.full(dim, 3000.0), np.full(dim, 1e-30),
+            np.linspace(-22.6, 22.6, dim), np.full(dim, 448.0), np.full(dim, 2.0 ** -130)]
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "fp8"])
+@pytest.mark.parametrize("src_dt", ["f32", "bf16"])
+def test_quantize_bitexact(C, fmt, src_dt):
+    _say("quantize", fmt, src_dt)
+    rng = np.random.default_rng(1)
+    dim = 512 if fmt != "mxfp4" else 128
+    group = {"nvfp4": 16, "mxfp4": 32, "fp8": 8}[fmt]
+    x = np.concatenate([
+        (rng.normal(size=(300, dim)) * 10.0 ** rng.uniform(-3, 2, size=(300, 1))).astype(np.float32),
+        _adversarial_rows(rng, 40, dim, 16 if fmt == "nvfp4" else group),
+        _special_rows(dim)])
+    xt = torch.from_numpy(x).cuda()
+    if src_dt == "bf16":
+        xt = xt.to(torch.bfloat16)
+        x = xt.float().cpu().numpy()
+    rows = x.shape[0]
+    # scatter into a larger table with a permutation; two rows point outside and are skipped
+    dst_rows = rows + 5
+    dst = rng.permutation(dst_rows)[:rows].astype(np.int64)
+    dst[3], dst[7] = -1, dst_rows + 2
+    f = {"nvfp4": C.FMT_NVFP4, "mxfp4": C.FMT_MXFP4, "fp8": C.FMT_FP8}[fmt]
+    per = dim if fmt == "fp8" else dim // 2
+    codes = torch.full((dst_rows, per), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = None if fmt == "fp8" else torch.full((dst_rows, dim // group), 0xCD, dtype=torch.uint8, device="cuda")
+    C.csa2_quantize_kv(xt, f, codes, scales, torch.from_numpy(dst).cuda())
+    torch.cuda.synchronize()
+    gc = codes.cpu().numpy()
+    if fmt == "nvfp4":
+        rc, rs = O.quantize_nvfp4(x)
+    elif fmt == "mxfp4":
+        rc, rs = O.quantize_mxfp4(x)
+    else:
+        rc, rs = O.quantize_fp8(x), None
+    ok = (dst >= 0) & (dst < dst_rows)
+    assert np.array_equal(gc[dst[ok]], rc[ok])
+    untouched = np.setdiff1d(np.arange(dst_rows), dst[ok])
+    assert np.all(gc[untouched] == 0xAB)
+    if rs is not None:
+        gs = scales.cpu().numpy()
+        assert np.array_equal(gs[dst[ok]], rs[ok])
+        assert np.all(gs[untouched] == 0xCD)
+
+
+def _score_case(seed, n_seq, seq_cap, n_vis, idx_heads):
+    wl = G.workloads.Workload(
+        name="small", seed=seed, n_seq=n_seq, seq_cap=seq_cap, m=1, heads=16, idx_heads=idx_heads,
+        q_seq=np.array([i % n_seq for i in range(len(n_vis))], np.int32),
+        q_pos=np.array(n_vis, np.int64) - 1, replay_start=np.zeros(len(n_vis), np.int64), layers=("full",),
+        new_entries=(0, 0))
+    return G.Case(wl)
+
+
+@pytest.mark.parametrize("idx_heads", [16, 8, 5])
+def test_index_score_parity(C, idx_heads):
+    _say("index_score", idx_heads)
+    case = _score_case(10 + idx_heads, 3, 9000, [9000, 4097, 1, 8999, 64], idx_heads)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq, n_vis, _, _ = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(wl.n_q, 16, idx_heads, wl.seq_cap)
+    st.scores.fill_(12345.0)
+    st.quantize_index_q(q_idx)
+    st.score(caches, w, q_seq, n_vis)
+    torch.cuda.synchronize()
+    gs = st.scores.cpu().numpy()
+    for qi in range(wl.n_q):
+        seq = int(wl.q_seq[qi])
+        oc = case.oracle_caches(seq)
+        assert np.array_equal(caches.ik_codes[seq].cpu().numpy(), oc.ik_codes)
+        assert np.array_equal(caches.ik_scales[seq].cpu().numpy(), oc.ik_scales)
+        qc, qs, wq, _ = case.oracle_query(0, qi)
+        assert np.array_equal(st.qi_codes[qi].cpu().numpy(), qc)
+        nv = int(wl.n_vis[qi])
+        _, ref = O.full_scores(qc, qs, wq, oc, nv)
+        got = gs[qi, :nv]
+        assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+        assert np.all(gs[qi, nv:] == 12345.0)   # positions past n_vis untouched
+
+
+def test_index_score_pool_slots(C):
+    _say("index_score pool")
+    case = _score_case(21, 2, 6000, [6000, 5003, 333], 16)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq, n_vis, _, _ = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, max_blocks=300)
+    rng = np.random.default_rng(3)
+    blocks = np.full((wl.n_q, 300), -1, np.int32)
+    ncb = np.array([300, 250, 60], np.int32)
+    for qi in range(wl.n_q):
+        nb = -(-int(wl.n_vis[qi]) // 8)
+        b = np.sort(rng.choice(nb + 20, size=ncb[qi], replace=False)).astype(np.int32)  # some beyond n_vis
+        blocks[qi, :ncb[qi]] = b
+    blocks[1, 5] = -1
+    st.pool.copy_(torch.from_numpy(blocks))
+    st.pool_count.copy_(torch.from_numpy(ncb))
+    st.quantize_index_q(q_idx)
+    st.score(caches, w, q_seq, n_vis, in_pool=True)
+    torch.cuda.synchronize()
+    gs = st.scores.cpu().numpy()
+    for qi in range(wl.n_q):
+        seq = int(wl.q_seq[qi])
+        oc = case.oracle_caches(seq)
+        qc, qs, wq, _ = case.oracle_query(0, qi)
+        nv = int(wl.n_vis[qi])
+        for slot in range(300 * 8):
+            b = blocks[qi, slot // 8]
+            pos = b * 8 + slot % 8
+            valid = slot < ncb[qi] * 8 and b >= 0 and pos < nv
+            if not valid:
+                assert gs[qi, slot] == -np.inf
+        slots = np.array([s for s in range(ncb[qi] * 8) if blocks[qi, s // 8] >= 0
+                          and blocks[qi, s // 8] * 8 + s % 8 < nv])
+        pos = blocks[qi, slots // 8].astype(np.int64) * 8 + slots % 8
+        _, ref = O.full_scores(qc, qs, wq, oc, nv, cand=pos)
+        got = gs[qi, slots]
+        assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("n,k", [(1, 512), (511, 512), (512, 512), (513, 512), (8192, 512), (8193, 512),
+                                 (20000, 7), (70001, 512), (200000, 2048), (9000, 1), (300000, 512)])
+def test_topk_exact_on_same_scores(C, n, k):
+    """Selection is an integer decision: on identical fp32 scores the GPU set must equal the
+    oracle's ranking (score desc, position asc) exactly, ties included."""
+    _say("topk", n, k)
+    rng = np.random.default_rng(n + k)
+    n_q = 3
+    sc = rng.normal(size=(n_q, n)).astype(np.float32)
+    sc[1] = rng.integers(0, 50, size=n).astype(np.float32)     # heavy ties
+    sc[2, : n // 2] = 1.0                                       # a tied plateau
+    n_vis = np.array([n, max(1, n - 37), n], np.int64)
+    idx = torch.empty(n_q, k, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(n_q, dtype=torch.int32, device="cuda")
+    C.csa2_topk(torch.from_numpy(sc).cuda(), torch.from_numpy(n_vis).cuda(), n, k, idx, cnt)
+    torch.cuda.synchronize()
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    for qi in range(n_q):
+        nv = int(n_vis[qi])
+        ref = O.topk_positions(sc[qi, :nv].astype(np.float64), np.arange(nv), k)
+        assert gc[qi] == min(k, nv)
+        assert np.array_equal(gi[qi], ref.astype(np.int32))
+
+
+def test_topk_pool_slots_exact(C):
+    _say("topk pool slots")
+    rng = np.random.default_rng(5)
+    n_q, mb, k = 2, 2048, 512
+    nv = np.array([100000, 7000], np.int64)
+    blocks = np.full((n_q, mb), -1, np.int32)
+    ncb = np.array([2048, 800], np.int32)
+    for qi in range(n_q):
+        nb = -(-int(nv[qi]) // 8)
+        blocks[qi, :ncb[qi]] = np.sort(rng.choice(nb + 5, size=ncb[qi], replace=False))
+    sc = rng.normal(size=(n_q, mb * 8)).astype(np.float32)
+    idx = torch.empty(n_q, k, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(n_q, dtype=torch.int32, device="cuda")
+    C.csa2_topk(torch.from_numpy(sc).cuda(), torch.from_numpy(nv).cuda(), int(nv.max()), k, idx, cnt, None,
+                torch.from_numpy(blocks).cuda(), torch.from_numpy(ncb).cuda(), 8)
+    torch.cuda.synchronize()
+    for qi in range(n_q):
+        slots = np.arange(ncb[qi] * 8)
+        b = blocks[qi, slots // 8]
+        pos = b.astype(np.int64) * 8 + slots % 8
+        ok = (b >= 0) & (pos < nv[qi])
+        ref = O.topk_positions(sc[qi, slots[ok]].astype(np.float64), pos[ok], k)
+        assert np.array_equal(idx[qi].cpu().numpy(), ref.astype(np.int32))
+
+
+@pytest.mark.parametrize("n_vis,mb", [(1_000_003, 2048), (16384, 2048), (16385, 2048), (77, 4), (5000, 100)])
+def test_build_pool_exact(C, n_vis, mb):
+    _say("build_pool", n_vis, mb)
+    rng = np.random.default_rng(n_vis)
+    n_q = 2
+    sc = rng.standard_t(3, size=(n_q, n_vis)).astype(np.float32)
+    nv = np.array([n_vis, max(1, n_vis - 3)], np.int64)
+    blk = torch.empty(n_q, mb, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(n_q, dtype=torch.int32, device="cuda")
+    C.csa2_build_pool(torch.from_numpy(sc).cuda(), torch.from_numpy(nv).cuda(), n_vis, blk, cnt, 8)
+    torch.cuda.synchronize()
+    for qi in range(n_q):
+        ref = O.build_pool(sc[qi].astype(np.float64), int(nv[qi]), 8, mb)
+        assert np.array_equal(blk[qi].cpu().numpy(), ref.astype(np.int32))
+        assert cnt[qi].item() == min(mb, -(-int(nv[qi]) // 8))
+
+
+def _attn_case(seed, n_seq, seq_cap, heads, t_list, s_list, swa_cap=128):
+    n_q = len(t_list)
+    wl = G.workloads.Workload(
+        name="attn", seed=seed, n_seq=n_seq, seq_cap=seq_cap, m=1, heads=heads, idx_heads=16,
+        q_seq=np.array([i % n_seq for i in range(n_q)], np.int32), q_pos=np.array(t_list, np.int64),
+        replay_start=np.array(s_list, np.int64), layers=("full",), new_entries=(0, 0), swa_cap=swa_cap)
+    return G.Case(wl)
+
+
+@pytest.mark.parametrize("heads,out_dt", [(64, "f32"), (16, "f32"), (80, "f32"), (64, "bf16")])
+def test_sparse_attn_parity(C, heads, out_dt):
+    _say("sparse_attn", heads, out_dt)
+    t = [3000, 2999, 100, 5, 2500, 2000]
+    s = [0, 2999 - 5, 0, 5, 2500 - 126, 0]
+    case = _attn_case(7 + heads, len(t), 3001, heads, t, s)   # one sequence per query
+    wl = case.wl
+    caches = case.gpu_caches()
+    _, _, qa = case.gpu_query_inputs(0)
+    q_seq, _, q_pos, rs = case.gpu_meta()
+    rng = np.random.default_rng(heads)
+    k = 512
+    idx = np.full((wl.n_q, k), -1, np.int32)
+    counts = [512, 300, 0, 512, 17, 512]
+    for qi in range(wl.n_q):
+        idx[qi, :counts[qi]] = np.sort(rng.choice(3001, size=counts[qi], replace=False))
+    idx[3, 10] = 3001            # out of range: skipped
+    idx[5, 20] = -7              # negative: skipped
+    dt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    out = torch.empty(wl.n_q, heads, 512, dtype=dt, device="cuda")
+    lse = torch.empty(wl.n_q, heads, dtype=torch.float32, device="cuda")
+    C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, torch.from_numpy(idx).cuda(), caches.swa[0],
+                       caches.swa_base, q_pos, rs, 128, 1.0 / math.sqrt(512), out, lse)
+    torch.cuda.synchronize()
+    go, gl = out.float().cpu().numpy(), lse.cpu().numpy()
+    for qi in range(wl.n_q):
+        seq = int(wl.q_seq[qi])
+        oc = case.oracle_caches(seq)
+        assert np.array_equal(caches.kv_codes[seq].cpu().numpy(), oc.kv_codes)
+        assert np.array_equal(caches.swa[0][seq].cpu().numpy(), oc.swa[0][0])
+        _, _, _, qa_np = case.oracle_query(0, qi)
+        sel = idx[qi][(idx[qi] >= 0) & (idx[qi] < 3001)]
+        ref, ref_lse = O.sparse_attention(qa_np, oc.main_rows(sel),
+                                          oc.swa_rows(0, O.swa_positions(t[qi], s[qi], 128)), 1 / math.sqrt(512))
+        G.attn_close(go[qi], ref, 2e-3 if out_dt == "f32" else 6e-3)
+        assert np.abs(gl[qi] - ref_lse).max() <= 1e-3
+
+
+def test_sparse_attn_no_keys(C):
+    """s > t leaves the window empty; with no main entries the output is 0 and lse -inf."""
+    _say("sparse_attn no keys")
+    case = _attn_case(3, 1, 100, 16, [50, 60], [51, 0])
+    caches = case.gpu_caches()
+    _, _, qa = case.gpu_query_inputs(0)
+    q_seq, _, q_pos, rs = case.gpu_meta()
+    idx = torch.full((2, 4), -1, dtype=torch.int32, device="cuda")
+    out = torch.full((2, 16, 512), 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.empty(2, 16, dtype=torch.float32, device="cuda")
+    C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, idx, caches.swa[0], caches.swa_base, q_pos, rs,
+                       128, 0.05, out, lse)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(torch.isfinite(lse[1]))
+
+
+def test_smoke_tiny_decode(C):
+    _say("smoke c1")
+    res = G.smoke_check()
+    assert res["attn_err"] < 2e-3
