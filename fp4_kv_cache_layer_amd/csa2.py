@@ -78,6 +78,19 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _run(name: str, args: tuple, bind: bool):
+    """Call the C entry point now, or (bind=True) return a zero-argument callable that
+    repeats the call with the same pointers, sizes and stream (validated once)."""
+    fn = getattr(lib(), name)
+    if bind:
+        def call():
+            _check(fn(*args), name)
+        call.__name__ = name
+        return call
+    _check(fn(*args), name)
+    return None
+
+
 def _check(rc: int, name: str):
     if rc != 0:
         L = lib()
@@ -103,12 +116,15 @@ def csa2_init():
     _check(lib().csa2_init(), "csa2_init")
 
 
-def csa2_quantize_kv(src, fmt: int, codes, scales=None, dst_row=None):
+def csa2_quantize_kv(src, fmt: int, codes, scales=None, dst_row=None, _bind: bool = False):
     """src [rows, dim] f32/bf16; codes [dst_rows, dim/2] (FP4) or [dst_rows, dim] (FP8) u8;
     scales [dst_rows, dim/16 | dim/32] u8; dst_row [rows] int64 or None."""
     if src.dtype not in (torch.float32, torch.bfloat16) or src.dim() != 2 or not src.is_cuda:
         raise TypeError("src must be a 2-D f32/bf16 device tensor")
-    src = src.contiguous()
+    if not src.is_contiguous():
+        if _bind:
+            raise ValueError("src must be contiguous when binding a call")
+        src = src.contiguous()
     rows, dim = src.shape
     _need(codes, torch.uint8, 2, "codes")
     per = dim if fmt == FMT_FP8 else dim // 2
@@ -124,13 +140,12 @@ def csa2_quantize_kv(src, fmt: int, codes, scales=None, dst_row=None):
         if dst_row.shape[0] != rows:
             raise ValueError("dst_row length != rows")
     dt = DT_F32 if src.dtype == torch.float32 else DT_BF16
-    rc = lib().csa2_quantize_kv(_p(src), dt, rows, dim, fmt, _p(dst_row), codes.shape[0], _p(codes),
-                                _p(scales) if fmt != FMT_FP8 else None, _stream())
-    _check(rc, "csa2_quantize_kv")
+    return _run("csa2_quantize_kv", (_p(src), dt, rows, dim, fmt, _p(dst_row), codes.shape[0], _p(codes),
+                                     _p(scales) if fmt != FMT_FP8 else None, _stream()), _bind)
 
 
 def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
-                     cand_blocks=None, n_cand_blocks=None, block: int = 8):
+                     cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
     """q_codes [n_q, H_I, 64], q_scales [n_q, H_I, 4], w [n_q, H_I] f32;
     k_codes [n_seq, seq_cap, 64], k_scales [n_seq, seq_cap, 4]; q_seq [n_q] int32,
     n_vis [n_q] int64; scores [n_q, stride] f32; cand_blocks [n_q, max_blocks] int32."""
@@ -155,10 +170,9 @@ def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scor
         max_blocks = cand_blocks.shape[1]
         if cand_blocks.shape[0] != n_q or n_cand_blocks.shape[0] != n_q:
             raise ValueError("index_score: inconsistent pool shapes")
-    rc = lib().csa2_index_score(_p(q_codes), _p(q_scales), _p(w), n_q, h, 2 * half, _p(k_codes), _p(k_scales),
-                                seq_cap, n_seq, _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks), block,
-                                max_blocks, _p(scores), scores.stride(0), _stream())
-    _check(rc, "csa2_index_score")
+    return _run("csa2_index_score", (_p(q_codes), _p(q_scales), _p(w), n_q, h, 2 * half, _p(k_codes), _p(k_scales),
+                                     seq_cap, n_seq, _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks),
+                                     block, max_blocks, _p(scores), scores.stride(0), _stream()), _bind)
 
 
 def csa2_topk_workspace_bytes(n_q: int, n_slots: int, k: int) -> int:
@@ -166,7 +180,7 @@ def csa2_topk_workspace_bytes(n_q: int, n_slots: int, k: int) -> int:
 
 
 def csa2_topk(scores, n_vis, max_vis: int, k: int, idx_out, count_out, workspace=None,
-              cand_blocks=None, n_cand_blocks=None, block: int = 8):
+              cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
     """scores [n_q, stride] f32 -> idx_out [n_q, k] int32 ascending, -1 padded; count_out [n_q] int32."""
     _need(scores, torch.float32, 2, "scores")
     _need(n_vis, torch.int64, 1, "n_vis")
@@ -185,17 +199,17 @@ def csa2_topk(scores, n_vis, max_vis: int, k: int, idx_out, count_out, workspace
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    rc = lib().csa2_topk(_p(scores), scores.stride(0), n_q, _p(n_vis), max_vis, _p(cand_blocks),
-                         _p(n_cand_blocks), block, max_blocks, k, _p(idx_out), _p(count_out), _p(workspace),
-                         ws_bytes, _stream())
-    _check(rc, "csa2_topk")
+    return _run("csa2_topk", (_p(scores), scores.stride(0), n_q, _p(n_vis), max_vis, _p(cand_blocks),
+                              _p(n_cand_blocks), block, max_blocks, k, _p(idx_out), _p(count_out), _p(workspace),
+                              ws_bytes, _stream()), _bind)
 
 
 def csa2_pool_workspace_bytes(n_q: int, max_vis: int, block: int, max_blocks: int) -> int:
     return int(lib().csa2_pool_workspace_bytes(n_q, max_vis, block, max_blocks))
 
 
-def csa2_build_pool(scores, n_vis, max_vis: int, blocks_out, count_out, block: int = 8, workspace=None):
+def csa2_build_pool(scores, n_vis, max_vis: int, blocks_out, count_out, block: int = 8, workspace=None,
+                    _bind: bool = False):
     """scores [n_q, stride] f32 -> blocks_out [n_q, max_blocks] int32 ascending, -1 padded."""
     _need(scores, torch.float32, 2, "scores")
     _need(n_vis, torch.int64, 1, "n_vis")
@@ -206,9 +220,8 @@ def csa2_build_pool(scores, n_vis, max_vis: int, blocks_out, count_out, block: i
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    rc = lib().csa2_build_pool(_p(scores), scores.stride(0), n_q, _p(n_vis), max_vis, block, max_blocks,
-                               _p(blocks_out), _p(count_out), _p(workspace), ws_bytes, _stream())
-    _check(rc, "csa2_build_pool")
+    return _run("csa2_build_pool", (_p(scores), scores.stride(0), n_q, _p(n_vis), max_vis, block, max_blocks,
+                                    _p(blocks_out), _p(count_out), _p(workspace), ws_bytes, _stream()), _bind)
 
 
 def csa2_attn_workspace_bytes(n_q: int, n_heads: int, dim: int, k: int, window: int) -> int:
@@ -216,7 +229,7 @@ def csa2_attn_workspace_bytes(n_q: int, n_heads: int, dim: int, k: int, window: 
 
 
 def csa2_sparse_attn(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, replay_start, window: int,
-                     sm_scale: float, out, lse=None, workspace=None):
+                     sm_scale: float, out, lse=None, workspace=None, _bind: bool = False):
     """q [n_q, H, 512] bf16; kv_codes [n_seq, seq_cap, 256], kv_scales [n_seq, seq_cap, 32];
     idx [n_q, k] int32; swa [n_seq, swa_cap, 512] u8; swa_base [n_seq] int64;
     q_pos, replay_start [n_q] int64; out [n_q, H, 512] f32/bf16; lse [n_q, H] f32."""
@@ -246,7 +259,7 @@ def csa2_sparse_attn(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, r
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
     odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
-    rc = lib().csa2_sparse_attn(_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq), _p(idx), k,
-                                _p(swa), swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), window,
-                                float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes, _stream())
-    _check(rc, "csa2_sparse_attn")
+    return _run("csa2_sparse_attn", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq), _p(idx),
+                                     k, _p(swa), swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), window,
+                                     ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes,
+                                     _stream()), _bind)

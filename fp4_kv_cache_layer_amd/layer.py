@@ -11,7 +11,9 @@ Top-K inside it.
 
 This module only allocates buffers and sequences calls into the C ABI; it moves no
 data itself.  One `Csa2Step` holds the buffers of a batch of query rows; `full`,
-`reindex` and `reuse` run one layer each on the caller's stream.
+`reindex` and `reuse` run one layer each on the caller's stream.  With bind=True they
+return the layer's calls as a list of zero-argument callables with every argument
+validated and marshalled once, for tight decode loops.
 """
 from __future__ import annotations
 
@@ -74,51 +76,56 @@ class Csa2Step:
         self.sm_scale = 1.0 / math.sqrt(dim)
 
     # ---- steps ----
-    def quantize_index_q(self, q_f32):
+    def quantize_index_q(self, q_f32, bind=False):
         """indexer Q [n_q, H_I, d] f32 -> MXFP4 (per query, per head, per 32 channels)."""
         n_q, h, d = q_f32.shape
-        C.csa2_quantize_kv(q_f32.reshape(n_q * h, d), C.FMT_MXFP4, self.qi_codes.view(n_q * h, d // 2),
-                           self.qi_scales.view(n_q * h, d // 32))
+        return C.csa2_quantize_kv(q_f32.view(n_q * h, d), C.FMT_MXFP4, self.qi_codes.view(n_q * h, d // 2),
+                                  self.qi_scales.view(n_q * h, d // 32), _bind=bind)
 
-    def score(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False):
+    def score(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False):
         if in_pool:
-            C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
-                               self.scores, self.pool, self.pool_count, self.block)
-        else:
-            C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
-                               self.scores)
+            return C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq,
+                                      n_vis, self.scores, self.pool, self.pool_count, self.block, _bind=bind)
+        return C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
+                                  self.scores, _bind=bind)
 
-    def select(self, n_vis, in_pool: bool = False):
+    def select(self, n_vis, in_pool: bool = False, bind=False):
         if in_pool:
-            C.csa2_topk(self.scores, n_vis, self.seq_cap, self.k, self.idx, self.count, self.ws_topk,
-                        self.pool, self.pool_count, self.block)
-        else:
-            C.csa2_topk(self.scores, n_vis, self.seq_cap, self.k, self.idx, self.count, self.ws_topk)
+            return C.csa2_topk(self.scores, n_vis, self.seq_cap, self.k, self.idx, self.count, self.ws_topk,
+                               self.pool, self.pool_count, self.block, _bind=bind)
+        return C.csa2_topk(self.scores, n_vis, self.seq_cap, self.k, self.idx, self.count, self.ws_topk, _bind=bind)
 
-    def build_pool(self, n_vis):
-        C.csa2_build_pool(self.scores, n_vis, self.seq_cap, self.pool, self.pool_count, self.block, self.ws_pool)
+    def build_pool(self, n_vis, bind=False):
+        return C.csa2_build_pool(self.scores, n_vis, self.seq_cap, self.pool, self.pool_count, self.block,
+                                 self.ws_pool, _bind=bind)
 
-    def attend(self, caches: Caches, layer: int, q_attn, q_seq, q_pos, replay_start, out=None, lse=None):
-        C.csa2_sparse_attn(q_attn, caches.kv_codes, caches.kv_scales, q_seq, self.idx, caches.swa[layer],
-                           caches.swa_base, q_pos, replay_start, self.window, self.sm_scale,
-                           self.out if out is None else out, self.lse if lse is None else lse, self.ws_attn)
+    def attend(self, caches: Caches, layer: int, q_attn, q_seq, q_pos, replay_start, out=None, lse=None,
+               bind=False):
+        return C.csa2_sparse_attn(q_attn, caches.kv_codes, caches.kv_scales, q_seq, self.idx, caches.swa[layer],
+                                  caches.swa_base, q_pos, replay_start, self.window, self.sm_scale,
+                                  self.out if out is None else out, self.lse if lse is None else lse, self.ws_attn,
+                                  _bind=bind)
 
     # ---- layer modes ----
+    @staticmethod
+    def _seq(calls, bind):
+        return calls if bind else None
+
     def full(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, make_pool=False,
-             out=None, lse=None):
-        self.quantize_index_q(q_index_f32)
-        self.score(caches, w, q_seq, n_vis)
-        self.select(n_vis)
+             out=None, lse=None, bind=False):
+        calls = [self.quantize_index_q(q_index_f32, bind), self.score(caches, w, q_seq, n_vis, bind=bind),
+                 self.select(n_vis, bind=bind)]
         if make_pool:
-            self.build_pool(n_vis)
-        self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse)
+            calls.append(self.build_pool(n_vis, bind))
+        calls.append(self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind))
+        return self._seq(calls, bind)
 
     def reindex(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, in_pool=False,
-                out=None, lse=None):
-        self.quantize_index_q(q_index_f32)
-        self.score(caches, w, q_seq, n_vis, in_pool)
-        self.select(n_vis, in_pool)
-        self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse)
+                out=None, lse=None, bind=False):
+        calls = [self.quantize_index_q(q_index_f32, bind), self.score(caches, w, q_seq, n_vis, in_pool, bind),
+                 self.select(n_vis, in_pool, bind),
+                 self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
+        return self._seq(calls, bind)
 
-    def reuse(self, caches, layer, q_attn, q_seq, q_pos, replay_start, out=None, lse=None):
-        self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse)
+    def reuse(self, caches, layer, q_attn, q_seq, q_pos, replay_start, out=None, lse=None, bind=False):
+        return self._seq([self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)], bind)
