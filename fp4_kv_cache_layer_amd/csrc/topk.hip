@@ -7,23 +7,28 @@
 // complemented position in the low word, so keys are unique and "larger key" is exactly
 // "ranked earlier".  Selecting the K largest keys is then an exact radix select.
 //
-// Work split: a query's candidates are cut into segments of 8,192 (one 1,024-thread
-// workgroup each, 8 keys per thread held in registers).  A workgroup finds its segment's
-// K largest keys with a most-significant-digit radix select: it starts at the highest
-// bit where the segment's largest and smallest keys differ and walks down 8 bits per pass
-// with a 256-bin LDS histogram, stopping as soon as the boundary bin is taken whole
-// (usually after 2-3 passes).  The global Top-K lies inside the union of the segments'
-// Top-K sets, so the survivors (n_seg * K keys) go through the same kernel again until
-// one segment is left; that last workgroup sorts the positions ascending and writes the
-// output.  Scores are read from HBM once; later levels read K keys per segment.
+// Work split: a query's candidates are cut into segments of 8,192, one 256-thread
+// workgroup each with 32 keys per thread held in registers.  A workgroup finds its
+// segment's K largest keys with a most-significant-digit radix select: it starts at the
+// highest bit where the segment's largest and smallest keys differ and walks down 8 bits
+// per pass, stopping as soon as the boundary bin is taken whole (usually after 3 passes).
+// Each wave counts into its own 256-bin LDS histogram (two sets, alternating per pass),
+// then every wave scans the sum of the four itself, so a pass costs one barrier and no
+// wave waits on another's serial work.  The global Top-K lies inside the union of the
+// segments' Top-K sets, so the survivors (n_seg * K keys) go through the same kernel again
+// until one segment is left.  Survivors are compacted stably, in candidate order, with
+// ballots and one prefix sum (no atomics): candidates enter every level in ascending
+// position order, so the last level's output is already ascending and no sort is needed,
+// and the result is deterministic.  Scores are read from HBM once; later levels read K
+// keys per segment.
 #include "device.h"
 
 namespace csa2 {
 
-constexpr int kTkThreads = 1024;
-constexpr int kTkEpt = 8;
-constexpr int kTkSeg = kTkThreads * kTkEpt;
+constexpr int kTkThreads = 256;
 constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kTkEpt = 32;
+constexpr int kTkSeg = kTkThreads * kTkEpt;
 
 enum TkMode { kFromScores = 0, kFromBlockMax = 1, kFromKeys = 2 };
 
@@ -59,6 +64,16 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// wave-wide inclusive suffix sum (lane l gets the sum over lanes >= l)
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v, int lane) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const uint32_t o = __shfl_down(v, m);
+    v += (lane + m < 64) ? o : 0u;
+  }
+  return v;
+}
+
 template <int kMode, bool kFinal>
 __global__ __launch_bounds__(kTkThreads) void k_topk(TkArgs a) {
   const int q = blockIdx.y;
@@ -67,48 +82,66 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(TkArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int K = a.k;
 
-  __shared__ uint32_t hist[256];
-  __shared__ uint64_t sel[CSA2_MAX_TOPK];
-  __shared__ int32_t sortbuf[CSA2_MAX_TOPK];
+  __shared__ uint32_t hist[2][kTkWaves][256];
+  __shared__ uint32_t cnt[kTkWaves][kTkEpt];
   __shared__ uint64_t red_hi[kTkWaves], red_lo[kTkWaves];
   __shared__ uint32_t red_n[kTkWaves];
-  __shared__ uint32_t s_digit, s_above, s_inbin, s_nsel;
 
   int64_t nv = a.n_vis[q];
   nv = nv < 0 ? 0 : (nv > a.max_vis ? a.max_vis : nv);
+  const int64_t c0 = (int64_t)seg * kTkSeg;
 
-  // ---- load this segment's candidates as keys (0 = no candidate) ----
+  // ---- load this segment's candidates as keys (0 = no candidate); candidate c0 + i*256 + tid ----
   uint64_t key[kTkEpt];
+  if (kMode == kFromScores && a.cand_blocks == nullptr) {
+    const float* sp = a.scores + q * a.scores_stride + c0;
+    const int lim = (int)(nv - c0 < kTkSeg ? (nv - c0 > 0 ? nv - c0 : 0) : kTkSeg);
 #pragma unroll
-  for (int i = 0; i < kTkEpt; ++i) {
-    int64_t c = (int64_t)seg * kTkSeg + (int64_t)i * kTkThreads + tid;
-    uint64_t kk = 0;
-    if (kMode == kFromScores) {
-      if (a.cand_blocks == nullptr) {
-        if (c < nv) kk = make_key(a.scores[q * a.scores_stride + c], (uint32_t)c);
-      } else {
-        int64_t nc = a.n_cand_blocks[q];
-        nc = nc < 0 ? 0 : (nc > a.max_cand_blocks ? a.max_cand_blocks : nc);
-        if (c < nc * a.block) {
-          int32_t b = a.cand_blocks[(int64_t)q * a.max_cand_blocks + c / a.block];
-          int64_t pos = (int64_t)b * a.block + c % a.block;
-          if (b >= 0 && pos < nv) kk = make_key(a.scores[q * a.scores_stride + c], (uint32_t)pos);
-        }
+    for (int i = 0; i < kTkEpt; ++i) {
+      const int o = i * kTkThreads + tid;
+      key[i] = o < lim ? make_key(sp[o], (uint32_t)(c0 + o)) : 0ull;
+    }
+  } else if (kMode == kFromScores) {
+    int64_t nc = a.n_cand_blocks[q];
+    nc = nc < 0 ? 0 : (nc > a.max_cand_blocks ? a.max_cand_blocks : nc);
+    const float* sp = a.scores + q * a.scores_stride;
+    const int32_t* cb = a.cand_blocks + (int64_t)q * a.max_cand_blocks;
+#pragma unroll
+    for (int i = 0; i < kTkEpt; ++i) {
+      const int64_t c = c0 + i * kTkThreads + tid;
+      uint64_t kk = 0;
+      if (c < nc * a.block) {
+        const int32_t b = cb[c / a.block];
+        const int64_t pos = (int64_t)b * a.block + c % a.block;
+        if (b >= 0 && pos < nv) kk = make_key(sp[c], (uint32_t)pos);
       }
-    } else if (kMode == kFromBlockMax) {
-      int64_t nblk = (nv + a.block - 1) / a.block;
+      key[i] = kk;
+    }
+  } else if (kMode == kFromBlockMax) {
+    const int64_t nblk = (nv + a.block - 1) / a.block;
+    const float* sp = a.scores + q * a.scores_stride;
+#pragma unroll
+    for (int i = 0; i < kTkEpt; ++i) {
+      const int64_t c = c0 + i * kTkThreads + tid;
+      uint64_t kk = 0;
       if (c < nblk) {
-        const float* s = a.scores + q * a.scores_stride + c * a.block;
+        const float* s = sp + c * a.block;
         int64_t nin = nv - c * a.block;
         nin = nin < a.block ? nin : a.block;
         float m = s[0];
         for (int j = 1; j < nin; ++j) m = fmaxf(m, s[j]);
         kk = make_key(m, (uint32_t)c);
       }
-    } else {
-      if (c < a.keys_in_per_q) kk = a.keys_in[q * a.keys_in_per_q + c];
+      key[i] = kk;
     }
-    key[i] = kk;
+  } else {
+    const uint64_t* kp = a.keys_in + q * a.keys_in_per_q + c0;
+    const int lim = (int)(a.keys_in_per_q - c0 < kTkSeg ? a.keys_in_per_q - c0 : kTkSeg);
+#pragma unroll
+    for (int i = 0; i < kTkEpt; ++i) {
+      const int o = i * kTkThreads + tid;
+      key[i] = o < lim ? kp[o] : 0ull;
+    }
   }
 
   // ---- count, max and min of the valid keys ----
@@ -134,11 +167,11 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(TkArgs a) {
     red_hi[wave] = kmax;
     red_lo[wave] = kmin;
   }
-  if (tid == 0) s_nsel = 0;
   __syncthreads();
   n = 0;
   kmax = 0;
   kmin = ~0ull;
+#pragma unroll
   for (int wv = 0; wv < kTkWaves; ++wv) {
     n += red_n[wv];
     kmax = red_hi[wv] > kmax ? red_hi[wv] : kmax;
@@ -148,98 +181,109 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(TkArgs a) {
   // ---- radix select: find (prefix, mask) such that exactly K keys have (key&mask) >= prefix ----
   uint64_t prefix = 0, mask = 0;
   if (n > (uint32_t)K) {
-    int hb = 63 - __clzll(kmax ^ kmin);  // n >= 2 unique keys -> kmax != kmin
+    const int hb = 63 - __clzll(kmax ^ kmin);  // n >= 2 unique keys -> kmax != kmin
     mask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
     prefix = kmax & mask;
     int shift = hb - 7 > 0 ? hb - 7 : 0;
     uint32_t need = (uint32_t)K;
-    while (true) {
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
+    for (int pass = 0;; ++pass) {
+      uint32_t* h = hist[pass & 1][wave];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[lane + 64 * i] = 0;
 #pragma unroll
       for (int i = 0; i < kTkEpt; ++i)
-        if (key[i] && (key[i] & mask) == prefix) atomicAdd(&hist[(uint32_t)(key[i] >> shift) & 255u], 1u);
+        if (key[i] && (key[i] & mask) == prefix) atomicAdd(&h[(uint32_t)(key[i] >> shift) & 255u], 1u);
       __syncthreads();
-      if (wave == 0) {
-        // lane l owns bins 4l..4l+3; S(d) = number of counted keys with digit >= d
-        uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-        uint32_t tot = h0 + h1 + h2 + h3;
-        // exclusive suffix sum over lanes above this one
-        uint32_t incl = tot;
-        for (int m = 1; m < 64; m <<= 1) {
-          uint32_t o = __shfl_down(incl, m);
-          if (lane + m < 64) incl += o;
-        }
-        uint32_t above_lane = incl - tot;
-        uint32_t s3 = above_lane + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
-        int d = -1;
-        uint32_t ab = 0, ib = 0;
-        if (s3 >= need) { d = 4 * lane + 3; ab = above_lane; ib = h3; }
-        else if (s2 >= need) { d = 4 * lane + 2; ab = s3; ib = h2; }
-        else if (s1 >= need) { d = 4 * lane + 1; ab = s2; ib = h1; }
-        else if (s0 >= need) { d = 4 * lane; ab = s1; ib = h0; }
-        // the boundary digit is the largest d with S(d) >= need
-        int dm = d;
-        for (int m = 32; m >= 1; m >>= 1) {
-          int o = __shfl_xor(dm, m);
-          dm = o > dm ? o : dm;
-        }
-        if (d == dm && d >= 0) {
-          s_digit = (uint32_t)d;
-          s_above = ab;
-          s_inbin = ib;
+      // every wave: lane l owns bins 4l..4l+3 of the summed histogram
+      uint32_t hs[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int wv = 0; wv < kTkWaves; ++wv) v += hist[pass & 1][wv][4 * lane + j];
+        hs[j] = v;
+      }
+      const uint32_t tot = hs[0] + hs[1] + hs[2] + hs[3];
+      const uint32_t incl = wave_suffix_sum(tot, lane);
+      const uint32_t above_lane = incl - tot;
+      // the boundary digit is the largest d with (count of digits >= d) >= need
+      uint32_t d = 0, above = 0, inbin = 0;
+      const bool mine = above_lane < need && incl >= need;
+      if (mine) {
+        uint32_t acc = above_lane;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (acc + hs[j] >= need) {
+            d = 4 * lane + j;
+            above = acc;
+            inbin = hs[j];
+            break;
+          }
+          acc += hs[j];
         }
       }
-      __syncthreads();
-      uint32_t d = s_digit, above = s_above, inbin = s_inbin;
+      const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
+      d = __builtin_amdgcn_readlane(d, owner);
+      above = __builtin_amdgcn_readlane(above, owner);
+      inbin = __builtin_amdgcn_readlane(inbin, owner);
       need -= above;
       prefix |= (uint64_t)d << shift;
       mask |= 255ull << shift;
       if (inbin == need || shift == 0) break;
       shift = shift - 8 > 0 ? shift - 8 : 0;
-      __syncthreads();  // everyone has read s_* before the next pass rewrites hist
     }
   }
 
-  // ---- compact the selected keys into LDS ----
+  // ---- stable compaction in candidate order (i-major, then thread) ----
+  // survivors of slot i in wave w: one ballot; cnt[w][i] = their number
 #pragma unroll
   for (int i = 0; i < kTkEpt; ++i) {
-    if (key[i] && (key[i] & mask) >= prefix) {
-      uint32_t slot = atomicAdd(&s_nsel, 1u);
-      if (slot < (uint32_t)K) sel[slot] = key[i];
-    }
+    const uint64_t m = __ballot(key[i] && (key[i] & mask) >= prefix);
+    if (lane == 0) cnt[wave][i] = (uint32_t)__popcll(m);
   }
   __syncthreads();
-  uint32_t nsel = s_nsel < (uint32_t)K ? s_nsel : (uint32_t)K;
+  // lane i < 32: off = (survivors of slots < i, all waves) + (survivors of slot i, waves < w)
+  uint32_t tot_i = 0, before_w = 0;
+  if (lane < kTkEpt) {
+#pragma unroll
+    for (int wv = 0; wv < kTkWaves; ++wv) {
+      const uint32_t c = cnt[wv][lane];
+      tot_i += c;
+      before_w += wv < wave ? c : 0u;
+    }
+  }
+  uint32_t excl = tot_i;  // exclusive prefix over lanes 0..31
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    const uint32_t o = __shfl_up(excl, m);
+    excl += (lane >= m) ? o : 0u;
+  }
+  const uint32_t total = __builtin_amdgcn_readlane(excl, kTkEpt - 1);
+  const uint32_t off = excl - tot_i + before_w;
+  const uint32_t nsel = total < (uint32_t)K ? total : (uint32_t)K;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   if (!kFinal) {
     uint64_t* out = a.keys_out + ((int64_t)q * gridDim.x + seg) * K;
-    for (int i = tid; i < K; i += kTkThreads) out[i] = i < (int)nsel ? sel[i] : 0ull;
+#pragma unroll
+    for (int i = 0; i < kTkEpt; ++i) {
+      const bool take = key[i] && (key[i] & mask) >= prefix;
+      const uint64_t m = __ballot(take);
+      const uint32_t slot = __builtin_amdgcn_readlane(off, i) + (uint32_t)__popcll(m & lt_mask);
+      if (take && slot < (uint32_t)K) out[slot] = key[i];
+    }
+    for (int i = (int)nsel + tid; i < K; i += kTkThreads) out[i] = 0ull;
     return;
   }
-
-  // ---- final: ascending positions, -1 padded ----
-  int P = 2;
-  while (P < (int)nsel) P <<= 1;
-  for (int i = tid; i < P; i += kTkThreads) sortbuf[i] = i < (int)nsel ? key_pos(sel[i]) : 0x7fffffff;
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < P / 2; i += kTkThreads) {
-        int lo = (i / stride) * 2 * stride + (i % stride);
-        int hi = lo + stride;
-        bool asc = (lo & size) == 0;
-        int32_t x = sortbuf[lo], y = sortbuf[hi];
-        if ((x > y) == asc) {
-          sortbuf[lo] = y;
-          sortbuf[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
   int32_t* out = a.idx_out + (int64_t)q * K;
-  for (int i = tid; i < K; i += kTkThreads) out[i] = i < (int)nsel ? sortbuf[i] : -1;
+#pragma unroll
+  for (int i = 0; i < kTkEpt; ++i) {
+    const bool take = key[i] && (key[i] & mask) >= prefix;
+    const uint64_t m = __ballot(take);
+    const uint32_t slot = __builtin_amdgcn_readlane(off, i) + (uint32_t)__popcll(m & lt_mask);
+    if (take && slot < (uint32_t)K) out[slot] = key_pos(key[i]);
+  }
+  for (int i = (int)nsel + tid; i < K; i += kTkThreads) out[i] = -1;
   if (tid == 0) a.count_out[q] = (int32_t)nsel;
 }
 

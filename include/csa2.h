@@ -166,7 +166,9 @@ int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const floa
  *   cand_blocks NULL: candidates are positions [0, min(n_vis[q], max_vis)), score of
  *                     position j at scores[q, j].
  *   cand_blocks given: the slot layout of csa2_index_score (slots whose position is
- *                     invalid or invisible are not candidates).
+ *                     invalid or invisible are not candidates); with ascending block ids
+ *                     (as csa2_build_pool returns them) the output is ascending, otherwise
+ *                     it follows slot order.
  *   k in 1..2048.  Workspace: csa2_topk_workspace_bytes(n_q, n_slots, k) bytes, where
  *   n_slots = max_vis (no pool) or max_cand_blocks*block.
  * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_WORKSPACE.
