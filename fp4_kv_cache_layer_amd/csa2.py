@@ -54,6 +54,9 @@ def lib() -> ctypes.CDLL:
         "csa2_quantize_kv": ([vp, i32, i64, i32, i32, vp, i64, vp, vp, vp], i32),
         "csa2_index_score": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64, vp],
                              i32),
+        "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp,
+                             sz, vp], i32),
+        "csa2_index_topk_workspace_bytes": ([i32, i64, i32], sz),
         "csa2_topk": ([vp, i64, i32, vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_topk_workspace_bytes": ([i32, i64, i32], sz),
         "csa2_build_pool": ([vp, i64, i32, vp, i64, i32, i32, vp, vp, vp, sz, vp], i32),
@@ -144,11 +147,9 @@ def csa2_quantize_kv(src, fmt: int, codes, scales=None, dst_row=None, _bind: boo
                                      _p(scales) if fmt != FMT_FP8 else None, _stream()), _bind)
 
 
-def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
-                     cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
-    """q_codes [n_q, H_I, 64], q_scales [n_q, H_I, 4], w [n_q, H_I] f32;
-    k_codes [n_seq, seq_cap, 64], k_scales [n_seq, seq_cap, 4]; q_seq [n_q] int32,
-    n_vis [n_q] int64; scores [n_q, stride] f32; cand_blocks [n_q, max_blocks] int32."""
+def _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block):
+    """Checks the indexer operands shared by csa2_index_score and csa2_index_topk and returns
+    the C arguments from q_codes to max_cand_blocks, and n_slots."""
     _need(q_codes, torch.uint8, 3, "q_codes")
     _need(q_scales, torch.uint8, 3, "q_scales")
     _need(w, torch.float32, 2, "w")
@@ -156,23 +157,56 @@ def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scor
     _need(k_scales, torch.uint8, 3, "k_scales")
     _need(q_seq, torch.int32, 1, "q_seq")
     _need(n_vis, torch.int64, 1, "n_vis")
-    _need(scores, torch.float32, 2, "scores")
     n_q, h, half = q_codes.shape
     n_seq, seq_cap, kh = k_codes.shape
     if q_scales.shape != (n_q, h, half // 16) or w.shape != (n_q, h) or kh != half or \
-            k_scales.shape != (n_seq, seq_cap, half // 16) or q_seq.shape[0] != n_q or n_vis.shape[0] != n_q or \
-            scores.shape[0] != n_q:
-        raise ValueError("index_score: inconsistent shapes")
+            k_scales.shape != (n_seq, seq_cap, half // 16) or q_seq.shape[0] != n_q or n_vis.shape[0] != n_q:
+        raise ValueError("index: inconsistent shapes")
     max_blocks = 0
     if cand_blocks is not None:
         _need(cand_blocks, torch.int32, 2, "cand_blocks")
         _need(n_cand_blocks, torch.int32, 1, "n_cand_blocks")
         max_blocks = cand_blocks.shape[1]
         if cand_blocks.shape[0] != n_q or n_cand_blocks.shape[0] != n_q:
-            raise ValueError("index_score: inconsistent pool shapes")
-    return _run("csa2_index_score", (_p(q_codes), _p(q_scales), _p(w), n_q, h, 2 * half, _p(k_codes), _p(k_scales),
-                                     seq_cap, n_seq, _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks),
-                                     block, max_blocks, _p(scores), scores.stride(0), _stream()), _bind)
+            raise ValueError("index: inconsistent pool shapes")
+    n_slots = max_blocks * block if cand_blocks is not None else seq_cap
+    return (_p(q_codes), _p(q_scales), _p(w), n_q, h, 2 * half, _p(k_codes), _p(k_scales), seq_cap, n_seq,
+            _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks), block, max_blocks), n_slots
+
+
+def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
+                     cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
+    """q_codes [n_q, H_I, 64], q_scales [n_q, H_I, 4], w [n_q, H_I] f32;
+    k_codes [n_seq, seq_cap, 64], k_scales [n_seq, seq_cap, 4]; q_seq [n_q] int32,
+    n_vis [n_q] int64; scores [n_q, stride] f32; cand_blocks [n_q, max_blocks] int32."""
+    args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block)
+    _need(scores, torch.float32, 2, "scores")
+    if scores.shape[0] != q_codes.shape[0]:
+        raise ValueError("index_score: scores rows != n_q")
+    return _run("csa2_index_score", args + (_p(scores), scores.stride(0), _stream()), _bind)
+
+
+def csa2_index_topk_workspace_bytes(n_q: int, n_slots: int, k: int) -> int:
+    return int(lib().csa2_index_topk_workspace_bytes(n_q, n_slots, k))
+
+
+def csa2_index_topk(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, idx_out, count_out,
+                    workspace=None, cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
+    """Scores and Top-K in one pass: the operands of csa2_index_score (without scores) ->
+    idx_out [n_q, k] int32, count_out [n_q] int32, as csa2_topk returns them."""
+    args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks,
+                                block)
+    _need(idx_out, torch.int32, 2, "idx_out")
+    _need(count_out, torch.int32, 1, "count_out")
+    n_q = q_codes.shape[0]
+    if idx_out.shape != (n_q, k) or count_out.shape[0] != n_q:
+        raise ValueError("index_topk: inconsistent output shapes")
+    need = csa2_index_topk_workspace_bytes(n_q, max(n_slots, 1), k)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_codes.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    return _run("csa2_index_topk", args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, _stream()),
+                _bind)
 
 
 def csa2_topk_workspace_bytes(n_q: int, n_slots: int, k: int) -> int:

@@ -1,5 +1,5 @@
-// csa2_index_score: FP4 indexer scores, one query per stream over its sequence's
-// indexer-K cache ([W] "CSA2：跨层复用，能借就不自己算", "分层稀疏索引器",
+// csa2_index_score / csa2_index_topk: FP4 indexer scores, one query per stream over its
+// sequence's indexer-K cache ([W] "CSA2：跨层复用，能借就不自己算", "分层稀疏索引器",
 // "FP4 与 SWA Bounded Replay").
 //
 //   score(q, j) = sum_h w[q,h] * max(0, Q[q,h,:] . K[j,:])     (MXFP4 Q and K, d = 128)
@@ -11,98 +11,139 @@
 // its E8M0 scale map one-to-one onto what one lane feeds the instruction, so the FP4
 // products and their scaling happen inside the matrix core, exactly.  A lane loads one
 // 16-byte chunk per entry (lane l: entry l%16, K-block l/16), so a wave's four loads
-// cover 16 entries x 64 B = 1 KB contiguously.  The output rows are the heads; each lane
-// weights and ReLUs its 4 heads, and a 3-shuffle reduce-scatter over the 4 lane groups
-// leaves lane l with the score of entry l of the 64-entry step, stored coalesced.
+// cover 16 entries x 64 B = 1 KB contiguously; the code loads are non-temporal (the cache
+// is streamed once) and branch-free, and the next 64-entry step is in flight while the
+// current one is multiplied.  The output rows are the heads; each lane weights and ReLUs
+// its 4 heads, and a 3-shuffle reduce-scatter over the 4 lane groups leaves lane l with
+// the score of entry l of the 64-entry step.
 //
 // Per entry the work is 2*16*128 = 4096 FLOP on 68 B: ~60 FLOP/B, which fp32 vector ALUs
 // cannot sustain at HBM speed (~480 TFLOP/s needed at 8 TB/s), but which is ~5% of the
-// FP4 matrix-core rate.  The kernel is HBM-bound by design.
-#include "device.h"
+// FP4 matrix-core rate.  The kernels are HBM-bound by design.
+//
+// csa2_index_topk fuses the first Top-K level into the scoring pass (the selection is in
+// select.h): a workgroup scores 8,192 consecutive slots, keeps its 32 scores per lane in
+// registers as selection keys and writes only its K survivors.  Writing every 4-byte
+// score and reading it back would add 8 B of HBM traffic per entry, and interleaving the
+// score writes with the streaming reads slows the scoring pass down by about a fifth.
+#include "select.h"
 
 namespace csa2 {
 
 constexpr int kScoreThreads = 256;   // 4 waves
 constexpr int kScoreStep = 64;       // entries per wave step (4 MFMA tiles)
-constexpr int kScoreChunk = 4096;    // entries per workgroup
+constexpr int kScoreChunk = 4096;    // entries per workgroup (csa2_index_score)
+static_assert(kScoreThreads == kTkThreads, "the fused kernel hands its registers to select_segment");
 
+struct ScoreArgs {
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  const float* w;
+  int n_heads;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  int64_t seq_cap;
+  int n_seq;
+  const int32_t* q_seq;
+  const int64_t* n_vis;
+  const int32_t* cand_blocks;
+  const int32_t* n_cand_blocks;
+  int block;
+  int max_cand_blocks;
+  int64_t n_slots;
+  // csa2_index_score
+  float* scores;
+  int64_t scores_stride;
+  int chunks;
+  // csa2_index_topk
+  int k;
+  uint64_t* keys_out;
+  int32_t* idx_out;
+  int32_t* count_out;
+};
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// One query's view of the cache: MFMA operands, slot -> row mapping, one scoring step.
 template <bool kPool>
-__global__ __launch_bounds__(kScoreThreads) void k_score_decode(
-    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, const float* __restrict__ w,
-    int n_heads, const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, int64_t seq_cap,
-    int n_seq, const int32_t* __restrict__ q_seq, const int64_t* __restrict__ n_vis,
-    const int32_t* __restrict__ cand_blocks, const int32_t* __restrict__ n_cand_blocks, int block,
-    int max_cand_blocks, float* __restrict__ scores, int64_t scores_stride, int64_t n_slots, int chunks) {
-  const int q = blockIdx.x / chunks;
-  const int chunk = blockIdx.x % chunks;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int row = lane & 15;   // A row (head) / B column (entry within tile)
-  const int kb = lane >> 4;    // K-block of 32 elements
+struct QueryScorer {
+  v8i a;             // A operand: indexer Q rows (heads), 32 FP4 values per lane
+  int a_scale;
+  float wv[4];       // weights of the 4 output rows (heads 4*kb .. 4*kb+3) of this lane
+  int64_t nv;        // visible entries, clamped to the cache
+  int64_t n_valid;   // slots that may hold a real candidate
+  int64_t seq_base;
+  const int32_t* cb;
+  int row, kb;       // A row (head) / B column (entry within tile); K-block of 32
 
-  const int seq = q_seq[q];
-  if (seq < 0 || seq >= n_seq) return;
-  int64_t nv = n_vis[q];
-  nv = nv < 0 ? 0 : (nv > seq_cap ? seq_cap : nv);
-  int64_t n_valid;  // slots that may hold a real candidate
-  if (kPool) {
-    int64_t nc = n_cand_blocks[q];
-    nc = nc < 0 ? 0 : (nc > max_cand_blocks ? max_cand_blocks : nc);
-    n_valid = nc * block;
-  } else {
-    n_valid = nv;
-  }
-  const int64_t chunk_lo = (int64_t)chunk * kScoreChunk;
-  const int64_t write_hi = kPool ? n_slots : n_valid;  // pool mode also writes -inf pads
-  if (chunk_lo >= write_hi) return;
-
-  // ---- A operand: the query's indexer Q, row = head, 32 FP4 values per lane ----
-  v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
-  int a_scale = 127;
-  if (row < n_heads) {
-    const uint4 qa = *reinterpret_cast<const uint4*>(q_codes + ((int64_t)q * n_heads + row) * 64 + kb * 16);
-    a[0] = (int)qa.x; a[1] = (int)qa.y; a[2] = (int)qa.z; a[3] = (int)qa.w;
-    a_scale = q_scales[((int64_t)q * n_heads + row) * 4 + kb];
-  }
-  // weights of the 4 output rows (heads 4*kb .. 4*kb+3) this lane accumulates
-  float wv[4];
+  __device__ __forceinline__ bool init(const ScoreArgs& s, int q) {
+    const int lane = threadIdx.x & 63;
+    row = lane & 15;
+    kb = lane >> 4;
+    const int seq = s.q_seq[q];
+    if (seq < 0 || seq >= s.n_seq) return false;
+    nv = s.n_vis[q];
+    nv = nv < 0 ? 0 : (nv > s.seq_cap ? s.seq_cap : nv);
+    if (kPool) {
+      int64_t nc = s.n_cand_blocks[q];
+      nc = nc < 0 ? 0 : (nc > s.max_cand_blocks ? s.max_cand_blocks : nc);
+      n_valid = nc * s.block;
+      cb = s.cand_blocks + (int64_t)q * s.max_cand_blocks;
+    } else {
+      n_valid = nv;
+      cb = nullptr;
+    }
+    seq_base = (int64_t)seq * s.seq_cap;
+    a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    a_scale = 127;
+    if (row < s.n_heads) {
+      const int64_t r = (int64_t)q * s.n_heads + row;
+      const uint4 qa = *reinterpret_cast<const uint4*>(s.q_codes + r * 64 + kb * 16);
+      a[0] = (int)qa.x;
+      a[1] = (int)qa.y;
+      a[2] = (int)qa.z;
+      a[3] = (int)qa.w;
+      a_scale = s.q_scales[r * 4 + kb];
+    }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    int h = 4 * kb + r;
-    wv[r] = h < n_heads ? w[(int64_t)q * n_heads + h] : 0.0f;
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * kb + r;
+      wv[r] = h < s.n_heads ? s.w[(int64_t)q * s.n_heads + h] : 0.0f;
+    }
+    return true;
   }
 
-  const int64_t seq_base = (int64_t)seq * seq_cap;
-  const int32_t* cb = kPool ? cand_blocks + (int64_t)q * max_cand_blocks : nullptr;
-  float* out = scores + (int64_t)q * scores_stride;
+  // slot -> (row to read, valid); invalid slots read row 0 and their results are discarded,
+  // so the loads need no per-lane branches
+  __device__ __forceinline__ bool slot_pos(const ScoreArgs& s, int64_t slot, int64_t& pos) const {
+    bool valid = slot < n_valid;
+    pos = slot;
+    if (kPool && valid) {
+      const int32_t b = cb[slot / s.block];
+      pos = (int64_t)b * s.block + slot % s.block;
+      valid = b >= 0 && pos < nv;
+    }
+    if (!valid) pos = 0;
+    return valid;
+  }
 
-  int64_t hi = chunk_lo + kScoreChunk;
-  hi = hi < write_hi ? hi : write_hi;
-  for (int64_t base = chunk_lo + wave * kScoreStep; base < hi; base += 4 * kScoreStep) {
-    uint4 bc[4];
-    int bs[4];
+  __device__ __forceinline__ void load_step(const ScoreArgs& s, int64_t base, uint4 (&bc)[4], int (&bs)[4]) const {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      int64_t slot = base + 16 * t + row;
-      int64_t pos = slot;
-      bool valid = slot < n_valid;
-      if (kPool && valid) {
-        int32_t b = cb[slot / block];
-        pos = (int64_t)b * block + slot % block;
-        valid = b >= 0 && pos < nv;
-      }
-      if (valid) {
-        bc[t] = *reinterpret_cast<const uint4*>(k_codes + (seq_base + pos) * 64 + kb * 16);
-        bs[t] = k_scales[(seq_base + pos) * 4 + kb];
-      } else {
-        bc[t] = make_uint4(0u, 0u, 0u, 0u);
-        bs[t] = 127;
-      }
+      int64_t pos;
+      slot_pos(s, base + 16 * t + row, pos);
+      const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(s.k_codes + (seq_base + pos) * 64 + kb * 16));
+      bc[t] = make_uint4(v.x, v.y, v.z, v.w);
+      bs[t] = s.k_scales[(seq_base + pos) * 4 + kb];
     }
+  }
+
+  // scores of the 64 entries of one step; lane l returns the score of entry l
+  __device__ __forceinline__ float score_step(const uint4 (&bc)[4], const int (&bs)[4]) const {
     float part[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      v8i b = {(int)bc[t].x, (int)bc[t].y, (int)bc[t].z, (int)bc[t].w, 0, 0, 0, 0};
+      const v8i b = {(int)bc[t].x, (int)bc[t].y, (int)bc[t].z, (int)bc[t].w, 0, 0, 0, 0};
       v4f acc = {0.f, 0.f, 0.f, 0.f};
       // formats 4/4 = E2M1 for both operands; scales are E8M0, byte 0 of each lane's VGPR
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 4, 0, a_scale, 0, bs[t]);
@@ -113,32 +154,143 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_decode(
     }
     // reduce-scatter over the 4 lane groups: lane group g ends with tile g's full sum
     const bool b1 = (kb & 2) != 0, b0 = (kb & 1) != 0;
-    float s0 = b1 ? part[0] : part[2];
-    float s1 = b1 ? part[1] : part[3];
-    float r0 = __shfl_xor(s0, 32);
-    float r1 = __shfl_xor(s1, 32);
-    float k0 = (b1 ? part[2] : part[0]) + r0;
-    float k1 = (b1 ? part[3] : part[1]) + r1;
-    float send = b0 ? k0 : k1;
-    float recv = __shfl_xor(send, 16);
-    float sc = (b0 ? k1 : k0) + recv;
-    // lane l now holds entry base + l (tile kb, column row)
-    int64_t slot = base + lane;
+    const float s0 = b1 ? part[0] : part[2];
+    const float s1 = b1 ? part[1] : part[3];
+    const float r0 = __shfl_xor(s0, 32);
+    const float r1 = __shfl_xor(s1, 32);
+    const float k0 = (b1 ? part[2] : part[0]) + r0;
+    const float k1 = (b1 ? part[3] : part[1]) + r1;
+    const float send = b0 ? k0 : k1;
+    const float recv = __shfl_xor(send, 16);
+    return (b0 ? k1 : k0) + recv;
+  }
+};
+
+template <bool kPool>
+__global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
+  const int q = blockIdx.x / s.chunks;
+  const int chunk = blockIdx.x % s.chunks;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  QueryScorer<kPool> sc;
+  if (!sc.init(s, q)) return;
+  const int64_t chunk_lo = (int64_t)chunk * kScoreChunk;
+  const int64_t write_hi = kPool ? s.n_slots : sc.n_valid;  // pool mode also writes -inf pads
+  if (chunk_lo >= write_hi) return;
+  float* out = s.scores + (int64_t)q * s.scores_stride;
+  int64_t hi = chunk_lo + kScoreChunk;
+  hi = hi < write_hi ? hi : write_hi;
+
+  int64_t base = chunk_lo + wave * kScoreStep;
+  if (sc.nv <= 0) {  // nothing to read: pool slots are all -inf, no-pool chunks never get here
+    for (; base < hi; base += 4 * kScoreStep)
+      if (base + lane < hi) out[base + lane] = -__builtin_inff();
+    return;
+  }
+  uint4 bc[4];
+  int bs[4];
+  if (base < hi) sc.load_step(s, base, bc, bs);
+  for (; base < hi; base += 4 * kScoreStep) {
+    // prefetch the next step while this one is computed; past the end, re-read this step
+    // (an L2 hit) so that the load stays unconditional
+    uint4 bcn[4];
+    int bsn[4];
+    const int64_t next = base + 4 * kScoreStep;
+    sc.load_step(s, next < hi ? next : base, bcn, bsn);
+    const float v = sc.score_step(bc, bs);
+    const int64_t slot = base + lane;
     if (slot < hi) {
-      bool v;
-      if (kPool) {
-        v = slot < n_valid;
-        if (v) {
-          int32_t b = cb[slot / block];
-          int64_t pos = (int64_t)b * block + slot % block;
-          v = b >= 0 && pos < nv;
-        }
-        out[slot] = v ? sc : -__builtin_inff();
-      } else {
-        out[slot] = sc;  // slot < hi <= n_valid
+      int64_t pos;
+      const bool valid = sc.slot_pos(s, slot, pos);
+      out[slot] = (kPool && !valid) ? -__builtin_inff() : v;   // without a pool, slot < hi <= n_valid
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bc[t] = bcn[t];
+      bs[t] = bsn[t];
+    }
+  }
+}
+
+// Scores one segment of kTkSeg slots and selects its K best in the same workgroup.  Step i
+// of wave w covers slots i*256 + w*64 + lane of the segment, so thread t's key[i] is
+// candidate i*256 + t: the candidate order select_segment expects.
+template <bool kPool, bool kFinal>
+__global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
+  const int seg = blockIdx.x;
+  const int q = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint64_t key[kTkEpt];
+#pragma unroll
+  for (int i = 0; i < kTkEpt; ++i) key[i] = 0ull;
+  QueryScorer<kPool> sc;
+  const int64_t c0 = (int64_t)seg * kTkSeg;
+  // workgroup-uniform condition: every thread reaches select_segment's barriers
+  if (sc.init(s, q) && sc.nv > 0 && c0 < sc.n_valid) {
+    uint4 bc[4];
+    int bs[4];
+    sc.load_step(s, c0 + wave * kScoreStep, bc, bs);
+#pragma unroll
+    for (int i = 0; i < kTkEpt; ++i) {
+      const int64_t base = c0 + (int64_t)i * kTkThreads + wave * kScoreStep;
+      uint4 bcn[4];
+      int bsn[4];
+      // the last step re-reads itself so that the prefetch stays unconditional
+      sc.load_step(s, i + 1 < kTkEpt ? base + kTkThreads : base, bcn, bsn);
+      const float v = sc.score_step(bc, bs);
+      int64_t pos;
+      const bool valid = sc.slot_pos(s, base + lane, pos);
+      key[i] = valid ? make_key(v, (uint32_t)pos) : 0ull;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bc[t] = bcn[t];
+        bs[t] = bsn[t];
       }
     }
   }
+  select_segment<kFinal>(key, q, seg, gridDim.x, s.k, s.keys_out, s.idx_out, s.count_out);
+}
+
+static int check_score_args(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q, int n_heads,
+                            int dim, const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
+                            const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
+                            const int32_t* n_cand_blocks, int block, int max_cand_blocks, int64_t* n_slots) {
+  if (!q_codes || !q_scales || !w || !k_codes || !k_scales || !q_seq || !n_vis) return CSA2_ERR_NULL;
+  if (n_q < 0 || n_heads < 1 || n_heads > CSA2_MAX_INDEX_HEADS || dim != CSA2_INDEX_DIM || seq_cap < 0 || n_seq < 1)
+    return CSA2_ERR_SHAPE;
+  if (!aligned16(q_codes) || !aligned16(k_codes)) return CSA2_ERR_SHAPE;
+  if (cand_blocks) {
+    if (!n_cand_blocks) return CSA2_ERR_NULL;
+    if (block < 1 || block > 64 || max_cand_blocks < 1 || max_cand_blocks > (1 << 20)) return CSA2_ERR_SHAPE;
+    *n_slots = (int64_t)max_cand_blocks * block;
+  } else {
+    *n_slots = seq_cap;
+  }
+  return CSA2_OK;
+}
+
+static ScoreArgs make_args(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_heads,
+                           const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
+                           const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
+                           const int32_t* n_cand_blocks, int block, int max_cand_blocks, int64_t n_slots) {
+  ScoreArgs a = {};
+  a.q_codes = q_codes;
+  a.q_scales = q_scales;
+  a.w = w;
+  a.n_heads = n_heads;
+  a.k_codes = k_codes;
+  a.k_scales = k_scales;
+  a.seq_cap = seq_cap;
+  a.n_seq = n_seq;
+  a.q_seq = q_seq;
+  a.n_vis = n_vis;
+  a.cand_blocks = cand_blocks;
+  a.n_cand_blocks = n_cand_blocks;
+  a.block = block;
+  a.max_cand_blocks = max_cand_blocks;
+  a.n_slots = n_slots;
+  return a;
 }
 
 }  // namespace csa2
@@ -150,33 +302,75 @@ extern "C" int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales,
                                 int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
                                 const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
                                 int max_cand_blocks, float* scores, int64_t scores_stride, void* stream) {
-  if (!q_codes || !q_scales || !w || !k_codes || !k_scales || !q_seq || !n_vis || !scores) return CSA2_ERR_NULL;
-  if (n_q < 0 || n_heads < 1 || n_heads > CSA2_MAX_INDEX_HEADS || dim != CSA2_INDEX_DIM || seq_cap < 0 ||
-      n_seq < 1)
-    return CSA2_ERR_SHAPE;
-  if (!aligned16(q_codes) || !aligned16(k_codes)) return CSA2_ERR_SHAPE;
-  const bool pool = cand_blocks != nullptr;
-  int64_t n_slots;
-  if (pool) {
-    if (!n_cand_blocks) return CSA2_ERR_NULL;
-    if (block < 1 || block > 64 || max_cand_blocks < 1 || max_cand_blocks > (1 << 20)) return CSA2_ERR_SHAPE;
-    n_slots = (int64_t)max_cand_blocks * block;
-  } else {
-    n_slots = seq_cap;
-  }
+  int64_t n_slots = 0;
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                            cand_blocks, n_cand_blocks, block, max_cand_blocks, &n_slots);
+  if (rc != CSA2_OK) return rc;
+  if (!scores) return CSA2_ERR_NULL;
   if (scores_stride < n_slots) return CSA2_ERR_SHAPE;
   if (n_q == 0 || n_slots == 0) return CSA2_OK;
-  int64_t chunks = (n_slots + kScoreChunk - 1) / kScoreChunk;
+  const int64_t chunks = (n_slots + kScoreChunk - 1) / kScoreChunk;
   if (chunks * (int64_t)n_q > 0x7fffffffLL) return CSA2_ERR_SHAPE;
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
+                          n_cand_blocks, block, max_cand_blocks, n_slots);
+  a.scores = scores;
+  a.scores_stride = scores_stride;
+  a.chunks = (int)chunks;
   dim3 grid((unsigned)(chunks * n_q)), blk(kScoreThreads);
   hipStream_t st = (hipStream_t)stream;
-  if (pool)
-    hipLaunchKernelGGL(k_score_decode<true>, grid, blk, 0, st, q_codes, q_scales, w, n_heads, k_codes, k_scales,
-                       seq_cap, n_seq, q_seq, n_vis, cand_blocks, n_cand_blocks, block, max_cand_blocks, scores,
-                       scores_stride, n_slots, (int)chunks);
-  else
-    hipLaunchKernelGGL(k_score_decode<false>, grid, blk, 0, st, q_codes, q_scales, w, n_heads, k_codes, k_scales,
-                       seq_cap, n_seq, q_seq, n_vis, cand_blocks, n_cand_blocks, block, max_cand_blocks, scores,
-                       scores_stride, n_slots, (int)chunks);
+  if (cand_blocks) hipLaunchKernelGGL(k_score_decode<true>, grid, blk, 0, st, a);
+  else hipLaunchKernelGGL(k_score_decode<false>, grid, blk, 0, st, a);
   return csa2_check_launch();
+}
+
+extern "C" size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k) {
+  if (n_q <= 0 || n_slots <= 0 || k < 1 || k > CSA2_MAX_TOPK) return 0;
+  return ws_bytes(n_q, n_slots, k);
+}
+
+extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                               int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                               int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                               const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                               int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  int64_t n_slots = 0;
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                            cand_blocks, n_cand_blocks, block, max_cand_blocks, &n_slots);
+  if (rc != CSA2_OK) return rc;
+  if (!idx_out || !count_out) return CSA2_ERR_NULL;
+  if (n_q > 65535 || k < 1 || k > CSA2_MAX_TOPK || n_slots > 0x7fffffffLL) return CSA2_ERR_SHAPE;
+  if (n_q == 0) return CSA2_OK;
+  const int64_t n0 = n_slots < 1 ? 1 : n_slots;
+  int64_t segs[16];
+  const int L = plan_levels(n0, k, segs, 16);
+  if (L >= 16) return CSA2_ERR_SHAPE;
+  const size_t need = ws_bytes(n_q, n0, k);
+  if (need > workspace_bytes || (need && !workspace)) return CSA2_ERR_WORKSPACE;
+  uint64_t* bufA = (uint64_t*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  uint64_t* bufB = bufA + (size_t)k * n_q * segs[0];
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
+                          n_cand_blocks, block, max_cand_blocks, n_slots);
+  a.k = k;
+  a.keys_out = bufA;
+  a.idx_out = idx_out;
+  a.count_out = count_out;
+  hipStream_t st = (hipStream_t)stream;
+  dim3 grid((unsigned)segs[0], (unsigned)n_q), blk(kScoreThreads);
+  if (cand_blocks) {
+    if (L == 1) hipLaunchKernelGGL((k_score_select<true, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_score_select<true, false>), grid, blk, 0, st, a);
+  } else {
+    if (L == 1) hipLaunchKernelGGL((k_score_select<false, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_score_select<false, false>), grid, blk, 0, st, a);
+  }
+  rc = csa2_check_launch();
+  if (rc != CSA2_OK) return rc;
+  TkArgs t = {};
+  t.n_vis = n_vis;
+  t.max_vis = seq_cap;
+  t.k = k;
+  t.idx_out = idx_out;
+  t.count_out = count_out;
+  return select_levels_after0(segs, L, t, n_q, bufA, bufB, st);
 }

@@ -1,0 +1,241 @@
+// Segment-level exact Top-K selection shared by the Top-K / pool kernels and the fused
+// scoring kernel (see topk.hip for the method).
+#pragma once
+
+#include "device.h"
+
+namespace csa2 {
+
+
+constexpr int kTkThreads = 256;
+constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kTkEpt = 32;
+constexpr int kTkSeg = kTkThreads * kTkEpt;
+
+enum TkMode { kFromScores = 0, kFromBlockMax = 1, kFromKeys = 2 };
+
+struct TkArgs {
+  const float* scores;
+  int64_t scores_stride;
+  const int64_t* n_vis;
+  int64_t max_vis;
+  const int32_t* cand_blocks;    // pool slot map (kFromScores) or nullptr
+  const int32_t* n_cand_blocks;
+  int block;
+  int max_cand_blocks;
+  const uint64_t* keys_in;       // kFromKeys: [n_q, keys_in_per_q]
+  int64_t keys_in_per_q;
+  uint64_t* keys_out;            // non-final: [n_q, gridDim.x, k]
+  int32_t* idx_out;              // final: [n_q, k]
+  int32_t* count_out;            // final: [n_q]
+  int k;
+  int64_t n_slots;               // candidate slots per query at this level
+};
+
+__device__ __forceinline__ uint32_t ord_f32(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t make_key(float s, uint32_t pos) {
+  return ((uint64_t)ord_f32(s) << 32) | (uint64_t)(0xffffffffu - pos);
+}
+__device__ __forceinline__ int32_t key_pos(uint64_t k) { return (int32_t)(0xffffffffu - (uint32_t)k); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// wave-wide inclusive suffix sum (lane l gets the sum over lanes >= l)
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v, int lane) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const uint32_t o = __shfl_down(v, m);
+    v += (lane + m < 64) ? o : 0u;
+  }
+  return v;
+}
+
+// Selects the K largest of the 32*256 keys held by a 256-thread workgroup (key[i] of thread
+// t is candidate i*256 + t of the segment; 0 = no candidate) and writes them in candidate
+// order: non-final levels write the keys to keys_out[(q*n_seg + seg)*K ..], zero padded;
+// the final level writes positions to idx_out[q*K ..], -1 padded, and count_out[q].
+template <bool kFinal>
+__device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, int seg, int n_seg, int K,
+                                               uint64_t* __restrict__ keys_out, int32_t* __restrict__ idx_out,
+                                               int32_t* __restrict__ count_out) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  __shared__ uint32_t hist[2][kTkWaves][256];
+  __shared__ uint32_t cnt[kTkWaves][kTkEpt];
+  __shared__ uint64_t red_hi[kTkWaves], red_lo[kTkWaves];
+  __shared__ uint32_t red_n[kTkWaves];
+
+  // ---- count, max and min of the valid keys ----
+  uint32_t n = 0;
+  uint64_t kmax = 0, kmin = ~0ull;
+#pragma unroll
+  for (int i = 0; i < kTkEpt; ++i) {
+    if (key[i]) {
+      ++n;
+      kmax = key[i] > kmax ? key[i] : kmax;
+      kmin = key[i] < kmin ? key[i] : kmin;
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    n += __shfl_xor(n, m);
+    uint64_t o = shfl_xor_u64(kmax, m);
+    kmax = o > kmax ? o : kmax;
+    o = shfl_xor_u64(kmin, m);
+    kmin = o < kmin ? o : kmin;
+  }
+  if (lane == 0) {
+    red_n[wave] = n;
+    red_hi[wave] = kmax;
+    red_lo[wave] = kmin;
+  }
+  __syncthreads();
+  n = 0;
+  kmax = 0;
+  kmin = ~0ull;
+#pragma unroll
+  for (int wv = 0; wv < kTkWaves; ++wv) {
+    n += red_n[wv];
+    kmax = red_hi[wv] > kmax ? red_hi[wv] : kmax;
+    kmin = red_lo[wv] < kmin ? red_lo[wv] : kmin;
+  }
+
+  // ---- radix select: find (prefix, mask) such that exactly K keys have (key&mask) >= prefix ----
+  uint64_t prefix = 0, mask = 0;
+  if (n > (uint32_t)K) {
+    const int hb = 63 - __clzll(kmax ^ kmin);  // n >= 2 unique keys -> kmax != kmin
+    mask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+    prefix = kmax & mask;
+    int shift = hb - 7 > 0 ? hb - 7 : 0;
+    uint32_t need = (uint32_t)K;
+    for (int pass = 0;; ++pass) {
+      uint32_t* h = hist[pass & 1][wave];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[lane + 64 * i] = 0;
+#pragma unroll
+      for (int i = 0; i < kTkEpt; ++i)
+        if (key[i] && (key[i] & mask) == prefix) atomicAdd(&h[(uint32_t)(key[i] >> shift) & 255u], 1u);
+      __syncthreads();
+      // every wave: lane l owns bins 4l..4l+3 of the summed histogram
+      uint32_t hs[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int wv = 0; wv < kTkWaves; ++wv) v += hist[pass & 1][wv][4 * lane + j];
+        hs[j] = v;
+      }
+      const uint32_t tot = hs[0] + hs[1] + hs[2] + hs[3];
+      const uint32_t incl = wave_suffix_sum(tot, lane);
+      const uint32_t above_lane = incl - tot;
+      // the boundary digit is the largest d with (count of digits >= d) >= need
+      uint32_t d = 0, above = 0, inbin = 0;
+      const bool mine = above_lane < need && incl >= need;
+      if (mine) {
+        uint32_t acc = above_lane;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (acc + hs[j] >= need) {
+            d = 4 * lane + j;
+            above = acc;
+            inbin = hs[j];
+            break;
+          }
+          acc += hs[j];
+        }
+      }
+      const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
+      d = __builtin_amdgcn_readlane(d, owner);
+      above = __builtin_amdgcn_readlane(above, owner);
+      inbin = __builtin_amdgcn_readlane(inbin, owner);
+      need -= above;
+      prefix |= (uint64_t)d << shift;
+      mask |= 255ull << shift;
+      if (inbin == need || shift == 0) break;
+      shift = shift - 8 > 0 ? shift - 8 : 0;
+    }
+  }
+
+  // ---- stable compaction in candidate order (i-major, then thread) ----
+  // survivors of slot i in wave w: one ballot; cnt[w][i] = their number
+#pragma unroll
+  for (int i = 0; i < kTkEpt; ++i) {
+    const uint64_t m = __ballot(key[i] && (key[i] & mask) >= prefix);
+    if (lane == 0) cnt[wave][i] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  // lane i < 32: off = (survivors of slots < i, all waves) + (survivors of slot i, waves < w)
+  uint32_t tot_i = 0, before_w = 0;
+  if (lane < kTkEpt) {
+#pragma unroll
+    for (int wv = 0; wv < kTkWaves; ++wv) {
+      const uint32_t c = cnt[wv][lane];
+      tot_i += c;
+      before_w += wv < wave ? c : 0u;
+    }
+  }
+  uint32_t excl = tot_i;  // exclusive prefix over lanes 0..31
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    const uint32_t o = __shfl_up(excl, m);
+    excl += (lane >= m) ? o : 0u;
+  }
+  const uint32_t total = __builtin_amdgcn_readlane(excl, kTkEpt - 1);
+  const uint32_t off = excl - tot_i + before_w;
+  const uint32_t nsel = total < (uint32_t)K ? total : (uint32_t)K;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  if (!kFinal) {
+    uint64_t* out = keys_out + ((int64_t)q * n_seg + seg) * K;
+#pragma unroll
+    for (int i = 0; i < kTkEpt; ++i) {
+      const bool take = key[i] && (key[i] & mask) >= prefix;
+      const uint64_t m = __ballot(take);
+      const uint32_t slot = __builtin_amdgcn_readlane(off, i) + (uint32_t)__popcll(m & lt_mask);
+      if (take && slot < (uint32_t)K) out[slot] = key[i];
+    }
+    for (int i = (int)nsel + tid; i < K; i += kTkThreads) out[i] = 0ull;
+    return;
+  }
+  int32_t* out = idx_out + (int64_t)q * K;
+#pragma unroll
+  for (int i = 0; i < kTkEpt; ++i) {
+    const bool take = key[i] && (key[i] & mask) >= prefix;
+    const uint64_t m = __ballot(take);
+    const uint32_t slot = __builtin_amdgcn_readlane(off, i) + (uint32_t)__popcll(m & lt_mask);
+    if (take && slot < (uint32_t)K) out[slot] = key_pos(key[i]);
+  }
+  for (int i = (int)nsel + tid; i < K; i += kTkThreads) out[i] = -1;
+  if (tid == 0) count_out[q] = (int32_t)nsel;
+}
+
+// number of segments per level, level 0 first; the last entry is 1
+inline int plan_levels(int64_t n0, int k, int64_t* segs, int max_levels) {
+  int L = 0;
+  int64_t cur = (n0 + kTkSeg - 1) / kTkSeg;
+  if (cur < 1) cur = 1;
+  segs[L++] = cur;
+  while (cur > 1 && L < max_levels) {
+    cur = (cur * k + kTkSeg - 1) / kTkSeg;
+    segs[L++] = cur;
+  }
+  return L;
+}
+
+inline size_t ws_bytes(int n_q, int64_t n0, int k) {
+  int64_t segs[16];
+  int L = plan_levels(n0, k, segs, 16);
+  if (L == 1) return 0;
+  int64_t s1 = L > 2 ? segs[1] : 0;
+  return (size_t)8 * (size_t)k * (size_t)n_q * (size_t)(segs[0] + s1) + 256;
+}
+
+int select_levels_after0(const int64_t* segs, int L, TkArgs base, int n_q, uint64_t* bufA, uint64_t* bufB,
+                         hipStream_t st);
+
+}  // namespace csa2

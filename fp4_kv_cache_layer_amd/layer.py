@@ -53,8 +53,11 @@ class Csa2Step:
 
     def __init__(self, n_q: int, n_heads: int, idx_heads: int, seq_cap: int, k: int = 512, window: int = 128,
                  block: int = 8, max_blocks: int = 2048, idx_dim: int = 128, dim: int = 512,
-                 out_dtype=torch.float32, device="cuda"):
+                 out_dtype=torch.float32, fused: bool = True, device="cuda"):
+        """fused: score and select in one call (csa2_index_topk) wherever the layer does not
+        need the score array itself (it does only when it builds the pool)."""
         self.n_q, self.n_heads, self.idx_heads = n_q, n_heads, idx_heads
+        self.fused = fused
         self.seq_cap, self.k, self.window = seq_cap, k, window
         self.block, self.max_blocks, self.dim = block, max_blocks, dim
         dev = dict(device=device)
@@ -69,6 +72,8 @@ class Csa2Step:
         self.lse = torch.empty(n_q, n_heads, dtype=torch.float32, **dev)
         n_slots = max(seq_cap, max_blocks * block, 1)
         self.ws_topk = torch.empty(max(C.csa2_topk_workspace_bytes(n_q, n_slots, k), 1), dtype=torch.uint8, **dev)
+        self.ws_index_topk = torch.empty(max(C.csa2_index_topk_workspace_bytes(n_q, n_slots, k), 1),
+                                         dtype=torch.uint8, **dev)
         self.ws_pool = torch.empty(max(C.csa2_pool_workspace_bytes(n_q, max(seq_cap, 1), block, max_blocks), 1),
                                    dtype=torch.uint8, **dev)
         self.ws_attn = torch.empty(max(C.csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window), 1),
@@ -95,6 +100,18 @@ class Csa2Step:
                                self.pool, self.pool_count, self.block, _bind=bind)
         return C.csa2_topk(self.scores, n_vis, self.seq_cap, self.k, self.idx, self.count, self.ws_topk, _bind=bind)
 
+    def index_topk(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False):
+        """score + select in one pass, without the score array."""
+        pool = (self.pool, self.pool_count) if in_pool else (None, None)
+        return C.csa2_index_topk(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
+                                 self.k, self.idx, self.count, self.ws_index_topk, pool[0], pool[1], self.block,
+                                 _bind=bind)
+
+    def _score_select(self, caches, w, q_seq, n_vis, in_pool, bind):
+        if self.fused:
+            return [self.index_topk(caches, w, q_seq, n_vis, in_pool, bind)]
+        return [self.score(caches, w, q_seq, n_vis, in_pool, bind), self.select(n_vis, in_pool, bind)]
+
     def build_pool(self, n_vis, bind=False):
         return C.csa2_build_pool(self.scores, n_vis, self.seq_cap, self.pool, self.pool_count, self.block,
                                  self.ws_pool, _bind=bind)
@@ -113,17 +130,18 @@ class Csa2Step:
 
     def full(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, make_pool=False,
              out=None, lse=None, bind=False):
-        calls = [self.quantize_index_q(q_index_f32, bind), self.score(caches, w, q_seq, n_vis, bind=bind),
-                 self.select(n_vis, bind=bind)]
-        if make_pool:
-            calls.append(self.build_pool(n_vis, bind))
+        calls = [self.quantize_index_q(q_index_f32, bind)]
+        if make_pool:   # the pool ranks blocks by their max score: keep the score array
+            calls += [self.score(caches, w, q_seq, n_vis, bind=bind), self.select(n_vis, bind=bind),
+                      self.build_pool(n_vis, bind)]
+        else:
+            calls += self._score_select(caches, w, q_seq, n_vis, False, bind)
         calls.append(self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind))
         return self._seq(calls, bind)
 
     def reindex(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, in_pool=False,
                 out=None, lse=None, bind=False):
-        calls = [self.quantize_index_q(q_index_f32, bind), self.score(caches, w, q_seq, n_vis, in_pool, bind),
-                 self.select(n_vis, in_pool, bind),
+        calls = [self.quantize_index_q(q_index_f32, bind), *self._score_select(caches, w, q_seq, n_vis, in_pool, bind),
                  self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
         return self._seq(calls, bind)
 

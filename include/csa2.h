@@ -158,6 +158,29 @@ int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const floa
                      int max_cand_blocks, float* scores, int64_t scores_stride, void* stream);
 
 /*
+ * csa2_index_topk -- csa2_index_score followed by csa2_topk in one pass, without the score
+ * array.  [W] "CSA2：跨层复用，能借就不自己算" (indexer scores, then Top-K, K = 512),
+ * "分层稀疏索引器" (inside the pool).
+ *
+ * Arguments up to max_cand_blocks are those of csa2_index_score; k, idx_out and count_out
+ * are those of csa2_topk.  The result (idx_out, count_out) is identical to calling
+ * csa2_index_score and then csa2_topk with the same arguments: the same fp32 scores in
+ * the same ranking (score descending, position ascending).
+ *   k in 1..2048; n_q <= 65535.
+ *   Workspace: csa2_index_topk_workspace_bytes(n_q, n_slots, k) bytes, n_slots = seq_cap
+ *   (no pool) or max_cand_blocks*block.
+ * Errors: those of csa2_index_score (except the score array's), CSA2_ERR_NULL (idx_out,
+ * count_out), CSA2_ERR_SHAPE (k, n_q), CSA2_ERR_WORKSPACE.
+ */
+int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                    int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                    int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                    const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                    int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k);
+
+/*
  * csa2_topk -- the k highest-scoring candidates of each query.
  * [W] "CSA2：跨层复用，能借就不自己算" (Top-K, K = 512).
  *
@@ -222,8 +245,10 @@ size_t csa2_pool_workspace_bytes(int n_q, int64_t max_vis, int block, int max_bl
  *             window <= swa_cap
  *   out       [n_q, n_heads, dim] f32 or bf16 (out_dtype); lse [n_q, n_heads] f32 or NULL
  *   Workspace: csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window).
- * Arithmetic: Q.K on bf16 matrix cores with fp32 accumulation (K is exact in bf16);
- * softmax in fp32; P.V with P rounded to fp16 and V exact in fp16, fp32 accumulation.
+ * Arithmetic: Q.K and P.V on fp16 matrix cores with fp32 accumulation.  Every key/value
+ * (E2M1 x E4M3, or E4M3) is exact in fp16; Q is converted from bf16 to fp16, exact for
+ * |q| in [2^-14, 65504) (smaller magnitudes round to fp16 subnormals, larger ones
+ * overflow); softmax in fp32; P rounded to fp16.
  * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED (out_dtype),
  * CSA2_ERR_WORKSPACE.
  */

@@ -174,6 +174,81 @@ def test_index_score_pool_slots(C):
         assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max())
 
 
+def _run_index_topk(C, st, caches, w, q_seq, n_vis, k, in_pool=False):
+    """(fused idx, count), (two-call idx, count) on the same inputs."""
+    idx_f = torch.full((st.n_q, k), 77, dtype=torch.int32, device="cuda")
+    cnt_f = torch.full((st.n_q,), 77, dtype=torch.int32, device="cuda")
+    pool = (st.pool, st.pool_count) if in_pool else (None, None)
+    C.csa2_index_topk(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, k, idx_f, cnt_f,
+                      None, pool[0], pool[1], 8)
+    idx_u = torch.empty(st.n_q, k, dtype=torch.int32, device="cuda")
+    cnt_u = torch.empty(st.n_q, dtype=torch.int32, device="cuda")
+    st.score(caches, w, q_seq, n_vis, in_pool)
+    C.csa2_topk(st.scores, n_vis, st.seq_cap, k, idx_u, cnt_u, None, pool[0], pool[1], 8)
+    torch.cuda.synchronize()
+    return (idx_f.cpu().numpy(), cnt_f.cpu().numpy()), (idx_u.cpu().numpy(), cnt_u.cpu().numpy())
+
+
+@pytest.mark.parametrize("k", [512, 2048, 7])
+def test_index_topk_fused(C, k):
+    """Fused scoring + selection returns exactly what scoring then selecting returns (the same
+    fp32 scores, the same exact ranking), and that set passes the oracle's Top-K rule."""
+    _say("index_topk", k)
+    n_vis = [40000, 8193, 1, 0, 511, 20001, 16384]
+    case = _score_case(30 + k, 3, 40000, n_vis, 16)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq, n_vis_t, _, _ = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, k=k)
+    st.quantize_index_q(q_idx)
+    (gi, gc), (ui, uc) = _run_index_topk(C, st, caches, w, q_seq, n_vis_t, k)
+    assert np.array_equal(gc, uc) and np.array_equal(gi, ui)
+    for qi in (0, 1, 2, 3, 4):
+        nv = int(wl.n_vis[qi])
+        if nv == 0:
+            assert gc[qi] == 0 and np.all(gi[qi] == -1)
+            continue
+        seq = int(wl.q_seq[qi])
+        qc, qs, wq, _ = case.oracle_query(0, qi)
+        pos, ref = O.full_scores(qc, qs, wq, case.oracle_caches(seq), nv)
+        G.topk_accept(gi[qi], int(gc[qi]), pos, ref, k)
+
+
+def test_index_topk_fused_pool(C):
+    _say("index_topk pool")
+    case = _score_case(41, 2, 30000, [30000, 12000, 333], 16)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq, n_vis_t, _, _ = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    mb = 2048
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, max_blocks=mb)
+    rng = np.random.default_rng(9)
+    blocks = np.full((wl.n_q, mb), -1, np.int32)
+    ncb = np.array([2048, 1500, 45], np.int32)
+    for qi in range(wl.n_q):
+        nb = -(-int(wl.n_vis[qi]) // 8)
+        blocks[qi, :ncb[qi]] = np.sort(rng.choice(nb + 10, size=ncb[qi], replace=False))
+    blocks[0, 100] = -1
+    st.pool.copy_(torch.from_numpy(blocks))
+    st.pool_count.copy_(torch.from_numpy(ncb))
+    st.quantize_index_q(q_idx)
+    (gi, gc), (ui, uc) = _run_index_topk(C, st, caches, w, q_seq, n_vis_t, 512, in_pool=True)
+    assert np.array_equal(gc, uc) and np.array_equal(gi, ui)
+    for qi in range(wl.n_q):
+        nv = int(wl.n_vis[qi])
+        slots = np.arange(ncb[qi] * 8)
+        b = blocks[qi, slots // 8]
+        pos = b.astype(np.int64) * 8 + slots % 8
+        pos = pos[(b >= 0) & (pos < nv)]
+        qc, qs, wq, _ = case.oracle_query(0, qi)
+        _, ref = O.full_scores(qc, qs, wq, case.oracle_caches(int(wl.q_seq[qi])), nv, cand=pos)
+        G.topk_accept(gi[qi], int(gc[qi]), pos, ref, 512)
+
+
 @pytest.mark.parametrize("n,k", [(1, 512), (511, 512), (512, 512), (513, 512), (8192, 512), (8193, 512),
                                  (20000, 7), (70001, 512), (200000, 2048), (9000, 1), (300000, 512)])
 def test_topk_exact_on_same_scores(C, n, k):
