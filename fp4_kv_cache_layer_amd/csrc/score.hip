@@ -65,15 +65,20 @@ struct ScoreArgs {
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // One query's view of the cache: MFMA operands, slot -> row mapping, one scoring step.
+// Slots and rows are 32-bit (seq_cap <= 2^26, so byte offsets within a sequence fit in 32
+// bits) and the sequence's base pointers are workgroup-uniform, so each load is a scalar
+// base plus one 32-bit vector offset.
 template <bool kPool>
 struct QueryScorer {
   v8i a;             // A operand: indexer Q rows (heads), 32 FP4 values per lane
   int a_scale;
   float wv[4];       // weights of the 4 output rows (heads 4*kb .. 4*kb+3) of this lane
-  int64_t nv;        // visible entries, clamped to the cache
-  int64_t n_valid;   // slots that may hold a real candidate
-  int64_t seq_base;
+  int nv;            // visible entries, clamped to the cache
+  int n_valid;       // slots that may hold a real candidate
+  const uint8_t* kc; // this sequence's indexer-K codes / scales
+  const uint8_t* ks;
   const int32_t* cb;
+  int blk_lim;       // nv / block: no visible position lies in a block past this one
   int row, kb;       // A row (head) / B column (entry within tile); K-block of 32
 
   __device__ __forceinline__ bool init(const ScoreArgs& s, int q) {
@@ -82,18 +87,20 @@ struct QueryScorer {
     kb = lane >> 4;
     const int seq = s.q_seq[q];
     if (seq < 0 || seq >= s.n_seq) return false;
-    nv = s.n_vis[q];
-    nv = nv < 0 ? 0 : (nv > s.seq_cap ? s.seq_cap : nv);
+    int64_t v = s.n_vis[q];
+    nv = (int)(v < 0 ? 0 : (v > s.seq_cap ? s.seq_cap : v));
     if (kPool) {
       int64_t nc = s.n_cand_blocks[q];
       nc = nc < 0 ? 0 : (nc > s.max_cand_blocks ? s.max_cand_blocks : nc);
-      n_valid = nc * s.block;
+      n_valid = (int)nc * s.block;
       cb = s.cand_blocks + (int64_t)q * s.max_cand_blocks;
+      blk_lim = nv / s.block;
     } else {
       n_valid = nv;
       cb = nullptr;
     }
-    seq_base = (int64_t)seq * s.seq_cap;
+    kc = s.k_codes + (int64_t)seq * s.seq_cap * 64;
+    ks = s.k_scales + (int64_t)seq * s.seq_cap * 4;
     a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     a_scale = 127;
     if (row < s.n_heads) {
@@ -115,26 +122,27 @@ struct QueryScorer {
 
   // slot -> (row to read, valid); invalid slots read row 0 and their results are discarded,
   // so the loads need no per-lane branches
-  __device__ __forceinline__ bool slot_pos(const ScoreArgs& s, int64_t slot, int64_t& pos) const {
+  __device__ __forceinline__ bool slot_pos(const ScoreArgs& s, int slot, uint32_t& pos) const {
     bool valid = slot < n_valid;
-    pos = slot;
+    int p = slot;
     if (kPool && valid) {
-      const int32_t b = cb[slot / s.block];
-      pos = (int64_t)b * s.block + slot % s.block;
-      valid = b >= 0 && pos < nv;
+      const int32_t b = cb[(uint32_t)slot / (uint32_t)s.block];
+      valid = b >= 0 && b <= blk_lim;   // bounds b before b * block can overflow
+      p = b * s.block + (int)((uint32_t)slot % (uint32_t)s.block);
+      valid = valid && p < nv;
     }
-    if (!valid) pos = 0;
+    pos = valid ? (uint32_t)p : 0u;
     return valid;
   }
 
-  __device__ __forceinline__ void load_step(const ScoreArgs& s, int64_t base, uint4 (&bc)[4], int (&bs)[4]) const {
+  __device__ __forceinline__ void load_step(const ScoreArgs& s, int base, uint4 (&bc)[4], int (&bs)[4]) const {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      int64_t pos;
+      uint32_t pos;
       slot_pos(s, base + 16 * t + row, pos);
-      const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(s.k_codes + (seq_base + pos) * 64 + kb * 16));
+      const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(kc + (pos * 64u + kb * 16u)));
       bc[t] = make_uint4(v.x, v.y, v.z, v.w);
-      bs[t] = s.k_scales[(seq_base + pos) * 4 + kb];
+      bs[t] = ks[pos * 4u + kb];
     }
   }
 
@@ -174,14 +182,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
   const int wave = threadIdx.x >> 6;
   QueryScorer<kPool> sc;
   if (!sc.init(s, q)) return;
-  const int64_t chunk_lo = (int64_t)chunk * kScoreChunk;
-  const int64_t write_hi = kPool ? s.n_slots : sc.n_valid;  // pool mode also writes -inf pads
+  const int chunk_lo = chunk * kScoreChunk;
+  const int write_hi = kPool ? (int)s.n_slots : sc.n_valid;  // pool mode also writes -inf pads
   if (chunk_lo >= write_hi) return;
   float* out = s.scores + (int64_t)q * s.scores_stride;
-  int64_t hi = chunk_lo + kScoreChunk;
-  hi = hi < write_hi ? hi : write_hi;
+  const int hi = chunk_lo + kScoreChunk < write_hi ? chunk_lo + kScoreChunk : write_hi;
 
-  int64_t base = chunk_lo + wave * kScoreStep;
+  int base = chunk_lo + wave * kScoreStep;
   if (sc.nv <= 0) {  // nothing to read: pool slots are all -inf, no-pool chunks never get here
     for (; base < hi; base += 4 * kScoreStep)
       if (base + lane < hi) out[base + lane] = -__builtin_inff();
@@ -195,12 +202,12 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
     // (an L2 hit) so that the load stays unconditional
     uint4 bcn[4];
     int bsn[4];
-    const int64_t next = base + 4 * kScoreStep;
+    const int next = base + 4 * kScoreStep;
     sc.load_step(s, next < hi ? next : base, bcn, bsn);
     const float v = sc.score_step(bc, bs);
-    const int64_t slot = base + lane;
+    const int slot = base + lane;
     if (slot < hi) {
-      int64_t pos;
+      uint32_t pos;
       const bool valid = sc.slot_pos(s, slot, pos);
       out[slot] = (kPool && !valid) ? -__builtin_inff() : v;   // without a pool, slot < hi <= n_valid
     }
@@ -213,43 +220,55 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
 }
 
 // Scores one segment of kTkSeg slots and selects its K best in the same workgroup.  Step i
-// of wave w covers slots i*256 + w*64 + lane of the segment, so thread t's key[i] is
-// candidate i*256 + t: the candidate order select_segment expects.
+// of wave w covers slots i*256 + w*64 + lane of the segment, so thread t scores candidates
+// i*256 + t: the candidate order select_segment expects.  While the loads stream, each
+// thread parks its 32 scores in its own column of an LDS array (stride 256 words: no bank
+// conflicts, no barrier needed) instead of registers, so the loop keeps the register
+// budget of the plain scoring kernel and four workgroups fit a CU; once the keys are back
+// in registers the same LDS holds the selection histograms.
 template <bool kPool, bool kFinal>
 __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
+  static_assert(kTkSeg >= kTkHistWords, "the score array doubles as the selection histograms");
+  __shared__ float park[kTkSeg];
   const int seg = blockIdx.x;
   const int q = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   uint64_t key[kTkEpt];
-#pragma unroll
-  for (int i = 0; i < kTkEpt; ++i) key[i] = 0ull;
   QueryScorer<kPool> sc;
-  const int64_t c0 = (int64_t)seg * kTkSeg;
+  const int c0 = seg * kTkSeg;
   // workgroup-uniform condition: every thread reaches select_segment's barriers
   if (sc.init(s, q) && sc.nv > 0 && c0 < sc.n_valid) {
     uint4 bc[4];
     int bs[4];
     sc.load_step(s, c0 + wave * kScoreStep, bc, bs);
-#pragma unroll
+#pragma unroll 2
     for (int i = 0; i < kTkEpt; ++i) {
-      const int64_t base = c0 + (int64_t)i * kTkThreads + wave * kScoreStep;
+      const int base = c0 + i * kTkThreads + wave * kScoreStep;
       uint4 bcn[4];
       int bsn[4];
       // the last step re-reads itself so that the prefetch stays unconditional
       sc.load_step(s, i + 1 < kTkEpt ? base + kTkThreads : base, bcn, bsn);
-      const float v = sc.score_step(bc, bs);
-      int64_t pos;
-      const bool valid = sc.slot_pos(s, base + lane, pos);
-      key[i] = valid ? make_key(v, (uint32_t)pos) : 0ull;
+      park[i * kTkThreads + tid] = sc.score_step(bc, bs);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         bc[t] = bcn[t];
         bs[t] = bsn[t];
       }
     }
+#pragma unroll
+    for (int i = 0; i < kTkEpt; ++i) {
+      uint32_t pos;
+      const bool valid = sc.slot_pos(s, c0 + i * kTkThreads + tid, pos);
+      key[i] = valid ? make_key(park[i * kTkThreads + tid], pos) : 0ull;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kTkEpt; ++i) key[i] = 0ull;
   }
-  select_segment<kFinal>(key, q, seg, gridDim.x, s.k, s.keys_out, s.idx_out, s.count_out);
+  select_segment<kFinal>(key, q, seg, gridDim.x, s.k, reinterpret_cast<uint32_t*>(park), s.keys_out, s.idx_out,
+                         s.count_out);
 }
 
 static int check_score_args(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q, int n_heads,
@@ -257,7 +276,8 @@ static int check_score_args(const uint8_t* q_codes, const uint8_t* q_scales, con
                             const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
                             const int32_t* n_cand_blocks, int block, int max_cand_blocks, int64_t* n_slots) {
   if (!q_codes || !q_scales || !w || !k_codes || !k_scales || !q_seq || !n_vis) return CSA2_ERR_NULL;
-  if (n_q < 0 || n_heads < 1 || n_heads > CSA2_MAX_INDEX_HEADS || dim != CSA2_INDEX_DIM || seq_cap < 0 || n_seq < 1)
+  if (n_q < 0 || n_heads < 1 || n_heads > CSA2_MAX_INDEX_HEADS || dim != CSA2_INDEX_DIM || seq_cap < 0 ||
+      seq_cap > CSA2_MAX_INDEX_ENTRIES || n_seq < 1)
     return CSA2_ERR_SHAPE;
   if (!aligned16(q_codes) || !aligned16(k_codes)) return CSA2_ERR_SHAPE;
   if (cand_blocks) {

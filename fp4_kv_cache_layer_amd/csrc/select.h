@@ -60,13 +60,16 @@ __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v, int lane) {
 // t is candidate i*256 + t of the segment; 0 = no candidate) and writes them in candidate
 // order: non-final levels write the keys to keys_out[(q*n_seg + seg)*K ..], zero padded;
 // the final level writes positions to idx_out[q*K ..], -1 padded, and count_out[q].
+// `hist` is kTkHistWords words of LDS; the caller may have used them for anything before
+// the call (the first write to them follows the call's first barrier).
+constexpr int kTkHistWords = 2 * kTkWaves * 256;
+
 template <bool kFinal>
 __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, int seg, int n_seg, int K,
-                                               uint64_t* __restrict__ keys_out, int32_t* __restrict__ idx_out,
-                                               int32_t* __restrict__ count_out) {
+                                               uint32_t* hist, uint64_t* __restrict__ keys_out,
+                                               int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  __shared__ uint32_t hist[2][kTkWaves][256];
   __shared__ uint32_t cnt[kTkWaves][kTkEpt];
   __shared__ uint64_t red_hi[kTkWaves], red_lo[kTkWaves];
   __shared__ uint32_t red_n[kTkWaves];
@@ -114,7 +117,7 @@ __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, i
     int shift = hb - 7 > 0 ? hb - 7 : 0;
     uint32_t need = (uint32_t)K;
     for (int pass = 0;; ++pass) {
-      uint32_t* h = hist[pass & 1][wave];
+      uint32_t* h = hist + ((pass & 1) * kTkWaves + wave) * 256;
 #pragma unroll
       for (int i = 0; i < 4; ++i) h[lane + 64 * i] = 0;
 #pragma unroll
@@ -127,7 +130,7 @@ __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, i
       for (int j = 0; j < 4; ++j) {
         uint32_t v = 0;
 #pragma unroll
-        for (int wv = 0; wv < kTkWaves; ++wv) v += hist[pass & 1][wv][4 * lane + j];
+        for (int wv = 0; wv < kTkWaves; ++wv) v += hist[((pass & 1) * kTkWaves + wv) * 256 + 4 * lane + j];
         hs[j] = v;
       }
       const uint32_t tot = hs[0] + hs[1] + hs[2] + hs[3];

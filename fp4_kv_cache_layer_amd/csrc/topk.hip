@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(TkArgs a) {
     }
   }
 
-  select_segment<kFinal>(key, q, seg, gridDim.x, K, a.keys_out, a.idx_out, a.count_out);
+  __shared__ uint32_t hist[kTkHistWords];
+  select_segment<kFinal>(key, q, seg, gridDim.x, K, hist, a.keys_out, a.idx_out, a.count_out);
 }
 
 // Launch the key-merging levels 1..L-1 (level 0 has written bufA); returns a csa2 status.

@@ -24,6 +24,41 @@ import torch
 from . import csa2 as C
 
 
+MODES = ("full", "full_pool", "reuse", "reindex", "reindex_pool")
+
+
+def plan_group(modes, fused: bool = True) -> list:
+    """Checks a layer group's mode sequence and returns the calls each layer makes.
+
+    [W] "CSA2：跨层复用，能借就不自己算" and Figure 4: a Reindex layer re-scores the KV of the
+    Full layer before it, a Reuse layer borrows the index set of the last scoring layer, so
+    a group opens with a Full layer.  [W] "分层稀疏索引器": only the decoder's first Full
+    layer builds the pool, and Reindex-in-pool layers need it.  Raises ValueError for a
+    sequence that breaks these rules."""
+    plan, have_kv, have_pool = [], False, False
+    for i, m in enumerate(modes):
+        if m not in MODES:
+            raise ValueError(f"layer {i}: unknown mode {m!r}")
+        if m.startswith("full"):
+            have_kv, have_pool = True, m == "full_pool"
+        elif not have_kv:
+            raise ValueError(f"layer {i}: {m} needs a Full layer before it in the group")
+        if m == "reindex_pool" and not have_pool:
+            raise ValueError(f"layer {i}: reindex_pool needs a pool built by the group's Full layer")
+        if m == "reuse":
+            calls = ["attend"]
+        elif m == "full_pool":   # the pool ranks blocks by their max score: keep the score array
+            calls = ["quantize_index_q", "score", "select", "build_pool", "attend"]
+        elif fused:
+            calls = ["quantize_index_q", "index_topk_pool" if m == "reindex_pool" else "index_topk", "attend"]
+        else:
+            pool = m == "reindex_pool"
+            calls = ["quantize_index_q", "score_pool" if pool else "score", "select_pool" if pool else "select",
+                     "attend"]
+        plan.append(calls)
+    return plan
+
+
 class Caches:
     """Device caches of a layer group: main KV (NVFP4), indexer K (MXFP4), and the
     per-layer FP8 window caches with their ring bases."""
@@ -122,6 +157,35 @@ class Csa2Step:
                                   caches.swa_base, q_pos, replay_start, self.window, self.sm_scale,
                                   self.out if out is None else out, self.lse if lse is None else lse, self.ws_attn,
                                   _bind=bind)
+
+    def run_group(self, caches: Caches, modes, inputs, q_seq, n_vis, q_pos, replay_start, outs=None, lses=None,
+                  bind=False):
+        """Runs the layers of a group in order.  inputs[i] = (indexer Q f32 [n_q, H_I, d] or
+        None for Reuse, w [n_q, H_I] or None, attention Q bf16 [n_q, H, D]); layer i attends
+        with its own window cache caches.swa[i].  outs/lses: optional per-layer outputs
+        (default: the step's own buffers, overwritten by each layer).  With bind=True returns
+        the group's calls as one flat list of callables."""
+        plan = plan_group(modes, self.fused)
+        calls = []
+        for i, (m, names) in enumerate(zip(modes, plan)):
+            q_index, w, q_attn = inputs[i]
+            out = None if outs is None else outs[i]
+            lse = None if lses is None else lses[i]
+            for name in names:
+                if name == "quantize_index_q":
+                    c = self.quantize_index_q(q_index, bind)
+                elif name in ("index_topk", "index_topk_pool"):
+                    c = self.index_topk(caches, w, q_seq, n_vis, name.endswith("pool"), bind)
+                elif name in ("score", "score_pool"):
+                    c = self.score(caches, w, q_seq, n_vis, name.endswith("pool"), bind)
+                elif name in ("select", "select_pool"):
+                    c = self.select(n_vis, name.endswith("pool"), bind)
+                elif name == "build_pool":
+                    c = self.build_pool(n_vis, bind)
+                else:
+                    c = self.attend(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind)
+                calls.append(c)
+        return calls if bind else None
 
     # ---- layer modes ----
     @staticmethod

@@ -79,6 +79,7 @@ extern "C" {
 #define CSA2_MAX_TOPK 2048         /* k of csa2_topk, max_blocks of csa2_build_pool */
 #define CSA2_MAX_INDEX_HEADS 16    /* H_I of csa2_index_score */
 #define CSA2_INDEX_DIM 128         /* d of csa2_index_score */
+#define CSA2_MAX_INDEX_ENTRIES (1 << 26)  /* seq_cap of csa2_index_score / csa2_index_topk */
 #define CSA2_MAIN_DIM 512          /* D of csa2_sparse_attn */
 #define CSA2_MAX_WINDOW 1024       /* window of csa2_sparse_attn */
 
@@ -149,7 +150,8 @@ int csa2_quantize_kv(const void* src, int src_dtype, int64_t rows, int dim, int 
  *   block             positions per pool block (1..64) when cand_blocks is given
  *   scores            [n_q, scores_stride] f32
  * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (n_q < 0, n_heads not in 1..16, dim != 128,
- * seq_cap < 0, n_seq < 1, scores_stride too small for seq_cap or max_cand_blocks*block).
+ * seq_cap outside 0..CSA2_MAX_INDEX_ENTRIES, n_seq < 1, scores_stride too small for
+ * seq_cap or max_cand_blocks*block).
  */
 int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
                      int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,

@@ -7,6 +7,7 @@ its own copy.
 """
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -151,3 +152,96 @@ def smoke_check() -> dict:
     lse_err = float(np.abs(step.lse[0].cpu().numpy() - ref_lse).max())
     assert lse_err <= 1e-3
     return {"topk_set_diff": miss, "attn_err": err, "lse_err": lse_err}
+
+
+# ---------- full-size layer groups: sampled oracle parity ----------
+
+def oracle_main_rows(wl: Workload, seq: int, positions: np.ndarray):
+    """Oracle NVFP4 codes, scales and dequantised rows of one sequence's main-KV entries at
+    the given positions (regenerated one by one from the seeded latents)."""
+    pos = np.asarray(positions, np.int64)
+    lat = np.stack([wl.main_latents(seq, int(p), 1)[0] for p in pos]) if pos.size else np.zeros((0, DIM), np.float32)
+    codes, scales = O.quantize_nvfp4(lat)
+    return codes, scales, O.dequant_nvfp4(codes, scales)
+
+
+@functools.lru_cache(maxsize=4)
+def _oracle_index_cache(name: str, seq: int) -> O.PackedCaches:
+    wl = workloads.config(name)
+    ik_c, ik_s = O.quantize_mxfp4(wl.index_k_latents(seq, 0, wl.seq_cap))
+    return O.PackedCaches(None, None, ik_c, ik_s)
+
+
+def oracle_index_cache(wl: Workload, seq: int) -> O.PackedCaches:
+    """Oracle caches of one sequence holding the indexer K only (the part scoring reads);
+    kept for reuse across tests of the same named workload."""
+    if wl.name in workloads.CONFIG_NAMES:
+        return _oracle_index_cache(wl.name, seq)
+    ik_c, ik_s = O.quantize_mxfp4(wl.index_k_latents(seq, 0, wl.seq_cap))
+    return O.PackedCaches(None, None, ik_c, ik_s)
+
+
+def run_group_snapshots(case: Case, step, caches):
+    """Runs the workload's layer group on the GPU layer by layer and returns per-layer
+    snapshots: idx, count (the set each layer attended over), out, lse, and the pool."""
+    from fp4_kv_cache_layer_amd.layer import plan_group
+    wl = case.wl
+    q_seq, n_vis, q_pos, rs = case.gpu_meta()
+    modes = list(wl.layers)
+    inputs = [case.gpu_query_inputs(L) for L in range(len(modes))]
+    calls = step.run_group(caches, modes, inputs, q_seq, n_vis, q_pos, rs, bind=True)
+    snaps, at = [], 0
+    for names in plan_group(modes, step.fused):
+        for fn in calls[at:at + len(names)]:
+            fn()
+        at += len(names)
+        torch.cuda.synchronize()
+        snaps.append({"idx": step.idx.cpu().numpy().copy(), "count": step.count.cpu().numpy().copy(),
+                      "out": step.out.cpu().numpy().copy(), "lse": step.lse.cpu().numpy().copy(),
+                      "pool": step.pool.cpu().numpy().copy(), "pool_count": step.pool_count.cpu().numpy().copy()})
+    return snaps
+
+
+def check_group_query(case: Case, caches, snaps, qi: int, k: int = 512, window: int = 128,
+                      block: int = 8, max_blocks: int = 2048) -> dict:
+    """Oracle parity of one query row through every layer of the group.  Index sets and the
+    pool pass the oracle's acceptance rules; each layer's attention is compared with the
+    oracle's over the set the GPU attended (so a legitimate near-tie swap upstream does not
+    fail the attention check)."""
+    wl = case.wl
+    seq, nv = int(wl.q_seq[qi]), int(wl.n_vis[qi])
+    t, s = int(wl.q_pos[qi]), int(wl.replay_start[qi])
+    oc = oracle_index_cache(wl, seq)
+    assert np.array_equal(caches.ik_codes[seq].cpu().numpy(), oc.ik_codes)
+    assert np.array_equal(caches.ik_scales[seq].cpu().numpy(), oc.ik_scales)
+    stats = {"set_diff": []}
+    pool = None
+    for L, mode in enumerate(wl.layers):
+        snap = snaps[L]
+        idx, cnt = snap["idx"][qi], int(snap["count"][qi])
+        if mode != "reuse":
+            qc, qs, w, _ = case.oracle_query(L, qi)
+            cand = pool_pos = None
+            if mode == "reindex_pool":
+                pool_pos = O.pool_positions(pool, nv, block)
+                cand = pool_pos
+            pos, sc = O.full_scores(qc, qs, w, oc, nv, cand)
+            stats["set_diff"].append(topk_accept(idx, cnt, pos, sc, k))
+            if mode == "full_pool":
+                bs = O.block_scores(sc, nv, block)
+                pool = snap["pool"][qi]
+                topk_accept(pool, int(snap["pool_count"][qi]), np.arange(bs.size), bs, max_blocks)
+        else:
+            assert np.array_equal(idx, snaps[L - 1]["idx"][qi])   # borrowed, untouched
+        sel = idx[:cnt]
+        codes, scales, main = oracle_main_rows(wl, seq, sel)
+        assert np.array_equal(caches.kv_codes[seq][torch.from_numpy(sel).long().cuda()].cpu().numpy(), codes)
+        assert np.array_equal(caches.kv_scales[seq][torch.from_numpy(sel).long().cuda()].cpu().numpy(), scales)
+        swa = O.quantize_fp8(swa_ring_latents(wl, L, seq))
+        rows = np.mod(O.swa_positions(t, s, window) - wl.swa_base, wl.swa_cap)
+        assert np.array_equal(caches.swa[L][seq][torch.from_numpy(rows).cuda()].cpu().numpy(), swa[rows])
+        _, _, _, qa = case.oracle_query(L, qi)
+        ref, ref_lse = O.sparse_attention(qa, main, O.dequant_fp8(swa[rows]), 1.0 / math.sqrt(DIM))
+        attn_close(snap["out"][qi], ref)
+        assert np.abs(snap["lse"][qi] - ref_lse).max() <= 1e-3
+    return stats

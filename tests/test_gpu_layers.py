@@ -1,0 +1,42 @@
+"""Full-size layer groups on the GPU: the 128K group (Full, 3 Reuse, Reindex; 32 queries)
+and the 1M group (Full + pool, 4 Reindex inside the pool; 8 queries), run through the layer
+driver exactly as the benchmark runs them, with oracle parity on sampled query rows."""
+import sys
+
+import pytest
+import torch
+
+from synth import workloads
+from tests import gpu_cases as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def C():
+    from fp4_kv_cache_layer_amd import csa2
+    csa2.csa2_init()
+    return csa2
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,samples", [("c3", (0, 13, 31)), ("c4", (0, 5))])
+@pytest.mark.parametrize("fused", [True, False])
+def test_layer_group_full_size(C, name, samples, fused):
+    _say("layer group", name, "fused" if fused else "two-call")
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    wl = workloads.config(name)
+    case = G.Case(wl, swa_layers=range(len(wl.layers)))
+    caches = case.gpu_caches()
+    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, fused=fused)
+    snaps = G.run_group_snapshots(case, step, caches)
+    for qi in samples:
+        _say("  oracle query", qi)
+        G.check_group_query(case, caches, snaps, qi)
+    del caches, step
+    torch.cuda.empty_cache()

@@ -1,0 +1,48 @@
+"""Host-side orchestration of a layer group (no GPU): the mode rules of the pages and the
+calls each layer makes, checked against the oracle's model schedule."""
+import pytest
+
+from fp4_kv_cache_layer_amd.layer import plan_group
+from oracle import csa2_oracle as O
+
+
+def _groups(schedule):
+    """Splits the model schedule into groups, each opened by a Full layer."""
+    groups = []
+    for part, _, mode in schedule:
+        if mode == "full":
+            groups.append([])
+        groups[-1].append(mode)
+    return groups
+
+
+def test_model_schedule_groups_plan():
+    groups = _groups(O.layer_schedule())
+    assert len(groups) == 4            # 3 encoder groups, 1 decoder group with 4 Reindex layers
+    for g in groups:
+        plan = plan_group(g)
+        assert len(plan) == len(g)
+        for mode, calls in zip(g, plan):
+            assert calls[-1] == "attend"
+            if mode == "reuse":
+                assert calls == ["attend"]          # borrows the index set: no scoring
+            else:
+                assert calls[0] == "quantize_index_q"  # its own indexer Q
+    dec = _groups(O.layer_schedule())[-1]
+    dec = ["full_pool"] + ["reindex_pool" if m == "reindex" else m for m in dec[1:]]
+    plan = plan_group(dec)
+    assert "build_pool" in plan[0] and plan[0].index("build_pool") < plan[0].index("attend")
+    assert all(p == ["quantize_index_q", "index_topk_pool", "attend"] for m, p in zip(dec, plan) if m == "reindex_pool")
+
+
+def test_unfused_plan_keeps_two_calls():
+    plan = plan_group(["full", "reuse", "reindex", "reindex"], fused=False)
+    assert plan[0] == ["quantize_index_q", "score", "select", "attend"]
+    assert plan[2] == ["quantize_index_q", "score", "select", "attend"]
+
+
+@pytest.mark.parametrize("modes", [["reuse"], ["reindex", "reuse"], ["full", "reindex_pool"], ["full_pool", "bogus"],
+                                   ["reindex_pool"]])
+def test_invalid_groups_rejected(modes):
+    with pytest.raises(ValueError):
+        plan_group(modes)
