@@ -1,15 +1,20 @@
 #!/usr/bin/env python3
-"""Benchmark of one CSA2 Full-mode decode layer step on one MI355X.
+"""Benchmark of the CSA2 layer step on one MI355X.
 
-Step (per timed iteration, all on one stream, inputs resident in HBM):
-  quantise-and-write the new token's main-KV entry (NVFP4), indexer-K entry (MXFP4) and
-  sliding-window entry (FP8) of every sequence; quantise the indexer Q (MXFP4); score every
-  visible entry (FP4 matrix cores); Top-512; sparse attention over the 512 entries plus the
-  128-token window.  Metric: query tokens per second per layer.
+A layer step (one graph launch, inputs resident in HBM): append the new token's cache
+entries (Full layers: main KV in NVFP4 and indexer K in MXFP4; every layer: its FP8
+window entry), quantise the layer's indexer Q (MXFP4), score the candidates on the FP4
+matrix cores and keep the Top-512 (Full: every visible entry; Reindex: the same cache
+with the layer's own indexer Q, inside the pool when there is one), and attend over the
+512 entries plus the 128-token window.  A Reuse layer only appends its window entry and
+attends with the borrowed index set.  The appends that only attention reads run on
+parallel graph branches.
 
-Default workload: batched decode, 64 queries, 131,072 compressed entries per sequence (128K
-tokens at m=1), 64 heads, 16 indexer heads.  `--ctx1m` adds the 1M-entry decode (8 queries)
-as a second measurement.  The CPU baseline times the fp64 oracle on a bounded sample.
+Headline: the Full decode step of 64 queries x 131,072 entries (128K tokens at m=1), 64
+heads, 16 indexer heads; metric query tokens per second per layer.  Also reported (unless
+--no-modes): every mode of the 128K layer group (Full, 3 Reuse, Reindex; 32 queries) and
+of the 1M group (Full + pool, 4 Reindex inside the pool; 8 queries), and each group as one
+graph.  The CPU baseline times the fp64 oracle on a bounded sample of the headline step.
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -29,73 +34,152 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MAIN_ENTRY_B = 288      # 256 B E2M1 codes + 32 E4M3 scales
 INDEX_ENTRY_B = 68      # 64 B E2M1 codes + 4 E8M0 scales
+TOPK, WINDOW, BLOCK, MAX_BLOCKS = 512, 128, 8, 2048
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def build_gpu_state(wl, torch, C):
-    """Seeded latents -> HBM caches through the library's own quantiser (setup, untimed)."""
-    from fp4_kv_cache_layer_amd.layer import Caches, Csa2Step
-    from synth.workloads import DIM, IDX_DIM
-    dev = "cuda"
-    caches = Caches.empty(wl.n_seq, wl.seq_cap, (0,), wl.swa_cap)
-    caches.swa_base.fill_(wl.swa_base)
-    chunk = 1 << 16
-    t0 = time.time()
-    for b in range(wl.n_seq):
-        for r0 in range(0, wl.seq_cap, chunk):
-            n = min(chunk, wl.seq_cap - r0)
-            lat = torch.from_numpy(wl.main_latents(b, r0, n)).to(dev)
-            C.csa2_quantize_kv(lat, C.FMT_NVFP4, caches.kv_codes[b, r0:r0 + n], caches.kv_scales[b, r0:r0 + n])
-            ik = torch.from_numpy(wl.index_k_latents(b, r0, n)).to(dev)
-            C.csa2_quantize_kv(ik, C.FMT_MXFP4, caches.ik_codes[b, r0:r0 + n], caches.ik_scales[b, r0:r0 + n])
-        t = int(wl.q_pos[wl.q_seq == b].max())
-        p0 = max(0, t - wl.swa_cap + 1)
-        sw = wl.swa_latents(0, b, p0, t - p0 + 1)
-        rows = torch.from_numpy(((np.arange(p0, t + 1) - wl.swa_base) % wl.swa_cap).astype(np.int64)).to(dev)
-        C.csa2_quantize_kv(torch.from_numpy(sw).to(dev), C.FMT_FP8, caches.swa[0][b], None, rows)
-        if b % 16 == 15:
-            log(f"  caches: {b + 1}/{wl.n_seq} sequences ({time.time() - t0:.1f}s)")
-    torch.cuda.synchronize()
+class LayerBench:
+    """GPU state of one workload's layer group: caches built from the seeded latents by the
+    library's own quantiser (setup, untimed), per-layer query inputs, the new token's
+    latents, and a Csa2Step.  A layer step = appending the new token's cache entries, then
+    the layer's own calls (Full: main KV + indexer K + its window entry; Reuse / Reindex:
+    its window entry only, since they share the Full layer's global KV)."""
 
-    st = {}
-    q_seq = torch.from_numpy(wl.q_seq.astype(np.int32)).to(dev)
-    st["q_seq"], st["n_vis"] = q_seq, torch.from_numpy(wl.n_vis).to(dev)
-    st["q_pos"], st["rs"] = torch.from_numpy(wl.q_pos).to(dev), torch.from_numpy(wl.replay_start).to(dev)
-    st["q_idx"] = torch.from_numpy(wl.index_q(0)).to(dev)
-    st["w"] = torch.from_numpy(wl.index_w(0)).to(dev)
-    st["qa"] = torch.from_numpy(wl.attn_q_bits(0).view(np.int16)).to(dev).view(torch.bfloat16)
-    # the newest token of every sequence: its entry latents, written inside the step
-    first_new = int(wl.new_entries[0])
-    new_main = np.stack([wl.main_latents(int(b), first_new, 1)[0] for b in wl.q_seq])
-    new_ik = np.stack([wl.index_k_latents(int(b), first_new, 1)[0] for b in wl.q_seq])
-    new_swa = np.stack([wl.swa_latents(0, int(b), int(t), 1)[0] for b, t in zip(wl.q_seq, wl.q_pos)])
-    st["new_main"], st["new_ik"] = torch.from_numpy(new_main).to(dev), torch.from_numpy(new_ik).to(dev)
-    st["new_swa"] = torch.from_numpy(new_swa).to(dev)
-    st["dst_entry"] = torch.from_numpy((wl.q_seq.astype(np.int64) * wl.seq_cap + first_new)).to(dev)
-    st["dst_swa"] = torch.from_numpy(wl.q_seq.astype(np.int64) * wl.swa_cap +
-                                     (wl.q_pos - wl.swa_base) % wl.swa_cap).to(dev)
-    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap)
-    return caches, st, step
+    def __init__(self, wl, torch, C):
+        from fp4_kv_cache_layer_amd.layer import Caches, Csa2Step, plan_group
+        self.wl, self.torch, self.C = wl, torch, C
+        self.plan = plan_group(wl.layers)
+        n_layers = len(wl.layers)
+        dev = "cuda"
+        caches = Caches.empty(wl.n_seq, wl.seq_cap, range(n_layers), wl.swa_cap)
+        caches.swa_base.fill_(wl.swa_base)
+        chunk = 1 << 16
+        t0 = time.time()
+        for b in range(wl.n_seq):
+            for r0 in range(0, wl.seq_cap, chunk):
+                n = min(chunk, wl.seq_cap - r0)
+                lat = torch.from_numpy(wl.main_latents(b, r0, n)).to(dev)
+                C.csa2_quantize_kv(lat, C.FMT_NVFP4, caches.kv_codes[b, r0:r0 + n], caches.kv_scales[b, r0:r0 + n])
+                ik = torch.from_numpy(wl.index_k_latents(b, r0, n)).to(dev)
+                C.csa2_quantize_kv(ik, C.FMT_MXFP4, caches.ik_codes[b, r0:r0 + n], caches.ik_scales[b, r0:r0 + n])
+            t = int(wl.q_pos[wl.q_seq == b].max())
+            p0 = max(0, t - wl.swa_cap + 1)
+            rows = torch.from_numpy(((np.arange(p0, t + 1) - wl.swa_base) % wl.swa_cap).astype(np.int64)).to(dev)
+            for L in range(n_layers):
+                sw = wl.swa_latents(L, b, p0, t - p0 + 1)
+                C.csa2_quantize_kv(torch.from_numpy(sw).to(dev), C.FMT_FP8, caches.swa[L][b], None, rows)
+            if b % 16 == 15 or b == wl.n_seq - 1:
+                log(f"  caches: {b + 1}/{wl.n_seq} sequences ({time.time() - t0:.1f}s)")
+        torch.cuda.synchronize()
+        self.caches = caches
+        self.q_seq = torch.from_numpy(wl.q_seq.astype(np.int32)).to(dev)
+        self.n_vis = torch.from_numpy(wl.n_vis).to(dev)
+        self.q_pos = torch.from_numpy(wl.q_pos).to(dev)
+        self.rs = torch.from_numpy(wl.replay_start).to(dev)
+        self.inputs = []
+        for L in range(n_layers):
+            q_idx = torch.from_numpy(wl.index_q(L)).to(dev)
+            w = torch.from_numpy(wl.index_w(L)).to(dev)
+            qa = torch.from_numpy(wl.attn_q_bits(L).view(np.int16)).to(dev).view(torch.bfloat16)
+            self.inputs.append((q_idx, w, qa))
+        # the newest token of every sequence: its entry latents, written inside the step
+        first_new = int(wl.new_entries[0])
+        self.new_main = torch.from_numpy(np.stack([wl.main_latents(int(b), first_new, 1)[0] for b in wl.q_seq])).to(dev)
+        self.new_ik = torch.from_numpy(np.stack([wl.index_k_latents(int(b), first_new, 1)[0] for b in wl.q_seq])).to(dev)
+        self.new_swa = [torch.from_numpy(np.stack([wl.swa_latents(L, int(b), int(t), 1)[0]
+                                                   for b, t in zip(wl.q_seq, wl.q_pos)])).to(dev)
+                        for L in range(n_layers)]
+        self.dst_entry = torch.from_numpy(wl.q_seq.astype(np.int64) * wl.seq_cap + first_new).to(dev)
+        self.dst_swa = torch.from_numpy(wl.q_seq.astype(np.int64) * wl.swa_cap +
+                                        (wl.q_pos - wl.swa_base) % wl.swa_cap).to(dev)
+        self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap)
 
+    def calls(self, L: int):
+        """Layer L's step as {phase: bound call} bound to the current stream, in order."""
+        C, c, st = self.C, self.caches, self.step
+        mode = self.wl.layers[L]
+        flat = lambda t: t.view(-1, t.shape[2])
+        out = {}
+        if mode.startswith("full"):
+            out["quant_main"] = C.csa2_quantize_kv(self.new_main, C.FMT_NVFP4, flat(c.kv_codes), flat(c.kv_scales),
+                                                   self.dst_entry, _bind=True)
+            out["quant_index_k"] = C.csa2_quantize_kv(self.new_ik, C.FMT_MXFP4, flat(c.ik_codes), flat(c.ik_scales),
+                                                      self.dst_entry, _bind=True)
+        out["quant_swa"] = C.csa2_quantize_kv(self.new_swa[L], C.FMT_FP8, flat(c.swa[L]), None, self.dst_swa,
+                                              _bind=True)
+        q_idx, w, qa = self.inputs[L]
+        names = self.plan[L]
+        if "quantize_index_q" in names:
+            out["quant_index_q"] = st.quantize_index_q(q_idx, bind=True)
+        if mode == "full_pool":
+            out["score"] = st.score(c, w, self.q_seq, self.n_vis, bind=True)
+            out["topk"] = st.select(self.n_vis, bind=True)
+            out["build_pool"] = st.build_pool(self.n_vis, bind=True)
+        elif mode != "reuse":
+            out["index_topk"] = st.index_topk(c, w, self.q_seq, self.n_vis, mode == "reindex_pool", bind=True)
+        out["attn"] = st.attend(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True)
+        return out
 
-def bound_calls(wl, caches, st, step, C):
-    """The step's calls, validated and marshalled once: list of (phase, callable)."""
-    kvc = caches.kv_codes.view(-1, caches.kv_codes.shape[2])
-    kvs = caches.kv_scales.view(-1, caches.kv_scales.shape[2])
-    ikc = caches.ik_codes.view(-1, caches.ik_codes.shape[2])
-    iks = caches.ik_scales.view(-1, caches.ik_scales.shape[2])
-    swa = caches.swa[0].view(-1, caches.swa[0].shape[2])
-    return [
-        ("quant_main", C.csa2_quantize_kv(st["new_main"], C.FMT_NVFP4, kvc, kvs, st["dst_entry"], _bind=True)),
-        ("quant_index_k", C.csa2_quantize_kv(st["new_ik"], C.FMT_MXFP4, ikc, iks, st["dst_entry"], _bind=True)),
-        ("quant_swa", C.csa2_quantize_kv(st["new_swa"], C.FMT_FP8, swa, None, st["dst_swa"], _bind=True)),
-        ("quant_index_q", step.quantize_index_q(st["q_idx"], bind=True)),
-        ("index_topk", step.index_topk(caches, st["w"], st["q_seq"], st["n_vis"], bind=True)),
-        ("attn", step.attend(caches, 0, st["qa"], st["q_seq"], st["q_pos"], st["rs"], bind=True)),
-    ]
+    # appends that only attention reads run on a side branch of the graph, the indexer-K
+    # append on a second one; both join before their first reader
+    _SIDE = ("quant_main", "quant_swa")
+
+    def record(self, layers):
+        """Issues the steps of `layers` on the current stream with the appends on forked
+        streams (captured as parallel graph branches)."""
+        torch = self.torch
+        main = torch.cuda.current_stream()
+        for L in layers:
+            side, side2 = self._side
+            side.wait_stream(main)
+            side2.wait_stream(main)
+            with torch.cuda.stream(side):
+                sc = self.calls(L)
+                for name in self._SIDE:
+                    if name in sc:
+                        sc[name]()
+            with torch.cuda.stream(side2):
+                s2 = self.calls(L)
+                if "quant_index_k" in s2:
+                    s2["quant_index_k"]()
+            mc = self.calls(L)
+            for name, fn in mc.items():
+                if name in self._SIDE or name == "quant_index_k":
+                    continue
+                if name in ("index_topk", "score"):
+                    main.wait_stream(side2)
+                if name == "attn":
+                    main.wait_stream(side)
+                    main.wait_stream(side2)
+                fn()
+
+    def capture(self, layers):
+        """One HIP graph of the steps of `layers`; three replays are checked bitwise against
+        an eager run of the same calls."""
+        torch = self.torch
+        self._side = (torch.cuda.Stream(), torch.cuda.Stream())
+        # a Reuse layer reads the index set the previous scoring layer left: only the
+        # attention outputs are outputs there
+        scoring = any(self.wl.layers[L] != "reuse" for L in layers)
+        outs = ((self.step.idx, self.step.count) if scoring else ()) + (self.step.out, self.step.lse)
+        self.record(layers)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outs]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.record(layers)
+        for rep in range(3):
+            for t in outs:  # eager work between replays
+                t.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            for t, r in zip(outs, ref):
+                if not torch.equal(t, r):
+                    raise RuntimeError(f"graph replay {rep} of layers {layers} differs from the eager run")
+        return graph
 
 
 def time_isolated(fn, iters, torch):
@@ -112,27 +196,6 @@ def time_isolated(fn, iters, torch):
     return e0.elapsed_time(e1) / iters
 
 
-def capture_step(wl, caches, st, step, C, torch):
-    """Record the step's calls into one HIP graph and check replays against an eager run."""
-    for _, fn in bound_calls(wl, caches, st, step, C):
-        fn()
-    torch.cuda.synchronize()
-    ref = [t.clone() for t in (step.idx, step.count, step.out, step.lse)]
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _, fn in bound_calls(wl, caches, st, step, C):   # bound to the capture stream
-            fn()
-    for rep in range(3):
-        for t in (step.idx, step.count, step.out, step.lse):  # eager work between replays
-            t.zero_()
-        graph.replay()
-        torch.cuda.synchronize()
-        for t, r in zip((step.idx, step.count, step.out, step.lse), ref):
-            if not torch.equal(t, r):
-                raise RuntimeError(f"graph replay {rep} differs from the eager step")
-    return graph
-
-
 def time_graph(graph, steps, warmup, torch):
     for _ in range(warmup):
         graph.replay()
@@ -147,18 +210,24 @@ def time_graph(graph, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps, time.perf_counter() - wall0
 
 
-def score_bytes(wl) -> int:
-    """Algorithmic HBM bytes of one scoring launch: every visible indexer-K entry (68 B) of
-    every query, plus each query's MXFP4 indexer Q and head weights."""
-    per_q_fixed = wl.idx_heads * (64 + 4 + 4)
-    return int(wl.n_vis.sum()) * INDEX_ENTRY_B + wl.n_q * per_q_fixed
+def score_bytes(wl, mode: str) -> int:
+    """Algorithmic HBM bytes of one scoring pass: every candidate's indexer-K entry (68 B;
+    all visible entries, or the 16,384 pool positions) plus each query's MXFP4 indexer Q
+    and head weights."""
+    if mode == "reuse":
+        return 0
+    cand = np.minimum(wl.n_vis, MAX_BLOCKS * BLOCK) if mode == "reindex_pool" else wl.n_vis
+    return int(cand.sum()) * INDEX_ENTRY_B + wl.n_q * wl.idx_heads * (64 + 4 + 4)
 
 
-def step_bytes(wl) -> int:
-    """Algorithmic HBM bytes of one Full layer step (what must cross HBM at least once)."""
-    k, W = 512, 128
-    per_q = (k * MAIN_ENTRY_B + W * 512 + wl.heads * 512 * (2 + 4) + k * 4)   # gather, window, Q bf16, out f32, idx
-    return score_bytes(wl) + wl.n_q * per_q
+def step_bytes(wl, mode: str) -> int:
+    """Algorithmic HBM bytes of one layer step: what must cross HBM at least once
+    (scoring input; the gathered main-KV entries, window, Q, output, LSE and index set of
+    attention; the pool ids where a pool is written or read)."""
+    k, W = TOPK, WINDOW
+    attn = k * MAIN_ENTRY_B + W * 512 + wl.heads * 512 * (2 + 4) + wl.heads * 4 + k * 4
+    pool = MAX_BLOCKS * 4 if mode in ("full_pool", "reindex_pool") else 0
+    return score_bytes(wl, mode) + wl.n_q * (attn + pool)
 
 
 def cpu_baseline(wl, n_sample: int, reps: int):
@@ -206,16 +275,35 @@ def cpu_baseline(wl, n_sample: int, reps: int):
                       f"run {reps}x; {el:.1f}s; numpy fp64, BLAS threads = cores"}
 
 
-def run_workload(name, steps, warmup, torch, C):
+def measure_layers(name, steps, warmup, torch, C, layers_to_time):
+    """Graph-replay time of each listed layer's step and of the whole group; isolated
+    launch times of the first listed layer's calls."""
     from synth import workloads
     wl = workloads.config(name)
     log(f"workload {name}: {wl.description}")
-    caches, st, step = build_gpu_state(wl, torch, C)
-    graph = capture_step(wl, caches, st, step, C, torch)
-    ms, wall = time_graph(graph, steps, warmup, torch)
-    calls = dict(bound_calls(wl, caches, st, step, C))
-    phase = {name: time_isolated(fn, 20, torch) for name, fn in calls.items()}
-    return wl, ms, phase, wall
+    lb = LayerBench(wl, torch, C)
+    res = {"wl": wl, "layers": {}}
+    for L in layers_to_time:
+        g = lb.capture([L])
+        ms, wall = time_graph(g, steps, warmup, torch)
+        res["layers"][L] = {"mode": wl.layers[L], "ms": ms, "wall": wall}
+        del g
+    if len(wl.layers) > 1:
+        g = lb.capture(list(range(len(wl.layers))))
+        ms, _ = time_graph(g, steps, warmup, torch)
+        res["group_ms"] = ms
+        del g
+    res["isolated"] = {n: time_isolated(fn, 20, torch) for n, fn in lb.calls(layers_to_time[0]).items()}
+    del lb
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def mode_entry(wl, mode, ms):
+    b = step_bytes(wl, mode)
+    return {"query_tokens_per_s": round(wl.n_q / (ms / 1e3), 1), "us_per_layer_step": round(ms * 1e3, 2),
+            "hbm_frac": round(b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": b}
 
 
 def main():
@@ -223,8 +311,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2")
-    ap.add_argument("--ctx1m", action="store_true", help="also measure the 1M-entry decode workload")
+    ap.add_argument("--no-modes", action="store_true", help="skip the per-mode 128K group and 1M pool group")
     ap.add_argument("--cpu-sample", type=int, default=4)
     ap.add_argument("--cpu-reps", type=int, default=48)
     ap.add_argument("--no-cpu", action="store_true")
@@ -239,9 +326,12 @@ def main():
     C.csa2_init()
     torch.cuda.set_device(0)
 
-    wl, ms, phase, wall = run_workload(args.workload, args.steps, args.warmup, torch, C)
+    head = measure_layers("c2", args.steps, args.warmup, torch, C, [0])
+    wl = head["wl"]
+    ms = head["layers"][0]["ms"]
+    phase = head["isolated"]
     value = wl.n_q / (ms / 1000.0)
-    sb = score_bytes(wl)
+    sb = score_bytes(wl, "full")
     achieved = sb / (phase["index_topk"] / 1000.0) / 1e9
     log(f"step {ms * 1000:.1f} us (graph replay); isolated launches (us): " +
         ", ".join(f"{k}={v * 1000:.1f}" for k, v in phase.items()))
@@ -260,21 +350,31 @@ def main():
         "dtype": "fp4 scoring (mxfp4 x mxfp4 -> fp32), bf16/fp16 attention -> fp32",
         "data": "synthetic (seeded counter-based generator; no datasets or weights)",
         "config": {"workload": f"{wl.name}: {wl.description}", "queries": wl.n_q, "context_entries": wl.seq_cap,
-                   "m": wl.m, "heads": wl.heads, "index_heads": wl.idx_heads, "topk": 512, "window": 128},
-        "timing": "HIP events around graph replays of the whole step (one graph launch per step)",
+                   "m": wl.m, "heads": wl.heads, "index_heads": wl.idx_heads, "topk": TOPK, "window": WINDOW},
+        "timing": "HIP events around graph replays of the whole layer step (one graph launch per step)",
         "isolated_launch_us": {k: round(v * 1000, 2) for k, v in phase.items()},
-        "hbm_frac_step": round(step_bytes(wl) / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "csa2_index_topk (k_score_select + last selection level)", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": sb, "traffic": None},
+        "hbm_frac_step": round(step_bytes(wl, "full") / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "csa2_index_topk (k_score_select + last selection level)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": sb, "traffic": None},
     }
-    if args.ctx1m:
-        wl4, ms4, phase4, _ = run_workload("c4", args.steps, args.warmup, torch, C)
-        sb4 = score_bytes(wl4)
-        result["ctx_1m"] = {"workload": f"{wl4.name}: Full layer only, {wl4.n_q} queries x {wl4.seq_cap} entries",
-                            "value": round(wl4.n_q / (ms4 / 1000.0), 1), "ms_per_step": round(ms4, 5),
-                            "isolated_launch_us": {k: round(v * 1000, 2) for k, v in phase4.items()},
-                            "index_topk_frac_hbm": round(sb4 / (phase4["index_topk"] / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
+    if not args.no_modes:
+        modes = {}
+        r3 = measure_layers("c3", args.steps, args.warmup, torch, C, [0, 1, 4])
+        for L, v in r3["layers"].items():
+            modes[f"{v['mode']}_128k"] = mode_entry(r3["wl"], v["mode"], v["ms"])
+        n3 = len(r3["wl"].layers)
+        modes["group_128k"] = {"layers": list(r3["wl"].layers), "us_per_group": round(r3["group_ms"] * 1e3, 2),
+                               "query_tokens_per_s_per_layer": round(r3["wl"].n_q * n3 / (r3["group_ms"] / 1e3), 1)}
+        r4 = measure_layers("c4", args.steps, args.warmup, torch, C, [0, 1])
+        for L, v in r4["layers"].items():
+            modes[f"{v['mode']}_1m"] = mode_entry(r4["wl"], v["mode"], v["ms"])
+        n4 = len(r4["wl"].layers)
+        modes["group_1m"] = {"layers": list(r4["wl"].layers), "us_per_group": round(r4["group_ms"] * 1e3, 2),
+                             "query_tokens_per_s_per_layer": round(r4["wl"].n_q * n4 / (r4["group_ms"] / 1e3), 1)}
+        result["modes"] = modes
+        for k, v in modes.items():
+            log(f"  {k}: {v}")
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample, args.cpu_reps)

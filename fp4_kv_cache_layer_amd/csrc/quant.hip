@@ -1,10 +1,12 @@
 // csa2_quantize_kv: quantise post-RoPE rows to NVFP4 / MXFP4 / FP8 and scatter them
 // into a cache ([W] "FP4 与 SWA Bounded Replay"; [L] 4.3 and 5; OCP MX v1.0).
 //
-// Rounding is decided without division: "x rounds to a code >= c" is the comparison of
-// x against the exact midpoint between codes c-1 and c (ties go to the even code).  All
-// midpoints and their products with the scale carry at most 7 significant bits, so every
-// comparison is exact in fp32 and the codes are bit-exact.
+// Every code is the exact round-to-nearest, ties-to-even, of the real value.  E2M1 codes
+// compare x against the exact midpoints between neighbouring codes times the scale; FP8
+// codes round the fp32 bit pattern directly; the NVFP4 scale code (nearest to amax/6)
+// starts from the fp32 quotient and is settled by exact midpoint tests.  All midpoints
+// and their products with the scale carry at most 7 significant bits, so every comparison
+// is exact in fp32 and the codes are bit-exact.
 //
 // One thread quantises one scale group (16 / 32 channels) or, for FP8, 8 channels.
 // Consecutive threads take consecutive groups of a row, so a wave reads a contiguous
@@ -14,32 +16,34 @@
 
 namespace csa2 {
 
-// E4M3 code nearest to a/6 (a >= 0), ties to even, saturating at 448 (code 126).
-// Binary search for the largest c with "a/6 rounds to >= c", i.e. a > 6*mid(c-1,c) or
-// (a == 6*mid(c-1,c) and c even); 6*mid = 3*(v(c-1)+v(c)) is exact.
-__device__ __forceinline__ int nvfp4_scale_code(float a) {
-  int lo = 0, hi = 126;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    float t = 3.0f * (e4m3_mag(mid - 1) + e4m3_mag(mid));
-    bool up = a > t || (a == t && !(mid & 1));
-    lo = up ? mid : lo;
-    hi = up ? hi : mid - 1;
-  }
-  return lo;
+// E4M3 magnitude code (0..126) nearest to a >= 0 (finite), ties to the even code,
+// saturating at 448 (code 126).  Normal range (a >= 2^-6): the fp32 significand is rounded
+// to 3 bits, ties to even, on the bit pattern (a carry out of the significand is the next
+// binade, as it should be) and the exponent is rebiased from 127 to 7.  Subnormal range:
+// the code is a * 2^9 rounded to an integer, ties to even (a * 2^9 is exact); 8 is the
+// smallest normal code, so a carry there is also right.
+__device__ __forceinline__ int fp8_mag_code(float a) {
+  if (a < 0x1p-6f) return (int)__builtin_rintf(a * 512.0f);
+  const uint32_t b = __float_as_uint(a);
+  const int c = (int)((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120 << 3);
+  return c > 126 ? 126 : c;
 }
 
-// E4M3 code (0..126) nearest to a >= 0, ties to even, saturating at 448.
-__device__ __forceinline__ int fp8_mag_code(float a) {
-  int lo = 0, hi = 126;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    float t = 0.5f * (e4m3_mag(mid - 1) + e4m3_mag(mid));
-    bool up = a > t || (a == t && !(mid & 1));
-    lo = up ? mid : lo;
-    hi = up ? hi : mid - 1;
-  }
-  return lo;
+// "a/6 rounds to an E4M3 code >= c" for c >= 1: a/6 lies above the midpoint of codes c-1
+// and c, or on it with c even.  6 * midpoint = 3 * (v(c-1) + v(c)) is exact in fp32.
+__device__ __forceinline__ bool scale_at_least(float a, int c) {
+  const float t = 3.0f * (e4m3_mag(c - 1) + e4m3_mag(c));
+  return a > t || (a == t && !(c & 1));
+}
+
+// E4M3 code nearest to the exact quotient a/6 (a >= 0), ties to even, saturating at 448.
+// The correctly rounded fp32 quotient lands on the right code or, when a/6 sits within
+// an fp32 ulp of a midpoint, on its neighbour; the exact midpoint tests settle which.
+__device__ __forceinline__ int nvfp4_scale_code(float a) {
+  int c = fp8_mag_code(a / 6.0f);
+  if (c < 126 && scale_at_least(a, c + 1)) ++c;
+  else if (c > 0 && !scale_at_least(a, c)) --c;
+  return c;
 }
 
 // E2M1 magnitude code of a/s (a >= 0, s > 0), ties to even, saturating at 6.

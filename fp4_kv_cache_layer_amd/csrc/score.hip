@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
 template <bool kPool, bool kFinal>
 __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
   static_assert(kTkSeg >= kTkHistWords, "the score array doubles as the selection histograms");
-  __shared__ float park[kTkSeg];
+  __shared__ __attribute__((aligned(16))) float park[kTkSeg];
   const int seg = blockIdx.x;
   const int q = blockIdx.y;
   const int tid = threadIdx.x;

@@ -60,9 +60,13 @@ __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v, int lane) {
 // t is candidate i*256 + t of the segment; 0 = no candidate) and writes them in candidate
 // order: non-final levels write the keys to keys_out[(q*n_seg + seg)*K ..], zero padded;
 // the final level writes positions to idx_out[q*K ..], -1 padded, and count_out[q].
-// `hist` is kTkHistWords words of LDS; the caller may have used them for anything before
-// the call (the first write to them follows the call's first barrier).
-constexpr int kTkHistWords = 2 * kTkWaves * 256;
+// `hist` is kTkHistWords words of 16-byte aligned LDS; the caller may have used them for anything before
+// the call (the first write to them follows the call's first barrier).  Each wave counts
+// into kTkCopies interleaved copies of its 256 bins (word bin*kTkCopies + lane%kTkCopies),
+// so lanes that hit the same bin land on different LDS banks: the digits of a segment's
+// best keys bunch into few bins, and same-address atomics would serialise.
+constexpr int kTkCopies = 4;
+constexpr int kTkHistWords = 2 * kTkWaves * 256 * kTkCopies;
 
 template <bool kFinal>
 __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, int seg, int n_seg, int K,
@@ -117,21 +121,25 @@ __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, i
     int shift = hb - 7 > 0 ? hb - 7 : 0;
     uint32_t need = (uint32_t)K;
     for (int pass = 0;; ++pass) {
-      uint32_t* h = hist + ((pass & 1) * kTkWaves + wave) * 256;
+      uint32_t* h = hist + ((pass & 1) * kTkWaves + wave) * 256 * kTkCopies;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[lane + 64 * i] = 0;
+      for (int i = 0; i < kTkCopies; ++i)
+        reinterpret_cast<uint4*>(h)[lane + 64 * i] = make_uint4(0u, 0u, 0u, 0u);
+      uint32_t* hc = h + (lane & (kTkCopies - 1));
 #pragma unroll
       for (int i = 0; i < kTkEpt; ++i)
-        if (key[i] && (key[i] & mask) == prefix) atomicAdd(&h[(uint32_t)(key[i] >> shift) & 255u], 1u);
+        if (key[i] && (key[i] & mask) == prefix) atomicAdd(&hc[((uint32_t)(key[i] >> shift) & 255u) * kTkCopies], 1u);
       __syncthreads();
-      // every wave: lane l owns bins 4l..4l+3 of the summed histogram
-      uint32_t hs[4];
+      // every wave: lane l owns bins 4l..4l+3 of the histogram summed over waves and copies
+      uint32_t hs[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t v = 0;
+      for (int wv = 0; wv < kTkWaves; ++wv) {
+        const uint4* hw = reinterpret_cast<const uint4*>(hist + ((pass & 1) * kTkWaves + wv) * 256 * kTkCopies);
 #pragma unroll
-        for (int wv = 0; wv < kTkWaves; ++wv) v += hist[((pass & 1) * kTkWaves + wv) * 256 + 4 * lane + j];
-        hs[j] = v;
+        for (int j = 0; j < 4; ++j) {
+          const uint4 c = hw[4 * lane + j];
+          hs[j] += c.x + c.y + c.z + c.w;
+        }
       }
       const uint32_t tot = hs[0] + hs[1] + hs[2] + hs[3];
       const uint32_t incl = wave_suffix_sum(tot, lane);

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(TkArgs a) {
     }
   }
 
-  __shared__ uint32_t hist[kTkHistWords];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kTkHistWords];
   select_segment<kFinal>(key, q, seg, gridDim.x, K, hist, a.keys_out, a.idx_out, a.count_out);
 }
 
