@@ -56,7 +56,7 @@ def lib() -> ctypes.CDLL:
                              i32),
         "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp,
                              sz, vp], i32),
-        "csa2_index_topk_workspace_bytes": ([i32, i64, i32], sz),
+        "csa2_index_topk_workspace_bytes": ([i32, i64, i32, i32], sz),
         "csa2_topk": ([vp, i64, i32, vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_topk_workspace_bytes": ([i32, i64, i32], sz),
         "csa2_build_pool": ([vp, i64, i32, vp, i64, i32, i32, vp, vp, vp, sz, vp], i32),
@@ -186,8 +186,8 @@ def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scor
     return _run("csa2_index_score", args + (_p(scores), scores.stride(0), _stream()), _bind)
 
 
-def csa2_index_topk_workspace_bytes(n_q: int, n_slots: int, k: int) -> int:
-    return int(lib().csa2_index_topk_workspace_bytes(n_q, n_slots, k))
+def csa2_index_topk_workspace_bytes(n_q: int, n_slots: int, k: int, in_pool: bool = False) -> int:
+    return int(lib().csa2_index_topk_workspace_bytes(n_q, n_slots, k, int(in_pool)))
 
 
 def csa2_index_topk(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, idx_out, count_out,
@@ -201,7 +201,7 @@ def csa2_index_topk(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: in
     n_q = q_codes.shape[0]
     if idx_out.shape != (n_q, k) or count_out.shape[0] != n_q:
         raise ValueError("index_topk: inconsistent output shapes")
-    need = csa2_index_topk_workspace_bytes(n_q, max(n_slots, 1), k)
+    need = csa2_index_topk_workspace_bytes(n_q, max(n_slots, 1), k, cand_blocks is not None)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_codes.device)
     ws_bytes = 0 if workspace is None else workspace.numel()

@@ -32,7 +32,8 @@ namespace csa2 {
 
 constexpr int kScoreThreads = 256;   // 4 waves
 constexpr int kScoreStep = 64;       // entries per wave step (4 MFMA tiles)
-constexpr int kScoreChunk = 4096;    // entries per workgroup (csa2_index_score)
+constexpr int kScoreChunk = 4096;    // slots per workgroup, all visible entries
+constexpr int kPoolChunk = 512;      // slots per workgroup inside a pool (see launch_score)
 static_assert(kScoreThreads == kTkThreads, "the fused kernel hands its registers to select_segment");
 
 struct ScoreArgs {
@@ -55,6 +56,7 @@ struct ScoreArgs {
   float* scores;
   int64_t scores_stride;
   int chunks;
+  int chunk_len;
   // csa2_index_topk
   int k;
   uint64_t* keys_out;
@@ -182,11 +184,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
   const int wave = threadIdx.x >> 6;
   QueryScorer<kPool> sc;
   if (!sc.init(s, q)) return;
-  const int chunk_lo = chunk * kScoreChunk;
+  const int chunk_lo = chunk * s.chunk_len;
   const int write_hi = kPool ? (int)s.n_slots : sc.n_valid;  // pool mode also writes -inf pads
   if (chunk_lo >= write_hi) return;
   float* out = s.scores + (int64_t)q * s.scores_stride;
-  const int hi = chunk_lo + kScoreChunk < write_hi ? chunk_lo + kScoreChunk : write_hi;
+  const int hi = chunk_lo + s.chunk_len < write_hi ? chunk_lo + s.chunk_len : write_hi;
 
   int base = chunk_lo + wave * kScoreStep;
   if (sc.nv <= 0) {  // nothing to read: pool slots are all -inf, no-pool chunks never get here
@@ -313,6 +315,31 @@ static ScoreArgs make_args(const uint8_t* q_codes, const uint8_t* q_scales, cons
   return a;
 }
 
+// Writes scores[q, slot].  Inside a pool each slot's row comes from a block-id load, so a
+// wave's step is two dependent memory round trips and a workgroup is latency-bound:
+// pool chunks are small (2 steps per wave) to spread the pool over many workgroups.
+static int launch_score(ScoreArgs a, int n_q, float* scores, int64_t scores_stride, hipStream_t st) {
+  a.chunk_len = a.cand_blocks ? kPoolChunk : kScoreChunk;
+  const int64_t chunks = (a.n_slots + a.chunk_len - 1) / a.chunk_len;
+  if (chunks * (int64_t)n_q > 0x7fffffffLL) return CSA2_ERR_SHAPE;
+  a.scores = scores;
+  a.scores_stride = scores_stride;
+  a.chunks = (int)chunks;
+  dim3 grid((unsigned)(chunks * n_q)), blk(kScoreThreads);
+  if (a.cand_blocks) hipLaunchKernelGGL(k_score_decode<true>, grid, blk, 0, st, a);
+  else hipLaunchKernelGGL(k_score_decode<false>, grid, blk, 0, st, a);
+  return csa2_check_launch();
+}
+
+// Bytes of the csa2_index_topk workspace: the selection levels' keys; inside a pool also
+// the score array (the pool is small: the round trip is cheap there and the unfused
+// kernels spread a latency-bound gather over more workgroups).
+static size_t index_topk_ws(int n_q, int64_t n_slots, int k, bool pool) {
+  const size_t sel = ws_bytes(n_q, n_slots, k);
+  if (!pool) return sel;
+  return (((size_t)n_q * n_slots * sizeof(float) + 255) & ~(size_t)255) + sel + 256;
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -329,23 +356,14 @@ extern "C" int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales,
   if (!scores) return CSA2_ERR_NULL;
   if (scores_stride < n_slots) return CSA2_ERR_SHAPE;
   if (n_q == 0 || n_slots == 0) return CSA2_OK;
-  const int64_t chunks = (n_slots + kScoreChunk - 1) / kScoreChunk;
-  if (chunks * (int64_t)n_q > 0x7fffffffLL) return CSA2_ERR_SHAPE;
   ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
                           n_cand_blocks, block, max_cand_blocks, n_slots);
-  a.scores = scores;
-  a.scores_stride = scores_stride;
-  a.chunks = (int)chunks;
-  dim3 grid((unsigned)(chunks * n_q)), blk(kScoreThreads);
-  hipStream_t st = (hipStream_t)stream;
-  if (cand_blocks) hipLaunchKernelGGL(k_score_decode<true>, grid, blk, 0, st, a);
-  else hipLaunchKernelGGL(k_score_decode<false>, grid, blk, 0, st, a);
-  return csa2_check_launch();
+  return launch_score(a, n_q, scores, scores_stride, (hipStream_t)stream);
 }
 
-extern "C" size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k) {
+extern "C" size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_pool) {
   if (n_q <= 0 || n_slots <= 0 || k < 1 || k > CSA2_MAX_TOPK) return 0;
-  return ws_bytes(n_q, n_slots, k);
+  return index_topk_ws(n_q, n_slots, k, in_pool != 0);
 }
 
 extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
@@ -365,8 +383,31 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
   int64_t segs[16];
   const int L = plan_levels(n0, k, segs, 16);
   if (L >= 16) return CSA2_ERR_SHAPE;
-  const size_t need = ws_bytes(n_q, n0, k);
+  const size_t need = index_topk_ws(n_q, n0, k, cand_blocks != nullptr);
   if (need > workspace_bytes || (need && !workspace)) return CSA2_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (cand_blocks) {  // inside a pool: scores into the workspace, then the selection levels
+    float* sc = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+    const size_t sc_bytes = ((size_t)n_q * n0 * sizeof(float) + 255) & ~(size_t)255;
+    ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                            cand_blocks, n_cand_blocks, block, max_cand_blocks, n_slots);
+    rc = launch_score(a, n_q, sc, n0, st);
+    if (rc != CSA2_OK) return rc;
+    TkArgs t = {};
+    t.scores = sc;
+    t.scores_stride = n0;
+    t.n_vis = n_vis;
+    t.max_vis = seq_cap;
+    t.cand_blocks = cand_blocks;
+    t.n_cand_blocks = n_cand_blocks;
+    t.block = block;
+    t.max_cand_blocks = max_cand_blocks;
+    t.idx_out = idx_out;
+    t.count_out = count_out;
+    t.k = k;
+    t.n_slots = n0;
+    return select_from_scores(t, n_q, n0, (uint8_t*)sc + sc_bytes, workspace_bytes - (size_t)((uint8_t*)sc + sc_bytes - (uint8_t*)workspace), st);
+  }
   uint64_t* bufA = (uint64_t*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   uint64_t* bufB = bufA + (size_t)k * n_q * segs[0];
   ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
@@ -375,15 +416,9 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
   a.keys_out = bufA;
   a.idx_out = idx_out;
   a.count_out = count_out;
-  hipStream_t st = (hipStream_t)stream;
   dim3 grid((unsigned)segs[0], (unsigned)n_q), blk(kScoreThreads);
-  if (cand_blocks) {
-    if (L == 1) hipLaunchKernelGGL((k_score_select<true, true>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((k_score_select<true, false>), grid, blk, 0, st, a);
-  } else {
-    if (L == 1) hipLaunchKernelGGL((k_score_select<false, true>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((k_score_select<false, false>), grid, blk, 0, st, a);
-  }
+  if (L == 1) hipLaunchKernelGGL((k_score_select<false, true>), grid, blk, 0, st, a);
+  else hipLaunchKernelGGL((k_score_select<false, false>), grid, blk, 0, st, a);
   rc = csa2_check_launch();
   if (rc != CSA2_OK) return rc;
   TkArgs t = {};

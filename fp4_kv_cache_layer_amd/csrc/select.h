@@ -249,4 +249,8 @@ inline size_t ws_bytes(int n_q, int64_t n0, int k) {
 int select_levels_after0(const int64_t* segs, int L, TkArgs base, int n_q, uint64_t* bufA, uint64_t* bufB,
                          hipStream_t st);
 
+// The Top-K levels over a score array (the csa2_topk path; `base` as csa2_topk fills it);
+// `workspace` holds ws_bytes(n_q, n0, base.k) bytes.  Returns a csa2 status.
+int select_from_scores(TkArgs base, int n_q, int64_t n0, void* workspace, size_t workspace_bytes, hipStream_t st);
+
 }  // namespace csa2

@@ -135,6 +135,10 @@ static int run_select(int mode0, TkArgs base, int n_q, int64_t n0, void* workspa
   return select_levels_after0(segs, L, base, n_q, bufA, bufB, st);
 }
 
+int select_from_scores(TkArgs base, int n_q, int64_t n0, void* workspace, size_t workspace_bytes, hipStream_t st) {
+  return run_select(kFromScores, base, n_q, n0 < 1 ? 1 : n0, workspace, workspace_bytes, st);
+}
+
 }  // namespace csa2
 
 using namespace csa2;

@@ -107,7 +107,8 @@ class Csa2Step:
         self.lse = torch.empty(n_q, n_heads, dtype=torch.float32, **dev)
         n_slots = max(seq_cap, max_blocks * block, 1)
         self.ws_topk = torch.empty(max(C.csa2_topk_workspace_bytes(n_q, n_slots, k), 1), dtype=torch.uint8, **dev)
-        self.ws_index_topk = torch.empty(max(C.csa2_index_topk_workspace_bytes(n_q, n_slots, k), 1),
+        self.ws_index_topk = torch.empty(max(C.csa2_index_topk_workspace_bytes(n_q, max(seq_cap, 1), k),
+                                             C.csa2_index_topk_workspace_bytes(n_q, max_blocks * block, k, True), 1),
                                          dtype=torch.uint8, **dev)
         self.ws_pool = torch.empty(max(C.csa2_pool_workspace_bytes(n_q, max(seq_cap, 1), block, max_blocks), 1),
                                    dtype=torch.uint8, **dev)

@@ -169,8 +169,12 @@ int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const floa
  * csa2_index_score and then csa2_topk with the same arguments: the same fp32 scores in
  * the same ranking (score descending, position ascending).
  *   k in 1..2048; n_q <= 65535.
- *   Workspace: csa2_index_topk_workspace_bytes(n_q, n_slots, k) bytes, n_slots = seq_cap
- *   (no pool) or max_cand_blocks*block.
+ *   Workspace: csa2_index_topk_workspace_bytes(n_q, n_slots, k, in_pool) bytes, with
+ *   n_slots = seq_cap and in_pool = 0 (no pool), or n_slots = max_cand_blocks*block and
+ *   in_pool = 1.  Without a pool no score array exists: each workgroup scores 8,192 slots
+ *   and keeps its best k in registers.  Inside a pool (at most a few thousand blocks) the
+ *   scores go through the workspace, which lets the block-id gather spread over many
+ *   workgroups.
  * Errors: those of csa2_index_score (except the score array's), CSA2_ERR_NULL (idx_out,
  * count_out), CSA2_ERR_SHAPE (k, n_q), CSA2_ERR_WORKSPACE.
  */
@@ -180,7 +184,7 @@ int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float
                     const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
                     int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
                     void* workspace, size_t workspace_bytes, void* stream);
-size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k);
+size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_pool);
 
 /*
  * csa2_topk -- the k highest-scoring candidates of each query.
