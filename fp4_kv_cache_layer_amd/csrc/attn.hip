@@ -5,7 +5,7 @@
 //
 // Per query the key set is at most k + window entries (640 in the decode configurations)
 // of 512 channels, with V = K, against H heads: two dense H x 640 x 512 products, run on
-// the fp16 matrix cores (V_MFMA_F32_16X16X32_F16) with fp32 accumulation.
+// the fp16 matrix cores with fp32 accumulation.
 //
 // Exactness of the operands: every main-KV value is E2M1 x E4M3 (at most 6 significant
 // bits, magnitude in [2^-10, 2688]) and every window value is E4M3, so both are exact in
@@ -13,39 +13,41 @@
 // magnitudes round to fp16 subnormals (absolute error below 2^-25).  P = exp2(logit - max)
 // is rounded to fp16 (11 significant bits) for the P.V product.
 //
-// Decomposition: one workgroup = (query, 16 heads, slice of the key list), 4 waves.  The
-// workgroups of one query are numbered so that they land on the same XCD (dispatch is
-// round-robin over the 8 XCDs) and share its L2 for the gathered rows.  The key list is the
-// k main slots rounded up to whole tiles of 32, then the window keys, so every tile is
-// all-main or all-window.  Per tile:
-//   * gather: thread (key, 64-channel block) issues 3 wide loads (32 B of E2M1 codes + 4 B
-//     of E4M3 scales, or 64 B of window E4M3), dequantises with the hardware FP4/FP8 -> fp16
-//     converts (then an exact packed fp16 multiply by the group scale) and writes 128 B of
-//     the tile's K rows, [key][channel] fp16, into LDS (row stride 1,072 B: conflict-free for
-//     both reads below).
-//   * S^T = K Q^T: wave w takes the tile's 16 keys (w & 1) and channel half (w >> 1): 8 MFMAs
-//     with K read from LDS and Q in registers; the two channel halves meet in a small LDS
-//     buffer.
-//   * every wave forms P for the 16 heads x 32 keys (identical online-softmax statistics in
-//     all 4 waves) and accumulates O^T for its 128 channels.  The V^T operand of P.V comes
-//     from the same K rows through DS_READ_B64_TR_B16, which hands each lane one channel of
-//     4 keys: no transposed copy is stored.
-// LDS is double buffered, so each tile costs one barrier; the raw bytes of tile i+1 and the
-// index of tile i+2 are in flight while tile i is processed.  When a batch has too few
-// queries to fill the GPU, the key list is split over workgroups and a combine kernel merges
-// the partial (O, m, l) with the log-sum-exp rule.
+// Decomposition: one workgroup = (query, 16 heads, slice of the key list), 4 waves, and
+// every wave works on its own keys: the key list is cut into tiles of 16 keys and wave w
+// takes tiles w, w+4, w+8, ... of the slice, keeping its own online-softmax state (m, l)
+// and its own O^T (512 channels x 16 heads, 32 MFMA accumulators).  Per tile a wave
+//   * gathers its 16 keys (lane = key x channel quarter: 64 B of E2M1 codes + 8 B of E4M3
+//     scales, or 128 B of window E4M3), dequantises them with the hardware FP4/FP8 -> fp16
+//     converts and an exact packed multiply by the group scale, and writes the 16 rows
+//     into its own LDS buffer (row stride 1,072 B: conflict-free for both reads below);
+//   * forms S^T = K Q^T (16 keys x 16 heads) with 16 V_MFMA_F32_16X16X32_F16, K read from
+//     LDS and Q held in registers;
+//   * updates (m, l) per head (m lazily: see compute_tile) and turns S^T into P^T in
+//     fp16: the accumulator layout of that MFMA (lane: head l%16, keys 4(l/16)..+3) is
+//     exactly the B-operand layout of V_MFMA_F32_16X16X16_F16, so P needs no shuffle;
+//   * accumulates O^T += V^T P^T with 32 of those, V^T read from the same K rows through
+//     DS_READ_B64_TR_B16 (each lane receives one channel of 4 keys).
+// No barrier is needed inside the loop (the buffer is the wave's own); the raw bytes of the
+// next two tiles are in flight while a tile is processed.  At the end the four waves merge
+// (O, m, l) with the log-sum-exp rule through LDS, 256 channels at a time.  The workgroups
+// of one query are numbered so that they land on the same XCD (dispatch is round-robin
+// over the 8 XCDs) and share its L2 for the gathered rows.  When a batch has too few
+// queries to fill the GPU, the key list is split over workgroups and a combine kernel
+// merges the partial (O, m, l).
 #include "device.h"
 
 namespace csa2 {
 
-constexpr int kAttnThreads = 256;
-constexpr int kT = 32;                    // keys per tile
+constexpr int kPairs = 4;                 // key streams per workgroup
+constexpr int kAttnThreads = 2 * kPairs * 64;  // 8 waves: each stream has two channel halves
+constexpr int kT = 16;                    // keys per tile (one MFMA block)
 constexpr int kHG = 16;                   // heads per workgroup
 constexpr int kD = 512;
-constexpr int kKRow = kD * 2 + 48;        // bytes per K row in LDS: 1,072 (see the header)
-constexpr int kKBuf = kT * kKRow;
-constexpr int kSRow = 20;                 // floats per key row of the logit exchange
-constexpr int kSBuf = 2 * kT * kSRow;     // floats: 2 channel halves x 32 keys
+constexpr int kDT = kD / 32;              // 16-channel blocks of a wave's O^T half: 16
+constexpr int kKRow = kD * 2 + 48;        // bytes per K row in LDS (padding against bank conflicts)
+constexpr int kTileBuf = kT * kKRow;      // one K tile: 17,152 B
+constexpr float kLazy = 8.0f;              // log2 headroom of the lazy softmax reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -89,11 +91,10 @@ __device__ __forceinline__ _Float16 bf16_to_f16(uint32_t b) { return (_Float16)_
 
 __device__ __forceinline__ uint32_t h2_bits(v2h v) { return *reinterpret_cast<uint32_t*>(&v); }
 
-// 8 E2M1 values of one code dword (channel 2i in the low nibble of byte i) times an E4M3
-// scale, as 4 packed fp16 pairs; exact
-__device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t codes, uint32_t scale_code) {
-  const _Float16 s = (_Float16)e4m3_val(scale_code);
-  const v2h ss = {s, s};
+// 8 E2M1 values of one code dword (channel 2i in the low nibble of byte i) times a group
+// scale given as an fp16 pair, as 4 packed fp16 pairs; exact (E2M1 x E4M3 has at most 6
+// significant bits and lies inside the fp16 range)
+__device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t codes, v2h ss) {
   return make_uint4(h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss),
                     h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss),
                     h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss),
@@ -108,7 +109,15 @@ __device__ __forceinline__ uint4 fp8x8_to_f16(uint32_t lo, uint32_t hi) {
                     h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true)));
 }
 
-__global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
+// raw bytes of one gather slot (one key, 64 channels): main = 32 B of codes (r[0..1]) and
+// 4 scale bytes (sc); window = 64 B of E4M3 (r[0..3]).  kind: 1 main, 2 window, 0 no key
+struct GatherSlot {
+  uint4 r[4];
+  uint32_t sc;
+  uint32_t kind;
+};
+
+__global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
   // ---- which (query, head group, split) this workgroup is; same query -> same XCD ----
   const int G = a.head_groups * a.nsplit;
   const int L = blockIdx.x;
@@ -120,13 +129,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
   const int split = rem / a.head_groups;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
-  const int gk = tid & 31, cb = tid >> 5;       // gather role: key of the tile, 64-channel block
-  const int rt = wave & 1, dh = wave >> 1;      // QK role: key half of the tile, channel half
+  const int pair = wave & (kPairs - 1), half = wave / kPairs;  // key stream, channel half
+  const int col = lane & 15, grp = lane >> 4;   // MFMA: column (head), lane group
+  const int gk = lane >> 2, cq = lane & 3;      // gather: key of the tile, 64-channel block
 
-  __shared__ __attribute__((aligned(16))) uint8_t kl[2][kKBuf];
-  __shared__ float sx[2][kSBuf];
-  __shared__ int s_valid[2][kT];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPairs * 2 * kTileBuf];
+  __shared__ int32_t s_idx[CSA2_MAX_TOPK];
+  __shared__ float s_ml[kPairs][kHG][2];
 
   const int seq = a.q_seq[q];
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
@@ -134,221 +143,256 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
   const int64_t lo = s > t - a.window + 1 ? s : t - a.window + 1;
   const int64_t n_swa = seq_ok && t >= lo ? t - lo + 1 : 0;
   const int64_t swa_b = seq_ok ? a.swa_base[seq] : 0;
+  // ring row of the first window key; later keys wrap at most once (window <= swa_cap)
+  int64_t r_lo = (lo - swa_b) % a.swa_cap;
+  r_lo = r_lo < 0 ? r_lo + a.swa_cap : r_lo;
+  const uint32_t win_row0 = (uint32_t)r_lo, swa_cap32 = (uint32_t)a.swa_cap;
   const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 2);
   const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 16);
   const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_cap * kD;
-  const int32_t* idxq = a.idx + (int64_t)q * a.k;
 
-  // ---- Q of head (hg*16 + col) as the fp16 B operand, 8 steps of 8 channels ----
-  // step (e, s4): channels 256*dh + 128*e + 32*g + 8*s4 .. +7 (same order as the K operand)
-  v8h qf[8];
+  // ---- Q of head (hg*16 + col) as the fp16 B operand: step s holds channels 32s + 8grp.. ----
+  v8h qf[16];
   {
-    const uint16_t* qp = a.q + ((int64_t)q * a.n_heads + hg * kHG + col) * kD + 256 * dh + 32 * g;
+    const uint16_t* qp = a.q + ((int64_t)q * a.n_heads + hg * kHG + col) * kD + 8 * grp;
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+    for (int st = 0; st < 16; ++st) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * st);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      v8h h;
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qp + 128 * e + 8 * s4);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        v8h h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h[2 * i] = bf16_to_f16(w4[i] & 0xffffu);
-          h[2 * i + 1] = bf16_to_f16(w4[i] >> 16);
-        }
-        qf[4 * e + s4] = h;
+      for (int i = 0; i < 4; ++i) {
+        h[2 * i] = bf16_to_f16(w4[i] & 0xffffu);
+        h[2 * i + 1] = bf16_to_f16(w4[i] >> 16);
       }
+      qf[st] = h;
+    }
   }
 
-  // position of this thread's gather key in a main tile (-1: none)
-  auto load_idx = [&](int tile) -> int32_t {
-    const int slot = tile * kT + gk;
-    return (seq_ok && tile < a.main_tiles && slot < a.k) ? idxq[slot] : -1;
-  };
-  // raw bytes of the gather key's 64 channels: main = 2 x 16 B codes + 4 scale bytes,
-  // window = 4 x 16 B of E4M3; r[4] = 0 marks "no key"
-  auto load_raw = [&](int tile, int32_t p, uint4 r[4], uint32_t& kind) {
-    kind = 0;
-    r[0] = r[1] = r[2] = r[3] = make_uint4(0u, 0u, 0u, 0u);
-    if (tile < a.main_tiles) {
-      if (p >= 0 && p < a.seq_cap) {
-        const uint4* c = reinterpret_cast<const uint4*>(kvc + (int64_t)p * (kD / 2) + cb * 32);
-        r[0] = c[0];
-        r[1] = c[1];
-        r[2].x = *reinterpret_cast<const uint32_t*>(kvs + (int64_t)p * (kD / 16) + cb * 4);
-        kind = 1;
-      }
-    } else {
-      const int64_t j = (int64_t)(tile - a.main_tiles) * kT + gk;
-      if (seq_ok && j < n_swa) {
-        int64_t row = (lo + j - swa_b) % a.swa_cap;
-        row = row < 0 ? row + a.swa_cap : row;
-        const uint4* c = reinterpret_cast<const uint4*>(swq + row * kD + cb * 64);
-        r[0] = c[0];
-        r[1] = c[1];
-        r[2] = c[2];
-        r[3] = c[3];
-        kind = 2;
-      }
+  // ---- this split's tiles and its slice of the index list (staged in LDS once) ----
+  const int tile_lo = split * a.tiles_per_split;
+  const int tile_hi = tile_lo + a.tiles_per_split < a.n_tiles ? tile_lo + a.tiles_per_split : a.n_tiles;
+  {
+    const int main_hi = a.main_tiles < tile_hi ? a.main_tiles : tile_hi;
+    const int n_keys = main_hi > tile_lo ? (main_hi - tile_lo) * kT : 0;
+    for (int i = tid; i < n_keys; i += kAttnThreads) {
+      const int slot = tile_lo * kT + i;
+      s_idx[i] = (seq_ok && slot < a.k) ? a.idx[(int64_t)q * a.k + slot] : -1;
     }
+  }
+  __syncthreads();
+
+  // Every gather load is unconditional, to an in-bounds address (an absent key reads row 0
+  // and is flagged), so no branch sits around the loads of the prefetch ring.  This wave
+  // fetches channels 256*half + 64*cq .. +63 of key gk.
+  auto load_slot = [&](int tile, bool real, GatherSlot& g) {
+    const bool is_main = tile < a.main_tiles;  // wave-uniform
+    const int32_t p = is_main ? s_idx[(tile - tile_lo) * kT + gk] : -1;
+    const bool ok_main = real && p >= 0 && p < a.seq_cap;
+    const uint32_t pm = ok_main ? (uint32_t)p : 0u;
+    const int j = (tile - a.main_tiles) * kT + gk;
+    const bool ok_win = real && seq_ok && j >= 0 && j < n_swa;
+    uint32_t row = win_row0 + (uint32_t)j;
+    row = ok_win ? (row >= swa_cap32 ? row - swa_cap32 : row) : 0u;
+    const uint32_t c0 = 256 * half + 64 * cq;   // first channel
+    // byte offsets fit 32 bits: seq_cap <= 2^24 rows of 256 B, swa_cap <= 2^23 rows of 512 B
+    const uint4* c = is_main ? reinterpret_cast<const uint4*>(kvc + (pm * (kD / 2) + c0 / 2))
+                             : reinterpret_cast<const uint4*>(swq + (row * kD + c0));
+    const uint4* c2 = is_main ? c : c + 2;  // main needs 32 B: the second pair re-reads them
+    g.r[0] = c[0];
+    g.r[1] = c[1];
+    g.r[2] = c2[0];
+    g.r[3] = c2[1];
+    g.sc = *reinterpret_cast<const uint32_t*>(kvs + (pm * (kD / 16) + c0 / 16));
+    g.kind = is_main ? (ok_main ? 1u : 0u) : (ok_win ? 2u : 0u);
+  };
+
+  // dequantise the slot's 64 channels into K tile `buf` of this pair; returns the tile's
+  // key-valid mask (bit 4*key)
+  auto store_slot = [&](const GatherSlot& g, uint8_t* tb) -> uint64_t {
+    uint4* dst = reinterpret_cast<uint4*>(tb + gk * kKRow + (256 * half + 64 * cq) * 2);
+    if (g.kind == 1) {
+      const uint32_t cw[8] = {g.r[0].x, g.r[0].y, g.r[0].z, g.r[0].w, g.r[1].x, g.r[1].y, g.r[1].z, g.r[1].w};
+      // the four E4M3 group scales to fp16 with the hardware convert (exact)
+      const v2h s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(g.sc, 1.0f, false);
+      const v2h s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(g.sc, 1.0f, true);
+      const v2h ss[4] = {__builtin_shufflevector(s01, s01, 0, 0), __builtin_shufflevector(s01, s01, 1, 1),
+                         __builtin_shufflevector(s23, s23, 0, 0), __builtin_shufflevector(s23, s23, 1, 1)};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i] = fp4x8_to_f16(cw[i], ss[i >> 1]);
+    } else if (g.kind == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dst[2 * i] = fp8x8_to_f16(g.r[i].x, g.r[i].y);
+        dst[2 * i + 1] = fp8x8_to_f16(g.r[i].z, g.r[i].w);
+      }
+    } else {  // no key: zeros (its logit is masked)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return __ballot(g.kind != 0);
   };
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
-  v4f o[8];
+  v4f o[kDT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kDT; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int tile_lo = split * a.tiles_per_split;
-  int tile_hi = tile_lo + a.tiles_per_split;
-  tile_hi = tile_hi < a.n_tiles ? tile_hi : a.n_tiles;
-
-  uint4 raw[4], raw_n[4];
-  uint32_t kind = 0, kind_n = 0;
-  int32_t p_next = -1;
-  if (tile_lo < tile_hi) {
-    load_raw(tile_lo, load_idx(tile_lo), raw, kind);
-    if (tile_lo + 1 < tile_hi) p_next = load_idx(tile_lo + 1);
-  }
-
-  for (int tile = tile_lo; tile < tile_hi; ++tile) {
-    const int buf = (tile - tile_lo) & 1;
-    int32_t p_after = -1;
-    if (tile + 1 < tile_hi) load_raw(tile + 1, p_next, raw_n, kind_n);
-    if (tile + 2 < tile_hi) p_after = load_idx(tile + 2);
-
-    // ---- gather: dequantise 64 channels of one key into the K tile ----
-    {
-      uint4 h[8];
-      if (kind == 1) {
-        const uint32_t cw[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+  // one tile: S^T = K Q^T over all 512 channels (both waves of the pair, identical), online
+  // softmax, O^T += V^T P^T over this wave's 256 channels
+  auto compute_tile = [&](const uint8_t* tb, uint64_t valid) {
+    v4f sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* kr = tb + col * kKRow + 16 * grp;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = fp4x8_to_f16(cw[i], (raw[2].x >> (8 * (i >> 1))) & 255u);
-      } else {
-        // window bytes (or zeros for an empty slot: E4M3 0x00 is +0)
-        const uint32_t bw[16] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w,
-                                 raw[2].x, raw[2].y, raw[2].z, raw[2].w, raw[3].x, raw[3].y, raw[3].z, raw[3].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = fp8x8_to_f16(bw[2 * i], bw[2 * i + 1]);
-      }
-      uint4* dst = reinterpret_cast<uint4*>(&kl[buf][gk * kKRow + cb * 128]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = h[i];
-      if (cb == 0) s_valid[buf][gk] = kind != 0;
+    for (int st = 0; st < 16; st += 2) {
+      const v8h k0 = *reinterpret_cast<const v8h*>(kr + 64 * st);
+      const v8h k1 = *reinterpret_cast<const v8h*>(kr + 64 * (st + 1));
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st + 1], sb, 0, 0, 0);
     }
-    __syncthreads();
-
-    // ---- QK role: partial S^T over one channel half ----
-    {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* kr = &kl[buf][(16 * rt + col) * kKRow + (256 * dh + 32 * g) * 2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const v8h av = *reinterpret_cast<const v8h*>(kr + (128 * e + 8 * s4) * 2);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qf[4 * e + s4], acc, 0, 0, 0);
-        }
-      // lane holds S^T[key 16*rt + 4*g + r][head col] for this channel half
-      float* sp = &sx[buf][(dh * kT + 16 * rt + 4 * g) * kSRow + col];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sp[r * kSRow] = acc[r];
-    }
-    __syncthreads();
-
-    // ---- softmax over the tile's 32 keys for head col (all waves, same statistics) ----
-    float x[8];
+    // lane: head col, keys 4*grp + r; the two halves of a key's valid bits come from the
+    // pair's two waves, which gathered the same keys
+    float x[4];
     float mt = -__builtin_inff();
 #pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) {
-      const int key = 8 * g + e8;
-      const float sv = sx[buf][key * kSRow + col] + sx[buf][(kT + key) * kSRow + col];
-      const float xv = s_valid[buf][key] ? sv * a.scale_log2 : -__builtin_inff();
-      x[e8] = xv;
-      mt = fmaxf(mt, xv);
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = (valid >> (4 * (4 * grp + r))) & 1ull;
+      x[r] = ok ? (sa[r] + sb[r]) * a.scale_log2 : -__builtin_inff();
+      mt = fmaxf(mt, x[r]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
+    // Lazy rescaling: m_run is a reference, not necessarily the running maximum.  It moves
+    // only when a logit exceeds it by more than 2^kLazy (or on the first key), so
+    // p = 2^(x - m_run) <= 2^kLazy stays far inside fp16 and the accumulators, which live in
+    // AGPRs, are rescaled only rarely.  The softmax is invariant to the reference.
+    const bool first = m_run == -__builtin_inff();
+    const bool move = first ? mt != -__builtin_inff() : mt > m_run + kLazy;
+    const float m_new = move ? mt : m_run;
+    const float alpha = (move && !first) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     const bool none = m_new == -__builtin_inff();
-    const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    v4h pb;
     float psum = 0.f;
-    v8h pb;
 #pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) {
-      const float p = none ? 0.0f : __builtin_amdgcn_exp2f(x[e8] - m_new);
-      psum += p;
-      pb[e8] = (_Float16)p;
+    for (int r = 0; r < 4; ++r) {
+      const float pr = none ? 0.0f : __builtin_amdgcn_exp2f(x[r] - m_new);
+      psum += pr;
+      pb[r] = (_Float16)pr;
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
     if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < kDT; ++dt) o[dt] *= alpha;
     }
+    // A = V^T (16 channels x 16 keys): in each 16-lane group (keys 4grp..4grp+3), lane
+    // 4a+b receives element b of the 8-byte reads of lanes a, a+4, a+8, a+12, so lane r of
+    // the group points at channels 4*(r & 3).. of key 4*grp + (r >> 2)
+    const __attribute__((address_space(3))) uint8_t* vb =
+        (const __attribute__((address_space(3))) uint8_t*)tb + (4 * grp + (col >> 2)) * kKRow + 8 * (col & 3) +
+        512 * half;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) {
+      const v4h av = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + 32 * dt)));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, o[dt], 0, 0, 0);
+    }
+  };
 
-    // ---- O^T += V^T P^T for this wave's 128 channels; V^T via transposing LDS reads ----
-    // lane (c, g) needs V[keys 8g..8g+7][channel c]; in its 16-lane group, lane 4a+b gets
-    // element b of the 8-byte chunks of lanes a, a+4, a+8, a+12, so lane r of the group points
-    // at channels 4*(r & 3).. of key (r >> 2).
+  // ---- this pair's tiles: tile_lo + pair + 4i; every wave runs the same number of steps
+  // (the workgroup barrier of each step), masking steps past its pair's end ----
+  const int span = tile_hi - tile_lo;
+  const int n_steps = (span + kPairs - 1) / kPairs;
+  const int n_my = span > pair ? (span - pair + kPairs - 1) / kPairs : 0;
+  auto my_tile = [&](int i) { return tile_lo + pair + kPairs * (i < n_my ? i : (n_my > 0 ? n_my - 1 : 0)); };
+  uint8_t* pbuf = kbuf + pair * 2 * kTileBuf;
+  GatherSlot g0, g1;
+  load_slot(my_tile(0), 0 < n_my, g0);
+  load_slot(my_tile(1), 1 < n_my, g1);
+  // One barrier per step: the pair writes tile i into buffer i&1, meets at the barrier,
+  // then both waves read it.  Buffer i&1 was last read in step i-2, which every wave has
+  // finished before it reaches the barrier of step i-1.
+  for (int i = 0; i < n_steps; i += 2) {
     {
-      const int kq = col >> 2, cq = col & 3;
-      const __attribute__((address_space(3))) uint8_t* kb =
-          (const __attribute__((address_space(3))) uint8_t*)&kl[buf][0];
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int ch = 128 * wave + 16 * dt + 4 * cq;
-        // whole-vector casts: building the operand element by element from the i16 lanes
-        // was observed to lose the upper dword of each read in this compiler
-        const v4h h0 = __builtin_bit_cast(
-            v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(kb + (8 * g + kq) * kKRow + ch * 2)));
-        const v4h h1 = __builtin_bit_cast(
-            v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(kb + (8 * g + 4 + kq) * kKRow + ch * 2)));
-        const v8h av = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, o[dt], 0, 0, 0);
-      }
+      uint8_t* tb = pbuf;
+      const uint64_t valid = store_slot(g0, tb);
+      load_slot(my_tile(i + 2), i + 2 < n_my, g0);
+      __syncthreads();
+      compute_tile(tb, valid);
     }
-
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = raw_n[i];
-    kind = kind_n;
-    p_next = p_after;
+    if (i + 1 < n_steps) {  // uniform over the workgroup
+      uint8_t* tb = pbuf + kTileBuf;
+      const uint64_t valid = store_slot(g1, tb);
+      load_slot(my_tile(i + 3), i + 3 < n_my, g1);
+      __syncthreads();
+      compute_tile(tb, valid);
+    }
   }
 
+  // ---- merge the four pairs' (O, m, l); the two waves of a pair hold the same (m, l) ----
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot = l_tot + __shfl_xor(l_tot, 32);
+  if (half == 0 && lane < kHG) {
+    s_ml[pair][lane][0] = m_run;
+    s_ml[pair][lane][1] = l_tot;
+  }
+  __syncthreads();  // every wave is past its loop: the K buffers are free
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int w = 0; w < kPairs; ++w) M = fmaxf(M, s_ml[w][col][0]);
+  float Ltot = 0.0f, mine = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kPairs; ++w) {
+    const float mw = s_ml[w][col][0];
+    const float sw = mw == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+    Ltot += sw * s_ml[w][col][1];
+    mine = w == pair ? sw : mine;
+  }
   const int head = hg * kHG + col;
-  const int ch0 = 128 * wave + 4 * g;
-
-  if (a.nsplit == 1) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const int64_t ob = ((int64_t)q * a.n_heads + head) * kD + ch0;
-    if (a.out_dtype == CSA2_DT_F32) {
-      float* out = reinterpret_cast<float*>(a.out) + ob;
+  const float inv = Ltot > 0.0f ? 1.0f / Ltot : 0.0f;
+  float4* part = reinterpret_cast<float4*>(kbuf);   // [half][pair][16 blocks][64 lanes]: 128 KB
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<float4*>(out + 16 * dt) =
-            make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-    } else {
-      uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ob;
+  for (int b = 0; b < kDT; ++b) {
+    const v4f v = o[b] * mine;
+    part[((half * kPairs + pair) * kDT + b) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  __syncthreads();
+  // wave w sums blocks 4*(w % 4) .. +3 of channel half w / 4 over the four pairs
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        uint2 pk;
-        pk.x = f32_to_bf16_rne(o[dt][0] * inv) | (f32_to_bf16_rne(o[dt][1] * inv) << 16);
-        pk.y = f32_to_bf16_rne(o[dt][2] * inv) | (f32_to_bf16_rne(o[dt][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(out + 16 * dt) = pk;
-      }
+  for (int bb = 0; bb < 4; ++bb) {
+    const int b = 4 * pair + bb;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kPairs; ++w) {
+      const float4 v = part[((half * kPairs + w) * kDT + b) * 64 + lane];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
     }
-    if (a.lse && wave == 0 && g == 0)
-      a.lse[(int64_t)q * a.n_heads + head] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
-  } else {
-    const int64_t pbase = ((int64_t)split * a.n_q + q) * a.n_heads + head;
-    float* wo = a.ws_o + pbase * kD + ch0;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(wo + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (wave == 0 && g == 0) {
-      a.ws_ml[pbase * 2] = m_run;
-      a.ws_ml[pbase * 2 + 1] = l_tot;
+    const int ch = 256 * half + 16 * b + 4 * grp;   // channels ch..ch+3 of head col
+    if (a.nsplit == 1) {
+      const int64_t ob = ((int64_t)q * a.n_heads + head) * kD + ch;
+      if (a.out_dtype == CSA2_DT_F32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + ob) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      } else {
+        uint2 pk;
+        pk.x = f32_to_bf16_rne(acc.x * inv) | (f32_to_bf16_rne(acc.y * inv) << 16);
+        pk.y = f32_to_bf16_rne(acc.z * inv) | (f32_to_bf16_rne(acc.w * inv) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + ob) = pk;
+      }
+    } else {
+      const int64_t pb = ((int64_t)split * a.n_q + q) * a.n_heads + head;
+      *reinterpret_cast<float4*>(a.ws_o + pb * kD + ch) = acc;
+    }
+  }
+  if (wave == 0 && lane < kHG) {
+    if (a.nsplit == 1) {
+      if (a.lse) a.lse[(int64_t)q * a.n_heads + head] = Ltot > 0.0f ? (M + __log2f(Ltot)) * kLn2 : -__builtin_inff();
+    } else {
+      const int64_t pb = ((int64_t)split * a.n_q + q) * a.n_heads + head;
+      a.ws_ml[pb * 2] = M;
+      a.ws_ml[pb * 2 + 1] = Ltot;
     }
   }
 }
@@ -394,7 +438,9 @@ struct AttnPlan {
   int64_t grid;
 };
 
-// Split the key list only when (query, head group) pairs alone cannot fill the 256 CUs.
+// One workgroup per CU (its four waves fill the four SIMDs): split the key list only when
+// (query, head group) pairs alone cannot fill the 256 CUs, keeping at least one tile per
+// wave in every split.
 static AttnPlan plan(int n_q, int n_heads, int k, int window) {
   AttnPlan p;
   p.head_groups = n_heads / kHG;
@@ -402,7 +448,8 @@ static AttnPlan plan(int n_q, int n_heads, int k, int window) {
   p.n_tiles = p.main_tiles + (window + kT - 1) / kT;
   const int64_t base = (int64_t)n_q * p.head_groups;
   int want = (int)((256 + base - 1) / (base > 0 ? base : 1));
-  want = want < 1 ? 1 : (want > p.n_tiles ? p.n_tiles : want);
+  const int max_split = (p.n_tiles + kPairs - 1) / kPairs;
+  want = want < 1 ? 1 : (want > max_split ? max_split : want);
   p.tiles_per_split = (p.n_tiles + want - 1) / want;
   p.nsplit = (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   const int64_t q_pad = ((int64_t)n_q + 7) / 8 * 8;
@@ -430,11 +477,13 @@ extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, co
   if (!q || !kv_codes || !kv_scales || !q_seq || !swa || !swa_base || !q_pos || !replay_start || !out)
     return CSA2_ERR_NULL;
   if (k > 0 && !idx) return CSA2_ERR_NULL;
-  if (n_q < 0 || n_heads < kHG || n_heads > 256 || n_heads % kHG || dim != kD || seq_cap < 0 || n_seq < 1 ||
-      k < 0 || k > CSA2_MAX_TOPK || window < 1 || window > CSA2_MAX_WINDOW || swa_cap < window)
+  if (n_q < 0 || n_heads < kHG || n_heads > 256 || n_heads % kHG || dim != kD || seq_cap < 0 ||
+      seq_cap > CSA2_MAX_ATTN_ENTRIES || n_seq < 1 || k < 0 || k > CSA2_MAX_TOPK || window < 1 ||
+      window > CSA2_MAX_WINDOW || swa_cap < window || swa_cap > CSA2_MAX_WINDOW_ROWS)
     return CSA2_ERR_SHAPE;
   if (out_dtype != CSA2_DT_F32 && out_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(kv_codes) || !aligned16(swa) || !aligned16(out)) return CSA2_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(kv_codes) || !aligned16(swa) || !aligned16(out) || ((uintptr_t)kv_scales & 7))
+    return CSA2_ERR_SHAPE;
   if (n_q == 0) return CSA2_OK;
   AttnPlan p = plan(n_q, n_heads, k, window);
   if (p.grid > 0x7fffffffLL) return CSA2_ERR_SHAPE;

@@ -33,7 +33,8 @@
  *     in-kernel so that no access leaves the buffers the sizes describe.
  *   - Inputs are finite; NaN/Inf inputs are outside the contract.
  *   - Code arrays (codes, q_codes, k_codes, kv_codes, swa), q and out must start on a
- *     16-byte boundary (CSA2_ERR_SHAPE otherwise); row sizes keep every row aligned.
+ *     16-byte boundary and kv_scales on an 8-byte one (CSA2_ERR_SHAPE otherwise); row
+ *     sizes keep every row aligned.
  *
  * Layouts (row-major, contiguous):
  *   main-KV cache   kv_codes  [n_seq, seq_cap, D/2]  E2M1 pairs, channel 2i in the low
@@ -82,6 +83,8 @@ extern "C" {
 #define CSA2_MAX_INDEX_ENTRIES (1 << 26)  /* seq_cap of csa2_index_score / csa2_index_topk */
 #define CSA2_MAIN_DIM 512          /* D of csa2_sparse_attn */
 #define CSA2_MAX_WINDOW 1024       /* window of csa2_sparse_attn */
+#define CSA2_MAX_ATTN_ENTRIES (1 << 24)   /* seq_cap of csa2_sparse_attn */
+#define CSA2_MAX_WINDOW_ROWS (1 << 23)    /* swa_cap of csa2_sparse_attn */
 
 /* Library version (major*10000 + minor*100 + patch). */
 int csa2_version(void);
@@ -248,7 +251,7 @@ size_t csa2_pool_workspace_bytes(int n_q, int64_t max_vis, int block, int max_bl
  *   idx       [n_q, k] int32 positions, any order, -1 (or any value outside
  *             [0, seq_cap)) = empty;  k in 0..2048
  *   swa       [n_seq, swa_cap, dim] E4M3; swa_base [n_seq] int64; window in 1..1024 and
- *             window <= swa_cap
+ *             window <= swa_cap <= CSA2_MAX_WINDOW_ROWS; seq_cap <= CSA2_MAX_ATTN_ENTRIES
  *   out       [n_q, n_heads, dim] f32 or bf16 (out_dtype); lse [n_q, n_heads] f32 or NULL
  *   Workspace: csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window).
  * Arithmetic: Q.K and P.V on fp16 matrix cores with fp32 accumulation.  Every key/value
