@@ -300,6 +300,53 @@ def measure_layers(name, steps, warmup, torch, C, layers_to_time):
     return res
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_score_select_c2_128k_traffic.md")
+TRAFFIC_SOURCES = ("fp4_kv_cache_layer_amd/csrc/score.hip", "fp4_kv_cache_layer_amd/csrc/select.h",
+                   "fp4_kv_cache_layer_amd/csrc/topk.hip", "fp4_kv_cache_layer_amd/build.py")
+COPY_BYTES = 1 << 30   # the calibration copy: 1 GiB read + 1 GiB written
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per csa2_index_topk call from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE runs, scaled by the calibration copy), or None when the summary is missing or
+    the kernel sources changed since it was taken."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    vals = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(("digest:", "traffic_bytes:")))
+    if vals.get("digest", "").strip() != sources_digest():
+        return None
+    return int(vals["traffic_bytes"].strip())
+
+
+def pmc_run(torch, C):
+    """Workload of the counter runs: one plain 1 GiB device copy (the calibration of
+    FETCH_SIZE / WRITE_SIZE), then each call of the 64 x 128K Full step three times."""
+    from synth import workloads
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    lb = LayerBench(workloads.config("c2"), torch, C)
+    for name, fn in lb.calls(0).items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        log(f"pmc: {name} done")
+
+
 def mode_entry(wl, mode, ms):
     b = step_bytes(wl, mode)
     return {"query_tokens_per_s": round(wl.n_q / (ms / 1e3), 1), "us_per_layer_step": round(ms * 1e3, 2),
@@ -315,6 +362,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4)
     ap.add_argument("--cpu-reps", type=int, default=48)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="only run the workload of the FETCH_SIZE / WRITE_SIZE counter runs and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the CSA2 step is built and measured on a single MI355X "
@@ -325,6 +374,9 @@ def main():
     from fp4_kv_cache_layer_amd import csa2 as C
     C.csa2_init()
     torch.cuda.set_device(0)
+    if args.pmc_run:
+        pmc_run(torch, C)
+        return
 
     head = measure_layers("c2", args.steps, args.warmup, torch, C, [0])
     wl = head["wl"]
@@ -356,7 +408,8 @@ def main():
         "hbm_frac_step": round(step_bytes(wl, "full") / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": "csa2_index_topk (k_score_select + last selection level)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": sb, "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": sb,
+                     "traffic": measured_traffic()},
     }
     if not args.no_modes:
         modes = {}

@@ -23,9 +23,17 @@ FLAGS = [
 ]
 
 
+# Per-file extras.  The scoring kernels keep their few MFMA accumulators in ordinary VGPRs:
+# accumulation registers would count against the same register file and cost the fused
+# kernel its fourth workgroup per CU.
+FILE_FLAGS = {
+    "score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -216,6 +216,32 @@ def test_index_topk_fused(C, k):
         G.topk_accept(gi[qi], int(gc[qi]), pos, ref, k)
 
 
+def test_index_topk_repeated_calls_share_workspace(C):
+    """Back-to-back calls on one workspace, with pool calls (which lay the workspace out
+    differently) in between, give identical results."""
+    _say("index_topk repeated")
+    case = _score_case(52, 2, 50000, [50000, 24577, 9000], 16)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq, n_vis_t, _, _ = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, max_blocks=64)
+    st.quantize_index_q(q_idx)
+    st.pool.copy_(torch.arange(64, dtype=torch.int32, device="cuda").repeat(wl.n_q, 1))
+    st.pool_count.fill_(64)
+    outs = []
+    for rep in range(3):
+        st.idx.fill_(99)
+        st.index_topk(caches, w, q_seq, n_vis_t)
+        outs.append(st.idx.clone())
+        st.index_topk(caches, w, q_seq, n_vis_t, in_pool=True)   # the pool path shares the workspace
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    (gi, gc), (ui, uc) = _run_index_topk(C, st, caches, w, q_seq, n_vis_t, 512)
+    assert np.array_equal(gi, ui) and np.array_equal(gc, uc) and np.array_equal(outs[0].cpu().numpy(), gi)
+
+
 def test_index_topk_fused_pool(C):
     _say("index_topk pool")
     case = _score_case(41, 2, 30000, [30000, 12000, 333], 16)
