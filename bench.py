@@ -85,16 +85,28 @@ class LayerBench:
             w = torch.from_numpy(wl.index_w(L)).to(dev)
             qa = torch.from_numpy(wl.attn_q_bits(L).view(np.int16)).to(dev).view(torch.bfloat16)
             self.inputs.append((q_idx, w, qa))
-        # the newest token of every sequence: its entry latents, written inside the step
-        first_new = int(wl.new_entries[0])
-        self.new_main = torch.from_numpy(np.stack([wl.main_latents(int(b), first_new, 1)[0] for b in wl.q_seq])).to(dev)
-        self.new_ik = torch.from_numpy(np.stack([wl.index_k_latents(int(b), first_new, 1)[0] for b in wl.q_seq])).to(dev)
+        first_new, n_new = int(wl.new_entries[0]), int(wl.new_entries[1])
+        if n_new == 1:
+            # decode: the newest token of every sequence, one entry and one window row each
+            ent_seq = wl.q_seq.astype(np.int64)
+            ent_row = np.full(wl.n_q, first_new, np.int64)
+            tok_seq, tok_pos = wl.q_seq.astype(np.int64), wl.q_pos
+        else:
+            # prefill chunk (one sequence): the chunk's entries and its new tokens' window rows
+            # (the replay rows' window entries are already cached)
+            ent_seq = np.zeros(n_new, np.int64)
+            ent_row = first_new + np.arange(n_new, dtype=np.int64)
+            new_tok = wl.q_pos >= first_new * wl.m
+            tok_seq, tok_pos = wl.q_seq[new_tok].astype(np.int64), wl.q_pos[new_tok]
+        self.new_main = torch.from_numpy(np.stack([wl.main_latents(int(b), int(r), 1)[0]
+                                                   for b, r in zip(ent_seq, ent_row)])).to(dev)
+        self.new_ik = torch.from_numpy(np.stack([wl.index_k_latents(int(b), int(r), 1)[0]
+                                                 for b, r in zip(ent_seq, ent_row)])).to(dev)
         self.new_swa = [torch.from_numpy(np.stack([wl.swa_latents(L, int(b), int(t), 1)[0]
-                                                   for b, t in zip(wl.q_seq, wl.q_pos)])).to(dev)
+                                                   for b, t in zip(tok_seq, tok_pos)])).to(dev)
                         for L in range(n_layers)]
-        self.dst_entry = torch.from_numpy(wl.q_seq.astype(np.int64) * wl.seq_cap + first_new).to(dev)
-        self.dst_swa = torch.from_numpy(wl.q_seq.astype(np.int64) * wl.swa_cap +
-                                        (wl.q_pos - wl.swa_base) % wl.swa_cap).to(dev)
+        self.dst_entry = torch.from_numpy(ent_seq * wl.seq_cap + ent_row).to(dev)
+        self.dst_swa = torch.from_numpy(tok_seq * wl.swa_cap + (tok_pos - wl.swa_base) % wl.swa_cap).to(dev)
         self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap)
 
     def calls(self, L: int):
@@ -425,6 +437,13 @@ def main():
         n4 = len(r4["wl"].layers)
         modes["group_1m"] = {"layers": list(r4["wl"].layers), "us_per_group": round(r4["group_ms"] * 1e3, 2),
                              "query_tokens_per_s_per_layer": round(r4["wl"].n_q * n4 / (r4["group_ms"] / 1e3), 1)}
+        r5 = measure_layers("c5", max(args.steps // 5, 3), max(args.warmup // 5, 1), torch, C, [0])
+        wl5, ms5 = r5["wl"], r5["layers"][0]["ms"]
+        rows = int(wl5.extra["counted_rows"])
+        modes["prefill_chunk_m2"] = {"query_rows": wl5.n_q, "counted_new_tokens": rows,
+                                     "us_per_chunk": round(ms5 * 1e3, 1),
+                                     "new_tokens_per_s": round(rows / (ms5 / 1e3), 1),
+                                     "isolated_launch_us": {k: round(v * 1000, 1) for k, v in r5["isolated"].items()}}
         result["modes"] = modes
         for k, v in modes.items():
             log(f"  {k}: {v}")

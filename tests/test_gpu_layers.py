@@ -40,3 +40,22 @@ def test_layer_group_full_size(C, name, samples, fused):
         G.check_group_query(case, caches, snaps, qi)
     del caches, step
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_prefill_chunk_full_size(C):
+    """The m = 2 encoder prefill chunk: 4,096 new tokens after a 262,144-token prefix plus the
+    128 bounded-replay rows, one sequence of 133,120 entries, run as one Full layer; oracle
+    parity on replay rows (first, middle, last), the first new row, a middle and the last row."""
+    _say("prefill chunk")
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    wl = workloads.config("c5")
+    case = G.Case(wl, swa_layers=(0,))
+    caches = case.gpu_caches()
+    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap)
+    snaps = G.run_group_snapshots(case, step, caches)
+    for qi in (0, 63, 127, 128, 2100, wl.n_q - 1):
+        _say("  oracle query", qi, "t", int(wl.q_pos[qi]), "n_vis", int(wl.n_vis[qi]))
+        G.check_group_query(case, caches, snaps, qi)
+    del caches, step
+    torch.cuda.empty_cache()
