@@ -128,7 +128,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
   const int hg = rem % a.head_groups;
   const int split = rem / a.head_groups;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform over the wave; saying so keeps tile-level decisions scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave & (kPairs - 1), half = wave / kPairs;  // key stream, channel half
   const int col = lane & 15, grp = lane >> 4;   // MFMA: column (head), lane group
   const int gk = lane >> 2, cq = lane & 3;      // gather: key of the tile, 64-channel block
@@ -207,30 +209,32 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
     g.kind = is_main ? (ok_main ? 1u : 0u) : (ok_win ? 2u : 0u);
   };
 
-  // dequantise the slot's 64 channels into K tile `buf` of this pair; returns the tile's
-  // key-valid mask (bit 4*key)
-  auto store_slot = [&](const GatherSlot& g, uint8_t* tb) -> uint64_t {
+  // dequantise the slot's 64 channels into a K tile of this pair; returns the tile's
+  // key-valid mask (bit 4*key).  The tile's format is uniform over the wave (a tile holds
+  // main entries only or window keys only), so the only branch is a scalar one; an absent
+  // key's raw bytes are zeroed (E2M1 / E4M3 zero is +0) instead of branching per lane.
+  auto store_slot = [&](const GatherSlot& g, uint8_t* tb, bool is_main) -> uint64_t {
+    const bool ok = g.kind != 0;
+    const uint32_t keep = 0u - (uint32_t)ok;   // all ones for a key, zero otherwise (no branch)
     uint4* dst = reinterpret_cast<uint4*>(tb + gk * kKRow + (256 * half + 64 * cq) * 2);
-    if (g.kind == 1) {
+    if (is_main) {
       const uint32_t cw[8] = {g.r[0].x, g.r[0].y, g.r[0].z, g.r[0].w, g.r[1].x, g.r[1].y, g.r[1].z, g.r[1].w};
+      const uint32_t sc = g.sc & keep;   // a zero scale zeroes the whole key
       // the four E4M3 group scales to fp16 with the hardware convert (exact)
-      const v2h s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(g.sc, 1.0f, false);
-      const v2h s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(g.sc, 1.0f, true);
+      const v2h s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+      const v2h s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true);
       const v2h ss[4] = {__builtin_shufflevector(s01, s01, 0, 0), __builtin_shufflevector(s01, s01, 1, 1),
                          __builtin_shufflevector(s23, s23, 0, 0), __builtin_shufflevector(s23, s23, 1, 1)};
 #pragma unroll
       for (int i = 0; i < 8; ++i) dst[i] = fp4x8_to_f16(cw[i], ss[i >> 1]);
-    } else if (g.kind == 2) {
+    } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dst[2 * i] = fp8x8_to_f16(g.r[i].x, g.r[i].y);
-        dst[2 * i + 1] = fp8x8_to_f16(g.r[i].z, g.r[i].w);
+        dst[2 * i] = fp8x8_to_f16(g.r[i].x & keep, g.r[i].y & keep);
+        dst[2 * i + 1] = fp8x8_to_f16(g.r[i].z & keep, g.r[i].w & keep);
       }
-    } else {  // no key: zeros (its logit is masked)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = make_uint4(0u, 0u, 0u, 0u);
     }
-    return __ballot(g.kind != 0);
+    return __ballot(ok);
   };
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
@@ -305,26 +309,33 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
   const int n_my = span > pair ? (span - pair + kPairs - 1) / kPairs : 0;
   auto my_tile = [&](int i) { return tile_lo + pair + kPairs * (i < n_my ? i : (n_my > 0 ? n_my - 1 : 0)); };
   uint8_t* pbuf = kbuf + pair * 2 * kTileBuf;
+  uint8_t* buf0 = pbuf;
+  uint8_t* buf1 = pbuf + kTileBuf;
+  // Software pipeline, one barrier per step: step i computes tile i from one buffer while
+  // it dequantises tile i+1 into the other (independent work the compiler can interleave:
+  // converts and LDS writes beside the matrix-core chain).  Buffer b is written again two
+  // steps after it was read, and every wave has passed the barrier in between.  The raw
+  // bytes of tile i+3 are requested during step i.  Slots: at the start of an even step i,
+  // g1 holds tile i+1 and g0 tile i+2.
   GatherSlot g0, g1;
   load_slot(my_tile(0), 0 < n_my, g0);
   load_slot(my_tile(1), 1 < n_my, g1);
-  // One barrier per step: the pair writes tile i into buffer i&1, meets at the barrier,
-  // then both waves read it.  Buffer i&1 was last read in step i-2, which every wave has
-  // finished before it reaches the barrier of step i-1.
+  auto tile_is_main = [&](int i) { return my_tile(i) < a.main_tiles; };
+  uint64_t v0 = store_slot(g0, buf0, tile_is_main(0)), v1 = 0;
+  load_slot(my_tile(2), 2 < n_my, g0);
+  __syncthreads();
   for (int i = 0; i < n_steps; i += 2) {
-    {
-      uint8_t* tb = pbuf;
-      const uint64_t valid = store_slot(g0, tb);
-      load_slot(my_tile(i + 2), i + 2 < n_my, g0);
-      __syncthreads();
-      compute_tile(tb, valid);
-    }
+    v1 = store_slot(g1, buf1, tile_is_main(i + 1));  // tile i+1
+    load_slot(my_tile(i + 3), i + 3 < n_my, g1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile(buf0, v0);                        // tile i
+    __syncthreads();
     if (i + 1 < n_steps) {  // uniform over the workgroup
-      uint8_t* tb = pbuf + kTileBuf;
-      const uint64_t valid = store_slot(g1, tb);
-      load_slot(my_tile(i + 3), i + 3 < n_my, g1);
+      v0 = store_slot(g0, buf0, tile_is_main(i + 2));  // tile i+2
+      load_slot(my_tile(i + 4), i + 4 < n_my, g0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile(buf1, v1);                      // tile i+1
       __syncthreads();
-      compute_tile(tb, valid);
     }
   }
 
