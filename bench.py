@@ -127,9 +127,7 @@ class LayerBench:
         if "quantize_index_q" in names:
             out["quant_index_q"] = st.quantize_index_q(q_idx, bind=True)
         if mode == "full_pool":
-            out["score"] = st.score(c, w, self.q_seq, self.n_vis, bind=True)
-            out["topk"] = st.select(self.n_vis, bind=True)
-            out["build_pool"] = st.build_pool(self.n_vis, bind=True)
+            out["index_topk_pool"] = st.index_topk_build_pool(c, w, self.q_seq, self.n_vis, bind=True)
         elif mode != "reuse":
             out["index_topk"] = st.index_topk(c, w, self.q_seq, self.n_vis, mode == "reindex_pool", bind=True)
         out["attn"] = st.attend(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True)
@@ -161,7 +159,7 @@ class LayerBench:
             for name, fn in mc.items():
                 if name in self._SIDE or name == "quant_index_k":
                     continue
-                if name in ("index_topk", "score"):
+                if name in ("index_topk", "index_topk_pool"):
                     main.wait_stream(side2)
                 if name == "attn":
                     main.wait_stream(side)

@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
         "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp,
                              sz, vp], i32),
         "csa2_index_topk_workspace_bytes": ([i32, i64, i32, i32], sz),
+        "csa2_index_topk_pool": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp, i32, i32, vp, vp,
+                                  vp, sz, vp], i32),
+        "csa2_index_topk_pool_workspace_bytes": ([i32, i64, i32, i32, i32], sz),
         "csa2_topk": ([vp, i64, i32, vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_topk_workspace_bytes": ([i32, i64, i32], sz),
         "csa2_build_pool": ([vp, i64, i32, vp, i64, i32, i32, vp, vp, vp, sz, vp], i32),
@@ -206,6 +209,33 @@ def csa2_index_topk(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: in
         workspace = torch.empty(need, dtype=torch.uint8, device=q_codes.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
     return _run("csa2_index_topk", args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, _stream()),
+                _bind)
+
+
+def csa2_index_topk_pool_workspace_bytes(n_q: int, n_slots: int, k: int, block: int, max_blocks: int) -> int:
+    return int(lib().csa2_index_topk_pool_workspace_bytes(n_q, n_slots, k, block, max_blocks))
+
+
+def csa2_index_topk_pool(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, idx_out, count_out,
+                         blocks_out, blocks_count, block: int = 8, workspace=None, _bind: bool = False):
+    """Top-K and candidate pool in one scoring pass: the operands of csa2_index_score (no
+    pool) -> idx_out [n_q, k], count_out [n_q] (as csa2_topk) and blocks_out [n_q, max_blocks],
+    blocks_count [n_q] (as csa2_build_pool)."""
+    args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, block)
+    for t, name in ((idx_out, "idx_out"), (blocks_out, "blocks_out")):
+        _need(t, torch.int32, 2, name)
+    _need(count_out, torch.int32, 1, "count_out")
+    _need(blocks_count, torch.int32, 1, "blocks_count")
+    n_q = q_codes.shape[0]
+    max_blocks = blocks_out.shape[1]
+    if idx_out.shape != (n_q, k) or count_out.shape[0] != n_q or blocks_out.shape[0] != n_q or \
+            blocks_count.shape[0] != n_q:
+        raise ValueError("index_topk_pool: inconsistent output shapes")
+    need = csa2_index_topk_pool_workspace_bytes(n_q, max(n_slots, 1), k, block, max_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_codes.device)
+    return _run("csa2_index_topk_pool", args[:12] + (k, _p(idx_out), _p(count_out), block, max_blocks, _p(blocks_out),
+                                                     _p(blocks_count), _p(workspace), workspace.numel(), _stream()),
                 _bind)
 
 

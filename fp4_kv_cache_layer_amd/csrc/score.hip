@@ -60,6 +60,10 @@ struct ScoreArgs {
   // csa2_index_topk
   int k;
   uint64_t* keys_out;
+  // csa2_index_topk_pool: per-query maxima of the visible positions of each block of
+  // `block` positions ([n_q, bmax_stride] f32)
+  float* bmax;
+  int64_t bmax_stride;
   int32_t* idx_out;
   int32_t* count_out;
 };
@@ -228,7 +232,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
 // conflicts, no barrier needed) instead of registers, so the loop keeps the register
 // budget of the plain scoring kernel and four workgroups fit a CU; once the keys are back
 // in registers the same LDS holds the selection histograms.
-template <bool kPool, bool kFinal>
+//
+// kBlockMax: the segment also writes the maximum visible score of each of its blocks of
+// s.block positions (the pool's block scores), read from the parked scores before the
+// selection reuses that LDS.
+template <bool kPool, bool kFinal, bool kBlockMax>
 __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
   static_assert(kTkSeg >= kTkHistWords, "the score array doubles as the selection histograms");
   __shared__ __attribute__((aligned(16))) float park[kTkSeg];
@@ -240,8 +248,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
   uint64_t key[kTkEpt];
   QueryScorer<kPool> sc;
   const int c0 = seg * kTkSeg;
+  const bool seq_ok = sc.init(s, q);
   // workgroup-uniform condition: every thread reaches select_segment's barriers
-  if (sc.init(s, q) && sc.nv > 0 && c0 < sc.n_valid) {
+  if (seq_ok && sc.nv > 0 && c0 < sc.n_valid) {
     uint4 bc[4];
     int bs[4];
     sc.load_step(s, c0 + wave * kScoreStep, bc, bs);
@@ -268,6 +277,28 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
   } else {
 #pragma unroll
     for (int i = 0; i < kTkEpt; ++i) key[i] = 0ull;
+  }
+  if (kBlockMax) {
+    // block b of the segment is positions c0 + b*block .. +block-1: in the parked layout
+    // (candidate i*256 + t at park[i*256 + t]) that is `block` consecutive words, written by
+    // other threads
+    __syncthreads();
+    const int nb = kTkSeg / s.block;
+    const int nv = seq_ok ? sc.nv : 0;
+    const int64_t nb_q = ((int64_t)nv + s.block - 1) / s.block;   // blocks holding a visible entry
+    for (int b = tid; b < nb; b += kTkThreads) {
+      const int64_t gb = (int64_t)seg * nb + b;
+      if (gb >= s.bmax_stride) break;
+      float m = -__builtin_inff();
+      if (gb < nb_q) {
+        for (int j = 0; j < s.block; ++j) {
+          const int p = c0 + b * s.block + j;
+          if (p < nv) m = fmaxf(m, park[b * s.block + j]);
+        }
+      }
+      s.bmax[(int64_t)q * s.bmax_stride + gb] = m;
+    }
+    __syncthreads();  // the parked scores are read before select_segment reuses the LDS
   }
   select_segment<kFinal>(key, q, seg, gridDim.x, s.k, reinterpret_cast<uint32_t*>(park), s.keys_out, s.idx_out,
                          s.count_out);
@@ -417,8 +448,8 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
   a.idx_out = idx_out;
   a.count_out = count_out;
   dim3 grid((unsigned)segs[0], (unsigned)n_q), blk(kScoreThreads);
-  if (L == 1) hipLaunchKernelGGL((k_score_select<false, true>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((k_score_select<false, false>), grid, blk, 0, st, a);
+  if (L == 1) hipLaunchKernelGGL((k_score_select<false, true, false>), grid, blk, 0, st, a);
+  else hipLaunchKernelGGL((k_score_select<false, false, false>), grid, blk, 0, st, a);
   rc = csa2_check_launch();
   if (rc != CSA2_OK) return rc;
   TkArgs t = {};
@@ -428,4 +459,86 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
   t.idx_out = idx_out;
   t.count_out = count_out;
   return select_levels_after0(segs, L, t, n_q, bufA, bufB, st);
+}
+
+static size_t index_topk_pool_ws(int n_q, int64_t n_slots, int k, int block, int max_blocks, size_t* bmax_bytes,
+                                 size_t* sel_bytes) {
+  const int64_t nblk = (n_slots + block - 1) / block;
+  *bmax_bytes = (((size_t)n_q * nblk * sizeof(float)) + 255) & ~(size_t)255;
+  *sel_bytes = (ws_bytes(n_q, n_slots, k) + 255) & ~(size_t)255;
+  return 256 + *bmax_bytes + *sel_bytes + ws_bytes(n_q, nblk, max_blocks) + 256;
+}
+
+extern "C" size_t csa2_index_topk_pool_workspace_bytes(int n_q, int64_t n_slots, int k, int block, int max_blocks) {
+  if (n_q <= 0 || n_slots <= 0 || k < 1 || k > CSA2_MAX_TOPK || block < 1 || block > 64 || (block & (block - 1)) ||
+      max_blocks < 1 || max_blocks > CSA2_MAX_TOPK)
+    return 0;
+  size_t b, t;
+  return index_topk_pool_ws(n_q, n_slots, k, block, max_blocks, &b, &t);
+}
+
+extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                                    int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                                    int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k,
+                                    int32_t* idx_out, int32_t* count_out, int block, int max_blocks,
+                                    int32_t* blocks_out, int32_t* blocks_count, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  int64_t n_slots = 0;
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                            nullptr, nullptr, 0, 0, &n_slots);
+  if (rc != CSA2_OK) return rc;
+  if (!idx_out || !count_out || !blocks_out || !blocks_count) return CSA2_ERR_NULL;
+  if (n_q > 65535 || k < 1 || k > CSA2_MAX_TOPK || block < 1 || block > 64 || (block & (block - 1)) ||
+      max_blocks < 1 || max_blocks > CSA2_MAX_TOPK)
+    return CSA2_ERR_SHAPE;
+  if (n_q == 0) return CSA2_OK;
+  const int64_t n0 = n_slots < 1 ? 1 : n_slots;
+  int64_t segs[16];
+  const int L = plan_levels(n0, k, segs, 16);
+  if (L >= 16) return CSA2_ERR_SHAPE;
+  size_t bmax_bytes, sel_bytes;
+  const size_t need = index_topk_pool_ws(n_q, n0, k, block, max_blocks, &bmax_bytes, &sel_bytes);
+  if (need > workspace_bytes || !workspace) return CSA2_ERR_WORKSPACE;
+  uint8_t* w0 = (uint8_t*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  float* bmax = (float*)w0;
+  uint64_t* bufA = (uint64_t*)(w0 + bmax_bytes);
+  uint64_t* bufB = bufA + (size_t)k * n_q * segs[0];
+  uint8_t* pool_ws = w0 + bmax_bytes + sel_bytes;
+  const size_t pool_ws_bytes = workspace_bytes - (size_t)(pool_ws - (uint8_t*)workspace);
+  const int64_t nblk = (n0 + block - 1) / block;
+
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, nullptr,
+                          nullptr, block, 0, n_slots);
+  a.k = k;
+  a.keys_out = bufA;
+  a.idx_out = idx_out;
+  a.count_out = count_out;
+  a.bmax = bmax;
+  a.bmax_stride = nblk;
+  hipStream_t st = (hipStream_t)stream;
+  dim3 grid((unsigned)segs[0], (unsigned)n_q), blk(kScoreThreads);
+  if (L == 1) hipLaunchKernelGGL((k_score_select<false, true, true>), grid, blk, 0, st, a);
+  else hipLaunchKernelGGL((k_score_select<false, false, true>), grid, blk, 0, st, a);
+  rc = csa2_check_launch();
+  if (rc != CSA2_OK) return rc;
+  TkArgs t = {};
+  t.n_vis = n_vis;
+  t.max_vis = seq_cap;
+  t.k = k;
+  t.idx_out = idx_out;
+  t.count_out = count_out;
+  rc = select_levels_after0(segs, L, t, n_q, bufA, bufB, st);
+  if (rc != CSA2_OK) return rc;
+  // the pool: top max_blocks blocks by block maximum (ties to the lower block id)
+  TkArgs pa = {};
+  pa.scores = bmax;
+  pa.scores_stride = nblk;
+  pa.n_vis = n_vis;
+  pa.vis_div = block;
+  pa.max_vis = nblk;
+  pa.k = max_blocks;
+  pa.idx_out = blocks_out;
+  pa.count_out = blocks_count;
+  pa.n_slots = nblk;
+  return select_from_scores(pa, n_q, nblk, pool_ws, pool_ws_bytes, st);
 }

@@ -30,6 +30,9 @@ struct TkArgs {
   int32_t* count_out;            // final: [n_q]
   int k;
   int64_t n_slots;               // candidate slots per query at this level
+  int vis_div;                   // kFromScores without a slot map: candidates are the first
+                                 // ceil(n_vis / vis_div) scores (0 or 1: n_vis; block size
+                                 // when the scores are block maxima)
 };
 
 __device__ __forceinline__ uint32_t ord_f32(float f) {

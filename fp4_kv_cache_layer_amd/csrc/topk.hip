@@ -33,6 +33,7 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(TkArgs a) {
   const int K = a.k;
 
   int64_t nv = a.n_vis[q];
+  if (kMode == kFromScores && a.vis_div > 1) nv = nv > 0 ? (nv + a.vis_div - 1) / a.vis_div : 0;
   nv = nv < 0 ? 0 : (nv > a.max_vis ? a.max_vis : nv);
   const int64_t c0 = (int64_t)seg * kTkSeg;
 

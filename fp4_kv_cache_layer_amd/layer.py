@@ -47,10 +47,11 @@ def plan_group(modes, fused: bool = True) -> list:
             raise ValueError(f"layer {i}: reindex_pool needs a pool built by the group's Full layer")
         if m == "reuse":
             calls = ["attend"]
-        elif m == "full_pool":   # the pool ranks blocks by their max score: keep the score array
-            calls = ["quantize_index_q", "score", "select", "build_pool", "attend"]
+        elif m == "full_pool":
+            calls = (["quantize_index_q", "index_topk_pool", "attend"] if fused else
+                     ["quantize_index_q", "score", "select", "build_pool", "attend"])
         elif fused:
-            calls = ["quantize_index_q", "index_topk_pool" if m == "reindex_pool" else "index_topk", "attend"]
+            calls = ["quantize_index_q", "index_topk_in_pool" if m == "reindex_pool" else "index_topk", "attend"]
         else:
             pool = m == "reindex_pool"
             calls = ["quantize_index_q", "score_pool" if pool else "score", "select_pool" if pool else "select",
@@ -110,6 +111,9 @@ class Csa2Step:
         self.ws_index_topk = torch.empty(max(C.csa2_index_topk_workspace_bytes(n_q, max(seq_cap, 1), k),
                                              C.csa2_index_topk_workspace_bytes(n_q, max_blocks * block, k, True), 1),
                                          dtype=torch.uint8, **dev)
+        self.ws_index_topk_pool = torch.empty(
+            max(C.csa2_index_topk_pool_workspace_bytes(n_q, max(seq_cap, 1), k, block, max_blocks), 1),
+            dtype=torch.uint8, **dev)
         self.ws_pool = torch.empty(max(C.csa2_pool_workspace_bytes(n_q, max(seq_cap, 1), block, max_blocks), 1),
                                    dtype=torch.uint8, **dev)
         self.ws_attn = torch.empty(max(C.csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window), 1),
@@ -143,6 +147,12 @@ class Csa2Step:
                                  self.k, self.idx, self.count, self.ws_index_topk, pool[0], pool[1], self.block,
                                  _bind=bind)
 
+    def index_topk_build_pool(self, caches: Caches, w, q_seq, n_vis, bind=False):
+        """score + select + pool in one pass (the decoder's first Full layer)."""
+        return C.csa2_index_topk_pool(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq,
+                                      n_vis, self.k, self.idx, self.count, self.pool, self.pool_count, self.block,
+                                      self.ws_index_topk_pool, _bind=bind)
+
     def _score_select(self, caches, w, q_seq, n_vis, in_pool, bind):
         if self.fused:
             return [self.index_topk(caches, w, q_seq, n_vis, in_pool, bind)]
@@ -175,8 +185,10 @@ class Csa2Step:
             for name in names:
                 if name == "quantize_index_q":
                     c = self.quantize_index_q(q_index, bind)
-                elif name in ("index_topk", "index_topk_pool"):
-                    c = self.index_topk(caches, w, q_seq, n_vis, name.endswith("pool"), bind)
+                elif name == "index_topk_pool":
+                    c = self.index_topk_build_pool(caches, w, q_seq, n_vis, bind)
+                elif name in ("index_topk", "index_topk_in_pool"):
+                    c = self.index_topk(caches, w, q_seq, n_vis, name.endswith("in_pool"), bind)
                 elif name in ("score", "score_pool"):
                     c = self.score(caches, w, q_seq, n_vis, name.endswith("pool"), bind)
                 elif name in ("select", "select_pool"):
@@ -196,7 +208,9 @@ class Csa2Step:
     def full(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, make_pool=False,
              out=None, lse=None, bind=False):
         calls = [self.quantize_index_q(q_index_f32, bind)]
-        if make_pool:   # the pool ranks blocks by their max score: keep the score array
+        if make_pool and self.fused:
+            calls.append(self.index_topk_build_pool(caches, w, q_seq, n_vis, bind))
+        elif make_pool:
             calls += [self.score(caches, w, q_seq, n_vis, bind=bind), self.select(n_vis, bind=bind),
                       self.build_pool(n_vis, bind)]
         else:

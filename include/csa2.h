@@ -190,6 +190,30 @@ int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float
 size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_pool);
 
 /*
+ * csa2_index_topk_pool -- the decoder's first Full layer in one pass over the indexer-K
+ * cache: the Top-K of csa2_index_topk (no pool) and the candidate pool of
+ * csa2_build_pool over the same scores.  [W] "CSA2：跨层复用，能借就不自己算" (Top-K),
+ * "分层稀疏索引器" and Figure 5 (at most 2,048 blocks of 8 positions by max indexer score).
+ *
+ * Arguments up to n_vis are those of csa2_index_score without a pool; k, idx_out,
+ * count_out as csa2_topk; block (a power of two, 1..64), max_blocks (1..2048), blocks_out
+ * [n_q, max_blocks] and blocks_count [n_q] as csa2_build_pool.  Results are identical to
+ * csa2_index_score + csa2_topk + csa2_build_pool with the same arguments.  The scoring pass
+ * writes only each block's maximum visible score (4 B per block) besides the per-segment
+ * Top-K survivors.  A query whose q_seq is outside [0, n_seq) gets count 0 and a pool of
+ * its lowest visible block ids (all their scores are -inf).
+ *   Workspace: csa2_index_topk_pool_workspace_bytes(n_q, seq_cap, k, block, max_blocks).
+ * Errors: as csa2_index_topk; CSA2_ERR_SHAPE for block or max_blocks out of range.
+ */
+int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                         int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                         int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k,
+                         int32_t* idx_out, int32_t* count_out, int block, int max_blocks,
+                         int32_t* blocks_out, int32_t* blocks_count, void* workspace,
+                         size_t workspace_bytes, void* stream);
+size_t csa2_index_topk_pool_workspace_bytes(int n_q, int64_t n_slots, int k, int block, int max_blocks);
+
+/*
  * csa2_topk -- the k highest-scoring candidates of each query.
  * [W] "CSA2：跨层复用，能借就不自己算" (Top-K, K = 512).
  *

@@ -242,6 +242,45 @@ def test_index_topk_repeated_calls_share_workspace(C):
     assert np.array_equal(gi, ui) and np.array_equal(gc, uc) and np.array_equal(outs[0].cpu().numpy(), gi)
 
 
+@pytest.mark.parametrize("block,max_blocks,k", [(8, 2048, 512), (4, 100, 64), (16, 300, 2048)])
+def test_index_topk_with_pool_build(C, block, max_blocks, k):
+    """Top-K and pool from one scoring pass equal csa2_index_score + csa2_topk +
+    csa2_build_pool on the same inputs, exactly (ragged tails, blocks cut by n_vis, an
+    empty query)."""
+    _say("index_topk_pool", block, max_blocks, k)
+    n_vis = [40000, 8193, 1, 0, 16385, 20001, 7]
+    case = _score_case(60 + block, 3, 40000, n_vis, 16)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq, n_vis_t, _, _ = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, k=k, block=block, max_blocks=max_blocks)
+    st.quantize_index_q(q_idx)
+    idx_f = torch.full((wl.n_q, k), 77, dtype=torch.int32, device="cuda")
+    cnt_f = torch.full((wl.n_q,), 77, dtype=torch.int32, device="cuda")
+    blk_f = torch.full((wl.n_q, max_blocks), 77, dtype=torch.int32, device="cuda")
+    bc_f = torch.full((wl.n_q,), 77, dtype=torch.int32, device="cuda")
+    C.csa2_index_topk_pool(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis_t, k, idx_f,
+                           cnt_f, blk_f, bc_f, block)
+    st.score(caches, w, q_seq, n_vis_t)
+    idx_u = torch.empty(wl.n_q, k, dtype=torch.int32, device="cuda")
+    cnt_u = torch.empty(wl.n_q, dtype=torch.int32, device="cuda")
+    C.csa2_topk(st.scores, n_vis_t, st.seq_cap, k, idx_u, cnt_u)
+    blk_u = torch.empty(wl.n_q, max_blocks, dtype=torch.int32, device="cuda")
+    bc_u = torch.empty(wl.n_q, dtype=torch.int32, device="cuda")
+    C.csa2_build_pool(st.scores, n_vis_t, st.seq_cap, blk_u, bc_u, block)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx_u) and torch.equal(cnt_f, cnt_u)
+    assert torch.equal(blk_f, blk_u) and torch.equal(bc_f, bc_u)
+    for qi in (0, 4):
+        nv = int(wl.n_vis[qi])
+        qc, qs, wq, _ = case.oracle_query(0, qi)
+        _, ref = O.full_scores(qc, qs, wq, case.oracle_caches(int(wl.q_seq[qi])), nv)
+        bs = O.block_scores(ref, nv, block)
+        G.topk_accept(blk_f[qi].cpu().numpy(), int(bc_f[qi]), np.arange(bs.size), bs, max_blocks)
+
+
 def test_index_topk_fused_pool(C):
     _say("index_topk pool")
     case = _score_case(41, 2, 30000, [30000, 12000, 333], 16)

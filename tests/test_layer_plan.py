@@ -31,8 +31,11 @@ def test_model_schedule_groups_plan():
     dec = _groups(O.layer_schedule())[-1]
     dec = ["full_pool"] + ["reindex_pool" if m == "reindex" else m for m in dec[1:]]
     plan = plan_group(dec)
+    assert plan[0] == ["quantize_index_q", "index_topk_pool", "attend"]     # Top-K and pool in one pass
+    assert all(p == ["quantize_index_q", "index_topk_in_pool", "attend"] for m, p in zip(dec, plan)
+               if m == "reindex_pool")
+    plan = plan_group(dec, fused=False)
     assert "build_pool" in plan[0] and plan[0].index("build_pool") < plan[0].index("attend")
-    assert all(p == ["quantize_index_q", "index_topk_pool", "attend"] for m, p in zip(dec, plan) if m == "reindex_pool")
 
 
 def test_unfused_plan_keeps_two_calls():
