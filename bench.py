@@ -7,8 +7,7 @@ window entry), quantise the layer's indexer Q (MXFP4), score the candidates on t
 matrix cores and keep the Top-512 (Full: every visible entry; Reindex: the same cache
 with the layer's own indexer Q, inside the pool when there is one), and attend over the
 512 entries plus the 128-token window.  A Reuse layer only appends its window entry and
-attends with the borrowed index set.  The appends that only attention reads run on
-parallel graph branches.
+attends with the borrowed index set.  A step's quantisations run as one launch.
 
 Headline: the Full decode step of 64 queries x 131,072 entries (128K tokens at m=1), 64
 heads, 16 indexer heads; metric query tokens per second per layer.  Also reported (unless
@@ -115,17 +114,20 @@ class LayerBench:
         mode = self.wl.layers[L]
         flat = lambda t: t.view(-1, t.shape[2])
         out = {}
+        # the step's quantisations in one launch: the new entries (Full layers: main KV and
+        # indexer K; every layer: its window entry) and the layer's indexer Q
+        jobs = []
         if mode.startswith("full"):
-            out["quant_main"] = C.csa2_quantize_kv(self.new_main, C.FMT_NVFP4, flat(c.kv_codes), flat(c.kv_scales),
-                                                   self.dst_entry, _bind=True)
-            out["quant_index_k"] = C.csa2_quantize_kv(self.new_ik, C.FMT_MXFP4, flat(c.ik_codes), flat(c.ik_scales),
-                                                      self.dst_entry, _bind=True)
-        out["quant_swa"] = C.csa2_quantize_kv(self.new_swa[L], C.FMT_FP8, flat(c.swa[L]), None, self.dst_swa,
-                                              _bind=True)
+            jobs += [(self.new_main, C.FMT_NVFP4, flat(c.kv_codes), flat(c.kv_scales), self.dst_entry),
+                     (self.new_ik, C.FMT_MXFP4, flat(c.ik_codes), flat(c.ik_scales), self.dst_entry)]
+        jobs.append((self.new_swa[L], C.FMT_FP8, flat(c.swa[L]), None, self.dst_swa))
         q_idx, w, qa = self.inputs[L]
         names = self.plan[L]
         if "quantize_index_q" in names:
-            out["quant_index_q"] = st.quantize_index_q(q_idx, bind=True)
+            n_q, h, d = q_idx.shape
+            jobs.append((q_idx.view(n_q * h, d), C.FMT_MXFP4, st.qi_codes.view(n_q * h, d // 2),
+                         st.qi_scales.view(n_q * h, d // 32), None))
+        out["quantize"] = C.csa2_quantize_kv_multi(jobs, _bind=True)
         if mode == "full_pool":
             out["index_topk_pool"] = st.index_topk_build_pool(c, w, self.q_seq, self.n_vis, bind=True)
         elif mode != "reuse":
@@ -133,44 +135,17 @@ class LayerBench:
         out["attn"] = st.attend(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True)
         return out
 
-    # appends that only attention reads run on a side branch of the graph, the indexer-K
-    # append on a second one; both join before their first reader
-    _SIDE = ("quant_main", "quant_swa")
-
     def record(self, layers):
-        """Issues the steps of `layers` on the current stream with the appends on forked
-        streams (captured as parallel graph branches)."""
-        torch = self.torch
-        main = torch.cuda.current_stream()
+        """Issues the steps of `layers` on the current stream.  (Forking the appends onto
+        parallel graph branches was measured slower: the joins cost more than the overlap.)"""
         for L in layers:
-            side, side2 = self._side
-            side.wait_stream(main)
-            side2.wait_stream(main)
-            with torch.cuda.stream(side):
-                sc = self.calls(L)
-                for name in self._SIDE:
-                    if name in sc:
-                        sc[name]()
-            with torch.cuda.stream(side2):
-                s2 = self.calls(L)
-                if "quant_index_k" in s2:
-                    s2["quant_index_k"]()
-            mc = self.calls(L)
-            for name, fn in mc.items():
-                if name in self._SIDE or name == "quant_index_k":
-                    continue
-                if name in ("index_topk", "index_topk_pool"):
-                    main.wait_stream(side2)
-                if name == "attn":
-                    main.wait_stream(side)
-                    main.wait_stream(side2)
+            for fn in self.calls(L).values():
                 fn()
 
     def capture(self, layers):
         """One HIP graph of the steps of `layers`; three replays are checked bitwise against
         an eager run of the same calls."""
         torch = self.torch
-        self._side = (torch.cuda.Stream(), torch.cuda.Stream())
         # a Reuse layer reads the index set the previous scoring layer left: only the
         # attention outputs are outputs there
         scoring = any(self.wl.layers[L] != "reuse" for L in layers)

@@ -52,6 +52,7 @@ def lib() -> ctypes.CDLL:
         "csa2_status_string": ([i32], ctypes.c_char_p),
         "csa2_last_error": ([], ctypes.c_char_p),
         "csa2_quantize_kv": ([vp, i32, i64, i32, i32, vp, i64, vp, vp, vp], i32),
+        "csa2_quantize_kv_multi": ([vp, i32, vp], i32),
         "csa2_index_score": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64, vp],
                              i32),
         "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp,
@@ -122,13 +123,12 @@ def csa2_init():
     _check(lib().csa2_init(), "csa2_init")
 
 
-def csa2_quantize_kv(src, fmt: int, codes, scales=None, dst_row=None, _bind: bool = False):
-    """src [rows, dim] f32/bf16; codes [dst_rows, dim/2] (FP4) or [dst_rows, dim] (FP8) u8;
-    scales [dst_rows, dim/16 | dim/32] u8; dst_row [rows] int64 or None."""
+def _quant_args(src, fmt: int, codes, scales, dst_row, bind: bool):
+    """Checks one quantise job and returns its C arguments (src .. scales)."""
     if src.dtype not in (torch.float32, torch.bfloat16) or src.dim() != 2 or not src.is_cuda:
         raise TypeError("src must be a 2-D f32/bf16 device tensor")
     if not src.is_contiguous():
-        if _bind:
+        if bind:
             raise ValueError("src must be contiguous when binding a call")
         src = src.contiguous()
     rows, dim = src.shape
@@ -146,8 +146,31 @@ def csa2_quantize_kv(src, fmt: int, codes, scales=None, dst_row=None, _bind: boo
         if dst_row.shape[0] != rows:
             raise ValueError("dst_row length != rows")
     dt = DT_F32 if src.dtype == torch.float32 else DT_BF16
-    return _run("csa2_quantize_kv", (_p(src), dt, rows, dim, fmt, _p(dst_row), codes.shape[0], _p(codes),
-                                     _p(scales) if fmt != FMT_FP8 else None, _stream()), _bind)
+    return (_p(src), dt, rows, dim, fmt, _p(dst_row), codes.shape[0], _p(codes),
+            _p(scales) if fmt != FMT_FP8 else None)
+
+
+def csa2_quantize_kv(src, fmt: int, codes, scales=None, dst_row=None, _bind: bool = False):
+    """src [rows, dim] f32/bf16; codes [dst_rows, dim/2] (FP4) or [dst_rows, dim] (FP8) u8;
+    scales [dst_rows, dim/16 | dim/32] u8; dst_row [rows] int64 or None."""
+    return _run("csa2_quantize_kv", _quant_args(src, fmt, codes, scales, dst_row, _bind) + (_stream(),), _bind)
+
+
+class QuantJob(ctypes.Structure):
+    """csa2_quant_job of include/csa2.h."""
+    _fields_ = [("src", ctypes.c_void_p), ("src_dtype", ctypes.c_int), ("rows", ctypes.c_int64),
+                ("dim", ctypes.c_int), ("fmt", ctypes.c_int), ("dst_row", ctypes.c_void_p),
+                ("dst_rows", ctypes.c_int64), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+def csa2_quantize_kv_multi(jobs, _bind: bool = False):
+    """Several csa2_quantize_kv jobs in one launch; jobs = [(src, fmt, codes, scales, dst_row), ...]."""
+    if len(jobs) > 8:
+        raise ValueError("at most 8 jobs per launch")
+    arr = (QuantJob * max(len(jobs), 1))()
+    for i, (src, fmt, codes, scales, dst_row) in enumerate(jobs):
+        arr[i] = QuantJob(*_quant_args(src, fmt, codes, scales, dst_row, _bind))
+    return _run("csa2_quantize_kv_multi", (ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream()), _bind)
 
 
 def _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block):

@@ -74,11 +74,11 @@ __device__ __forceinline__ uint32_t load_bits<uint16_t>(const uint16_t* p, int64
 
 // ---- NVFP4: one thread per 16-channel group ----
 template <typename T>
-__global__ __launch_bounds__(256) void k_quant_nvfp4(const T* __restrict__ src, int64_t rows, int dim,
-                                                     const int64_t* __restrict__ dst_row, int64_t dst_rows,
-                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+__device__ __forceinline__ void quant_group_nvfp4(const T* __restrict__ src, int64_t rows, int dim,
+                                                  const int64_t* __restrict__ dst_row, int64_t dst_rows,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  int64_t gid) {
   const int gpr = dim / 16;
-  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= rows * gpr) return;
   int64_t r = gid / gpr;
   int g = (int)(gid % gpr);
@@ -109,11 +109,11 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(const T* __restrict__ src, 
 
 // ---- MXFP4: one thread per 32-channel group ----
 template <typename T>
-__global__ __launch_bounds__(256) void k_quant_mxfp4(const T* __restrict__ src, int64_t rows, int dim,
-                                                     const int64_t* __restrict__ dst_row, int64_t dst_rows,
-                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+__device__ __forceinline__ void quant_group_mxfp4(const T* __restrict__ src, int64_t rows, int dim,
+                                                  const int64_t* __restrict__ dst_row, int64_t dst_rows,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  int64_t gid) {
   const int gpr = dim / 32;
-  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= rows * gpr) return;
   int64_t r = gid / gpr;
   int g = (int)(gid % gpr);
@@ -154,11 +154,10 @@ __global__ __launch_bounds__(256) void k_quant_mxfp4(const T* __restrict__ src, 
 
 // ---- FP8 (E4M3, unscaled): one thread per 8 channels ----
 template <typename T>
-__global__ __launch_bounds__(256) void k_quant_fp8(const T* __restrict__ src, int64_t rows, int dim,
-                                                   const int64_t* __restrict__ dst_row, int64_t dst_rows,
-                                                   uint8_t* __restrict__ codes) {
+__device__ __forceinline__ void quant_group_fp8(const T* __restrict__ src, int64_t rows, int dim,
+                                                const int64_t* __restrict__ dst_row, int64_t dst_rows,
+                                                uint8_t* __restrict__ codes, int64_t gid) {
   const int gpr = dim / 8;
-  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= rows * gpr) return;
   int64_t r = gid / gpr;
   int g = (int)(gid % gpr);
@@ -175,6 +174,76 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const T* __restrict__ src, in
   *reinterpret_cast<uint2*>(codes + d * dim + g * 8) = make_uint2(lo, hi);
 }
 
+// one job of a (multi-)quantise launch
+struct QuantJob {
+  const void* src;
+  int64_t rows;
+  const int64_t* dst_row;
+  int64_t dst_rows;
+  uint8_t* codes;
+  uint8_t* scales;
+  int dim, fmt, bf16;
+  int64_t block0;   // first workgroup of this job
+};
+
+struct QuantJobs {
+  QuantJob job[CSA2_MAX_QUANT_JOBS];
+  int n;
+};
+
+__device__ __forceinline__ void quant_dispatch(const QuantJob& j, int64_t gid) {
+  if (j.fmt == CSA2_FMT_NVFP4) {
+    if (j.bf16) quant_group_nvfp4((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
+    else quant_group_nvfp4((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
+  } else if (j.fmt == CSA2_FMT_MXFP4) {
+    if (j.bf16) quant_group_mxfp4((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
+    else quant_group_mxfp4((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
+  } else {
+    if (j.bf16) quant_group_fp8((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, gid);
+    else quant_group_fp8((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, gid);
+  }
+}
+
+// Every job of the launch gets its own range of workgroups; a workgroup finds its job by the
+// (uniform) range its index falls in.
+__global__ __launch_bounds__(256) void k_quant(QuantJobs jobs) {
+  int j = 0;
+  for (int i = 1; i < jobs.n; ++i)
+    if ((int64_t)blockIdx.x >= jobs.job[i].block0) j = i;
+  const QuantJob& jb = jobs.job[j];
+  quant_dispatch(jb, ((int64_t)blockIdx.x - jb.block0) * blockDim.x + threadIdx.x);
+}
+
+static int make_job(const void* src, int src_dtype, int64_t rows, int dim, int fmt, const int64_t* dst_row,
+                    int64_t dst_rows, uint8_t* codes, uint8_t* scales, QuantJob* out, int64_t* blocks) {
+  if (fmt != CSA2_FMT_NVFP4 && fmt != CSA2_FMT_MXFP4 && fmt != CSA2_FMT_FP8) return CSA2_ERR_UNSUPPORTED;
+  if (src_dtype != CSA2_DT_F32 && src_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
+  if (rows != 0 && (!src || !codes || (fmt != CSA2_FMT_FP8 && !scales))) return CSA2_ERR_NULL;
+  const int group = fmt == CSA2_FMT_NVFP4 ? 16 : (fmt == CSA2_FMT_MXFP4 ? 32 : 8);
+  if (rows < 0 || dim <= 0 || dim > 8192 || dim % group || dst_rows < 0) return CSA2_ERR_SHAPE;
+  if (rows != 0 && !aligned16(codes)) return CSA2_ERR_SHAPE;
+  const int64_t work = rows * (dim / group);
+  *blocks = (work + 255) / 256;
+  if (*blocks > 0x7fffffff) return CSA2_ERR_SHAPE;
+  out->src = src;
+  out->rows = rows;
+  out->dst_row = dst_row;
+  out->dst_rows = dst_rows;
+  out->codes = codes;
+  out->scales = scales;
+  out->dim = dim;
+  out->fmt = fmt;
+  out->bf16 = src_dtype == CSA2_DT_BF16;
+  return CSA2_OK;
+}
+
+static int launch_jobs(QuantJobs& jobs, int64_t total_blocks, hipStream_t st) {
+  if (total_blocks == 0) return CSA2_OK;
+  if (total_blocks > 0x7fffffff) return CSA2_ERR_SHAPE;
+  hipLaunchKernelGGL(k_quant, dim3((unsigned)total_blocks), dim3(256), 0, st, jobs);
+  return csa2_check_launch();
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -182,28 +251,30 @@ using namespace csa2;
 extern "C" int csa2_quantize_kv(const void* src, int src_dtype, int64_t rows, int dim, int fmt,
                                 const int64_t* dst_row, int64_t dst_rows, uint8_t* codes,
                                 uint8_t* scales, void* stream) {
-  if (!src || !codes) return CSA2_ERR_NULL;
-  if (fmt != CSA2_FMT_NVFP4 && fmt != CSA2_FMT_MXFP4 && fmt != CSA2_FMT_FP8) return CSA2_ERR_UNSUPPORTED;
-  if (src_dtype != CSA2_DT_F32 && src_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
-  if (fmt != CSA2_FMT_FP8 && !scales) return CSA2_ERR_NULL;
-  int group = fmt == CSA2_FMT_NVFP4 ? 16 : (fmt == CSA2_FMT_MXFP4 ? 32 : 8);
-  if (rows < 0 || dim <= 0 || dim > 8192 || dim % group || dst_rows < 0) return CSA2_ERR_SHAPE;
-  if (!aligned16(codes)) return CSA2_ERR_SHAPE;
-  if (rows == 0) return CSA2_OK;
-  hipStream_t st = (hipStream_t)stream;
-  int64_t work = rows * (dim / group);
-  dim3 grid((unsigned)((work + 255) / 256)), block(256);
-  if (grid.x == 0 || (work + 255) / 256 > 0x7fffffff) return CSA2_ERR_SHAPE;
-  bool bf = src_dtype == CSA2_DT_BF16;
-  if (fmt == CSA2_FMT_NVFP4) {
-    if (bf) hipLaunchKernelGGL(k_quant_nvfp4<uint16_t>, grid, block, 0, st, (const uint16_t*)src, rows, dim, dst_row, dst_rows, codes, scales);
-    else hipLaunchKernelGGL(k_quant_nvfp4<float>, grid, block, 0, st, (const float*)src, rows, dim, dst_row, dst_rows, codes, scales);
-  } else if (fmt == CSA2_FMT_MXFP4) {
-    if (bf) hipLaunchKernelGGL(k_quant_mxfp4<uint16_t>, grid, block, 0, st, (const uint16_t*)src, rows, dim, dst_row, dst_rows, codes, scales);
-    else hipLaunchKernelGGL(k_quant_mxfp4<float>, grid, block, 0, st, (const float*)src, rows, dim, dst_row, dst_rows, codes, scales);
-  } else {
-    if (bf) hipLaunchKernelGGL(k_quant_fp8<uint16_t>, grid, block, 0, st, (const uint16_t*)src, rows, dim, dst_row, dst_rows, codes);
-    else hipLaunchKernelGGL(k_quant_fp8<float>, grid, block, 0, st, (const float*)src, rows, dim, dst_row, dst_rows, codes);
+  QuantJobs jobs = {};
+  int64_t blocks = 0;
+  const int rc = make_job(src, src_dtype, rows, dim, fmt, dst_row, dst_rows, codes, scales, &jobs.job[0], &blocks);
+  if (rc != CSA2_OK) return rc;
+  jobs.n = 1;
+  return launch_jobs(jobs, blocks, (hipStream_t)stream);
+}
+
+extern "C" int csa2_quantize_kv_multi(const csa2_quant_job* jobs, int n_jobs, void* stream) {
+  if (!jobs) return CSA2_ERR_NULL;
+  if (n_jobs < 0 || n_jobs > CSA2_MAX_QUANT_JOBS) return CSA2_ERR_SHAPE;
+  QuantJobs kj = {};
+  int64_t total = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    const csa2_quant_job& j = jobs[i];
+    int64_t blocks = 0;
+    QuantJob q;
+    const int rc = make_job(j.src, j.src_dtype, j.rows, j.dim, j.fmt, j.dst_row, j.dst_rows, j.codes, j.scales, &q,
+                            &blocks);
+    if (rc != CSA2_OK) return rc;
+    if (blocks == 0) continue;
+    q.block0 = total;
+    kj.job[kj.n++] = q;
+    total += blocks;
   }
-  return csa2_check_launch();
+  return launch_jobs(kj, total, (hipStream_t)stream);
 }

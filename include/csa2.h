@@ -121,11 +121,34 @@ const char* csa2_last_error(void);
  *   scales     [dst_rows, dim/16] (NVFP4) or [dst_rows, dim/32] (MXFP4); unused for FP8
  * Errors: NULL src/codes (or scales for FP4) -> CSA2_ERR_NULL; rows < 0, dim <= 0, dim not
  * a multiple of the group (16 / 32 / 8 for FP8) or dim > 8192 -> CSA2_ERR_SHAPE; unknown
- * fmt or src_dtype -> CSA2_ERR_UNSUPPORTED.  rows == 0 launches nothing.
+ * fmt or src_dtype -> CSA2_ERR_UNSUPPORTED.  rows == 0 launches nothing (src, codes and
+ * scales may then be NULL).
  */
 int csa2_quantize_kv(const void* src, int src_dtype, int64_t rows, int dim, int fmt,
                      const int64_t* dst_row, int64_t dst_rows, uint8_t* codes, uint8_t* scales,
                      void* stream);
+
+/*
+ * csa2_quantize_kv_multi -- several csa2_quantize_kv jobs in one launch (a decode step's
+ * appends: the new main-KV entry, indexer-K entry and window entry of every sequence, and
+ * the queries' indexer Q).  Each job has the arguments and semantics of csa2_quantize_kv.
+ *   jobs    host array of n_jobs descriptors, read during the call; n_jobs in 0..8.
+ * The jobs must not write overlapping destinations.  Errors: those of csa2_quantize_kv for
+ * any job (nothing is launched), CSA2_ERR_SHAPE for n_jobs out of range.
+ */
+#define CSA2_MAX_QUANT_JOBS 8
+typedef struct {
+  const void* src;
+  int src_dtype;
+  int64_t rows;
+  int dim;
+  int fmt;
+  const int64_t* dst_row;
+  int64_t dst_rows;
+  uint8_t* codes;
+  uint8_t* scales;
+} csa2_quant_job;
+int csa2_quantize_kv_multi(const csa2_quant_job* jobs, int n_jobs, void* stream);
 
 /*
  * csa2_index_score -- indexer scores of each query over its sequence's entries.

@@ -94,6 +94,39 @@ def test_quantize_bitexact(C, fmt, src_dt):
         assert np.all(gs[untouched] == 0xCD)
 
 
+def test_quantize_multi_matches_single_calls(C):
+    """One launch of several jobs (all formats, both input types, scatter rows, a job with no
+    rows) writes exactly what the same jobs do as separate calls."""
+    _say("quantize multi")
+    rng = np.random.default_rng(11)
+    mk = lambda r, d, dt: torch.from_numpy((rng.normal(size=(r, d)) * 3).astype(np.float32)).cuda().to(dt)
+    specs = [(C.FMT_NVFP4, 512, 70, torch.float32), (C.FMT_MXFP4, 128, 33, torch.bfloat16),
+             (C.FMT_FP8, 512, 50, torch.float32), (C.FMT_MXFP4, 2048, 9, torch.float32),
+             (C.FMT_NVFP4, 512, 0, torch.bfloat16)]
+    outs_a, outs_b, jobs_a = [], [], []
+    for fmt, dim, rows, dt in specs:
+        src = mk(rows, dim, dt)
+        dst_rows = rows + 7
+        dst = torch.from_numpy(rng.permutation(dst_rows)[:rows].astype(np.int64)).cuda()
+        per = dim if fmt == C.FMT_FP8 else dim // 2
+        g = {C.FMT_NVFP4: 16, C.FMT_MXFP4: 32, C.FMT_FP8: 1}[fmt]
+        pair = []
+        for _ in range(2):
+            codes = torch.full((dst_rows, per), 0x5A, dtype=torch.uint8, device="cuda")
+            scales = None if fmt == C.FMT_FP8 else torch.full((dst_rows, dim // g), 0xA5, dtype=torch.uint8,
+                                                              device="cuda")
+            pair.append((codes, scales))
+        C.csa2_quantize_kv(src, fmt, pair[0][0], pair[0][1], dst)
+        jobs_a.append((src, fmt, pair[1][0], pair[1][1], dst))
+        outs_a.append(pair[0])
+        outs_b.append(pair[1])
+    C.csa2_quantize_kv_multi(jobs_a)
+    torch.cuda.synchronize()
+    for (ca, sa), (cb, sb) in zip(outs_a, outs_b):
+        assert torch.equal(ca, cb)
+        assert (sa is None) == (sb is None) and (sa is None or torch.equal(sa, sb))
+
+
 def _score_case(seed, n_seq, seq_cap, n_vis, idx_heads):
     wl = G.workloads.Workload(
         name="small", seed=seed, n_seq=n_seq, seq_cap=seq_cap, m=1, heads=16, idx_heads=idx_heads,
