@@ -13,41 +13,46 @@
 // magnitudes round to fp16 subnormals (absolute error below 2^-25).  P = exp2(logit - max)
 // is rounded to fp16 (11 significant bits) for the P.V product.
 //
-// Decomposition: one workgroup = (query, 16 heads, slice of the key list), 4 waves, and
-// every wave works on its own keys: the key list is cut into tiles of 16 keys and wave w
-// takes tiles w, w+4, w+8, ... of the slice, keeping its own online-softmax state (m, l)
-// and its own O^T (512 channels x 16 heads, 32 MFMA accumulators).  Per tile a wave
-//   * gathers its 16 keys (lane = key x channel quarter: 64 B of E2M1 codes + 8 B of E4M3
-//     scales, or 128 B of window E4M3), dequantises them with the hardware FP4/FP8 -> fp16
-//     converts and an exact packed multiply by the group scale, and writes the 16 rows
-//     into its own LDS buffer (row stride 1,072 B: conflict-free for both reads below);
-//   * forms S^T = K Q^T (16 keys x 16 heads) with 16 V_MFMA_F32_16X16X32_F16, K read from
-//     LDS and Q held in registers;
-//   * updates (m, l) per head (m lazily: see compute_tile) and turns S^T into P^T in
-//     fp16: the accumulator layout of that MFMA (lane: head l%16, keys 4(l/16)..+3) is
-//     exactly the B-operand layout of V_MFMA_F32_16X16X16_F16, so P needs no shuffle;
-//   * accumulates O^T += V^T P^T with 32 of those, V^T read from the same K rows through
-//     DS_READ_B64_TR_B16 (each lane receives one channel of 4 keys).
-// No barrier is needed inside the loop (the buffer is the wave's own); the raw bytes of the
-// next two tiles are in flight while a tile is processed.  At the end the four waves merge
-// (O, m, l) with the log-sum-exp rule through LDS, 256 channels at a time.  The workgroups
-// of one query are numbered so that they land on the same XCD (dispatch is round-robin
-// over the 8 XCDs) and share its L2 for the gathered rows.  When a batch has too few
-// queries to fill the GPU, the key list is split over workgroups and a combine kernel
-// merges the partial (O, m, l).
+// Decomposition: one workgroup = (query, 16 heads, slice of the key list), 8 waves in four
+// pairs.  The key list is cut into tiles of 16 keys; pair p takes every fourth tile of the
+// slice (window tiles first, since their rows need no index), and the two waves of a pair
+// split the 512 channels into halves.  Per tile a wave
+//   * gathers its half of the 16 keys straight into registers (lane = key x 64 channels:
+//     32 B of E2M1 codes + 4 B of E4M3 scales, or 64 B of window E4M3), three tiles ahead;
+//   * dequantises them with the hardware FP4/FP8 -> fp16 converts and an exact packed
+//     multiply by the group scale, directly in the A-operand layout of
+//     V_MFMA_F32_16X16X32_F16, and forms the partial S^T = K Q^T over its 256 channels
+//     (Q held in registers in the same channel order);
+//   * writes the same fp16 values as its own V half-tile in LDS (row stride 528 B, double
+//     buffered);
+//   * adds its partner's partial S^T, exchanged through LDS with the one workgroup barrier
+//     of the step, so both waves hold the same S^T and run the same online softmax;
+//   * turns S^T into P^T in fp16: the accumulator layout of the QK MFMA (lane: head l%16,
+//     keys 4(l/16)..+3) is exactly the B-operand layout of V_MFMA_F32_16X16X16_F16, so P
+//     needs no shuffle; and accumulates O^T += V^T P^T over its 256 channels, V^T read from
+//     its V half-tile through DS_READ_B64_TR_B16 (each lane receives one channel of 4 keys).
+// Steps are software-pipelined: after the barrier of step i, P.V of tile i and the softmax
+// of tile i+1 are independent work.  At the end the four pairs merge (O, m, l) with the
+// log-sum-exp rule through LDS.  The workgroups of one query are numbered so that they land
+// on the same XCD (dispatch is round-robin over the 8 XCDs) and share its L2 for the
+// gathered rows.  When a batch has too few queries to fill the GPU, the key list is split
+// over workgroups and a combine kernel merges the partial (O, m, l).
 #include "device.h"
 
 namespace csa2 {
 
-constexpr int kPairs = 4;                 // key streams per workgroup
+constexpr int kPairs = 4;                      // key streams per workgroup
 constexpr int kAttnThreads = 2 * kPairs * 64;  // 8 waves: each stream has two channel halves
-constexpr int kT = 16;                    // keys per tile (one MFMA block)
-constexpr int kHG = 16;                   // heads per workgroup
+constexpr int kT = 16;                         // keys per tile (one MFMA block)
+constexpr int kHG = 16;                        // heads per workgroup
 constexpr int kD = 512;
-constexpr int kDT = kD / 32;              // 16-channel blocks of a wave's O^T half: 16
-constexpr int kKRow = kD * 2 + 48;        // bytes per K row in LDS (padding against bank conflicts)
-constexpr int kTileBuf = kT * kKRow;      // one K tile: 17,152 B
-constexpr float kLazy = 8.0f;              // log2 headroom of the lazy softmax reference
+constexpr int kHalf = kD / 2;                  // channels per wave
+constexpr int kQS = kHalf / 32;                // QK steps per wave and tile: 8
+constexpr int kDT = kHalf / 16;                // 16-channel blocks of a wave's O^T: 16
+constexpr int kVRow = kHalf * 2 + 16;          // bytes per V row in LDS (padding against bank conflicts)
+constexpr int kVBuf = kT * kVRow;              // one wave's V half-tile: 8,448 B
+constexpr int kRing = 3;                       // tiles whose raw bytes are in flight
+constexpr float kLazy = 8.0f;                  // log2 headroom of the lazy softmax reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -89,35 +94,40 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // bf16 bits -> fp16 (see the header comment for the range)
 __device__ __forceinline__ _Float16 bf16_to_f16(uint32_t b) { return (_Float16)__uint_as_float(b << 16); }
 
-__device__ __forceinline__ uint32_t h2_bits(v2h v) { return *reinterpret_cast<uint32_t*>(&v); }
-
 // 8 E2M1 values of one code dword (channel 2i in the low nibble of byte i) times a group
-// scale given as an fp16 pair, as 4 packed fp16 pairs; exact (E2M1 x E4M3 has at most 6
-// significant bits and lies inside the fp16 range)
-__device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t codes, v2h ss) {
-  return make_uint4(h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss),
-                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss),
-                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss),
-                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss));
+// scale given as an fp16 pair, as 8 fp16; exact (E2M1 x E4M3 has at most 6 significant
+// bits and lies inside the fp16 range)
+__device__ __forceinline__ v8h fp4x8_to_f16(uint32_t codes, v2h ss) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss;
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss;
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss;
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// 8 E4M3 values (two dwords) as 4 packed fp16 pairs; exact
-__device__ __forceinline__ uint4 fp8x8_to_f16(uint32_t lo, uint32_t hi) {
-  return make_uint4(h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false)),
-                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true)),
-                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false)),
-                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true)));
+// 8 E4M3 values (two dwords) as 8 fp16; exact
+__device__ __forceinline__ v8h fp8x8_to_f16(uint32_t lo, uint32_t hi) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// raw bytes of one gather slot (one key, 64 channels): main = 32 B of codes (r[0..1]) and
-// 4 scale bytes (sc); window = 64 B of E4M3 (r[0..3]).  kind: 1 main, 2 window, 0 no key
+// raw bytes of one gather slot (one key, 64 channels of the wave's half): main = 32 B of
+// codes (r[0..1]) and 4 scale bytes (sc); window = 64 B of E4M3 (r[0..3])
 struct GatherSlot {
   uint4 r[4];
   uint32_t sc;
-  uint32_t kind;
+  uint32_t ok;
 };
 
-__global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
+// The per-query arrays come as restrict-qualified arguments of their own: nothing this
+// kernel writes can alias them, so their uniform loads go through the scalar cache.
+__global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int32_t* __restrict__ q_seq,
+                                                           const int64_t* __restrict__ q_pos,
+                                                           const int64_t* __restrict__ replay_start,
+                                                           const int64_t* __restrict__ swa_base) {
   // ---- which (query, head group, split) this workgroup is; same query -> same XCD ----
   const int G = a.head_groups * a.nsplit;
   const int L = blockIdx.x;
@@ -132,109 +142,165 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
   // the wave index is uniform over the wave; saying so keeps tile-level decisions scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave & (kPairs - 1), half = wave / kPairs;  // key stream, channel half
-  const int col = lane & 15, grp = lane >> 4;   // MFMA: column (head), lane group
-  const int gk = lane >> 2, cq = lane & 3;      // gather: key of the tile, 64-channel block
+  const int partner = wave ^ kPairs;                           // the other half of the stream
+  // MFMA lane roles: col = key row of K / head column of Q^T and S^T, grp = lane group
+  const int col = lane & 15, grp = lane >> 4;
 
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPairs * 2 * kTileBuf];
-  __shared__ int32_t s_idx[CSA2_MAX_TOPK];
+  // LDS: two V half-tiles per wave, two partial-S exchange slots per wave and the staged
+  // index list; after the loop the first 128 KB hold the partial outputs of the merge
+  constexpr int kVBytes = 2 * kPairs * 2 * kVBuf;               // 135,168
+  constexpr int kSxBytes = 2 * kPairs * 2 * 64 * 16;            // 16,384
+  constexpr int kLdsBytes = kVBytes + kSxBytes + CSA2_MAX_TOPK * 4;   // 159,744
+  static_assert(2 * kPairs * kDT * 64 * 16 <= kLdsBytes, "merge area");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   __shared__ float s_ml[kPairs][kHG][2];
+  uint8_t* vbuf = lds + wave * 2 * kVBuf;                       // [buffer][16 rows][kVRow]
+  float4* sx = reinterpret_cast<float4*>(lds + kVBytes);        // [wave][slot][lane]
+  int32_t* s_idx = reinterpret_cast<int32_t*>(lds + kVBytes + kSxBytes);
 
-  const int seq = a.q_seq[q];
+  // ---- this split's tiles: main tiles [tile_lo, main_hi), window tiles after them ----
+  const int tile_lo = split * a.tiles_per_split;
+  const int tile_hi = tile_lo + a.tiles_per_split < a.n_tiles ? tile_lo + a.tiles_per_split : a.n_tiles;
+  const int main_hi = a.main_tiles < tile_hi ? a.main_tiles : tile_hi;
+  const int n_main = main_hi > tile_lo ? main_hi - tile_lo : 0;
+
+  // ---- the query's sequence and positions head the memory queue (scalar loads), then this
+  // split's slice of the index list (it does not depend on them), then Q ----
+  const int seq = q_seq[q];
+  const int64_t t = q_pos[q], s = replay_start[q];
+  constexpr int kIdxPer = CSA2_MAX_TOPK / kAttnThreads;
+  const int n_keys = n_main * kT;
+  int32_t iv[kIdxPer];
+  if (n_keys > 0) {  // uniform; idx may be absent when k == 0
+#pragma unroll
+    for (int r = 0; r < kIdxPer; ++r) {
+      int i = tid + r * kAttnThreads;
+      i = i < n_keys ? i : n_keys - 1;              // in-bounds, unconditional loads
+      const int slot = tile_lo * kT + i;
+      iv[r] = a.idx[(int64_t)q * a.k + (slot < a.k ? slot : a.k - 1)];
+    }
+  }
+
+  // ---- Q of head (hg*16 + col): step st of this wave holds channels
+  //      256*half + 64*grp + 8*st .. +7 (the same channel order as the K operand) ----
+  uint4 qraw[kQS];
+  {
+    const uint16_t* qp = a.q + ((int64_t)q * a.n_heads + hg * kHG + col) * kD + kHalf * half + 64 * grp;
+#pragma unroll
+    for (int st = 0; st < kQS; ++st) qraw[st] = *reinterpret_cast<const uint4*>(qp + 8 * st);
+  }
+
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
-  const int64_t t = a.q_pos[q], s = a.replay_start[q];
   const int64_t lo = s > t - a.window + 1 ? s : t - a.window + 1;
   const int64_t n_swa = seq_ok && t >= lo ? t - lo + 1 : 0;
-  const int64_t swa_b = seq_ok ? a.swa_base[seq] : 0;
-  // ring row of the first window key; later keys wrap at most once (window <= swa_cap)
-  int64_t r_lo = (lo - swa_b) % a.swa_cap;
-  r_lo = r_lo < 0 ? r_lo + a.swa_cap : r_lo;
-  const uint32_t win_row0 = (uint32_t)r_lo, swa_cap32 = (uint32_t)a.swa_cap;
+  const int64_t swa_b = seq_ok ? swa_base[seq] : 0;
+  if (n_keys > 0) {
+#pragma unroll
+    for (int r = 0; r < kIdxPer; ++r) {
+      const int i = tid + r * kAttnThreads;
+      if (i < n_keys) s_idx[i] = tile_lo * kT + i < a.k ? iv[r] : -1;
+    }
+  }
+  // ring row of the first window key; later keys wrap at most once (window <= swa_cap).
+  // The offset from the ring base nearly always fits 32 bits: then a 32-bit remainder
+  const int64_t rel = lo - swa_b;
+  const uint32_t swa_cap32 = (uint32_t)a.swa_cap;
+  int64_t r_lo;
+  if (rel >= 0 && rel <= 0xffffffffLL) {
+    r_lo = (uint32_t)rel % swa_cap32;
+  } else {
+    r_lo = rel % a.swa_cap;
+    r_lo = r_lo < 0 ? r_lo + a.swa_cap : r_lo;
+  }
+  const uint32_t win_row0 = (uint32_t)r_lo;
   const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 2);
   const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 16);
   const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_cap * kD;
+  __syncthreads();  // s_idx
 
-  // ---- Q of head (hg*16 + col) as the fp16 B operand: step s holds channels 32s + 8grp.. ----
-  v8h qf[16];
-  {
-    const uint16_t* qp = a.q + ((int64_t)q * a.n_heads + hg * kHG + col) * kD + 8 * grp;
-#pragma unroll
-    for (int st = 0; st < 16; ++st) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * st);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      v8h h;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h[2 * i] = bf16_to_f16(w4[i] & 0xffffu);
-        h[2 * i + 1] = bf16_to_f16(w4[i] >> 16);
-      }
-      qf[st] = h;
-    }
-  }
-
-  // ---- this split's tiles and its slice of the index list (staged in LDS once) ----
-  const int tile_lo = split * a.tiles_per_split;
-  const int tile_hi = tile_lo + a.tiles_per_split < a.n_tiles ? tile_lo + a.tiles_per_split : a.n_tiles;
-  {
-    const int main_hi = a.main_tiles < tile_hi ? a.main_tiles : tile_hi;
-    const int n_keys = main_hi > tile_lo ? (main_hi - tile_lo) * kT : 0;
-    for (int i = tid; i < n_keys; i += kAttnThreads) {
-      const int slot = tile_lo * kT + i;
-      s_idx[i] = (seq_ok && slot < a.k) ? a.idx[(int64_t)q * a.k + slot] : -1;
-    }
-  }
-  __syncthreads();
+  // ---- this pair's tiles: window tiles first (their rows need no index), then main tiles;
+  // pair p takes positions p, p+4, ... of that order.  Every wave runs the same number of
+  // steps (one workgroup barrier each) and masks the steps past its pair's end ----
+  const int span = tile_hi - tile_lo;
+  const int n_win = span - n_main;
+  const int n_steps = (span + kPairs - 1) / kPairs;
+  const int n_my = span > pair ? (span - pair + kPairs - 1) / kPairs : 0;
+  auto my_tile = [&](int i) {
+    const int j = pair + kPairs * (i < n_my ? i : (n_my > 0 ? n_my - 1 : 0));
+    return j < n_win ? tile_lo + n_main + j : tile_lo + (j - n_win);
+  };
 
   // Every gather load is unconditional, to an in-bounds address (an absent key reads row 0
-  // and is flagged), so no branch sits around the loads of the prefetch ring.  This wave
-  // fetches channels 256*half + 64*cq .. +63 of key gk.
+  // and is flagged), so no branch sits around the loads of the ring.  Lane (col, grp)
+  // fetches key col of the tile, channels 256*half + 64*grp .. +63.
   auto load_slot = [&](int tile, bool real, GatherSlot& g) {
     const bool is_main = tile < a.main_tiles;  // wave-uniform
-    const int32_t p = is_main ? s_idx[(tile - tile_lo) * kT + gk] : -1;
-    const bool ok_main = real && p >= 0 && p < a.seq_cap;
+    int si = (tile - tile_lo) * kT + col;
+    si = si < 0 ? 0 : (si >= n_main * kT ? (n_main > 0 ? n_main * kT - 1 : 0) : si);
+    const int32_t p = s_idx[si];
+    const bool ok_main = real && is_main && seq_ok && p >= 0 && p < a.seq_cap;
     const uint32_t pm = ok_main ? (uint32_t)p : 0u;
-    const int j = (tile - a.main_tiles) * kT + gk;
-    const bool ok_win = real && seq_ok && j >= 0 && j < n_swa;
+    const int j = (tile - a.main_tiles) * kT + col;
+    const bool ok_win = real && !is_main && seq_ok && j >= 0 && j < n_swa;
     uint32_t row = win_row0 + (uint32_t)j;
     row = ok_win ? (row >= swa_cap32 ? row - swa_cap32 : row) : 0u;
-    const uint32_t c0 = 256 * half + 64 * cq;   // first channel
     // byte offsets fit 32 bits: seq_cap <= 2^24 rows of 256 B, swa_cap <= 2^23 rows of 512 B
-    const uint4* c = is_main ? reinterpret_cast<const uint4*>(kvc + (pm * (kD / 2) + c0 / 2))
-                             : reinterpret_cast<const uint4*>(swq + (row * kD + c0));
+    const uint4* c = is_main ? reinterpret_cast<const uint4*>(kvc + (pm * (kD / 2) + 128 * half + 32 * grp))
+                             : reinterpret_cast<const uint4*>(swq + (row * kD + kHalf * half + 64 * grp));
     const uint4* c2 = is_main ? c : c + 2;  // main needs 32 B: the second pair re-reads them
     g.r[0] = c[0];
     g.r[1] = c[1];
     g.r[2] = c2[0];
     g.r[3] = c2[1];
-    g.sc = *reinterpret_cast<const uint32_t*>(kvs + (pm * (kD / 16) + c0 / 16));
-    g.kind = is_main ? (ok_main ? 1u : 0u) : (ok_win ? 2u : 0u);
+    g.sc = *reinterpret_cast<const uint32_t*>(kvs + (pm * (kD / 16) + 16 * half + 4 * grp));
+    g.ok = is_main ? ok_main : ok_win;
   };
 
-  // dequantise the slot's 64 channels into a K tile of this pair; returns the tile's
-  // key-valid mask (bit 4*key).  The tile's format is uniform over the wave (a tile holds
-  // main entries only or window keys only), so the only branch is a scalar one; an absent
-  // key's raw bytes are zeroed (E2M1 / E4M3 zero is +0) instead of branching per lane.
-  auto store_slot = [&](const GatherSlot& g, uint8_t* tb, bool is_main) -> uint64_t {
-    const bool ok = g.kind != 0;
-    const uint32_t keep = 0u - (uint32_t)ok;   // all ones for a key, zero otherwise (no branch)
-    uint4* dst = reinterpret_cast<uint4*>(tb + gk * kKRow + (256 * half + 64 * cq) * 2);
+  // Q as the fp16 B operand
+  v8h qf[kQS];
+
+  // Dequantise the slot (the wave's 256 channels of 16 keys), write them as this wave's
+  // V half-tile and form the partial S^T = K Q^T over those channels.  The format is
+  // uniform over the wave (a tile holds main entries only or window keys only), so the only
+  // branch is a scalar one; an absent key's raw bytes are zeroed (E2M1 / E4M3 zero is +0,
+  // a zero scale zeroes a main key) instead of branching per lane.  Returns the partial S^T
+  // (lane: head col, keys 4*grp..+3); *valid receives bit k for each present key k.
+  auto qk_tile = [&](const GatherSlot& g, bool is_main, uint8_t* vb, uint32_t* valid) -> v4f {
+    const uint32_t keep = 0u - g.ok;
+    uint8_t* dst = vb + col * kVRow + 128 * grp;
+    v4f sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
     if (is_main) {
       const uint32_t cw[8] = {g.r[0].x, g.r[0].y, g.r[0].z, g.r[0].w, g.r[1].x, g.r[1].y, g.r[1].z, g.r[1].w};
-      const uint32_t sc = g.sc & keep;   // a zero scale zeroes the whole key
+      const uint32_t sc = g.sc & keep;
       // the four E4M3 group scales to fp16 with the hardware convert (exact)
       const v2h s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
       const v2h s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true);
       const v2h ss[4] = {__builtin_shufflevector(s01, s01, 0, 0), __builtin_shufflevector(s01, s01, 1, 1),
                          __builtin_shufflevector(s23, s23, 0, 0), __builtin_shufflevector(s23, s23, 1, 1)};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = fp4x8_to_f16(cw[i], ss[i >> 1]);
+      for (int st = 0; st < kQS; st += 2) {
+        const v8h k0 = fp4x8_to_f16(cw[st], ss[st >> 1]);
+        const v8h k1 = fp4x8_to_f16(cw[st + 1], ss[st >> 1]);
+        *reinterpret_cast<v8h*>(dst + 16 * st) = k0;
+        *reinterpret_cast<v8h*>(dst + 16 * (st + 1)) = k1;
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st + 1], sb, 0, 0, 0);
+      }
     } else {
+      const uint32_t w[16] = {g.r[0].x, g.r[0].y, g.r[0].z, g.r[0].w, g.r[1].x, g.r[1].y, g.r[1].z, g.r[1].w,
+                              g.r[2].x, g.r[2].y, g.r[2].z, g.r[2].w, g.r[3].x, g.r[3].y, g.r[3].z, g.r[3].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dst[2 * i] = fp8x8_to_f16(g.r[i].x & keep, g.r[i].y & keep);
-        dst[2 * i + 1] = fp8x8_to_f16(g.r[i].z & keep, g.r[i].w & keep);
+      for (int st = 0; st < kQS; st += 2) {
+        const v8h k0 = fp8x8_to_f16(w[2 * st] & keep, w[2 * st + 1] & keep);
+        const v8h k1 = fp8x8_to_f16(w[2 * st + 2] & keep, w[2 * st + 3] & keep);
+        *reinterpret_cast<v8h*>(dst + 16 * st) = k0;
+        *reinterpret_cast<v8h*>(dst + 16 * (st + 1)) = k1;
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st + 1], sb, 0, 0, 0);
       }
     }
-    return __ballot(ok);
+    *valid = (uint32_t)__ballot(g.ok != 0) & 0xffffu;  // lanes 0..15 hold keys 0..15
+    return sa + sb;
   };
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
@@ -242,34 +308,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < kDT; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // one tile: S^T = K Q^T over all 512 channels (both waves of the pair, identical), online
-  // softmax, O^T += V^T P^T over this wave's 256 channels
-  auto compute_tile = [&](const uint8_t* tb, uint64_t valid) {
-    v4f sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* kr = tb + col * kKRow + 16 * grp;
-#pragma unroll
-    for (int st = 0; st < 16; st += 2) {
-      const v8h k0 = *reinterpret_cast<const v8h*>(kr + 64 * st);
-      const v8h k1 = *reinterpret_cast<const v8h*>(kr + 64 * (st + 1));
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[st], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st + 1], sb, 0, 0, 0);
-    }
-    // lane: head col, keys 4*grp + r; the two halves of a key's valid bits come from the
-    // pair's two waves, which gathered the same keys
+  // online softmax over one tile's full S^T (lane: head col, keys 4*grp + r); returns P^T
+  // in fp16, which is exactly the B operand of V_MFMA_F32_16X16X16_F16, and in *alpha the
+  // factor the accumulators must be scaled by once the previous tile's P.V is in them
+  auto softmax_tile = [&](v4f sv, uint32_t valid, float* alpha_out) -> v4h {
     float x[4];
     float mt = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = (valid >> (4 * (4 * grp + r))) & 1ull;
-      x[r] = ok ? (sa[r] + sb[r]) * a.scale_log2 : -__builtin_inff();
+      const bool ok = (valid >> (4 * grp + r)) & 1u;
+      x[r] = ok ? sv[r] * a.scale_log2 : -__builtin_inff();
       mt = fmaxf(mt, x[r]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     // Lazy rescaling: m_run is a reference, not necessarily the running maximum.  It moves
     // only when a logit exceeds it by more than 2^kLazy (or on the first key), so
-    // p = 2^(x - m_run) <= 2^kLazy stays far inside fp16 and the accumulators, which live in
-    // AGPRs, are rescaled only rarely.  The softmax is invariant to the reference.
+    // p = 2^(x - m_run) <= 2^kLazy stays far inside fp16 and the accumulators are rescaled
+    // only rarely.  The softmax is invariant to the reference.
     const bool first = m_run == -__builtin_inff();
     const bool move = first ? mt != -__builtin_inff() : mt > m_run + kLazy;
     const float m_new = move ? mt : m_run;
@@ -285,16 +341,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    *alpha_out = alpha;
+    return pb;
+  };
+  auto rescale = [&](float alpha) {
     if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) o[dt] *= alpha;
     }
-    // A = V^T (16 channels x 16 keys): in each 16-lane group (keys 4grp..4grp+3), lane
-    // 4a+b receives element b of the 8-byte reads of lanes a, a+4, a+8, a+12, so lane r of
-    // the group points at channels 4*(r & 3).. of key 4*grp + (r >> 2)
+  };
+
+  // O^T += V^T P^T over this wave's 256 channels.  A = V^T (16 channels x 16 keys): in each
+  // 16-lane group (keys 4grp..4grp+3), lane 4a+b receives element b of the 8-byte reads of
+  // lanes a, a+4, a+8, a+12, so lane r of the group points at channels 4*(r & 3).. of key
+  // 4*grp + (r >> 2)
+  auto pv_tile = [&](v4h pb, const uint8_t* vt) {
     const __attribute__((address_space(3))) uint8_t* vb =
-        (const __attribute__((address_space(3))) uint8_t*)tb + (4 * grp + (col >> 2)) * kKRow + 8 * (col & 3) +
-        512 * half;
+        (const __attribute__((address_space(3))) uint8_t*)vt + (4 * grp + (col >> 2)) * kVRow + 8 * (col & 3);
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) {
       const v4h av = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + 32 * dt)));
@@ -302,42 +365,67 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
     }
   };
 
-  // ---- this pair's tiles: tile_lo + pair + 4i; every wave runs the same number of steps
-  // (the workgroup barrier of each step), masking steps past its pair's end ----
-  const int span = tile_hi - tile_lo;
-  const int n_steps = (span + kPairs - 1) / kPairs;
-  const int n_my = span > pair ? (span - pair + kPairs - 1) / kPairs : 0;
-  auto my_tile = [&](int i) { return tile_lo + pair + kPairs * (i < n_my ? i : (n_my > 0 ? n_my - 1 : 0)); };
-  uint8_t* pbuf = kbuf + pair * 2 * kTileBuf;
-  uint8_t* buf0 = pbuf;
-  uint8_t* buf1 = pbuf + kTileBuf;
-  // Software pipeline, one barrier per step: step i computes tile i from one buffer while
-  // it dequantises tile i+1 into the other (independent work the compiler can interleave:
-  // converts and LDS writes beside the matrix-core chain).  Buffer b is written again two
-  // steps after it was read, and every wave has passed the barrier in between.  The raw
-  // bytes of tile i+3 are requested during step i.  Slots: at the start of an even step i,
-  // g1 holds tile i+1 and g0 tile i+2.
-  GatherSlot g0, g1;
+  // combine this wave's partial S^T with its partner's through exchange slot `sl` (one
+  // workgroup barrier); both waves add in the same order up to commutation, so the pair
+  // holds bit-identical S^T, softmax state and P
+  auto exchange = [&](v4f own, int sl) -> v4f {
+    sx[(wave * 2 + sl) * 64 + lane] = make_float4(own[0], own[1], own[2], own[3]);
+    __syncthreads();
+    const float4 o2 = sx[(partner * 2 + sl) * 64 + lane];
+    return v4f{own[0] + o2.x, own[1] + o2.y, own[2] + o2.z, own[3] + o2.w};
+  };
+
+  // the V reads of tile i-1 must stay before the V writes of tile i+1 in the same buffer
+  // (LDS executes one wave's accesses in order; this keeps the compiler from reordering)
+  auto lds_order = [] { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); };
+
+  // ---- software pipeline.  Step i dequantises tile i+1 into V buffer (i+1) % 2, forms its
+  // partial S and exchanges it (the one barrier of the step); after the barrier P.V of
+  // tile i (buffer i % 2) and the softmax of tile i+1 are independent work for the matrix
+  // cores and the vector units.  The raw bytes of tiles i+2 .. i+4 are in flight meanwhile:
+  // ring slot (i+1) % 3 is refilled with tile i+4 as soon as tile i+1 has left it ----
+  auto tile_is_main = [&](int i) { return my_tile(i) < a.main_tiles; };
+  GatherSlot g0, g1, g2;
   load_slot(my_tile(0), 0 < n_my, g0);
   load_slot(my_tile(1), 1 < n_my, g1);
-  auto tile_is_main = [&](int i) { return my_tile(i) < a.main_tiles; };
-  uint64_t v0 = store_slot(g0, buf0, tile_is_main(0)), v1 = 0;
-  load_slot(my_tile(2), 2 < n_my, g0);
-  __syncthreads();
-  for (int i = 0; i < n_steps; i += 2) {
-    v1 = store_slot(g1, buf1, tile_is_main(i + 1));  // tile i+1
-    load_slot(my_tile(i + 3), i + 3 < n_my, g1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_tile(buf0, v0);                        // tile i
-    __syncthreads();
-    if (i + 1 < n_steps) {  // uniform over the workgroup
-      v0 = store_slot(g0, buf0, tile_is_main(i + 2));  // tile i+2
-      load_slot(my_tile(i + 4), i + 4 < n_my, g0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile(buf1, v1);                      // tile i+1
-      __syncthreads();
+  load_slot(my_tile(2), 2 < n_my, g2);
+#pragma unroll
+  for (int st = 0; st < kQS; ++st) {
+    const uint32_t w4[4] = {qraw[st].x, qraw[st].y, qraw[st].z, qraw[st].w};
+    v8h h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[2 * i] = bf16_to_f16(w4[i] & 0xffffu);
+      h[2 * i + 1] = bf16_to_f16(w4[i] >> 16);
     }
+    qf[st] = h;
   }
+  uint32_t vmask;
+  float alpha;
+  v4f sp = qk_tile(g0, tile_is_main(0), vbuf, &vmask);
+  load_slot(my_tile(3), 3 < n_my, g0);
+  v4h pb = softmax_tile(exchange(sp, 0), vmask, &alpha);
+
+  auto step = [&](int i, GatherSlot& g) {
+    const int nb = (i + 1) & 1;
+    lds_order();
+    sp = qk_tile(g, tile_is_main(i + 1), vbuf + nb * kVBuf, &vmask);
+    load_slot(my_tile(i + 4), i + 4 < n_my, g);
+    const v4f sv = exchange(sp, nb);
+    pv_tile(pb, vbuf + (nb ^ 1) * kVBuf);   // tile i
+    pb = softmax_tile(sv, vmask, &alpha);   // tile i+1
+    rescale(alpha);
+  };
+  // whole rounds of the ring inside the loop and the remainder after it: a loop with exits
+  // between its steps would make the compiler wait for every load in flight at its head
+  int i = 0;
+  for (; i + kRing <= n_steps; i += kRing) {
+    step(i, g1);
+    step(i + 1, g2);
+    step(i + 2, g0);
+  }
+  if (i < n_steps) step(i, g1);  // uniform over the workgroup
+  if (i + 1 < n_steps) step(i + 1, g2);
 
   // ---- merge the four pairs' (O, m, l); the two waves of a pair hold the same (m, l) ----
   float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -346,7 +434,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
     s_ml[pair][lane][0] = m_run;
     s_ml[pair][lane][1] = l_tot;
   }
-  __syncthreads();  // every wave is past its loop: the K buffers are free
+  __syncthreads();  // every wave is past its loop: the V buffers and exchange slots are free
   float M = -__builtin_inff();
 #pragma unroll
   for (int w = 0; w < kPairs; ++w) M = fmaxf(M, s_ml[w][col][0]);
@@ -360,7 +448,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a) {
   }
   const int head = hg * kHG + col;
   const float inv = Ltot > 0.0f ? 1.0f / Ltot : 0.0f;
-  float4* part = reinterpret_cast<float4*>(kbuf);   // [half][pair][16 blocks][64 lanes]: 128 KB
+  float4* part = reinterpret_cast<float4*>(lds);   // [half][pair][16 blocks][64 lanes]: 128 KB
 #pragma unroll
   for (int b = 0; b < kDT; ++b) {
     const v4f v = o[b] * mine;
@@ -449,9 +537,9 @@ struct AttnPlan {
   int64_t grid;
 };
 
-// One workgroup per CU (its four waves fill the four SIMDs): split the key list only when
-// (query, head group) pairs alone cannot fill the 256 CUs, keeping at least one tile per
-// wave in every split.
+// One workgroup per CU (its eight waves, two per SIMD, and its 160 KB of LDS): split the
+// key list only when (query, head group) pairs alone cannot fill the 256 CUs, keeping at
+// least one tile per key stream in every split.
 static AttnPlan plan(int n_q, int n_heads, int k, int window) {
   AttnPlan p;
   p.head_groups = n_heads / kHG;
@@ -532,7 +620,8 @@ extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, co
     a.ws_ml = a.ws_o + (size_t)p.nsplit * n_q * n_heads * kD;
   }
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(k_attn, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a);
+  hipLaunchKernelGGL(k_attn, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos, a.replay_start,
+                     a.swa_base);
   int rc = csa2_check_launch();
   if (rc != CSA2_OK || p.nsplit == 1) return rc;
   hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(n_q * n_heads)), dim3(128), 0, st, a);
