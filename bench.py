@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the CSA2 layer step on one MI355X.
 
-A layer step (one graph launch, inputs resident in HBM): append the new token's cache
+A layer step (inputs resident in HBM): append the new token's cache
 entries (Full layers: main KV in NVFP4 and indexer K in MXFP4; every layer: its FP8
 window entry), quantise the layer's indexer Q (MXFP4), score the candidates on the FP4
 matrix cores and keep the Top-512 (Full: every visible entry; Reindex: the same cache
@@ -181,18 +181,26 @@ def time_isolated(fn, iters, torch):
     return e0.elapsed_time(e1) / iters
 
 
-def time_graph(graph, steps, warmup, torch):
+def steps_per_graph(steps: int) -> int:
+    """Layer steps captured in one graph: consecutive layers of a decode step replay as one
+    graph, so the per-launch cost of the runtime is paid once per group, not per layer.
+    The largest divisor of `steps` up to 8, so that exactly `steps` steps are timed."""
+    return max(d for d in range(1, 9) if steps % d == 0)
+
+
+def time_graph(graph, replays, warmup, torch, per_replay=1):
+    """Mean time per step of `replays` graph replays, each running `per_replay` steps."""
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     e0.record()
-    for _ in range(steps):
+    for _ in range(replays):
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, time.perf_counter() - wall0
+    return e0.elapsed_time(e1) / (replays * per_replay), time.perf_counter() - wall0
 
 
 def score_bytes(wl, mode: str) -> int:
@@ -261,16 +269,19 @@ def cpu_baseline(wl, n_sample: int, reps: int):
 
 
 def measure_layers(name, steps, warmup, torch, C, layers_to_time):
-    """Graph-replay time of each listed layer's step and of the whole group; isolated
-    launch times of the first listed layer's calls."""
+    """Graph-replay time of each listed layer's step (`steps` steps in graphs of
+    steps_per_graph(steps) consecutive steps of that layer) and of the whole group (one
+    group per graph); isolated launch times of the first listed layer's calls."""
     from synth import workloads
     wl = workloads.config(name)
     log(f"workload {name}: {wl.description}")
     lb = LayerBench(wl, torch, C)
     res = {"wl": wl, "layers": {}}
+    G = steps_per_graph(steps)
+    res["per_graph"] = G
     for L in layers_to_time:
-        g = lb.capture([L])
-        ms, wall = time_graph(g, steps, warmup, torch)
+        g = lb.capture([L] * G)
+        ms, wall = time_graph(g, steps // G, max(warmup // G, 1), torch, per_replay=G)
         res["layers"][L] = {"mode": wl.layers[L], "ms": ms, "wall": wall}
         del g
     if len(wl.layers) > 1:
@@ -388,7 +399,8 @@ def main():
         "data": "synthetic (seeded counter-based generator; no datasets or weights)",
         "config": {"workload": f"{wl.name}: {wl.description}", "queries": wl.n_q, "context_entries": wl.seq_cap,
                    "m": wl.m, "heads": wl.heads, "index_heads": wl.idx_heads, "topk": TOPK, "window": WINDOW},
-        "timing": "HIP events around graph replays of the whole layer step (one graph launch per step)",
+        "timing": f"HIP events around graph replays; each replay runs {head['per_graph']} consecutive layer "
+                  f"steps (a decode step replays its layers as one graph), {args.steps} steps in total",
         "isolated_launch_us": {k: round(v * 1000, 2) for k, v in phase.items()},
         "hbm_frac_step": round(step_bytes(wl, "full") / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": "csa2_index_topk (k_score_select + last selection level)",

@@ -94,6 +94,215 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(TkArgs a) {
   select_segment<kFinal>(key, q, seg, gridDim.x, K, hist, a.keys_out, a.idx_out, a.count_out);
 }
 
+// ---- the last level: one query's at most 8,192 survivors, 1,024 threads x 8 keys ----
+// Same selection and output as select_segment<true> (exact radix select on the 64-bit keys,
+// then a stable compaction in candidate order), laid out for 16 waves so that the serial
+// parts of the single workgroup per query are short: the count comes from ballots, the
+// range of the keys from DPP reductions of their high words, each wave counts into its own
+// 256-bin histogram and the sixteen are summed in two stages.
+constexpr int kFinThreads = 1024;
+constexpr int kFinWaves = kFinThreads / 64;
+constexpr int kFinEpt = kTkSeg / kFinThreads;   // 8
+
+// max / min over the wave with DPP row operations and four readlanes (no LDS traffic)
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));  // row rotate 4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));  // row rotate 8
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
+}
+__device__ __forceinline__ uint32_t dpp_min_u32(uint32_t v) { return ~dpp_max_u32(~v); }
+
+// inclusive prefix sum over the wave with DPP: row shifts 1, 2, 4, 8 (zero fill) give each
+// 16-lane row its own scan, then row broadcasts of lanes 15 and 31 carry the row totals
+__device__ __forceinline__ uint32_t dpp_prefix_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr 1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr 2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr 4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr 8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast 15 -> rows 1, 3
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast 31 -> rows 2, 3
+  return v;
+}
+
+__global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
+  const int q = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = a.k;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kFinWaves][256];
+  __shared__ __attribute__((aligned(16))) uint32_t part[4][256];
+  __shared__ uint32_t red[3][kFinWaves];
+  __shared__ uint32_t cnt[kFinWaves][kFinEpt];
+
+  // ---- keys: candidate i*1024 + tid ----
+  uint64_t key[kFinEpt];
+  {
+    const uint64_t* kp = a.keys_in + q * a.keys_in_per_q;
+    const int lim = (int)(a.keys_in_per_q < kTkSeg ? a.keys_in_per_q : kTkSeg);
+#pragma unroll
+    for (int i = 0; i < kFinEpt; ++i) {
+      const int o = i * kFinThreads + tid;
+      key[i] = o < lim ? kp[o] : 0ull;
+    }
+  }
+
+  // ---- count and the range of the high (score) words ----
+  uint32_t nw = 0, hmax = 0u, hmin = ~0u;
+#pragma unroll
+  for (int i = 0; i < kFinEpt; ++i) {
+    nw += (uint32_t)__popcll(__ballot(key[i] != 0ull));
+    const uint32_t h = (uint32_t)(key[i] >> 32);
+    hmax = key[i] ? max(hmax, h) : hmax;
+    hmin = key[i] ? min(hmin, h) : hmin;
+  }
+  hmax = dpp_max_u32(hmax);
+  hmin = dpp_min_u32(hmin);
+  if (lane == 0) {
+    red[0][wave] = nw;
+    red[1][wave] = hmax;
+    red[2][wave] = hmin;
+  }
+  __syncthreads();
+  uint32_t n = 0;
+  hmax = 0u;
+  hmin = ~0u;
+#pragma unroll
+  for (int w = 0; w < kFinWaves; ++w) {
+    n += red[0][w];
+    hmax = max(hmax, red[1][w]);
+    hmin = min(hmin, red[2][w]);
+  }
+
+  // ---- radix select: (prefix, mask) such that exactly K keys have (key & mask) >= prefix ----
+  uint64_t prefix = 0, mask = 0;
+  if (n > (uint32_t)K) {
+    int hb;        // highest bit where the largest and smallest key differ
+    uint64_t top;  // the largest key's bits above hb
+    if (hmax != hmin) {
+      hb = 32 + 31 - __clz(hmax ^ hmin);
+      top = (uint64_t)hmax << 32;
+    } else {       // every score equal: the keys differ in their position words only
+      uint32_t lmax = 0u, lmin = ~0u;
+#pragma unroll
+      for (int i = 0; i < kFinEpt; ++i) {
+        lmax = key[i] ? max(lmax, (uint32_t)key[i]) : lmax;
+        lmin = key[i] ? min(lmin, (uint32_t)key[i]) : lmin;
+      }
+      lmax = dpp_max_u32(lmax);
+      lmin = dpp_min_u32(lmin);
+      __syncthreads();  // red[] was read above
+      if (lane == 0) {
+        red[1][wave] = lmax;
+        red[2][wave] = lmin;
+      }
+      __syncthreads();
+      lmax = 0u;
+      lmin = ~0u;
+#pragma unroll
+      for (int w = 0; w < kFinWaves; ++w) {
+        lmax = max(lmax, red[1][w]);
+        lmin = min(lmin, red[2][w]);
+      }
+      hb = 31 - __clz(lmax ^ lmin);  // n >= 2 unique keys: lmax != lmin
+      top = ((uint64_t)hmax << 32) | lmax;
+    }
+    mask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+    prefix = top & mask;
+    int shift = hb - 7 > 0 ? hb - 7 : 0;
+    uint32_t need = (uint32_t)K;
+    for (;;) {
+      reinterpret_cast<uint4*>(hist[wave])[lane] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int i = 0; i < kFinEpt; ++i)
+        if (key[i] && (key[i] & mask) == prefix) atomicAdd(&hist[wave][(uint32_t)(key[i] >> shift) & 255u], 1u);
+      __syncthreads();
+      {  // stage 1: thread t sums bin t % 256 over waves 4*(t / 256) .. +3
+        const int b = tid & 255, g4 = tid >> 8;
+        part[g4][b] = hist[4 * g4][b] + hist[4 * g4 + 1][b] + hist[4 * g4 + 2][b] + hist[4 * g4 + 3][b];
+      }
+      __syncthreads();
+      // stage 2, in every wave: lane l owns bins 4l..4l+3
+      uint32_t hs[4];
+      {
+        const uint4 p0 = reinterpret_cast<const uint4*>(part[0])[lane];
+        const uint4 p1 = reinterpret_cast<const uint4*>(part[1])[lane];
+        const uint4 p2 = reinterpret_cast<const uint4*>(part[2])[lane];
+        const uint4 p3 = reinterpret_cast<const uint4*>(part[3])[lane];
+        hs[0] = p0.x + p1.x + p2.x + p3.x;
+        hs[1] = p0.y + p1.y + p2.y + p3.y;
+        hs[2] = p0.z + p1.z + p2.z + p3.z;
+        hs[3] = p0.w + p1.w + p2.w + p3.w;
+      }
+      const uint32_t tot = hs[0] + hs[1] + hs[2] + hs[3];
+      const uint32_t pre = dpp_prefix_sum(tot);
+      const uint32_t incl = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + tot;  // bins >= 4*lane
+      const uint32_t above_lane = incl - tot;
+      // the boundary digit is the largest d with (count of digits >= d) >= need
+      uint32_t d = 0, above = 0, inbin = 0;
+      const bool mine = above_lane < need && incl >= need;
+      if (mine) {
+        uint32_t acc = above_lane;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (acc + hs[j] >= need) {
+            d = 4 * lane + j;
+            above = acc;
+            inbin = hs[j];
+            break;
+          }
+          acc += hs[j];
+        }
+      }
+      const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
+      d = __builtin_amdgcn_readlane(d, owner);
+      above = __builtin_amdgcn_readlane(above, owner);
+      inbin = __builtin_amdgcn_readlane(inbin, owner);
+      need -= above;
+      prefix |= (uint64_t)d << shift;
+      mask |= 255ull << shift;
+      if (inbin == need || shift == 0) break;
+      shift = shift - 8 > 0 ? shift - 8 : 0;
+    }
+  }
+
+  // ---- stable compaction in candidate order (i-major, then thread) ----
+#pragma unroll
+  for (int i = 0; i < kFinEpt; ++i) {
+    const uint64_t m = __ballot(key[i] && (key[i] & mask) >= prefix);
+    if (lane == 0) cnt[wave][i] = (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  // lane i < 8: off = (survivors of slots < i, all waves) + (survivors of slot i, waves < w)
+  uint32_t tot_i = 0, before_w = 0;
+  if (lane < kFinEpt) {
+#pragma unroll
+    for (int w = 0; w < kFinWaves; ++w) {
+      const uint32_t c = cnt[w][lane];
+      tot_i += c;
+      before_w += w < wave ? c : 0u;
+    }
+  }
+  const uint32_t excl = dpp_prefix_sum(tot_i);   // lanes 0..7 (row 0): inclusive over slots
+  const uint32_t total = __builtin_amdgcn_readlane(excl, kFinEpt - 1);
+  const uint32_t off = excl - tot_i + before_w;
+  const uint32_t nsel = total < (uint32_t)K ? total : (uint32_t)K;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t* out = a.idx_out + (int64_t)q * K;
+#pragma unroll
+  for (int i = 0; i < kFinEpt; ++i) {
+    const bool take = key[i] && (key[i] & mask) >= prefix;
+    const uint64_t m = __ballot(take);
+    const uint32_t slot = __builtin_amdgcn_readlane(off, i) + (uint32_t)__popcll(m & lt_mask);
+    if (take && slot < (uint32_t)K) out[slot] = key_pos(key[i]);
+  }
+  for (int i = (int)nsel + tid; i < K; i += kFinThreads) out[i] = -1;
+  if (tid == 0) a.count_out[q] = (int32_t)nsel;
+}
+
 // Launch the key-merging levels 1..L-1 (level 0 has written bufA); returns a csa2 status.
 int select_levels_after0(const int64_t* segs, int L, TkArgs base, int n_q, uint64_t* bufA, uint64_t* bufB,
                          hipStream_t st) {
@@ -104,7 +313,7 @@ int select_levels_after0(const int64_t* segs, int L, TkArgs base, int n_q, uint6
     a.keys_in_per_q = segs[l - 1] * base.k;
     a.keys_out = (l % 2 == 0) ? bufA : bufB;
     dim3 grid((unsigned)segs[l], (unsigned)n_q), blk(kTkThreads);
-    if (final) hipLaunchKernelGGL((k_topk<kFromKeys, true>), grid, blk, 0, st, a);
+    if (final) hipLaunchKernelGGL(k_topk_final, dim3(1u, (unsigned)n_q), dim3(kFinThreads), 0, st, a);
     else hipLaunchKernelGGL((k_topk<kFromKeys, false>), grid, blk, 0, st, a);
     const int rc = csa2_check_launch();
     if (rc != CSA2_OK) return rc;
