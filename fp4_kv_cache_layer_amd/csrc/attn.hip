@@ -154,6 +154,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   static_assert(2 * kPairs * kDT * 64 * 16 <= kLdsBytes, "merge area");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   __shared__ float s_ml[kPairs][kHG][2];
+  __shared__ uint32_t s_flag[2 * kPairs];   // per wave: number of partial-S slots written
   uint8_t* vbuf = lds + wave * 2 * kVBuf;                       // [buffer][16 rows][kVRow]
   float4* sx = reinterpret_cast<float4*>(lds + kVBytes);        // [wave][slot][lane]
   int32_t* s_idx = reinterpret_cast<int32_t*>(lds + kVBytes + kSxBytes);
@@ -216,7 +217,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 2);
   const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 16);
   const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_cap * kD;
-  __syncthreads();  // s_idx
+  if (lane == 0) s_flag[wave] = 0u;
+  __syncthreads();  // s_idx, s_flag
 
   // ---- this pair's tiles: window tiles first (their rows need no index), then main tiles;
   // pair p takes positions p, p+4, ... of that order.  Every wave runs the same number of
@@ -365,12 +367,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     }
   };
 
-  // combine this wave's partial S^T with its partner's through exchange slot `sl` (one
-  // workgroup barrier); both waves add in the same order up to commutation, so the pair
-  // holds bit-identical S^T, softmax state and P
-  auto exchange = [&](v4f own, int sl) -> v4f {
+  // Combine this wave's partial S^T with its partner's.  Exchange number `id` goes through
+  // slot id % 2: the wave writes its slot, then its flag (id + 1), then waits for the
+  // partner's flag to reach id + 1 and reads the partner's slot.  Only the two waves of a
+  // stream synchronise, so the four streams drift freely.  Both waves make the same
+  // sequence of exchanges, so every wait is met; a slot is rewritten two exchanges later,
+  // which the writer can only reach after the partner's flag shows the read was done.  The
+  // wait is bounded so that it always ends.  Both waves add in the same order up to
+  // commutation, so the pair holds bit-identical S^T, softmax state and P.
+  auto exchange = [&](v4f own, int id) -> v4f {
+    const int sl = id & 1;
     sx[(wave * 2 + sl) * 64 + lane] = make_float4(own[0], own[1], own[2], own[3]);
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) __hip_atomic_store(&s_flag[wave], (uint32_t)(id + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      if (__hip_atomic_load(&s_flag[partner], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= (uint32_t)(id + 1))
+        break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const float4 o2 = sx[(partner * 2 + sl) * 64 + lane];
     return v4f{own[0] + o2.x, own[1] + o2.y, own[2] + o2.z, own[3] + o2.w};
   };
@@ -411,7 +426,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     lds_order();
     sp = qk_tile(g, tile_is_main(i + 1), vbuf + nb * kVBuf, &vmask);
     load_slot(my_tile(i + 4), i + 4 < n_my, g);
-    const v4f sv = exchange(sp, nb);
+    const v4f sv = exchange(sp, i + 1);
     pv_tile(pb, vbuf + (nb ^ 1) * kVBuf);   // tile i
     pb = softmax_tile(sv, vmask, &alpha);   // tile i+1
     rescale(alpha);
