@@ -12,8 +12,9 @@ attends with the borrowed index set.  A step's quantisations run as one launch.
 Headline: the Full decode step of 64 queries x 131,072 entries (128K tokens at m=1), 64
 heads, 16 indexer heads; metric query tokens per second per layer.  Also reported (unless
 --no-modes): every mode of the 128K layer group (Full, 3 Reuse, Reindex; 32 queries) and
-of the 1M group (Full + pool, 4 Reindex inside the pool; 8 queries), and each group as one
-graph.  The CPU baseline times the fp64 oracle on a bounded sample of the headline step.
+of the 1M group (Full + pool, 4 Reindex inside the pool; 8 queries), each group as one
+graph, the m = 2 prefill chunk, and the whole decoder step (its 20 CSA2 layers as one graph)
+at 128K and 1M.  The CPU baseline times the fp64 oracle on a bounded sample of the headline step.
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -296,6 +297,29 @@ def measure_layers(name, steps, warmup, torch, C, layers_to_time):
     return res
 
 
+def measure_decoder(name, steps, warmup, torch, C):
+    """Graph-replay time of one whole decoder step: the 20 CSA2 layers of a decode token
+    (each with its own appends) captured as one graph."""
+    from synth import workloads
+    wl = workloads.config(name)
+    log(f"workload {name}: {wl.description}")
+    lb = LayerBench(wl, torch, C)
+    g = lb.capture(list(range(len(wl.layers))))
+    ms, _ = time_graph(g, steps, warmup, torch)
+    del g, lb
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return wl, ms
+
+
+def decoder_entry(wl, ms) -> dict:
+    n = len(wl.layers)
+    return {"layers": n, "structure": "Full + pool, 3 Reuse, 4 x (Reindex in the pool, 3 Reuse)",
+            "queries": wl.n_q, "context_entries": wl.seq_cap,
+            "us_per_decode_step": round(ms * 1e3, 2), "us_per_layer": round(ms * 1e3 / n, 2),
+            "query_tokens_per_s": round(wl.n_q / (ms / 1e3), 1)}
+
+
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_score_select_c2_128k_traffic.md")
 TRAFFIC_SOURCES = ("fp4_kv_cache_layer_amd/csrc/score.hip", "fp4_kv_cache_layer_amd/csrc/select.h",
                    "fp4_kv_cache_layer_amd/csrc/topk.hip", "fp4_kv_cache_layer_amd/build.py")
@@ -429,6 +453,9 @@ def main():
                                      "us_per_chunk": round(ms5 * 1e3, 1),
                                      "new_tokens_per_s": round(rows / (ms5 / 1e3), 1),
                                      "isolated_launch_us": {k: round(v * 1000, 1) for k, v in r5["isolated"].items()}}
+        for name, key in (("dec_128k", "decoder_128k"), ("dec_1m", "decoder_1m")):
+            wld, msd = measure_decoder(name, args.steps, args.warmup, torch, C)
+            modes[key] = decoder_entry(wld, msd)
         result["modes"] = modes
         for k, v in modes.items():
             log(f"  {k}: {v}")

@@ -125,6 +125,13 @@ def prefill(name: str, seed: int, prefix_tokens: int, chunk_tokens: int, m: int,
     return wl
 
 
+def decoder_modes() -> tuple:
+    """The decoder's 20 CSA2 layers ([W] "CSA2：跨层复用，能借就不自己算": five groups, the
+    first Full + 3 Reuse, then four of Reindex + 3 Reuse; [W] "分层稀疏索引器": the first Full
+    layer builds the shared candidate pool and the Reindex layers search only inside it)."""
+    return ("full_pool",) + ("reuse",) * 3 + (("reindex_pool",) + ("reuse",) * 3) * 4
+
+
 def config(name: str) -> Workload:
     """The five workloads: tiny decode, 128K batched decode, one layer group at 128K,
     1M decode with the candidate pool, and an m=2 encoder prefill chunk."""
@@ -144,7 +151,14 @@ def config(name: str) -> Workload:
     if name == "c5":
         return prefill("c5", 4, 262144, 4096, 2, 64, 16,
                        "encoder prefill chunk: 4,096 tokens after a 262,144-token prefix, m=2")
+    if name == "dec_128k":
+        return decode("dec_128k", 5, 32, 131072, 64, 16, decoder_modes(),
+                      "decoder step: the 20 CSA2 layers of one decode token, 32 queries x 128K entries")
+    if name == "dec_1m":
+        return decode("dec_1m", 6, 8, 1048576, 64, 16, decoder_modes(),
+                      "decoder step: the 20 CSA2 layers of one decode token, 8 queries x 1M entries")
     raise KeyError(name)
 
 
 CONFIG_NAMES = ("c1", "c2", "c3", "c4", "c5")
+DECODER_NAMES = ("dec_128k", "dec_1m")   # whole decoder steps (all 20 CSA2 layers)

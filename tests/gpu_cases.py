@@ -175,7 +175,7 @@ def _oracle_index_cache(name: str, seq: int) -> O.PackedCaches:
 def oracle_index_cache(wl: Workload, seq: int) -> O.PackedCaches:
     """Oracle caches of one sequence holding the indexer K only (the part scoring reads);
     kept for reuse across tests of the same named workload."""
-    if wl.name in workloads.CONFIG_NAMES:
+    if wl.name in workloads.CONFIG_NAMES + workloads.DECODER_NAMES:
         return _oracle_index_cache(wl.name, seq)
     ik_c, ik_s = O.quantize_mxfp4(wl.index_k_latents(seq, 0, wl.seq_cap))
     return O.PackedCaches(None, None, ik_c, ik_s)

@@ -1,6 +1,7 @@
-"""Full-size layer groups on the GPU: the 128K group (Full, 3 Reuse, Reindex; 32 queries)
-and the 1M group (Full + pool, 4 Reindex inside the pool; 8 queries), run through the layer
-driver exactly as the benchmark runs them, with oracle parity on sampled query rows."""
+"""Full-size layer groups on the GPU: the 128K group (Full, 3 Reuse, Reindex; 32 queries),
+the 1M group (Full + pool, 4 Reindex inside the pool; 8 queries), the whole 20-layer decoder
+step at 128K and 1M, and the m = 2 prefill chunk, run through the layer driver exactly as
+the benchmark runs them, with oracle parity on sampled query rows."""
 import sys
 
 import pytest
@@ -34,6 +35,26 @@ def test_layer_group_full_size(C, name, samples, fused):
     case = G.Case(wl, swa_layers=range(len(wl.layers)))
     caches = case.gpu_caches()
     step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, fused=fused)
+    snaps = G.run_group_snapshots(case, step, caches)
+    for qi in samples:
+        _say("  oracle query", qi)
+        G.check_group_query(case, caches, snaps, qi)
+    del caches, step
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,samples", [("dec_128k", (0, 31)), ("dec_1m", (0, 7))])
+def test_decoder_step_full_size(C, name, samples):
+    """The whole decoder step: 20 CSA2 layers (Full + pool, 3 Reuse, 4 x (Reindex in the pool,
+    3 Reuse)) at 128K and 1M, through the layer driver as the benchmark runs it, with oracle
+    parity of every layer on sampled query rows."""
+    _say("decoder step", name)
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    wl = workloads.config(name)
+    case = G.Case(wl, swa_layers=range(len(wl.layers)))
+    caches = case.gpu_caches()
+    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap)
     snaps = G.run_group_snapshots(case, step, caches)
     for qi in samples:
         _say("  oracle query", qi)

@@ -38,6 +38,19 @@ def test_model_schedule_groups_plan():
     assert "build_pool" in plan[0] and plan[0].index("build_pool") < plan[0].index("attend")
 
 
+def test_decoder_step_is_the_model_decoder():
+    """The benchmarked decoder step runs the model's 20 decoder layers, pool-based."""
+    from synth.workloads import decoder_modes, config
+    dec = _groups(O.layer_schedule())[-1]
+    assert len(dec) == 20
+    want = ["full_pool"] + ["reindex_pool" if m == "reindex" else m for m in dec[1:]]
+    assert list(decoder_modes()) == want
+    plan = plan_group(decoder_modes())
+    assert sum(1 for p in plan if p != ["attend"]) == 5      # 1 Full + 4 Reindex score
+    for name in ("dec_128k", "dec_1m"):
+        assert config(name).layers == decoder_modes()
+
+
 def test_unfused_plan_keeps_two_calls():
     plan = plan_group(["full", "reuse", "reindex", "reindex"], fused=False)
     assert plan[0] == ["quantize_index_q", "score", "select", "attend"]
