@@ -13,8 +13,9 @@ Headline: the Full decode step of 64 queries x 131,072 entries (128K tokens at m
 heads, 16 indexer heads; metric query tokens per second per layer.  Also reported (unless
 --no-modes): every mode of the 128K layer group (Full, 3 Reuse, Reindex; 32 queries) and
 of the 1M group (Full + pool, 4 Reindex inside the pool; 8 queries), each group as one
-graph, the m = 2 prefill chunk, and the whole decoder step (its 20 CSA2 layers as one graph)
-at 128K and 1M.  The CPU baseline times the fp64 oracle on a bounded sample of the headline step.
+graph, the m = 2 prefill chunk, an encoder group (Full + 5 Reuse) over that chunk after a
+window-state miss, and the whole decoder step (its 20 CSA2 layers as one graph) at 128K and
+1M.  The CPU baseline times the fp64 oracle on a bounded sample of the headline step.
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -46,7 +47,9 @@ class LayerBench:
     library's own quantiser (setup, untimed), per-layer query inputs, the new token's
     latents, and a Csa2Step.  A layer step = appending the new token's cache entries, then
     the layer's own calls (Full: main KV + indexer K + its window entry; Reuse / Reindex:
-    its window entry only, since they share the Full layer's global KV)."""
+    its window entry only, since they share the Full layer's global KV).  With a window miss
+    (`swa_miss`: the prefix's window state is not cached) the rings start empty and every
+    layer writes the window entries of all its query rows, replay rows included."""
 
     def __init__(self, wl, torch, C):
         from fp4_kv_cache_layer_amd.layer import Caches, Csa2Step, plan_group
@@ -68,7 +71,7 @@ class LayerBench:
             t = int(wl.q_pos[wl.q_seq == b].max())
             p0 = max(0, t - wl.swa_cap + 1)
             rows = torch.from_numpy(((np.arange(p0, t + 1) - wl.swa_base) % wl.swa_cap).astype(np.int64)).to(dev)
-            for L in range(n_layers):
+            for L in range(n_layers) if not wl.extra.get("swa_miss") else ():
                 sw = wl.swa_latents(L, b, p0, t - p0 + 1)
                 C.csa2_quantize_kv(torch.from_numpy(sw).to(dev), C.FMT_FP8, caches.swa[L][b], None, rows)
             if b % 16 == 15 or b == wl.n_seq - 1:
@@ -93,10 +96,10 @@ class LayerBench:
             tok_seq, tok_pos = wl.q_seq.astype(np.int64), wl.q_pos
         else:
             # prefill chunk (one sequence): the chunk's entries and its new tokens' window rows
-            # (the replay rows' window entries are already cached)
+            # (the replay rows' window entries are cached, unless the window state missed)
             ent_seq = np.zeros(n_new, np.int64)
             ent_row = first_new + np.arange(n_new, dtype=np.int64)
-            new_tok = wl.q_pos >= first_new * wl.m
+            new_tok = wl.q_pos >= (-1 if wl.extra.get("swa_miss") else first_new * wl.m)
             tok_seq, tok_pos = wl.q_seq[new_tok].astype(np.int64), wl.q_pos[new_tok]
         self.new_main = torch.from_numpy(np.stack([wl.main_latents(int(b), int(r), 1)[0]
                                                    for b, r in zip(ent_seq, ent_row)])).to(dev)
@@ -297,9 +300,9 @@ def measure_layers(name, steps, warmup, torch, C, layers_to_time):
     return res
 
 
-def measure_decoder(name, steps, warmup, torch, C):
-    """Graph-replay time of one whole decoder step: the 20 CSA2 layers of a decode token
-    (each with its own appends) captured as one graph."""
+def measure_group(name, steps, warmup, torch, C):
+    """Graph-replay time of a workload's whole layer group (each layer with its own appends)
+    captured as one graph: a decoder step, or an encoder group over a prefill chunk."""
     from synth import workloads
     wl = workloads.config(name)
     log(f"workload {name}: {wl.description}")
@@ -453,8 +456,14 @@ def main():
                                      "us_per_chunk": round(ms5 * 1e3, 1),
                                      "new_tokens_per_s": round(rows / (ms5 / 1e3), 1),
                                      "isolated_launch_us": {k: round(v * 1000, 1) for k, v in r5["isolated"].items()}}
+        wle, mse = measure_group("enc_group", max(args.steps // 5, 3), max(args.warmup // 5, 1), torch, C)
+        rows = int(wle.extra["counted_rows"])
+        modes["encoder_group_prefill_m2"] = {
+            "layers": len(wle.layers), "structure": "Full + 5 Reuse, window state missed (replay rows rewrite it)",
+            "query_rows": wle.n_q, "counted_new_tokens": rows, "us_per_chunk": round(mse * 1e3, 1),
+            "us_per_layer": round(mse * 1e3 / len(wle.layers), 1), "new_tokens_per_s": round(rows / (mse / 1e3), 1)}
         for name, key in (("dec_128k", "decoder_128k"), ("dec_1m", "decoder_1m")):
-            wld, msd = measure_decoder(name, args.steps, args.warmup, torch, C)
+            wld, msd = measure_group(name, args.steps, args.warmup, torch, C)
             modes[key] = decoder_entry(wld, msd)
         result["modes"] = modes
         for k, v in modes.items():

@@ -109,20 +109,29 @@ def decode(name: str, seed: int, batch: int, n_entries: int, heads: int, idx_hea
 
 
 def prefill(name: str, seed: int, prefix_tokens: int, chunk_tokens: int, m: int, heads: int,
-            idx_heads: int, description: str = "") -> Workload:
+            idx_heads: int, description: str = "", layers=("full",), swa_miss: bool = False) -> Workload:
     """One sequence: a cached prefix, then a chunk of new tokens.  The query rows are the
-    last WINDOW prefix tokens (bounded replay from s = prefix - WINDOW) and the new tokens."""
+    last WINDOW prefix tokens (bounded replay from s = prefix - WINDOW) and the new tokens.
+    swa_miss: the prefix's window state is not cached (a prefix-cache miss): every layer
+    writes the window entries of all its query rows, replay rows included, before attending."""
     s = prefix_tokens - WINDOW
     q_pos = np.arange(s, prefix_tokens + chunk_tokens, dtype=np.int64)
     total_entries = (prefix_tokens + chunk_tokens) // m
     first_new = prefix_tokens // m
     wl = Workload(name=name, seed=seed, n_seq=1, seq_cap=total_entries, m=m, heads=heads,
                   idx_heads=idx_heads, q_seq=np.zeros(q_pos.shape[0], dtype=np.int32), q_pos=q_pos,
-                  replay_start=np.full(q_pos.shape[0], s, dtype=np.int64), layers=("full",),
+                  replay_start=np.full(q_pos.shape[0], s, dtype=np.int64), layers=tuple(layers),
                   new_entries=(first_new, total_entries - first_new),
                   swa_cap=chunk_tokens + WINDOW, swa_base=s, description=description)
     wl.extra["counted_rows"] = chunk_tokens
+    wl.extra["swa_miss"] = swa_miss
     return wl
+
+
+def encoder_modes() -> tuple:
+    """One encoder CSA2 group ([W] "CSA2：跨层复用，能借就不自己算": the encoder's 18 CSA2
+    layers at m = 2 form 3 groups of 6, one Full layer and 5 Reuse layers each)."""
+    return ("full",) + ("reuse",) * 5
 
 
 def decoder_modes() -> tuple:
@@ -151,6 +160,11 @@ def config(name: str) -> Workload:
     if name == "c5":
         return prefill("c5", 4, 262144, 4096, 2, 64, 16,
                        "encoder prefill chunk: 4,096 tokens after a 262,144-token prefix, m=2")
+    if name == "enc_group":
+        return prefill("enc_group", 7, 262144, 4096, 2, 64, 16,
+                       "encoder group prefill (Full + 5 Reuse, m=2) of a 4,096-token chunk after a "
+                       "262,144-token prefix, prefix-cache miss: 128 replay rows rebuild the window",
+                       layers=encoder_modes(), swa_miss=True)
     if name == "dec_128k":
         return decode("dec_128k", 5, 32, 131072, 64, 16, decoder_modes(),
                       "decoder step: the 20 CSA2 layers of one decode token, 32 queries x 128K entries")
@@ -162,3 +176,4 @@ def config(name: str) -> Workload:
 
 CONFIG_NAMES = ("c1", "c2", "c3", "c4", "c5")
 DECODER_NAMES = ("dec_128k", "dec_1m")   # whole decoder steps (all 20 CSA2 layers)
+GROUP_NAMES = DECODER_NAMES + ("enc_group",)   # multi-layer workloads beyond the five configs

@@ -47,7 +47,10 @@ class Case:
         self.swa_layers = tuple(swa_layers)
 
     # ---------- HIP side ----------
-    def gpu_caches(self):
+    def gpu_caches(self, window_empty: bool = False):
+        """The sequences' caches built by the library's quantiser from the seeded latents;
+        window_empty leaves the window rings zero (a prefix-cache miss: the layer steps
+        write them)."""
         from fp4_kv_cache_layer_amd.layer import Caches
         wl, C_ = self.wl, C()
         caches = Caches.empty(wl.n_seq, wl.seq_cap, self.swa_layers, wl.swa_cap)
@@ -59,7 +62,7 @@ class Case:
                 C_.csa2_quantize_kv(lat, C_.FMT_NVFP4, caches.kv_codes[b, r0:r0 + n], caches.kv_scales[b, r0:r0 + n])
                 ik = torch.from_numpy(wl.index_k_latents(b, r0, n)).cuda()
                 C_.csa2_quantize_kv(ik, C_.FMT_MXFP4, caches.ik_codes[b, r0:r0 + n], caches.ik_scales[b, r0:r0 + n])
-            for L in self.swa_layers:
+            for L in self.swa_layers if not window_empty else ():
                 ring = torch.from_numpy(swa_ring_latents(wl, L, b)).cuda()
                 C_.csa2_quantize_kv(ring, C_.FMT_FP8, caches.swa[L][b])
         torch.cuda.synchronize()
@@ -175,15 +178,17 @@ def _oracle_index_cache(name: str, seq: int) -> O.PackedCaches:
 def oracle_index_cache(wl: Workload, seq: int) -> O.PackedCaches:
     """Oracle caches of one sequence holding the indexer K only (the part scoring reads);
     kept for reuse across tests of the same named workload."""
-    if wl.name in workloads.CONFIG_NAMES + workloads.DECODER_NAMES:
+    if wl.name in workloads.CONFIG_NAMES + workloads.GROUP_NAMES:
         return _oracle_index_cache(wl.name, seq)
     ik_c, ik_s = O.quantize_mxfp4(wl.index_k_latents(seq, 0, wl.seq_cap))
     return O.PackedCaches(None, None, ik_c, ik_s)
 
 
-def run_group_snapshots(case: Case, step, caches):
+def run_group_snapshots(case: Case, step, caches, window_appends: bool = False):
     """Runs the workload's layer group on the GPU layer by layer and returns per-layer
-    snapshots: idx, count (the set each layer attended over), out, lse, and the pool."""
+    snapshots: idx, count (the set each layer attended over), out, lse, and the pool.
+    window_appends: before its calls, each layer writes the FP8 window entry of every query
+    row into its own ring (what a layer step does when the window state is not cached)."""
     from fp4_kv_cache_layer_amd.layer import plan_group
     wl = case.wl
     q_seq, n_vis, q_pos, rs = case.gpu_meta()
@@ -191,7 +196,13 @@ def run_group_snapshots(case: Case, step, caches):
     inputs = [case.gpu_query_inputs(L) for L in range(len(modes))]
     calls = step.run_group(caches, modes, inputs, q_seq, n_vis, q_pos, rs, bind=True)
     snaps, at = [], 0
-    for names in plan_group(modes, step.fused):
+    for L, names in enumerate(plan_group(modes, step.fused)):
+        if window_appends:
+            C_ = C()
+            lat = np.stack([wl.swa_latents(L, int(b), int(t), 1)[0] for b, t in zip(wl.q_seq, wl.q_pos)])
+            dst = torch.from_numpy(wl.q_seq.astype(np.int64) * wl.swa_cap
+                                   + np.mod(wl.q_pos - wl.swa_base, wl.swa_cap)).cuda()
+            C_.csa2_quantize_kv(torch.from_numpy(lat).cuda(), C_.FMT_FP8, caches.swa[L].view(-1, DIM), None, dst)
         for fn in calls[at:at + len(names)]:
             fn()
         at += len(names)

@@ -64,6 +64,28 @@ def test_decoder_step_full_size(C, name, samples):
 
 
 @pytest.mark.timeout(900)
+def test_encoder_group_prefill_window_miss(C):
+    """An encoder CSA2 group (Full + 5 Reuse, m = 2) over a 4,096-token chunk after a
+    262,144-token prefix whose window state is not cached: every layer writes the FP8 window
+    entries of its 128 replay rows and 4,096 new rows, then attends with the window bounded
+    at the replay start.  Oracle parity of every layer (index set, window rows written,
+    attention) on replay and new rows."""
+    _say("encoder group prefill, window miss")
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    wl = workloads.config("enc_group")
+    assert wl.extra["swa_miss"]
+    case = G.Case(wl, swa_layers=range(len(wl.layers)))
+    caches = case.gpu_caches(window_empty=True)
+    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap)
+    snaps = G.run_group_snapshots(case, step, caches, window_appends=True)
+    for qi in (0, 127, 128, 3000, wl.n_q - 1):
+        _say("  oracle query", qi, "t", int(wl.q_pos[qi]))
+        G.check_group_query(case, caches, snaps, qi)
+    del caches, step
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
 def test_prefill_chunk_full_size(C):
     """The m = 2 encoder prefill chunk: 4,096 new tokens after a 262,144-token prefix plus the
     128 bounded-replay rows, one sequence of 133,120 entries, run as one Full layer; oracle
