@@ -51,10 +51,10 @@ class LayerBench:
     (`swa_miss`: the prefix's window state is not cached) the rings start empty and every
     layer writes the window entries of all its query rows, replay rows included."""
 
-    def __init__(self, wl, torch, C):
+    def __init__(self, wl, torch, C, group: int = 1):
         from fp4_kv_cache_layer_amd.layer import Caches, Csa2Step, plan_group
         self.wl, self.torch, self.C = wl, torch, C
-        self.plan = plan_group(wl.layers)
+        self.plan = plan_group(wl.layers, group=group)
         n_layers = len(wl.layers)
         dev = "cuda"
         caches = Caches.empty(wl.n_seq, wl.seq_cap, range(n_layers), wl.swa_cap)
@@ -88,19 +88,16 @@ class LayerBench:
             w = torch.from_numpy(wl.index_w(L)).to(dev)
             qa = torch.from_numpy(wl.attn_q_bits(L).view(np.int16)).to(dev).view(torch.bfloat16)
             self.inputs.append((q_idx, w, qa))
+        # every queried sequence's new entries [first_new, first_new + n_new) (decode: its
+        # newest token; multi-token decode: its tokens; prefill: the chunk's entries), and the
+        # window rows of the new tokens (of every query row when the window state missed;
+        # otherwise the replay rows' window entries are cached)
         first_new, n_new = int(wl.new_entries[0]), int(wl.new_entries[1])
-        if n_new == 1:
-            # decode: the newest token of every sequence, one entry and one window row each
-            ent_seq = wl.q_seq.astype(np.int64)
-            ent_row = np.full(wl.n_q, first_new, np.int64)
-            tok_seq, tok_pos = wl.q_seq.astype(np.int64), wl.q_pos
-        else:
-            # prefill chunk (one sequence): the chunk's entries and its new tokens' window rows
-            # (the replay rows' window entries are cached, unless the window state missed)
-            ent_seq = np.zeros(n_new, np.int64)
-            ent_row = first_new + np.arange(n_new, dtype=np.int64)
-            new_tok = wl.q_pos >= (-1 if wl.extra.get("swa_miss") else first_new * wl.m)
-            tok_seq, tok_pos = wl.q_seq[new_tok].astype(np.int64), wl.q_pos[new_tok]
+        seqs = np.unique(wl.q_seq).astype(np.int64)
+        ent_seq = np.repeat(seqs, n_new)
+        ent_row = np.tile(first_new + np.arange(n_new, dtype=np.int64), seqs.size)
+        new_tok = wl.q_pos >= (-1 if wl.extra.get("swa_miss") else first_new * wl.m)
+        tok_seq, tok_pos = wl.q_seq[new_tok].astype(np.int64), wl.q_pos[new_tok]
         self.new_main = torch.from_numpy(np.stack([wl.main_latents(int(b), int(r), 1)[0]
                                                    for b, r in zip(ent_seq, ent_row)])).to(dev)
         self.new_ik = torch.from_numpy(np.stack([wl.index_k_latents(int(b), int(r), 1)[0]
@@ -110,7 +107,7 @@ class LayerBench:
                         for L in range(n_layers)]
         self.dst_entry = torch.from_numpy(ent_seq * wl.seq_cap + ent_row).to(dev)
         self.dst_swa = torch.from_numpy(tok_seq * wl.swa_cap + (tok_pos - wl.swa_base) % wl.swa_cap).to(dev)
-        self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap)
+        self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group)
 
     def calls(self, L: int):
         """Layer L's step as {phase: bound call} bound to the current stream, in order."""
@@ -134,6 +131,9 @@ class LayerBench:
         out["quantize"] = C.csa2_quantize_kv_multi(jobs, _bind=True)
         if mode == "full_pool":
             out["index_topk_pool"] = st.index_topk_build_pool(c, w, self.q_seq, self.n_vis, bind=True)
+        elif "score_grouped" in names:
+            out["score"] = st.score_grouped(c, w, self.q_seq, self.n_vis, bind=True)
+            out["select"] = st.select(self.n_vis, bind=True)
         elif mode != "reuse":
             out["index_topk"] = st.index_topk(c, w, self.q_seq, self.n_vis, mode == "reindex_pool", bind=True)
         out["attn"] = st.attend(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True)
@@ -272,14 +272,14 @@ def cpu_baseline(wl, n_sample: int, reps: int):
                       f"run {reps}x; {el:.1f}s; numpy fp64, BLAS threads = cores"}
 
 
-def measure_layers(name, steps, warmup, torch, C, layers_to_time):
+def measure_layers(name, steps, warmup, torch, C, layers_to_time, group: int = 1):
     """Graph-replay time of each listed layer's step (`steps` steps in graphs of
     steps_per_graph(steps) consecutive steps of that layer) and of the whole group (one
     group per graph); isolated launch times of the first listed layer's calls."""
     from synth import workloads
     wl = workloads.config(name)
     log(f"workload {name}: {wl.description}")
-    lb = LayerBench(wl, torch, C)
+    lb = LayerBench(wl, torch, C, group)
     res = {"wl": wl, "layers": {}}
     G = steps_per_graph(steps)
     res["per_graph"] = G
@@ -300,13 +300,13 @@ def measure_layers(name, steps, warmup, torch, C, layers_to_time):
     return res
 
 
-def measure_group(name, steps, warmup, torch, C):
+def measure_group(name, steps, warmup, torch, C, group: int = 1):
     """Graph-replay time of a workload's whole layer group (each layer with its own appends)
     captured as one graph: a decoder step, or an encoder group over a prefill chunk."""
     from synth import workloads
     wl = workloads.config(name)
     log(f"workload {name}: {wl.description}")
-    lb = LayerBench(wl, torch, C)
+    lb = LayerBench(wl, torch, C, group)
     g = lb.capture(list(range(len(wl.layers))))
     ms, _ = time_graph(g, steps, warmup, torch)
     del g, lb
@@ -322,6 +322,8 @@ def decoder_entry(wl, ms) -> dict:
             "us_per_decode_step": round(ms * 1e3, 2), "us_per_layer": round(ms * 1e3 / n, 2),
             "query_tokens_per_s": round(wl.n_q / (ms / 1e3), 1)}
 
+
+PREFILL_GROUP = 8   # rows of a prefill chunk scored per pass over the sequence's indexer K
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_score_select_c2_128k_traffic.md")
 TRAFFIC_SOURCES = ("fp4_kv_cache_layer_amd/csrc/score.hip", "fp4_kv_cache_layer_amd/csrc/select.h",
@@ -449,19 +451,36 @@ def main():
         n4 = len(r4["wl"].layers)
         modes["group_1m"] = {"layers": list(r4["wl"].layers), "us_per_group": round(r4["group_ms"] * 1e3, 2),
                              "query_tokens_per_s_per_layer": round(r4["wl"].n_q * n4 / (r4["group_ms"] / 1e3), 1)}
-        r5 = measure_layers("c5", max(args.steps // 5, 3), max(args.warmup // 5, 1), torch, C, [0])
+        # the chunk's rows all belong to one sequence: scored in groups of 8 over one pass of K
+        r5 = measure_layers("c5", max(args.steps // 5, 3), max(args.warmup // 5, 1), torch, C, [0], group=PREFILL_GROUP)
         wl5, ms5 = r5["wl"], r5["layers"][0]["ms"]
         rows = int(wl5.extra["counted_rows"])
-        modes["prefill_chunk_m2"] = {"query_rows": wl5.n_q, "counted_new_tokens": rows,
+        modes["prefill_chunk_m2"] = {"query_rows": wl5.n_q, "counted_new_tokens": rows, "scoring_group": PREFILL_GROUP,
                                      "us_per_chunk": round(ms5 * 1e3, 1),
                                      "new_tokens_per_s": round(rows / (ms5 / 1e3), 1),
                                      "isolated_launch_us": {k: round(v * 1000, 1) for k, v in r5["isolated"].items()}}
-        wle, mse = measure_group("enc_group", max(args.steps // 5, 3), max(args.warmup // 5, 1), torch, C)
+        wle, mse = measure_group("enc_group", max(args.steps // 5, 3), max(args.warmup // 5, 1), torch, C,
+                                 PREFILL_GROUP)
         rows = int(wle.extra["counted_rows"])
         modes["encoder_group_prefill_m2"] = {
             "layers": len(wle.layers), "structure": "Full + 5 Reuse, window state missed (replay rows rewrite it)",
             "query_rows": wle.n_q, "counted_new_tokens": rows, "us_per_chunk": round(mse * 1e3, 1),
-            "us_per_layer": round(mse * 1e3 / len(wle.layers), 1), "new_tokens_per_s": round(rows / (mse / 1e3), 1)}
+            "us_per_layer": round(mse * 1e3 / len(wle.layers), 1), "new_tokens_per_s": round(rows / (mse / 1e3), 1),
+            "scoring_group": PREFILL_GROUP}
+        # multi-token decode: 4 tokens of each of 16 sequences; the Full layer's scoring with
+        # each sequence's 4 rows in one pass over its K (group 4) and per row (group 1)
+        mt = {}
+        for g in (1, 4):
+            rm = measure_layers("mtd_128k", args.steps, args.warmup, torch, C, [0], group=g)
+            mt[g] = (rm["wl"], rm["layers"][0]["ms"], rm["isolated"])
+        wlm = mt[1][0]
+        modes["multi_token_decode_128k"] = {
+            "sequences": wlm.n_seq, "tokens_per_seq": int(wlm.extra["tokens_per_seq"]), "query_rows": wlm.n_q,
+            "us_per_layer_step": round(mt[1][1] * 1e3, 2),
+            "query_tokens_per_s": round(wlm.n_q / (mt[1][1] / 1e3), 1),
+            "us_per_layer_step_grouped_scoring": round(mt[4][1] * 1e3, 2),
+            "isolated_launch_us": {k: round(v * 1e3, 1) for k, v in mt[1][2].items()},
+            "isolated_launch_us_grouped": {k: round(v * 1e3, 1) for k, v in mt[4][2].items()}}
         for name, key in (("dec_128k", "decoder_128k"), ("dec_1m", "decoder_1m")):
             wld, msd = measure_group(name, args.steps, args.warmup, torch, C)
             modes[key] = decoder_entry(wld, msd)

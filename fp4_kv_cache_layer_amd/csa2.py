@@ -53,6 +53,7 @@ def lib() -> ctypes.CDLL:
         "csa2_last_error": ([], ctypes.c_char_p),
         "csa2_quantize_kv": ([vp, i32, i64, i32, i32, vp, i64, vp, vp, vp], i32),
         "csa2_quantize_kv_multi": ([vp, i32, vp], i32),
+        "csa2_index_score_grouped": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp], i32),
         "csa2_index_score": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64, vp],
                              i32),
         "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp,
@@ -210,6 +211,17 @@ def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scor
     if scores.shape[0] != q_codes.shape[0]:
         raise ValueError("index_score: scores rows != n_q")
     return _run("csa2_index_score", args + (_p(scores), scores.stride(0), _stream()), _bind)
+
+
+def csa2_index_score_grouped(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, group: int, scores,
+                             _bind: bool = False):
+    """csa2_index_score without a pool for rows in groups of `group` consecutive rows that
+    share a sequence (each group's indexer K is read once); operands as csa2_index_score."""
+    args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8)
+    _need(scores, torch.float32, 2, "scores")
+    if scores.shape[0] != q_codes.shape[0]:
+        raise ValueError("index_score_grouped: scores rows != n_q")
+    return _run("csa2_index_score_grouped", args[:12] + (int(group), _p(scores), scores.stride(0), _stream()), _bind)
 
 
 def csa2_index_topk_workspace_bytes(n_q: int, n_slots: int, k: int, in_pool: bool = False) -> int:

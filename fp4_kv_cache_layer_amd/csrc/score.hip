@@ -74,6 +74,36 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 // Slots and rows are 32-bit (seq_cap <= 2^26, so byte offsets within a sequence fit in 32
 // bits) and the sequence's base pointers are workgroup-uniform, so each load is a scalar
 // base plus one 32-bit vector offset.
+// Scores of the 64 entries of one step (four 16-entry MFMA tiles) for one query row: A =
+// the row's indexer Q (16 heads x 128 channels, this lane: head `lane % 16`, channels
+// 32*kb..+31), B = the tiles' indexer K.  Lane l returns the score of entry l of the step.
+__device__ __forceinline__ float score_tiles(const v8i& a, int a_scale, const float (&wv)[4], int kb,
+                                             const uint4 (&bc)[4], const int (&bs)[4]) {
+  float part[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const v8i b = {(int)bc[t].x, (int)bc[t].y, (int)bc[t].z, (int)bc[t].w, 0, 0, 0, 0};
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    // formats 4/4 = E2M1 for both operands; scales are E8M0, byte 0 of each lane's VGPR
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 4, 0, a_scale, 0, bs[t]);
+    float p = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p += wv[r] * fmaxf(acc[r], 0.0f);
+    part[t] = p;
+  }
+  // reduce-scatter over the 4 lane groups: lane group g ends with tile g's full sum
+  const bool b1 = (kb & 2) != 0, b0 = (kb & 1) != 0;
+  const float s0 = b1 ? part[0] : part[2];
+  const float s1 = b1 ? part[1] : part[3];
+  const float r0 = __shfl_xor(s0, 32);
+  const float r1 = __shfl_xor(s1, 32);
+  const float k0 = (b1 ? part[2] : part[0]) + r0;
+  const float k1 = (b1 ? part[3] : part[1]) + r1;
+  const float send = b0 ? k0 : k1;
+  const float recv = __shfl_xor(send, 16);
+  return (b0 ? k1 : k0) + recv;
+}
+
 template <bool kPool>
 struct QueryScorer {
   v8i a;             // A operand: indexer Q rows (heads), 32 FP4 values per lane
@@ -154,31 +184,98 @@ struct QueryScorer {
 
   // scores of the 64 entries of one step; lane l returns the score of entry l
   __device__ __forceinline__ float score_step(const uint4 (&bc)[4], const int (&bs)[4]) const {
-    float part[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const v8i b = {(int)bc[t].x, (int)bc[t].y, (int)bc[t].z, (int)bc[t].w, 0, 0, 0, 0};
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      // formats 4/4 = E2M1 for both operands; scales are E8M0, byte 0 of each lane's VGPR
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 4, 0, a_scale, 0, bs[t]);
-      float p = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p += wv[r] * fmaxf(acc[r], 0.0f);
-      part[t] = p;
-    }
-    // reduce-scatter over the 4 lane groups: lane group g ends with tile g's full sum
-    const bool b1 = (kb & 2) != 0, b0 = (kb & 1) != 0;
-    const float s0 = b1 ? part[0] : part[2];
-    const float s1 = b1 ? part[1] : part[3];
-    const float r0 = __shfl_xor(s0, 32);
-    const float r1 = __shfl_xor(s1, 32);
-    const float k0 = (b1 ? part[2] : part[0]) + r0;
-    const float k1 = (b1 ? part[3] : part[1]) + r1;
-    const float send = b0 ? k0 : k1;
-    const float recv = __shfl_xor(send, 16);
-    return (b0 ? k1 : k0) + recv;
+    return score_tiles(a, a_scale, wv, kb, bc, bs);
   }
 };
+
+// ---- several query rows of one sequence over one pass of its indexer K ----
+// Multi-token decode (several tokens of a sequence verified at once) and the rows of a
+// prefill chunk score the same K stream: a workgroup takes a group of up to kGroupMax
+// consecutive rows of one sequence and a chunk of its entries, loads each step's K tiles
+// once and runs the MFMAs of every row of the group on them, so K is read once per group
+// instead of once per row.  The arithmetic per (row, entry) is that of k_score_decode, so
+// the scores are bit-identical to the per-row kernel's.
+constexpr int kGroupMax = 8;
+
+__global__ __launch_bounds__(kScoreThreads) void k_score_grouped(ScoreArgs s, int n_q, int group) {
+  const int gi = blockIdx.y;
+  const int chunk = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = lane & 15, kb = lane >> 4;
+  const int r0 = gi * group;
+  const int nr = n_q - r0 < group ? n_q - r0 : group;
+  const int seq = s.q_seq[r0];
+  if (seq < 0 || seq >= s.n_seq) return;
+
+  // the rows' A operands, scales, head weights and visible counts; a row of another
+  // sequence than the group's first row is left out (it gets no scores)
+  uint4 qa[kGroupMax];
+  int asc[kGroupMax];
+  float wv[kGroupMax][4];
+  int nvr[kGroupMax];
+  int nv_max = 0;
+#pragma unroll
+  for (int r = 0; r < kGroupMax; ++r) {
+    const int q = r0 + r;
+    const bool ok = r < nr && s.q_seq[q] == seq;
+    int64_t v = ok ? s.n_vis[q] : 0;
+    nvr[r] = (int)(v < 0 ? 0 : (v > s.seq_cap ? s.seq_cap : v));
+    nv_max = nvr[r] > nv_max ? nvr[r] : nv_max;
+    qa[r] = make_uint4(0u, 0u, 0u, 0u);
+    asc[r] = 127;
+    if (ok && row < s.n_heads) {
+      const int64_t hr = (int64_t)q * s.n_heads + row;
+      qa[r] = *reinterpret_cast<const uint4*>(s.q_codes + hr * 64 + kb * 16);
+      asc[r] = s.q_scales[hr * 4 + kb];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 4 * kb + j;
+      wv[r][j] = ok && h < s.n_heads ? s.w[(int64_t)q * s.n_heads + h] : 0.0f;
+    }
+  }
+  const int chunk_lo = chunk * s.chunk_len;
+  if (chunk_lo >= nv_max) return;
+  const int hi = chunk_lo + s.chunk_len < nv_max ? chunk_lo + s.chunk_len : nv_max;
+  const uint8_t* kc = s.k_codes + (int64_t)seq * s.seq_cap * 64;
+  const uint8_t* ks = s.k_scales + (int64_t)seq * s.seq_cap * 4;
+  // entries past the group's visible range read entry 0 and their results are discarded
+  auto load_step = [&](int base, uint4 (&bc)[4], int (&bs)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int e = base + 16 * t + row;
+      const uint32_t pos = e < nv_max ? (uint32_t)e : 0u;
+      const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(kc + (pos * 64u + kb * 16u)));
+      bc[t] = make_uint4(v.x, v.y, v.z, v.w);
+      bs[t] = ks[pos * 4u + kb];
+    }
+  };
+  int base = chunk_lo + wave * kScoreStep;
+  uint4 bc[4];
+  int bs[4];
+  if (base < hi) load_step(base, bc, bs);
+  for (; base < hi; base += 4 * kScoreStep) {
+    uint4 bcn[4];
+    int bsn[4];
+    const int next = base + 4 * kScoreStep;
+    load_step(next < hi ? next : base, bcn, bsn);
+    const int slot = base + lane;
+#pragma unroll
+    for (int r = 0; r < kGroupMax; ++r) {
+      if (r < nr) {  // uniform
+        const v8i a = {(int)qa[r].x, (int)qa[r].y, (int)qa[r].z, (int)qa[r].w, 0, 0, 0, 0};
+        const float v = score_tiles(a, asc[r], wv[r], kb, bc, bs);
+        if (slot < nvr[r]) s.scores[(int64_t)(r0 + r) * s.scores_stride + slot] = v;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bc[t] = bcn[t];
+      bs[t] = bsn[t];
+    }
+  }
+}
 
 template <bool kPool>
 __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
@@ -390,6 +487,35 @@ extern "C" int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales,
   ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
                           n_cand_blocks, block, max_cand_blocks, n_slots);
   return launch_score(a, n_q, scores, scores_stride, (hipStream_t)stream);
+}
+
+extern "C" int csa2_index_score_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                                        int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                                        int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                                        int group, float* scores, int64_t scores_stride, void* stream) {
+  int64_t n_slots = 0;
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                            nullptr, nullptr, 0, 0, &n_slots);
+  if (rc != CSA2_OK) return rc;
+  if (!scores) return CSA2_ERR_NULL;
+  if (group < 1 || group > kGroupMax || scores_stride < n_slots) return CSA2_ERR_SHAPE;
+  if (n_q == 0 || n_slots == 0) return CSA2_OK;
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, nullptr,
+                          nullptr, 0, 0, n_slots);
+  const int64_t groups = ((int64_t)n_q + group - 1) / group;
+  // chunks of 4,096 entries, halved (down to 1,024) while that leaves fewer than four
+  // workgroups per CU
+  int chunk_len = kScoreChunk;
+  while (chunk_len > 1024 && ((n_slots + chunk_len - 1) / chunk_len) * groups < 1024) chunk_len /= 2;
+  const int64_t chunks = (n_slots + chunk_len - 1) / chunk_len;
+  if (chunks > 0x7fffffffLL || groups > 65535) return CSA2_ERR_SHAPE;
+  a.scores = scores;
+  a.scores_stride = scores_stride;
+  a.chunk_len = chunk_len;
+  a.chunks = (int)chunks;
+  hipLaunchKernelGGL(k_score_grouped, dim3((unsigned)chunks, (unsigned)groups), dim3(kScoreThreads), 0,
+                     (hipStream_t)stream, a, n_q, group);
+  return csa2_check_launch();
 }
 
 extern "C" size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_pool) {

@@ -27,14 +27,16 @@ from . import csa2 as C
 MODES = ("full", "full_pool", "reuse", "reindex", "reindex_pool")
 
 
-def plan_group(modes, fused: bool = True) -> list:
+def plan_group(modes, fused: bool = True, group: int = 1) -> list:
     """Checks a layer group's mode sequence and returns the calls each layer makes.
 
     [W] "CSA2：跨层复用，能借就不自己算" and Figure 4: a Reindex layer re-scores the KV of the
     Full layer before it, a Reuse layer borrows the index set of the last scoring layer, so
     a group opens with a Full layer.  [W] "分层稀疏索引器": only the decoder's first Full
     layer builds the pool, and Reindex-in-pool layers need it.  Raises ValueError for a
-    sequence that breaks these rules."""
+    sequence that breaks these rules.  group > 1: the query rows come in groups of `group`
+    rows of one sequence, and the layers that score all visible entries read each group's
+    indexer K once (csa2_index_score_grouped, then csa2_topk)."""
     plan, have_kv, have_pool = [], False, False
     for i, m in enumerate(modes):
         if m not in MODES:
@@ -50,6 +52,8 @@ def plan_group(modes, fused: bool = True) -> list:
         elif m == "full_pool":
             calls = (["quantize_index_q", "index_topk_pool", "attend"] if fused else
                      ["quantize_index_q", "score", "select", "build_pool", "attend"])
+        elif group > 1 and m in ("full", "reindex"):
+            calls = ["quantize_index_q", "score_grouped", "select", "attend"]
         elif fused:
             calls = ["quantize_index_q", "index_topk_in_pool" if m == "reindex_pool" else "index_topk", "attend"]
         else:
@@ -89,11 +93,14 @@ class Csa2Step:
 
     def __init__(self, n_q: int, n_heads: int, idx_heads: int, seq_cap: int, k: int = 512, window: int = 128,
                  block: int = 8, max_blocks: int = 2048, idx_dim: int = 128, dim: int = 512,
-                 out_dtype=torch.float32, fused: bool = True, device="cuda"):
+                 out_dtype=torch.float32, fused: bool = True, group: int = 1, device="cuda"):
         """fused: score and select in one call (csa2_index_topk) wherever the layer does not
-        need the score array itself (it does only when it builds the pool)."""
+        need the score array itself (it does only when it builds the pool).  group: query
+        rows come in groups of `group` consecutive rows of one sequence (several tokens of a
+        sequence at once); layers scoring all visible entries then read each group's indexer
+        K once."""
         self.n_q, self.n_heads, self.idx_heads = n_q, n_heads, idx_heads
-        self.fused = fused
+        self.fused, self.group = fused, group
         self.seq_cap, self.k, self.window = seq_cap, k, window
         self.block, self.max_blocks, self.dim = block, max_blocks, dim
         dev = dict(device=device)
@@ -133,6 +140,10 @@ class Csa2Step:
                                       n_vis, self.scores, self.pool, self.pool_count, self.block, _bind=bind)
         return C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
                                   self.scores, _bind=bind)
+
+    def score_grouped(self, caches: Caches, w, q_seq, n_vis, bind=False):
+        return C.csa2_index_score_grouped(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq,
+                                          n_vis, self.group, self.scores, _bind=bind)
 
     def select(self, n_vis, in_pool: bool = False, bind=False):
         if in_pool:
@@ -176,7 +187,7 @@ class Csa2Step:
         with its own window cache caches.swa[i].  outs/lses: optional per-layer outputs
         (default: the step's own buffers, overwritten by each layer).  With bind=True returns
         the group's calls as one flat list of callables."""
-        plan = plan_group(modes, self.fused)
+        plan = plan_group(modes, self.fused, self.group)
         calls = []
         for i, (m, names) in enumerate(zip(modes, plan)):
             q_index, w, q_attn = inputs[i]
@@ -189,6 +200,8 @@ class Csa2Step:
                     c = self.index_topk_build_pool(caches, w, q_seq, n_vis, bind)
                 elif name in ("index_topk", "index_topk_in_pool"):
                     c = self.index_topk(caches, w, q_seq, n_vis, name.endswith("in_pool"), bind)
+                elif name == "score_grouped":
+                    c = self.score_grouped(caches, w, q_seq, n_vis, bind)
                 elif name in ("score", "score_pool"):
                     c = self.score(caches, w, q_seq, n_vis, name.endswith("pool"), bind)
                 elif name in ("select", "select_pool"):

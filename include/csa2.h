@@ -186,6 +186,26 @@ int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const floa
                      int max_cand_blocks, float* scores, int64_t scores_stride, void* stream);
 
 /*
+ * csa2_index_score_grouped -- csa2_index_score (without a pool) for query rows that come in
+ * groups sharing one sequence, reading each group's indexer K once.  For the tokens of a
+ * sequence scored together: several decode tokens verified at once, or the rows of a
+ * prefill chunk ([W] "CSA2：跨层复用，能借就不自己算": every query row is scored by the
+ * indexer against the sequence's visible entries; here rows of one sequence share the pass).
+ *
+ * Arguments as csa2_index_score with cand_blocks = NULL, plus
+ *   group   1..8: rows [g*group, (g+1)*group) form group g (the last one may be shorter)
+ *           and read the indexer K of the sequence of the group's first row.
+ * Every row's scores are written exactly as csa2_index_score writes them (bit-identical:
+ * the same arithmetic per row and entry); positions past a row's n_vis are not written.  A
+ * row whose q_seq differs from its group's first row, or lies outside [0, n_seq), gets no
+ * scores.  Errors: those of csa2_index_score, CSA2_ERR_SHAPE for group out of range.
+ */
+int csa2_index_score_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                             int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                             int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                             int group, float* scores, int64_t scores_stride, void* stream);
+
+/*
  * csa2_index_topk -- csa2_index_score followed by csa2_topk in one pass, without the score
  * array.  [W] "CSA2：跨层复用，能借就不自己算" (indexer scores, then Top-K, K = 512),
  * "分层稀疏索引器" (inside the pool).

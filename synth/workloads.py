@@ -108,6 +108,20 @@ def decode(name: str, seed: int, batch: int, n_entries: int, heads: int, idx_hea
                     new_entries=(n_entries - 1, 1), description=description)
 
 
+def multi_token_decode(name: str, seed: int, batch: int, tokens: int, n_entries: int, heads: int,
+                       idx_heads: int, description: str = "") -> Workload:
+    """Several decode tokens of each sequence at once (draft tokens verified together): the
+    last `tokens` positions of sequence b are query rows tokens*b .. tokens*b + tokens - 1,
+    each seeing the entries up to its own position (m = 1)."""
+    q_seq = np.repeat(np.arange(batch), tokens).astype(np.int32)
+    q_pos = np.tile(np.arange(n_entries - tokens, n_entries), batch).astype(np.int64)
+    wl = Workload(name=name, seed=seed, n_seq=batch, seq_cap=n_entries, m=1, heads=heads, idx_heads=idx_heads,
+                  q_seq=q_seq, q_pos=q_pos, replay_start=np.zeros(batch * tokens, dtype=np.int64),
+                  layers=("full",), new_entries=(n_entries - tokens, tokens), description=description)
+    wl.extra["tokens_per_seq"] = tokens
+    return wl
+
+
 def prefill(name: str, seed: int, prefix_tokens: int, chunk_tokens: int, m: int, heads: int,
             idx_heads: int, description: str = "", layers=("full",), swa_miss: bool = False) -> Workload:
     """One sequence: a cached prefix, then a chunk of new tokens.  The query rows are the
@@ -165,6 +179,10 @@ def config(name: str) -> Workload:
                        "encoder group prefill (Full + 5 Reuse, m=2) of a 4,096-token chunk after a "
                        "262,144-token prefix, prefix-cache miss: 128 replay rows rebuild the window",
                        layers=encoder_modes(), swa_miss=True)
+    if name == "mtd_128k":
+        return multi_token_decode("mtd_128k", 8, 16, 4, 131072, 64, 16,
+                                  "multi-token decode: 16 sequences x 4 tokens verified at once, 128K entries, "
+                                  "Full layer")
     if name == "dec_128k":
         return decode("dec_128k", 5, 32, 131072, 64, 16, decoder_modes(),
                       "decoder step: the 20 CSA2 layers of one decode token, 32 queries x 128K entries")
@@ -176,4 +194,4 @@ def config(name: str) -> Workload:
 
 CONFIG_NAMES = ("c1", "c2", "c3", "c4", "c5")
 DECODER_NAMES = ("dec_128k", "dec_1m")   # whole decoder steps (all 20 CSA2 layers)
-GROUP_NAMES = DECODER_NAMES + ("enc_group",)   # multi-layer workloads beyond the five configs
+GROUP_NAMES = DECODER_NAMES + ("enc_group", "mtd_128k")   # workloads beyond the five configs

@@ -196,7 +196,7 @@ def run_group_snapshots(case: Case, step, caches, window_appends: bool = False):
     inputs = [case.gpu_query_inputs(L) for L in range(len(modes))]
     calls = step.run_group(caches, modes, inputs, q_seq, n_vis, q_pos, rs, bind=True)
     snaps, at = [], 0
-    for L, names in enumerate(plan_group(modes, step.fused)):
+    for L, names in enumerate(plan_group(modes, step.fused, step.group)):
         if window_appends:
             C_ = C()
             lat = np.stack([wl.swa_latents(L, int(b), int(t), 1)[0] for b, t in zip(wl.q_seq, wl.q_pos)])

@@ -165,6 +165,49 @@ def test_index_score_parity(C, idx_heads):
         assert np.all(gs[qi, nv:] == 12345.0)   # positions past n_vis untouched
 
 
+@pytest.mark.parametrize("group", [1, 3, 8])
+def test_index_score_grouped_matches_per_row(C, group):
+    """Rows in groups sharing a sequence: bit-identical to the per-row kernel's scores; a row
+    of another sequence than its group's first row, and positions past n_vis, untouched."""
+    _say("index_score grouped", group)
+    q_seq = np.array([0, 0, 0, 1, 1, 1, 2, 2, 0, 1], np.int32)
+    n_vis = np.array([9000, 8990, 4097, 9000, 1, 64, 8999, 5000, 7000, 3333], np.int64)
+    wl = G.workloads.Workload(name="grouped", seed=31, n_seq=3, seq_cap=9000, m=1, heads=16, idx_heads=16,
+                              q_seq=q_seq, q_pos=n_vis - 1, replay_start=np.zeros(10, np.int64),
+                              layers=("full",), new_entries=(0, 0))
+    case = G.Case(wl)
+    caches = case.gpu_caches()
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq_d, n_vis_d, _, _ = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap)
+    st.quantize_index_q(q_idx)
+    st.scores.fill_(12345.0)
+    st.score(caches, w, q_seq_d, n_vis_d)
+    ref = st.scores.clone()
+    st.scores.fill_(-777.0)
+    C.csa2_index_score_grouped(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq_d, n_vis_d,
+                               group, st.scores)
+    torch.cuda.synchronize()
+    got, ref = st.scores.cpu().numpy(), ref.cpu().numpy()
+    for qi in range(wl.n_q):
+        nv = int(n_vis[qi])
+        if q_seq[qi] == q_seq[(qi // group) * group]:
+            assert np.array_equal(got[qi, :nv], ref[qi, :nv]), qi
+            assert np.all(got[qi, nv:] == -777.0)
+        else:
+            assert np.all(got[qi] == -777.0), qi
+    # and against the oracle on one row per sequence
+    for qi in (1, 3, 6):
+        if q_seq[qi] != q_seq[(qi // group) * group]:
+            continue
+        oc = case.oracle_caches(int(q_seq[qi]))
+        qc, qs, wq, _ = case.oracle_query(0, qi)
+        nv = int(n_vis[qi])
+        _, r = O.full_scores(qc, qs, wq, oc, nv)
+        assert np.all(np.abs(got[qi, :nv] - r) <= 1e-5 * np.abs(r) + 1e-6 * np.abs(r).max())
+
+
 def test_index_score_pool_slots(C):
     _say("index_score pool")
     case = _score_case(21, 2, 6000, [6000, 5003, 333], 16)

@@ -63,6 +63,27 @@ def test_decoder_step_full_size(C, name, samples):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("group,fused", [(4, True), (1, True), (1, False)])
+def test_multi_token_decode_full_size(C, group, fused):
+    """Multi-token decode: 16 sequences x 4 tokens at 128K through a Full layer, the 4 rows
+    of a sequence scored in one pass over its indexer K (group 4: grouped scores, then the
+    Top-K levels) or apart (group 1: fused per row, or scores then Top-K), with oracle parity
+    on rows of several sequences and token offsets."""
+    _say("multi-token decode, group", group, "fused" if fused else "two-call")
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    wl = workloads.config("mtd_128k")
+    case = G.Case(wl, swa_layers=range(len(wl.layers)))
+    caches = case.gpu_caches()
+    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group, fused=fused)
+    snaps = G.run_group_snapshots(case, step, caches)
+    for qi in (0, 3, 29, 62):
+        _say("  oracle query", qi)
+        G.check_group_query(case, caches, snaps, qi)
+    del caches, step
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.timeout(900)
 def test_encoder_group_prefill_window_miss(C):
     """An encoder CSA2 group (Full + 5 Reuse, m = 2) over a 4,096-token chunk after a
@@ -76,7 +97,7 @@ def test_encoder_group_prefill_window_miss(C):
     assert wl.extra["swa_miss"]
     case = G.Case(wl, swa_layers=range(len(wl.layers)))
     caches = case.gpu_caches(window_empty=True)
-    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap)
+    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=8)   # the chunk's rows: one sequence
     snaps = G.run_group_snapshots(case, step, caches, window_appends=True)
     for qi in (0, 127, 128, 3000, wl.n_q - 1):
         _say("  oracle query", qi, "t", int(wl.q_pos[qi]))
@@ -86,16 +107,18 @@ def test_encoder_group_prefill_window_miss(C):
 
 
 @pytest.mark.timeout(900)
-def test_prefill_chunk_full_size(C):
+@pytest.mark.parametrize("group", [8, 1])
+def test_prefill_chunk_full_size(C, group):
     """The m = 2 encoder prefill chunk: 4,096 new tokens after a 262,144-token prefix plus the
     128 bounded-replay rows, one sequence of 133,120 entries, run as one Full layer; oracle
-    parity on replay rows (first, middle, last), the first new row, a middle and the last row."""
-    _say("prefill chunk")
+    parity on replay rows (first, middle, last), the first new row, a middle and the last row;
+    the rows scored in groups of 8 over one pass of the indexer K, and one by one."""
+    _say("prefill chunk, group", group)
     from fp4_kv_cache_layer_amd.layer import Csa2Step
     wl = workloads.config("c5")
     case = G.Case(wl, swa_layers=(0,))
     caches = case.gpu_caches()
-    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap)
+    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group)
     snaps = G.run_group_snapshots(case, step, caches)
     for qi in (0, 63, 127, 128, 2100, wl.n_q - 1):
         _say("  oracle query", qi, "t", int(wl.q_pos[qi]), "n_vis", int(wl.n_vis[qi]))

@@ -51,6 +51,16 @@ def test_decoder_step_is_the_model_decoder():
         assert config(name).layers == decoder_modes()
 
 
+def test_grouped_plan_scores_then_selects():
+    plan = plan_group(["full", "reuse", "reindex", "full_pool", "reindex_pool"], group=4)
+    assert plan[0] == ["quantize_index_q", "score_grouped", "select", "attend"]
+    assert plan[2] == ["quantize_index_q", "score_grouped", "select", "attend"]
+    assert plan[3] == ["quantize_index_q", "index_topk_pool", "attend"]      # pool layers keep their path
+    assert plan[4] == ["quantize_index_q", "index_topk_in_pool", "attend"]
+    assert plan_group(["full"], group=1)[0] == ["quantize_index_q", "index_topk", "attend"]
+    assert plan_group(["full"], fused=False, group=4)[0] == ["quantize_index_q", "score_grouped", "select", "attend"]
+
+
 def test_unfused_plan_keeps_two_calls():
     plan = plan_group(["full", "reuse", "reindex", "reindex"], fused=False)
     assert plan[0] == ["quantize_index_q", "score", "select", "attend"]
