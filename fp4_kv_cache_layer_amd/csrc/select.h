@@ -44,20 +44,31 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t pos) {
 }
 __device__ __forceinline__ int32_t key_pos(uint64_t k) { return (int32_t)(0xffffffffu - (uint32_t)k); }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
 
-// wave-wide inclusive suffix sum (lane l gets the sum over lanes >= l)
-__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v, int lane) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const uint32_t o = __shfl_down(v, m);
-    v += (lane + m < 64) ? o : 0u;
-  }
+// max / min over the wave with DPP row operations and four readlanes (no LDS traffic)
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));  // row rotate 4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));  // row rotate 8
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
+}
+__device__ __forceinline__ uint32_t dpp_min_u32(uint32_t v) { return ~dpp_max_u32(~v); }
+
+// inclusive prefix sum over the wave with DPP: row shifts 1, 2, 4, 8 (zero fill) give each
+// 16-lane row its own scan, then row broadcasts of lanes 15 and 31 carry the row totals
+__device__ __forceinline__ uint32_t dpp_prefix_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr 1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr 2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr 4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr 8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast 15 -> rows 1, 3
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast 31 -> rows 2, 3
   return v;
 }
+
 
 // Selects the K largest of the 32*256 keys held by a 256-thread workgroup (key[i] of thread
 // t is candidate i*256 + t of the segment; 0 = no candidate) and writes them in candidate
@@ -78,49 +89,62 @@ __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, i
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   __shared__ uint32_t cnt[kTkWaves][kTkEpt];
-  __shared__ uint64_t red_hi[kTkWaves], red_lo[kTkWaves];
-  __shared__ uint32_t red_n[kTkWaves];
+  __shared__ uint32_t red[5][kTkWaves];
 
-  // ---- count, max and min of the valid keys ----
-  uint32_t n = 0;
-  uint64_t kmax = 0, kmin = ~0ull;
+  // ---- count (ballots) and the range of the high (score) words (DPP reductions) ----
+  uint32_t nw = 0, hmax = 0u, hmin = ~0u, lmax = 0u, lmin = ~0u;
 #pragma unroll
   for (int i = 0; i < kTkEpt; ++i) {
-    if (key[i]) {
-      ++n;
-      kmax = key[i] > kmax ? key[i] : kmax;
-      kmin = key[i] < kmin ? key[i] : kmin;
-    }
+    nw += (uint32_t)__popcll(__ballot(key[i] != 0ull));
+    const uint32_t h = (uint32_t)(key[i] >> 32), l = (uint32_t)key[i];
+    hmax = key[i] ? max(hmax, h) : hmax;
+    hmin = key[i] ? min(hmin, h) : hmin;
+    lmax = key[i] ? max(lmax, l) : lmax;
+    lmin = key[i] ? min(lmin, l) : lmin;
   }
-  for (int m = 32; m >= 1; m >>= 1) {
-    n += __shfl_xor(n, m);
-    uint64_t o = shfl_xor_u64(kmax, m);
-    kmax = o > kmax ? o : kmax;
-    o = shfl_xor_u64(kmin, m);
-    kmin = o < kmin ? o : kmin;
-  }
+  hmax = dpp_max_u32(hmax);
+  hmin = dpp_min_u32(hmin);
+  lmax = dpp_max_u32(lmax);
+  lmin = dpp_min_u32(lmin);
   if (lane == 0) {
-    red_n[wave] = n;
-    red_hi[wave] = kmax;
-    red_lo[wave] = kmin;
+    red[0][wave] = nw;
+    red[1][wave] = hmax;
+    red[2][wave] = hmin;
+    red[3][wave] = lmax;
+    red[4][wave] = lmin;
   }
   __syncthreads();
-  n = 0;
-  kmax = 0;
-  kmin = ~0ull;
+  uint32_t n = 0;
+  hmax = 0u;
+  hmin = ~0u;
 #pragma unroll
   for (int wv = 0; wv < kTkWaves; ++wv) {
-    n += red_n[wv];
-    kmax = red_hi[wv] > kmax ? red_hi[wv] : kmax;
-    kmin = red_lo[wv] < kmin ? red_lo[wv] : kmin;
+    n += red[0][wv];
+    hmax = max(hmax, red[1][wv]);
+    hmin = min(hmin, red[2][wv]);
   }
 
   // ---- radix select: find (prefix, mask) such that exactly K keys have (key&mask) >= prefix ----
   uint64_t prefix = 0, mask = 0;
   if (n > (uint32_t)K) {
-    const int hb = 63 - __clzll(kmax ^ kmin);  // n >= 2 unique keys -> kmax != kmin
+    int hb;        // highest bit where the largest and smallest key differ
+    uint64_t top;  // the largest key's bits above hb
+    if (hmax != hmin) {
+      hb = 32 + 31 - __clz(hmax ^ hmin);
+      top = (uint64_t)hmax << 32;
+    } else {       // every score equal: the keys differ in their position words only
+      lmax = 0u;
+      lmin = ~0u;
+#pragma unroll
+      for (int wv = 0; wv < kTkWaves; ++wv) {
+        lmax = max(lmax, red[3][wv]);
+        lmin = min(lmin, red[4][wv]);
+      }
+      hb = 31 - __clz(lmax ^ lmin);  // n >= 2 unique keys: lmax != lmin
+      top = ((uint64_t)hmax << 32) | lmax;
+    }
     mask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
-    prefix = kmax & mask;
+    prefix = top & mask;
     int shift = hb - 7 > 0 ? hb - 7 : 0;
     uint32_t need = (uint32_t)K;
     for (int pass = 0;; ++pass) {
@@ -145,7 +169,8 @@ __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, i
         }
       }
       const uint32_t tot = hs[0] + hs[1] + hs[2] + hs[3];
-      const uint32_t incl = wave_suffix_sum(tot, lane);
+      const uint32_t pre = dpp_prefix_sum(tot);
+      const uint32_t incl = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + tot;  // bins >= 4*lane
       const uint32_t above_lane = incl - tot;
       // the boundary digit is the largest d with (count of digits >= d) >= need
       uint32_t d = 0, above = 0, inbin = 0;
@@ -193,12 +218,7 @@ __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, i
       before_w += wv < wave ? c : 0u;
     }
   }
-  uint32_t excl = tot_i;  // exclusive prefix over lanes 0..31
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) {
-    const uint32_t o = __shfl_up(excl, m);
-    excl += (lane >= m) ? o : 0u;
-  }
+  const uint32_t excl = dpp_prefix_sum(tot_i);   // inclusive over slots (lanes 0..31; the rest hold 0)
   const uint32_t total = __builtin_amdgcn_readlane(excl, kTkEpt - 1);
   const uint32_t off = excl - tot_i + before_w;
   const uint32_t nsel = total < (uint32_t)K ? total : (uint32_t)K;

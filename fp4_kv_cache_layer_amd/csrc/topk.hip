@@ -104,30 +104,6 @@ constexpr int kFinThreads = 1024;
 constexpr int kFinWaves = kFinThreads / 64;
 constexpr int kFinEpt = kTkSeg / kFinThreads;   // 8
 
-// max / min over the wave with DPP row operations and four readlanes (no LDS traffic)
-__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));   // lane ^ 1
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));   // lane ^ 2
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false));  // row rotate 4
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false));  // row rotate 8
-  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
-  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
-  return max(a, b);
-}
-__device__ __forceinline__ uint32_t dpp_min_u32(uint32_t v) { return ~dpp_max_u32(~v); }
-
-// inclusive prefix sum over the wave with DPP: row shifts 1, 2, 4, 8 (zero fill) give each
-// 16-lane row its own scan, then row broadcasts of lanes 15 and 31 carry the row totals
-__device__ __forceinline__ uint32_t dpp_prefix_sum(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr 1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr 2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr 4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr 8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast 15 -> rows 1, 3
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast 31 -> rows 2, 3
-  return v;
-}
-
 __global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
   const int q = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
