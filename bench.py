@@ -14,8 +14,9 @@ heads, 16 indexer heads; metric query tokens per second per layer.  Also reporte
 --no-modes): every mode of the 128K layer group (Full, 3 Reuse, Reindex; 32 queries) and
 of the 1M group (Full + pool, 4 Reindex inside the pool; 8 queries), each group as one
 graph, the m = 2 prefill chunk, an encoder group (Full + 5 Reuse) over that chunk after a
-window-state miss, and the whole decoder step (its 20 CSA2 layers as one graph) at 128K and
-1M.  The CPU baseline times the fp64 oracle on a bounded sample of the headline step.
+window-state miss, multi-token decode, the headline step with the NVFP4-style indexer
+(E4M3 per 16 channels), and the whole decoder step (its 20 CSA2 layers as one graph) at
+128K and 1M.  The CPU baseline times the fp64 oracle on a bounded sample of the headline step.
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -34,7 +35,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MAIN_ENTRY_B = 288      # 256 B E2M1 codes + 32 E4M3 scales
-INDEX_ENTRY_B = 68      # 64 B E2M1 codes + 4 E8M0 scales
 TOPK, WINDOW, BLOCK, MAX_BLOCKS = 512, 128, 8, 2048
 
 
@@ -51,13 +51,14 @@ class LayerBench:
     (`swa_miss`: the prefix's window state is not cached) the rings start empty and every
     layer writes the window entries of all its query rows, replay rows included."""
 
-    def __init__(self, wl, torch, C, group: int = 1):
-        from fp4_kv_cache_layer_amd.layer import Caches, Csa2Step, plan_group
+    def __init__(self, wl, torch, C, group: int = 1, index_fmt: str = "mxfp4"):
+        from fp4_kv_cache_layer_amd.layer import INDEX_FORMATS, Caches, Csa2Step, plan_group
         self.wl, self.torch, self.C = wl, torch, C
-        self.plan = plan_group(wl.layers, group=group)
+        self.plan = plan_group(wl.layers, group=group, index_fmt=index_fmt)
+        self.ik_fmt, self.ik_group = INDEX_FORMATS[index_fmt]
         n_layers = len(wl.layers)
         dev = "cuda"
-        caches = Caches.empty(wl.n_seq, wl.seq_cap, range(n_layers), wl.swa_cap)
+        caches = Caches.empty(wl.n_seq, wl.seq_cap, range(n_layers), wl.swa_cap, index_fmt=index_fmt)
         caches.swa_base.fill_(wl.swa_base)
         chunk = 1 << 16
         t0 = time.time()
@@ -67,7 +68,7 @@ class LayerBench:
                 lat = torch.from_numpy(wl.main_latents(b, r0, n)).to(dev)
                 C.csa2_quantize_kv(lat, C.FMT_NVFP4, caches.kv_codes[b, r0:r0 + n], caches.kv_scales[b, r0:r0 + n])
                 ik = torch.from_numpy(wl.index_k_latents(b, r0, n)).to(dev)
-                C.csa2_quantize_kv(ik, C.FMT_MXFP4, caches.ik_codes[b, r0:r0 + n], caches.ik_scales[b, r0:r0 + n])
+                C.csa2_quantize_kv(ik, self.ik_fmt, caches.ik_codes[b, r0:r0 + n], caches.ik_scales[b, r0:r0 + n])
             t = int(wl.q_pos[wl.q_seq == b].max())
             p0 = max(0, t - wl.swa_cap + 1)
             rows = torch.from_numpy(((np.arange(p0, t + 1) - wl.swa_base) % wl.swa_cap).astype(np.int64)).to(dev)
@@ -107,7 +108,7 @@ class LayerBench:
                         for L in range(n_layers)]
         self.dst_entry = torch.from_numpy(ent_seq * wl.seq_cap + ent_row).to(dev)
         self.dst_swa = torch.from_numpy(tok_seq * wl.swa_cap + (tok_pos - wl.swa_base) % wl.swa_cap).to(dev)
-        self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group)
+        self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group, index_fmt=index_fmt)
 
     def calls(self, L: int):
         """Layer L's step as {phase: bound call} bound to the current stream, in order."""
@@ -120,14 +121,14 @@ class LayerBench:
         jobs = []
         if mode.startswith("full"):
             jobs += [(self.new_main, C.FMT_NVFP4, flat(c.kv_codes), flat(c.kv_scales), self.dst_entry),
-                     (self.new_ik, C.FMT_MXFP4, flat(c.ik_codes), flat(c.ik_scales), self.dst_entry)]
+                     (self.new_ik, self.ik_fmt, flat(c.ik_codes), flat(c.ik_scales), self.dst_entry)]
         jobs.append((self.new_swa[L], C.FMT_FP8, flat(c.swa[L]), None, self.dst_swa))
         q_idx, w, qa = self.inputs[L]
         names = self.plan[L]
         if "quantize_index_q" in names:
             n_q, h, d = q_idx.shape
-            jobs.append((q_idx.view(n_q * h, d), C.FMT_MXFP4, st.qi_codes.view(n_q * h, d // 2),
-                         st.qi_scales.view(n_q * h, d // 32), None))
+            jobs.append((q_idx.view(n_q * h, d), self.ik_fmt, st.qi_codes.view(n_q * h, d // 2),
+                         st.qi_scales.view(n_q * h, d // self.ik_group), None))
         out["quantize"] = C.csa2_quantize_kv_multi(jobs, _bind=True)
         if mode == "full_pool":
             out["index_topk_pool"] = st.index_topk_build_pool(c, w, self.q_seq, self.n_vis, bind=True)
@@ -207,24 +208,25 @@ def time_graph(graph, replays, warmup, torch, per_replay=1):
     return e0.elapsed_time(e1) / (replays * per_replay), time.perf_counter() - wall0
 
 
-def score_bytes(wl, mode: str) -> int:
-    """Algorithmic HBM bytes of one scoring pass: every candidate's indexer-K entry (68 B;
-    all visible entries, or the 16,384 pool positions) plus each query's MXFP4 indexer Q
-    and head weights."""
+def score_bytes(wl, mode: str, index_fmt: str = "mxfp4") -> int:
+    """Algorithmic HBM bytes of one scoring pass: every candidate's indexer-K entry (68 B in
+    MXFP4, 72 B in NVFP4; all visible entries, or the 16,384 pool positions) plus each
+    query's indexer Q and head weights."""
     if mode == "reuse":
         return 0
+    n_sc = 8 if index_fmt == "nvfp4" else 4
     cand = np.minimum(wl.n_vis, MAX_BLOCKS * BLOCK) if mode == "reindex_pool" else wl.n_vis
-    return int(cand.sum()) * INDEX_ENTRY_B + wl.n_q * wl.idx_heads * (64 + 4 + 4)
+    return int(cand.sum()) * (64 + n_sc) + wl.n_q * wl.idx_heads * (64 + n_sc + 4)
 
 
-def step_bytes(wl, mode: str) -> int:
+def step_bytes(wl, mode: str, index_fmt: str = "mxfp4") -> int:
     """Algorithmic HBM bytes of one layer step: what must cross HBM at least once
     (scoring input; the gathered main-KV entries, window, Q, output, LSE and index set of
     attention; the pool ids where a pool is written or read)."""
     k, W = TOPK, WINDOW
     attn = k * MAIN_ENTRY_B + W * 512 + wl.heads * 512 * (2 + 4) + wl.heads * 4 + k * 4
     pool = MAX_BLOCKS * 4 if mode in ("full_pool", "reindex_pool") else 0
-    return score_bytes(wl, mode) + wl.n_q * (attn + pool)
+    return score_bytes(wl, mode, index_fmt) + wl.n_q * (attn + pool)
 
 
 def cpu_baseline(wl, n_sample: int, reps: int):
@@ -272,14 +274,14 @@ def cpu_baseline(wl, n_sample: int, reps: int):
                       f"run {reps}x; {el:.1f}s; numpy fp64, BLAS threads = cores"}
 
 
-def measure_layers(name, steps, warmup, torch, C, layers_to_time, group: int = 1):
+def measure_layers(name, steps, warmup, torch, C, layers_to_time, group: int = 1, index_fmt: str = "mxfp4"):
     """Graph-replay time of each listed layer's step (`steps` steps in graphs of
     steps_per_graph(steps) consecutive steps of that layer) and of the whole group (one
     group per graph); isolated launch times of the first listed layer's calls."""
     from synth import workloads
     wl = workloads.config(name)
     log(f"workload {name}: {wl.description}")
-    lb = LayerBench(wl, torch, C, group)
+    lb = LayerBench(wl, torch, C, group, index_fmt)
     res = {"wl": wl, "layers": {}}
     G = steps_per_graph(steps)
     res["per_graph"] = G
@@ -481,6 +483,17 @@ def main():
             "us_per_layer_step_grouped_scoring": round(mt[4][1] * 1e3, 2),
             "isolated_launch_us": {k: round(v * 1e3, 1) for k, v in mt[1][2].items()},
             "isolated_launch_us_grouped": {k: round(v * 1e3, 1) for k, v in mt[4][2].items()}}
+        # the NVFP4-style indexer variant on the headline step
+        rn = measure_layers("c2", args.steps, args.warmup, torch, C, [0], index_fmt="nvfp4")
+        wln, msn, isn = rn["wl"], rn["layers"][0]["ms"], rn["isolated"]
+        bn = score_bytes(wln, "full", "nvfp4")
+        gbs = bn / (isn["index_topk"] / 1e3) / 1e9
+        modes["full_128k_nvfp4_indexer"] = {
+            "index_format": "E2M1 + E4M3 per 16 (72 B per indexer-K entry), fp16 MFMA scoring",
+            "us_per_layer_step": round(msn * 1e3, 2), "query_tokens_per_s": round(wln.n_q / (msn / 1e3), 1),
+            "index_topk_us": round(isn["index_topk"] * 1e3, 2), "index_topk_gb_per_s": round(gbs, 1),
+            "index_topk_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "index_topk_bytes": bn,
+            "isolated_launch_us": {k: round(v * 1e3, 2) for k, v in isn.items()}}
         for name, key in (("dec_128k", "decoder_128k"), ("dec_1m", "decoder_1m")):
             wld, msd = measure_group(name, args.steps, args.warmup, torch, C)
             modes[key] = decoder_entry(wld, msd)

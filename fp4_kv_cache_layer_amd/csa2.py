@@ -59,6 +59,10 @@ def lib() -> ctypes.CDLL:
         "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp,
                              sz, vp], i32),
         "csa2_index_topk_workspace_bytes": ([i32, i64, i32, i32], sz),
+        "csa2_index_score_nvfp4": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64,
+                                    vp], i32),
+        "csa2_index_topk_nvfp4": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp,
+                                   vp, sz, vp], i32),
         "csa2_index_topk_pool": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp, i32, i32, vp, vp,
                                   vp, sz, vp], i32),
         "csa2_index_topk_pool_workspace_bytes": ([i32, i64, i32, i32, i32], sz),
@@ -174,9 +178,11 @@ def csa2_quantize_kv_multi(jobs, _bind: bool = False):
     return _run("csa2_quantize_kv_multi", (ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream()), _bind)
 
 
-def _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block):
+def _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block,
+                scale_group: int = 32):
     """Checks the indexer operands shared by csa2_index_score and csa2_index_topk and returns
-    the C arguments from q_codes to max_cand_blocks, and n_slots."""
+    the C arguments from q_codes to max_cand_blocks, and n_slots.  scale_group: channels per
+    scale byte (32 for MXFP4, 16 for the NVFP4 variants)."""
     _need(q_codes, torch.uint8, 3, "q_codes")
     _need(q_scales, torch.uint8, 3, "q_scales")
     _need(w, torch.float32, 2, "w")
@@ -186,8 +192,9 @@ def _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_bloc
     _need(n_vis, torch.int64, 1, "n_vis")
     n_q, h, half = q_codes.shape
     n_seq, seq_cap, kh = k_codes.shape
-    if q_scales.shape != (n_q, h, half // 16) or w.shape != (n_q, h) or kh != half or \
-            k_scales.shape != (n_seq, seq_cap, half // 16) or q_seq.shape[0] != n_q or n_vis.shape[0] != n_q:
+    n_sc = 2 * half // scale_group
+    if q_scales.shape != (n_q, h, n_sc) or w.shape != (n_q, h) or kh != half or \
+            k_scales.shape != (n_seq, seq_cap, n_sc) or q_seq.shape[0] != n_q or n_vis.shape[0] != n_q:
         raise ValueError("index: inconsistent shapes")
     max_blocks = 0
     if cand_blocks is not None:
@@ -201,16 +208,31 @@ def _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_bloc
             _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks), block, max_blocks), n_slots
 
 
+def _index_score(name, scale_group, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores, cand_blocks,
+                 n_cand_blocks, block, bind):
+    args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block,
+                          scale_group)
+    _need(scores, torch.float32, 2, "scores")
+    if scores.shape[0] != q_codes.shape[0]:
+        raise ValueError("index_score: scores rows != n_q")
+    return _run(name, args + (_p(scores), scores.stride(0), _stream()), bind)
+
+
 def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
                      cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
     """q_codes [n_q, H_I, 64], q_scales [n_q, H_I, 4], w [n_q, H_I] f32;
     k_codes [n_seq, seq_cap, 64], k_scales [n_seq, seq_cap, 4]; q_seq [n_q] int32,
     n_vis [n_q] int64; scores [n_q, stride] f32; cand_blocks [n_q, max_blocks] int32."""
-    args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block)
-    _need(scores, torch.float32, 2, "scores")
-    if scores.shape[0] != q_codes.shape[0]:
-        raise ValueError("index_score: scores rows != n_q")
-    return _run("csa2_index_score", args + (_p(scores), scores.stride(0), _stream()), _bind)
+    return _index_score("csa2_index_score", 32, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
+                        cand_blocks, n_cand_blocks, block, _bind)
+
+
+def csa2_index_score_nvfp4(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
+                           cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
+    """csa2_index_score for NVFP4 indexer Q/K: q_scales [n_q, H_I, 8] and k_scales
+    [n_seq, seq_cap, 8] hold one E4M3 scale per 16 channels."""
+    return _index_score("csa2_index_score_nvfp4", 16, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
+                        cand_blocks, n_cand_blocks, block, _bind)
 
 
 def csa2_index_score_grouped(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, group: int, scores,
@@ -232,8 +254,21 @@ def csa2_index_topk(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: in
                     workspace=None, cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
     """Scores and Top-K in one pass: the operands of csa2_index_score (without scores) ->
     idx_out [n_q, k] int32, count_out [n_q] int32, as csa2_topk returns them."""
+    return _index_topk("csa2_index_topk", 32, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k, idx_out,
+                       count_out, workspace, cand_blocks, n_cand_blocks, block, _bind)
+
+
+def csa2_index_topk_nvfp4(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, idx_out, count_out,
+                          workspace=None, cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
+    """csa2_index_topk for NVFP4 indexer Q/K (scales [.., 8]: one E4M3 per 16 channels)."""
+    return _index_topk("csa2_index_topk_nvfp4", 16, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k,
+                       idx_out, count_out, workspace, cand_blocks, n_cand_blocks, block, _bind)
+
+
+def _index_topk(name, scale_group, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k, idx_out, count_out,
+                workspace, cand_blocks, n_cand_blocks, block, _bind):
     args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks,
-                                block)
+                                block, scale_group)
     _need(idx_out, torch.int32, 2, "idx_out")
     _need(count_out, torch.int32, 1, "count_out")
     n_q = q_codes.shape[0]
@@ -243,8 +278,7 @@ def csa2_index_topk(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: in
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_codes.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    return _run("csa2_index_topk", args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, _stream()),
-                _bind)
+    return _run(name, args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, _stream()), _bind)
 
 
 def csa2_index_topk_pool_workspace_bytes(n_q: int, n_slots: int, k: int, block: int, max_blocks: int) -> int:

@@ -70,10 +70,21 @@ struct ScoreArgs {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-// One query's view of the cache: MFMA operands, slot -> row mapping, one scoring step.
-// Slots and rows are 32-bit (seq_cap <= 2^26, so byte offsets within a sequence fit in 32
-// bits) and the sequence's base pointers are workgroup-uniform, so each load is a scalar
-// base plus one 32-bit vector offset.
+// reduce-scatter of the four tiles' per-lane-group partial sums: lane group g ends with tile
+// g's full sum, so lane l holds the score of entry l of the step
+__device__ __forceinline__ float scatter_tiles(const float (&part)[4], int kb) {
+  const bool b1 = (kb & 2) != 0, b0 = (kb & 1) != 0;
+  const float s0 = b1 ? part[0] : part[2];
+  const float s1 = b1 ? part[1] : part[3];
+  const float r0 = __shfl_xor(s0, 32);
+  const float r1 = __shfl_xor(s1, 32);
+  const float k0 = (b1 ? part[2] : part[0]) + r0;
+  const float k1 = (b1 ? part[3] : part[1]) + r1;
+  const float send = b0 ? k0 : k1;
+  const float recv = __shfl_xor(send, 16);
+  return (b0 ? k1 : k0) + recv;
+}
+
 // Scores of the 64 entries of one step (four 16-entry MFMA tiles) for one query row: A =
 // the row's indexer Q (16 heads x 128 channels, this lane: head `lane % 16`, channels
 // 32*kb..+31), B = the tiles' indexer K.  Lane l returns the score of entry l of the step.
@@ -91,23 +102,67 @@ __device__ __forceinline__ float score_tiles(const v8i& a, int a_scale, const fl
     for (int r = 0; r < 4; ++r) p += wv[r] * fmaxf(acc[r], 0.0f);
     part[t] = p;
   }
-  // reduce-scatter over the 4 lane groups: lane group g ends with tile g's full sum
-  const bool b1 = (kb & 2) != 0, b0 = (kb & 1) != 0;
-  const float s0 = b1 ? part[0] : part[2];
-  const float s1 = b1 ? part[1] : part[3];
-  const float r0 = __shfl_xor(s0, 32);
-  const float r1 = __shfl_xor(s1, 32);
-  const float k0 = (b1 ? part[2] : part[0]) + r0;
-  const float k1 = (b1 ? part[3] : part[1]) + r1;
-  const float send = b0 ? k0 : k1;
-  const float recv = __shfl_xor(send, 16);
-  return (b0 ? k1 : k0) + recv;
+  return scatter_tiles(part, kb);
 }
 
-template <bool kPool>
+// ---- NVFP4-style indexer operands (E2M1 + one E4M3 scale per 16 channels) ----
+// The scaled matrix-core instruction takes power-of-two (E8M0) scales per 32 elements, so
+// this format runs as fp16 MFMAs on dequantised operands.  A lane's 16 code bytes (32
+// channels) become 32 fp16 values: the gfx950 converts apply only the exponent of their
+// fp32 scale operand, so they run unscaled (exact E2M1 -> fp16 and E4M3 -> fp16) and the
+// E4M3 scale is one packed fp16 multiply, exact because E2M1 x E4M3 has at most 5
+// significant bits and |x| <= 6 * 448 (no fp16 rounding, overflow or subnormal).  Code
+// bytes 0-7 take the low scale byte, 8-15 the high one.  Dword u of the codes becomes
+// x[u] (byte b -> elements 2b, 2b+1), the K-slice of the u-th 16x16x32 MFMA; A and B lanes
+// use the same mapping, so every step multiplies matching channels.
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void nv_dequant(const uint4& c, uint32_t sc, v8h (&x)[4]) {
+  const v2h s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+  const v2h s0 = {s[0], s[0]}, s1 = {s[1], s[1]};
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const v2h su = u < 2 ? s0 : s1;
+    const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[u], 1.0f, 0) * su;
+    const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[u], 1.0f, 1) * su;
+    const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[u], 1.0f, 2) * su;
+    const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[u], 1.0f, 3) * su;
+    x[u] = v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
+}
+
+// as score_tiles, for NVFP4 operands: A = the row's dequantised indexer Q, bs[t] = the two
+// E4M3 scale bytes of this lane's 32 channels of tile t's entry
+__device__ __forceinline__ float score_tiles_nv(const v8h (&a)[4], const float (&wv)[4], int kb,
+                                                const uint4 (&bc)[4], const int (&bs)[4]) {
+  float part[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v8h b[4];
+    nv_dequant(bc[t], (uint32_t)bs[t], b);
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u], b[u], acc, 0, 0, 0);
+    float p = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p += wv[r] * fmaxf(acc[r], 0.0f);
+    part[t] = p;
+  }
+  return scatter_tiles(part, kb);
+}
+
+// One query's view of the cache: MFMA operands, slot -> row mapping, one scoring step.
+// Slots and rows are 32-bit (seq_cap <= 2^26, so byte offsets within a sequence fit in 32
+// bits) and the sequence's base pointers are workgroup-uniform, so each load is a scalar
+// base plus one 32-bit vector offset.
+template <bool kPool, bool kNv>
 struct QueryScorer {
-  v8i a;             // A operand: indexer Q rows (heads), 32 FP4 values per lane
+  // scale bytes per entry (and per query head row): one per 32 channels (MXFP4) or per 16
+  static constexpr uint32_t kScalesPerRow = kNv ? 8u : 4u;
+  v8i a;             // A operand (MXFP4): indexer Q rows (heads), 32 FP4 values per lane
   int a_scale;
+  v8h an[4];         // A operand (NVFP4): the same 32 channels dequantised to fp16
   float wv[4];       // weights of the 4 output rows (heads 4*kb .. 4*kb+3) of this lane
   int nv;            // visible entries, clamped to the cache
   int n_valid;       // slots that may hold a real candidate
@@ -136,17 +191,24 @@ struct QueryScorer {
       cb = nullptr;
     }
     kc = s.k_codes + (int64_t)seq * s.seq_cap * 64;
-    ks = s.k_scales + (int64_t)seq * s.seq_cap * 4;
+    ks = s.k_scales + (int64_t)seq * s.seq_cap * kScalesPerRow;
     a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     a_scale = 127;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) an[u] = v8h{};
     if (row < s.n_heads) {
       const int64_t r = (int64_t)q * s.n_heads + row;
       const uint4 qa = *reinterpret_cast<const uint4*>(s.q_codes + r * 64 + kb * 16);
-      a[0] = (int)qa.x;
-      a[1] = (int)qa.y;
-      a[2] = (int)qa.z;
-      a[3] = (int)qa.w;
-      a_scale = s.q_scales[r * 4 + kb];
+      if (kNv) {
+        const uint32_t qs = *reinterpret_cast<const uint16_t*>(s.q_scales + r * 8 + kb * 2);
+        nv_dequant(qa, qs, an);
+      } else {
+        a[0] = (int)qa.x;
+        a[1] = (int)qa.y;
+        a[2] = (int)qa.z;
+        a[3] = (int)qa.w;
+        a_scale = s.q_scales[r * 4 + kb];
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -178,12 +240,14 @@ struct QueryScorer {
       slot_pos(s, base + 16 * t + row, pos);
       const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(kc + (pos * 64u + kb * 16u)));
       bc[t] = make_uint4(v.x, v.y, v.z, v.w);
-      bs[t] = ks[pos * 4u + kb];
+      // NVFP4: the two scale bytes of this lane's 32 channels, one 16-bit load
+      bs[t] = kNv ? (int)*reinterpret_cast<const uint16_t*>(ks + (pos * 8u + kb * 2u)) : (int)ks[pos * 4u + kb];
     }
   }
 
   // scores of the 64 entries of one step; lane l returns the score of entry l
   __device__ __forceinline__ float score_step(const uint4 (&bc)[4], const int (&bs)[4]) const {
+    if (kNv) return score_tiles_nv(an, wv, kb, bc, bs);
     return score_tiles(a, a_scale, wv, kb, bc, bs);
   }
 };
@@ -277,13 +341,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_grouped(ScoreArgs s, in
   }
 }
 
-template <bool kPool>
+template <bool kPool, bool kNv>
 __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
   const int q = blockIdx.x / s.chunks;
   const int chunk = blockIdx.x % s.chunks;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  QueryScorer<kPool> sc;
+  QueryScorer<kPool, kNv> sc;
   if (!sc.init(s, q)) return;
   const int chunk_lo = chunk * s.chunk_len;
   const int write_hi = kPool ? (int)s.n_slots : sc.n_valid;  // pool mode also writes -inf pads
@@ -333,7 +397,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
 // kBlockMax: the segment also writes the maximum visible score of each of its blocks of
 // s.block positions (the pool's block scores), read from the parked scores before the
 // selection reuses that LDS.
-template <bool kPool, bool kFinal, bool kBlockMax>
+template <bool kPool, bool kFinal, bool kBlockMax, bool kNv>
 __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
   static_assert(kTkSeg >= kTkHistWords, "the score array doubles as the selection histograms");
   __shared__ __attribute__((aligned(16))) float park[kTkSeg];
@@ -343,7 +407,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   uint64_t key[kTkEpt];
-  QueryScorer<kPool> sc;
+  QueryScorer<kPool, kNv> sc;
   const int c0 = seg * kTkSeg;
   const bool seq_ok = sc.init(s, q);
   // workgroup-uniform condition: every thread reaches select_segment's barriers
@@ -446,7 +510,7 @@ static ScoreArgs make_args(const uint8_t* q_codes, const uint8_t* q_scales, cons
 // Writes scores[q, slot].  Inside a pool each slot's row comes from a block-id load, so a
 // wave's step is two dependent memory round trips and a workgroup is latency-bound:
 // pool chunks are small (2 steps per wave) to spread the pool over many workgroups.
-static int launch_score(ScoreArgs a, int n_q, float* scores, int64_t scores_stride, hipStream_t st) {
+static int launch_score(ScoreArgs a, int n_q, float* scores, int64_t scores_stride, bool nv, hipStream_t st) {
   a.chunk_len = a.cand_blocks ? kPoolChunk : kScoreChunk;
   const int64_t chunks = (a.n_slots + a.chunk_len - 1) / a.chunk_len;
   if (chunks * (int64_t)n_q > 0x7fffffffLL) return CSA2_ERR_SHAPE;
@@ -454,8 +518,13 @@ static int launch_score(ScoreArgs a, int n_q, float* scores, int64_t scores_stri
   a.scores_stride = scores_stride;
   a.chunks = (int)chunks;
   dim3 grid((unsigned)(chunks * n_q)), blk(kScoreThreads);
-  if (a.cand_blocks) hipLaunchKernelGGL(k_score_decode<true>, grid, blk, 0, st, a);
-  else hipLaunchKernelGGL(k_score_decode<false>, grid, blk, 0, st, a);
+  if (nv) {
+    if (a.cand_blocks) hipLaunchKernelGGL((k_score_decode<true, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_score_decode<false, true>), grid, blk, 0, st, a);
+  } else {
+    if (a.cand_blocks) hipLaunchKernelGGL((k_score_decode<true, false>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_score_decode<false, false>), grid, blk, 0, st, a);
+  }
   return csa2_check_launch();
 }
 
@@ -472,21 +541,45 @@ static size_t index_topk_ws(int n_q, int64_t n_slots, int k, bool pool) {
 
 using namespace csa2;
 
-extern "C" int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                                int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                                int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                                const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
-                                int max_cand_blocks, float* scores, int64_t scores_stride, void* stream) {
+// the NVFP4 scale arrays are read two bytes at a time
+static int check_nv_scales(const uint8_t* q_scales, const uint8_t* k_scales) {
+  return (((uintptr_t)q_scales | (uintptr_t)k_scales) & 1u) ? CSA2_ERR_SHAPE : CSA2_OK;
+}
+
+static int index_score(bool nv, const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q, int n_heads,
+                       int dim, const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
+                       const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
+                       const int32_t* n_cand_blocks, int block, int max_cand_blocks, float* scores,
+                       int64_t scores_stride, void* stream) {
   int64_t n_slots = 0;
   int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
                             cand_blocks, n_cand_blocks, block, max_cand_blocks, &n_slots);
+  if (rc == CSA2_OK && nv) rc = check_nv_scales(q_scales, k_scales);
   if (rc != CSA2_OK) return rc;
   if (!scores) return CSA2_ERR_NULL;
   if (scores_stride < n_slots) return CSA2_ERR_SHAPE;
   if (n_q == 0 || n_slots == 0) return CSA2_OK;
   ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
                           n_cand_blocks, block, max_cand_blocks, n_slots);
-  return launch_score(a, n_q, scores, scores_stride, (hipStream_t)stream);
+  return launch_score(a, n_q, scores, scores_stride, nv, (hipStream_t)stream);
+}
+
+extern "C" int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                                int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                                int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                                const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                                int max_cand_blocks, float* scores, int64_t scores_stride, void* stream) {
+  return index_score(false, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                     cand_blocks, n_cand_blocks, block, max_cand_blocks, scores, scores_stride, stream);
+}
+
+extern "C" int csa2_index_score_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                                      int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                                      int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                                      const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                                      int max_cand_blocks, float* scores, int64_t scores_stride, void* stream) {
+  return index_score(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                     cand_blocks, n_cand_blocks, block, max_cand_blocks, scores, scores_stride, stream);
 }
 
 extern "C" int csa2_index_score_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
@@ -523,15 +616,15 @@ extern "C" size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int 
   return index_topk_ws(n_q, n_slots, k, in_pool != 0);
 }
 
-extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                               int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                               int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                               const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
-                               int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+static int index_topk(bool nv, const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q, int n_heads,
+                      int dim, const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
+                      const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
+                      const int32_t* n_cand_blocks, int block, int max_cand_blocks, int k, int32_t* idx_out,
+                      int32_t* count_out, void* workspace, size_t workspace_bytes, void* stream) {
   int64_t n_slots = 0;
   int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
                             cand_blocks, n_cand_blocks, block, max_cand_blocks, &n_slots);
+  if (rc == CSA2_OK && nv) rc = check_nv_scales(q_scales, k_scales);
   if (rc != CSA2_OK) return rc;
   if (!idx_out || !count_out) return CSA2_ERR_NULL;
   if (n_q > 65535 || k < 1 || k > CSA2_MAX_TOPK || n_slots > 0x7fffffffLL) return CSA2_ERR_SHAPE;
@@ -548,7 +641,7 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
     const size_t sc_bytes = ((size_t)n_q * n0 * sizeof(float) + 255) & ~(size_t)255;
     ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
                             cand_blocks, n_cand_blocks, block, max_cand_blocks, n_slots);
-    rc = launch_score(a, n_q, sc, n0, st);
+    rc = launch_score(a, n_q, sc, n0, nv, st);
     if (rc != CSA2_OK) return rc;
     TkArgs t = {};
     t.scores = sc;
@@ -574,8 +667,13 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
   a.idx_out = idx_out;
   a.count_out = count_out;
   dim3 grid((unsigned)segs[0], (unsigned)n_q), blk(kScoreThreads);
-  if (L == 1) hipLaunchKernelGGL((k_score_select<false, true, false>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((k_score_select<false, false, false>), grid, blk, 0, st, a);
+  if (nv) {
+    if (L == 1) hipLaunchKernelGGL((k_score_select<false, true, false, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_score_select<false, false, false, true>), grid, blk, 0, st, a);
+  } else {
+    if (L == 1) hipLaunchKernelGGL((k_score_select<false, true, false, false>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_score_select<false, false, false, false>), grid, blk, 0, st, a);
+  }
   rc = csa2_check_launch();
   if (rc != CSA2_OK) return rc;
   TkArgs t = {};
@@ -585,6 +683,28 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
   t.idx_out = idx_out;
   t.count_out = count_out;
   return select_levels_after0(segs, L, t, n_q, bufA, bufB, st);
+}
+
+extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                               int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                               int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                               const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                               int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return index_topk(false, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                    cand_blocks, n_cand_blocks, block, max_cand_blocks, k, idx_out, count_out, workspace,
+                    workspace_bytes, stream);
+}
+
+extern "C" int csa2_index_topk_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                                     int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                                     int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                                     const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                                     int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return index_topk(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                    cand_blocks, n_cand_blocks, block, max_cand_blocks, k, idx_out, count_out, workspace,
+                    workspace_bytes, stream);
 }
 
 static size_t index_topk_pool_ws(int n_q, int64_t n_slots, int k, int block, int max_blocks, size_t* bmax_bytes,
@@ -643,8 +763,8 @@ extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_sca
   a.bmax_stride = nblk;
   hipStream_t st = (hipStream_t)stream;
   dim3 grid((unsigned)segs[0], (unsigned)n_q), blk(kScoreThreads);
-  if (L == 1) hipLaunchKernelGGL((k_score_select<false, true, true>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((k_score_select<false, false, true>), grid, blk, 0, st, a);
+  if (L == 1) hipLaunchKernelGGL((k_score_select<false, true, true, false>), grid, blk, 0, st, a);
+  else hipLaunchKernelGGL((k_score_select<false, false, true, false>), grid, blk, 0, st, a);
   rc = csa2_check_launch();
   if (rc != CSA2_OK) return rc;
   TkArgs t = {};

@@ -25,9 +25,12 @@ from . import csa2 as C
 
 
 MODES = ("full", "full_pool", "reuse", "reindex", "reindex_pool")
+# indexer Q/K formats: MXFP4 (E8M0 per 32 channels, the scaled FP4 matrix-core path) or the
+# main KV's NVFP4-style format (E4M3 per 16 channels, dequantised to fp16 MFMAs)
+INDEX_FORMATS = {"mxfp4": (C.FMT_MXFP4, 32), "nvfp4": (C.FMT_NVFP4, 16)}
 
 
-def plan_group(modes, fused: bool = True, group: int = 1) -> list:
+def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp4") -> list:
     """Checks a layer group's mode sequence and returns the calls each layer makes.
 
     [W] "CSA2：跨层复用，能借就不自己算" and Figure 4: a Reindex layer re-scores the KV of the
@@ -36,7 +39,13 @@ def plan_group(modes, fused: bool = True, group: int = 1) -> list:
     layer builds the pool, and Reindex-in-pool layers need it.  Raises ValueError for a
     sequence that breaks these rules.  group > 1: the query rows come in groups of `group`
     rows of one sequence, and the layers that score all visible entries read each group's
-    indexer K once (csa2_index_score_grouped, then csa2_topk)."""
+    indexer K once (csa2_index_score_grouped, then csa2_topk).  index_fmt "nvfp4": the
+    fused pool build and grouped scoring exist for MXFP4 only, so the pool-building layer
+    scores, selects and builds the pool in separate calls, and group must be 1."""
+    if index_fmt not in INDEX_FORMATS:
+        raise ValueError(f"unknown indexer format {index_fmt!r}")
+    if index_fmt != "mxfp4" and group > 1:
+        raise ValueError("grouped scoring reads an MXFP4 indexer only")
     plan, have_kv, have_pool = [], False, False
     for i, m in enumerate(modes):
         if m not in MODES:
@@ -50,7 +59,7 @@ def plan_group(modes, fused: bool = True, group: int = 1) -> list:
         if m == "reuse":
             calls = ["attend"]
         elif m == "full_pool":
-            calls = (["quantize_index_q", "index_topk_pool", "attend"] if fused else
+            calls = (["quantize_index_q", "index_topk_pool", "attend"] if fused and index_fmt == "mxfp4" else
                      ["quantize_index_q", "score", "select", "build_pool", "attend"])
         elif group > 1 and m in ("full", "reindex"):
             calls = ["quantize_index_q", "score_grouped", "select", "attend"]
@@ -65,8 +74,8 @@ def plan_group(modes, fused: bool = True, group: int = 1) -> list:
 
 
 class Caches:
-    """Device caches of a layer group: main KV (NVFP4), indexer K (MXFP4), and the
-    per-layer FP8 window caches with their ring bases."""
+    """Device caches of a layer group: main KV (NVFP4), indexer K (MXFP4, or NVFP4 with
+    index_fmt "nvfp4"), and the per-layer FP8 window caches with their ring bases."""
 
     def __init__(self, kv_codes, kv_scales, ik_codes, ik_scales, swa: dict, swa_base):
         self.kv_codes, self.kv_scales = kv_codes, kv_scales
@@ -80,10 +89,11 @@ class Caches:
 
     @staticmethod
     def empty(n_seq: int, seq_cap: int, swa_layers, swa_cap: int, dim: int = 512, idx_dim: int = 128,
-              device="cuda"):
+              device="cuda", index_fmt: str = "mxfp4"):
         u8 = dict(dtype=torch.uint8, device=device)
+        per = INDEX_FORMATS[index_fmt][1]
         return Caches(torch.zeros(n_seq, seq_cap, dim // 2, **u8), torch.zeros(n_seq, seq_cap, dim // 16, **u8),
-                      torch.zeros(n_seq, seq_cap, idx_dim // 2, **u8), torch.zeros(n_seq, seq_cap, idx_dim // 32, **u8),
+                      torch.zeros(n_seq, seq_cap, idx_dim // 2, **u8), torch.zeros(n_seq, seq_cap, idx_dim // per, **u8),
                       {L: torch.zeros(n_seq, swa_cap, dim, **u8) for L in swa_layers},
                       torch.zeros(n_seq, dtype=torch.int64, device=device))
 
@@ -93,19 +103,23 @@ class Csa2Step:
 
     def __init__(self, n_q: int, n_heads: int, idx_heads: int, seq_cap: int, k: int = 512, window: int = 128,
                  block: int = 8, max_blocks: int = 2048, idx_dim: int = 128, dim: int = 512,
-                 out_dtype=torch.float32, fused: bool = True, group: int = 1, device="cuda"):
+                 out_dtype=torch.float32, fused: bool = True, group: int = 1, index_fmt: str = "mxfp4",
+                 device="cuda"):
         """fused: score and select in one call (csa2_index_topk) wherever the layer does not
         need the score array itself (it does only when it builds the pool).  group: query
         rows come in groups of `group` consecutive rows of one sequence (several tokens of a
         sequence at once); layers scoring all visible entries then read each group's indexer
-        K once."""
+        K once.  index_fmt: the indexer Q/K format ("mxfp4" or "nvfp4", see INDEX_FORMATS)."""
+        plan_group(["full"], fused, group, index_fmt)   # validates the combination
+        self.index_fmt = index_fmt
+        self.idx_qfmt, self.idx_group = INDEX_FORMATS[index_fmt]
         self.n_q, self.n_heads, self.idx_heads = n_q, n_heads, idx_heads
         self.fused, self.group = fused, group
         self.seq_cap, self.k, self.window = seq_cap, k, window
         self.block, self.max_blocks, self.dim = block, max_blocks, dim
         dev = dict(device=device)
         self.qi_codes = torch.empty(n_q, idx_heads, idx_dim // 2, dtype=torch.uint8, **dev)
-        self.qi_scales = torch.empty(n_q, idx_heads, idx_dim // 32, dtype=torch.uint8, **dev)
+        self.qi_scales = torch.empty(n_q, idx_heads, idx_dim // self.idx_group, dtype=torch.uint8, **dev)
         self.scores = torch.empty(n_q, max(seq_cap, max_blocks * block), dtype=torch.float32, **dev)
         self.idx = torch.empty(n_q, k, dtype=torch.int32, **dev)
         self.count = torch.empty(n_q, dtype=torch.int32, **dev)
@@ -129,19 +143,26 @@ class Csa2Step:
 
     # ---- steps ----
     def quantize_index_q(self, q_f32, bind=False):
-        """indexer Q [n_q, H_I, d] f32 -> MXFP4 (per query, per head, per 32 channels)."""
+        """indexer Q [n_q, H_I, d] f32 -> the indexer format (per query, per head, per 32
+        channels for MXFP4, per 16 for NVFP4)."""
         n_q, h, d = q_f32.shape
-        return C.csa2_quantize_kv(q_f32.view(n_q * h, d), C.FMT_MXFP4, self.qi_codes.view(n_q * h, d // 2),
-                                  self.qi_scales.view(n_q * h, d // 32), _bind=bind)
+        return C.csa2_quantize_kv(q_f32.view(n_q * h, d), self.idx_qfmt, self.qi_codes.view(n_q * h, d // 2),
+                                  self.qi_scales.view(n_q * h, d // self.idx_group), _bind=bind)
 
     def score(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False):
+        fn = C.csa2_index_score_nvfp4 if self.index_fmt == "nvfp4" else C.csa2_index_score
         if in_pool:
-            return C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq,
-                                      n_vis, self.scores, self.pool, self.pool_count, self.block, _bind=bind)
-        return C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
-                                  self.scores, _bind=bind)
+            return fn(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.scores,
+                      self.pool, self.pool_count, self.block, _bind=bind)
+        return fn(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.scores,
+                  _bind=bind)
+
+    def _mx_only(self, what):
+        if self.index_fmt != "mxfp4":
+            raise ValueError(f"{what} reads an MXFP4 indexer only")
 
     def score_grouped(self, caches: Caches, w, q_seq, n_vis, bind=False):
+        self._mx_only("grouped scoring")
         return C.csa2_index_score_grouped(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq,
                                           n_vis, self.group, self.scores, _bind=bind)
 
@@ -154,12 +175,13 @@ class Csa2Step:
     def index_topk(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False):
         """score + select in one pass, without the score array."""
         pool = (self.pool, self.pool_count) if in_pool else (None, None)
-        return C.csa2_index_topk(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
-                                 self.k, self.idx, self.count, self.ws_index_topk, pool[0], pool[1], self.block,
-                                 _bind=bind)
+        fn = C.csa2_index_topk_nvfp4 if self.index_fmt == "nvfp4" else C.csa2_index_topk
+        return fn(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.k, self.idx,
+                  self.count, self.ws_index_topk, pool[0], pool[1], self.block, _bind=bind)
 
     def index_topk_build_pool(self, caches: Caches, w, q_seq, n_vis, bind=False):
         """score + select + pool in one pass (the decoder's first Full layer)."""
+        self._mx_only("the fused pool build")
         return C.csa2_index_topk_pool(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq,
                                       n_vis, self.k, self.idx, self.count, self.pool, self.pool_count, self.block,
                                       self.ws_index_topk_pool, _bind=bind)
@@ -187,7 +209,7 @@ class Csa2Step:
         with its own window cache caches.swa[i].  outs/lses: optional per-layer outputs
         (default: the step's own buffers, overwritten by each layer).  With bind=True returns
         the group's calls as one flat list of callables."""
-        plan = plan_group(modes, self.fused, self.group)
+        plan = plan_group(modes, self.fused, self.group, self.index_fmt)
         calls = []
         for i, (m, names) in enumerate(zip(modes, plan)):
             q_index, w, q_attn = inputs[i]
@@ -221,7 +243,7 @@ class Csa2Step:
     def full(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, make_pool=False,
              out=None, lse=None, bind=False):
         calls = [self.quantize_index_q(q_index_f32, bind)]
-        if make_pool and self.fused:
+        if make_pool and self.fused and self.index_fmt == "mxfp4":
             calls.append(self.index_topk_build_pool(caches, w, q_seq, n_vis, bind))
         elif make_pool:
             calls += [self.score(caches, w, q_seq, n_vis, bind=bind), self.select(n_vis, bind=bind),

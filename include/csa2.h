@@ -233,6 +233,35 @@ int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float
 size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_pool);
 
 /*
+ * csa2_index_score_nvfp4 / csa2_index_topk_nvfp4 -- csa2_index_score / csa2_index_topk for
+ * an indexer kept in the main KV's NVFP4-style format instead of MXFP4: E2M1 codes with one
+ * E4M3 scale per 16 channels, as CSA2_FMT_NVFP4 of csa2_quantize_kv writes them.
+ * [W] "FP4 与 SWA Bounded Replay" (indexer Q/K in FP4, main KV in E2M1 + E4M3 per 16; the
+ * page does not fix the indexer's scale format, so both readings are served).
+ *
+ *   score(q, j) = sum_h w[q,h] * max(0, sum_c Q[q,h,c] K[seq(q), j, c])
+ * with Q and K the exact NVFP4 values; products are exact, sums are fp32.
+ *
+ * Arguments, layouts, outputs, workspace and errors are those of csa2_index_score and
+ * csa2_index_topk, except:
+ *   q_scales   [n_q, n_heads, dim/16] E4M3 (8 per head row)
+ *   k_scales   [n_seq, seq_cap, dim/16] E4M3 (8 per entry); both scale arrays 2-byte
+ *              aligned (CSA2_ERR_SHAPE otherwise)
+ * A cache entry is 72 bytes (64 code + 8 scale bytes) against MXFP4's 68.
+ */
+int csa2_index_score_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                           int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                           int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                           const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                           int max_cand_blocks, float* scores, int64_t scores_stride, void* stream);
+int csa2_index_topk_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                          int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                          int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                          const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                          int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * csa2_index_topk_pool -- the decoder's first Full layer in one pass over the indexer-K
  * cache: the Top-K of csa2_index_topk (no pool) and the candidate pool of
  * csa2_build_pool over the same scores.  [W] "CSA2：跨层复用，能借就不自己算" (Top-K),

@@ -25,6 +25,8 @@ Readings where the pages are silent (each also listed in the design notes):
     lightning-indexer form; the pages only say a lightweight indexer scores the
     main KV with indexer Q/K).            -- parity unpinned for the formula choice
   * indexer Q/K are MXFP4 (E2M1 + E8M0 per 32); the main KV is E2M1 + E4M3 per 16.
+    The page leaves the indexer's scale format open, so the NVFP4-style alternative (the
+    main KV's format, E4M3 per 16) is served too: `index_fmt="nvfp4"`.
   * rounding is to nearest with ties to the even code; scales saturate.
   * a compressed entry j is visible to token t iff (j+1)*m <= t+1.
   * ties in Top-K / pool ranking go to the lower position; outputs are ascending.
@@ -188,6 +190,28 @@ def dequant_fp8(codes: np.ndarray) -> np.ndarray:
     return E4M3[np.asarray(codes, dtype=np.int64)]
 
 
+INDEX_FORMATS = ("mxfp4", "nvfp4")
+
+
+def quantize_indexer(x: np.ndarray, index_fmt: str = "mxfp4"):
+    """Indexer Q / K rows in the chosen format: MXFP4 (the reading above) or the NVFP4-style
+    alternative, E2M1 with one E4M3 scale per 16 channels as for the main KV.
+    [W] "FP4 与 SWA Bounded Replay" (indexer Q/K in FP4; the scale format is not given)."""
+    if index_fmt == "mxfp4":
+        return quantize_mxfp4(x)
+    if index_fmt == "nvfp4":
+        return quantize_nvfp4(x)
+    raise ValueError(index_fmt)
+
+
+def dequant_indexer(codes: np.ndarray, scales: np.ndarray, index_fmt: str = "mxfp4") -> np.ndarray:
+    if index_fmt == "mxfp4":
+        return dequant_mxfp4(codes, scales)
+    if index_fmt == "nvfp4":
+        return dequant_nvfp4(codes, scales)
+    raise ValueError(index_fmt)
+
+
 # --------------------------------------------------------------------------------------
 # Indexer scoring, Top-K, candidate pool
 # --------------------------------------------------------------------------------------
@@ -287,18 +311,20 @@ def sparse_attention(q: np.ndarray, main_rows: np.ndarray, swa_rows: np.ndarray,
 class PackedCaches:
     """Packed caches of one sequence, exactly as stored in HBM:
     kv_codes [N, D/2] u8, kv_scales [N, D/16] u8 (main KV, NVFP4);
-    ik_codes [N, d/2] u8, ik_scales [N, d/32] u8 (indexer K, MXFP4);
+    ik_codes [N, d/2] u8, ik_scales [N, d/32] u8 (indexer K, MXFP4; [N, d/16] with
+    index_fmt "nvfp4");
     swa: dict layer -> (codes [cap, D] u8 E4M3, base, cap) with row(p) = (p - base) mod cap."""
 
-    def __init__(self, kv_codes, kv_scales, ik_codes, ik_scales, swa=None):
+    def __init__(self, kv_codes, kv_scales, ik_codes, ik_scales, swa=None, index_fmt: str = "mxfp4"):
         self.kv_codes, self.kv_scales = kv_codes, kv_scales
         self.ik_codes, self.ik_scales = ik_codes, ik_scales
         self.swa = swa or {}
+        self.index_fmt = index_fmt
         self._ik_deq = None
 
     def ik_deq(self, n: int) -> np.ndarray:
         if self._ik_deq is None or self._ik_deq.shape[0] < n:
-            self._ik_deq = dequant_mxfp4(self.ik_codes[:n], self.ik_scales[:n])
+            self._ik_deq = dequant_indexer(self.ik_codes[:n], self.ik_scales[:n], self.index_fmt)
         return self._ik_deq[:n]
 
     def main_rows(self, positions: np.ndarray) -> np.ndarray:
@@ -314,8 +340,8 @@ class PackedCaches:
 
 def full_scores(q_codes, q_scales, w, caches: PackedCaches, n_vis: int, cand=None) -> tuple:
     """Scores of one query over all visible entries (cand None) or over given candidate
-    positions.  Returns (positions, scores)."""
-    qd = dequant_mxfp4(q_codes, q_scales)
+    positions.  Returns (positions, scores).  The indexer Q is in the caches' indexer format."""
+    qd = dequant_indexer(q_codes, q_scales, caches.index_fmt)
     kd = caches.ik_deq(n_vis)
     pos = np.arange(n_vis, dtype=np.int64) if cand is None else np.asarray(cand, np.int64)
     return pos, index_scores(qd, w, kd[pos])

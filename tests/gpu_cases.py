@@ -42,9 +42,10 @@ def swa_ring_latents(wl: Workload, layer: int, seq: int) -> np.ndarray:
 class Case:
     """A workload's inputs on both sides."""
 
-    def __init__(self, wl: Workload, swa_layers=(0,)):
+    def __init__(self, wl: Workload, swa_layers=(0,), index_fmt: str = "mxfp4"):
         self.wl = wl
         self.swa_layers = tuple(swa_layers)
+        self.index_fmt = index_fmt
 
     # ---------- HIP side ----------
     def gpu_caches(self, window_empty: bool = False):
@@ -53,7 +54,8 @@ class Case:
         write them)."""
         from fp4_kv_cache_layer_amd.layer import Caches
         wl, C_ = self.wl, C()
-        caches = Caches.empty(wl.n_seq, wl.seq_cap, self.swa_layers, wl.swa_cap)
+        caches = Caches.empty(wl.n_seq, wl.seq_cap, self.swa_layers, wl.swa_cap, index_fmt=self.index_fmt)
+        ik_fmt = C_.FMT_NVFP4 if self.index_fmt == "nvfp4" else C_.FMT_MXFP4
         caches.swa_base.fill_(wl.swa_base)
         for b in range(wl.n_seq):
             for r0 in range(0, wl.seq_cap, ROWS_PER_UPLOAD):
@@ -61,7 +63,7 @@ class Case:
                 lat = torch.from_numpy(wl.main_latents(b, r0, n)).cuda()
                 C_.csa2_quantize_kv(lat, C_.FMT_NVFP4, caches.kv_codes[b, r0:r0 + n], caches.kv_scales[b, r0:r0 + n])
                 ik = torch.from_numpy(wl.index_k_latents(b, r0, n)).cuda()
-                C_.csa2_quantize_kv(ik, C_.FMT_MXFP4, caches.ik_codes[b, r0:r0 + n], caches.ik_scales[b, r0:r0 + n])
+                C_.csa2_quantize_kv(ik, ik_fmt, caches.ik_codes[b, r0:r0 + n], caches.ik_scales[b, r0:r0 + n])
             for L in self.swa_layers if not window_empty else ():
                 ring = torch.from_numpy(swa_ring_latents(wl, L, b)).cuda()
                 C_.csa2_quantize_kv(ring, C_.FMT_FP8, caches.swa[L][b])
@@ -87,13 +89,13 @@ class Case:
         wl = self.wl
         n = wl.seq_cap if n_rows is None else n_rows
         kv_c, kv_s = O.quantize_nvfp4(wl.main_latents(seq, 0, n))
-        ik_c, ik_s = O.quantize_mxfp4(wl.index_k_latents(seq, 0, n))
+        ik_c, ik_s = O.quantize_indexer(wl.index_k_latents(seq, 0, n), self.index_fmt)
         swa = {L: (O.quantize_fp8(swa_ring_latents(wl, L, seq)), wl.swa_base, wl.swa_cap) for L in self.swa_layers}
-        return O.PackedCaches(kv_c, kv_s, ik_c, ik_s, swa)
+        return O.PackedCaches(kv_c, kv_s, ik_c, ik_s, swa, self.index_fmt)
 
     def oracle_query(self, layer: int, qi: int):
         wl = self.wl
-        qc, qs = O.quantize_mxfp4(wl.index_q(layer, qi, 1)[0])
+        qc, qs = O.quantize_indexer(wl.index_q(layer, qi, 1)[0], self.index_fmt)
         w = wl.index_w(layer, qi, 1)[0]
         qa = bf16_bits_to_f32(wl.attn_q_bits(layer, qi, 1)[0]).astype(np.float64)
         return qc, qs, w, qa
@@ -169,19 +171,19 @@ def oracle_main_rows(wl: Workload, seq: int, positions: np.ndarray):
 
 
 @functools.lru_cache(maxsize=4)
-def _oracle_index_cache(name: str, seq: int) -> O.PackedCaches:
+def _oracle_index_cache(name: str, seq: int, index_fmt: str) -> O.PackedCaches:
     wl = workloads.config(name)
-    ik_c, ik_s = O.quantize_mxfp4(wl.index_k_latents(seq, 0, wl.seq_cap))
-    return O.PackedCaches(None, None, ik_c, ik_s)
+    ik_c, ik_s = O.quantize_indexer(wl.index_k_latents(seq, 0, wl.seq_cap), index_fmt)
+    return O.PackedCaches(None, None, ik_c, ik_s, index_fmt=index_fmt)
 
 
-def oracle_index_cache(wl: Workload, seq: int) -> O.PackedCaches:
+def oracle_index_cache(wl: Workload, seq: int, index_fmt: str = "mxfp4") -> O.PackedCaches:
     """Oracle caches of one sequence holding the indexer K only (the part scoring reads);
     kept for reuse across tests of the same named workload."""
     if wl.name in workloads.CONFIG_NAMES + workloads.GROUP_NAMES:
-        return _oracle_index_cache(wl.name, seq)
-    ik_c, ik_s = O.quantize_mxfp4(wl.index_k_latents(seq, 0, wl.seq_cap))
-    return O.PackedCaches(None, None, ik_c, ik_s)
+        return _oracle_index_cache(wl.name, seq, index_fmt)
+    ik_c, ik_s = O.quantize_indexer(wl.index_k_latents(seq, 0, wl.seq_cap), index_fmt)
+    return O.PackedCaches(None, None, ik_c, ik_s, index_fmt=index_fmt)
 
 
 def run_group_snapshots(case: Case, step, caches, window_appends: bool = False):
@@ -196,7 +198,7 @@ def run_group_snapshots(case: Case, step, caches, window_appends: bool = False):
     inputs = [case.gpu_query_inputs(L) for L in range(len(modes))]
     calls = step.run_group(caches, modes, inputs, q_seq, n_vis, q_pos, rs, bind=True)
     snaps, at = [], 0
-    for L, names in enumerate(plan_group(modes, step.fused, step.group)):
+    for L, names in enumerate(plan_group(modes, step.fused, step.group, step.index_fmt)):
         if window_appends:
             C_ = C()
             lat = np.stack([wl.swa_latents(L, int(b), int(t), 1)[0] for b, t in zip(wl.q_seq, wl.q_pos)])
@@ -222,7 +224,7 @@ def check_group_query(case: Case, caches, snaps, qi: int, k: int = 512, window: 
     wl = case.wl
     seq, nv = int(wl.q_seq[qi]), int(wl.n_vis[qi])
     t, s = int(wl.q_pos[qi]), int(wl.replay_start[qi])
-    oc = oracle_index_cache(wl, seq)
+    oc = oracle_index_cache(wl, seq, case.index_fmt)
     assert np.array_equal(caches.ik_codes[seq].cpu().numpy(), oc.ik_codes)
     assert np.array_equal(caches.ik_scales[seq].cpu().numpy(), oc.ik_scales)
     stats = {"set_diff": []}

@@ -127,25 +127,28 @@ def test_quantize_multi_matches_single_calls(C):
         assert (sa is None) == (sb is None) and (sa is None or torch.equal(sa, sb))
 
 
-def _score_case(seed, n_seq, seq_cap, n_vis, idx_heads):
+def _score_case(seed, n_seq, seq_cap, n_vis, idx_heads, index_fmt="mxfp4"):
     wl = G.workloads.Workload(
         name="small", seed=seed, n_seq=n_seq, seq_cap=seq_cap, m=1, heads=16, idx_heads=idx_heads,
         q_seq=np.array([i % n_seq for i in range(len(n_vis))], np.int32),
         q_pos=np.array(n_vis, np.int64) - 1, replay_start=np.zeros(len(n_vis), np.int64), layers=("full",),
         new_entries=(0, 0))
-    return G.Case(wl)
+    return G.Case(wl, index_fmt=index_fmt)
 
 
-@pytest.mark.parametrize("idx_heads", [16, 8, 5])
-def test_index_score_parity(C, idx_heads):
-    _say("index_score", idx_heads)
-    case = _score_case(10 + idx_heads, 3, 9000, [9000, 4097, 1, 8999, 64], idx_heads)
+@pytest.mark.parametrize("idx_heads,fmt", [(16, "mxfp4"), (8, "mxfp4"), (5, "mxfp4"), (16, "nvfp4"), (5, "nvfp4")])
+def test_index_score_parity(C, idx_heads, fmt):
+    """Scores of the MXFP4 indexer (scaled FP4 MFMA) and of the NVFP4-style one (dequantised
+    fp16 MFMA) against the oracle's fp64 scores; the caches and the quantised indexer Q
+    bit-exact against the oracle's quantiser."""
+    _say("index_score", idx_heads, fmt)
+    case = _score_case(10 + idx_heads, 3, 9000, [9000, 4097, 1, 8999, 64], idx_heads, fmt)
     wl = case.wl
     caches = case.gpu_caches()
     q_idx, w, _ = case.gpu_query_inputs(0)
     q_seq, n_vis, _, _ = case.gpu_meta()
     from fp4_kv_cache_layer_amd.layer import Csa2Step
-    st = Csa2Step(wl.n_q, 16, idx_heads, wl.seq_cap)
+    st = Csa2Step(wl.n_q, 16, idx_heads, wl.seq_cap, index_fmt=fmt)
     st.scores.fill_(12345.0)
     st.quantize_index_q(q_idx)
     st.score(caches, w, q_seq, n_vis)
@@ -158,6 +161,7 @@ def test_index_score_parity(C, idx_heads):
         assert np.array_equal(caches.ik_scales[seq].cpu().numpy(), oc.ik_scales)
         qc, qs, wq, _ = case.oracle_query(0, qi)
         assert np.array_equal(st.qi_codes[qi].cpu().numpy(), qc)
+        assert np.array_equal(st.qi_scales[qi].cpu().numpy(), qs)
         nv = int(wl.n_vis[qi])
         _, ref = O.full_scores(qc, qs, wq, oc, nv)
         got = gs[qi, :nv]
@@ -208,15 +212,16 @@ def test_index_score_grouped_matches_per_row(C, group):
         assert np.all(np.abs(got[qi, :nv] - r) <= 1e-5 * np.abs(r) + 1e-6 * np.abs(r).max())
 
 
-def test_index_score_pool_slots(C):
-    _say("index_score pool")
-    case = _score_case(21, 2, 6000, [6000, 5003, 333], 16)
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_index_score_pool_slots(C, fmt):
+    _say("index_score pool", fmt)
+    case = _score_case(21, 2, 6000, [6000, 5003, 333], 16, fmt)
     wl = case.wl
     caches = case.gpu_caches()
     q_idx, w, _ = case.gpu_query_inputs(0)
     q_seq, n_vis, _, _ = case.gpu_meta()
     from fp4_kv_cache_layer_amd.layer import Csa2Step
-    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, max_blocks=300)
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, max_blocks=300, index_fmt=fmt)
     rng = np.random.default_rng(3)
     blocks = np.full((wl.n_q, 300), -1, np.int32)
     ncb = np.array([300, 250, 60], np.int32)
@@ -255,8 +260,9 @@ def _run_index_topk(C, st, caches, w, q_seq, n_vis, k, in_pool=False):
     idx_f = torch.full((st.n_q, k), 77, dtype=torch.int32, device="cuda")
     cnt_f = torch.full((st.n_q,), 77, dtype=torch.int32, device="cuda")
     pool = (st.pool, st.pool_count) if in_pool else (None, None)
-    C.csa2_index_topk(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, k, idx_f, cnt_f,
-                      None, pool[0], pool[1], 8)
+    fn = C.csa2_index_topk_nvfp4 if st.index_fmt == "nvfp4" else C.csa2_index_topk
+    fn(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, k, idx_f, cnt_f, None, pool[0],
+       pool[1], 8)
     idx_u = torch.empty(st.n_q, k, dtype=torch.int32, device="cuda")
     cnt_u = torch.empty(st.n_q, dtype=torch.int32, device="cuda")
     st.score(caches, w, q_seq, n_vis, in_pool)
@@ -265,19 +271,19 @@ def _run_index_topk(C, st, caches, w, q_seq, n_vis, k, in_pool=False):
     return (idx_f.cpu().numpy(), cnt_f.cpu().numpy()), (idx_u.cpu().numpy(), cnt_u.cpu().numpy())
 
 
-@pytest.mark.parametrize("k", [512, 2048, 7])
-def test_index_topk_fused(C, k):
+@pytest.mark.parametrize("k,fmt", [(512, "mxfp4"), (2048, "mxfp4"), (7, "mxfp4"), (512, "nvfp4"), (7, "nvfp4")])
+def test_index_topk_fused(C, k, fmt):
     """Fused scoring + selection returns exactly what scoring then selecting returns (the same
     fp32 scores, the same exact ranking), and that set passes the oracle's Top-K rule."""
-    _say("index_topk", k)
+    _say("index_topk", k, fmt)
     n_vis = [40000, 8193, 1, 0, 511, 20001, 16384]
-    case = _score_case(30 + k, 3, 40000, n_vis, 16)
+    case = _score_case(30 + k, 3, 40000, n_vis, 16, fmt)
     wl = case.wl
     caches = case.gpu_caches()
     q_idx, w, _ = case.gpu_query_inputs(0)
     q_seq, n_vis_t, _, _ = case.gpu_meta()
     from fp4_kv_cache_layer_amd.layer import Csa2Step
-    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, k=k)
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, k=k, index_fmt=fmt)
     st.quantize_index_q(q_idx)
     (gi, gc), (ui, uc) = _run_index_topk(C, st, caches, w, q_seq, n_vis_t, k)
     assert np.array_equal(gc, uc) and np.array_equal(gi, ui)
@@ -357,16 +363,17 @@ def test_index_topk_with_pool_build(C, block, max_blocks, k):
         G.topk_accept(blk_f[qi].cpu().numpy(), int(bc_f[qi]), np.arange(bs.size), bs, max_blocks)
 
 
-def test_index_topk_fused_pool(C):
-    _say("index_topk pool")
-    case = _score_case(41, 2, 30000, [30000, 12000, 333], 16)
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_index_topk_fused_pool(C, fmt):
+    _say("index_topk pool", fmt)
+    case = _score_case(41, 2, 30000, [30000, 12000, 333], 16, fmt)
     wl = case.wl
     caches = case.gpu_caches()
     q_idx, w, _ = case.gpu_query_inputs(0)
     q_seq, n_vis_t, _, _ = case.gpu_meta()
     from fp4_kv_cache_layer_amd.layer import Csa2Step
     mb = 2048
-    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, max_blocks=mb)
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, max_blocks=mb, index_fmt=fmt)
     rng = np.random.default_rng(9)
     blocks = np.full((wl.n_q, mb), -1, np.int32)
     ncb = np.array([2048, 1500, 45], np.int32)

@@ -1,6 +1,7 @@
 """Full-size layer groups on the GPU: the 128K group (Full, 3 Reuse, Reindex; 32 queries),
-the 1M group (Full + pool, 4 Reindex inside the pool; 8 queries), the whole 20-layer decoder
-step at 128K and 1M, and the m = 2 prefill chunk, run through the layer driver exactly as
+the 1M group (Full + pool, 4 Reindex inside the pool; 8 queries), both also with the
+NVFP4-style indexer, the whole 20-layer decoder step at 128K and 1M, and the m = 2 prefill
+chunk, run through the layer driver exactly as
 the benchmark runs them, with oracle parity on sampled query rows."""
 import sys
 
@@ -35,6 +36,27 @@ def test_layer_group_full_size(C, name, samples, fused):
     case = G.Case(wl, swa_layers=range(len(wl.layers)))
     caches = case.gpu_caches()
     step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, fused=fused)
+    snaps = G.run_group_snapshots(case, step, caches)
+    for qi in samples:
+        _say("  oracle query", qi)
+        G.check_group_query(case, caches, snaps, qi)
+    del caches, step
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,samples", [("c2", (0, 63)), ("c4", (0, 5))])
+def test_nvfp4_indexer_full_size(C, name, samples):
+    """The NVFP4-style indexer variant (E4M3 per 16 channels, fp16 matrix-core scoring) at
+    full size: the 64 x 128K Full step and the 1M group (Full + pool through the unfused
+    score / select / pool calls, then Reindex inside the pool), with oracle parity of
+    every layer on sampled query rows."""
+    _say("nvfp4 indexer", name)
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    wl = workloads.config(name)
+    case = G.Case(wl, swa_layers=range(len(wl.layers)), index_fmt="nvfp4")
+    caches = case.gpu_caches()
+    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, index_fmt="nvfp4")
     snaps = G.run_group_snapshots(case, step, caches)
     for qi in samples:
         _say("  oracle query", qi)

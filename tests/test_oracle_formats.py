@@ -232,3 +232,68 @@ def test_fp8_roundtrip_all_codes():
     codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
     x = O.dequant_fp8(codes).astype(np.float32)
     assert np.array_equal(O.quantize_fp8(x), codes)
+
+
+def _rows_in_both_indexer_formats(rng, rows, d=128):
+    """Rows that MXFP4 and the NVFP4-style format both hold exactly, with the same values:
+    each 32-channel block is E2M1 grid values times one power of two 2^e (e within both
+    scale ranges), and each 16-channel half holds a +-6 * 2^e element, so the per-32 E8M0
+    rule and the per-16 amax/6 E4M3 rule both pick the scale 2^e."""
+    grid = np.array([O.e2m1_value(c) for c in range(16)])
+    x = rng.choice(grid, size=(rows, d))
+    x[:, ::16] = rng.choice([-6.0, 6.0], size=(rows, d // 16))
+    e = rng.integers(-6, 5, size=(rows, d // 32))
+    return x * np.ldexp(1.0, np.repeat(e, 32, axis=1))
+
+
+def test_indexer_formats_lossless_on_shared_grid():
+    """[W] "FP4 与 SWA Bounded Replay": the indexer in FP4, either scale format.  On rows both
+    formats represent, each round trip is exact and the two layouts differ only in their
+    scale arrays (4 E8M0 bytes per 128 channels against 8 E4M3 bytes)."""
+    rng = np.random.default_rng(41)
+    x = _rows_in_both_indexer_formats(rng, 50)
+    for fmt, n_sc in (("mxfp4", 4), ("nvfp4", 8)):
+        codes, scales = O.quantize_indexer(x, fmt)
+        assert codes.shape == (50, 64) and scales.shape == (50, n_sc)
+        assert np.array_equal(O.dequant_indexer(codes, scales, fmt), x)
+    mx, nv = O.quantize_indexer(x, "mxfp4"), O.quantize_indexer(x, "nvfp4")
+    assert np.array_equal(mx[0], nv[0])        # same E2M1 codes, different scales
+    with pytest.raises(ValueError):
+        O.quantize_indexer(x, "fp8")
+
+
+def test_indexer_scores_nvfp4_closed_form():
+    """Scores over an NVFP4 indexer cache: on shared-grid rows they equal the MXFP4 scores
+    and the definition sum_h w_h * max(0, q_h . k_j) evaluated term by term in exact
+    rationals; on general rows they follow the NVFP4 dequantised values (which differ from
+    the MXFP4 ones there)."""
+    rng = np.random.default_rng(42)
+    H, n = 4, 30
+    qx = _rows_in_both_indexer_formats(rng, H)
+    kx = _rows_in_both_indexer_formats(rng, n)
+    w = rng.uniform(size=H)
+    res = {}
+    for fmt in ("mxfp4", "nvfp4"):
+        kc, ks = O.quantize_indexer(kx, fmt)
+        qc, qs = O.quantize_indexer(qx, fmt)
+        caches = O.PackedCaches(None, None, kc, ks, index_fmt=fmt)
+        res[fmt] = O.full_scores(qc, qs, w, caches, n)[1]
+    for j in range(n):
+        exact = sum(Fraction(float(w[h])) * max(Fraction(0), sum(Fraction(float(a)) * Fraction(float(b))
+                                                                 for a, b in zip(qx[h], kx[j])))
+                    for h in range(H))
+        assert res["nvfp4"][j] == res["mxfp4"][j]
+        assert abs(Fraction(float(res["nvfp4"][j])) - exact) <= abs(exact) * Fraction(1, 2 ** 50)
+    # general rows: per-16 E4M3 scales hold values the per-32 power-of-two scales cannot
+    g = rng.normal(size=(8, 128))
+    mx = O.dequant_indexer(*O.quantize_indexer(g, "mxfp4"), "mxfp4")
+    nv = O.dequant_indexer(*O.quantize_indexer(g, "nvfp4"), "nvfp4")
+    assert not np.array_equal(mx, nv)
+    assert np.abs(nv - g).mean() < np.abs(mx - g).mean()
+    kc, ks = O.quantize_indexer(g, "nvfp4")
+    caches = O.PackedCaches(None, None, kc, ks, index_fmt="nvfp4")
+    qc, qs = O.quantize_indexer(g[:2], "nvfp4")
+    qd = O.dequant_nvfp4(qc, qs)
+    got = O.full_scores(qc, qs, np.array([0.5, 2.0]), caches, 8)[1]
+    want = [0.5 * max(0.0, math.fsum(qd[0] * nv[j])) + 2.0 * max(0.0, math.fsum(qd[1] * nv[j])) for j in range(8)]
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-12)
