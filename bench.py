@@ -186,6 +186,30 @@ def time_isolated(fn, iters, torch):
     return e0.elapsed_time(e1) / iters
 
 
+def time_call_graph(make, calls, replays, torch):
+    """Mean GPU time of one call, from HIP events (on the launch stream) around `replays`
+    replays of a graph holding `calls` back-to-back launches of it: the kernels' own
+    durations and the gaps between them, without the host's launch cost.  `make()` binds
+    the call to the current stream, so it is called inside the capture."""
+    make()()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn = make()
+        for _ in range(calls):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / (replays * calls)
+
+
 def steps_per_graph(steps: int) -> int:
     """Layer steps captured in one graph: consecutive layers of a decode step replay as one
     graph, so the per-launch cost of the runtime is paid once per group, not per layer.
@@ -227,6 +251,21 @@ def step_bytes(wl, mode: str, index_fmt: str = "mxfp4") -> int:
     attn = k * MAIN_ENTRY_B + W * 512 + wl.heads * 512 * (2 + 4) + wl.heads * 4 + k * 4
     pool = MAX_BLOCKS * 4 if mode in ("full_pool", "reindex_pool") else 0
     return score_bytes(wl, mode, index_fmt) + wl.n_q * (attn + pool)
+
+
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16 / bf16 matrix-core peak
+
+
+def attn_flops(wl) -> int:
+    """Algorithmic FLOPs of one attention launch: S = Q K^T and O = P V over the Top-512
+    entries plus the 128 window keys, 2 FLOP per multiply-add, for every head and query."""
+    return wl.n_q * 4 * wl.heads * (TOPK + WINDOW) * 512
+
+
+def attn_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one attention launch: the gathered main-KV entries (288 B),
+    the window keys (512 B), Q (bf16), the fp32 output and LSE and the index set."""
+    return wl.n_q * (TOPK * MAIN_ENTRY_B + WINDOW * 512 + wl.heads * 512 * (2 + 4) + wl.heads * 4 + TOPK * 4)
 
 
 def cpu_baseline(wl, n_sample: int, reps: int):
@@ -295,8 +334,12 @@ def measure_layers(name, steps, warmup, torch, C, layers_to_time, group: int = 1
         ms, _ = time_graph(g, steps, warmup, torch)
         res["group_ms"] = ms
         del g
-    res["isolated"] = {n: time_isolated(fn, 20, torch) for n, fn in lb.calls(layers_to_time[0]).items()}
-    del lb
+    L0 = layers_to_time[0]
+    calls0 = lb.calls(L0)
+    res["isolated"] = {n: time_isolated(fn, 20, torch) for n, fn in calls0.items()}
+    res["graph_call"] = {n: time_call_graph(lambda n=n: lb.calls(L0)[n], 8, max(steps // 8, 3), torch)
+                         for n in calls0}
+    del lb, calls0
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
@@ -409,12 +452,18 @@ def main():
     wl = head["wl"]
     ms = head["layers"][0]["ms"]
     phase = head["isolated"]
+    gcall = head["graph_call"]
     value = wl.n_q / (ms / 1000.0)
     sb = score_bytes(wl, "full")
-    achieved = sb / (phase["index_topk"] / 1000.0) / 1e9
+    achieved = sb / (gcall["index_topk"] / 1000.0) / 1e9
+    at_ms = gcall["attn"]
+    at_tflops = attn_flops(wl) / (at_ms / 1e3) / 1e12
+    at_gbs = attn_bytes(wl) / (at_ms / 1e3) / 1e9
     log(f"step {ms * 1000:.1f} us (graph replay); isolated launches (us): " +
-        ", ".join(f"{k}={v * 1000:.1f}" for k, v in phase.items()))
-    log(f"index_topk {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak)")
+        ", ".join(f"{k}={v * 1000:.1f}" for k, v in phase.items()) + "; per call in graphs (us): " +
+        ", ".join(f"{k}={v * 1000:.1f}" for k, v in gcall.items()))
+    log(f"index_topk {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak); attention "
+        f"{at_tflops:.1f} TFLOP/s ({at_tflops / MFMA_F16_PEAK_TFLOPS:.2%} of fp16 MFMA peak), {at_gbs:.0f} GB/s")
     result = {
         "metric": "CSA2 decode query-tokens/s per layer at 128K & 1M ctx; % HBM peak",
         "value": round(value, 1),
@@ -433,11 +482,19 @@ def main():
         "timing": f"HIP events around graph replays; each replay runs {head['per_graph']} consecutive layer "
                   f"steps (a decode step replays its layers as one graph), {args.steps} steps in total",
         "isolated_launch_us": {k: round(v * 1000, 2) for k, v in phase.items()},
+        "graph_call_us": {k: round(v * 1000, 2) for k, v in gcall.items()},
         "hbm_frac_step": round(step_bytes(wl, "full") / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": "csa2_index_topk (k_score_select + last selection level)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": sb,
-                     "traffic": measured_traffic()},
+                     "traffic": measured_traffic(),
+                     "timing": "HIP events around graph replays of 8 back-to-back csa2_index_topk calls"},
+        "attention": {"kernel": "csa2_sparse_attn (k_attn)", "us": round(at_ms * 1e3, 2),
+                      "flops_per_launch": attn_flops(wl), "tflops": round(at_tflops, 2),
+                      "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS, "mfma_frac": round(at_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                      "bytes_per_launch": attn_bytes(wl), "gb_per_s": round(at_gbs, 1),
+                      "hbm_frac": round(at_gbs / HBM_PEAK_GBS, 4),
+                      "timing": "HIP events around graph replays of 8 back-to-back csa2_sparse_attn calls"},
     }
     if not args.no_modes:
         modes = {}
@@ -485,13 +542,13 @@ def main():
             "isolated_launch_us_grouped": {k: round(v * 1e3, 1) for k, v in mt[4][2].items()}}
         # the NVFP4-style indexer variant on the headline step
         rn = measure_layers("c2", args.steps, args.warmup, torch, C, [0], index_fmt="nvfp4")
-        wln, msn, isn = rn["wl"], rn["layers"][0]["ms"], rn["isolated"]
+        wln, msn, isn, gcn = rn["wl"], rn["layers"][0]["ms"], rn["isolated"], rn["graph_call"]
         bn = score_bytes(wln, "full", "nvfp4")
-        gbs = bn / (isn["index_topk"] / 1e3) / 1e9
+        gbs = bn / (gcn["index_topk"] / 1e3) / 1e9
         modes["full_128k_nvfp4_indexer"] = {
             "index_format": "E2M1 + E4M3 per 16 (72 B per indexer-K entry), fp16 MFMA scoring",
             "us_per_layer_step": round(msn * 1e3, 2), "query_tokens_per_s": round(wln.n_q / (msn / 1e3), 1),
-            "index_topk_us": round(isn["index_topk"] * 1e3, 2), "index_topk_gb_per_s": round(gbs, 1),
+            "index_topk_us": round(gcn["index_topk"] * 1e3, 2), "index_topk_gb_per_s": round(gbs, 1),
             "index_topk_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "index_topk_bytes": bn,
             "isolated_launch_us": {k: round(v * 1e3, 2) for k, v in isn.items()}}
         for name, key in (("dec_128k", "decoder_128k"), ("dec_1m", "decoder_1m")):

@@ -511,26 +511,49 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   }
 }
 
-// merge the per-split (O, m, l) of one (query, head): 128 threads x 4 channels
-__global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
+// merge the per-split (O, m, l) of one (query, head): 128 threads x 4 channels.  Thread
+// sp < nsplit reads split sp's (m, l) into LDS; the partial outputs are read eight splits
+// at a time with unconditional (clamped) loads and weights that are zero past the last
+// split, so the merge costs a few memory round trips instead of two per split.  (Merging
+// inside the attention kernel, in the last split's workgroup to finish, was measured much
+// slower: the agent-scope release that publishes the partial results writes back the L2.)
+constexpr int kCombThreads = 128;   // also the most splits a merge takes
+
+__global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
   const int qh = blockIdx.x;  // q * n_heads + h
   const int tid = threadIdx.x;
+  const int ns = a.nsplit;
   const int64_t stride = (int64_t)a.n_q * a.n_heads;
+  __shared__ float s_m[kCombThreads], s_l[kCombThreads];
+  if (tid < ns) {
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (tid * stride + qh) * 2);
+    s_m[tid] = ml.x;
+    s_l[tid] = ml.y;
+  }
+  __syncthreads();
   float M = -__builtin_inff();
-  for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, a.ws_ml[(sp * stride + qh) * 2]);
+  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_m[sp]);
   float L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (M != -__builtin_inff()) {
-    for (int sp = 0; sp < a.nsplit; ++sp) {
-      const int64_t pb = sp * stride + qh;
-      const float m = a.ws_ml[pb * 2];
-      const float wgt = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-      L += wgt * a.ws_ml[pb * 2 + 1];
-      const float4 v = *reinterpret_cast<const float4*>(a.ws_o + pb * kD + tid * 4);
-      acc.x += wgt * v.x;
-      acc.y += wgt * v.y;
-      acc.z += wgt * v.z;
-      acc.w += wgt * v.w;
+    for (int sp0 = 0; sp0 < ns; sp0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sp = sp0 + u < ns ? sp0 + u : ns - 1;
+        v[u] = *reinterpret_cast<const float4*>(a.ws_o + (sp * stride + qh) * kD + tid * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sp = sp0 + u < ns ? sp0 + u : ns - 1;
+        const float m = s_m[sp];
+        const float wgt = (sp0 + u < ns && m != -__builtin_inff()) ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+        L += wgt * s_l[sp];
+        acc.x += wgt * v[u].x;
+        acc.y += wgt * v[u].y;
+        acc.z += wgt * v[u].z;
+        acc.w += wgt * v[u].w;
+      }
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -600,7 +623,7 @@ extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, co
     return CSA2_ERR_SHAPE;
   if (n_q == 0) return CSA2_OK;
   AttnPlan p = plan(n_q, n_heads, k, window);
-  if (p.grid > 0x7fffffffLL) return CSA2_ERR_SHAPE;
+  if (p.grid > 0x7fffffffLL || p.nsplit > kCombThreads) return CSA2_ERR_SHAPE;
   AttnArgs a = {};
   a.q = (const uint16_t*)q;
   a.n_q = n_q;
@@ -639,6 +662,6 @@ extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, co
                      a.swa_base);
   int rc = csa2_check_launch();
   if (rc != CSA2_OK || p.nsplit == 1) return rc;
-  hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(n_q * n_heads)), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(n_q * n_heads)), dim3(kCombThreads), 0, st, a);
   return csa2_check_launch();
 }

@@ -22,11 +22,14 @@ namespace csa2 {
 // binade, as it should be) and the exponent is rebiased from 127 to 7.  Subnormal range:
 // the code is a * 2^9 rounded to an integer, ties to even (a * 2^9 is exact); 8 is the
 // smallest normal code, so a carry there is also right.
+// Both ranges are computed and one is selected, so that the code has no branch (a branch
+// here would sit between the loads of a group's values and make them wait one by one).
 __device__ __forceinline__ int fp8_mag_code(float a) {
-  if (a < 0x1p-6f) return (int)__builtin_rintf(a * 512.0f);
+  const int sub = (int)__builtin_rintf(fminf(a, 0x1p-6f) * 512.0f);
   const uint32_t b = __float_as_uint(a);
-  const int c = (int)((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120 << 3);
-  return c > 126 ? 126 : c;
+  int c = (int)((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120 << 3);
+  c = c > 126 ? 126 : c;
+  return a < 0x1p-6f ? sub : c;
 }
 
 // "a/6 rounds to an E4M3 code >= c" for c >= 1: a/6 lies above the midpoint of codes c-1
@@ -60,6 +63,14 @@ __device__ __forceinline__ uint32_t e2m1_code(float a, float s) {
   return c;
 }
 
+// An empty asm that takes a group's results as inputs: the arithmetic (and the loads it
+// depends on) must then run before the destination check that follows, instead of being
+// moved behind it, where the loads would only be issued once the destination row has
+// arrived.
+__device__ __forceinline__ void keep_before_branch(uint32_t a, uint32_t b, uint32_t c) {
+  asm volatile("" ::"v"(a), "v"(b), "v"(c));
+}
+
 template <typename T>
 __device__ __forceinline__ uint32_t load_bits(const T* p, int64_t i);
 
@@ -73,7 +84,7 @@ __device__ __forceinline__ uint32_t load_bits<uint16_t>(const uint16_t* p, int64
 }
 
 // ---- NVFP4: one thread per 16-channel group ----
-template <typename T>
+template <bool kMap, typename T>
 __device__ __forceinline__ void quant_group_nvfp4(const T* __restrict__ src, int64_t rows, int dim,
                                                   const int64_t* __restrict__ dst_row, int64_t dst_rows,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -82,8 +93,9 @@ __device__ __forceinline__ void quant_group_nvfp4(const T* __restrict__ src, int
   if (gid >= rows * gpr) return;
   int64_t r = gid / gpr;
   int g = (int)(gid % gpr);
-  int64_t d = dst_row ? dst_row[r] : r;
-  if (d < 0 || d >= dst_rows) return;
+  // the destination row is loaded together with the source values and checked only at the
+  // stores, so that both loads are one memory round trip
+  const int64_t d = kMap ? dst_row[r] : r;
   uint32_t bits[16];
   uint32_t amax_bits = 0;
 #pragma unroll
@@ -102,13 +114,15 @@ __device__ __forceinline__ void quant_group_nvfp4(const T* __restrict__ src, int
     if (i < 8) lo |= c << (4 * i);
     else hi |= c << (4 * (i - 8));
   }
+  keep_before_branch(lo, hi, (uint32_t)sc);
+  if (d < 0 || d >= dst_rows) return;
   uint2* out = reinterpret_cast<uint2*>(codes + d * (dim / 2) + g * 8);
   *out = make_uint2(lo, hi);
   scales[d * gpr + g] = (uint8_t)sc;
 }
 
 // ---- MXFP4: one thread per 32-channel group ----
-template <typename T>
+template <bool kMap, typename T>
 __device__ __forceinline__ void quant_group_mxfp4(const T* __restrict__ src, int64_t rows, int dim,
                                                   const int64_t* __restrict__ dst_row, int64_t dst_rows,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -117,8 +131,7 @@ __device__ __forceinline__ void quant_group_mxfp4(const T* __restrict__ src, int
   if (gid >= rows * gpr) return;
   int64_t r = gid / gpr;
   int g = (int)(gid % gpr);
-  int64_t d = dst_row ? dst_row[r] : r;
-  if (d < 0 || d >= dst_rows) return;
+  const int64_t d = kMap ? dst_row[r] : r;   // checked at the stores (see above)
   uint32_t bits[32];
   uint32_t amax_bits = 0;
 #pragma unroll
@@ -147,13 +160,15 @@ __device__ __forceinline__ void quant_group_mxfp4(const T* __restrict__ src, int
     uint32_t c = mag | ((bits[i] >> 28) & 8u);
     w[i >> 3] |= c << (4 * (i & 7));
   }
+  keep_before_branch(w[0] ^ w[1], w[2] ^ w[3], (uint32_t)code);
+  if (d < 0 || d >= dst_rows) return;
   uint4* out = reinterpret_cast<uint4*>(codes + d * (dim / 2) + g * 16);
   *out = make_uint4(w[0], w[1], w[2], w[3]);
   scales[d * gpr + g] = (uint8_t)code;
 }
 
 // ---- FP8 (E4M3, unscaled): one thread per 8 channels ----
-template <typename T>
+template <bool kMap, typename T>
 __device__ __forceinline__ void quant_group_fp8(const T* __restrict__ src, int64_t rows, int dim,
                                                 const int64_t* __restrict__ dst_row, int64_t dst_rows,
                                                 uint8_t* __restrict__ codes, int64_t gid) {
@@ -161,16 +176,20 @@ __device__ __forceinline__ void quant_group_fp8(const T* __restrict__ src, int64
   if (gid >= rows * gpr) return;
   int64_t r = gid / gpr;
   int g = (int)(gid % gpr);
-  int64_t d = dst_row ? dst_row[r] : r;
-  if (d < 0 || d >= dst_rows) return;
+  const int64_t d = kMap ? dst_row[r] : r;   // checked at the store (see above)
+  uint32_t bits[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bits[i] = load_bits(src, r * dim + g * 8 + i);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    uint32_t b = load_bits(src, r * dim + g * 8 + i);
+    const uint32_t b = bits[i];
     uint32_t c = (uint32_t)fp8_mag_code(__uint_as_float(b & 0x7fffffffu)) | ((b >> 24) & 0x80u);
     if (i < 4) lo |= c << (8 * i);
     else hi |= c << (8 * (i - 4));
   }
+  keep_before_branch(lo, hi, 0u);
+  if (d < 0 || d >= dst_rows) return;
   *reinterpret_cast<uint2*>(codes + d * dim + g * 8) = make_uint2(lo, hi);
 }
 
@@ -191,17 +210,25 @@ struct QuantJobs {
   int n;
 };
 
-__device__ __forceinline__ void quant_dispatch(const QuantJob& j, int64_t gid) {
+template <bool kMap>
+__device__ __forceinline__ void quant_dispatch_map(const QuantJob& j, int64_t gid) {
   if (j.fmt == CSA2_FMT_NVFP4) {
-    if (j.bf16) quant_group_nvfp4((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
-    else quant_group_nvfp4((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
+    if (j.bf16) quant_group_nvfp4<kMap>((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
+    else quant_group_nvfp4<kMap>((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
   } else if (j.fmt == CSA2_FMT_MXFP4) {
-    if (j.bf16) quant_group_mxfp4((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
-    else quant_group_mxfp4((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
+    if (j.bf16) quant_group_mxfp4<kMap>((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
+    else quant_group_mxfp4<kMap>((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
   } else {
-    if (j.bf16) quant_group_fp8((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, gid);
-    else quant_group_fp8((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, gid);
+    if (j.bf16) quant_group_fp8<kMap>((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, gid);
+    else quant_group_fp8<kMap>((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, gid);
   }
+}
+
+// (the row map is a separate instantiation: a load behind a branch on whether the map
+// exists would be waited for before the source values are requested)
+__device__ __forceinline__ void quant_dispatch(const QuantJob& j, int64_t gid) {
+  if (j.dst_row) quant_dispatch_map<true>(j, gid);
+  else quant_dispatch_map<false>(j, gid);
 }
 
 // Every job of the launch gets its own range of workgroups; a workgroup finds its job by the

@@ -219,13 +219,15 @@ struct QueryScorer {
   }
 
   // slot -> (row to read, valid); invalid slots read row 0 and their results are discarded,
-  // so the loads need no per-lane branches
+  // so the loads need no per-lane branches.  Inside a pool the block id is loaded for every
+  // slot (slot 0's for an invalid one): a load under a per-lane condition would be waited
+  // for on its own, before the loads that follow it are issued.
   __device__ __forceinline__ bool slot_pos(const ScoreArgs& s, int slot, uint32_t& pos) const {
     bool valid = slot < n_valid;
     int p = slot;
-    if (kPool && valid) {
-      const int32_t b = cb[(uint32_t)slot / (uint32_t)s.block];
-      valid = b >= 0 && b <= blk_lim;   // bounds b before b * block can overflow
+    if (kPool) {
+      const int32_t b = cb[(valid ? (uint32_t)slot : 0u) / (uint32_t)s.block];
+      valid = valid && b >= 0 && b <= blk_lim;   // bounds b before b * block can overflow
       p = b * s.block + (int)((uint32_t)slot % (uint32_t)s.block);
       valid = valid && p < nv;
     }
@@ -371,13 +373,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
     int bsn[4];
     const int next = base + 4 * kScoreStep;
     sc.load_step(s, next < hi ? next : base, bcn, bsn);
-    const float v = sc.score_step(bc, bs);
     const int slot = base + lane;
-    if (slot < hi) {
-      uint32_t pos;
-      const bool valid = sc.slot_pos(s, slot, pos);
-      out[slot] = (kPool && !valid) ? -__builtin_inff() : v;   // without a pool, slot < hi <= n_valid
-    }
+    uint32_t pos;
+    const bool valid = sc.slot_pos(s, slot, pos);   // (its block-id load overlaps the MFMAs)
+    const float v = sc.score_step(bc, bs);
+    if (slot < hi) out[slot] = (kPool && !valid) ? -__builtin_inff() : v;   // without a pool, slot < hi <= n_valid
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       bc[t] = bcn[t];

@@ -38,47 +38,90 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(TkArgs a) {
   const int64_t c0 = (int64_t)seg * kTkSeg;
 
   // ---- load this segment's candidates as keys (0 = no candidate); candidate c0 + i*256 + tid ----
+  // Every load is unconditional, to a clamped in-bounds address, and absent candidates are
+  // masked afterwards without a branch: a load under a per-lane condition compiles to a
+  // branch around it and a wait for it, which turns the 32 loads of a thread into 32
+  // memory round trips one after another.
   uint64_t key[kTkEpt];
   if (kMode == kFromScores && a.cand_blocks == nullptr) {
-    const float* sp = a.scores + q * a.scores_stride + c0;
     const int lim = (int)(nv - c0 < kTkSeg ? (nv - c0 > 0 ? nv - c0 : 0) : kTkSeg);
+    if (lim > 0) {  // uniform
+      const float* sp = a.scores + q * a.scores_stride + c0;
+      float v[kTkEpt];
 #pragma unroll
-    for (int i = 0; i < kTkEpt; ++i) {
-      const int o = i * kTkThreads + tid;
-      key[i] = o < lim ? make_key(sp[o], (uint32_t)(c0 + o)) : 0ull;
+      for (int i = 0; i < kTkEpt; ++i) {
+        const int o = i * kTkThreads + tid;
+        v[i] = sp[o < lim ? o : lim - 1];
+      }
+#pragma unroll
+      for (int i = 0; i < kTkEpt; ++i) {
+        const int o = i * kTkThreads + tid;
+        key[i] = make_key(v[i], (uint32_t)(c0 + o)) & (0ull - (uint64_t)(o < lim));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTkEpt; ++i) key[i] = 0ull;
     }
   } else if (kMode == kFromScores) {
     int64_t nc = a.n_cand_blocks[q];
     nc = nc < 0 ? 0 : (nc > a.max_cand_blocks ? a.max_cand_blocks : nc);
-    const float* sp = a.scores + q * a.scores_stride;
-    const int32_t* cb = a.cand_blocks + (int64_t)q * a.max_cand_blocks;
+    // slots holding a candidate; at most 2^20 blocks of at most 64 slots, so 32 bits suffice
+    const int64_t nslot = nc * a.block;
+    if (c0 < nslot) {  // uniform
+      const float* sp = a.scores + q * a.scores_stride;
+      const int32_t* cb = a.cand_blocks + (int64_t)q * a.max_cand_blocks;
+      const uint32_t blk = (uint32_t)a.block;
+      const uint32_t last = (uint32_t)(nslot - 1);
+      int32_t bv[kTkEpt];
+      float v[kTkEpt];
 #pragma unroll
-    for (int i = 0; i < kTkEpt; ++i) {
-      const int64_t c = c0 + i * kTkThreads + tid;
-      uint64_t kk = 0;
-      if (c < nc * a.block) {
-        const int32_t b = cb[c / a.block];
-        const int64_t pos = (int64_t)b * a.block + c % a.block;
-        if (b >= 0 && pos < nv) kk = make_key(sp[c], (uint32_t)pos);
+      for (int i = 0; i < kTkEpt; ++i) {
+        uint32_t c = (uint32_t)c0 + (uint32_t)(i * kTkThreads + tid);
+        c = c < last ? c : last;
+        bv[i] = cb[c / blk];
+        v[i] = sp[c];
       }
-      key[i] = kk;
+#pragma unroll
+      for (int i = 0; i < kTkEpt; ++i) {
+        const int64_t c = c0 + i * kTkThreads + tid;
+        const int64_t pos = (int64_t)bv[i] * blk + (uint32_t)c % blk;
+        const bool ok = c < nslot && bv[i] >= 0 && pos < nv;
+        key[i] = make_key(v[i], (uint32_t)pos) & (0ull - (uint64_t)ok);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTkEpt; ++i) key[i] = 0ull;
     }
   } else if (kMode == kFromBlockMax) {
     const int64_t nblk = (nv + a.block - 1) / a.block;
-    const float* sp = a.scores + q * a.scores_stride;
+    if (c0 < nblk) {  // uniform; then nv >= 1
+      const float* sp = a.scores + q * a.scores_stride;
+      float m[kTkEpt];
+      // position j of every block, clamped to the last visible position: that position lies
+      // in the last block, so a clamped read repeats one of that block's own scores
+      // (offsets fit 32 bits: nv <= 2^31 - 1 and a block is at most 64 positions)
+      const uint32_t blk = (uint32_t)a.block, lastb = (uint32_t)(nblk - 1), lastp = (uint32_t)(nv - 1);
+      for (uint32_t j = 0; j < blk; ++j) {
+        float x[kTkEpt];
 #pragma unroll
-    for (int i = 0; i < kTkEpt; ++i) {
-      const int64_t c = c0 + i * kTkThreads + tid;
-      uint64_t kk = 0;
-      if (c < nblk) {
-        const float* s = sp + c * a.block;
-        int64_t nin = nv - c * a.block;
-        nin = nin < a.block ? nin : a.block;
-        float m = s[0];
-        for (int j = 1; j < nin; ++j) m = fmaxf(m, s[j]);
-        kk = make_key(m, (uint32_t)c);
+        for (int i = 0; i < kTkEpt; ++i) {
+          uint32_t c = (uint32_t)c0 + (uint32_t)(i * kTkThreads + tid);
+          c = c < lastb ? c : lastb;
+          uint32_t p = c * blk + j;
+          p = p < lastp ? p : lastp;
+          x[i] = sp[p];
+        }
+#pragma unroll
+        for (int i = 0; i < kTkEpt; ++i) m[i] = j == 0 ? x[i] : fmaxf(m[i], x[i]);
       }
-      key[i] = kk;
+#pragma unroll
+      for (int i = 0; i < kTkEpt; ++i) {
+        const int64_t c = c0 + i * kTkThreads + tid;
+        key[i] = make_key(m[i], (uint32_t)c) & (0ull - (uint64_t)(c < nblk));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTkEpt; ++i) key[i] = 0ull;
     }
   } else {
     const uint64_t* kp = a.keys_in + q * a.keys_in_per_q + c0;

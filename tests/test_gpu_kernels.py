@@ -510,6 +510,45 @@ def test_sparse_attn_parity(C, heads, out_dt):
         assert np.abs(gl[qi] - ref_lse).max() <= 1e-3
 
 
+@pytest.mark.parametrize("n_q", [6, 32])
+def test_sparse_attn_split_workspace_reuse(C, n_q):
+    """Split key lists (10 splits at 6 queries, 2 at 32): consecutive calls on one
+    workspace give bit-identical outputs and match the oracle."""
+    _say("sparse_attn split reuse", n_q)
+    heads = 64
+    t = [2000 - 37 * i for i in range(n_q)]
+    s = [0] * n_q
+    case = _attn_case(11 + n_q, n_q, 2001, heads, t, s)
+    wl = case.wl
+    caches = case.gpu_caches()
+    _, _, qa = case.gpu_query_inputs(0)
+    q_seq, _, q_pos, rs = case.gpu_meta()
+    rng = np.random.default_rng(n_q)
+    idx = np.stack([np.sort(rng.choice(t[i] + 1, size=512, replace=False)) for i in range(n_q)]).astype(np.int32)
+    need = C.csa2_attn_workspace_bytes(n_q, heads, 512, 512, 128)
+    assert need > 0                                  # the key list is split at these sizes
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        out = torch.empty(n_q, heads, 512, dtype=torch.float32, device="cuda")
+        lse = torch.empty(n_q, heads, dtype=torch.float32, device="cuda")
+        C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, torch.from_numpy(idx).cuda(), caches.swa[0],
+                           caches.swa_base, q_pos, rs, 128, 1.0 / math.sqrt(512), out, lse, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((out.cpu(), lse.cpu()))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    go, gl = outs[0][0].numpy(), outs[0][1].numpy()
+    for qi in (0, n_q - 1):
+        seq = int(wl.q_seq[qi])
+        oc = case.oracle_caches(seq)
+        _, _, _, qa_np = case.oracle_query(0, qi)
+        ref, ref_lse = O.sparse_attention(qa_np, oc.main_rows(idx[qi]),
+                                          oc.swa_rows(0, O.swa_positions(t[qi], s[qi], 128)), 1 / math.sqrt(512))
+        G.attn_close(go[qi], ref, 2e-3)
+        assert np.abs(gl[qi] - ref_lse).max() <= 1e-3
+
+
 def test_sparse_attn_no_keys(C):
     """s > t leaves the window empty; with no main entries the output is 0 and lse -inf."""
     _say("sparse_attn no keys")
