@@ -195,13 +195,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   const int64_t lo = s > t - a.window + 1 ? s : t - a.window + 1;
   const int64_t n_swa = seq_ok && t >= lo ? t - lo + 1 : 0;
   const int64_t swa_b = seq_ok ? swa_base[seq] : 0;
-  if (n_keys > 0) {
-#pragma unroll
-    for (int r = 0; r < kIdxPer; ++r) {
-      const int i = tid + r * kAttnThreads;
-      if (i < n_keys) s_idx[i] = tile_lo * kT + i < a.k ? iv[r] : -1;
-    }
-  }
   // ring row of the first window key; later keys wrap at most once (window <= swa_cap).
   // The offset from the ring base nearly always fits 32 bits: then a 32-bit remainder
   const int64_t rel = lo - swa_b;
@@ -217,9 +210,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 2);
   const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 16);
   const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_cap * kD;
-  if (lane == 0) s_flag[wave] = 0u;
-  __syncthreads();  // s_idx, s_flag
-
   // ---- this pair's tiles: window tiles first (their rows need no index), then main tiles;
   // pair p takes positions p, p+4, ... of that order.  Every wave runs the same number of
   // steps (one workgroup barrier each) and masks the steps past its pair's end ----
@@ -257,6 +247,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     g.sc = *reinterpret_cast<const uint32_t*>(kvs + (pm * (kD / 16) + 16 * half + 4 * grp));
     g.ok = is_main ? ok_main : ok_win;
   };
+
+  // The first two tiles of every key stream are window tiles when the slice holds at least
+  // 2 * kPairs of them (always without a key split); their rows need no index, so their
+  // gathers go out before the wait for the index list.  Either way the ring slots are filled
+  // in the order g0, g1, g2.
+  const bool early = n_win >= 2 * kPairs;   // uniform over the workgroup
+  GatherSlot g0, g1, g2;
+  if (early) {
+    load_slot(my_tile(0), 0 < n_my, g0);
+    load_slot(my_tile(1), 1 < n_my, g1);
+  }
+
+  if (n_keys > 0) {
+#pragma unroll
+    for (int r = 0; r < kIdxPer; ++r) {
+      const int i = tid + r * kAttnThreads;
+      if (i < n_keys) s_idx[i] = tile_lo * kT + i < a.k ? iv[r] : -1;
+    }
+  }
+  if (lane == 0) s_flag[wave] = 0u;
+  __syncthreads();  // s_idx, s_flag
+  if (!early) {
+    load_slot(my_tile(0), 0 < n_my, g0);
+    load_slot(my_tile(1), 1 < n_my, g1);
+  }
 
   // Q as the fp16 B operand
   v8h qf[kQS];
@@ -400,9 +415,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   // cores and the vector units.  The raw bytes of tiles i+2 .. i+4 are in flight meanwhile:
   // ring slot (i+1) % 3 is refilled with tile i+4 as soon as tile i+1 has left it ----
   auto tile_is_main = [&](int i) { return my_tile(i) < a.main_tiles; };
-  GatherSlot g0, g1, g2;
-  load_slot(my_tile(0), 0 < n_my, g0);
-  load_slot(my_tile(1), 1 < n_my, g1);
   load_slot(my_tile(2), 2 < n_my, g2);
 #pragma unroll
   for (int st = 0; st < kQS; ++st) {
@@ -431,16 +443,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     pb = softmax_tile(sv, vmask, &alpha);   // tile i+1
     rescale(alpha);
   };
-  // whole rounds of the ring inside the loop and the remainder after it: a loop with exits
-  // between its steps would make the compiler wait for every load in flight at its head
+  // Steps 0 .. n_steps-2 form S of tiles 1 .. n_steps-1; the last tile then only needs its
+  // P.V (a full last step would form and exchange the S of a tile past the end).  Whole
+  // rounds of the ring inside the loop and the remainder after it: a loop with exits
+  // between its steps would make the compiler wait for every load in flight at its head.
+  const int n_full = n_steps - 1;
   int i = 0;
-  for (; i + kRing <= n_steps; i += kRing) {
+  for (; i + kRing <= n_full; i += kRing) {
     step(i, g1);
     step(i + 1, g2);
     step(i + 2, g0);
   }
-  if (i < n_steps) step(i, g1);  // uniform over the workgroup
-  if (i + 1 < n_steps) step(i + 1, g2);
+  if (i < n_full) step(i, g1);  // uniform over the workgroup
+  if (i + 1 < n_full) step(i + 1, g2);
+  if (n_steps > 0) pv_tile(pb, vbuf + (n_full & 1) * kVBuf);   // tile n_steps-1
 
   // ---- merge the four pairs' (O, m, l); the two waves of a pair hold the same (m, l) ----
   float l_tot = l_run + __shfl_xor(l_run, 16);
