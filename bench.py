@@ -51,10 +51,9 @@ class LayerBench:
     (`swa_miss`: the prefix's window state is not cached) the rings start empty and every
     layer writes the window entries of all its query rows, replay rows included."""
 
-    def __init__(self, wl, torch, C, group: int = 1, index_fmt: str = "mxfp4"):
+    def __init__(self, wl, torch, C, group: int = 1, index_fmt: str = "mxfp4", attn_select: bool = False):
         from fp4_kv_cache_layer_amd.layer import INDEX_FORMATS, Caches, Csa2Step, plan_group
         self.wl, self.torch, self.C = wl, torch, C
-        self.plan = plan_group(wl.layers, group=group, index_fmt=index_fmt)
         self.ik_fmt, self.ik_group = INDEX_FORMATS[index_fmt]
         n_layers = len(wl.layers)
         dev = "cuda"
@@ -108,7 +107,9 @@ class LayerBench:
                         for L in range(n_layers)]
         self.dst_entry = torch.from_numpy(ent_seq * wl.seq_cap + ent_row).to(dev)
         self.dst_swa = torch.from_numpy(tok_seq * wl.swa_cap + (tok_pos - wl.swa_base) % wl.swa_cap).to(dev)
-        self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group, index_fmt=index_fmt)
+        self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group, index_fmt=index_fmt,
+                             attn_select=attn_select)
+        self.plan = plan_group(wl.layers, group=group, index_fmt=index_fmt, attn_select=self.step.attn_select)
 
     def calls(self, L: int):
         """Layer L's step as {phase: bound call} bound to the current stream, in order."""
@@ -135,10 +136,24 @@ class LayerBench:
         elif "score_grouped" in names:
             out["score"] = st.score_grouped(c, w, self.q_seq, self.n_vis, bind=True)
             out["select"] = st.select(self.n_vis, bind=True)
+        elif "index_segments" in names:
+            out["index_segments"] = st.index_segments(c, w, self.q_seq, self.n_vis, bind=True)
         elif mode != "reuse":
             out["index_topk"] = st.index_topk(c, w, self.q_seq, self.n_vis, mode == "reindex_pool", bind=True)
-        out["attn"] = st.attend(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True)
+        if "attend_topk" in names:   # the last Top-K level runs inside the attention call
+            out["attn"] = st.attend_topk(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True)
+        else:
+            out["attn"] = st.attend(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True)
         return out
+
+    def segments_call(self, L: int):
+        """Layer L's scoring pass alone (csa2_index_segments: the one k_score_select launch of
+        csa2_index_topk, same grid and arguments), bound to the current stream; None where the
+        layer does not score every visible entry or its survivors exceed one selection."""
+        mode, st = self.wl.layers[L], self.step
+        if mode not in ("full", "reindex") or not 1 <= self.C.csa2_segment_keys(self.wl.seq_cap, st.k) <= 8192:
+            return None
+        return st.index_segments(self.caches, self.inputs[L][1], self.q_seq, self.n_vis, bind=True)
 
     def record(self, layers):
         """Issues the steps of `layers` on the current stream.  (Forking the appends onto
@@ -313,14 +328,15 @@ def cpu_baseline(wl, n_sample: int, reps: int):
                       f"run {reps}x; {el:.1f}s; numpy fp64, BLAS threads = cores"}
 
 
-def measure_layers(name, steps, warmup, torch, C, layers_to_time, group: int = 1, index_fmt: str = "mxfp4"):
+def measure_layers(name, steps, warmup, torch, C, layers_to_time, group: int = 1, index_fmt: str = "mxfp4",
+                   attn_select: bool = False):
     """Graph-replay time of each listed layer's step (`steps` steps in graphs of
     steps_per_graph(steps) consecutive steps of that layer) and of the whole group (one
     group per graph); isolated launch times of the first listed layer's calls."""
     from synth import workloads
     wl = workloads.config(name)
     log(f"workload {name}: {wl.description}")
-    lb = LayerBench(wl, torch, C, group, index_fmt)
+    lb = LayerBench(wl, torch, C, group, index_fmt, attn_select)
     res = {"wl": wl, "layers": {}}
     G = steps_per_graph(steps)
     res["per_graph"] = G
@@ -339,6 +355,10 @@ def measure_layers(name, steps, warmup, torch, C, layers_to_time, group: int = 1
     res["isolated"] = {n: time_isolated(fn, 20, torch) for n, fn in calls0.items()}
     res["graph_call"] = {n: time_call_graph(lambda n=n: lb.calls(L0)[n], 8, max(steps // 8, 3), torch)
                          for n in calls0}
+    if "index_segments" not in calls0 and lb.segments_call(L0) is not None:
+        # the dominant kernel on its own, for its roofline
+        res["graph_call"]["scoring_kernel"] = time_call_graph(lambda: lb.segments_call(L0), 8, max(steps // 8, 3),
+                                                              torch)
     del lb, calls0
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -455,14 +475,20 @@ def main():
     gcall = head["graph_call"]
     value = wl.n_q / (ms / 1000.0)
     sb = score_bytes(wl, "full")
-    achieved = sb / (gcall["index_topk"] / 1000.0) / 1e9
+    # the dominant kernel, k_score_select (FP4 scores of every visible entry and the first
+    # Top-K level), timed alone through csa2_index_segments, which launches just that kernel
+    # with the grid and arguments of the step's csa2_index_topk call
+    score_call = "scoring_kernel"
+    achieved = sb / (gcall[score_call] / 1000.0) / 1e9
+    call_gbs = sb / (gcall["index_topk"] / 1000.0) / 1e9
     at_ms = gcall["attn"]
     at_tflops = attn_flops(wl) / (at_ms / 1e3) / 1e12
     at_gbs = attn_bytes(wl) / (at_ms / 1e3) / 1e9
     log(f"step {ms * 1000:.1f} us (graph replay); isolated launches (us): " +
         ", ".join(f"{k}={v * 1000:.1f}" for k, v in phase.items()) + "; per call in graphs (us): " +
         ", ".join(f"{k}={v * 1000:.1f}" for k, v in gcall.items()))
-    log(f"index_topk {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak); attention "
+    log(f"k_score_select {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak); csa2_index_topk call "
+        f"{call_gbs:.0f} GB/s ({call_gbs / HBM_PEAK_GBS:.1%}); attention "
         f"{at_tflops:.1f} TFLOP/s ({at_tflops / MFMA_F16_PEAK_TFLOPS:.2%} of fp16 MFMA peak), {at_gbs:.0f} GB/s")
     result = {
         "metric": "CSA2 decode query-tokens/s per layer at 128K & 1M ctx; % HBM peak",
@@ -484,11 +510,17 @@ def main():
         "isolated_launch_us": {k: round(v * 1000, 2) for k, v in phase.items()},
         "graph_call_us": {k: round(v * 1000, 2) for k, v in gcall.items()},
         "hbm_frac_step": round(step_bytes(wl, "full") / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "csa2_index_topk (k_score_select + last selection level)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "k_score_select (FP4 scoring of every visible entry + the first Top-K level; "
+                               "timed alone through csa2_index_segments)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": sb,
                      "traffic": measured_traffic(),
-                     "timing": "HIP events around graph replays of 8 back-to-back csa2_index_topk calls"},
+                     "timing": "HIP events around graph replays of 8 back-to-back csa2_index_segments calls",
+                     "index_topk_call": {"us": round(gcall["index_topk"] * 1e3, 2), "gb_per_s": round(call_gbs, 1),
+                                         "frac": round(call_gbs / HBM_PEAK_GBS, 4),
+                                         "note": "the step's whole scoring call: k_score_select + the last "
+                                                 "selection level (a launch of its own)"}},
         "attention": {"kernel": "csa2_sparse_attn (k_attn)", "us": round(at_ms * 1e3, 2),
                       "flops_per_launch": attn_flops(wl), "tflops": round(at_tflops, 2),
                       "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS, "mfma_frac": round(at_tflops / MFMA_F16_PEAK_TFLOPS, 4),
@@ -540,16 +572,26 @@ def main():
             "us_per_layer_step_grouped_scoring": round(mt[4][1] * 1e3, 2),
             "isolated_launch_us": {k: round(v * 1e3, 1) for k, v in mt[1][2].items()},
             "isolated_launch_us_grouped": {k: round(v * 1e3, 1) for k, v in mt[4][2].items()}}
+        # the headline step with the last Top-K level inside the attention call
+        rs_ = measure_layers("c2", args.steps, args.warmup, torch, C, [0], attn_select=True)
+        modes["full_128k_select_in_attention"] = {
+            "calls": "csa2_index_segments, then csa2_sparse_attn_topk (the last Top-K level in the attention call)",
+            "us_per_layer_step": round(rs_["layers"][0]["ms"] * 1e3, 2),
+            "query_tokens_per_s": round(rs_["wl"].n_q / (rs_["layers"][0]["ms"] / 1e3), 1),
+            "graph_call_us": {k: round(v * 1e3, 2) for k, v in rs_["graph_call"].items()}}
         # the NVFP4-style indexer variant on the headline step
         rn = measure_layers("c2", args.steps, args.warmup, torch, C, [0], index_fmt="nvfp4")
         wln, msn, isn, gcn = rn["wl"], rn["layers"][0]["ms"], rn["isolated"], rn["graph_call"]
         bn = score_bytes(wln, "full", "nvfp4")
-        gbs = bn / (gcn["index_topk"] / 1e3) / 1e9
+        scn = "index_topk"
+        gbs = bn / (gcn[scn] / 1e3) / 1e9
         modes["full_128k_nvfp4_indexer"] = {
             "index_format": "E2M1 + E4M3 per 16 (72 B per indexer-K entry), fp16 MFMA scoring",
             "us_per_layer_step": round(msn * 1e3, 2), "query_tokens_per_s": round(wln.n_q / (msn / 1e3), 1),
-            "index_topk_us": round(gcn["index_topk"] * 1e3, 2), "index_topk_gb_per_s": round(gbs, 1),
-            "index_topk_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "index_topk_bytes": bn,
+            "scoring_call": f"csa2_{scn}_nvfp4", "scoring_us": round(gcn[scn] * 1e3, 2),
+            "scoring_gb_per_s": round(gbs, 1),
+            "scoring_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "scoring_bytes": bn,
+            "scoring_kernel_us": round(gcn["scoring_kernel"] * 1e3, 2) if "scoring_kernel" in gcn else None,
             "isolated_launch_us": {k: round(v * 1e3, 2) for k, v in isn.items()}}
         for name, key in (("dec_128k", "decoder_128k"), ("dec_1m", "decoder_1m")):
             wld, msd = measure_group(name, args.steps, args.warmup, torch, C)

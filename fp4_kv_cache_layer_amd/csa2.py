@@ -73,6 +73,11 @@ def lib() -> ctypes.CDLL:
         "csa2_sparse_attn": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp, vp, vp, i32, f32, vp,
                               i32, vp, vp, sz, vp], i32),
         "csa2_attn_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
+        "csa2_index_segments": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp], i32),
+        "csa2_index_segments_nvfp4": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp], i32),
+        "csa2_segment_keys": ([i64, i32], i64),
+        "csa2_sparse_attn_topk": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, i64, vp, vp, vp,
+                                   i32, f32, vp, i32, vp, vp, sz, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -281,6 +286,35 @@ def _index_topk(name, scale_group, q_codes, q_scales, w, k_codes, k_scales, q_se
     return _run(name, args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, _stream()), _bind)
 
 
+def csa2_segment_keys(n_slots: int, k: int) -> int:
+    return int(lib().csa2_segment_keys(n_slots, k))
+
+
+def _index_segments(name, scale_group, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k, cand_keys, _bind):
+    args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8, scale_group)
+    _need(cand_keys, torch.int64, 2, "cand_keys")
+    n_q = q_codes.shape[0]
+    if tuple(cand_keys.shape) != (n_q, csa2_segment_keys(n_slots, k)):
+        raise ValueError("index_segments: cand_keys must be [n_q, csa2_segment_keys(seq_cap, k)]")
+    return _run(name, args[:12] + (k, _p(cand_keys), _stream()), _bind)
+
+
+def csa2_index_segments(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, cand_keys,
+                        _bind: bool = False):
+    """The fused first Top-K level alone: the operands of csa2_index_score (no pool) ->
+    cand_keys [n_q, csa2_segment_keys(seq_cap, k)] (opaque 64-bit keys, held in an int64
+    tensor) for csa2_sparse_attn_topk."""
+    return _index_segments("csa2_index_segments", 32, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k,
+                           cand_keys, _bind)
+
+
+def csa2_index_segments_nvfp4(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, cand_keys,
+                              _bind: bool = False):
+    """csa2_index_segments for an NVFP4-style indexer (E4M3 scale per 16 channels)."""
+    return _index_segments("csa2_index_segments_nvfp4", 16, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k,
+                           cand_keys, _bind)
+
+
 def csa2_index_topk_pool_workspace_bytes(n_q: int, n_slots: int, k: int, block: int, max_blocks: int) -> int:
     return int(lib().csa2_index_topk_pool_workspace_bytes(n_q, n_slots, k, block, max_blocks))
 
@@ -359,6 +393,53 @@ def csa2_build_pool(scores, n_vis, max_vis: int, blocks_out, count_out, block: i
 
 def csa2_attn_workspace_bytes(n_q: int, n_heads: int, dim: int, k: int, window: int) -> int:
     return int(lib().csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window))
+
+
+def _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, n_q_rows):
+    _need(q, torch.bfloat16, 3, "q")
+    _need(kv_codes, torch.uint8, 3, "kv_codes")
+    _need(kv_scales, torch.uint8, 3, "kv_scales")
+    _need(q_seq, torch.int32, 1, "q_seq")
+    _need(swa, torch.uint8, 3, "swa")
+    _need(swa_base, torch.int64, 1, "swa_base")
+    _need(q_pos, torch.int64, 1, "q_pos")
+    _need(replay_start, torch.int64, 1, "replay_start")
+    n_q, H, D = q.shape
+    n_seq, seq_cap, _ = kv_codes.shape
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (n_q, H, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [n_q, H, D] f32/bf16 tensor")
+    if kv_codes.shape[2] != D // 2 or kv_scales.shape != (n_seq, seq_cap, D // 16) or swa.shape[0] != n_seq or \
+            swa.shape[2] != D or swa_base.shape[0] != n_seq or n_q_rows != n_q:
+        raise ValueError("sparse_attn: inconsistent shapes")
+    if lse is not None:
+        _need(lse, torch.float32, 2, "lse")
+        if tuple(lse.shape) != (n_q, H):
+            raise ValueError("lse shape")
+
+
+def csa2_sparse_attn_topk(q, kv_codes, kv_scales, q_seq, cand_keys, k: int, idx_out, count_out, swa, swa_base, q_pos,
+                          replay_start, window: int, sm_scale: float, out, lse=None, workspace=None,
+                          _bind: bool = False):
+    """csa2_sparse_attn with the index set selected in the call from csa2_index_segments'
+    cand_keys [n_q, n_cand]; writes it to idx_out [n_q, k] int32 and count_out [n_q] int32."""
+    _need(cand_keys, torch.int64, 2, "cand_keys")
+    _need(idx_out, torch.int32, 2, "idx_out")
+    _need(count_out, torch.int32, 1, "count_out")
+    _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, cand_keys.shape[0])
+    n_q, H, D = q.shape
+    n_seq, seq_cap, _ = kv_codes.shape
+    if tuple(idx_out.shape) != (n_q, k) or count_out.shape[0] != n_q:
+        raise ValueError("sparse_attn_topk: inconsistent index output shapes")
+    need = csa2_attn_workspace_bytes(n_q, H, D, k, window)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
+    return _run("csa2_sparse_attn_topk", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq),
+                                          _p(cand_keys), cand_keys.shape[1], k, _p(idx_out), _p(count_out), _p(swa),
+                                          swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), window,
+                                          ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes,
+                                          _stream()), _bind)
 
 
 def csa2_sparse_attn(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, replay_start, window: int,

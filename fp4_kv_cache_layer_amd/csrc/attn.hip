@@ -37,7 +37,7 @@
 // on the same XCD (dispatch is round-robin over the 8 XCDs) and share its L2 for the
 // gathered rows.  When a batch has too few queries to fill the GPU, the key list is split
 // over workgroups and a combine kernel merges the partial (O, m, l).
-#include "device.h"
+#include "select.h"
 
 namespace csa2 {
 
@@ -83,6 +83,12 @@ struct AttnArgs {
   float* ws_o;
   float* ws_ml;
   int nsplit, tiles_per_split, n_tiles, main_tiles, head_groups;
+  // csa2_sparse_attn_topk: the segment survivors of the first Top-K level ([n_q, cand_per_q]
+  // selection keys) and the index set the selection writes for later layers
+  const uint64_t* cand_keys;
+  int cand_per_q;
+  int32_t* idx_out;
+  int32_t* count_out;
 };
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -124,6 +130,18 @@ struct GatherSlot {
 
 // The per-query arrays come as restrict-qualified arguments of their own: nothing this
 // kernel writes can alias them, so their uniform loads go through the scalar cache.
+//
+// kSelect: the index list is not given but selected here, in every workgroup of the query,
+// from the survivors of the first Top-K level (csa2_index_segments): the same exact radix
+// select as the last level of csa2_index_topk (select.h), 512 threads x 16 keys, with the
+// histograms in the LDS of the V buffers (unused until the first tile), straight into the
+// staged index list.  Workgroup (head group 0, split 0) of the query also writes the list
+// and its count out for the layers that reuse it.
+constexpr int kSelEpt = 16;
+constexpr int kSelMax = kAttnThreads * kSelEpt;   // 8,192 survivor keys per query at most
+static_assert(2 * (kAttnThreads / 64) * 256 * kTkCopies * 4 <= 2 * kPairs * 2 * kVBuf, "selection histograms");
+
+template <bool kSelect>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int32_t* __restrict__ q_seq,
                                                            const int64_t* __restrict__ q_pos,
                                                            const int64_t* __restrict__ replay_start,
@@ -172,7 +190,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   constexpr int kIdxPer = CSA2_MAX_TOPK / kAttnThreads;
   const int n_keys = n_main * kT;
   int32_t iv[kIdxPer];
-  if (n_keys > 0) {  // uniform; idx may be absent when k == 0
+  uint64_t key[kSelEpt];
+  if (kSelect) {  // candidate i*512 + tid of the query's survivors (cand_per_q >= 1)
+    const uint64_t* kp = a.cand_keys + (int64_t)q * a.cand_per_q;
+    const int lim = a.cand_per_q;
+#pragma unroll
+    for (int i = 0; i < kSelEpt; ++i) {
+      const int o = i * kAttnThreads + tid;
+      key[i] = kp[o < lim ? o : lim - 1] & (0ull - (uint64_t)(o < lim));
+    }
+  } else if (n_keys > 0) {  // uniform; idx may be absent when k == 0
 #pragma unroll
     for (int r = 0; r < kIdxPer; ++r) {
       int i = tid + r * kAttnThreads;
@@ -229,7 +256,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     const bool is_main = tile < a.main_tiles;  // wave-uniform
     int si = (tile - tile_lo) * kT + col;
     si = si < 0 ? 0 : (si >= n_main * kT ? (n_main > 0 ? n_main * kT - 1 : 0) : si);
-    const int32_t p = s_idx[si];
+    // with kSelect s_idx holds the whole list (k entries, -1 padded), and a main tile's
+    // slots from k on (the last tile when k is not a multiple of 16) are empty; otherwise
+    // s_idx is this split's slice
+    const int slot = tile_lo * kT + si;
+    const int32_t pv = s_idx[kSelect ? (slot < a.k ? slot : a.k - 1) : si];
+    const int32_t p = (kSelect && slot >= a.k) ? -1 : pv;
     const bool ok_main = real && is_main && seq_ok && p >= 0 && p < a.seq_cap;
     const uint32_t pm = ok_main ? (uint32_t)p : 0u;
     const int j = (tile - a.main_tiles) * kT + col;
@@ -259,7 +291,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     load_slot(my_tile(1), 1 < n_my, g1);
   }
 
-  if (n_keys > 0) {
+  if constexpr (kSelect) {
+    // the whole index list, s_idx[0 .. k), ascending; the tiles index it from tile_lo * 16
+    __shared__ int32_t s_count;
+    select_block<kAttnThreads, kSelEpt, true>(key, a.k, reinterpret_cast<uint32_t*>(lds), nullptr, s_idx, &s_count);
+    __syncthreads();
+    if (hg == 0 && split == 0) {
+      for (int i = tid; i < a.k; i += kAttnThreads) a.idx_out[(int64_t)q * a.k + i] = s_idx[i];
+      if (tid == 0) a.count_out[q] = s_count;
+    }
+  } else if (n_keys > 0) {
 #pragma unroll
     for (int r = 0; r < kIdxPer; ++r) {
       const int i = tid + r * kAttnThreads;
@@ -621,19 +662,21 @@ extern "C" size_t csa2_attn_workspace_bytes(int n_q, int n_heads, int dim, int k
   return (size_t)p.nsplit * n_q * n_heads * (kD + 2) * sizeof(float) + 256;
 }
 
-extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
-                                const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
-                                const int32_t* idx, int k, const uint8_t* swa, int64_t swa_cap,
-                                const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
-                                int window, float sm_scale, void* out, int out_dtype, float* lse, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                       int64_t seq_cap, int n_seq, const int32_t* q_seq, const int32_t* idx, const uint64_t* cand_keys,
+                       int cand_per_q, int32_t* idx_out, int32_t* count_out, int k, const uint8_t* swa,
+                       int64_t swa_cap, const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
+                       int window, float sm_scale, void* out, int out_dtype, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (!q || !kv_codes || !kv_scales || !q_seq || !swa || !swa_base || !q_pos || !replay_start || !out)
     return CSA2_ERR_NULL;
-  if (k > 0 && !idx) return CSA2_ERR_NULL;
+  const bool select = cand_keys != nullptr;
+  if (!select && k > 0 && !idx) return CSA2_ERR_NULL;
   if (n_q < 0 || n_heads < kHG || n_heads > 256 || n_heads % kHG || dim != kD || seq_cap < 0 ||
       seq_cap > CSA2_MAX_ATTN_ENTRIES || n_seq < 1 || k < 0 || k > CSA2_MAX_TOPK || window < 1 ||
       window > CSA2_MAX_WINDOW || swa_cap < window || swa_cap > CSA2_MAX_WINDOW_ROWS)
     return CSA2_ERR_SHAPE;
+  if (select && (k < 1 || cand_per_q < 1 || cand_per_q > kSelMax)) return CSA2_ERR_SHAPE;
   if (out_dtype != CSA2_DT_F32 && out_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(kv_codes) || !aligned16(swa) || !aligned16(out) || ((uintptr_t)kv_scales & 7))
     return CSA2_ERR_SHAPE;
@@ -666,6 +709,10 @@ extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, co
   a.n_tiles = p.n_tiles;
   a.main_tiles = p.main_tiles;
   a.head_groups = p.head_groups;
+  a.cand_keys = cand_keys;
+  a.cand_per_q = cand_per_q;
+  a.idx_out = idx_out;
+  a.count_out = count_out;
   if (p.nsplit > 1) {
     size_t need = csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window);
     if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
@@ -674,10 +721,38 @@ extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, co
     a.ws_ml = a.ws_o + (size_t)p.nsplit * n_q * n_heads * kD;
   }
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(k_attn, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos, a.replay_start,
-                     a.swa_base);
+  if (select)
+    hipLaunchKernelGGL(k_attn<true>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
+                       a.replay_start, a.swa_base);
+  else
+    hipLaunchKernelGGL(k_attn<false>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
+                       a.replay_start, a.swa_base);
   int rc = csa2_check_launch();
   if (rc != CSA2_OK || p.nsplit == 1) return rc;
   hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(n_q * n_heads)), dim3(kCombThreads), 0, st, a);
   return csa2_check_launch();
+}
+
+extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
+                                const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                                const int32_t* idx, int k, const uint8_t* swa, int64_t swa_cap,
+                                const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
+                                int window, float sm_scale, void* out, int out_dtype, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, idx, nullptr, 0, nullptr,
+                     nullptr, k, swa, swa_cap, swa_base, q_pos, replay_start, window, sm_scale, out, out_dtype, lse,
+                     workspace, workspace_bytes, stream);
+}
+
+extern "C" int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
+                                     const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                                     const uint64_t* cand_keys, int cand_per_q, int k, int32_t* idx_out,
+                                     int32_t* count_out, const uint8_t* swa, int64_t swa_cap,
+                                     const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
+                                     int window, float sm_scale, void* out, int out_dtype, float* lse,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cand_keys || !idx_out || !count_out) return CSA2_ERR_NULL;
+  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, nullptr, cand_keys, cand_per_q,
+                     idx_out, count_out, k, swa, swa_cap, swa_base, q_pos, replay_start, window, sm_scale, out,
+                     out_dtype, lse, workspace, workspace_bytes, stream);
 }

@@ -715,6 +715,54 @@ static size_t index_topk_pool_ws(int n_q, int64_t n_slots, int k, int block, int
   return 256 + *bmax_bytes + *sel_bytes + ws_bytes(n_q, nblk, max_blocks) + 256;
 }
 
+// ---- csa2_index_segments: the fused first level alone; the last one runs in the
+// attention kernel (csa2_sparse_attn_topk) ----
+extern "C" int64_t csa2_segment_keys(int64_t n_slots, int k) {
+  if (n_slots < 0 || k < 1 || k > CSA2_MAX_TOPK) return 0;
+  const int64_t n_seg = n_slots > 0 ? (n_slots + kTkSeg - 1) / kTkSeg : 1;
+  return n_seg * k;
+}
+
+static int index_segments(bool nv, const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                          int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap,
+                          int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k, uint64_t* cand_keys,
+                          void* stream) {
+  int64_t n_slots = 0;
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                            nullptr, nullptr, 8, 1, &n_slots);
+  if (rc == CSA2_OK && nv) rc = check_nv_scales(q_scales, k_scales);
+  if (rc != CSA2_OK) return rc;
+  if (!cand_keys) return CSA2_ERR_NULL;
+  if (n_q > 65535 || k < 1 || k > CSA2_MAX_TOPK || n_slots > 0x7fffffffLL) return CSA2_ERR_SHAPE;
+  if (n_q == 0) return CSA2_OK;
+  const int64_t n_seg = csa2_segment_keys(n_slots, k) / k;
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, nullptr,
+                          nullptr, 8, 1, n_slots);
+  a.k = k;
+  a.keys_out = cand_keys;
+  dim3 grid((unsigned)n_seg, (unsigned)n_q), blk(kScoreThreads);
+  hipStream_t st = (hipStream_t)stream;
+  if (nv) hipLaunchKernelGGL((k_score_select<false, false, false, true>), grid, blk, 0, st, a);
+  else hipLaunchKernelGGL((k_score_select<false, false, false, false>), grid, blk, 0, st, a);
+  return csa2_check_launch();
+}
+
+extern "C" int csa2_index_segments(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                                   int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                                   int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k,
+                                   uint64_t* cand_keys, void* stream) {
+  return index_segments(false, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq,
+                        n_vis, k, cand_keys, stream);
+}
+
+extern "C" int csa2_index_segments_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                                         int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                                         int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                                         int k, uint64_t* cand_keys, void* stream) {
+  return index_segments(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq,
+                        n_vis, k, cand_keys, stream);
+}
+
 extern "C" size_t csa2_index_topk_pool_workspace_bytes(int n_q, int64_t n_slots, int k, int block, int max_blocks) {
   if (n_q <= 0 || n_slots <= 0 || k < 1 || k > CSA2_MAX_TOPK || block < 1 || block > 64 || (block & (block - 1)) ||
       max_blocks < 1 || max_blocks > CSA2_MAX_TOPK)

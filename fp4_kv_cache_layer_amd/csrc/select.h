@@ -70,31 +70,34 @@ __device__ __forceinline__ uint32_t dpp_prefix_sum(uint32_t v) {
 }
 
 
-// Selects the K largest of the 32*256 keys held by a 256-thread workgroup (key[i] of thread
-// t is candidate i*256 + t of the segment; 0 = no candidate) and writes them in candidate
-// order: non-final levels write the keys to keys_out[(q*n_seg + seg)*K ..], zero padded;
-// the final level writes positions to idx_out[q*K ..], -1 padded, and count_out[q].
-// `hist` is kTkHistWords words of 16-byte aligned LDS; the caller may have used them for anything before
-// the call (the first write to them follows the call's first barrier).  Each wave counts
-// into kTkCopies interleaved copies of its 256 bins (word bin*kTkCopies + lane%kTkCopies),
-// so lanes that hit the same bin land on different LDS banks: the digits of a segment's
-// best keys bunch into few bins, and same-address atomics would serialise.
+// Selects the K largest of the kEpt*kThreads keys held by a kThreads-thread workgroup (key[i]
+// of thread t is candidate i*kThreads + t of the block; 0 = no candidate) and writes them
+// in candidate order: non-final levels write the keys to keys_out[0 .. K), zero padded;
+// the final level writes positions to idx_out[0 .. K), -1 padded, and *count_out (either
+// may point to LDS).  `hist` is 2 * (kThreads / 64) * 256 * kTkCopies words of 16-byte
+// aligned LDS; the caller may have used them for anything before the call (the first write
+// to them follows the call's first barrier).  Each wave counts into kTkCopies interleaved
+// copies of its 256 bins (word bin*kTkCopies + lane%kTkCopies), so lanes that hit the same
+// bin land on different LDS banks: the digits of a segment's best keys bunch into few bins,
+// and same-address atomics would serialise.
 constexpr int kTkCopies = 4;
 constexpr int kTkHistWords = 2 * kTkWaves * 256 * kTkCopies;
 
-template <bool kFinal>
-__device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, int seg, int n_seg, int K,
-                                               uint32_t* hist, uint64_t* __restrict__ keys_out,
-                                               int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out) {
+template <int kThreads, int kEpt, bool kFinal>
+__device__ __forceinline__ void select_block(uint64_t (&key)[kEpt], int K, uint32_t* hist,
+                                             uint64_t* __restrict__ keys_out, int32_t* __restrict__ idx_out,
+                                             int32_t* __restrict__ count_out) {
+  constexpr int kWaves = kThreads / 64;
+  static_assert(kEpt <= 64 && kThreads % 64 == 0, "one lane per slot in the compaction scan");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  __shared__ uint32_t cnt[kTkWaves][kTkEpt];
-  __shared__ uint32_t red[5][kTkWaves];
+  __shared__ uint32_t cnt[kWaves][kEpt];
+  __shared__ uint32_t red[5][kWaves];
 
   // ---- count (ballots) and the range of the high (score) words (DPP reductions) ----
   uint32_t nw = 0, hmax = 0u, hmin = ~0u, lmax = 0u, lmin = ~0u;
 #pragma unroll
-  for (int i = 0; i < kTkEpt; ++i) {
+  for (int i = 0; i < kEpt; ++i) {
     nw += (uint32_t)__popcll(__ballot(key[i] != 0ull));
     const uint32_t h = (uint32_t)(key[i] >> 32), l = (uint32_t)key[i];
     hmax = key[i] ? max(hmax, h) : hmax;
@@ -118,7 +121,7 @@ __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, i
   hmax = 0u;
   hmin = ~0u;
 #pragma unroll
-  for (int wv = 0; wv < kTkWaves; ++wv) {
+  for (int wv = 0; wv < kWaves; ++wv) {
     n += red[0][wv];
     hmax = max(hmax, red[1][wv]);
     hmin = min(hmin, red[2][wv]);
@@ -136,7 +139,7 @@ __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, i
       lmax = 0u;
       lmin = ~0u;
 #pragma unroll
-      for (int wv = 0; wv < kTkWaves; ++wv) {
+      for (int wv = 0; wv < kWaves; ++wv) {
         lmax = max(lmax, red[3][wv]);
         lmin = min(lmin, red[4][wv]);
       }
@@ -148,20 +151,20 @@ __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, i
     int shift = hb - 7 > 0 ? hb - 7 : 0;
     uint32_t need = (uint32_t)K;
     for (int pass = 0;; ++pass) {
-      uint32_t* h = hist + ((pass & 1) * kTkWaves + wave) * 256 * kTkCopies;
+      uint32_t* h = hist + ((pass & 1) * kWaves + wave) * 256 * kTkCopies;
 #pragma unroll
       for (int i = 0; i < kTkCopies; ++i)
         reinterpret_cast<uint4*>(h)[lane + 64 * i] = make_uint4(0u, 0u, 0u, 0u);
       uint32_t* hc = h + (lane & (kTkCopies - 1));
 #pragma unroll
-      for (int i = 0; i < kTkEpt; ++i)
+      for (int i = 0; i < kEpt; ++i)
         if (key[i] && (key[i] & mask) == prefix) atomicAdd(&hc[((uint32_t)(key[i] >> shift) & 255u) * kTkCopies], 1u);
       __syncthreads();
       // every wave: lane l owns bins 4l..4l+3 of the histogram summed over waves and copies
       uint32_t hs[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int wv = 0; wv < kTkWaves; ++wv) {
-        const uint4* hw = reinterpret_cast<const uint4*>(hist + ((pass & 1) * kTkWaves + wv) * 256 * kTkCopies);
+      for (int wv = 0; wv < kWaves; ++wv) {
+        const uint4* hw = reinterpret_cast<const uint4*>(hist + ((pass & 1) * kWaves + wv) * 256 * kTkCopies);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint4 c = hw[4 * lane + j];
@@ -203,49 +206,61 @@ __device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, i
   // ---- stable compaction in candidate order (i-major, then thread) ----
   // survivors of slot i in wave w: one ballot; cnt[w][i] = their number
 #pragma unroll
-  for (int i = 0; i < kTkEpt; ++i) {
+  for (int i = 0; i < kEpt; ++i) {
     const uint64_t m = __ballot(key[i] && (key[i] & mask) >= prefix);
     if (lane == 0) cnt[wave][i] = (uint32_t)__popcll(m);
   }
   __syncthreads();
   // lane i < 32: off = (survivors of slots < i, all waves) + (survivors of slot i, waves < w)
   uint32_t tot_i = 0, before_w = 0;
-  if (lane < kTkEpt) {
+  if (lane < kEpt) {
 #pragma unroll
-    for (int wv = 0; wv < kTkWaves; ++wv) {
+    for (int wv = 0; wv < kWaves; ++wv) {
       const uint32_t c = cnt[wv][lane];
       tot_i += c;
       before_w += wv < wave ? c : 0u;
     }
   }
   const uint32_t excl = dpp_prefix_sum(tot_i);   // inclusive over slots (lanes 0..31; the rest hold 0)
-  const uint32_t total = __builtin_amdgcn_readlane(excl, kTkEpt - 1);
+  const uint32_t total = __builtin_amdgcn_readlane(excl, kEpt - 1);
   const uint32_t off = excl - tot_i + before_w;
   const uint32_t nsel = total < (uint32_t)K ? total : (uint32_t)K;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   if (!kFinal) {
-    uint64_t* out = keys_out + ((int64_t)q * n_seg + seg) * K;
+    uint64_t* out = keys_out;
 #pragma unroll
-    for (int i = 0; i < kTkEpt; ++i) {
+    for (int i = 0; i < kEpt; ++i) {
       const bool take = key[i] && (key[i] & mask) >= prefix;
       const uint64_t m = __ballot(take);
       const uint32_t slot = __builtin_amdgcn_readlane(off, i) + (uint32_t)__popcll(m & lt_mask);
       if (take && slot < (uint32_t)K) out[slot] = key[i];
     }
-    for (int i = (int)nsel + tid; i < K; i += kTkThreads) out[i] = 0ull;
+    for (int i = (int)nsel + tid; i < K; i += kThreads) out[i] = 0ull;
     return;
   }
-  int32_t* out = idx_out + (int64_t)q * K;
+  int32_t* out = idx_out;
 #pragma unroll
-  for (int i = 0; i < kTkEpt; ++i) {
+  for (int i = 0; i < kEpt; ++i) {
     const bool take = key[i] && (key[i] & mask) >= prefix;
     const uint64_t m = __ballot(take);
     const uint32_t slot = __builtin_amdgcn_readlane(off, i) + (uint32_t)__popcll(m & lt_mask);
     if (take && slot < (uint32_t)K) out[slot] = key_pos(key[i]);
   }
-  for (int i = (int)nsel + tid; i < K; i += kTkThreads) out[i] = -1;
-  if (tid == 0) count_out[q] = (int32_t)nsel;
+  for (int i = (int)nsel + tid; i < K; i += kThreads) out[i] = -1;
+  if (tid == 0) *count_out = (int32_t)nsel;
+}
+
+
+// The 256-thread, 32-keys-per-thread segment of the Top-K levels: segment seg of query q
+// writes keys_out[(q*n_seg + seg)*K ..] (non-final) or idx_out[q*K ..] and count_out[q].
+template <bool kFinal>
+__device__ __forceinline__ void select_segment(uint64_t (&key)[kTkEpt], int q, int seg, int n_seg, int K,
+                                               uint32_t* hist, uint64_t* __restrict__ keys_out,
+                                               int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out) {
+  select_block<kTkThreads, kTkEpt, kFinal>(
+      key, K, hist, kFinal ? nullptr : keys_out + ((int64_t)q * n_seg + seg) * K,
+      kFinal ? idx_out + (int64_t)q * K : nullptr, kFinal ? count_out + q : nullptr);
 }
 
 // number of segments per level, level 0 first; the last entry is 1

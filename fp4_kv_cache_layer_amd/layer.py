@@ -30,7 +30,8 @@ MODES = ("full", "full_pool", "reuse", "reindex", "reindex_pool")
 INDEX_FORMATS = {"mxfp4": (C.FMT_MXFP4, 32), "nvfp4": (C.FMT_NVFP4, 16)}
 
 
-def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp4") -> list:
+def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp4",
+               attn_select: bool = False) -> list:
     """Checks a layer group's mode sequence and returns the calls each layer makes.
 
     [W] "CSA2：跨层复用，能借就不自己算" and Figure 4: a Reindex layer re-scores the KV of the
@@ -41,7 +42,12 @@ def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp
     rows of one sequence, and the layers that score all visible entries read each group's
     indexer K once (csa2_index_score_grouped, then csa2_topk).  index_fmt "nvfp4": the
     fused pool build and grouped scoring exist for MXFP4 only, so the pool-building layer
-    scores, selects and builds the pool in separate calls, and group must be 1."""
+    scores, selects and builds the pool in separate calls, and group must be 1.
+    attn_select (fused, group 1, and a cache whose segment survivors fit one selection,
+    i.e. up to 131,072 entries at k = 512): Full and Reindex layers without a pool keep
+    only the first Top-K level in the scoring call (csa2_index_segments) and finish the
+    selection inside their attention call (csa2_sparse_attn_topk), which also writes the
+    index set for the Reuse layers."""
     if index_fmt not in INDEX_FORMATS:
         raise ValueError(f"unknown indexer format {index_fmt!r}")
     if index_fmt != "mxfp4" and group > 1:
@@ -63,6 +69,8 @@ def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp
                      ["quantize_index_q", "score", "select", "build_pool", "attend"])
         elif group > 1 and m in ("full", "reindex"):
             calls = ["quantize_index_q", "score_grouped", "select", "attend"]
+        elif attn_select and fused and m in ("full", "reindex"):
+            calls = ["quantize_index_q", "index_segments", "attend_topk"]
         elif fused:
             calls = ["quantize_index_q", "index_topk_in_pool" if m == "reindex_pool" else "index_topk", "attend"]
         else:
@@ -104,13 +112,19 @@ class Csa2Step:
     def __init__(self, n_q: int, n_heads: int, idx_heads: int, seq_cap: int, k: int = 512, window: int = 128,
                  block: int = 8, max_blocks: int = 2048, idx_dim: int = 128, dim: int = 512,
                  out_dtype=torch.float32, fused: bool = True, group: int = 1, index_fmt: str = "mxfp4",
-                 device="cuda"):
+                 attn_select: bool = False, device="cuda"):
         """fused: score and select in one call (csa2_index_topk) wherever the layer does not
         need the score array itself (it does only when it builds the pool).  group: query
         rows come in groups of `group` consecutive rows of one sequence (several tokens of a
         sequence at once); layers scoring all visible entries then read each group's indexer
-        K once.  index_fmt: the indexer Q/K format ("mxfp4" or "nvfp4", see INDEX_FORMATS)."""
+        K once.  index_fmt: the indexer Q/K format ("mxfp4" or "nvfp4", see INDEX_FORMATS).
+        attn_select: finish the Top-K inside the attention call where plan_group allows it
+        (a variant: measured slower than the separate last selection level, see
+        csa2_sparse_attn_topk)."""
         plan_group(["full"], fused, group, index_fmt)   # validates the combination
+        n_cand = C.csa2_segment_keys(seq_cap, k)
+        fits = fused and group == 1 and 1 <= n_cand <= 8192
+        self.attn_select = bool(attn_select) and fits
         self.index_fmt = index_fmt
         self.idx_qfmt, self.idx_group = INDEX_FORMATS[index_fmt]
         self.n_q, self.n_heads, self.idx_heads = n_q, n_heads, idx_heads
@@ -139,6 +153,7 @@ class Csa2Step:
                                    dtype=torch.uint8, **dev)
         self.ws_attn = torch.empty(max(C.csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window), 1),
                                    dtype=torch.uint8, **dev)
+        self.cand_keys = torch.empty(n_q, max(n_cand, 1), dtype=torch.int64, **dev)
         self.sm_scale = 1.0 / math.sqrt(dim)
 
     # ---- steps ----
@@ -186,6 +201,21 @@ class Csa2Step:
                                       n_vis, self.k, self.idx, self.count, self.pool, self.pool_count, self.block,
                                       self.ws_index_topk_pool, _bind=bind)
 
+    def index_segments(self, caches: Caches, w, q_seq, n_vis, bind=False):
+        """the first Top-K level alone (its survivors feed attend_topk)."""
+        fn = C.csa2_index_segments_nvfp4 if self.index_fmt == "nvfp4" else C.csa2_index_segments
+        return fn(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.k,
+                  self.cand_keys, _bind=bind)
+
+    def attend_topk(self, caches: Caches, layer: int, q_attn, q_seq, q_pos, replay_start, out=None, lse=None,
+                    bind=False):
+        """attention that first selects the Top-K from index_segments' survivors and writes it
+        to the step's index set."""
+        return C.csa2_sparse_attn_topk(q_attn, caches.kv_codes, caches.kv_scales, q_seq, self.cand_keys, self.k,
+                                       self.idx, self.count, caches.swa[layer], caches.swa_base, q_pos, replay_start,
+                                       self.window, self.sm_scale, self.out if out is None else out,
+                                       self.lse if lse is None else lse, self.ws_attn, _bind=bind)
+
     def _score_select(self, caches, w, q_seq, n_vis, in_pool, bind):
         if self.fused:
             return [self.index_topk(caches, w, q_seq, n_vis, in_pool, bind)]
@@ -209,7 +239,7 @@ class Csa2Step:
         with its own window cache caches.swa[i].  outs/lses: optional per-layer outputs
         (default: the step's own buffers, overwritten by each layer).  With bind=True returns
         the group's calls as one flat list of callables."""
-        plan = plan_group(modes, self.fused, self.group, self.index_fmt)
+        plan = plan_group(modes, self.fused, self.group, self.index_fmt, self.attn_select)
         calls = []
         for i, (m, names) in enumerate(zip(modes, plan)):
             q_index, w, q_attn = inputs[i]
@@ -230,6 +260,10 @@ class Csa2Step:
                     c = self.select(n_vis, name.endswith("pool"), bind)
                 elif name == "build_pool":
                     c = self.build_pool(n_vis, bind)
+                elif name == "index_segments":
+                    c = self.index_segments(caches, w, q_seq, n_vis, bind)
+                elif name == "attend_topk":
+                    c = self.attend_topk(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind)
                 else:
                     c = self.attend(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind)
                 calls.append(c)
@@ -248,6 +282,10 @@ class Csa2Step:
         elif make_pool:
             calls += [self.score(caches, w, q_seq, n_vis, bind=bind), self.select(n_vis, bind=bind),
                       self.build_pool(n_vis, bind)]
+        elif self.attn_select:
+            calls += [self.index_segments(caches, w, q_seq, n_vis, bind),
+                      self.attend_topk(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
+            return self._seq(calls, bind)
         else:
             calls += self._score_select(caches, w, q_seq, n_vis, False, bind)
         calls.append(self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind))
@@ -255,6 +293,10 @@ class Csa2Step:
 
     def reindex(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, in_pool=False,
                 out=None, lse=None, bind=False):
+        if self.attn_select and not in_pool:
+            calls = [self.quantize_index_q(q_index_f32, bind), self.index_segments(caches, w, q_seq, n_vis, bind),
+                     self.attend_topk(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
+            return self._seq(calls, bind)
         calls = [self.quantize_index_q(q_index_f32, bind), *self._score_select(caches, w, q_seq, n_vis, in_pool, bind),
                  self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
         return self._seq(calls, bind)

@@ -233,7 +233,30 @@ int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float
 size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_pool);
 
 /*
- * csa2_index_score_nvfp4 / csa2_index_topk_nvfp4 -- csa2_index_score / csa2_index_topk for
+ * csa2_index_segments -- the first half of csa2_index_topk without a pool: scores every
+ * visible entry (as csa2_index_score) and keeps, for every run of 8,192 consecutive
+ * positions of a query's sequence, the k best of them (score descending, position
+ * ascending), as selection keys that csa2_sparse_attn_topk turns into the query's Top-k.
+ * [W] "CSA2：跨层复用，能借就不自己算" (indexer scores, then Top-K): the Top-k of a query is
+ * the Top-k of the union of its runs' Top-k, so nothing is lost.
+ *
+ * Arguments up to n_vis are those of csa2_index_score; k in 1..2048; n_q <= 65535.
+ *   cand_keys  [n_q, csa2_segment_keys(seq_cap, k)] uint64, caller-owned device memory,
+ *              fully overwritten: per run its k keys in position order, then zeros.  The
+ *              keys are opaque (0 = no candidate): only csa2_sparse_attn_topk reads them.
+ * csa2_segment_keys(n_slots, k) = ceil(n_slots / 8192) * k (at least k; 0 for a bad k).
+ * Errors: those of csa2_index_score (except the score array's), CSA2_ERR_NULL (cand_keys),
+ * CSA2_ERR_SHAPE (k, n_q).
+ */
+int csa2_index_segments(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                        int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                        int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                        int k, uint64_t* cand_keys, void* stream);
+int64_t csa2_segment_keys(int64_t n_slots, int k);
+
+/*
+ * csa2_index_score_nvfp4 / csa2_index_topk_nvfp4 / csa2_index_segments_nvfp4 --
+ * csa2_index_score / csa2_index_topk / csa2_index_segments for
  * an indexer kept in the main KV's NVFP4-style format instead of MXFP4: E2M1 codes with one
  * E4M3 scale per 16 channels, as CSA2_FMT_NVFP4 of csa2_quantize_kv writes them.
  * [W] "FP4 与 SWA Bounded Replay" (indexer Q/K in FP4, main KV in E2M1 + E4M3 per 16; the
@@ -242,8 +265,8 @@ size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_p
  *   score(q, j) = sum_h w[q,h] * max(0, sum_c Q[q,h,c] K[seq(q), j, c])
  * with Q and K the exact NVFP4 values; products are exact, sums are fp32.
  *
- * Arguments, layouts, outputs, workspace and errors are those of csa2_index_score and
- * csa2_index_topk, except:
+ * Arguments, layouts, outputs, workspace and errors are those of csa2_index_score,
+ * csa2_index_topk and csa2_index_segments, except:
  *   q_scales   [n_q, n_heads, dim/16] E4M3 (8 per head row)
  *   k_scales   [n_seq, seq_cap, dim/16] E4M3 (8 per entry); both scale arrays 2-byte
  *              aligned (CSA2_ERR_SHAPE otherwise)
@@ -260,6 +283,10 @@ int csa2_index_topk_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const
                           const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
                           int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
                           void* workspace, size_t workspace_bytes, void* stream);
+int csa2_index_segments_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                              int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                              int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                              int k, uint64_t* cand_keys, void* stream);
 
 /*
  * csa2_index_topk_pool -- the decoder's first Full layer in one pass over the indexer-K
@@ -364,6 +391,32 @@ int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t
                      int window, float sm_scale, void* out, int out_dtype, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream);
 size_t csa2_attn_workspace_bytes(int n_q, int n_heads, int dim, int k, int window);
+
+/*
+ * csa2_sparse_attn_topk -- csa2_sparse_attn whose index set is selected in the same call
+ * from csa2_index_segments' keys: the Top-k of the keys (score descending, position
+ * ascending), as ascending positions, -1 padded -- exactly what csa2_index_topk returns for
+ * the same scoring arguments -- is written to idx_out / count_out (for the Reuse layers
+ * that borrow it) and attended over.  [W] "CSA2：跨层复用，能借就不自己算".
+ *
+ * Arguments are those of csa2_sparse_attn, with idx replaced by
+ *   cand_keys   [n_q, cand_per_q] uint64 from csa2_index_segments, cand_per_q =
+ *               csa2_segment_keys(seq_cap, k) in 1..8192 (seq_cap up to 131,072 at k = 512)
+ *   k           1..2048, the Top-k size given to csa2_index_segments
+ *   idx_out     [n_q, k] int32, count_out [n_q] int32 (caller-owned, overwritten)
+ * Every workgroup of a query runs the selection itself (the histograms use the LDS of the
+ * attention's V buffers before the first tile), so the index set needs no launch of its
+ * own and no memory round trip before the gathers.
+ * Errors: those of csa2_sparse_attn; CSA2_ERR_NULL (cand_keys, idx_out, count_out);
+ * CSA2_ERR_SHAPE (cand_per_q, k).
+ */
+int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
+                          const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                          const uint64_t* cand_keys, int cand_per_q, int k, int32_t* idx_out,
+                          int32_t* count_out, const uint8_t* swa, int64_t swa_cap,
+                          const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
+                          int window, float sm_scale, void* out, int out_dtype, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

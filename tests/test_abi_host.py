@@ -77,3 +77,36 @@ def test_validation_before_launch(L):
     a = list(args); a[9] = None                     # idx NULL with k > 0
     assert L.csa2_sparse_attn(*a) == -1
     assert L.csa2_sparse_attn(*args) == -5          # split over workgroups needs a workspace
+
+
+def test_select_in_attention_validation(L):
+    """csa2_index_segments / csa2_sparse_attn_topk reject bad calls on the host."""
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    fake = vp(0x1000)   # never dereferenced
+    L.csa2_segment_keys.restype = i64
+    L.csa2_segment_keys.argtypes = [i64, i32]
+    assert L.csa2_segment_keys(131072, 512) == 8192
+    assert L.csa2_segment_keys(131073, 512) == 8704
+    assert L.csa2_segment_keys(0, 512) == 512
+    assert L.csa2_segment_keys(100, 0) == 0
+    L.csa2_index_segments.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp]
+    seg = [fake, fake, fake, 4, 16, 128, fake, fake, 4096, 1, fake, fake, 512, fake, None]
+    a = list(seg); a[13] = None                     # no key buffer
+    assert L.csa2_index_segments(*a) == -1
+    a = list(seg); a[12] = 4096                     # k > 2048
+    assert L.csa2_index_segments(*a) == -2
+    a = list(seg); a[5] = 64                        # indexer dim
+    assert L.csa2_index_segments(*a) == -2
+    L.csa2_sparse_attn_topk.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, i64, vp,
+                                        vp, vp, i32, ctypes.c_float, vp, i32, vp, vp, ctypes.c_size_t, vp]
+    att = [fake, 4, 64, 512, fake, fake, 100, 1, fake, fake, 8192, 512, fake, fake, fake, 128, fake, fake, fake, 128,
+           0.05, fake, 0, None, None, 0, None]
+    a = list(att); a[9] = None                      # no candidate keys
+    assert L.csa2_sparse_attn_topk(*a) == -1
+    a = list(att); a[12] = None                     # no index output
+    assert L.csa2_sparse_attn_topk(*a) == -1
+    a = list(att); a[10] = 8193                     # more survivors than one selection holds
+    assert L.csa2_sparse_attn_topk(*a) == -2
+    a = list(att); a[11] = 0                        # k = 0
+    assert L.csa2_sparse_attn_topk(*a) == -2
+    assert L.csa2_sparse_attn_topk(*att) == -5      # split over workgroups needs a workspace

@@ -298,6 +298,44 @@ def test_index_topk_fused(C, k, fmt):
         G.topk_accept(gi[qi], int(gc[qi]), pos, ref, k)
 
 
+@pytest.mark.parametrize("k,fmt", [(512, "mxfp4"), (7, "mxfp4"), (1500, "mxfp4"), (512, "nvfp4")])
+def test_segments_then_attention_topk(C, k, fmt):
+    """csa2_index_segments + csa2_sparse_attn_topk (the last Top-K level inside the attention
+    call) give the index set of csa2_index_topk bit for bit, and attention outputs identical
+    to csa2_sparse_attn over that set; repeated calls change nothing.  7 queries of 16 heads
+    split their key lists over 10 workgroups, each of which selects."""
+    _say("segments + attention topk", k, fmt)
+    n_vis = [40000, 8193, 1, 0, 511, 20001, 16384]
+    case = _score_case(50 + k, 3, 40000, n_vis, 16, fmt)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_idx, w, qa = case.gpu_query_inputs(0)
+    q_seq, n_vis_t, q_pos, rs = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, k=k, index_fmt=fmt, attn_select=True)
+    assert st.attn_select
+    st.quantize_index_q(q_idx)
+    (gi, gc), _ = _run_index_topk(C, st, caches, w, q_seq, n_vis_t, k)
+    sm = 1.0 / math.sqrt(512)
+    out_a = torch.empty(wl.n_q, 16, 512, dtype=torch.float32, device="cuda")
+    lse_a = torch.empty(wl.n_q, 16, dtype=torch.float32, device="cuda")
+    C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, torch.from_numpy(gi).cuda(), caches.swa[0],
+                       caches.swa_base, q_pos, rs, 128, sm, out_a, lse_a)
+    seg_fn = C.csa2_index_segments_nvfp4 if fmt == "nvfp4" else C.csa2_index_segments
+    for rep in range(2):
+        keys = torch.full((wl.n_q, C.csa2_segment_keys(wl.seq_cap, k)), 5, dtype=torch.int64, device="cuda")
+        seg_fn(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis_t, k, keys)
+        idx_b = torch.full((wl.n_q, k), 77, dtype=torch.int32, device="cuda")
+        cnt_b = torch.full((wl.n_q,), 77, dtype=torch.int32, device="cuda")
+        out_b = torch.empty_like(out_a)
+        lse_b = torch.empty_like(lse_a)
+        C.csa2_sparse_attn_topk(qa, caches.kv_codes, caches.kv_scales, q_seq, keys, k, idx_b, cnt_b, caches.swa[0],
+                                caches.swa_base, q_pos, rs, 128, sm, out_b, lse_b)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx_b.cpu().numpy(), gi) and np.array_equal(cnt_b.cpu().numpy(), gc), rep
+        assert torch.equal(out_b, out_a) and torch.equal(lse_b, lse_a), rep
+
+
 def test_index_topk_repeated_calls_share_workspace(C):
     """Back-to-back calls on one workspace, with pool calls (which lay the workspace out
     differently) in between, give identical results."""

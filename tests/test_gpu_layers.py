@@ -27,15 +27,20 @@ def C():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,samples", [("c3", (0, 13, 31)), ("c4", (0, 5))])
-@pytest.mark.parametrize("fused", [True, False])
-def test_layer_group_full_size(C, name, samples, fused):
-    _say("layer group", name, "fused" if fused else "two-call")
+@pytest.mark.parametrize("name,samples,fused,attn_select", [
+    ("c2", (0, 63), True, False), ("c2", (0, 63), True, True), ("c3", (0, 13, 31), True, False),
+    ("c3", (0, 13, 31), False, False), ("c3", (0, 13, 31), True, True), ("c4", (0, 5), True, False),
+    ("c4", (0, 5), False, False)])
+def test_layer_group_full_size(C, name, samples, fused, attn_select):
+    """Every layer of a group at full size against the oracle on sampled queries: fused
+    scoring + selection, two calls, and the last Top-K level inside the attention call."""
+    _say("layer group", name, "fused" if fused else "two-call", "select in attention" if attn_select else "")
     from fp4_kv_cache_layer_amd.layer import Csa2Step
     wl = workloads.config(name)
     case = G.Case(wl, swa_layers=range(len(wl.layers)))
     caches = case.gpu_caches()
-    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, fused=fused)
+    step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, fused=fused, attn_select=attn_select)
+    assert step.attn_select == attn_select
     snaps = G.run_group_snapshots(case, step, caches)
     for qi in samples:
         _say("  oracle query", qi)
