@@ -406,9 +406,9 @@ def sources_digest() -> str:
 
 
 def measured_traffic():
-    """HBM bytes per csa2_index_topk call from the committed counter summary (FETCH_SIZE and
-    WRITE_SIZE runs, scaled by the calibration copy), or None when the summary is missing or
-    the kernel sources changed since it was taken."""
+    """HBM bytes per k_score_select launch (the roofline's kernel) from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE runs, scaled by the calibration copy), or None when the
+    summary is missing or the kernel sources changed since it was taken."""
     try:
         text = open(TRAFFIC_SUMMARY).read()
     except OSError:
