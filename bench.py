@@ -51,7 +51,7 @@ class LayerBench:
     (`swa_miss`: the prefix's window state is not cached) the rings start empty and every
     layer writes the window entries of all its query rows, replay rows included."""
 
-    def __init__(self, wl, torch, C, group: int = 1, index_fmt: str = "mxfp4", attn_select: bool = False):
+    def __init__(self, wl, torch, C, group: int = 1, index_fmt: str = "mxfp4", attn_select: bool = True):
         from fp4_kv_cache_layer_amd.layer import INDEX_FORMATS, Caches, Csa2Step, plan_group
         self.wl, self.torch, self.C = wl, torch, C
         self.ik_fmt, self.ik_group = INDEX_FORMATS[index_fmt]
@@ -329,7 +329,7 @@ def cpu_baseline(wl, n_sample: int, reps: int):
 
 
 def measure_layers(name, steps, warmup, torch, C, layers_to_time, group: int = 1, index_fmt: str = "mxfp4",
-                   attn_select: bool = False):
+                   attn_select: bool = True):
     """Graph-replay time of each listed layer's step (`steps` steps in graphs of
     steps_per_graph(steps) consecutive steps of that layer) and of the whole group (one
     group per graph); isolated launch times of the first listed layer's calls."""
@@ -447,7 +447,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-modes", action="store_true", help="skip the per-mode 128K group and 1M pool group")
     ap.add_argument("--cpu-sample", type=int, default=4)
     ap.add_argument("--cpu-reps", type=int, default=48)
@@ -476,19 +476,17 @@ def main():
     value = wl.n_q / (ms / 1000.0)
     sb = score_bytes(wl, "full")
     # the dominant kernel, k_score_select (FP4 scores of every visible entry and the first
-    # Top-K level), timed alone through csa2_index_segments, which launches just that kernel
-    # with the grid and arguments of the step's csa2_index_topk call
-    score_call = "scoring_kernel"
+    # Top-K level): the step's scoring call csa2_index_segments launches just that kernel
+    # (the last Top-K level runs inside the attention call)
+    score_call = "index_segments"
     achieved = sb / (gcall[score_call] / 1000.0) / 1e9
-    call_gbs = sb / (gcall["index_topk"] / 1000.0) / 1e9
     at_ms = gcall["attn"]
     at_tflops = attn_flops(wl) / (at_ms / 1e3) / 1e12
     at_gbs = attn_bytes(wl) / (at_ms / 1e3) / 1e9
     log(f"step {ms * 1000:.1f} us (graph replay); isolated launches (us): " +
         ", ".join(f"{k}={v * 1000:.1f}" for k, v in phase.items()) + "; per call in graphs (us): " +
         ", ".join(f"{k}={v * 1000:.1f}" for k, v in gcall.items()))
-    log(f"k_score_select {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak); csa2_index_topk call "
-        f"{call_gbs:.0f} GB/s ({call_gbs / HBM_PEAK_GBS:.1%}); attention "
+    log(f"k_score_select {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak); attention "
         f"{at_tflops:.1f} TFLOP/s ({at_tflops / MFMA_F16_PEAK_TFLOPS:.2%} of fp16 MFMA peak), {at_gbs:.0f} GB/s")
     result = {
         "metric": "CSA2 decode query-tokens/s per layer at 128K & 1M ctx; % HBM peak",
@@ -511,17 +509,14 @@ def main():
         "graph_call_us": {k: round(v * 1000, 2) for k, v in gcall.items()},
         "hbm_frac_step": round(step_bytes(wl, "full") / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm",
-                     "kernel": "k_score_select (FP4 scoring of every visible entry + the first Top-K level; "
-                               "timed alone through csa2_index_segments)",
+                     "kernel": "k_score_select (csa2_index_segments: FP4 scoring of every visible entry + the "
+                               "first Top-K level, one launch; the last level runs in the attention call)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": sb,
                      "traffic": measured_traffic(),
-                     "timing": "HIP events around graph replays of 8 back-to-back csa2_index_segments calls",
-                     "index_topk_call": {"us": round(gcall["index_topk"] * 1e3, 2), "gb_per_s": round(call_gbs, 1),
-                                         "frac": round(call_gbs / HBM_PEAK_GBS, 4),
-                                         "note": "the step's whole scoring call: k_score_select + the last "
-                                                 "selection level (a launch of its own)"}},
-        "attention": {"kernel": "csa2_sparse_attn (k_attn)", "us": round(at_ms * 1e3, 2),
+                     "timing": "HIP events around graph replays of 8 back-to-back csa2_index_segments calls"},
+        "attention": {"kernel": "csa2_sparse_attn_topk (k_attn: the last Top-K level, then attention)",
+                      "us": round(at_ms * 1e3, 2),
                       "flops_per_launch": attn_flops(wl), "tflops": round(at_tflops, 2),
                       "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS, "mfma_frac": round(at_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                       "bytes_per_launch": attn_bytes(wl), "gb_per_s": round(at_gbs, 1),
@@ -572,18 +567,20 @@ def main():
             "us_per_layer_step_grouped_scoring": round(mt[4][1] * 1e3, 2),
             "isolated_launch_us": {k: round(v * 1e3, 1) for k, v in mt[1][2].items()},
             "isolated_launch_us_grouped": {k: round(v * 1e3, 1) for k, v in mt[4][2].items()}}
-        # the headline step with the last Top-K level inside the attention call
-        rs_ = measure_layers("c2", args.steps, args.warmup, torch, C, [0], attn_select=True)
-        modes["full_128k_select_in_attention"] = {
-            "calls": "csa2_index_segments, then csa2_sparse_attn_topk (the last Top-K level in the attention call)",
+        # the headline step with the last Top-K level as a launch of its own
+        rs_ = measure_layers("c2", args.steps, args.warmup, torch, C, [0], attn_select=False)
+        g_ = rs_["graph_call"]
+        modes["full_128k_last_level_kernel"] = {
+            "calls": "csa2_index_topk (k_score_select + the last Top-K level), then csa2_sparse_attn",
             "us_per_layer_step": round(rs_["layers"][0]["ms"] * 1e3, 2),
             "query_tokens_per_s": round(rs_["wl"].n_q / (rs_["layers"][0]["ms"] / 1e3), 1),
-            "graph_call_us": {k: round(v * 1e3, 2) for k, v in rs_["graph_call"].items()}}
+            "graph_call_us": {k: round(v * 1e3, 2) for k, v in g_.items()},
+            "index_topk_gb_per_s": round(score_bytes(rs_["wl"], "full") / (g_["index_topk"] / 1e3) / 1e9, 1)}
         # the NVFP4-style indexer variant on the headline step
         rn = measure_layers("c2", args.steps, args.warmup, torch, C, [0], index_fmt="nvfp4")
         wln, msn, isn, gcn = rn["wl"], rn["layers"][0]["ms"], rn["isolated"], rn["graph_call"]
         bn = score_bytes(wln, "full", "nvfp4")
-        scn = "index_topk"
+        scn = "index_segments" if "index_segments" in gcn else "index_topk"
         gbs = bn / (gcn[scn] / 1e3) / 1e9
         modes["full_128k_nvfp4_indexer"] = {
             "index_format": "E2M1 + E4M3 per 16 (72 B per indexer-K entry), fp16 MFMA scoring",

@@ -162,13 +162,42 @@ __device__ __forceinline__ void select_block(uint64_t (&key)[kEpt], int K, uint3
       __syncthreads();
       // every wave: lane l owns bins 4l..4l+3 of the histogram summed over waves and copies
       uint32_t hs[4] = {0u, 0u, 0u, 0u};
+      if constexpr (kWaves <= 4) {
 #pragma unroll
-      for (int wv = 0; wv < kWaves; ++wv) {
-        const uint4* hw = reinterpret_cast<const uint4*>(hist + ((pass & 1) * kWaves + wv) * 256 * kTkCopies);
+        for (int wv = 0; wv < kWaves; ++wv) {
+          const uint4* hw = reinterpret_cast<const uint4*>(hist + ((pass & 1) * kWaves + wv) * 256 * kTkCopies);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint4 c = hw[4 * lane + j];
-          hs[j] += c.x + c.y + c.z + c.w;
+          for (int j = 0; j < 4; ++j) {
+            const uint4 c = hw[4 * lane + j];
+            hs[j] += c.x + c.y + c.z + c.w;
+          }
+        }
+      } else {
+        // More waves: every wave reading every histogram would cost LDS reads that grow
+        // with the square of the wave count, so first thread t sums bin t % 256 over the
+        // four waves of group t / 256 (one thread per group and bin), then every wave adds
+        // the groups' sums.
+        static_assert(kWaves % 4 == 0, "waves in groups of four");
+        constexpr int kGroups = kWaves / 4;
+        __shared__ __attribute__((aligned(16))) uint32_t part[kGroups][256];
+        {
+          const int b = tid & 255, g = tid >> 8;
+          uint32_t sum = 0u;
+#pragma unroll
+          for (int wv = 4 * g; wv < 4 * g + 4; ++wv) {
+            const uint4 c = reinterpret_cast<const uint4*>(hist + ((pass & 1) * kWaves + wv) * 256 * kTkCopies)[b];
+            sum += c.x + c.y + c.z + c.w;
+          }
+          part[g][b] = sum;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+          const uint4 c = reinterpret_cast<const uint4*>(part[g])[lane];
+          hs[0] += c.x;
+          hs[1] += c.y;
+          hs[2] += c.z;
+          hs[3] += c.w;
         }
       }
       const uint32_t tot = hs[0] + hs[1] + hs[2] + hs[3];

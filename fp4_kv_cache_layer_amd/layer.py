@@ -112,15 +112,15 @@ class Csa2Step:
     def __init__(self, n_q: int, n_heads: int, idx_heads: int, seq_cap: int, k: int = 512, window: int = 128,
                  block: int = 8, max_blocks: int = 2048, idx_dim: int = 128, dim: int = 512,
                  out_dtype=torch.float32, fused: bool = True, group: int = 1, index_fmt: str = "mxfp4",
-                 attn_select: bool = False, device="cuda"):
+                 attn_select: bool = True, device="cuda"):
         """fused: score and select in one call (csa2_index_topk) wherever the layer does not
         need the score array itself (it does only when it builds the pool).  group: query
         rows come in groups of `group` consecutive rows of one sequence (several tokens of a
         sequence at once); layers scoring all visible entries then read each group's indexer
         K once.  index_fmt: the indexer Q/K format ("mxfp4" or "nvfp4", see INDEX_FORMATS).
         attn_select: finish the Top-K inside the attention call where plan_group allows it
-        (a variant: measured slower than the separate last selection level, see
-        csa2_sparse_attn_topk)."""
+        (the survivors of up to 131,072 entries at k = 512); False keeps the last selection
+        level as a launch of its own (csa2_index_topk, then csa2_sparse_attn)."""
         plan_group(["full"], fused, group, index_fmt)   # validates the combination
         n_cand = C.csa2_segment_keys(seq_cap, k)
         fits = fused and group == 1 and 1 <= n_cand <= 8192
