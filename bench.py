@@ -105,6 +105,10 @@ class LayerBench:
         self.new_swa = [torch.from_numpy(np.stack([wl.swa_latents(L, int(b), int(t), 1)[0]
                                                    for b, t in zip(tok_seq, tok_pos)])).to(dev)
                         for L in range(n_layers)]
+        # one new token per queried sequence and every row is one of them (decode): the
+        # attention call appends the row's window entry itself
+        self.fuse_window = bool(np.unique(wl.q_seq).size == wl.n_q and new_tok.all()
+                                and not wl.extra.get("swa_miss"))
         self.dst_entry = torch.from_numpy(ent_seq * wl.seq_cap + ent_row).to(dev)
         self.dst_swa = torch.from_numpy(tok_seq * wl.swa_cap + (tok_pos - wl.swa_base) % wl.swa_cap).to(dev)
         self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group, index_fmt=index_fmt,
@@ -123,14 +127,17 @@ class LayerBench:
         if mode.startswith("full"):
             jobs += [(self.new_main, C.FMT_NVFP4, flat(c.kv_codes), flat(c.kv_scales), self.dst_entry),
                      (self.new_ik, self.ik_fmt, flat(c.ik_codes), flat(c.ik_scales), self.dst_entry)]
-        jobs.append((self.new_swa[L], C.FMT_FP8, flat(c.swa[L]), None, self.dst_swa))
+        if not self.fuse_window:
+            jobs.append((self.new_swa[L], C.FMT_FP8, flat(c.swa[L]), None, self.dst_swa))
         q_idx, w, qa = self.inputs[L]
         names = self.plan[L]
         if "quantize_index_q" in names:
             n_q, h, d = q_idx.shape
             jobs.append((q_idx.view(n_q * h, d), self.ik_fmt, st.qi_codes.view(n_q * h, d // 2),
                          st.qi_scales.view(n_q * h, d // self.ik_group), None))
-        out["quantize"] = C.csa2_quantize_kv_multi(jobs, _bind=True)
+        if jobs:
+            out["quantize"] = C.csa2_quantize_kv_multi(jobs, _bind=True)
+        nw = self.new_swa[L] if self.fuse_window else None
         if mode == "full_pool":
             out["index_topk_pool"] = st.index_topk_build_pool(c, w, self.q_seq, self.n_vis, bind=True)
         elif "score_grouped" in names:
@@ -141,9 +148,9 @@ class LayerBench:
         elif mode != "reuse":
             out["index_topk"] = st.index_topk(c, w, self.q_seq, self.n_vis, mode == "reindex_pool", bind=True)
         if "attend_topk" in names:   # the last Top-K level runs inside the attention call
-            out["attn"] = st.attend_topk(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True)
+            out["attn"] = st.attend_topk(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True, new_win=nw)
         else:
-            out["attn"] = st.attend(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True)
+            out["attn"] = st.attend(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True, new_win=nw)
         return out
 
     def segments_call(self, L: int):

@@ -70,14 +70,14 @@ def lib() -> ctypes.CDLL:
         "csa2_topk_workspace_bytes": ([i32, i64, i32], sz),
         "csa2_build_pool": ([vp, i64, i32, vp, i64, i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_pool_workspace_bytes": ([i32, i64, i32, i32], sz),
-        "csa2_sparse_attn": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp, vp, vp, i32, f32, vp,
-                              i32, vp, vp, sz, vp], i32),
+        "csa2_sparse_attn": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp, vp, vp, vp, i32, i32, f32,
+                              vp, i32, vp, vp, sz, vp], i32),
         "csa2_attn_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
         "csa2_index_segments": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp], i32),
         "csa2_index_segments_nvfp4": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp], i32),
         "csa2_segment_keys": ([i64, i32], i64),
         "csa2_sparse_attn_topk": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, i64, vp, vp, vp,
-                                   i32, f32, vp, i32, vp, vp, sz, vp], i32),
+                                   vp, i32, i32, f32, vp, i32, vp, vp, sz, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -417,8 +417,18 @@ def _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start
             raise ValueError("lse shape")
 
 
+def _new_win(new_win, n_q, D):
+    """(pointer, dtype) of the optional window append: [n_q, D] f32 / bf16 latents."""
+    if new_win is None:
+        return None, DT_F32
+    if new_win.dtype not in (torch.float32, torch.bfloat16) or tuple(new_win.shape) != (n_q, D) or \
+            not new_win.is_contiguous() or not new_win.is_cuda:
+        raise ValueError("new_win must be a contiguous [n_q, D] f32/bf16 device tensor")
+    return _p(new_win), DT_F32 if new_win.dtype == torch.float32 else DT_BF16
+
+
 def csa2_sparse_attn_topk(q, kv_codes, kv_scales, q_seq, cand_keys, k: int, idx_out, count_out, swa, swa_base, q_pos,
-                          replay_start, window: int, sm_scale: float, out, lse=None, workspace=None,
+                          replay_start, window: int, sm_scale: float, out, lse=None, workspace=None, new_win=None,
                           _bind: bool = False):
     """csa2_sparse_attn with the index set selected in the call from csa2_index_segments'
     cand_keys [n_q, n_cand]; writes it to idx_out [n_q, k] int32 and count_out [n_q] int32."""
@@ -435,15 +445,16 @@ def csa2_sparse_attn_topk(q, kv_codes, kv_scales, q_seq, cand_keys, k: int, idx_
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
     odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
+    nw, nwt = _new_win(new_win, n_q, D)
     return _run("csa2_sparse_attn_topk", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq),
                                           _p(cand_keys), cand_keys.shape[1], k, _p(idx_out), _p(count_out), _p(swa),
-                                          swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), window,
+                                          swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), nw, nwt, window,
                                           ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes,
                                           _stream()), _bind)
 
 
 def csa2_sparse_attn(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, replay_start, window: int,
-                     sm_scale: float, out, lse=None, workspace=None, _bind: bool = False):
+                     sm_scale: float, out, lse=None, workspace=None, new_win=None, _bind: bool = False):
     """q [n_q, H, 512] bf16; kv_codes [n_seq, seq_cap, 256], kv_scales [n_seq, seq_cap, 32];
     idx [n_q, k] int32; swa [n_seq, swa_cap, 512] u8; swa_base [n_seq] int64;
     q_pos, replay_start [n_q] int64; out [n_q, H, 512] f32/bf16; lse [n_q, H] f32."""
@@ -473,7 +484,8 @@ def csa2_sparse_attn(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, r
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
     odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
+    nw, nwt = _new_win(new_win, n_q, D)
     return _run("csa2_sparse_attn", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq), _p(idx),
-                                     k, _p(swa), swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), window,
+                                     k, _p(swa), swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), nw, nwt, window,
                                      ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes,
                                      _stream()), _bind)

@@ -71,6 +71,7 @@ struct AttnArgs {
   const int32_t* idx;
   int k;
   const uint8_t* swa;
+  uint8_t* swa_w;     // the same ring, written only by the window append
   int64_t swa_cap;
   const int64_t* swa_base;
   const int64_t* q_pos;
@@ -89,6 +90,9 @@ struct AttnArgs {
   int cand_per_q;
   int32_t* idx_out;
   int32_t* count_out;
+  // window append: [n_q, 512] f32 or bf16 latents of each row's own token (or nullptr)
+  const void* new_win;
+  int new_win_bf16;
 };
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -126,6 +130,7 @@ struct GatherSlot {
   uint4 r[4];
   uint32_t sc;
   uint32_t ok;
+  uint32_t is_new;   // the window key of the row's own token, appended by this call
 };
 
 // The per-query arrays come as restrict-qualified arguments of their own: nothing this
@@ -218,6 +223,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     for (int st = 0; st < kQS; ++st) qraw[st] = *reinterpret_cast<const uint4*>(qp + 8 * st);
   }
 
+  // Window append: thread c quantises channel c of the row's new window latent (the
+  // quantiser's exact E4M3 rounding); the bytes are staged in LDS for this workgroup's own
+  // window tiles, and workgroup (head group 0, split 0) writes them to the ring.
+  static_assert(kAttnThreads == kD, "one thread per channel of the appended window entry");
+  __shared__ __attribute__((aligned(16))) uint8_t s_new[kD];
+  uint32_t new_code = 0;
+  if (a.new_win) {  // uniform
+    const uint32_t bits = a.new_win_bf16 ? (uint32_t)reinterpret_cast<const uint16_t*>(a.new_win)[(int64_t)q * kD + tid] << 16
+                                         : reinterpret_cast<const uint32_t*>(a.new_win)[(int64_t)q * kD + tid];
+    new_code = fp8_code_bits(bits);
+    s_new[tid] = (uint8_t)new_code;
+  }
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   const int64_t lo = s > t - a.window + 1 ? s : t - a.window + 1;
   const int64_t n_swa = seq_ok && t >= lo ? t - lo + 1 : 0;
@@ -234,6 +251,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     r_lo = r_lo < 0 ? r_lo + a.swa_cap : r_lo;
   }
   const uint32_t win_row0 = (uint32_t)r_lo;
+  if (a.new_win && hg == 0 && split == 0 && seq_ok && t >= 0) {
+    // ring row of token t: the window keys [lo, t] are consecutive rows from win_row0
+    int64_t rt = (t - swa_b) % a.swa_cap;
+    rt = rt < 0 ? rt + a.swa_cap : rt;
+    a.swa_w[((int64_t)seq * a.swa_cap + rt) * kD + tid] = (uint8_t)new_code;
+  }
   const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 2);
   const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 16);
   const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_cap * kD;
@@ -266,6 +289,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     const uint32_t pm = ok_main ? (uint32_t)p : 0u;
     const int j = (tile - a.main_tiles) * kT + col;
     const bool ok_win = real && !is_main && seq_ok && j >= 0 && j < n_swa;
+    g.is_new = a.new_win != nullptr && ok_win && j == n_swa - 1;   // window key j is token lo + j
     uint32_t row = win_row0 + (uint32_t)j;
     row = ok_win ? (row >= swa_cap32 ? row - swa_cap32 : row) : 0u;
     // byte offsets fit 32 bits: seq_cap <= 2^24 rows of 256 B, swa_cap <= 2^23 rows of 512 B
@@ -345,8 +369,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
         sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[st + 1], sb, 0, 0, 0);
       }
     } else {
-      const uint32_t w[16] = {g.r[0].x, g.r[0].y, g.r[0].z, g.r[0].w, g.r[1].x, g.r[1].y, g.r[1].z, g.r[1].w,
-                              g.r[2].x, g.r[2].y, g.r[2].z, g.r[2].w, g.r[3].x, g.r[3].y, g.r[3].z, g.r[3].w};
+      uint32_t w[16] = {g.r[0].x, g.r[0].y, g.r[0].z, g.r[0].w, g.r[1].x, g.r[1].y, g.r[1].z, g.r[1].w,
+                        g.r[2].x, g.r[2].y, g.r[2].z, g.r[2].w, g.r[3].x, g.r[3].y, g.r[3].z, g.r[3].w};
+      if (a.new_win) {  // uniform: the row's own token comes from the LDS copy, not the ring
+        const uint4* sn = reinterpret_cast<const uint4*>(s_new + kHalf * half + 64 * grp);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 n = sn[u];
+          w[4 * u] = g.is_new ? n.x : w[4 * u];
+          w[4 * u + 1] = g.is_new ? n.y : w[4 * u + 1];
+          w[4 * u + 2] = g.is_new ? n.z : w[4 * u + 2];
+          w[4 * u + 3] = g.is_new ? n.w : w[4 * u + 3];
+        }
+      }
 #pragma unroll
       for (int st = 0; st < kQS; st += 2) {
         const v8h k0 = fp8x8_to_f16(w[2 * st] & keep, w[2 * st + 1] & keep);
@@ -664,10 +699,10 @@ extern "C" size_t csa2_attn_workspace_bytes(int n_q, int n_heads, int dim, int k
 
 static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes, const uint8_t* kv_scales,
                        int64_t seq_cap, int n_seq, const int32_t* q_seq, const int32_t* idx, const uint64_t* cand_keys,
-                       int cand_per_q, int32_t* idx_out, int32_t* count_out, int k, const uint8_t* swa,
-                       int64_t swa_cap, const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
-                       int window, float sm_scale, void* out, int out_dtype, float* lse, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       int cand_per_q, int32_t* idx_out, int32_t* count_out, int k, uint8_t* swa, int64_t swa_cap,
+                       const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
+                       const void* new_win, int new_win_dtype, int window, float sm_scale, void* out, int out_dtype,
+                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !kv_codes || !kv_scales || !q_seq || !swa || !swa_base || !q_pos || !replay_start || !out)
     return CSA2_ERR_NULL;
   const bool select = cand_keys != nullptr;
@@ -678,6 +713,7 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
     return CSA2_ERR_SHAPE;
   if (select && (k < 1 || cand_per_q < 1 || cand_per_q > kSelMax)) return CSA2_ERR_SHAPE;
   if (out_dtype != CSA2_DT_F32 && out_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
+  if (new_win && new_win_dtype != CSA2_DT_F32 && new_win_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(kv_codes) || !aligned16(swa) || !aligned16(out) || ((uintptr_t)kv_scales & 7))
     return CSA2_ERR_SHAPE;
   if (n_q == 0) return CSA2_OK;
@@ -695,6 +731,7 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
   a.idx = idx;
   a.k = k;
   a.swa = swa;
+  a.swa_w = swa;
   a.swa_cap = swa_cap;
   a.swa_base = swa_base;
   a.q_pos = q_pos;
@@ -713,6 +750,8 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
   a.cand_per_q = cand_per_q;
   a.idx_out = idx_out;
   a.count_out = count_out;
+  a.new_win = new_win;
+  a.new_win_bf16 = new_win_dtype == CSA2_DT_BF16;
   if (p.nsplit > 1) {
     size_t need = csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window);
     if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
@@ -735,24 +774,24 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
 
 extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
                                 const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
-                                const int32_t* idx, int k, const uint8_t* swa, int64_t swa_cap,
-                                const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
-                                int window, float sm_scale, void* out, int out_dtype, float* lse, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                const int32_t* idx, int k, uint8_t* swa, int64_t swa_cap, const int64_t* swa_base,
+                                const int64_t* q_pos, const int64_t* replay_start, const void* new_win,
+                                int new_win_dtype, int window, float sm_scale, void* out, int out_dtype, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, idx, nullptr, 0, nullptr,
-                     nullptr, k, swa, swa_cap, swa_base, q_pos, replay_start, window, sm_scale, out, out_dtype, lse,
-                     workspace, workspace_bytes, stream);
+                     nullptr, k, swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window,
+                     sm_scale, out, out_dtype, lse, workspace, workspace_bytes, stream);
 }
 
 extern "C" int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
                                      const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
                                      const uint64_t* cand_keys, int cand_per_q, int k, int32_t* idx_out,
-                                     int32_t* count_out, const uint8_t* swa, int64_t swa_cap,
-                                     const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
-                                     int window, float sm_scale, void* out, int out_dtype, float* lse,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+                                     int32_t* count_out, uint8_t* swa, int64_t swa_cap, const int64_t* swa_base,
+                                     const int64_t* q_pos, const int64_t* replay_start, const void* new_win,
+                                     int new_win_dtype, int window, float sm_scale, void* out, int out_dtype,
+                                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (!cand_keys || !idx_out || !count_out) return CSA2_ERR_NULL;
   return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, nullptr, cand_keys, cand_per_q,
-                     idx_out, count_out, k, swa, swa_cap, swa_base, q_pos, replay_start, window, sm_scale, out,
-                     out_dtype, lse, workspace, workspace_bytes, stream);
+                     idx_out, count_out, k, swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype,
+                     window, sm_scale, out, out_dtype, lse, workspace, workspace_bytes, stream);
 }

@@ -42,6 +42,30 @@ __device__ __forceinline__ float e2m1_val(uint32_t c) {
   return __uint_as_float(bits | ((c & 8u) << 28));
 }
 
+// E4M3 magnitude code (0..126) nearest to a >= 0 (finite), ties to the even code,
+// saturating at 448 (code 126).  Normal range (a >= 2^-6): the fp32 significand is rounded
+// to 3 bits, ties to even, on the bit pattern (a carry out of the significand is the next
+// binade, as it should be) and the exponent is rebiased from 127 to 7.  Subnormal range:
+// the code is a * 2^9 rounded to an integer, ties to even (a * 2^9 is exact); 8 is the
+// smallest normal code, so a carry there is also right.
+// Both ranges are computed and one is selected, so that the code has no branch (a branch
+// here would sit between the loads of a group's values and make them wait one by one).
+// Used by the quantiser and by the attention kernel's window append, so both write the
+// same bytes.
+__device__ __forceinline__ int fp8_mag_code(float a) {
+  const int sub = (int)__builtin_rintf(fminf(a, 0x1p-6f) * 512.0f);
+  const uint32_t b = __float_as_uint(a);
+  int c = (int)((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120 << 3);
+  c = c > 126 ? 126 : c;
+  return a < 0x1p-6f ? sub : c;
+}
+
+// E4M3 byte of a finite fp32 value given as bits (unscaled: nearest code, ties to even,
+// saturating at +-448; the sign is kept, so -0 and small negatives give 0x80)
+__device__ __forceinline__ uint32_t fp8_code_bits(uint32_t b) {
+  return (uint32_t)fp8_mag_code(__uint_as_float(b & 0x7fffffffu)) | ((b >> 24) & 0x80u);
+}
+
 // fp32 holding a value exactly representable in bf16 -> bf16 bits (truncation is exact)
 __device__ __forceinline__ uint16_t exact_bf16_bits(float f) { return (uint16_t)(__float_as_uint(f) >> 16); }
 

@@ -16,22 +16,6 @@
 
 namespace csa2 {
 
-// E4M3 magnitude code (0..126) nearest to a >= 0 (finite), ties to the even code,
-// saturating at 448 (code 126).  Normal range (a >= 2^-6): the fp32 significand is rounded
-// to 3 bits, ties to even, on the bit pattern (a carry out of the significand is the next
-// binade, as it should be) and the exponent is rebiased from 127 to 7.  Subnormal range:
-// the code is a * 2^9 rounded to an integer, ties to even (a * 2^9 is exact); 8 is the
-// smallest normal code, so a carry there is also right.
-// Both ranges are computed and one is selected, so that the code has no branch (a branch
-// here would sit between the loads of a group's values and make them wait one by one).
-__device__ __forceinline__ int fp8_mag_code(float a) {
-  const int sub = (int)__builtin_rintf(fminf(a, 0x1p-6f) * 512.0f);
-  const uint32_t b = __float_as_uint(a);
-  int c = (int)((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120 << 3);
-  c = c > 126 ? 126 : c;
-  return a < 0x1p-6f ? sub : c;
-}
-
 // "a/6 rounds to an E4M3 code >= c" for c >= 1: a/6 lies above the midpoint of codes c-1
 // and c, or on it with c even.  6 * midpoint = 3 * (v(c-1) + v(c)) is exact in fp32.
 __device__ __forceinline__ bool scale_at_least(float a, int c) {
@@ -184,7 +168,7 @@ __device__ __forceinline__ void quant_group_fp8(const T* __restrict__ src, int64
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t b = bits[i];
-    uint32_t c = (uint32_t)fp8_mag_code(__uint_as_float(b & 0x7fffffffu)) | ((b >> 24) & 0x80u);
+    const uint32_t c = fp8_code_bits(b);
     if (i < 4) lo |= c << (8 * i);
     else hi |= c << (8 * (i - 4));
   }

@@ -208,13 +208,13 @@ class Csa2Step:
                   self.cand_keys, _bind=bind)
 
     def attend_topk(self, caches: Caches, layer: int, q_attn, q_seq, q_pos, replay_start, out=None, lse=None,
-                    bind=False):
+                    bind=False, new_win=None):
         """attention that first selects the Top-K from index_segments' survivors and writes it
-        to the step's index set."""
+        to the step's index set.  new_win: see attend."""
         return C.csa2_sparse_attn_topk(q_attn, caches.kv_codes, caches.kv_scales, q_seq, self.cand_keys, self.k,
                                        self.idx, self.count, caches.swa[layer], caches.swa_base, q_pos, replay_start,
                                        self.window, self.sm_scale, self.out if out is None else out,
-                                       self.lse if lse is None else lse, self.ws_attn, _bind=bind)
+                                       self.lse if lse is None else lse, self.ws_attn, new_win=new_win, _bind=bind)
 
     def _score_select(self, caches, w, q_seq, n_vis, in_pool, bind):
         if self.fused:
@@ -226,11 +226,13 @@ class Csa2Step:
                                  self.ws_pool, _bind=bind)
 
     def attend(self, caches: Caches, layer: int, q_attn, q_seq, q_pos, replay_start, out=None, lse=None,
-               bind=False):
+               bind=False, new_win=None):
+        """new_win: [n_q, D] window latents of each row's own token, appended to the layer's
+        window cache by the attention call itself (rows of distinct sequences only)."""
         return C.csa2_sparse_attn(q_attn, caches.kv_codes, caches.kv_scales, q_seq, self.idx, caches.swa[layer],
                                   caches.swa_base, q_pos, replay_start, self.window, self.sm_scale,
                                   self.out if out is None else out, self.lse if lse is None else lse, self.ws_attn,
-                                  _bind=bind)
+                                  new_win=new_win, _bind=bind)
 
     def run_group(self, caches: Caches, modes, inputs, q_seq, n_vis, q_pos, replay_start, outs=None, lses=None,
                   bind=False):

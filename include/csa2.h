@@ -375,21 +375,28 @@ size_t csa2_pool_workspace_bytes(int n_q, int64_t max_vis, int block, int max_bl
  *             [0, seq_cap)) = empty;  k in 0..2048
  *   swa       [n_seq, swa_cap, dim] E4M3; swa_base [n_seq] int64; window in 1..1024 and
  *             window <= swa_cap <= CSA2_MAX_WINDOW_ROWS; seq_cap <= CSA2_MAX_ATTN_ENTRIES
+ *   new_win   NULL, or [n_q, dim] f32 / bf16 (new_win_dtype): the post-RoPE window latent of
+ *             each row's own token t = q_pos[q].  The call appends it first: quantised to
+ *             E4M3 exactly as csa2_quantize_kv with CSA2_FMT_FP8 writes it, stored at ring
+ *             row (t - swa_base[seq]) mod swa_cap of sequence q_seq[q], and attended as
+ *             the window key of token t -- one launch instead of an append call and an
+ *             attention call.  Precondition: no two rows of the call belong to the same
+ *             sequence (every other window key must already be in the ring).
  *   out       [n_q, n_heads, dim] f32 or bf16 (out_dtype); lse [n_q, n_heads] f32 or NULL
  *   Workspace: csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window).
  * Arithmetic: Q.K and P.V on fp16 matrix cores with fp32 accumulation.  Every key/value
  * (E2M1 x E4M3, or E4M3) is exact in fp16; Q is converted from bf16 to fp16, exact for
  * |q| in [2^-14, 65504) (smaller magnitudes round to fp16 subnormals, larger ones
  * overflow); softmax in fp32; P rounded to fp16.
- * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED (out_dtype),
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED (out_dtype, new_win_dtype),
  * CSA2_ERR_WORKSPACE.
  */
 int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
                      const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
-                     const int32_t* idx, int k, const uint8_t* swa, int64_t swa_cap,
+                     const int32_t* idx, int k, uint8_t* swa, int64_t swa_cap,
                      const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
-                     int window, float sm_scale, void* out, int out_dtype, float* lse,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     const void* new_win, int new_win_dtype, int window, float sm_scale, void* out,
+                     int out_dtype, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 size_t csa2_attn_workspace_bytes(int n_q, int n_heads, int dim, int k, int window);
 
 /*
@@ -413,10 +420,11 @@ size_t csa2_attn_workspace_bytes(int n_q, int n_heads, int dim, int k, int windo
 int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
                           const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
                           const uint64_t* cand_keys, int cand_per_q, int k, int32_t* idx_out,
-                          int32_t* count_out, const uint8_t* swa, int64_t swa_cap,
+                          int32_t* count_out, uint8_t* swa, int64_t swa_cap,
                           const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
-                          int window, float sm_scale, void* out, int out_dtype, float* lse,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          const void* new_win, int new_win_dtype, int window, float sm_scale,
+                          void* out, int out_dtype, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -64,15 +64,17 @@ def test_validation_before_launch(L):
     assert L.csa2_topk_workspace_bytes(2, 8192, 512) == 0           # one segment: no scratch
     assert L.csa2_topk_workspace_bytes(2, 1 << 20, 512) > 0
     L.csa2_sparse_attn.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, i64, ctypes.c_int, vp, vp,
-                                   ctypes.c_int, vp, i64, vp, vp, vp, ctypes.c_int, ctypes.c_float, vp, ctypes.c_int,
-                                   vp, vp, ctypes.c_size_t, vp]
-    args = [fake, 4, 64, 512, fake, fake, 100, 1, fake, fake, 512, fake, 128, fake, fake, fake, 128, 0.05, fake, 0,
-            None, None, 0, None]
+                                   ctypes.c_int, vp, i64, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                   vp, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]
+    args = [fake, 4, 64, 512, fake, fake, 100, 1, fake, fake, 512, fake, 128, fake, fake, fake, None, 0, 128, 0.05,
+            fake, 0, None, None, 0, None]
     a = list(args); a[2] = 40                       # heads not a multiple of 16
     assert L.csa2_sparse_attn(*a) == -2
-    a = list(args); a[16] = 256                     # window > swa_cap
+    a = list(args); a[18] = 256                     # window > swa_cap
     assert L.csa2_sparse_attn(*a) == -2
-    a = list(args); a[19] = 7                       # out dtype
+    a = list(args); a[21] = 7                       # out dtype
+    assert L.csa2_sparse_attn(*a) == -3
+    a = list(args); a[16] = fake; a[17] = 9         # window-append dtype
     assert L.csa2_sparse_attn(*a) == -3
     a = list(args); a[9] = None                     # idx NULL with k > 0
     assert L.csa2_sparse_attn(*a) == -1
@@ -98,9 +100,9 @@ def test_select_in_attention_validation(L):
     a = list(seg); a[5] = 64                        # indexer dim
     assert L.csa2_index_segments(*a) == -2
     L.csa2_sparse_attn_topk.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, i64, vp,
-                                        vp, vp, i32, ctypes.c_float, vp, i32, vp, vp, ctypes.c_size_t, vp]
-    att = [fake, 4, 64, 512, fake, fake, 100, 1, fake, fake, 8192, 512, fake, fake, fake, 128, fake, fake, fake, 128,
-           0.05, fake, 0, None, None, 0, None]
+                                        vp, vp, vp, i32, i32, ctypes.c_float, vp, i32, vp, vp, ctypes.c_size_t, vp]
+    att = [fake, 4, 64, 512, fake, fake, 100, 1, fake, fake, 8192, 512, fake, fake, fake, 128, fake, fake, fake, None,
+           0, 128, 0.05, fake, 0, None, None, 0, None]
     a = list(att); a[9] = None                      # no candidate keys
     assert L.csa2_sparse_attn_topk(*a) == -1
     a = list(att); a[12] = None                     # no index output

@@ -587,6 +587,55 @@ def test_sparse_attn_split_workspace_reuse(C, n_q):
         assert np.abs(gl[qi] - ref_lse).max() <= 1e-3
 
 
+@pytest.mark.parametrize("select,dt", [(False, "f32"), (False, "bf16"), (True, "f32")])
+def test_window_append_in_attention(C, select, dt):
+    """Attention with new_win (the row's own window entry appended by the attention call)
+    writes the ring row csa2_quantize_kv writes and gives bit-identical outputs to appending
+    first and attending after; rows of distinct sequences, one with a replay start at t."""
+    _say("window append in attention", select, dt)
+    n_vis = [30000, 8193, 511, 20001, 16384, 3]
+    n_q = len(n_vis)
+    case = _score_case(61, n_q, 30000, n_vis, 16)           # one sequence per row
+    wl = case.wl
+    wl.replay_start[3] = wl.q_pos[3]                          # window = its own token only
+    caches = case.gpu_caches()
+    q_idx, w, qa = case.gpu_query_inputs(0)
+    q_seq, n_vis_t, q_pos, rs = case.gpu_meta()
+    rs = torch.from_numpy(wl.replay_start.astype(np.int64)).cuda()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(n_q, 16, 16, wl.seq_cap, attn_select=select)
+    st.quantize_index_q(q_idx)
+    if select:
+        st.index_segments(caches, w, q_seq, n_vis_t)
+    else:
+        st.index_topk(caches, w, q_seq, n_vis_t)
+    lat = np.stack([wl.swa_latents(0, int(wl.q_seq[i]), int(wl.q_pos[i]), 1)[0] for i in range(n_q)])
+    new = torch.from_numpy(lat).cuda()
+    if dt == "bf16":
+        new = new.to(torch.bfloat16)
+    rows = torch.from_numpy(((wl.q_pos - wl.swa_base) % wl.swa_cap).astype(np.int64)).cuda()
+    flat_rows = torch.arange(n_q, device="cuda", dtype=torch.int64) * wl.swa_cap + rows
+    ring = caches.swa[0].view(-1, 512)
+
+    def attend(new_win):
+        out = torch.empty(n_q, 16, 512, dtype=torch.float32, device="cuda")
+        lse = torch.empty(n_q, 16, dtype=torch.float32, device="cuda")
+        if select:
+            st.attend_topk(caches, 0, qa, q_seq, q_pos, rs, out, lse, new_win=new_win)
+        else:
+            st.attend(caches, 0, qa, q_seq, q_pos, rs, out, lse, new_win=new_win)
+        torch.cuda.synchronize()
+        return out, lse
+
+    C.csa2_quantize_kv(new, C.FMT_FP8, ring, None, flat_rows)     # append, then attend
+    ref_rows = ring[flat_rows].clone()
+    out_r, lse_r = attend(None)
+    ring[flat_rows] = 0x55                                        # stale bytes in the rows
+    out_f, lse_f = attend(new)
+    assert torch.equal(ring[flat_rows], ref_rows)
+    assert torch.equal(out_f, out_r) and torch.equal(lse_f, lse_r)
+
+
 def test_sparse_attn_no_keys(C):
     """s > t leaves the window empty; with no main entries the output is 0 and lse -inf."""
     _say("sparse_attn no keys")
