@@ -113,7 +113,8 @@ class LayerBench:
         self.dst_swa = torch.from_numpy(tok_seq * wl.swa_cap + (tok_pos - wl.swa_base) % wl.swa_cap).to(dev)
         self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group, index_fmt=index_fmt,
                              attn_select=attn_select)
-        self.plan = plan_group(wl.layers, group=group, index_fmt=index_fmt, attn_select=self.step.attn_select)
+        self.plan = plan_group(wl.layers, group=group, index_fmt=index_fmt, attn_select=self.step.attn_select,
+                               pool_select=self.step.pool_select)
 
     def calls(self, L: int):
         """Layer L's step as {phase: bound call} bound to the current stream, in order."""
@@ -145,10 +146,15 @@ class LayerBench:
             out["select"] = st.select(self.n_vis, bind=True)
         elif "index_segments" in names:
             out["index_segments"] = st.index_segments(c, w, self.q_seq, self.n_vis, bind=True)
+        elif "attend_pool_topk" in names:   # pool slot scores; the Top-K is selected in attention
+            out["score"] = st.score(c, w, self.q_seq, self.n_vis, in_pool=True, bind=True)
         elif mode != "reuse":
             out["index_topk"] = st.index_topk(c, w, self.q_seq, self.n_vis, mode == "reindex_pool", bind=True)
         if "attend_topk" in names:   # the last Top-K level runs inside the attention call
             out["attn"] = st.attend_topk(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True, new_win=nw)
+        elif "attend_pool_topk" in names:
+            out["attn"] = st.attend_pool_topk(c, L, qa, self.q_seq, self.n_vis, self.q_pos, self.rs, bind=True,
+                                              new_win=nw)
         else:
             out["attn"] = st.attend(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True, new_win=nw)
         return out

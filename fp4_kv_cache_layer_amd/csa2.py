@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         "csa2_segment_keys": ([i64, i32], i64),
         "csa2_sparse_attn_topk": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, i64, vp, vp, vp,
                                    vp, i32, i32, f32, vp, i32, vp, vp, sz, vp], i32),
+        "csa2_sparse_attn_pool_topk": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i64, vp, vp, vp, i32, i32, i32, vp,
+                                        vp, vp, i64, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, sz, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -451,6 +453,38 @@ def csa2_sparse_attn_topk(q, kv_codes, kv_scales, q_seq, cand_keys, k: int, idx_
                                           swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), nw, nwt, window,
                                           ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes,
                                           _stream()), _bind)
+
+
+def csa2_sparse_attn_pool_topk(q, kv_codes, kv_scales, q_seq, scores, n_vis, cand_blocks, n_cand_blocks, block: int,
+                               k: int, idx_out, count_out, swa, swa_base, q_pos, replay_start, window: int,
+                               sm_scale: float, out, lse=None, workspace=None, new_win=None, _bind: bool = False):
+    """csa2_sparse_attn inside a pool, with the Top-k selected in the call from the pool's
+    slot scores (scores [n_q, stride] f32 as csa2_index_score writes them with cand_blocks
+    [n_q, max_blocks] / n_cand_blocks [n_q]); writes idx_out [n_q, k] and count_out [n_q]."""
+    _need(scores, torch.float32, 2, "scores")
+    _need(n_vis, torch.int64, 1, "n_vis")
+    _need(cand_blocks, torch.int32, 2, "cand_blocks")
+    _need(n_cand_blocks, torch.int32, 1, "n_cand_blocks")
+    _need(idx_out, torch.int32, 2, "idx_out")
+    _need(count_out, torch.int32, 1, "count_out")
+    _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, scores.shape[0])
+    n_q, H, D = q.shape
+    n_seq, seq_cap, _ = kv_codes.shape
+    if tuple(idx_out.shape) != (n_q, k) or count_out.shape[0] != n_q or cand_blocks.shape[0] != n_q or \
+            n_cand_blocks.shape[0] != n_q or n_vis.shape[0] != n_q:
+        raise ValueError("sparse_attn_pool_topk: inconsistent shapes")
+    need = csa2_attn_workspace_bytes(n_q, H, D, k, window)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
+    nw, nwt = _new_win(new_win, n_q, D)
+    return _run("csa2_sparse_attn_pool_topk", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq,
+                                               _p(q_seq), _p(scores), scores.shape[1], _p(n_vis), _p(cand_blocks),
+                                               _p(n_cand_blocks), block, cand_blocks.shape[1], k, _p(idx_out),
+                                               _p(count_out), _p(swa), swa.shape[1], _p(swa_base), _p(q_pos),
+                                               _p(replay_start), nw, nwt, window, ctypes.c_float(sm_scale), _p(out),
+                                               odt, _p(lse), _p(workspace), ws_bytes, _stream()), _bind)
 
 
 def csa2_sparse_attn(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, replay_start, window: int,

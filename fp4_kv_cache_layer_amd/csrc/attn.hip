@@ -93,6 +93,13 @@ struct AttnArgs {
   // window append: [n_q, 512] f32 or bf16 latents of each row's own token (or nullptr)
   const void* new_win;
   int new_win_bf16;
+  // csa2_sparse_attn_pool_topk: the pool's slot scores [n_q, pool_stride] and slot map
+  const float* pool_scores;
+  int64_t pool_stride;
+  const int32_t* cand_blocks;
+  const int32_t* n_cand_blocks;
+  const int64_t* n_vis;
+  int block, max_cand_blocks;
 };
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -136,17 +143,19 @@ struct GatherSlot {
 // The per-query arrays come as restrict-qualified arguments of their own: nothing this
 // kernel writes can alias them, so their uniform loads go through the scalar cache.
 //
-// kSelect: the index list is not given but selected here, in every workgroup of the query,
-// from the survivors of the first Top-K level (csa2_index_segments): the same exact radix
-// select as the last level of csa2_index_topk (select.h), 512 threads x 16 keys, with the
-// histograms in the LDS of the V buffers (unused until the first tile), straight into the
-// staged index list.  Workgroup (head group 0, split 0) of the query also writes the list
-// and its count out for the layers that reuse it.
-constexpr int kSelEpt = 16;
-constexpr int kSelMax = kAttnThreads * kSelEpt;   // 8,192 survivor keys per query at most
-static_assert(2 * (kAttnThreads / 64) * 256 * kTkCopies * 4 <= 2 * kPairs * 2 * kVBuf, "selection histograms");
+// kSel != 0: the index list is not given but selected here, in every workgroup of the
+// query: from the survivors of the first Top-K level (kSel 1, csa2_index_segments, 16 keys
+// per thread) or from the scores of the pool's slots (kSel 2, at most 2,048 blocks x 8 =
+// 16,384 slots, 32 keys per thread), with the same exact radix select as the Top-K levels
+// (select.h), its histograms and scratch in the LDS of the V buffers (unused until the
+// first tile), straight into the staged index list.  Workgroup (head group 0, split 0) of
+// the query also writes the list and its count out for the layers that reuse it.
+constexpr int kSelMax = kAttnThreads * 16;      // 8,192 survivor keys per query at most
+constexpr int kPoolMax = kAttnThreads * 32;     // 16,384 pool slots per query at most
+constexpr int kSelHistWords = 2 * (kAttnThreads / 64) * 256 * kTkCopies;
+static_assert((kSelHistWords + 2 * 256 + 8 * 32) * 4 <= 2 * kPairs * 2 * kVBuf, "selection LDS");
 
-template <bool kSelect>
+template <int kSel>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int32_t* __restrict__ q_seq,
                                                            const int64_t* __restrict__ q_pos,
                                                            const int64_t* __restrict__ replay_start,
@@ -192,17 +201,52 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   // split's slice of the index list (it does not depend on them), then Q ----
   const int seq = q_seq[q];
   const int64_t t = q_pos[q], s = replay_start[q];
+  constexpr bool kSelect = kSel != 0;
+  constexpr int kEpt = kSel == 2 ? 32 : 16;
   constexpr int kIdxPer = CSA2_MAX_TOPK / kAttnThreads;
   const int n_keys = n_main * kT;
   int32_t iv[kIdxPer];
-  uint64_t key[kSelEpt];
-  if (kSelect) {  // candidate i*512 + tid of the query's survivors (cand_per_q >= 1)
+  uint64_t key[kEpt];
+  if constexpr (kSel == 1) {  // candidate i*512 + tid of the query's survivors (cand_per_q >= 1)
     const uint64_t* kp = a.cand_keys + (int64_t)q * a.cand_per_q;
     const int lim = a.cand_per_q;
 #pragma unroll
-    for (int i = 0; i < kSelEpt; ++i) {
+    for (int i = 0; i < kEpt; ++i) {
       const int o = i * kAttnThreads + tid;
       key[i] = kp[o < lim ? o : lim - 1] & (0ull - (uint64_t)(o < lim));
+    }
+  } else if constexpr (kSel == 2) {
+    // pool slot c = i*512 + tid: block cand_blocks[q][c / block], position block id * block
+    // + c % block; a candidate if c lies in the query's first n_cand_blocks blocks, the block
+    // id is valid and the position visible (as the first Top-K level inside a pool)
+    int nc = a.n_cand_blocks[q];
+    nc = nc < 0 ? 0 : (nc > a.max_cand_blocks ? a.max_cand_blocks : nc);
+    int64_t nv = a.n_vis[q];
+    nv = nv < 0 ? 0 : (nv > a.seq_cap ? a.seq_cap : nv);
+    const uint32_t blk = (uint32_t)a.block;
+    const uint32_t nslot = (uint32_t)nc * blk;   // <= 16,384
+    if (nslot > 0) {  // uniform
+      const float* sp = a.pool_scores + (int64_t)q * a.pool_stride;
+      const int32_t* cb = a.cand_blocks + (int64_t)q * a.max_cand_blocks;
+      int32_t bv[kEpt];
+      float v[kEpt];
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        uint32_t c = (uint32_t)(i * kAttnThreads + tid);
+        c = c < nslot - 1 ? c : nslot - 1;
+        bv[i] = cb[c / blk];
+        v[i] = sp[c];
+      }
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        const uint32_t c = (uint32_t)(i * kAttnThreads + tid);
+        const int64_t pos = (int64_t)bv[i] * blk + c % blk;
+        const bool ok = c < nslot && bv[i] >= 0 && pos < nv;
+        key[i] = make_key(v[i], (uint32_t)pos) & (0ull - (uint64_t)ok);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) key[i] = 0ull;
     }
   } else if (n_keys > 0) {  // uniform; idx may be absent when k == 0
 #pragma unroll
@@ -318,7 +362,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   if constexpr (kSelect) {
     // the whole index list, s_idx[0 .. k), ascending; the tiles index it from tile_lo * 16
     __shared__ int32_t s_count;
-    select_block<kAttnThreads, kSelEpt, true>(key, a.k, reinterpret_cast<uint32_t*>(lds), nullptr, s_idx, &s_count);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(lds);
+    select_block<kAttnThreads, kEpt, true>(key, a.k, hist, nullptr, s_idx, &s_count, hist + kSelHistWords);
     __syncthreads();
     if (hg == 0 && split == 0) {
       for (int i = tid; i < a.k; i += kAttnThreads) a.idx_out[(int64_t)q * a.k + i] = s_idx[i];
@@ -697,21 +742,39 @@ extern "C" size_t csa2_attn_workspace_bytes(int n_q, int n_heads, int dim, int k
   return (size_t)p.nsplit * n_q * n_heads * (kD + 2) * sizeof(float) + 256;
 }
 
+// Where the index set comes from: a given list (mode 0), the first Top-K level's survivors
+// (mode 1) or the pool's slot scores (mode 2); the last two select inside the kernel.
+struct AttnSel {
+  int mode;
+  const uint64_t* cand_keys;
+  int cand_per_q;
+  const float* pool_scores;
+  int64_t pool_stride;
+  const int32_t* cand_blocks;
+  const int32_t* n_cand_blocks;
+  const int64_t* n_vis;
+  int block, max_cand_blocks;
+};
+
 static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes, const uint8_t* kv_scales,
-                       int64_t seq_cap, int n_seq, const int32_t* q_seq, const int32_t* idx, const uint64_t* cand_keys,
-                       int cand_per_q, int32_t* idx_out, int32_t* count_out, int k, uint8_t* swa, int64_t swa_cap,
+                       int64_t seq_cap, int n_seq, const int32_t* q_seq, const int32_t* idx, const AttnSel& sel,
+                       int32_t* idx_out, int32_t* count_out, int k, uint8_t* swa, int64_t swa_cap,
                        const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
                        const void* new_win, int new_win_dtype, int window, float sm_scale, void* out, int out_dtype,
                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !kv_codes || !kv_scales || !q_seq || !swa || !swa_base || !q_pos || !replay_start || !out)
     return CSA2_ERR_NULL;
-  const bool select = cand_keys != nullptr;
+  const bool select = sel.mode != 0;
   if (!select && k > 0 && !idx) return CSA2_ERR_NULL;
   if (n_q < 0 || n_heads < kHG || n_heads > 256 || n_heads % kHG || dim != kD || seq_cap < 0 ||
       seq_cap > CSA2_MAX_ATTN_ENTRIES || n_seq < 1 || k < 0 || k > CSA2_MAX_TOPK || window < 1 ||
       window > CSA2_MAX_WINDOW || swa_cap < window || swa_cap > CSA2_MAX_WINDOW_ROWS)
     return CSA2_ERR_SHAPE;
-  if (select && (k < 1 || cand_per_q < 1 || cand_per_q > kSelMax)) return CSA2_ERR_SHAPE;
+  if (sel.mode == 1 && (k < 1 || sel.cand_per_q < 1 || sel.cand_per_q > kSelMax)) return CSA2_ERR_SHAPE;
+  if (sel.mode == 2 && (k < 1 || sel.block < 1 || sel.block > 64 || sel.max_cand_blocks < 1 ||
+                        (int64_t)sel.max_cand_blocks * sel.block > kPoolMax ||
+                        sel.pool_stride < (int64_t)sel.max_cand_blocks * sel.block))
+    return CSA2_ERR_SHAPE;
   if (out_dtype != CSA2_DT_F32 && out_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
   if (new_win && new_win_dtype != CSA2_DT_F32 && new_win_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(kv_codes) || !aligned16(swa) || !aligned16(out) || ((uintptr_t)kv_scales & 7))
@@ -746,8 +809,15 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
   a.n_tiles = p.n_tiles;
   a.main_tiles = p.main_tiles;
   a.head_groups = p.head_groups;
-  a.cand_keys = cand_keys;
-  a.cand_per_q = cand_per_q;
+  a.cand_keys = sel.cand_keys;
+  a.cand_per_q = sel.cand_per_q;
+  a.pool_scores = sel.pool_scores;
+  a.pool_stride = sel.pool_stride;
+  a.cand_blocks = sel.cand_blocks;
+  a.n_cand_blocks = sel.n_cand_blocks;
+  a.n_vis = sel.n_vis;
+  a.block = sel.block;
+  a.max_cand_blocks = sel.max_cand_blocks;
   a.idx_out = idx_out;
   a.count_out = count_out;
   a.new_win = new_win;
@@ -760,11 +830,14 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
     a.ws_ml = a.ws_o + (size_t)p.nsplit * n_q * n_heads * kD;
   }
   hipStream_t st = (hipStream_t)stream;
-  if (select)
-    hipLaunchKernelGGL(k_attn<true>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
+  if (sel.mode == 2)
+    hipLaunchKernelGGL(k_attn<2>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
+                       a.replay_start, a.swa_base);
+  else if (sel.mode == 1)
+    hipLaunchKernelGGL(k_attn<1>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
                        a.replay_start, a.swa_base);
   else
-    hipLaunchKernelGGL(k_attn<false>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
+    hipLaunchKernelGGL(k_attn<0>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
                        a.replay_start, a.swa_base);
   int rc = csa2_check_launch();
   if (rc != CSA2_OK || p.nsplit == 1) return rc;
@@ -778,9 +851,10 @@ extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, co
                                 const int64_t* q_pos, const int64_t* replay_start, const void* new_win,
                                 int new_win_dtype, int window, float sm_scale, void* out, int out_dtype, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, idx, nullptr, 0, nullptr,
-                     nullptr, k, swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window,
-                     sm_scale, out, out_dtype, lse, workspace, workspace_bytes, stream);
+  AttnSel sel = {};
+  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, idx, sel, nullptr, nullptr, k,
+                     swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window, sm_scale, out,
+                     out_dtype, lse, workspace, workspace_bytes, stream);
 }
 
 extern "C" int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
@@ -791,7 +865,35 @@ extern "C" int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int di
                                      int new_win_dtype, int window, float sm_scale, void* out, int out_dtype,
                                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (!cand_keys || !idx_out || !count_out) return CSA2_ERR_NULL;
-  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, nullptr, cand_keys, cand_per_q,
-                     idx_out, count_out, k, swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype,
-                     window, sm_scale, out, out_dtype, lse, workspace, workspace_bytes, stream);
+  AttnSel sel = {};
+  sel.mode = 1;
+  sel.cand_keys = cand_keys;
+  sel.cand_per_q = cand_per_q;
+  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, nullptr, sel, idx_out,
+                     count_out, k, swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window,
+                     sm_scale, out, out_dtype, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" int csa2_sparse_attn_pool_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
+                                          const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                                          const float* scores, int64_t scores_stride, const int64_t* n_vis,
+                                          const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                                          int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
+                                          uint8_t* swa, int64_t swa_cap, const int64_t* swa_base,
+                                          const int64_t* q_pos, const int64_t* replay_start, const void* new_win,
+                                          int new_win_dtype, int window, float sm_scale, void* out, int out_dtype,
+                                          float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!scores || !n_vis || !cand_blocks || !n_cand_blocks || !idx_out || !count_out) return CSA2_ERR_NULL;
+  AttnSel sel = {};
+  sel.mode = 2;
+  sel.pool_scores = scores;
+  sel.pool_stride = scores_stride;
+  sel.cand_blocks = cand_blocks;
+  sel.n_cand_blocks = n_cand_blocks;
+  sel.n_vis = n_vis;
+  sel.block = block;
+  sel.max_cand_blocks = max_cand_blocks;
+  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, nullptr, sel, idx_out,
+                     count_out, k, swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window,
+                     sm_scale, out, out_dtype, lse, workspace, workspace_bytes, stream);
 }

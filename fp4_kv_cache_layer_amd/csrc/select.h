@@ -79,19 +79,28 @@ __device__ __forceinline__ uint32_t dpp_prefix_sum(uint32_t v) {
 // to them follows the call's first barrier).  Each wave counts into kTkCopies interleaved
 // copies of its 256 bins (word bin*kTkCopies + lane%kTkCopies), so lanes that hit the same
 // bin land on different LDS banks: the digits of a segment's best keys bunch into few bins,
-// and same-address atomics would serialise.
+// and same-address atomics would serialise.  With more than four waves the selection also
+// needs `scratch`: (kThreads / 256) * 256 + kWaves * kEpt words of LDS apart from `hist`
+// (the two-stage histogram sums and the compaction counts); up to four waves it uses small
+// static arrays of its own.
 constexpr int kTkCopies = 4;
 constexpr int kTkHistWords = 2 * kTkWaves * 256 * kTkCopies;
 
 template <int kThreads, int kEpt, bool kFinal>
 __device__ __forceinline__ void select_block(uint64_t (&key)[kEpt], int K, uint32_t* hist,
                                              uint64_t* __restrict__ keys_out, int32_t* __restrict__ idx_out,
-                                             int32_t* __restrict__ count_out) {
+                                             int32_t* __restrict__ count_out, uint32_t* scratch = nullptr) {
   constexpr int kWaves = kThreads / 64;
   static_assert(kEpt <= 64 && kThreads % 64 == 0, "one lane per slot in the compaction scan");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  __shared__ uint32_t cnt[kWaves][kEpt];
+  uint32_t (*cnt)[kEpt];
+  if constexpr (kWaves <= 4) {
+    __shared__ uint32_t cnt_s[kWaves][kEpt];
+    cnt = cnt_s;
+  } else {
+    cnt = reinterpret_cast<uint32_t(*)[kEpt]>(scratch + (kWaves / 4) * 256);
+  }
   __shared__ uint32_t red[5][kWaves];
 
   // ---- count (ballots) and the range of the high (score) words (DPP reductions) ----
@@ -179,7 +188,7 @@ __device__ __forceinline__ void select_block(uint64_t (&key)[kEpt], int K, uint3
         // the groups' sums.
         static_assert(kWaves % 4 == 0, "waves in groups of four");
         constexpr int kGroups = kWaves / 4;
-        __shared__ __attribute__((aligned(16))) uint32_t part[kGroups][256];
+        uint32_t (*part)[256] = reinterpret_cast<uint32_t(*)[256]>(scratch);
         {
           const int b = tid & 255, g = tid >> 8;
           uint32_t sum = 0u;

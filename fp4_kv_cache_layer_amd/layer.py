@@ -31,7 +31,7 @@ INDEX_FORMATS = {"mxfp4": (C.FMT_MXFP4, 32), "nvfp4": (C.FMT_NVFP4, 16)}
 
 
 def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp4",
-               attn_select: bool = False) -> list:
+               attn_select: bool = False, pool_select=None) -> list:
     """Checks a layer group's mode sequence and returns the calls each layer makes.
 
     [W] "CSA2：跨层复用，能借就不自己算" and Figure 4: a Reindex layer re-scores the KV of the
@@ -47,7 +47,9 @@ def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp
     i.e. up to 131,072 entries at k = 512): Full and Reindex layers without a pool keep
     only the first Top-K level in the scoring call (csa2_index_segments) and finish the
     selection inside their attention call (csa2_sparse_attn_topk), which also writes the
-    index set for the Reuse layers."""
+    index set for the Reuse layers; Reindex layers inside the pool write the pool's slot
+    scores (csa2_index_score) and select inside their attention call
+    (csa2_sparse_attn_pool_topk)."""
     if index_fmt not in INDEX_FORMATS:
         raise ValueError(f"unknown indexer format {index_fmt!r}")
     if index_fmt != "mxfp4" and group > 1:
@@ -71,6 +73,8 @@ def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp
             calls = ["quantize_index_q", "score_grouped", "select", "attend"]
         elif attn_select and fused and m in ("full", "reindex"):
             calls = ["quantize_index_q", "index_segments", "attend_topk"]
+        elif (attn_select if pool_select is None else pool_select) and fused and group == 1 and m == "reindex_pool":
+            calls = ["quantize_index_q", "score_pool", "attend_pool_topk"]
         elif fused:
             calls = ["quantize_index_q", "index_topk_in_pool" if m == "reindex_pool" else "index_topk", "attend"]
         else:
@@ -124,6 +128,8 @@ class Csa2Step:
         plan_group(["full"], fused, group, index_fmt)   # validates the combination
         n_cand = C.csa2_segment_keys(seq_cap, k)
         fits = fused and group == 1 and 1 <= n_cand <= 8192
+        # inside a pool the attention call selects from at most 16,384 slots
+        self.pool_select = bool(attn_select) and fused and group == 1 and max_blocks * block <= 16384
         self.attn_select = bool(attn_select) and fits
         self.index_fmt = index_fmt
         self.idx_qfmt, self.idx_group = INDEX_FORMATS[index_fmt]
@@ -216,6 +222,17 @@ class Csa2Step:
                                        self.window, self.sm_scale, self.out if out is None else out,
                                        self.lse if lse is None else lse, self.ws_attn, new_win=new_win, _bind=bind)
 
+    def attend_pool_topk(self, caches: Caches, layer: int, q_attn, q_seq, n_vis, q_pos, replay_start, out=None,
+                         lse=None, bind=False, new_win=None):
+        """attention that first selects the Top-K from the pool's slot scores (score with
+        in_pool=True before) and writes it to the step's index set."""
+        return C.csa2_sparse_attn_pool_topk(q_attn, caches.kv_codes, caches.kv_scales, q_seq, self.scores, n_vis,
+                                            self.pool, self.pool_count, self.block, self.k, self.idx, self.count,
+                                            caches.swa[layer], caches.swa_base, q_pos, replay_start, self.window,
+                                            self.sm_scale, self.out if out is None else out,
+                                            self.lse if lse is None else lse, self.ws_attn, new_win=new_win,
+                                            _bind=bind)
+
     def _score_select(self, caches, w, q_seq, n_vis, in_pool, bind):
         if self.fused:
             return [self.index_topk(caches, w, q_seq, n_vis, in_pool, bind)]
@@ -241,7 +258,8 @@ class Csa2Step:
         with its own window cache caches.swa[i].  outs/lses: optional per-layer outputs
         (default: the step's own buffers, overwritten by each layer).  With bind=True returns
         the group's calls as one flat list of callables."""
-        plan = plan_group(modes, self.fused, self.group, self.index_fmt, self.attn_select)
+        plan = plan_group(modes, self.fused, self.group, self.index_fmt, self.attn_select,
+                          pool_select=self.pool_select)
         calls = []
         for i, (m, names) in enumerate(zip(modes, plan)):
             q_index, w, q_attn = inputs[i]
@@ -266,6 +284,8 @@ class Csa2Step:
                     c = self.index_segments(caches, w, q_seq, n_vis, bind)
                 elif name == "attend_topk":
                     c = self.attend_topk(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind)
+                elif name == "attend_pool_topk":
+                    c = self.attend_pool_topk(caches, i, q_attn, q_seq, n_vis, q_pos, replay_start, out, lse, bind)
                 else:
                     c = self.attend(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind)
                 calls.append(c)
@@ -298,6 +318,10 @@ class Csa2Step:
         if self.attn_select and not in_pool:
             calls = [self.quantize_index_q(q_index_f32, bind), self.index_segments(caches, w, q_seq, n_vis, bind),
                      self.attend_topk(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
+            return self._seq(calls, bind)
+        if self.pool_select and in_pool:
+            calls = [self.quantize_index_q(q_index_f32, bind), self.score(caches, w, q_seq, n_vis, True, bind),
+                     self.attend_pool_topk(caches, layer, q_attn, q_seq, n_vis, q_pos, replay_start, out, lse, bind)]
             return self._seq(calls, bind)
         calls = [self.quantize_index_q(q_index_f32, bind), *self._score_select(caches, w, q_seq, n_vis, in_pool, bind),
                  self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]

@@ -426,6 +426,36 @@ int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const ui
                           void* out, int out_dtype, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * csa2_sparse_attn_pool_topk -- csa2_sparse_attn for a Reindex layer inside the pool, with
+ * the index set selected in the same call from the pool's slot scores: the Top-k of the
+ * valid slots (score descending, position ascending), as ascending positions, -1 padded --
+ * exactly what csa2_topk returns for the same scores and pool -- is written to idx_out /
+ * count_out and attended over.  [W] "分层稀疏索引器" (later layers choose their Top-K inside
+ * the pool), "CSA2：跨层复用，能借就不自己算".
+ *
+ * Arguments are those of csa2_sparse_attn, with idx replaced by
+ *   scores, scores_stride   the slot scores csa2_index_score writes with the same pool
+ *                           ([n_q, scores_stride] f32, stride >= max_cand_blocks*block)
+ *   n_vis, cand_blocks, n_cand_blocks, block, max_cand_blocks   as csa2_topk takes them;
+ *                           max_cand_blocks*block <= 16,384 (the pool's 2,048 x 8 slots)
+ *   k (1..2048), idx_out [n_q, k] int32, count_out [n_q] int32
+ * Every workgroup of a query selects (512 threads x 32 slots, histograms in the V buffers'
+ * LDS), so the pool's Top-K needs no launches of its own.
+ * Errors: those of csa2_sparse_attn; CSA2_ERR_NULL (scores, n_vis, cand_blocks,
+ * n_cand_blocks, idx_out, count_out); CSA2_ERR_SHAPE (block, max_cand_blocks, k, stride).
+ */
+int csa2_sparse_attn_pool_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
+                               const uint8_t* kv_scales, int64_t seq_cap, int n_seq,
+                               const int32_t* q_seq, const float* scores, int64_t scores_stride,
+                               const int64_t* n_vis, const int32_t* cand_blocks,
+                               const int32_t* n_cand_blocks, int block, int max_cand_blocks, int k,
+                               int32_t* idx_out, int32_t* count_out, uint8_t* swa, int64_t swa_cap,
+                               const int64_t* swa_base, const int64_t* q_pos,
+                               const int64_t* replay_start, const void* new_win, int new_win_dtype,
+                               int window, float sm_scale, void* out, int out_dtype, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -112,3 +112,23 @@ def test_select_in_attention_validation(L):
     a = list(att); a[11] = 0                        # k = 0
     assert L.csa2_sparse_attn_topk(*a) == -2
     assert L.csa2_sparse_attn_topk(*att) == -5      # split over workgroups needs a workspace
+
+
+def test_pool_select_in_attention_validation(L):
+    """csa2_sparse_attn_pool_topk rejects bad pools on the host."""
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    fake = vp(0x1000)   # never dereferenced
+    L.csa2_sparse_attn_pool_topk.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i64, vp, vp, vp, i32, i32,
+                                             i32, vp, vp, vp, i64, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, i32,
+                                             vp, vp, ctypes.c_size_t, vp]
+    att = [fake, 4, 64, 512, fake, fake, 100, 1, fake, fake, 16384, fake, fake, fake, 8, 2048, 512, fake, fake, fake,
+           128, fake, fake, fake, None, 0, 128, 0.05, fake, 0, None, None, 0, None]
+    a = list(att); a[9] = None                      # no scores
+    assert L.csa2_sparse_attn_pool_topk(*a) == -1
+    a = list(att); a[15] = 4096                     # more slots than one selection holds
+    assert L.csa2_sparse_attn_pool_topk(*a) == -2
+    a = list(att); a[10] = 1000                     # score stride below the pool's slots
+    assert L.csa2_sparse_attn_pool_topk(*a) == -2
+    a = list(att); a[14] = 0                        # block
+    assert L.csa2_sparse_attn_pool_topk(*a) == -2
+    assert L.csa2_sparse_attn_pool_topk(*att) == -5  # split over workgroups needs a workspace

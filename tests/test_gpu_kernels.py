@@ -435,6 +435,55 @@ def test_index_topk_fused_pool(C, fmt):
         G.topk_accept(gi[qi], int(gc[qi]), pos, ref, 512)
 
 
+@pytest.mark.parametrize("k,mb", [(512, 2048), (7, 2048), (512, 300)])
+def test_pool_select_in_attention(C, k, mb):
+    """csa2_sparse_attn_pool_topk (the Top-K selected inside the attention call from the
+    pool's slot scores) returns csa2_topk's index set over the same scores and pool bit for
+    bit, and attention outputs identical to csa2_sparse_attn over it; full pools, partial
+    ones, invalid block ids, blocks past n_vis and an empty pool."""
+    _say("pool select in attention", k, mb)
+    case = _score_case(71 + k, 4, 30000, [30000, 12000, 333, 5000], 16)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_idx, w, qa = case.gpu_query_inputs(0)
+    q_seq, n_vis_t, q_pos, rs = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap, k=k, max_blocks=mb)
+    assert st.pool_select
+    rng = np.random.default_rng(k + mb)
+    blocks = np.full((wl.n_q, mb), -1, np.int32)
+    ncb = np.array([mb, min(mb * 3 // 4, 1500), 45, 0], np.int32)   # at most the blocks a query has (+10)
+    for qi in range(wl.n_q):
+        nb = -(-int(wl.n_vis[qi]) // 8)
+        if ncb[qi]:
+            blocks[qi, :ncb[qi]] = np.sort(rng.choice(nb + 10, size=ncb[qi], replace=False))
+    blocks[0, 100] = -1
+    st.pool.copy_(torch.from_numpy(blocks))
+    st.pool_count.copy_(torch.from_numpy(ncb))
+    st.quantize_index_q(q_idx)
+    st.score(caches, w, q_seq, n_vis_t, in_pool=True)
+    idx_a = torch.empty(wl.n_q, k, dtype=torch.int32, device="cuda")
+    cnt_a = torch.empty(wl.n_q, dtype=torch.int32, device="cuda")
+    C.csa2_topk(st.scores, n_vis_t, st.seq_cap, k, idx_a, cnt_a, None, st.pool, st.pool_count, 8)
+    sm = 1.0 / math.sqrt(512)
+    out_a = torch.empty(wl.n_q, 16, 512, dtype=torch.float32, device="cuda")
+    lse_a = torch.empty(wl.n_q, 16, dtype=torch.float32, device="cuda")
+    C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, idx_a, caches.swa[0], caches.swa_base, q_pos, rs,
+                       128, sm, out_a, lse_a)
+    for rep in range(2):
+        idx_b = torch.full((wl.n_q, k), 77, dtype=torch.int32, device="cuda")
+        cnt_b = torch.full((wl.n_q,), 77, dtype=torch.int32, device="cuda")
+        out_b = torch.empty_like(out_a)
+        lse_b = torch.empty_like(lse_a)
+        C.csa2_sparse_attn_pool_topk(qa, caches.kv_codes, caches.kv_scales, q_seq, st.scores, n_vis_t, st.pool,
+                                     st.pool_count, 8, k, idx_b, cnt_b, caches.swa[0], caches.swa_base, q_pos, rs,
+                                     128, sm, out_b, lse_b)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_b, idx_a) and torch.equal(cnt_b, cnt_a), rep
+        assert torch.equal(out_b, out_a) and torch.equal(lse_b, lse_a), rep
+    assert cnt_a[3].item() == 0 and torch.all(idx_a[3] == -1)
+
+
 @pytest.mark.parametrize("n,k", [(1, 512), (511, 512), (512, 512), (513, 512), (8192, 512), (8193, 512),
                                  (20000, 7), (70001, 512), (200000, 2048), (9000, 1), (300000, 512)])
 def test_topk_exact_on_same_scores(C, n, k):

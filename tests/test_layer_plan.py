@@ -76,14 +76,19 @@ def test_invalid_groups_rejected(modes):
 
 def test_plan_select_in_attention():
     """With attn_select, Full and Reindex layers without a pool score with csa2_index_segments
-    and finish the Top-K in their attention call; pool layers and grouped scoring keep their
-    calls."""
+    and finish the Top-K in their attention call, Reindex layers in the pool write the slot
+    scores and select in their attention call (pool_select, default attn_select); the pool
+    build and grouped scoring keep their calls."""
     plan = plan_group(["full", "reuse", "reindex"], attn_select=True)
     assert plan[0] == ["quantize_index_q", "index_segments", "attend_topk"]
     assert plan[1] == ["attend"]
     assert plan[2] == ["quantize_index_q", "index_segments", "attend_topk"]
     plan = plan_group(["full_pool", "reuse", "reindex_pool"], attn_select=True)
     assert plan[0] == ["quantize_index_q", "index_topk_pool", "attend"]
+    assert plan[2] == ["quantize_index_q", "score_pool", "attend_pool_topk"]
+    plan = plan_group(["full_pool", "reuse", "reindex_pool"], attn_select=False, pool_select=True)
+    assert plan[2] == ["quantize_index_q", "score_pool", "attend_pool_topk"]
+    plan = plan_group(["full_pool", "reuse", "reindex_pool"], attn_select=True, pool_select=False)
     assert plan[2] == ["quantize_index_q", "index_topk_in_pool", "attend"]
     assert plan_group(["full"], group=4, attn_select=True)[0] == ["quantize_index_q", "score_grouped", "select",
                                                                    "attend"]
