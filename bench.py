@@ -534,7 +534,8 @@ def main():
                       "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS, "mfma_frac": round(at_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                       "bytes_per_launch": attn_bytes(wl), "gb_per_s": round(at_gbs, 1),
                       "hbm_frac": round(at_gbs / HBM_PEAK_GBS, 4),
-                      "timing": "HIP events around graph replays of 8 back-to-back csa2_sparse_attn calls"},
+                      "timing": "HIP events around graph replays of 8 back-to-back csa2_sparse_attn_topk calls "
+                                "(the selection of the last Top-K level included)"},
     }
     if not args.no_modes:
         modes = {}
