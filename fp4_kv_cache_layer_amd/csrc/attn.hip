@@ -37,6 +37,11 @@
 // on the same XCD (dispatch is round-robin over the 8 XCDs) and share its L2 for the
 // gathered rows.  When a batch has too few queries to fill the GPU, the key list is split
 // over workgroups and a combine kernel merges the partial (O, m, l).
+//
+// Two pieces of neighbouring work can run in the kernel's prologue, each saving a launch:
+// the last Top-K level (the index set selected from the first level's survivors or from
+// the pool's slot scores; see k_attn's kSel) and, in single-token decode, the append of the
+// row's own window entry (new_win).
 #include "select.h"
 
 namespace csa2 {
