@@ -25,13 +25,15 @@
 //     (Q held in registers in the same channel order);
 //   * writes the same fp16 values as its own V half-tile in LDS (row stride 528 B, double
 //     buffered);
-//   * adds its partner's partial S^T, exchanged through LDS with the one workgroup barrier
-//     of the step, so both waves hold the same S^T and run the same online softmax;
+//   * adds its partner's partial S^T, exchanged through LDS with a flag handshake between
+//     the two waves (the step's only synchronisation; the four key streams never wait for
+//     one another inside the loop), so both waves hold the same S^T and run the same
+//     online softmax;
 //   * turns S^T into P^T in fp16: the accumulator layout of the QK MFMA (lane: head l%16,
 //     keys 4(l/16)..+3) is exactly the B-operand layout of V_MFMA_F32_16X16X16_F16, so P
 //     needs no shuffle; and accumulates O^T += V^T P^T over its 256 channels, V^T read from
 //     its V half-tile through DS_READ_B64_TR_B16 (each lane receives one channel of 4 keys).
-// Steps are software-pipelined: after the barrier of step i, P.V of tile i and the softmax
+// Steps are software-pipelined: after the exchange of step i, P.V of tile i and the softmax
 // of tile i+1 are independent work.  At the end the four pairs merge (O, m, l) with the
 // log-sum-exp rule through LDS.  The workgroups of one query are numbered so that they land
 // on the same XCD (dispatch is round-robin over the 8 XCDs) and share its L2 for the
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_cap * kD;
   // ---- this pair's tiles: window tiles first (their rows need no index), then main tiles;
   // pair p takes positions p, p+4, ... of that order.  Every wave runs the same number of
-  // steps (one workgroup barrier each) and masks the steps past its pair's end ----
+  // steps (one exchange with its partner each) and masks the steps past its pair's end ----
   const int span = tile_hi - tile_lo;
   const int n_win = span - n_main;
   const int n_steps = (span + kPairs - 1) / kPairs;
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   auto lds_order = [] { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); };
 
   // ---- software pipeline.  Step i dequantises tile i+1 into V buffer (i+1) % 2, forms its
-  // partial S and exchanges it (the one barrier of the step); after the barrier P.V of
+  // partial S and exchanges it with its partner (the step's one wait); after that P.V of
   // tile i (buffer i % 2) and the softmax of tile i+1 are independent work for the matrix
   // cores and the vector units.  The raw bytes of tiles i+2 .. i+4 are in flight meanwhile:
   // ring slot (i+1) % 3 is refilled with tile i+4 as soon as tile i+1 has left it ----
