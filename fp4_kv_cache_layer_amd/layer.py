@@ -252,12 +252,14 @@ class Csa2Step:
                                   new_win=new_win, _bind=bind)
 
     def run_group(self, caches: Caches, modes, inputs, q_seq, n_vis, q_pos, replay_start, outs=None, lses=None,
-                  bind=False):
+                  bind=False, new_wins=None):
         """Runs the layers of a group in order.  inputs[i] = (indexer Q f32 [n_q, H_I, d] or
         None for Reuse, w [n_q, H_I] or None, attention Q bf16 [n_q, H, D]); layer i attends
         with its own window cache caches.swa[i].  outs/lses: optional per-layer outputs
-        (default: the step's own buffers, overwritten by each layer).  With bind=True returns
-        the group's calls as one flat list of callables."""
+        (default: the step's own buffers, overwritten by each layer).  new_wins: optional
+        per-layer window latents of each row's own token, appended by the layer's attention
+        call (see attend).  With bind=True returns the group's calls as one flat list of
+        callables."""
         plan = plan_group(modes, self.fused, self.group, self.index_fmt, self.attn_select,
                           pool_select=self.pool_select)
         calls = []
@@ -265,6 +267,7 @@ class Csa2Step:
             q_index, w, q_attn = inputs[i]
             out = None if outs is None else outs[i]
             lse = None if lses is None else lses[i]
+            nw = None if new_wins is None else new_wins[i]
             for name in names:
                 if name == "quantize_index_q":
                     c = self.quantize_index_q(q_index, bind)
@@ -283,11 +286,12 @@ class Csa2Step:
                 elif name == "index_segments":
                     c = self.index_segments(caches, w, q_seq, n_vis, bind)
                 elif name == "attend_topk":
-                    c = self.attend_topk(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind)
+                    c = self.attend_topk(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind, new_win=nw)
                 elif name == "attend_pool_topk":
-                    c = self.attend_pool_topk(caches, i, q_attn, q_seq, n_vis, q_pos, replay_start, out, lse, bind)
+                    c = self.attend_pool_topk(caches, i, q_attn, q_seq, n_vis, q_pos, replay_start, out, lse, bind,
+                                              new_win=nw)
                 else:
-                    c = self.attend(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind)
+                    c = self.attend(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind, new_win=nw)
                 calls.append(c)
         return calls if bind else None
 

@@ -186,17 +186,30 @@ def oracle_index_cache(wl: Workload, seq: int, index_fmt: str = "mxfp4") -> O.Pa
     return O.PackedCaches(None, None, ik_c, ik_s, index_fmt=index_fmt)
 
 
-def run_group_snapshots(case: Case, step, caches, window_appends: bool = False):
+def run_group_snapshots(case: Case, step, caches, window_appends: bool = False, fused_window: bool = False):
     """Runs the workload's layer group on the GPU layer by layer and returns per-layer
     snapshots: idx, count (the set each layer attended over), out, lse, and the pool.
     window_appends: before its calls, each layer writes the FP8 window entry of every query
-    row into its own ring (what a layer step does when the window state is not cached)."""
+    row into its own ring (what a layer step does when the window state is not cached).
+    fused_window: each row's own window entry is first zeroed in every layer's ring, and the
+    layer's attention call appends it (new_win), as the single-token decode step runs."""
     from fp4_kv_cache_layer_amd.layer import plan_group
     wl = case.wl
     q_seq, n_vis, q_pos, rs = case.gpu_meta()
     modes = list(wl.layers)
     inputs = [case.gpu_query_inputs(L) for L in range(len(modes))]
-    calls = step.run_group(caches, modes, inputs, q_seq, n_vis, q_pos, rs, bind=True)
+    new_wins = None
+    if fused_window:
+        assert np.unique(wl.q_seq).size == wl.n_q, "the append inside attention needs distinct sequences"
+        rows = torch.from_numpy(np.mod(wl.q_pos - wl.swa_base, wl.swa_cap)).long().cuda()
+        seqs = torch.from_numpy(wl.q_seq.astype(np.int64)).cuda()
+        new_wins = []
+        for L in range(len(modes)):
+            caches.swa[L][seqs, rows] = 0
+            lat = np.stack([wl.swa_latents(L, int(b), int(t), 1)[0] for b, t in zip(wl.q_seq, wl.q_pos)])
+            new_wins.append(torch.from_numpy(lat.astype(np.float32)).cuda())
+        torch.cuda.synchronize()
+    calls = step.run_group(caches, modes, inputs, q_seq, n_vis, q_pos, rs, bind=True, new_wins=new_wins)
     snaps, at = [], 0
     for L, names in enumerate(plan_group(modes, step.fused, step.group, step.index_fmt)):
         if window_appends:

@@ -30,18 +30,23 @@ def C():
 @pytest.mark.parametrize("name,samples,fused,attn_select", [
     ("c2", (0, 63), True, False), ("c2", (0, 63), True, True), ("c3", (0, 13, 31), True, False),
     ("c3", (0, 13, 31), False, False), ("c3", (0, 13, 31), True, True), ("c4", (0, 5), True, False),
-    ("c4", (0, 5), False, False)])
+    ("c4", (0, 5), False, False), ("c4", (0, 5), True, True)])
 def test_layer_group_full_size(C, name, samples, fused, attn_select):
     """Every layer of a group at full size against the oracle on sampled queries: fused
-    scoring + selection, two calls, and the last Top-K level inside the attention call."""
+    scoring + selection, two calls, and the last Top-K level inside the attention call.  The
+    cases with the selection inside attention run as the single-token decode step is
+    benchmarked: each row's own window entry is appended by the attention call (its ring
+    row zeroed beforehand); the others attend over a prefilled ring."""
     _say("layer group", name, "fused" if fused else "two-call", "select in attention" if attn_select else "")
     from fp4_kv_cache_layer_amd.layer import Csa2Step
     wl = workloads.config(name)
     case = G.Case(wl, swa_layers=range(len(wl.layers)))
     caches = case.gpu_caches()
     step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, fused=fused, attn_select=attn_select)
-    assert step.attn_select == attn_select
-    snaps = G.run_group_snapshots(case, step, caches)
+    # at 1M the segment survivors exceed one selection, so only the pool's Top-K (Reindex
+    # inside the pool) moves into the attention call
+    assert (step.attn_select or step.pool_select) == attn_select
+    snaps = G.run_group_snapshots(case, step, caches, fused_window=attn_select)
     for qi in samples:
         _say("  oracle query", qi)
         G.check_group_query(case, caches, snaps, qi)
@@ -74,15 +79,16 @@ def test_nvfp4_indexer_full_size(C, name, samples):
 @pytest.mark.parametrize("name,samples", [("dec_128k", (0, 31)), ("dec_1m", (0, 7))])
 def test_decoder_step_full_size(C, name, samples):
     """The whole decoder step: 20 CSA2 layers (Full + pool, 3 Reuse, 4 x (Reindex in the pool,
-    3 Reuse)) at 128K and 1M, through the layer driver as the benchmark runs it, with oracle
-    parity of every layer on sampled query rows."""
+    3 Reuse)) at 128K and 1M, through the layer driver as the benchmark runs it (each layer's
+    attention call appending the row's own window entry), with oracle parity of every layer
+    on sampled query rows."""
     _say("decoder step", name)
     from fp4_kv_cache_layer_amd.layer import Csa2Step
     wl = workloads.config(name)
     case = G.Case(wl, swa_layers=range(len(wl.layers)))
     caches = case.gpu_caches()
     step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap)
-    snaps = G.run_group_snapshots(case, step, caches)
+    snaps = G.run_group_snapshots(case, step, caches, fused_window=True)
     for qi in samples:
         _say("  oracle query", qi)
         G.check_group_query(case, caches, snaps, qi)
