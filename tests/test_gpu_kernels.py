@@ -597,6 +597,44 @@ def test_sparse_attn_parity(C, heads, out_dt):
         assert np.abs(gl[qi] - ref_lse).max() <= 1e-3
 
 
+@pytest.mark.parametrize("window,n_q,heads", [(1, 64, 64), (40, 64, 64), (200, 64, 64), (40, 6, 16), (200, 6, 16)])
+def test_sparse_attn_window_sizes(C, window, n_q, heads):
+    """Windows other than 128 keys: a single key, a ragged number of tiles too few for the
+    early window gathers, and more than 128 keys (ring of 256 rows); 64 queries x 64 heads run
+    without a key split, 6 queries x 16 heads split the key list over workgroups."""
+    _say("sparse_attn window", window, n_q, heads)
+    rng = np.random.default_rng(window * 100 + n_q)
+    t = [int(x) for x in rng.integers(0, 1200, size=n_q)]
+    t[0] = 1199
+    s = []
+    for i, ti in enumerate(t):   # no replay, a replay start inside the window, a start at t
+        s.append(0 if i % 3 == 0 else (max(0, ti - window // 2) if i % 3 == 1 else ti))
+    case = _attn_case(11 + window, n_q, 1200, heads, t, s, swa_cap=256)   # one sequence per query
+    wl = case.wl
+    caches = case.gpu_caches()
+    _, _, qa = case.gpu_query_inputs(0)
+    q_seq, _, q_pos, rs = case.gpu_meta()
+    k = 512
+    idx = np.full((n_q, k), -1, np.int32)
+    counts = [int(c) for c in rng.integers(0, k + 1, size=n_q)]
+    counts[0] = k
+    for qi in range(n_q):
+        idx[qi, :counts[qi]] = np.sort(rng.choice(1200, size=counts[qi], replace=False))
+    out = torch.empty(n_q, heads, 512, dtype=torch.float32, device="cuda")
+    lse = torch.empty(n_q, heads, dtype=torch.float32, device="cuda")
+    C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, torch.from_numpy(idx).cuda(), caches.swa[0],
+                       caches.swa_base, q_pos, rs, window, 1.0 / math.sqrt(512), out, lse)
+    torch.cuda.synchronize()
+    go, gl = out.cpu().numpy(), lse.cpu().numpy()
+    for qi in range(n_q):
+        oc = case.oracle_caches(int(wl.q_seq[qi]))
+        _, _, _, qa_np = case.oracle_query(0, qi)
+        ref, ref_lse = O.sparse_attention(qa_np, oc.main_rows(idx[qi, :counts[qi]]),
+                                          oc.swa_rows(0, O.swa_positions(t[qi], s[qi], window)), 1 / math.sqrt(512))
+        G.attn_close(go[qi], ref, 2e-3)
+        assert np.abs(gl[qi] - ref_lse).max() <= 1e-3
+
+
 @pytest.mark.parametrize("n_q", [6, 32])
 def test_sparse_attn_split_workspace_reuse(C, n_q):
     """Split key lists (10 splits at 6 queries, 2 at 32): consecutive calls on one
