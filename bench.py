@@ -146,6 +146,8 @@ class LayerBench:
             out["select"] = st.select(self.n_vis, bind=True)
         elif "index_segments" in names:
             out["index_segments"] = st.index_segments(c, w, self.q_seq, self.n_vis, bind=True)
+        elif "score_pool_q" in names:   # pool slot scores from the unquantised Q; Top-K in attention
+            out["score"] = st.score_q(c, q_idx, w, self.q_seq, self.n_vis, in_pool=True, bind=True)
         elif "attend_pool_topk" in names:   # pool slot scores; the Top-K is selected in attention
             out["score"] = st.score(c, w, self.q_seq, self.n_vis, in_pool=True, bind=True)
         elif mode != "reuse":

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         "csa2_index_score_grouped": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp], i32),
         "csa2_index_score": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64, vp],
                              i32),
+        "csa2_index_score_q": ([vp, i32, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64, vp],
+                               i32),
         "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp,
                              sz, vp], i32),
         "csa2_index_topk_workspace_bytes": ([i32, i64, i32, i32], sz),
@@ -232,6 +234,38 @@ def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scor
     n_vis [n_q] int64; scores [n_q, stride] f32; cand_blocks [n_q, max_blocks] int32."""
     return _index_score("csa2_index_score", 32, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
                         cand_blocks, n_cand_blocks, block, _bind)
+
+
+def csa2_index_score_q(q, w, k_codes, k_scales, q_seq, n_vis, scores, cand_blocks=None, n_cand_blocks=None,
+                       block: int = 8, _bind: bool = False):
+    """csa2_index_score with the indexer Q unquantised: q [n_q, H_I, 128] f32 or bf16, quantised
+    to MXFP4 inside the scoring kernel; the other operands as csa2_index_score."""
+    if q.dtype not in (torch.float32, torch.bfloat16) or q.dim() != 3 or not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous CUDA [n_q, H_I, 128] f32/bf16 tensor")
+    n_q, h, d = q.shape
+    _need(w, torch.float32, 2, "w")
+    _need(k_codes, torch.uint8, 3, "k_codes")
+    _need(k_scales, torch.uint8, 3, "k_scales")
+    _need(q_seq, torch.int32, 1, "q_seq")
+    _need(n_vis, torch.int64, 1, "n_vis")
+    n_seq, seq_cap, kh = k_codes.shape
+    if w.shape != (n_q, h) or kh != d // 2 or k_scales.shape != (n_seq, seq_cap, d // 32) or \
+            q_seq.shape[0] != n_q or n_vis.shape[0] != n_q:
+        raise ValueError("index_score_q: inconsistent shapes")
+    max_blocks = 0
+    if cand_blocks is not None:
+        _need(cand_blocks, torch.int32, 2, "cand_blocks")
+        _need(n_cand_blocks, torch.int32, 1, "n_cand_blocks")
+        max_blocks = cand_blocks.shape[1]
+        if cand_blocks.shape[0] != n_q or n_cand_blocks.shape[0] != n_q:
+            raise ValueError("index_score_q: inconsistent pool shapes")
+    _need(scores, torch.float32, 2, "scores")
+    if scores.shape[0] != n_q:
+        raise ValueError("index_score_q: scores rows != n_q")
+    qdt = DT_F32 if q.dtype == torch.float32 else DT_BF16
+    return _run("csa2_index_score_q", (_p(q), qdt, _p(w), n_q, h, d, _p(k_codes), _p(k_scales), seq_cap, n_seq,
+                                       _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks), block, max_blocks,
+                                       _p(scores), scores.stride(0), _stream()), _bind)
 
 
 def csa2_index_score_nvfp4(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,

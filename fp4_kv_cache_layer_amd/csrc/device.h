@@ -69,6 +69,46 @@ __device__ __forceinline__ uint32_t fp8_code_bits(uint32_t b) {
 // fp32 holding a value exactly representable in bf16 -> bf16 bits (truncation is exact)
 __device__ __forceinline__ uint16_t exact_bf16_bits(float f) { return (uint16_t)(__float_as_uint(f) >> 16); }
 
+// E2M1 magnitude code of a/s (a >= 0, s > 0), ties to even, saturating at 6.
+// Midpoints between the E2M1 magnitudes: .25 .75 1.25 1.75 2.5 3.5 5.
+__device__ __forceinline__ uint32_t e2m1_code(float a, float s) {
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    const float t = s * mids[i];
+    // code >= i+1 iff a > t, or a == t and i+1 is even
+    c += (a > t) || (a == t && (i & 1));
+  }
+  return c;
+}
+
+// One MXFP4 group: 32 finite fp32 values (as bits; bf16 inputs widened by a shift) ->
+// E8M0 scale code (returned) and 32 E2M1 codes packed as four words, channel 2i in the low
+// nibble of byte i.  E = floor(log2 amax) - 2 clamped to [-127, 127] (an all-zero group or
+// a subnormal amax gives -127); each magnitude is compared with the E2M1 midpoints times
+// 2^E (exact products) rather than divided.
+__device__ __forceinline__ int mxfp4_group(const uint32_t (&bits)[32], uint32_t (&w)[4]) {
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t ab = bits[i] & 0x7fffffffu;
+    amax_bits = ab > amax_bits ? ab : amax_bits;
+  }
+  const int e_field = (int)(amax_bits >> 23);
+  int E = e_field - 127 - 2;
+  E = (amax_bits == 0 || e_field == 0 || E < -127) ? -127 : E;
+  const int code = amax_bits == 0 ? 0 : E + 127;
+  const float s = ldexpf(1.0f, code - 127);
+  w[0] = w[1] = w[2] = w[3] = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t c = e2m1_code(__uint_as_float(bits[i] & 0x7fffffffu), s) | ((bits[i] >> 28) & 8u);
+    w[i >> 3] |= c << (4 * (i & 7));
+  }
+  return code;
+}
+
 }  // namespace csa2
 
 // Launch-error bookkeeping used by every entry point (defined in abi.hip).

@@ -33,20 +33,6 @@ __device__ __forceinline__ int nvfp4_scale_code(float a) {
   return c;
 }
 
-// E2M1 magnitude code of a/s (a >= 0, s > 0), ties to even, saturating at 6.
-// Midpoints between the E2M1 magnitudes: .25 .75 1.25 1.75 2.5 3.5 5.
-__device__ __forceinline__ uint32_t e2m1_code(float a, float s) {
-  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-  uint32_t c = 0;
-#pragma unroll
-  for (int i = 0; i < 7; ++i) {
-    float t = s * mids[i];
-    // code >= i+1 iff a > t, or a == t and i+1 is even
-    c += (a > t) || (a == t && (i & 1));
-  }
-  return c;
-}
-
 // An empty asm that takes a group's results as inputs: the arithmetic (and the loads it
 // depends on) must then run before the destination check that follows, instead of being
 // moved behind it, where the loads would only be issued once the destination row has
@@ -117,33 +103,10 @@ __device__ __forceinline__ void quant_group_mxfp4(const T* __restrict__ src, int
   int g = (int)(gid % gpr);
   const int64_t d = kMap ? dst_row[r] : r;   // checked at the stores (see above)
   uint32_t bits[32];
-  uint32_t amax_bits = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    bits[i] = load_bits(src, r * dim + g * 32 + i);
-    uint32_t ab = bits[i] & 0x7fffffffu;
-    amax_bits = ab > amax_bits ? ab : amax_bits;
-  }
-  // E = floor(log2 amax) - 2, clamped to [-127, 127]; subnormal amax gives -127
-  int code;
-  int e_field = (int)(amax_bits >> 23);
-  if (amax_bits == 0) code = 0;
-  else if (e_field == 0) code = 0;  // floor(log2 amax) <= -127 -> E clamps to -127
-  else {
-    int E = e_field - 127 - 2;
-    E = E < -127 ? -127 : E;
-    code = E + 127;
-  }
-  int E = code - 127;
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float a = __uint_as_float(bits[i] & 0x7fffffffu);
-    // compare a with mid*2^E instead of a*2^-E with mid; both exact
-    uint32_t mag = e2m1_code(a, ldexpf(1.0f, E));
-    uint32_t c = mag | ((bits[i] >> 28) & 8u);
-    w[i >> 3] |= c << (4 * (i & 7));
-  }
+  for (int i = 0; i < 32; ++i) bits[i] = load_bits(src, r * dim + g * 32 + i);
+  uint32_t w[4];
+  const int code = mxfp4_group(bits, w);
   keep_before_branch(w[0] ^ w[1], w[2] ^ w[3], (uint32_t)code);
   if (d < 0 || d >= dst_rows) return;
   uint4* out = reinterpret_cast<uint4*>(codes + d * (dim / 2) + g * 16);

@@ -40,6 +40,10 @@ static_assert(kScoreThreads == kTkThreads, "the fused kernel hands its registers
 struct ScoreArgs {
   const uint8_t* q_codes;
   const uint8_t* q_scales;
+  // csa2_index_score_q: the indexer Q unquantised ([n_q, n_heads, 128] f32 or bf16),
+  // quantised to MXFP4 by every workgroup for itself
+  const void* q_lat;
+  int q_bf16;
   const float* w;
   int n_heads;
   const uint8_t* k_codes;
@@ -157,7 +161,7 @@ __device__ __forceinline__ float score_tiles_nv(const v8h (&a)[4], const float (
 // Slots and rows are 32-bit (seq_cap <= 2^26, so byte offsets within a sequence fit in 32
 // bits) and the sequence's base pointers are workgroup-uniform, so each load is a scalar
 // base plus one 32-bit vector offset.
-template <bool kPool, bool kNv>
+template <bool kPool, bool kNv, bool kQLat = false>
 struct QueryScorer {
   // scale bytes per entry (and per query head row): one per 32 channels (MXFP4) or per 16
   static constexpr uint32_t kScalesPerRow = kNv ? 8u : 4u;
@@ -199,16 +203,51 @@ struct QueryScorer {
     for (int u = 0; u < 4; ++u) an[u] = v8h{};
     if (row < s.n_heads) {
       const int64_t r = (int64_t)q * s.n_heads + row;
-      const uint4 qa = *reinterpret_cast<const uint4*>(s.q_codes + r * 64 + kb * 16);
-      if (kNv) {
-        const uint32_t qs = *reinterpret_cast<const uint16_t*>(s.q_scales + r * 8 + kb * 2);
-        nv_dequant(qa, qs, an);
+      if constexpr (kQLat) {
+        // this lane's A operand is one whole MXFP4 group (head `row`, channels 32*kb ..
+        // +31): quantise it here, with the same rule as csa2_quantize_kv
+        uint32_t bits[32];
+        if (s.q_bf16) {
+          const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(s.q_lat) + r * 128 + kb * 32);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint4 v = src[u];
+            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              bits[8 * u + 2 * j] = wd[j] << 16;
+              bits[8 * u + 2 * j + 1] = wd[j] & 0xffff0000u;
+            }
+          }
+        } else {
+          const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(s.q_lat) + r * 128 + kb * 32);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const uint4 v = src[u];
+            bits[4 * u] = v.x;
+            bits[4 * u + 1] = v.y;
+            bits[4 * u + 2] = v.z;
+            bits[4 * u + 3] = v.w;
+          }
+        }
+        uint32_t wq[4];
+        a_scale = mxfp4_group(bits, wq);
+        a[0] = (int)wq[0];
+        a[1] = (int)wq[1];
+        a[2] = (int)wq[2];
+        a[3] = (int)wq[3];
       } else {
-        a[0] = (int)qa.x;
-        a[1] = (int)qa.y;
-        a[2] = (int)qa.z;
-        a[3] = (int)qa.w;
-        a_scale = s.q_scales[r * 4 + kb];
+        const uint4 qa = *reinterpret_cast<const uint4*>(s.q_codes + r * 64 + kb * 16);
+        if (kNv) {
+          const uint32_t qs = *reinterpret_cast<const uint16_t*>(s.q_scales + r * 8 + kb * 2);
+          nv_dequant(qa, qs, an);
+        } else {
+          a[0] = (int)qa.x;
+          a[1] = (int)qa.y;
+          a[2] = (int)qa.z;
+          a[3] = (int)qa.w;
+          a_scale = s.q_scales[r * 4 + kb];
+        }
       }
     }
 #pragma unroll
@@ -345,13 +384,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_grouped(ScoreArgs s, in
   }
 }
 
-template <bool kPool, bool kNv>
+template <bool kPool, bool kNv, bool kQLat = false>
 __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
   const int q = blockIdx.x / s.chunks;
   const int chunk = blockIdx.x % s.chunks;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  QueryScorer<kPool, kNv> sc;
+  QueryScorer<kPool, kNv, kQLat> sc;
   if (!sc.init(s, q)) return;
   const int chunk_lo = chunk * s.chunk_len;
   const int write_hi = kPool ? (int)s.n_slots : sc.n_valid;  // pool mode also writes -inf pads
@@ -512,7 +551,8 @@ static ScoreArgs make_args(const uint8_t* q_codes, const uint8_t* q_scales, cons
 // Writes scores[q, slot].  Inside a pool each slot's row comes from a block-id load, so a
 // wave's step is two dependent memory round trips and a workgroup is latency-bound:
 // pool chunks are small (2 steps per wave) to spread the pool over many workgroups.
-static int launch_score(ScoreArgs a, int n_q, float* scores, int64_t scores_stride, bool nv, hipStream_t st) {
+static int launch_score(ScoreArgs a, int n_q, float* scores, int64_t scores_stride, bool nv, hipStream_t st,
+                        bool q_lat = false) {
   a.chunk_len = a.cand_blocks ? kPoolChunk : kScoreChunk;
   const int64_t chunks = (a.n_slots + a.chunk_len - 1) / a.chunk_len;
   if (chunks * (int64_t)n_q > 0x7fffffffLL) return CSA2_ERR_SHAPE;
@@ -520,7 +560,10 @@ static int launch_score(ScoreArgs a, int n_q, float* scores, int64_t scores_stri
   a.scores_stride = scores_stride;
   a.chunks = (int)chunks;
   dim3 grid((unsigned)(chunks * n_q)), blk(kScoreThreads);
-  if (nv) {
+  if (q_lat) {   // MXFP4 only
+    if (a.cand_blocks) hipLaunchKernelGGL((k_score_decode<true, false, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_score_decode<false, false, true>), grid, blk, 0, st, a);
+  } else if (nv) {
     if (a.cand_blocks) hipLaunchKernelGGL((k_score_decode<true, true>), grid, blk, 0, st, a);
     else hipLaunchKernelGGL((k_score_decode<false, true>), grid, blk, 0, st, a);
   } else {
@@ -582,6 +625,27 @@ extern "C" int csa2_index_score_nvfp4(const uint8_t* q_codes, const uint8_t* q_s
                                       int max_cand_blocks, float* scores, int64_t scores_stride, void* stream) {
   return index_score(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
                      cand_blocks, n_cand_blocks, block, max_cand_blocks, scores, scores_stride, stream);
+}
+
+extern "C" int csa2_index_score_q(const void* q, int q_dtype, const float* w, int n_q, int n_heads, int dim,
+                                  const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
+                                  const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
+                                  const int32_t* n_cand_blocks, int block, int max_cand_blocks, float* scores,
+                                  int64_t scores_stride, void* stream) {
+  if (q_dtype != CSA2_DT_F32 && q_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
+  const uint8_t* qb = static_cast<const uint8_t*>(q);   // checked as the Q array: non-null, 16-byte aligned
+  int64_t n_slots = 0;
+  int rc = check_score_args(qb, qb, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                            cand_blocks, n_cand_blocks, block, max_cand_blocks, &n_slots);
+  if (rc != CSA2_OK) return rc;
+  if (!scores) return CSA2_ERR_NULL;
+  if (scores_stride < n_slots) return CSA2_ERR_SHAPE;
+  if (n_q == 0 || n_slots == 0) return CSA2_OK;
+  ScoreArgs a = make_args(nullptr, nullptr, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
+                          n_cand_blocks, block, max_cand_blocks, n_slots);
+  a.q_lat = q;
+  a.q_bf16 = q_dtype == CSA2_DT_BF16;
+  return launch_score(a, n_q, scores, scores_stride, false, (hipStream_t)stream, true);
 }
 
 extern "C" int csa2_index_score_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,

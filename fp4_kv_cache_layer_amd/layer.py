@@ -48,8 +48,10 @@ def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp
     only the first Top-K level in the scoring call (csa2_index_segments) and finish the
     selection inside their attention call (csa2_sparse_attn_topk), which also writes the
     index set for the Reuse layers; Reindex layers inside the pool write the pool's slot
-    scores (csa2_index_score) and select inside their attention call
-    (csa2_sparse_attn_pool_topk)."""
+    scores and select inside their attention call (csa2_sparse_attn_pool_topk).  With the
+    MXFP4 indexer those slot scores come from csa2_index_score_q, which quantises the
+    layer's indexer Q itself, so such a layer (which appends nothing) makes no quantise
+    call."""
     if index_fmt not in INDEX_FORMATS:
         raise ValueError(f"unknown indexer format {index_fmt!r}")
     if index_fmt != "mxfp4" and group > 1:
@@ -74,7 +76,8 @@ def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp
         elif attn_select and fused and m in ("full", "reindex"):
             calls = ["quantize_index_q", "index_segments", "attend_topk"]
         elif (attn_select if pool_select is None else pool_select) and fused and group == 1 and m == "reindex_pool":
-            calls = ["quantize_index_q", "score_pool", "attend_pool_topk"]
+            calls = (["score_pool_q", "attend_pool_topk"] if index_fmt == "mxfp4" else
+                     ["quantize_index_q", "score_pool", "attend_pool_topk"])
         elif fused:
             calls = ["quantize_index_q", "index_topk_in_pool" if m == "reindex_pool" else "index_topk", "attend"]
         else:
@@ -178,6 +181,15 @@ class Csa2Step:
         return fn(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.scores,
                   _bind=bind)
 
+    def score_q(self, caches: Caches, q_index_f32, w, q_seq, n_vis, in_pool: bool = False, bind=False):
+        """Slot scores from the unquantised indexer Q (MXFP4, quantised inside the call)."""
+        self._mx_only("scoring from an unquantised Q")
+        if in_pool:
+            return C.csa2_index_score_q(q_index_f32, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.scores,
+                                        self.pool, self.pool_count, self.block, _bind=bind)
+        return C.csa2_index_score_q(q_index_f32, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.scores,
+                                    _bind=bind)
+
     def _mx_only(self, what):
         if self.index_fmt != "mxfp4":
             raise ValueError(f"{what} reads an MXFP4 indexer only")
@@ -279,6 +291,8 @@ class Csa2Step:
                     c = self.score_grouped(caches, w, q_seq, n_vis, bind)
                 elif name in ("score", "score_pool"):
                     c = self.score(caches, w, q_seq, n_vis, name.endswith("pool"), bind)
+                elif name == "score_pool_q":
+                    c = self.score_q(caches, q_index, w, q_seq, n_vis, True, bind)
                 elif name in ("select", "select_pool"):
                     c = self.select(n_vis, name.endswith("pool"), bind)
                 elif name == "build_pool":
@@ -324,8 +338,12 @@ class Csa2Step:
                      self.attend_topk(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
             return self._seq(calls, bind)
         if self.pool_select and in_pool:
-            calls = [self.quantize_index_q(q_index_f32, bind), self.score(caches, w, q_seq, n_vis, True, bind),
-                     self.attend_pool_topk(caches, layer, q_attn, q_seq, n_vis, q_pos, replay_start, out, lse, bind)]
+            if self.index_fmt == "mxfp4":
+                calls = [self.score_q(caches, q_index_f32, w, q_seq, n_vis, True, bind)]
+            else:
+                calls = [self.quantize_index_q(q_index_f32, bind), self.score(caches, w, q_seq, n_vis, True, bind)]
+            calls.append(self.attend_pool_topk(caches, layer, q_attn, q_seq, n_vis, q_pos, replay_start, out, lse,
+                                               bind))
             return self._seq(calls, bind)
         calls = [self.quantize_index_q(q_index_f32, bind), *self._score_select(caches, w, q_seq, n_vis, in_pool, bind),
                  self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]

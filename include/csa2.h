@@ -186,6 +186,26 @@ int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const floa
                      int max_cand_blocks, float* scores, int64_t scores_stride, void* stream);
 
 /*
+ * csa2_index_score_q -- csa2_index_score with the indexer Q given unquantised: every
+ * workgroup quantises its query's Q to MXFP4 itself (the csa2_quantize_kv rule, bit for
+ * bit), so a layer step that appends nothing (Reindex) needs no quantise launch before
+ * scoring.  [W] "FP4 与 SWA Bounded Replay" (indexer Q in FP4 after RoPE);
+ * [W] "分层稀疏索引器" (Reindex inside the pool).
+ *
+ *   q        [n_q, n_heads, 128] f32 (q_dtype CSA2_DT_F32) or bf16 (CSA2_DT_BF16),
+ *            16-byte aligned, finite; read only
+ *   others   as csa2_index_score
+ * The scores equal those of csa2_quantize_kv (CSA2_FMT_MXFP4) followed by
+ * csa2_index_score on its codes.  Errors: as csa2_index_score; CSA2_ERR_UNSUPPORTED for
+ * another q_dtype.
+ */
+int csa2_index_score_q(const void* q, int q_dtype, const float* w, int n_q, int n_heads, int dim,
+                       const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
+                       const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
+                       const int32_t* n_cand_blocks, int block, int max_cand_blocks, float* scores,
+                       int64_t scores_stride, void* stream);
+
+/*
  * csa2_index_score_grouped -- csa2_index_score (without a pool) for query rows that come in
  * groups sharing one sequence, reading each group's indexer K once.  For the tokens of a
  * sequence scored together: several decode tokens verified at once, or the rows of a

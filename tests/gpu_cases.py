@@ -211,7 +211,10 @@ def run_group_snapshots(case: Case, step, caches, window_appends: bool = False, 
         torch.cuda.synchronize()
     calls = step.run_group(caches, modes, inputs, q_seq, n_vis, q_pos, rs, bind=True, new_wins=new_wins)
     snaps, at = [], 0
-    for L, names in enumerate(plan_group(modes, step.fused, step.group, step.index_fmt)):
+    # the calls of each layer as the step plans them (the flat list is cut by these counts)
+    plan = plan_group(modes, step.fused, step.group, step.index_fmt, step.attn_select, pool_select=step.pool_select)
+    assert sum(len(n) for n in plan) == len(calls)
+    for L, names in enumerate(plan):
         if window_appends:
             C_ = C()
             lat = np.stack([wl.swa_latents(L, int(b), int(t), 1)[0] for b, t in zip(wl.q_seq, wl.q_pos)])

@@ -132,3 +132,28 @@ def test_pool_select_in_attention_validation(L):
     a = list(att); a[14] = 0                        # block
     assert L.csa2_sparse_attn_pool_topk(*a) == -2
     assert L.csa2_sparse_attn_pool_topk(*att) == -5  # split over workgroups needs a workspace
+
+
+def test_index_score_q_validation(L):
+    """csa2_index_score_q (indexer Q unquantised) rejects bad arguments before any launch."""
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.csa2_index_score_q.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64,
+                                     vp]
+    fake = vp(0x1000)   # never dereferenced: every call below fails validation first or launches nothing
+    args = [fake, 0, fake, 4, 16, 128, fake, fake, 4096, 2, fake, fake, None, None, 8, 0, fake, 4096, None]
+    a = list(args); a[1] = 5                        # Q dtype
+    assert L.csa2_index_score_q(*a) == -3
+    a = list(args); a[0] = None                     # Q NULL
+    assert L.csa2_index_score_q(*a) == -1
+    a = list(args); a[0] = vp(0x1004)               # Q not 16-byte aligned
+    assert L.csa2_index_score_q(*a) == -2
+    a = list(args); a[5] = 64                       # indexer dim
+    assert L.csa2_index_score_q(*a) == -2
+    a = list(args); a[4] = 17                       # indexer heads
+    assert L.csa2_index_score_q(*a) == -2
+    a = list(args); a[17] = 100                     # scores stride below seq_cap
+    assert L.csa2_index_score_q(*a) == -2
+    a = list(args); a[12] = fake                    # pool map without its counts
+    assert L.csa2_index_score_q(*a) == -1
+    a = list(args); a[3] = 0                        # no rows: nothing launched
+    assert L.csa2_index_score_q(*a) == 0

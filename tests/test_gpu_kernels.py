@@ -255,6 +255,48 @@ def test_index_score_pool_slots(C, fmt):
         assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 1e-6 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("pool,q_dt,heads", [(True, "f32", 16), (False, "f32", 16), (True, "bf16", 16),
+                                             (False, "bf16", 5), (True, "f32", 5)])
+def test_index_score_q_matches_quantize_then_score(C, pool, q_dt, heads):
+    """csa2_index_score_q (the indexer Q unquantised, quantised inside the scoring call) gives
+    scores bit-identical to csa2_quantize_kv (MXFP4) followed by csa2_index_score on the same
+    values, inside a pool (every slot, -inf pads included) and over all visible entries;
+    the quantiser and the scores are pinned to the oracle by test_quantize_bitexact and
+    test_index_score_parity / test_index_score_pool_slots."""
+    _say("index_score_q", pool, q_dt, heads)
+    case = _score_case(31 + heads, 2, 6000, [6000, 5003, 333], heads)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq, n_vis, _, _ = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(wl.n_q, 16, heads, wl.seq_cap, max_blocks=300)
+    if pool:
+        rng = np.random.default_rng(5)
+        blocks = np.full((wl.n_q, 300), -1, np.int32)
+        ncb = np.array([300, 250, 60], np.int32)
+        for qi in range(wl.n_q):
+            nb = -(-int(wl.n_vis[qi]) // 8)
+            blocks[qi, :ncb[qi]] = np.sort(rng.choice(nb + 20, size=ncb[qi], replace=False))  # some beyond n_vis
+        blocks[1, 5] = -1
+        st.pool.copy_(torch.from_numpy(blocks))
+        st.pool_count.copy_(torch.from_numpy(ncb))
+    q_in = q_idx if q_dt == "f32" else q_idx.to(torch.bfloat16)
+    st.quantize_index_q(q_in.float().contiguous())      # exact widening of bf16 values
+    st.score(caches, w, q_seq, n_vis, in_pool=pool)
+    torch.cuda.synchronize()
+    ref = st.scores.clone()
+    st.scores.fill_(7.0)
+    st.score_q(caches, q_in.contiguous(), w, q_seq, n_vis, in_pool=pool)
+    torch.cuda.synchronize()
+    if pool:
+        assert torch.equal(st.scores[:, :300 * 8], ref[:, :300 * 8])
+    else:
+        for qi in range(wl.n_q):
+            nv = int(wl.n_vis[qi])
+            assert torch.equal(st.scores[qi, :nv], ref[qi, :nv])
+
+
 def _run_index_topk(C, st, caches, w, q_seq, n_vis, k, in_pool=False):
     """(fused idx, count), (two-call idx, count) on the same inputs."""
     idx_f = torch.full((st.n_q, k), 77, dtype=torch.int32, device="cuda")

@@ -85,8 +85,10 @@ def test_plan_select_in_attention():
     assert plan[2] == ["quantize_index_q", "index_segments", "attend_topk"]
     plan = plan_group(["full_pool", "reuse", "reindex_pool"], attn_select=True)
     assert plan[0] == ["quantize_index_q", "index_topk_pool", "attend"]
-    assert plan[2] == ["quantize_index_q", "score_pool", "attend_pool_topk"]
+    assert plan[2] == ["score_pool_q", "attend_pool_topk"]   # the scoring call quantises Q itself
     plan = plan_group(["full_pool", "reuse", "reindex_pool"], attn_select=False, pool_select=True)
+    assert plan[2] == ["score_pool_q", "attend_pool_topk"]
+    plan = plan_group(["full_pool", "reuse", "reindex_pool"], index_fmt="nvfp4", pool_select=True)
     assert plan[2] == ["quantize_index_q", "score_pool", "attend_pool_topk"]
     plan = plan_group(["full_pool", "reuse", "reindex_pool"], attn_select=True, pool_select=False)
     assert plan[2] == ["quantize_index_q", "index_topk_in_pool", "attend"]
