@@ -407,7 +407,8 @@ PREFILL_GROUP = 8   # rows of a prefill chunk scored per pass over the sequence'
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_score_select_c2_128k_traffic.md")
 TRAFFIC_SOURCES = ("fp4_kv_cache_layer_amd/csrc/score.hip", "fp4_kv_cache_layer_amd/csrc/select.h",
-                   "fp4_kv_cache_layer_amd/csrc/topk.hip", "fp4_kv_cache_layer_amd/build.py")
+                   "fp4_kv_cache_layer_amd/csrc/device.h", "fp4_kv_cache_layer_amd/csrc/topk.hip",
+                   "fp4_kv_cache_layer_amd/build.py")
 COPY_BYTES = 1 << 30   # the calibration copy: 1 GiB read + 1 GiB written
 
 

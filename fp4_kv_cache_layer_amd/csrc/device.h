@@ -86,8 +86,12 @@ __device__ __forceinline__ uint32_t e2m1_code(float a, float s) {
 // One MXFP4 group: 32 finite fp32 values (as bits; bf16 inputs widened by a shift) ->
 // E8M0 scale code (returned) and 32 E2M1 codes packed as four words, channel 2i in the low
 // nibble of byte i.  E = floor(log2 amax) - 2 clamped to [-127, 127] (an all-zero group or
-// a subnormal amax gives -127); each magnitude is compared with the E2M1 midpoints times
-// 2^E (exact products) rather than divided.
+// a subnormal amax gives -127).  The codes come from the hardware down-convert with scale
+// 2^E (V_CVT_SCALEF32_PK_FP4_F32: x / 2^E rounded to the nearest E2M1 value, ties to the
+// even code, saturating at 6, sign kept, -0 included), which gives the same code as
+// comparing |x| with the E2M1 midpoints times 2^E (e2m1_code) on every code boundary, the
+// floats next to each, the saturation range and scales from 2^-127 to 2^125 (measured on
+// this GPU).
 __device__ __forceinline__ int mxfp4_group(const uint32_t (&bits)[32], uint32_t (&w)[4]) {
   uint32_t amax_bits = 0;
 #pragma unroll
@@ -102,9 +106,10 @@ __device__ __forceinline__ int mxfp4_group(const uint32_t (&bits)[32], uint32_t 
   const float s = ldexpf(1.0f, code - 127);
   w[0] = w[1] = w[2] = w[3] = 0u;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t c = e2m1_code(__uint_as_float(bits[i] & 0x7fffffffu), s) | ((bits[i] >> 28) & 8u);
-    w[i >> 3] |= c << (4 * (i & 7));
+  for (int j = 0; j < 16; ++j) {   // channels 2j (low nibble) and 2j+1 (high nibble) -> byte j
+    const uint32_t b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, __uint_as_float(bits[2 * j]),
+                                                                __uint_as_float(bits[2 * j + 1]), s, 0) & 0xffu;
+    w[j >> 2] |= b << (8 * (j & 3));
   }
   return code;
 }

@@ -45,6 +45,26 @@ def _adversarial_rows(rng, rows, dim, group):
     return x
 
 
+def _mx_adversarial_rows(rng, rows, dim):
+    """MXFP4 groups (32 channels) whose maximum fixes the power-of-two scale 2^E and whose
+    elements sit on and 1 ulp beside the E2M1 midpoints times 2^E, in the saturation range
+    [6, 8) x 2^E, or at zero, with scales from the subnormal 2^-127 up to 2^120."""
+    t = np.array([0.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 6.5, 7.0, 7.9])
+    x = np.zeros((rows, dim), np.float32)
+    for r in range(rows):
+        for g in range(dim // 32):
+            s = np.float32(2.0 ** int(rng.choice([-127, -126, -125, -60, -3, 0, 4, 60, 120])))
+            v = (s * t[rng.integers(len(t), size=32)]).astype(np.float32)
+            v[0] = np.float32(4.0) * s          # floor(log2 amax) = E + 2
+            nudge = rng.integers(3, size=32)
+            nudge[0] = 0
+            v = np.where(nudge == 1, np.nextafter(v, np.float32(0)), v)
+            v = np.where(nudge == 2, np.nextafter(v, np.float32(1e38)), v)
+            v *= rng.choice([-1, 1], size=32).astype(np.float32)
+            x[r, g * 32:(g + 1) * 32] = rng.permutation(v)
+    return x
+
+
 def _special_rows(dim):
     rows = [np.zeros(dim), -np.zeros(dim), np.full(dim, 3000.0), np.full(dim, 1e-30),
             np.linspace(-22.6, 22.6, dim), np.full(dim, 448.0), np.full(dim, 2.0 ** -130)]
@@ -61,7 +81,7 @@ def test_quantize_bitexact(C, fmt, src_dt):
     x = np.concatenate([
         (rng.normal(size=(300, dim)) * 10.0 ** rng.uniform(-3, 2, size=(300, 1))).astype(np.float32),
         _adversarial_rows(rng, 40, dim, 16 if fmt == "nvfp4" else group),
-        _special_rows(dim)])
+        _special_rows(dim)] + ([_mx_adversarial_rows(rng, 60, dim)] if fmt == "mxfp4" else []))
     xt = torch.from_numpy(x).cuda()
     if src_dt == "bf16":
         xt = xt.to(torch.bfloat16)
