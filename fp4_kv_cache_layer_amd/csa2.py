@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
     sig = {
         "csa2_version": ([], i32),
         "csa2_init": ([], i32),
+        "csa2_device_status": ([i32], ctypes.c_uint32),
+        "csa2_debug_set_wait_limit": ([i32], i32),
         "csa2_status_string": ([i32], ctypes.c_char_p),
         "csa2_last_error": ([], ctypes.c_char_p),
         "csa2_quantize_kv": ([vp, i32, i64, i32, i32, vp, i64, vp, vp, vp], i32),
@@ -135,6 +137,27 @@ def csa2_version() -> int:
 
 def csa2_init():
     _check(lib().csa2_init(), "csa2_init")
+
+
+def csa2_device_status(clear: bool = False) -> int:
+    """The device status word (0, or a CSA2_STATUS_* code a kernel stored); clear resets it."""
+    return int(lib().csa2_device_status(int(clear)))
+
+
+def csa2_debug_set_wait_limit(polls: int) -> int:
+    """Testing aid: the attention kernel's partner-wait bound (negative restores the default)."""
+    return int(lib().csa2_debug_set_wait_limit(int(polls)))
+
+
+def _workspace(need: int, workspace, device, bind: bool, name: str):
+    """The caller's workspace, or (eager calls only) a temporary one of `need` bytes.  A
+    bound call keeps raw pointers, so a temporary would be freed while the callable still
+    writes into it: binding requires the caller's own workspace."""
+    if workspace is None and need:
+        if bind:
+            raise ValueError(f"{name}: a bound call needs a caller-owned workspace of {need} bytes")
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, (0 if workspace is None else workspace.numel())
 
 
 def _quant_args(src, fmt: int, codes, scales, dst_row, bind: bool):
@@ -316,9 +339,7 @@ def _index_topk(name, scale_group, q_codes, q_scales, w, k_codes, k_scales, q_se
     if idx_out.shape != (n_q, k) or count_out.shape[0] != n_q:
         raise ValueError("index_topk: inconsistent output shapes")
     need = csa2_index_topk_workspace_bytes(n_q, max(n_slots, 1), k, cand_blocks is not None)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q_codes.device)
-    ws_bytes = 0 if workspace is None else workspace.numel()
+    workspace, ws_bytes = _workspace(need, workspace, q_codes.device, _bind, "workspace")
     return _run(name, args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, _stream()), _bind)
 
 
@@ -371,10 +392,9 @@ def csa2_index_topk_pool(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, 
             blocks_count.shape[0] != n_q:
         raise ValueError("index_topk_pool: inconsistent output shapes")
     need = csa2_index_topk_pool_workspace_bytes(n_q, max(n_slots, 1), k, block, max_blocks)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_codes.device)
+    workspace, ws_bytes = _workspace(max(need, 1), workspace, q_codes.device, _bind, "index_topk_pool")
     return _run("csa2_index_topk_pool", args[:12] + (k, _p(idx_out), _p(count_out), block, max_blocks, _p(blocks_out),
-                                                     _p(blocks_count), _p(workspace), workspace.numel(), _stream()),
+                                                     _p(blocks_count), _p(workspace), ws_bytes, _stream()),
                 _bind)
 
 
@@ -399,9 +419,7 @@ def csa2_topk(scores, n_vis, max_vis: int, k: int, idx_out, count_out, workspace
         max_blocks = cand_blocks.shape[1]
     n_slots = max_blocks * block if cand_blocks is not None else max_vis
     need = csa2_topk_workspace_bytes(n_q, max(n_slots, 1), k)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
-    ws_bytes = 0 if workspace is None else workspace.numel()
+    workspace, ws_bytes = _workspace(need, workspace, scores.device, _bind, "workspace")
     return _run("csa2_topk", (_p(scores), scores.stride(0), n_q, _p(n_vis), max_vis, _p(cand_blocks),
                               _p(n_cand_blocks), block, max_blocks, k, _p(idx_out), _p(count_out), _p(workspace),
                               ws_bytes, _stream()), _bind)
@@ -420,9 +438,7 @@ def csa2_build_pool(scores, n_vis, max_vis: int, blocks_out, count_out, block: i
     _need(count_out, torch.int32, 1, "count_out")
     n_q, max_blocks = blocks_out.shape
     need = csa2_pool_workspace_bytes(n_q, max(max_vis, 1), block, max_blocks)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
-    ws_bytes = 0 if workspace is None else workspace.numel()
+    workspace, ws_bytes = _workspace(need, workspace, scores.device, _bind, "workspace")
     return _run("csa2_build_pool", (_p(scores), scores.stride(0), n_q, _p(n_vis), max_vis, block, max_blocks,
                                     _p(blocks_out), _p(count_out), _p(workspace), ws_bytes, _stream()), _bind)
 
@@ -453,13 +469,18 @@ def _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start
             raise ValueError("lse shape")
 
 
-def _new_win(new_win, n_q, D):
-    """(pointer, dtype) of the optional window append: [n_q, D] f32 / bf16 latents."""
+def _new_win(new_win, n_q, D, q_seq=None):
+    """(pointer, dtype) of the optional window append: [n_q, D] f32 / bf16 latents.  The
+    append needs every row of the call in a sequence of its own (otherwise one row's
+    workgroups would write a ring row that another row's workgroups read): checked here,
+    once per call or per bound callable, with one read of q_seq."""
     if new_win is None:
         return None, DT_F32
     if new_win.dtype not in (torch.float32, torch.bfloat16) or tuple(new_win.shape) != (n_q, D) or \
             not new_win.is_contiguous() or not new_win.is_cuda:
         raise ValueError("new_win must be a contiguous [n_q, D] f32/bf16 device tensor")
+    if q_seq is not None and n_q > 1 and torch.unique(q_seq).numel() != n_q:
+        raise ValueError("new_win: two rows of the call share a sequence (the append needs distinct sequences)")
     return _p(new_win), DT_F32 if new_win.dtype == torch.float32 else DT_BF16
 
 
@@ -477,11 +498,9 @@ def csa2_sparse_attn_topk(q, kv_codes, kv_scales, q_seq, cand_keys, k: int, idx_
     if tuple(idx_out.shape) != (n_q, k) or count_out.shape[0] != n_q:
         raise ValueError("sparse_attn_topk: inconsistent index output shapes")
     need = csa2_attn_workspace_bytes(n_q, H, D, k, window)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel()
+    workspace, ws_bytes = _workspace(need, workspace, q.device, _bind, "workspace")
     odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
-    nw, nwt = _new_win(new_win, n_q, D)
+    nw, nwt = _new_win(new_win, n_q, D, q_seq)
     return _run("csa2_sparse_attn_topk", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq),
                                           _p(cand_keys), cand_keys.shape[1], k, _p(idx_out), _p(count_out), _p(swa),
                                           swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), nw, nwt, window,
@@ -508,11 +527,9 @@ def csa2_sparse_attn_pool_topk(q, kv_codes, kv_scales, q_seq, scores, n_vis, can
             n_cand_blocks.shape[0] != n_q or n_vis.shape[0] != n_q:
         raise ValueError("sparse_attn_pool_topk: inconsistent shapes")
     need = csa2_attn_workspace_bytes(n_q, H, D, k, window)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel()
+    workspace, ws_bytes = _workspace(need, workspace, q.device, _bind, "workspace")
     odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
-    nw, nwt = _new_win(new_win, n_q, D)
+    nw, nwt = _new_win(new_win, n_q, D, q_seq)
     return _run("csa2_sparse_attn_pool_topk", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq,
                                                _p(q_seq), _p(scores), scores.shape[1], _p(n_vis), _p(cand_blocks),
                                                _p(n_cand_blocks), block, cand_blocks.shape[1], k, _p(idx_out),
@@ -548,11 +565,9 @@ def csa2_sparse_attn(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, r
         if tuple(lse.shape) != (n_q, H):
             raise ValueError("lse shape")
     need = csa2_attn_workspace_bytes(n_q, H, D, k, window)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel()
+    workspace, ws_bytes = _workspace(need, workspace, q.device, _bind, "workspace")
     odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
-    nw, nwt = _new_win(new_win, n_q, D)
+    nw, nwt = _new_win(new_win, n_q, D, q_seq)
     return _run("csa2_sparse_attn", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq), _p(idx),
                                      k, _p(swa), swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), nw, nwt, window,
                                      ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes,

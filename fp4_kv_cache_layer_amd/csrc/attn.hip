@@ -9,9 +9,12 @@
 //
 // Exactness of the operands: every main-KV value is E2M1 x E4M3 (at most 6 significant
 // bits, magnitude in [2^-10, 2688]) and every window value is E4M3, so both are exact in
-// fp16.  Q (bf16) is converted to fp16, which is exact for |q| in [2^-14, 65504); smaller
-// magnitudes round to fp16 subnormals (absolute error below 2^-25).  P = exp2(logit - max)
-// is rounded to fp16 (11 significant bits) for the P.V product.
+// fp16.  Q (bf16) enters the products as fp16 after a power-of-two scale per head: the
+// head's largest |q| is brought into [2^14, 2^15), which keeps every bf16 value within 2^32
+// of that maximum exact (8 significant bits in fp16's 11, normal or subnormal) over the
+// whole bf16 range, and the logits take the scale back exactly (a power of two commutes
+// with the fp32 rounding of the sums).  P = exp2(logit - max) is rounded to fp16 (11
+// significant bits) for the P.V product.
 //
 // Decomposition: one workgroup = (query, 16 heads, slice of the key list), 8 waves in four
 // pairs.  The key list is cut into tiles of 16 keys; pair p takes every fourth tile of the
@@ -107,6 +110,10 @@ struct AttnArgs {
   const int32_t* n_cand_blocks;
   const int64_t* n_vis;
   int block, max_cand_blocks;
+  // the partner-flag wait gives up after wait_limit polls; it then stores a nonzero code
+  // into the library's status word (pinned host memory; nullptr before csa2_init)
+  int wait_limit;
+  uint32_t* status;
 };
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -115,8 +122,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// bf16 bits -> fp16 (see the header comment for the range)
-__device__ __forceinline__ _Float16 bf16_to_f16(uint32_t b) { return (_Float16)__uint_as_float(b << 16); }
+// bf16 bits times 2^-shift -> fp16 (exact for the values the header comment names)
+__device__ __forceinline__ _Float16 bf16_to_f16(uint32_t b, int shift) {
+  return (_Float16)ldexpf(__uint_as_float(b << 16), -shift);
+}
+
+// Exponent shift that brings a head's largest |q| (given as bf16 magnitude bits) into
+// [2^14, 2^15): q * 2^-shift then fits fp16 with its top bits in the normal range.  An
+// all-zero head keeps shift 0; a subnormal maximum counts as 2^-127.
+__device__ __forceinline__ int q_shift(uint32_t max_bits) {
+  const int e = (int)(max_bits >> 7);
+  return max_bits == 0 ? 0 : (e == 0 ? -127 : e - 127) - 14;
+}
 
 // 8 E2M1 values of one code dword (channel 2i in the low nibble of byte i) times a group
 // scale given as an fp16 pair, as 8 fp16; exact (E2M1 x E4M3 has at most 6 significant
@@ -383,15 +400,41 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
       if (i < n_keys) s_idx[i] = tile_lo * kT + i < a.k ? iv[r] : -1;
     }
   }
+  // the largest |q| of head col over this wave's 256 channels (bf16 magnitude bits; the
+  // order of finite bf16 magnitudes is that of their bit patterns), then over both halves
+  // through LDS at the prologue's barrier
+  __shared__ uint32_t s_qmax[2][kHG];
+  {
+    uint32_t qm = 0;
+#pragma unroll
+    for (int st = 0; st < kQS; ++st) {
+      const uint32_t w4[4] = {qraw[st].x, qraw[st].y, qraw[st].z, qraw[st].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = w4[i] & 0x7fffu, hi = (w4[i] >> 16) & 0x7fffu;
+        qm = lo > qm ? lo : qm;
+        qm = hi > qm ? hi : qm;
+      }
+    }
+    uint32_t o = (uint32_t)__shfl_xor((int)qm, 16);
+    qm = o > qm ? o : qm;
+    o = (uint32_t)__shfl_xor((int)qm, 32);
+    qm = o > qm ? o : qm;
+    if (pair == 0 && grp == 0) s_qmax[half][col] = qm;
+  }
   if (lane == 0) s_flag[wave] = 0u;
-  __syncthreads();  // s_idx, s_flag
+  __syncthreads();  // s_idx, s_flag, s_qmax
   if (!early) {
     load_slot(my_tile(0), 0 < n_my, g0);
     load_slot(my_tile(1), 1 < n_my, g1);
   }
 
-  // Q as the fp16 B operand
+  // Q as the fp16 B operand, scaled by 2^-shift per head; the logits of head col take
+  // 2^shift back in qsl (log2-domain scale of this lane's head)
   v8h qf[kQS];
+  const uint32_t qmax_bits = s_qmax[0][col] > s_qmax[1][col] ? s_qmax[0][col] : s_qmax[1][col];
+  const int qsh = q_shift(qmax_bits);
+  const float qsl = ldexpf(a.scale_log2, qsh);
 
   // Dequantise the slot (the wave's 256 channels of 16 keys), write them as this wave's
   // V half-tile and form the partial S^T = K Q^T over those channels.  The format is
@@ -462,7 +505,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool ok = (valid >> (4 * grp + r)) & 1u;
-      x[r] = ok ? sv[r] * a.scale_log2 : -__builtin_inff();
+      x[r] = ok ? sv[r] * qsl : -__builtin_inff();
       mt = fmaxf(mt, x[r]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -516,18 +559,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   // stream synchronise, so the four streams drift freely.  Both waves make the same
   // sequence of exchanges, so every wait is met; a slot is rewritten two exchanges later,
   // which the writer can only reach after the partner's flag shows the read was done.  The
-  // wait is bounded so that it always ends.  Both waves add in the same order up to
+  // wait is bounded so that it always ends; a wait that gives up stores a nonzero code
+  // into the library's status word, which the host reports at its next call (the output
+  // of this call is then not to be trusted).  Both waves add in the same order up to
   // commutation, so the pair holds bit-identical S^T, softmax state and P.
   auto exchange = [&](v4f own, int id) -> v4f {
     const int sl = id & 1;
     sx[(wave * 2 + sl) * 64 + lane] = make_float4(own[0], own[1], own[2], own[3]);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) __hip_atomic_store(&s_flag[wave], (uint32_t)(id + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    for (int spin = 0; spin < (1 << 22); ++spin) {
-      if (__hip_atomic_load(&s_flag[partner], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= (uint32_t)(id + 1))
+    bool seen = false;
+    for (int spin = 0; spin < a.wait_limit; ++spin) {
+      if (__hip_atomic_load(&s_flag[partner], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= (uint32_t)(id + 1)) {
+        seen = true;
         break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
+    if (!seen && lane == 0 && a.status)
+      __hip_atomic_store(a.status, (uint32_t)CSA2_STATUS_ATTN_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const float4 o2 = sx[(partner * 2 + sl) * 64 + lane];
     return v4f{own[0] + o2.x, own[1] + o2.y, own[2] + o2.z, own[3] + o2.w};
@@ -550,8 +600,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     v8h h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      h[2 * i] = bf16_to_f16(w4[i] & 0xffffu);
-      h[2 * i + 1] = bf16_to_f16(w4[i] >> 16);
+      h[2 * i] = bf16_to_f16(w4[i] & 0xffffu, qsh);
+      h[2 * i + 1] = bf16_to_f16(w4[i] >> 16, qsh);
     }
     qf[st] = h;
   }
@@ -769,6 +819,7 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
                        const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
                        const void* new_win, int new_win_dtype, int window, float sm_scale, void* out, int out_dtype,
                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = csa2_take_device_status()) return rc;
   if (!q || !kv_codes || !kv_scales || !q_seq || !swa || !swa_base || !q_pos || !replay_start || !out)
     return CSA2_ERR_NULL;
   const bool select = sel.mode != 0;
@@ -829,6 +880,8 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
   a.count_out = count_out;
   a.new_win = new_win;
   a.new_win_bf16 = new_win_dtype == CSA2_DT_BF16;
+  a.wait_limit = csa2_wait_limit();
+  a.status = csa2_status_word();
   if (p.nsplit > 1) {
     size_t need = csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window);
     if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;

@@ -119,3 +119,9 @@ __device__ __forceinline__ int mxfp4_group(const uint32_t (&bits)[32], uint32_t 
 // Launch-error bookkeeping used by every entry point (defined in abi.hip).
 int csa2_record_hip_error(hipError_t e);
 int csa2_check_launch();
+// The device status word (device-visible address, nullptr before csa2_init), the bound of
+// the attention kernel's partner wait, and the check every compute entry point makes first:
+// CSA2_ERR_DEVICE (and the text in csa2_last_error) if a kernel stored a status code.
+uint32_t* csa2_status_word();
+int csa2_wait_limit();
+int csa2_take_device_status();

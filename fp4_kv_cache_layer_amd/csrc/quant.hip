@@ -225,6 +225,7 @@ using namespace csa2;
 extern "C" int csa2_quantize_kv(const void* src, int src_dtype, int64_t rows, int dim, int fmt,
                                 const int64_t* dst_row, int64_t dst_rows, uint8_t* codes,
                                 uint8_t* scales, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   QuantJobs jobs = {};
   int64_t blocks = 0;
   const int rc = make_job(src, src_dtype, rows, dim, fmt, dst_row, dst_rows, codes, scales, &jobs.job[0], &blocks);
@@ -234,6 +235,7 @@ extern "C" int csa2_quantize_kv(const void* src, int src_dtype, int64_t rows, in
 }
 
 extern "C" int csa2_quantize_kv_multi(const csa2_quant_job* jobs, int n_jobs, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   if (!jobs) return CSA2_ERR_NULL;
   if (n_jobs < 0 || n_jobs > CSA2_MAX_QUANT_JOBS) return CSA2_ERR_SHAPE;
   QuantJobs kj = {};

@@ -614,6 +614,7 @@ extern "C" int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales,
                                 int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
                                 const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
                                 int max_cand_blocks, float* scores, int64_t scores_stride, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   return index_score(false, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
                      cand_blocks, n_cand_blocks, block, max_cand_blocks, scores, scores_stride, stream);
 }
@@ -623,6 +624,7 @@ extern "C" int csa2_index_score_nvfp4(const uint8_t* q_codes, const uint8_t* q_s
                                       int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
                                       const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
                                       int max_cand_blocks, float* scores, int64_t scores_stride, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   return index_score(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
                      cand_blocks, n_cand_blocks, block, max_cand_blocks, scores, scores_stride, stream);
 }
@@ -632,6 +634,7 @@ extern "C" int csa2_index_score_q(const void* q, int q_dtype, const float* w, in
                                   const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
                                   const int32_t* n_cand_blocks, int block, int max_cand_blocks, float* scores,
                                   int64_t scores_stride, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   if (q_dtype != CSA2_DT_F32 && q_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
   const uint8_t* qb = static_cast<const uint8_t*>(q);   // checked as the Q array: non-null, 16-byte aligned
   int64_t n_slots = 0;
@@ -652,6 +655,7 @@ extern "C" int csa2_index_score_grouped(const uint8_t* q_codes, const uint8_t* q
                                         int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
                                         int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
                                         int group, float* scores, int64_t scores_stride, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   int64_t n_slots = 0;
   int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
                             nullptr, nullptr, 0, 0, &n_slots);
@@ -757,6 +761,7 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
                                const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
                                int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out, void* workspace,
                                size_t workspace_bytes, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   return index_topk(false, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
                     cand_blocks, n_cand_blocks, block, max_cand_blocks, k, idx_out, count_out, workspace,
                     workspace_bytes, stream);
@@ -768,6 +773,7 @@ extern "C" int csa2_index_topk_nvfp4(const uint8_t* q_codes, const uint8_t* q_sc
                                      const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
                                      int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   return index_topk(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
                     cand_blocks, n_cand_blocks, block, max_cand_blocks, k, idx_out, count_out, workspace,
                     workspace_bytes, stream);
@@ -817,6 +823,7 @@ extern "C" int csa2_index_segments(const uint8_t* q_codes, const uint8_t* q_scal
                                    int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
                                    int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k,
                                    uint64_t* cand_keys, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   return index_segments(false, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq,
                         n_vis, k, cand_keys, stream);
 }
@@ -825,6 +832,7 @@ extern "C" int csa2_index_segments_nvfp4(const uint8_t* q_codes, const uint8_t* 
                                          int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
                                          int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
                                          int k, uint64_t* cand_keys, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   return index_segments(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq,
                         n_vis, k, cand_keys, stream);
 }
@@ -843,6 +851,7 @@ extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_sca
                                     int32_t* idx_out, int32_t* count_out, int block, int max_blocks,
                                     int32_t* blocks_out, int32_t* blocks_count, void* workspace,
                                     size_t workspace_bytes, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   int64_t n_slots = 0;
   int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
                             nullptr, nullptr, 0, 0, &n_slots);

@@ -381,6 +381,7 @@ extern "C" int csa2_topk(const float* scores, int64_t scores_stride, int n_q, co
                          const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block, int max_cand_blocks,
                          int k, int32_t* idx_out, int32_t* count_out, void* workspace, size_t workspace_bytes,
                          void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   if (!scores || !n_vis || !idx_out || !count_out) return CSA2_ERR_NULL;
   if (n_q < 0 || n_q > 65535 || k < 1 || k > CSA2_MAX_TOPK || max_vis < 0 || max_vis > 0x7fffffffLL)
     return CSA2_ERR_SHAPE;
@@ -418,6 +419,7 @@ extern "C" size_t csa2_pool_workspace_bytes(int n_q, int64_t max_vis, int block,
 extern "C" int csa2_build_pool(const float* scores, int64_t scores_stride, int n_q, const int64_t* n_vis,
                                int64_t max_vis, int block, int max_blocks, int32_t* blocks_out, int32_t* count_out,
                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
   if (!scores || !n_vis || !blocks_out || !count_out) return CSA2_ERR_NULL;
   if (n_q < 0 || n_q > 65535 || block < 1 || block > 64 || max_blocks < 1 || max_blocks > CSA2_MAX_TOPK ||
       max_vis < 0 || max_vis > 0x7fffffffLL || scores_stride < max_vis)

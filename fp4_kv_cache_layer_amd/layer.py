@@ -129,6 +129,7 @@ class Csa2Step:
         (the survivors of up to 131,072 entries at k = 512); False keeps the last selection
         level as a launch of its own (csa2_index_topk, then csa2_sparse_attn)."""
         plan_group(["full"], fused, group, index_fmt)   # validates the combination
+        C.csa2_init()   # device check; the device status word the kernels report into
         n_cand = C.csa2_segment_keys(seq_cap, k)
         fits = fused and group == 1 and 1 <= n_cand <= 8192
         # inside a pool the attention call selects from at most 16,384 slots

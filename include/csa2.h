@@ -31,6 +31,9 @@
  *     runtime rejected a launch; csa2_last_error() then holds its text (per thread).
  *   - Values read from device arrays (positions, counts, indices) are clamped or skipped
  *     in-kernel so that no access leaves the buffers the sizes describe.
+ *   - A kernel cannot return a status; where one meets a condition its outputs cannot show
+ *     (a bounded wait that gave up) it stores a code into the device status word, and the
+ *     next call on the host returns CSA2_ERR_DEVICE (csa2_device_status).
  *   - Inputs are finite; NaN/Inf inputs are outside the contract.
  *   - Code arrays (codes, q_codes, k_codes, kv_codes, swa), q and out must start on a
  *     16-byte boundary and kv_scales on an 8-byte one (CSA2_ERR_SHAPE otherwise); row
@@ -64,6 +67,12 @@ extern "C" {
 #define CSA2_ERR_UNSUPPORTED (-3)  /* argument combination not supported (format, dtype, device) */
 #define CSA2_ERR_HIP (-4)          /* the HIP runtime reported an error */
 #define CSA2_ERR_WORKSPACE (-5)    /* workspace missing or smaller than required */
+#define CSA2_ERR_DEVICE (-6)       /* a kernel of an earlier call stored a device status code
+                                      (csa2_last_error names it); nothing was launched */
+
+/* ---- device status codes (csa2_device_status) ---- */
+#define CSA2_STATUS_ATTN_WAIT 1    /* an attention kernel's bounded wait for its partner wave
+                                      gave up: that call's out and lse are invalid */
 
 /* ---- storage formats ---- */
 #define CSA2_FMT_NVFP4 0  /* main KV: E2M1 + one E4M3 scale per 16 channels, no global scale
@@ -90,9 +99,24 @@ extern "C" {
 int csa2_version(void);
 
 /* Checks that the current HIP device is a gfx950 (MI355X) and that the library's code
- * objects load on it.  Returns CSA2_OK, CSA2_ERR_UNSUPPORTED (other device) or
- * CSA2_ERR_HIP (no device / runtime error). */
+ * objects load on it, and (once per process) allocates the library's 4-byte device status
+ * word in pinned, mapped host memory.  Returns CSA2_OK, CSA2_ERR_UNSUPPORTED (other
+ * device) or CSA2_ERR_HIP (no device / runtime error).  Calls made before csa2_init work,
+ * but their kernels have no status word to report into. */
 int csa2_init(void);
+
+/* The device status word: 0, or the CSA2_STATUS_* code a kernel stored since it was last
+ * cleared (clear != 0 clears it).  Every compute call first reads it on the host (no device
+ * synchronisation); if it is nonzero the call clears it, puts its text in csa2_last_error,
+ * launches nothing and returns CSA2_ERR_DEVICE.  A status stored by a kernel that is still
+ * running when the next call starts is reported by a later call. */
+uint32_t csa2_device_status(int clear);
+
+/* Testing aid for the status path: sets how many times the attention kernel polls its
+ * partner's flag before giving up (default 2^22; a negative value restores it) and returns
+ * the previous bound.  With 0 every exchange gives up at once: the kernel still completes,
+ * its output is wrong, and the status word is set. */
+int csa2_debug_set_wait_limit(int polls);
 
 /* Static text for a status code; never NULL. */
 const char* csa2_status_string(int status);
@@ -405,9 +429,12 @@ size_t csa2_pool_workspace_bytes(int n_q, int64_t max_vis, int block, int max_bl
  *   out       [n_q, n_heads, dim] f32 or bf16 (out_dtype); lse [n_q, n_heads] f32 or NULL
  *   Workspace: csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window).
  * Arithmetic: Q.K and P.V on fp16 matrix cores with fp32 accumulation.  Every key/value
- * (E2M1 x E4M3, or E4M3) is exact in fp16; Q is converted from bf16 to fp16, exact for
- * |q| in [2^-14, 65504) (smaller magnitudes round to fp16 subnormals, larger ones
- * overflow); softmax in fp32; P rounded to fp16.
+ * (E2M1 x E4M3, or E4M3) is exact in fp16.  Q enters as fp16 after a power-of-two scale per
+ * (query, head) that brings the head's largest |q| into [2^14, 2^15): every bf16 value
+ * within a factor 2^32 of that maximum is then exact, over the whole bf16 range, and the
+ * logits take the scale back exactly.  Softmax in fp32; P rounded to fp16.  The kernel's
+ * one wait (between the two waves that share a key stream) is bounded; if it gives up, the
+ * call's out and lse are invalid and the next call returns CSA2_ERR_DEVICE.
  * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED (out_dtype, new_win_dtype),
  * CSA2_ERR_WORKSPACE.
  */

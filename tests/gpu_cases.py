@@ -231,8 +231,46 @@ def run_group_snapshots(case: Case, step, caches, window_appends: bool = False, 
     return snaps
 
 
+def gather_group_row(case: Case, caches, snaps, qi: int, window: int = 128) -> dict:
+    """The device bytes the oracle checks of one query row need (read on the calling thread):
+    its sequence's indexer-K cache, and per layer the main-KV rows of the set it attended
+    and the window rows of its key range."""
+    wl = case.wl
+    seq = int(wl.q_seq[qi])
+    t, s = int(wl.q_pos[qi]), int(wl.replay_start[qi])
+    rows = np.mod(O.swa_positions(t, s, window) - wl.swa_base, wl.swa_cap)
+    rows_t = torch.from_numpy(rows).cuda()
+    g = {"ik_codes": caches.ik_codes[seq].cpu().numpy(), "ik_scales": caches.ik_scales[seq].cpu().numpy(),
+         "kv_codes": [], "kv_scales": [], "swa": []}
+    for L in range(len(wl.layers)):
+        snap = snaps[L]
+        sel = torch.from_numpy(snap["idx"][qi][:int(snap["count"][qi])].astype(np.int64)).cuda()
+        g["kv_codes"].append(caches.kv_codes[seq][sel].cpu().numpy())
+        g["kv_scales"].append(caches.kv_scales[seq][sel].cpu().numpy())
+        g["swa"].append(caches.swa[L][seq][rows_t].cpu().numpy())
+    return g
+
+
+def check_group_rows(case: Case, caches, snaps, rows, workers: int = 8, **kw) -> list:
+    """check_group_query for many rows: the device bytes are read first on this thread,
+    then the oracle work runs on a thread pool (numpy releases the interpreter lock in its
+    array loops).  The first failing row raises, with its row number."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows = list(rows)
+    data = {qi: gather_group_row(case, caches, snaps, qi, kw.get("window", 128)) for qi in rows}
+
+    def one(qi):
+        try:
+            return check_group_query(case, None, snaps, qi, gpu=data[qi], **kw)
+        except AssertionError as e:
+            raise AssertionError(f"query row {qi}: {e}") from e
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(one, rows))
+
+
 def check_group_query(case: Case, caches, snaps, qi: int, k: int = 512, window: int = 128,
-                      block: int = 8, max_blocks: int = 2048) -> dict:
+                      block: int = 8, max_blocks: int = 2048, gpu: dict | None = None) -> dict:
     """Oracle parity of one query row through every layer of the group.  Index sets and the
     pool pass the oracle's acceptance rules; each layer's attention is compared with the
     oracle's over the set the GPU attended (so a legitimate near-tie swap upstream does not
@@ -240,9 +278,14 @@ def check_group_query(case: Case, caches, snaps, qi: int, k: int = 512, window: 
     wl = case.wl
     seq, nv = int(wl.q_seq[qi]), int(wl.n_vis[qi])
     t, s = int(wl.q_pos[qi]), int(wl.replay_start[qi])
-    oc = oracle_index_cache(wl, seq, case.index_fmt)
-    assert np.array_equal(caches.ik_codes[seq].cpu().numpy(), oc.ik_codes)
-    assert np.array_equal(caches.ik_scales[seq].cpu().numpy(), oc.ik_scales)
+    if gpu is None:
+        gpu = gather_group_row(case, caches, snaps, qi, window)
+        oc = oracle_index_cache(wl, seq, case.index_fmt)
+    else:   # a thread of check_group_rows: a cache of its own, nothing shared
+        ik_c, ik_s = O.quantize_indexer(wl.index_k_latents(seq, 0, wl.seq_cap), case.index_fmt)
+        oc = O.PackedCaches(None, None, ik_c, ik_s, index_fmt=case.index_fmt)
+    assert np.array_equal(gpu["ik_codes"], oc.ik_codes)
+    assert np.array_equal(gpu["ik_scales"], oc.ik_scales)
     stats = {"set_diff": []}
     pool = None
     for L, mode in enumerate(wl.layers):
@@ -264,11 +307,11 @@ def check_group_query(case: Case, caches, snaps, qi: int, k: int = 512, window: 
             assert np.array_equal(idx, snaps[L - 1]["idx"][qi])   # borrowed, untouched
         sel = idx[:cnt]
         codes, scales, main = oracle_main_rows(wl, seq, sel)
-        assert np.array_equal(caches.kv_codes[seq][torch.from_numpy(sel).long().cuda()].cpu().numpy(), codes)
-        assert np.array_equal(caches.kv_scales[seq][torch.from_numpy(sel).long().cuda()].cpu().numpy(), scales)
+        assert np.array_equal(gpu["kv_codes"][L], codes)
+        assert np.array_equal(gpu["kv_scales"][L], scales)
         swa = O.quantize_fp8(swa_ring_latents(wl, L, seq))
         rows = np.mod(O.swa_positions(t, s, window) - wl.swa_base, wl.swa_cap)
-        assert np.array_equal(caches.swa[L][seq][torch.from_numpy(rows).cuda()].cpu().numpy(), swa[rows])
+        assert np.array_equal(gpu["swa"][L], swa[rows])
         _, _, _, qa = case.oracle_query(L, qi)
         ref, ref_lse = O.sparse_attention(qa, main, O.dequant_fp8(swa[rows]), 1.0 / math.sqrt(DIM))
         attn_close(snap["out"][qi], ref)

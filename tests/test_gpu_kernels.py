@@ -655,7 +655,10 @@ def test_sparse_attn_parity(C, heads, out_dt):
         sel = idx[qi][(idx[qi] >= 0) & (idx[qi] < 3001)]
         ref, ref_lse = O.sparse_attention(qa_np, oc.main_rows(sel),
                                           oc.swa_rows(0, O.swa_positions(t[qi], s[qi], 128)), 1 / math.sqrt(512))
-        G.attn_close(go[qi], ref, 2e-3 if out_dt == "f32" else 6e-3)
+        if out_dt == "f32":
+            G.attn_close(go[qi], ref, 2e-3)
+        else:
+            attn_close_bf16(go[qi], ref)
         assert np.abs(gl[qi] - ref_lse).max() <= 1e-3
 
 
@@ -783,6 +786,210 @@ def test_window_append_in_attention(C, select, dt):
     out_f, lse_f = attend(new)
     assert torch.equal(ring[flat_rows], ref_rows)
     assert torch.equal(out_f, out_r) and torch.equal(lse_f, lse_r)
+
+
+def _bf16(x: np.ndarray) -> torch.Tensor:
+    """float array -> bf16 device tensor (round to nearest even, as torch converts)."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda().to(torch.bfloat16)
+
+
+def _peaked_q(case, idx, counts, t, s, window, heads, rng):
+    """Attention Q whose logits are far from the N(0,1) of plain seeded Q: per head, Q is a
+    multiple of one key's post-RoPE latent (a main entry late in the index list, or a window
+    key), a scaled-up random vector, or plain N(0,1).  Then a later tile's logit exceeds the
+    running reference by much more than the kernel's lazy-rescale headroom, and the key
+    splits of a row end with widely separated maxima."""
+    wl = case.wl
+    n_q = len(t)
+    q = rng.standard_normal((n_q, heads, 512)).astype(np.float32)
+    for qi in range(n_q):
+        seq = int(wl.q_seq[qi])
+        win = O.swa_positions(t[qi], s[qi], window)
+        for h in range(heads):
+            kind = h % 4
+            if kind == 0 and counts[qi] > 0:      # one main entry, late in the list
+                j = int(idx[qi, max(0, counts[qi] - 1 - (h // 4) % 7 * 9)])
+                q[qi, h] = 3.0 * wl.main_latents(seq, j, 1)[0]
+            elif kind == 1 and win.size:          # one window key (its own token first)
+                p = int(win[max(0, win.size - 1 - (h // 4) % 5 * 17)])
+                lat = G.swa_ring_latents(wl, 0, seq)[(p - wl.swa_base) % wl.swa_cap]
+                q[qi, h] = 0.5 * lat + 0.1 * q[qi, h]
+            elif kind == 2:                       # broad but strongly peaked logits
+                q[qi, h] *= 6.0
+    return q
+
+
+def _attn_ref(case, qi, q_np, sel, t, s, window, sm_scale):
+    oc = case.oracle_caches(int(case.wl.q_seq[qi]))
+    return O.sparse_attention(q_np.astype(np.float64), oc.main_rows(sel),
+                              oc.swa_rows(0, O.swa_positions(t, s, window)), sm_scale)
+
+
+def attn_close_bf16(out_bf16: np.ndarray, ref: np.ndarray, tol: float = 2e-3):
+    """The bf16 output bar: every element within the fp32 bar (tol x max|ref|) plus one bf16
+    ulp of the reference element."""
+    ref = np.asarray(ref, np.float64)
+    mag = np.abs(ref)
+    ulp = np.where(mag > 0, np.ldexp(1.0, np.floor(np.log2(np.where(mag > 0, mag, 1.0))).astype(np.int64) - 7), 0.0)
+    err = np.abs(out_bf16.astype(np.float64) - ref)
+    bound = tol * mag.max() + ulp
+    assert np.all(err <= bound), f"bf16 output: {(err > bound).sum()} elements beyond fp32 bar + 1 ulp"
+
+
+@pytest.mark.parametrize("n_q,heads,sm", [(64, 64, None), (6, 16, None), (64, 64, 0.5), (6, 16, 0.5)])
+def test_sparse_attn_peaked_logits(C, n_q, heads, sm):
+    """Peaked attention: Q aligned with single keys placed late in the main list or in the
+    window, scaled-up random Q, or a large softmax scale (0.5 instead of 1/sqrt(512)) on
+    plain Q.  Later tiles beat the running reference by far more than the lazy-rescale
+    headroom (the accumulator rescale runs), and at 6 queries x 16 heads the key splits end
+    with widely separated maxima (the split merge runs).  fp32 and bf16 outputs; the bf16
+    output within the fp32 bar plus one bf16 ulp per element."""
+    _say("sparse_attn peaked", n_q, heads, sm)
+    rng = np.random.default_rng(1000 + n_q + heads)
+    t = [int(x) for x in rng.integers(600, 3000, size=n_q)]
+    s = [0 if i % 2 == 0 else max(0, ti - 60) for i, ti in enumerate(t)]
+    case = _attn_case(31 + n_q, n_q, 3001, heads, t, s)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_seq, _, q_pos, rs = case.gpu_meta()
+    k = 512
+    counts = [k if i % 3 else int(rng.integers(100, k)) for i in range(n_q)]
+    idx = np.full((n_q, k), -1, np.int32)
+    for qi in range(n_q):
+        idx[qi, :counts[qi]] = np.sort(rng.choice(t[qi] + 1, size=counts[qi], replace=False))
+    if sm is None:
+        sm_scale = 1.0 / math.sqrt(512)
+        q_np = _peaked_q(case, idx, counts, t, s, 128, heads, rng)
+    else:
+        sm_scale = sm
+        q_np = rng.standard_normal((n_q, heads, 512)).astype(np.float32)
+    qa = _bf16(q_np)
+    q_exact = qa.float().cpu().numpy()
+    idx_t = torch.from_numpy(idx).cuda()
+    outs = {}
+    for dt in (torch.float32, torch.bfloat16):
+        out = torch.empty(n_q, heads, 512, dtype=dt, device="cuda")
+        lse = torch.empty(n_q, heads, dtype=torch.float32, device="cuda")
+        C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, idx_t, caches.swa[0], caches.swa_base,
+                           q_pos, rs, 128, sm_scale, out, lse)
+        torch.cuda.synchronize()
+        outs[dt] = (out.float().cpu().numpy(), lse.cpu().numpy())
+    assert C.csa2_device_status() == 0
+    peaked = 0
+    for qi in range(n_q):
+        oc = case.oracle_caches(int(wl.q_seq[qi]))
+        keys = np.concatenate([oc.main_rows(idx[qi, :counts[qi]]),
+                               oc.swa_rows(0, O.swa_positions(t[qi], s[qi], 128))])
+        logit2 = sm_scale * (q_exact[qi].astype(np.float64) @ keys.T) / math.log(2.0)
+        peaked += int((logit2.max(axis=1) - np.median(logit2, axis=1) > 8.0).sum())
+        ref, ref_lse = _attn_ref(case, qi, q_exact[qi], idx[qi, :counts[qi]], t[qi], s[qi], 128, sm_scale)
+        G.attn_close(outs[torch.float32][0][qi], ref, 2e-3)
+        attn_close_bf16(outs[torch.bfloat16][0][qi], ref)
+        assert np.abs(outs[torch.float32][1][qi] - ref_lse).max() <= 1e-3
+        assert np.array_equal(outs[torch.bfloat16][1][qi], outs[torch.float32][1][qi])
+    # the inputs are what the test is for: most heads' largest logit stands more than the
+    # lazy-rescale headroom (2^8) above the typical one
+    assert peaked >= n_q * heads // 2, (peaked, n_q * heads)
+
+
+@pytest.mark.parametrize("mag", [1e6, 1e30, 1e-12, 1e-30])
+def test_sparse_attn_bf16_q_full_range(C, mag):
+    """Q far outside fp16's range (|q| up to ~1e31) or deep in its subnormals (~1e-31), with
+    the softmax scale compensating so the logits are ordinary: the per-head power-of-two
+    scale keeps every Q value exact, so the result matches the oracle as for unit Q.  Also
+    a head of zeros (uniform weights) and, in one row, heads of very different magnitudes."""
+    _say("sparse_attn bf16 Q range", mag)
+    rng = np.random.default_rng(int(abs(math.log10(mag))))
+    n_q, heads = 6, 32
+    t = [2000 - 111 * i for i in range(n_q)]
+    s = [0] * n_q
+    case = _attn_case(77, n_q, 2001, heads, t, s)
+    caches = case.gpu_caches()
+    q_seq, _, q_pos, rs = case.gpu_meta()
+    idx = np.stack([np.sort(rng.choice(t[i] + 1, size=512, replace=False)) for i in range(n_q)]).astype(np.int32)
+    q_np = rng.standard_normal((n_q, heads, 512)) * mag
+    q_np[0, 3] = 0.0                                    # an all-zero head
+    q_np[1, 5] *= 1e-3                                  # heads of another magnitude in the row
+    q_np[1, 6] *= 1e3
+    sm_scale = 1.0 / (math.sqrt(512) * mag)
+    qa = _bf16(q_np)
+    q_exact = qa.float().cpu().numpy()
+    out = torch.empty(n_q, heads, 512, dtype=torch.float32, device="cuda")
+    lse = torch.empty(n_q, heads, dtype=torch.float32, device="cuda")
+    C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, torch.from_numpy(idx).cuda(), caches.swa[0],
+                       caches.swa_base, q_pos, rs, 128, sm_scale, out, lse)
+    torch.cuda.synchronize()
+    go, gl = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+    for qi in range(n_q):
+        ref, ref_lse = _attn_ref(case, qi, q_exact[qi], idx[qi], t[qi], s[qi], 128, sm_scale)
+        G.attn_close(go[qi], ref, 2e-3)
+        assert np.abs(gl[qi] - ref_lse).max() <= 1e-3 * max(1.0, np.abs(ref_lse).max() * 1e-4)
+
+
+def test_device_status_reports_an_expired_wait(C):
+    """The status path of the attention's bounded partner wait, forced from the host: with
+    a wait bound of 0 polls every exchange gives up at once (the kernel still completes, with
+    a wrong output); the kernel stores its code into the device status word, the next call
+    returns CSA2_ERR_DEVICE without launching and names the cause, and once the bound is
+    restored the same call is correct again."""
+    _say("device status")
+    t, s = [1500, 1400], [0, 0]
+    case = _attn_case(5, 2, 1501, 16, t, s)
+    caches = case.gpu_caches()
+    _, _, qa = case.gpu_query_inputs(0)
+    q_seq, _, q_pos, rs = case.gpu_meta()
+    rng = np.random.default_rng(5)
+    idx = np.stack([np.sort(rng.choice(1401, size=512, replace=False)) for _ in range(2)]).astype(np.int32)
+    idx_t = torch.from_numpy(idx).cuda()
+    out = torch.empty(2, 16, 512, dtype=torch.float32, device="cuda")
+    lse = torch.empty(2, 16, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(C.csa2_attn_workspace_bytes(2, 16, 512, 512, 128), 1), dtype=torch.uint8, device="cuda")
+
+    def attend():
+        C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, idx_t, caches.swa[0], caches.swa_base, q_pos,
+                           rs, 128, 1.0 / math.sqrt(512), out, lse, workspace=ws)
+        torch.cuda.synchronize()
+
+    C.csa2_device_status(clear=True)
+    prev = C.csa2_debug_set_wait_limit(0)
+    try:
+        attend()
+    finally:
+        C.csa2_debug_set_wait_limit(prev)
+    assert C.csa2_device_status() == 1                   # CSA2_STATUS_ATTN_WAIT
+    with pytest.raises(C.Csa2Error, match=r"\(-6\).*partner"):
+        attend()
+    assert C.csa2_device_status() == 0                   # reported once, then cleared
+    attend()
+    assert C.csa2_device_status() == 0
+    for qi in range(2):
+        _, _, _, qa_np = case.oracle_query(0, qi)
+        ref, ref_lse = _attn_ref(case, qi, qa_np, idx[qi], t[qi], s[qi], 128, 1.0 / math.sqrt(512))
+        G.attn_close(out[qi].cpu().numpy(), ref, 2e-3)
+
+
+def test_binding_refuses_unsafe_calls(C):
+    """The binding's own checks: a bound call that would need a temporary workspace is
+    refused (the callable would keep a pointer to freed memory), and a window append whose
+    rows share a sequence is refused (its ring writes would race with the other rows' reads)."""
+    _say("binding checks")
+    t, s = [900, 800, 700], [0, 0, 0]
+    case = _attn_case(9, 3, 901, 16, t, s)
+    caches = case.gpu_caches()
+    _, _, qa = case.gpu_query_inputs(0)
+    q_seq, _, q_pos, rs = case.gpu_meta()
+    idx = torch.full((3, 512), -1, dtype=torch.int32, device="cuda")
+    out = torch.empty(3, 16, 512, dtype=torch.float32, device="cuda")
+    assert C.csa2_attn_workspace_bytes(3, 16, 512, 512, 128) > 0
+    with pytest.raises(ValueError, match="bound call needs a caller-owned workspace"):
+        C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, idx, caches.swa[0], caches.swa_base, q_pos,
+                           rs, 128, 0.05, out, _bind=True)
+    new = torch.zeros(3, 512, dtype=torch.float32, device="cuda")
+    dup = torch.tensor([0, 1, 0], dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="share a sequence"):
+        C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, dup, idx, caches.swa[0], caches.swa_base, q_pos,
+                           rs, 128, 0.05, out, new_win=new)
 
 
 def test_sparse_attn_no_keys(C):

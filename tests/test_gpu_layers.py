@@ -26,17 +26,22 @@ def C():
     return csa2
 
 
-@pytest.mark.timeout(600)
+ALL = None   # every query row of the workload
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,samples,fused,attn_select", [
-    ("c2", (0, 63), True, False), ("c2", (0, 63), True, True), ("c3", (0, 13, 31), True, False),
-    ("c3", (0, 13, 31), False, False), ("c3", (0, 13, 31), True, True), ("c4", (0, 5), True, False),
-    ("c4", (0, 5), False, False), ("c4", (0, 5), True, True)])
+    ("c2", (0, 63), True, False), ("c2", ALL, True, True), ("c3", (0, 13, 31), True, False),
+    ("c3", (0, 13, 31), False, False), ("c3", ALL, True, True), ("c4", (0, 5), True, False),
+    ("c4", (0, 5), False, False), ("c4", ALL, True, True)])
 def test_layer_group_full_size(C, name, samples, fused, attn_select):
-    """Every layer of a group at full size against the oracle on sampled queries: fused
-    scoring + selection, two calls, and the last Top-K level inside the attention call.  The
-    cases with the selection inside attention run as the single-token decode step is
-    benchmarked: each row's own window entry is appended by the attention call (its ring
-    row zeroed beforehand); the others attend over a prefilled ring."""
+    """Every layer of a group at full size against the oracle: fused scoring + selection,
+    two calls, and the last Top-K level inside the attention call.  The cases with the
+    selection inside attention run as the single-token decode step is benchmarked (each
+    row's own window entry appended by the attention call, its ring row zeroed beforehand)
+    and are checked on every query row: index set and pool by the acceptance rule, cache
+    bytes, and attention.  The other variants attend over a prefilled ring and are checked
+    on sampled rows."""
     _say("layer group", name, "fused" if fused else "two-call", "select in attention" if attn_select else "")
     from fp4_kv_cache_layer_amd.layer import Csa2Step
     wl = workloads.config(name)
@@ -47,9 +52,9 @@ def test_layer_group_full_size(C, name, samples, fused, attn_select):
     # inside the pool) moves into the attention call
     assert (step.attn_select or step.pool_select) == attn_select
     snaps = G.run_group_snapshots(case, step, caches, fused_window=attn_select)
-    for qi in samples:
-        _say("  oracle query", qi)
-        G.check_group_query(case, caches, snaps, qi)
+    rows = range(wl.n_q) if samples is ALL else samples
+    _say("  oracle rows", len(rows))
+    G.check_group_rows(case, caches, snaps, rows, workers=8 if wl.seq_cap > (1 << 18) else 16)
     del caches, step
     torch.cuda.empty_cache()
 
