@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import functools
 import math
+import threading
 
 import numpy as np
 import torch
@@ -251,10 +252,28 @@ def gather_group_row(case: Case, caches, snaps, qi: int, window: int = 128) -> d
     return g
 
 
+# The oracle's matrix products (scores over a whole cache, attention logits) go through the
+# BLAS library, whose own thread pool is not to be entered by several of our threads at once:
+# concurrent 1M-entry products from a thread pool gave wrong scores on a 16-core host.  Those
+# calls take this lock; the quantisation (most of the oracle's time) stays parallel.
+_BLAS_LOCK = threading.Lock()
+
+
+def _full_scores(*a, **kw):
+    with _BLAS_LOCK:
+        return O.full_scores(*a, **kw)
+
+
+def _sparse_attention(*a, **kw):
+    with _BLAS_LOCK:
+        return O.sparse_attention(*a, **kw)
+
+
 def check_group_rows(case: Case, caches, snaps, rows, workers: int = 8, **kw) -> list:
     """check_group_query for many rows: the device bytes are read first on this thread,
     then the oracle work runs on a thread pool (numpy releases the interpreter lock in its
-    array loops).  The first failing row raises, with its row number."""
+    array loops; the BLAS calls are serialised).  The first failing row raises, with its row
+    number."""
     from concurrent.futures import ThreadPoolExecutor
     rows = list(rows)
     data = {qi: gather_group_row(case, caches, snaps, qi, kw.get("window", 128)) for qi in rows}
@@ -297,7 +316,7 @@ def check_group_query(case: Case, caches, snaps, qi: int, k: int = 512, window: 
             if mode == "reindex_pool":
                 pool_pos = O.pool_positions(pool, nv, block)
                 cand = pool_pos
-            pos, sc = O.full_scores(qc, qs, w, oc, nv, cand)
+            pos, sc = _full_scores(qc, qs, w, oc, nv, cand)
             stats["set_diff"].append(topk_accept(idx, cnt, pos, sc, k))
             if mode == "full_pool":
                 bs = O.block_scores(sc, nv, block)
@@ -313,7 +332,7 @@ def check_group_query(case: Case, caches, snaps, qi: int, k: int = 512, window: 
         rows = np.mod(O.swa_positions(t, s, window) - wl.swa_base, wl.swa_cap)
         assert np.array_equal(gpu["swa"][L], swa[rows])
         _, _, _, qa = case.oracle_query(L, qi)
-        ref, ref_lse = O.sparse_attention(qa, main, O.dequant_fp8(swa[rows]), 1.0 / math.sqrt(DIM))
+        ref, ref_lse = _sparse_attention(qa, main, O.dequant_fp8(swa[rows]), 1.0 / math.sqrt(DIM))
         attn_close(snap["out"][qi], ref)
         assert np.abs(snap["lse"][qi] - ref_lse).max() <= 1e-3
     return stats
