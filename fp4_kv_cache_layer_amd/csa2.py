@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         "csa2_sparse_attn": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp, vp, vp, vp, i32, i32, f32,
                               vp, i32, vp, vp, sz, vp], i32),
         "csa2_attn_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
+        "csa2_sparse_attn_noalloc": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp, vp, vp, vp, i32,
+                                      i32, f32, vp, i32, vp, vp], i32),
+        "csa2_sparse_attn_noalloc_max_bytes": ([], sz),
         "csa2_index_segments": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp], i32),
         "csa2_index_segments_nvfp4": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp], i32),
         "csa2_segment_keys": ([i64, i32], i64),
@@ -572,3 +575,23 @@ def csa2_sparse_attn(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, r
                                      k, _p(swa), swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), nw, nwt, window,
                                      ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes,
                                      _stream()), _bind)
+
+
+def csa2_sparse_attn_noalloc_max_bytes() -> int:
+    return int(lib().csa2_sparse_attn_noalloc_max_bytes())
+
+
+def csa2_sparse_attn_noalloc(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, replay_start, window: int,
+                             sm_scale: float, out, lse=None, new_win=None, _bind: bool = False):
+    """csa2_sparse_attn without a workspace: a split key list's partials go to the library's
+    static per-GPU scratch (calls that overlap on one GPU race).  Arguments as csa2_sparse_attn."""
+    _need(idx, torch.int32, 2, "idx")
+    _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, idx.shape[0])
+    n_q, H, D = q.shape
+    n_seq, seq_cap, _ = kv_codes.shape
+    odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
+    nw, nwt = _new_win(new_win, n_q, D, q_seq)
+    return _run("csa2_sparse_attn_noalloc", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq),
+                                             _p(idx), idx.shape[1], _p(swa), swa.shape[1], _p(swa_base), _p(q_pos),
+                                             _p(replay_start), nw, nwt, window, ctypes.c_float(sm_scale), _p(out),
+                                             odt, _p(lse), _stream()), _bind)

@@ -79,6 +79,10 @@ extern "C" int csa2_init(void) {
     strncpy(g_last_error, prop.gcnArchName, sizeof(g_last_error) - 1);
     return CSA2_ERR_UNSUPPORTED;
   }
+  {   // the no-allocation attention entry point's static scratch on this device
+    int src = CSA2_OK;
+    if (!csa2_attn_scratch(&src)) return src != CSA2_OK ? src : CSA2_ERR_HIP;
+  }
   std::call_once(g_status_once, [] {
     void* h = nullptr;
     int rc = csa2_record_hip_error(

@@ -47,6 +47,8 @@
 // the last Top-K level (the index set selected from the first level's survivors or from
 // the pool's slot scores; see k_attn's kSel) and, in single-token decode, the append of the
 // row's own window entry (new_win).
+#include <mutex>
+
 #include "select.h"
 
 namespace csa2 {
@@ -915,6 +917,61 @@ extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, co
   return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, idx, sel, nullptr, nullptr, k,
                      swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window, sm_scale, out,
                      out_dtype, lse, workspace, workspace_bytes, stream);
+}
+
+// ---- the no-allocation variant: the split partials live in a static device array ----
+// Each GPU the library runs on holds its own copy of `scratch` (at its own address) until the
+// process ends.  Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in symbol): the device address comes from hipGetSymbolAddress, once per device,
+// with that device current, and is kept per device.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices] = {};
+static std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (nullptr and a recorded HIP error if the
+// runtime cannot give it).  Called by csa2_init and, for a device csa2_init never saw, by the
+// entry point's first call there.
+void* csa2_attn_scratch(int* rc_out) {
+  int dev = 0;
+  int rc = csa2_record_hip_error(hipGetDevice(&dev));
+  if (rc == CSA2_OK && (dev < 0 || dev >= kMaxDevices)) rc = CSA2_ERR_UNSUPPORTED;
+  if (rc != CSA2_OK) {
+    *rc_out = rc;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    rc = csa2_record_hip_error(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (rc == CSA2_OK) g_scratch_ptr[dev] = p;
+  }
+  *rc_out = rc;
+  return g_scratch_ptr[dev];
+}
+
+extern "C" size_t csa2_sparse_attn_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int csa2_sparse_attn_noalloc(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
+                                        const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                                        const int32_t* idx, int k, uint8_t* swa, int64_t swa_cap,
+                                        const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
+                                        const void* new_win, int new_win_dtype, int window, float sm_scale,
+                                        void* out, int out_dtype, float* lse, void* stream) {
+  const size_t need = csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window);
+  if (need > kScratchBytes) return CSA2_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    int rc = CSA2_OK;
+    ws = csa2_attn_scratch(&rc);
+    if (!ws) return rc != CSA2_OK ? rc : CSA2_ERR_HIP;
+  }
+  AttnSel sel = {};
+  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, idx, sel, nullptr, nullptr, k,
+                     swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window, sm_scale, out,
+                     out_dtype, lse, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
 extern "C" int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,

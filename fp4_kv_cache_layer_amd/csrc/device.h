@@ -125,3 +125,6 @@ int csa2_check_launch();
 uint32_t* csa2_status_word();
 int csa2_wait_limit();
 int csa2_take_device_status();
+// Device address of the no-allocation attention entry point's static scratch on the current
+// device (looked up once per device; nullptr with *rc set on failure).
+void* csa2_attn_scratch(int* rc);

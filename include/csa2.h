@@ -447,6 +447,31 @@ int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t
 size_t csa2_attn_workspace_bytes(int n_q, int n_heads, int dim, int k, int window);
 
 /*
+ * csa2_sparse_attn_noalloc -- csa2_sparse_attn for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels and results, with no workspace argument.  When the key list is split over
+ * workgroups, the partial results go to a static device array of the library's own,
+ * csa2_sparse_attn_noalloc_max_bytes() = 16 MiB per GPU, held from the library's load until
+ * the process ends; csa2_init (or this call's first use on a device) looks up its address
+ * once per device.  The call allocates nothing and calls no allocating routine.
+ *   Arguments: those of csa2_sparse_attn without workspace / workspace_bytes.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ *   (different streams, or different threads) race and give undefined results.  No part of
+ *   the array needs to start at zero (each call writes every partial it reads).
+ * Errors: those of csa2_sparse_attn; CSA2_ERR_WORKSPACE when the call would need more than
+ * the static array holds (csa2_attn_workspace_bytes(...) > 16 MiB: the key list is split
+ * only while fewer than 256 (query, 16-head group) pairs exist, which keeps every accepted
+ * shape within 16 MiB); CSA2_ERR_HIP if the array's address cannot be had.
+ */
+int csa2_sparse_attn_noalloc(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
+                             const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                             const int32_t* idx, int k, uint8_t* swa, int64_t swa_cap,
+                             const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
+                             const void* new_win, int new_win_dtype, int window, float sm_scale, void* out,
+                             int out_dtype, float* lse, void* stream);
+size_t csa2_sparse_attn_noalloc_max_bytes(void);
+
+/*
  * csa2_sparse_attn_topk -- csa2_sparse_attn whose index set is selected in the same call
  * from csa2_index_segments' keys: the Top-k of the keys (score descending, position
  * ascending), as ascending positions, -1 padded -- exactly what csa2_index_topk returns for
