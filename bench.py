@@ -51,7 +51,8 @@ class LayerBench:
     (`swa_miss`: the prefix's window state is not cached) the rings start empty and every
     layer writes the window entries of all its query rows, replay rows included."""
 
-    def __init__(self, wl, torch, C, group: int = 1, index_fmt: str = "mxfp4", attn_select: bool = True):
+    def __init__(self, wl, torch, C, group: int = 1, index_fmt: str = "mxfp4", attn_select: bool = True,
+                 fused: bool = True):
         from fp4_kv_cache_layer_amd.layer import INDEX_FORMATS, Caches, Csa2Step, plan_group
         self.wl, self.torch, self.C = wl, torch, C
         self.ik_fmt, self.ik_group = INDEX_FORMATS[index_fmt]
@@ -112,9 +113,10 @@ class LayerBench:
         self.dst_entry = torch.from_numpy(ent_seq * wl.seq_cap + ent_row).to(dev)
         self.dst_swa = torch.from_numpy(tok_seq * wl.swa_cap + (tok_pos - wl.swa_base) % wl.swa_cap).to(dev)
         self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group, index_fmt=index_fmt,
-                             attn_select=attn_select)
-        self.plan = plan_group(wl.layers, group=group, index_fmt=index_fmt, attn_select=self.step.attn_select,
-                               pool_select=self.step.pool_select)
+                             attn_select=attn_select, fused=fused)
+        self.plan = plan_group(wl.layers, fused=fused, group=group, index_fmt=index_fmt,
+                               attn_select=self.step.attn_select, pool_select=self.step.pool_select,
+                               group_select=self.step.group_select)
 
     def calls(self, L: int):
         """Layer L's step as {phase: bound call} bound to the current stream, in order."""
@@ -141,6 +143,8 @@ class LayerBench:
         nw = self.new_swa[L] if self.fuse_window else None
         if mode == "full_pool":
             out["index_topk_pool"] = st.index_topk_build_pool(c, w, self.q_seq, self.n_vis, bind=True)
+        elif "index_topk_grouped" in names:   # grouped rows scored and selected, no score array
+            out["index_topk_grouped"] = st.index_topk_grouped(c, w, self.q_seq, self.n_vis, bind=True)
         elif "score_grouped" in names:
             out["score"] = st.score_grouped(c, w, self.q_seq, self.n_vis, bind=True)
             out["select"] = st.select(self.n_vis, bind=True)
@@ -344,14 +348,14 @@ def cpu_baseline(wl, n_sample: int, reps: int):
 
 
 def measure_layers(name, steps, warmup, torch, C, layers_to_time, group: int = 1, index_fmt: str = "mxfp4",
-                   attn_select: bool = True):
+                   attn_select: bool = True, fused: bool = True):
     """Graph-replay time of each listed layer's step (`steps` steps in graphs of
     steps_per_graph(steps) consecutive steps of that layer) and of the whole group (one
     group per graph); isolated launch times of the first listed layer's calls."""
     from synth import workloads
     wl = workloads.config(name)
     log(f"workload {name}: {wl.description}")
-    lb = LayerBench(wl, torch, C, group, index_fmt, attn_select)
+    lb = LayerBench(wl, torch, C, group, index_fmt, attn_select, fused)
     res = {"wl": wl, "layers": {}}
     G = steps_per_graph(steps)
     res["per_graph"] = G

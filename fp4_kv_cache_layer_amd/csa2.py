@@ -63,6 +63,9 @@ def lib() -> ctypes.CDLL:
         "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp,
                              sz, vp], i32),
         "csa2_index_topk_workspace_bytes": ([i32, i64, i32, i32], sz),
+        "csa2_index_topk_grouped": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, sz,
+                                     vp], i32),
+        "csa2_index_topk_grouped_workspace_bytes": ([i32, i64, i32, i32], sz),
         "csa2_index_score_nvfp4": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64,
                                     vp], i32),
         "csa2_index_topk_nvfp4": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp,
@@ -311,6 +314,27 @@ def csa2_index_score_grouped(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_v
     if scores.shape[0] != q_codes.shape[0]:
         raise ValueError("index_score_grouped: scores rows != n_q")
     return _run("csa2_index_score_grouped", args[:12] + (int(group), _p(scores), scores.stride(0), _stream()), _bind)
+
+
+def csa2_index_topk_grouped_workspace_bytes(n_q: int, seq_cap: int, k: int, group: int) -> int:
+    return int(lib().csa2_index_topk_grouped_workspace_bytes(n_q, seq_cap, k, group))
+
+
+def csa2_index_topk_grouped(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, group: int, k: int, idx_out,
+                            count_out, workspace=None, _bind: bool = False):
+    """Grouped rows scored and selected without a score array: the operands of
+    csa2_index_score_grouped -> idx_out [n_q, k] int32, count_out [n_q] int32, as
+    csa2_index_score_grouped followed by csa2_topk returns them."""
+    args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8)
+    _need(idx_out, torch.int32, 2, "idx_out")
+    _need(count_out, torch.int32, 1, "count_out")
+    n_q = q_codes.shape[0]
+    if idx_out.shape != (n_q, k) or count_out.shape[0] != n_q:
+        raise ValueError("index_topk_grouped: inconsistent output shapes")
+    need = csa2_index_topk_grouped_workspace_bytes(n_q, k_codes.shape[1], k, int(group))
+    workspace, ws_bytes = _workspace(need, workspace, q_codes.device, _bind, "index_topk_grouped")
+    return _run("csa2_index_topk_grouped", args[:12] + (int(group), k, _p(idx_out), _p(count_out), _p(workspace),
+                                                        ws_bytes, _stream()), _bind)
 
 
 def csa2_index_topk_workspace_bytes(n_q: int, n_slots: int, k: int, in_pool: bool = False) -> int:

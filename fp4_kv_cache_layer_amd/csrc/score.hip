@@ -384,6 +384,146 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_grouped(ScoreArgs s, in
   }
 }
 
+// ---- grouped rows, scored and selected in one pass: no score array ----
+// The rows of a prefill chunk (or several decode tokens of one sequence) each need their own
+// Top-K over the sequence's visible entries.  A workgroup takes a group of up to kGroupMax
+// rows and a contiguous range of entries; each of its four waves owns kGtRowsPerWave of the
+// rows and streams the whole range (the waves read the same K tiles at about the same time,
+// so three of the four loads hit the L1 cache), scoring its rows on every 64-entry step.
+// Per row the owning wave keeps a list of candidate keys in LDS: an entry enters only if its
+// key is at or above the row's threshold, and when the list is about to overflow the wave
+// selects its best K in place (select_wave, stable) and raises the threshold to the K-th key:
+// keys below it can never reach the row's Top-K.  A list is written by its wave alone, in
+// position order (entries are appended in order, the selection keeps the order), so no wave
+// ever waits for another.  At the end of the range each row's best K, in position order, is
+// what a first Top-K level writes for that range, and the last level (k_topk_final) picks the
+// row's Top-K over the ranges.  Appends per row over R entries in random order: about
+// K * (1 + ln(R / K)).
+constexpr int kGtRowsPerWave = kGroupMax / (kScoreThreads / 64);   // 2
+constexpr int kGtCap = 768;                                        // candidate keys per row in LDS
+
+__global__ __launch_bounds__(kScoreThreads) void k_score_topk_grouped(ScoreArgs s, int n_q, int group,
+                                                                      int range_len, int n_ranges) {
+  const int range = blockIdx.x;    // consecutive workgroups take consecutive ranges, so one
+  const int gi = blockIdx.y;       // range's workgroups share an XCD (and its L2) when n_ranges | 8
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane & 15, kb = lane >> 4;
+  const int r0 = gi * group;
+  const int nr = n_q - r0 < group ? n_q - r0 : group;
+  const int K = s.k;
+  __shared__ __attribute__((aligned(16))) uint64_t list[kGroupMax][kGtCap];          // 48 KB
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kScoreThreads / 64][256];   // per wave
+
+  const int seq = s.q_seq[r0];
+  const bool seq_ok = seq >= 0 && seq < s.n_seq;
+  // this wave's rows: group rows wave, wave + 4 (so a group of 4 rows or fewer still spreads
+  // over the waves)
+  uint4 qa[kGtRowsPerWave];
+  int asc[kGtRowsPerWave];
+  float wv[kGtRowsPerWave][4];
+  int nvr[kGtRowsPerWave];
+  bool own[kGtRowsPerWave];
+  int nv_max = 0;
+#pragma unroll
+  for (int u = 0; u < kGtRowsPerWave; ++u) {
+    const int r = wave + (kScoreThreads / 64) * u;
+    const int q = r0 + r;
+    own[u] = r < nr;
+    const bool ok = seq_ok && own[u] && s.q_seq[q] == seq;
+    int64_t v = ok ? s.n_vis[q] : 0;
+    nvr[u] = (int)(v < 0 ? 0 : (v > s.seq_cap ? s.seq_cap : v));
+    nv_max = nvr[u] > nv_max ? nvr[u] : nv_max;
+    qa[u] = make_uint4(0u, 0u, 0u, 0u);
+    asc[u] = 127;
+    if (ok && row < s.n_heads) {
+      const int64_t hr = (int64_t)q * s.n_heads + row;
+      qa[u] = *reinterpret_cast<const uint4*>(s.q_codes + hr * 64 + kb * 16);
+      asc[u] = s.q_scales[hr * 4 + kb];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 4 * kb + j;
+      wv[u][j] = ok && h < s.n_heads ? s.w[(int64_t)q * s.n_heads + h] : 0.0f;
+    }
+  }
+  const int lo = range * range_len;
+  const int hi = lo + range_len < nv_max ? lo + range_len : nv_max;   // uniform over the wave
+  const uint8_t* kc = s.k_codes + (int64_t)(seq_ok ? seq : 0) * s.seq_cap * 64;
+  const uint8_t* ks = s.k_scales + (int64_t)(seq_ok ? seq : 0) * s.seq_cap * 4;
+  auto load_step = [&](int base, uint4 (&bc)[4], int (&bs)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int e = base + 16 * t + row;
+      const uint32_t pos = e < hi ? (uint32_t)e : 0u;
+      const v4u v = *reinterpret_cast<const v4u*>(kc + (pos * 64u + kb * 16u));
+      bc[t] = make_uint4(v.x, v.y, v.z, v.w);
+      bs[t] = ks[pos * 4u + kb];
+    }
+  };
+  int cnt[kGtRowsPerWave];
+  uint64_t thr[kGtRowsPerWave];
+#pragma unroll
+  for (int u = 0; u < kGtRowsPerWave; ++u) {
+    cnt[u] = 0;
+    thr[u] = 1ull;   // every real key (nonzero) enters until the first selection
+  }
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+
+  // the best K of list u, in place and in order; raises its threshold
+  auto shrink = [&](int u) {
+    uint64_t* l = list[wave + (kScoreThreads / 64) * u];
+    uint64_t key[kGtCap / 64];
+#pragma unroll
+    for (int i = 0; i < kGtCap / 64; ++i) {
+      const int j = i * 64 + lane;
+      key[i] = j < cnt[u] ? l[j] : 0ull;
+    }
+    const uint64_t t = select_wave<kGtCap / 64>(key, K, hist[wave], l);
+    thr[u] = t > thr[u] ? t : thr[u];
+    cnt[u] = cnt[u] < K ? cnt[u] : K;
+  };
+
+  if (lo < hi) {
+    uint4 bc[4];
+    int bs[4];
+    load_step(lo, bc, bs);
+    for (int base = lo; base < hi; base += 64) {
+      uint4 bcn[4];
+      int bsn[4];
+      load_step(base + 64 < hi ? base + 64 : base, bcn, bsn);
+      const int e = base + lane;
+#pragma unroll
+      for (int u = 0; u < kGtRowsPerWave; ++u) {
+        if (nvr[u] > base) {   // uniform
+          const v8i a = {(int)qa[u].x, (int)qa[u].y, (int)qa[u].z, (int)qa[u].w, 0, 0, 0, 0};
+          const float v = score_tiles(a, asc[u], wv[u], kb, bc, bs);
+          const uint64_t key = make_key(v, (uint32_t)e);
+          const bool in = e < hi && e < nvr[u] && key >= thr[u];   // past hi: the next range's entry
+          const uint64_t m = __ballot(in);
+          if (in) list[wave + (kScoreThreads / 64) * u][cnt[u] + (int)__popcll(m & lt_mask)] = key;
+          cnt[u] += (int)__popcll(m);
+          if (cnt[u] > kGtCap - 64) shrink(u);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bc[t] = bcn[t];
+        bs[t] = bsn[t];
+      }
+    }
+  }
+  // each row's best K of this range, in position order, zero padded
+#pragma unroll
+  for (int u = 0; u < kGtRowsPerWave; ++u) {
+    if (!own[u]) continue;
+    if (cnt[u] > K) shrink(u);
+    const uint64_t* l = list[wave + (kScoreThreads / 64) * u];
+    uint64_t* o = s.keys_out + ((int64_t)(r0 + wave + (kScoreThreads / 64) * u) * n_ranges + range) * K;
+    for (int j = lane; j < K; j += 64) o[j] = j < cnt[u] ? l[j] : 0ull;
+  }
+}
+
 template <bool kPool, bool kNv, bool kQLat = false>
 __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
   const int q = blockIdx.x / s.chunks;
@@ -835,6 +975,64 @@ extern "C" int csa2_index_segments_nvfp4(const uint8_t* q_codes, const uint8_t* 
   if (int rc_status = csa2_take_device_status()) return rc_status;
   return index_segments(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq,
                         n_vis, k, cand_keys, stream);
+}
+
+// ---- csa2_index_topk_grouped: grouped rows, scored and selected without a score array ----
+// Ranges per row: a power of two (so that, with consecutive workgroups on consecutive XCDs,
+// one range's workgroups share an XCD and its L2 holds the range's indexer K), with all
+// ranges' survivors within one last selection level (n_ranges * k <= 8,192) and ranges of at
+// least 8,192 entries; as many as that allows while the grid is below 3 workgroups per CU
+// (the LDS of the candidate lists fits three), and at least 16,384 entries per range beyond.
+static int grouped_ranges(int64_t seq_cap, int k, int64_t n_groups) {
+  int n = 1;
+  auto ok = [&](int m) { return m <= 16 && (int64_t)m * k <= kTkSeg && seq_cap >= (int64_t)m * 8192; };
+  while (ok(2 * n) && (n_groups * n < 3 * 256 || seq_cap >= (int64_t)2 * n * 16384)) n *= 2;
+  return n;
+}
+
+extern "C" size_t csa2_index_topk_grouped_workspace_bytes(int n_q, int64_t seq_cap, int k, int group) {
+  if (n_q <= 0 || seq_cap < 0 || k < 1 || k > CSA2_MAX_GROUPED_TOPK || group < 1 || group > kGroupMax) return 0;
+  return (size_t)n_q * grouped_ranges(seq_cap, k, (n_q + group - 1) / group) * k * sizeof(uint64_t) + 256;
+}
+
+extern "C" int csa2_index_topk_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                                       int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                                       int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                                       int group, int k, int32_t* idx_out, int32_t* count_out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
+  int64_t n_slots = 0;
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+                            nullptr, nullptr, 8, 1, &n_slots);
+  if (rc != CSA2_OK) return rc;
+  if (!idx_out || !count_out) return CSA2_ERR_NULL;
+  if (group < 1 || group > kGroupMax || k < 1 || k > CSA2_MAX_GROUPED_TOPK || n_q > 65535 * group)
+    return CSA2_ERR_SHAPE;
+  if (n_q == 0) return CSA2_OK;
+  const size_t need = csa2_index_topk_grouped_workspace_bytes(n_q, seq_cap, k, group);
+  if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+  const int n_groups = (n_q + group - 1) / group;
+  const int n_ranges = grouped_ranges(seq_cap, k, n_groups);
+  int64_t range_len = (seq_cap + n_ranges - 1) / n_ranges;
+  range_len = (range_len + 63) / 64 * 64;
+  if (range_len < 64) range_len = 64;
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, nullptr,
+                          nullptr, 8, 1, n_slots);
+  a.k = k;
+  a.keys_out = (uint64_t*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(k_score_topk_grouped, dim3((unsigned)n_ranges, (unsigned)n_groups), dim3(kScoreThreads), 0, st,
+                     a, n_q, group, (int)range_len, n_ranges);
+  rc = csa2_check_launch();
+  if (rc != CSA2_OK) return rc;
+  const int64_t segs[2] = {n_ranges, 1};
+  TkArgs t = {};
+  t.n_vis = n_vis;
+  t.max_vis = seq_cap;
+  t.k = k;
+  t.idx_out = idx_out;
+  t.count_out = count_out;
+  return select_levels_after0(segs, 2, t, n_q, a.keys_out, nullptr, st);
 }
 
 extern "C" size_t csa2_index_topk_pool_workspace_bytes(int n_q, int64_t n_slots, int k, int block, int max_blocks) {

@@ -86,10 +86,16 @@ __device__ __forceinline__ uint32_t dpp_prefix_sum(uint32_t v) {
 constexpr int kTkCopies = 4;
 constexpr int kTkHistWords = 2 * kTkWaves * 256 * kTkCopies;
 
-template <int kThreads, int kEpt, bool kFinal>
-__device__ __forceinline__ void select_block(uint64_t (&key)[kEpt], int K, uint32_t* hist,
-                                             uint64_t* __restrict__ keys_out, int32_t* __restrict__ idx_out,
-                                             int32_t* __restrict__ count_out, uint32_t* scratch = nullptr) {
+//
+// Returns the selection's threshold key T (the same in every thread): the K selected keys
+// are exactly the keys >= T (T = 0 when at most K keys are present, all of them kept), and
+// any key < T ranks below all K of them.  kCopies (1 or kTkCopies) sets the histogram
+// copies per wave: `hist` then holds 2 * (kThreads / 64) * 256 * kCopies words.
+template <int kThreads, int kEpt, bool kFinal, int kCopies = kTkCopies>
+__device__ __forceinline__ uint64_t select_block(uint64_t (&key)[kEpt], int K, uint32_t* hist,
+                                                 uint64_t* __restrict__ keys_out, int32_t* __restrict__ idx_out,
+                                                 int32_t* __restrict__ count_out, uint32_t* scratch = nullptr) {
+  static_assert(kCopies == 1 || kCopies == kTkCopies, "one or four histogram copies");
   constexpr int kWaves = kThreads / 64;
   static_assert(kEpt <= 64 && kThreads % 64 == 0, "one lane per slot in the compaction scan");
   const int tid = threadIdx.x;
@@ -160,25 +166,33 @@ __device__ __forceinline__ void select_block(uint64_t (&key)[kEpt], int K, uint3
     int shift = hb - 7 > 0 ? hb - 7 : 0;
     uint32_t need = (uint32_t)K;
     for (int pass = 0;; ++pass) {
-      uint32_t* h = hist + ((pass & 1) * kWaves + wave) * 256 * kTkCopies;
+      uint32_t* h = hist + ((pass & 1) * kWaves + wave) * 256 * kCopies;
 #pragma unroll
-      for (int i = 0; i < kTkCopies; ++i)
+      for (int i = 0; i < kCopies; ++i)
         reinterpret_cast<uint4*>(h)[lane + 64 * i] = make_uint4(0u, 0u, 0u, 0u);
-      uint32_t* hc = h + (lane & (kTkCopies - 1));
+      uint32_t* hc = h + (lane & (kCopies - 1));
 #pragma unroll
       for (int i = 0; i < kEpt; ++i)
-        if (key[i] && (key[i] & mask) == prefix) atomicAdd(&hc[((uint32_t)(key[i] >> shift) & 255u) * kTkCopies], 1u);
+        if (key[i] && (key[i] & mask) == prefix) atomicAdd(&hc[((uint32_t)(key[i] >> shift) & 255u) * kCopies], 1u);
       __syncthreads();
       // every wave: lane l owns bins 4l..4l+3 of the histogram summed over waves and copies
       uint32_t hs[4] = {0u, 0u, 0u, 0u};
       if constexpr (kWaves <= 4) {
 #pragma unroll
         for (int wv = 0; wv < kWaves; ++wv) {
-          const uint4* hw = reinterpret_cast<const uint4*>(hist + ((pass & 1) * kWaves + wv) * 256 * kTkCopies);
+          const uint4* hw = reinterpret_cast<const uint4*>(hist + ((pass & 1) * kWaves + wv) * 256 * kCopies);
+          if constexpr (kCopies == 1) {
+            const uint4 c = hw[lane];
+            hs[0] += c.x;
+            hs[1] += c.y;
+            hs[2] += c.z;
+            hs[3] += c.w;
+          } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint4 c = hw[4 * lane + j];
-            hs[j] += c.x + c.y + c.z + c.w;
+            for (int j = 0; j < 4; ++j) {
+              const uint4 c = hw[4 * lane + j];
+              hs[j] += c.x + c.y + c.z + c.w;
+            }
           }
         }
       } else {
@@ -194,8 +208,12 @@ __device__ __forceinline__ void select_block(uint64_t (&key)[kEpt], int K, uint3
           uint32_t sum = 0u;
 #pragma unroll
           for (int wv = 4 * g; wv < 4 * g + 4; ++wv) {
-            const uint4 c = reinterpret_cast<const uint4*>(hist + ((pass & 1) * kWaves + wv) * 256 * kTkCopies)[b];
-            sum += c.x + c.y + c.z + c.w;
+            if constexpr (kCopies == 1) {
+              sum += hist[((pass & 1) * kWaves + wv) * 256 + b];
+            } else {
+              const uint4 c = reinterpret_cast<const uint4*>(hist + ((pass & 1) * kWaves + wv) * 256 * kCopies)[b];
+              sum += c.x + c.y + c.z + c.w;
+            }
           }
           part[g][b] = sum;
         }
@@ -275,7 +293,7 @@ __device__ __forceinline__ void select_block(uint64_t (&key)[kEpt], int K, uint3
       if (take && slot < (uint32_t)K) out[slot] = key[i];
     }
     for (int i = (int)nsel + tid; i < K; i += kThreads) out[i] = 0ull;
-    return;
+    return prefix;
   }
   int32_t* out = idx_out;
 #pragma unroll
@@ -287,8 +305,95 @@ __device__ __forceinline__ void select_block(uint64_t (&key)[kEpt], int K, uint3
   }
   for (int i = (int)nsel + tid; i < K; i += kThreads) out[i] = -1;
   if (tid == 0) *count_out = (int32_t)nsel;
+  return prefix;
 }
 
+
+// The same exact selection by one wave alone (no barrier: a wave's LDS accesses execute in
+// order), for lists that a single wave owns: key[i] of lane l is candidate i*64 + l; the K
+// largest are written to out[0 .. K) in candidate order (out may alias the LDS the keys were
+// read from: every key is in registers before the first write).  `hist` is 256 words of LDS
+// private to the wave.  Returns the threshold T: the kept keys are exactly those >= T (0 when
+// at most K keys are present; then nothing is written).
+template <int kEpt>
+__device__ __forceinline__ uint64_t select_wave(uint64_t (&key)[kEpt], int K, uint32_t* hist, uint64_t* out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t n = 0, hmax = 0u, hmin = ~0u, lmax = 0u, lmin = ~0u;
+#pragma unroll
+  for (int i = 0; i < kEpt; ++i) {
+    n += (uint32_t)__popcll(__ballot(key[i] != 0ull));
+    const uint32_t h = (uint32_t)(key[i] >> 32), l = (uint32_t)key[i];
+    hmax = key[i] ? max(hmax, h) : hmax;
+    hmin = key[i] ? min(hmin, h) : hmin;
+    lmax = key[i] ? max(lmax, l) : lmax;
+    lmin = key[i] ? min(lmin, l) : lmin;
+  }
+  if (n <= (uint32_t)K) return 0ull;
+  hmax = dpp_max_u32(hmax);
+  hmin = dpp_min_u32(hmin);
+  int hb;
+  uint64_t top;
+  if (hmax != hmin) {
+    hb = 32 + 31 - __clz(hmax ^ hmin);
+    top = (uint64_t)hmax << 32;
+  } else {   // every score equal: the keys differ in their position words only
+    lmax = dpp_max_u32(lmax);
+    lmin = dpp_min_u32(lmin);
+    hb = 31 - __clz(lmax ^ lmin);
+    top = ((uint64_t)hmax << 32) | lmax;
+  }
+  uint64_t mask = hb >= 63 ? 0ull : ~((2ull << hb) - 1ull);
+  uint64_t prefix = top & mask;
+  int shift = hb - 7 > 0 ? hb - 7 : 0;
+  uint32_t need = (uint32_t)K;
+  for (;;) {
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kEpt; ++i)
+      if (key[i] && (key[i] & mask) == prefix) atomicAdd(&hist[(uint32_t)(key[i] >> shift) & 255u], 1u);
+    const uint4 c = reinterpret_cast<const uint4*>(hist)[lane];   // bins 4l .. 4l+3
+    const uint32_t hs[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t tot = hs[0] + hs[1] + hs[2] + hs[3];
+    const uint32_t pre = dpp_prefix_sum(tot);
+    const uint32_t incl = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + tot;  // bins >= 4*lane
+    const uint32_t above_lane = incl - tot;
+    uint32_t d = 0, above = 0, inbin = 0;
+    const bool mine = above_lane < need && incl >= need;
+    if (mine) {
+      uint32_t acc = above_lane;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (acc + hs[j] >= need) {
+          d = 4 * lane + j;
+          above = acc;
+          inbin = hs[j];
+          break;
+        }
+        acc += hs[j];
+      }
+    }
+    const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
+    d = __builtin_amdgcn_readlane(d, owner);
+    above = __builtin_amdgcn_readlane(above, owner);
+    inbin = __builtin_amdgcn_readlane(inbin, owner);
+    need -= above;
+    prefix |= (uint64_t)d << shift;
+    mask |= 255ull << shift;
+    if (inbin == need || shift == 0) break;
+    shift = shift - 8 > 0 ? shift - 8 : 0;
+  }
+  // stable compaction in candidate order: the kept keys are those >= prefix
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  uint32_t base = 0;
+#pragma unroll
+  for (int i = 0; i < kEpt; ++i) {
+    const bool take = key[i] && key[i] >= prefix;
+    const uint64_t m = __ballot(take);
+    if (take) out[base + (uint32_t)__popcll(m & lt_mask)] = key[i];
+    base += (uint32_t)__popcll(m);
+  }
+  return prefix;
+}
 
 // The 256-thread, 32-keys-per-thread segment of the Top-K levels: segment seg of query q
 // writes keys_out[(q*n_seg + seg)*K ..] (non-final) or idx_out[q*K ..] and count_out[q].

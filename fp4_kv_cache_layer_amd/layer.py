@@ -31,7 +31,7 @@ INDEX_FORMATS = {"mxfp4": (C.FMT_MXFP4, 32), "nvfp4": (C.FMT_NVFP4, 16)}
 
 
 def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp4",
-               attn_select: bool = False, pool_select=None) -> list:
+               attn_select: bool = False, pool_select=None, group_select: bool = True) -> list:
     """Checks a layer group's mode sequence and returns the calls each layer makes.
 
     [W] "CSA2：跨层复用，能借就不自己算" and Figure 4: a Reindex layer re-scores the KV of the
@@ -40,7 +40,8 @@ def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp
     layer builds the pool, and Reindex-in-pool layers need it.  Raises ValueError for a
     sequence that breaks these rules.  group > 1: the query rows come in groups of `group`
     rows of one sequence, and the layers that score all visible entries read each group's
-    indexer K once (csa2_index_score_grouped, then csa2_topk).  index_fmt "nvfp4": the
+    indexer K once: fused (and group_select), scored and selected without a score array
+    (csa2_index_topk_grouped); otherwise csa2_index_score_grouped, then csa2_topk.  index_fmt "nvfp4": the
     fused pool build and grouped scoring exist for MXFP4 only, so the pool-building layer
     scores, selects and builds the pool in separate calls, and group must be 1.
     attn_select (fused, group 1, and a cache whose segment survivors fit one selection,
@@ -72,7 +73,8 @@ def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp
             calls = (["quantize_index_q", "index_topk_pool", "attend"] if fused and index_fmt == "mxfp4" else
                      ["quantize_index_q", "score", "select", "build_pool", "attend"])
         elif group > 1 and m in ("full", "reindex"):
-            calls = ["quantize_index_q", "score_grouped", "select", "attend"]
+            calls = (["quantize_index_q", "index_topk_grouped", "attend"] if fused and group_select else
+                     ["quantize_index_q", "score_grouped", "select", "attend"])
         elif attn_select and fused and m in ("full", "reindex"):
             calls = ["quantize_index_q", "index_segments", "attend_topk"]
         elif (attn_select if pool_select is None else pool_select) and fused and group == 1 and m == "reindex_pool":
@@ -135,6 +137,11 @@ class Csa2Step:
         # inside a pool the attention call selects from at most 16,384 slots
         self.pool_select = bool(attn_select) and fused and group == 1 and max_blocks * block <= 16384
         self.attn_select = bool(attn_select) and fits
+        # grouped rows: the fused selection keeps one wave per row and range busy, which pays
+        # once the groups alone give the GPU a few hundred workgroups (a prefill chunk's
+        # hundreds of groups); a few groups (several decode tokens of a few sequences) keep
+        # the grouped scores and the Top-K levels
+        self.group_select = fused and group > 1 and (n_q + group - 1) // group >= 128
         self.index_fmt = index_fmt
         self.idx_qfmt, self.idx_group = INDEX_FORMATS[index_fmt]
         self.n_q, self.n_heads, self.idx_heads = n_q, n_heads, idx_heads
@@ -164,6 +171,8 @@ class Csa2Step:
         self.ws_attn = torch.empty(max(C.csa2_attn_workspace_bytes(n_q, n_heads, dim, k, window), 1),
                                    dtype=torch.uint8, **dev)
         self.cand_keys = torch.empty(n_q, max(n_cand, 1), dtype=torch.int64, **dev)
+        self.ws_grouped = torch.empty(max(C.csa2_index_topk_grouped_workspace_bytes(n_q, seq_cap, k, group), 1)
+                                      if self.group_select else 1, dtype=torch.uint8, **dev)
         self.sm_scale = 1.0 / math.sqrt(dim)
 
     # ---- steps ----
@@ -199,6 +208,12 @@ class Csa2Step:
         self._mx_only("grouped scoring")
         return C.csa2_index_score_grouped(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq,
                                           n_vis, self.group, self.scores, _bind=bind)
+
+    def index_topk_grouped(self, caches: Caches, w, q_seq, n_vis, bind=False):
+        """grouped scoring and selection in one pass, without the score array."""
+        self._mx_only("grouped scoring")
+        return C.csa2_index_topk_grouped(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq,
+                                         n_vis, self.group, self.k, self.idx, self.count, self.ws_grouped, _bind=bind)
 
     def select(self, n_vis, in_pool: bool = False, bind=False):
         if in_pool:
@@ -274,7 +289,7 @@ class Csa2Step:
         call (see attend).  With bind=True returns the group's calls as one flat list of
         callables."""
         plan = plan_group(modes, self.fused, self.group, self.index_fmt, self.attn_select,
-                          pool_select=self.pool_select)
+                          pool_select=self.pool_select, group_select=self.group_select)
         calls = []
         for i, (m, names) in enumerate(zip(modes, plan)):
             q_index, w, q_attn = inputs[i]
@@ -290,6 +305,8 @@ class Csa2Step:
                     c = self.index_topk(caches, w, q_seq, n_vis, name.endswith("in_pool"), bind)
                 elif name == "score_grouped":
                     c = self.score_grouped(caches, w, q_seq, n_vis, bind)
+                elif name == "index_topk_grouped":
+                    c = self.index_topk_grouped(caches, w, q_seq, n_vis, bind)
                 elif name in ("score", "score_pool"):
                     c = self.score(caches, w, q_seq, n_vis, name.endswith("pool"), bind)
                 elif name == "score_pool_q":

@@ -250,6 +250,34 @@ int csa2_index_score_grouped(const uint8_t* q_codes, const uint8_t* q_scales, co
                              int group, float* scores, int64_t scores_stride, void* stream);
 
 /*
+ * csa2_index_topk_grouped -- csa2_index_score_grouped followed by csa2_topk, without the
+ * score array: for query rows that come in groups sharing one sequence (the rows of a prefill
+ * chunk, several decode tokens of a sequence), each group's indexer K is read once and every
+ * row keeps only its running best candidates.  [W] "CSA2：跨层复用，能借就不自己算" (every
+ * query row's indexer scores, then its Top-K), "分层稀疏索引器" (the scoring of the whole
+ * visible range is the cost that matters).
+ *
+ * Arguments up to n_vis and `group` are those of csa2_index_score_grouped; k, idx_out and
+ * count_out are those of csa2_topk.  For every row whose q_seq equals its group's first
+ * row's (and lies in [0, n_seq)), idx_out / count_out are exactly what csa2_index_score_grouped
+ * followed by csa2_topk (no pool, n_vis as given) returns: the same fp32 scores in the same
+ * ranking (score descending, position ascending), ascending positions, -1 padded.  Any other
+ * row gets count 0 and an all -1 row.
+ *   k in 1..CSA2_MAX_GROUPED_TOPK; n_q <= 65535 * group.
+ *   Workspace: csa2_index_topk_grouped_workspace_bytes(n_q, seq_cap, k, group) bytes (each
+ *   row's best k of every range of its entries: at most 8,192 keys per row).
+ * Errors: those of csa2_index_score_grouped; CSA2_ERR_NULL (idx_out, count_out);
+ * CSA2_ERR_SHAPE (k, n_q); CSA2_ERR_WORKSPACE.
+ */
+#define CSA2_MAX_GROUPED_TOPK 704
+int csa2_index_topk_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                            int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
+                            int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis, int group,
+                            int k, int32_t* idx_out, int32_t* count_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+size_t csa2_index_topk_grouped_workspace_bytes(int n_q, int64_t seq_cap, int k, int group);
+
+/*
  * csa2_index_topk -- csa2_index_score followed by csa2_topk in one pass, without the score
  * array.  [W] "CSA2：跨层复用，能借就不自己算" (indexer scores, then Top-K, K = 512),
  * "分层稀疏索引器" (inside the pool).

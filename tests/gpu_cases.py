@@ -213,7 +213,8 @@ def run_group_snapshots(case: Case, step, caches, window_appends: bool = False, 
     calls = step.run_group(caches, modes, inputs, q_seq, n_vis, q_pos, rs, bind=True, new_wins=new_wins)
     snaps, at = [], 0
     # the calls of each layer as the step plans them (the flat list is cut by these counts)
-    plan = plan_group(modes, step.fused, step.group, step.index_fmt, step.attn_select, pool_select=step.pool_select)
+    plan = plan_group(modes, step.fused, step.group, step.index_fmt, step.attn_select, pool_select=step.pool_select,
+                      group_select=step.group_select)
     assert sum(len(n) for n in plan) == len(calls)
     for L, names in enumerate(plan):
         if window_appends:
@@ -269,7 +270,7 @@ def _sparse_attention(*a, **kw):
         return O.sparse_attention(*a, **kw)
 
 
-def check_group_rows(case: Case, caches, snaps, rows, workers: int = 8, **kw) -> list:
+def check_group_rows(case: Case, caches, snaps, rows, workers: int = 8, shared_index: bool = False, **kw) -> list:
     """check_group_query for many rows: the device bytes are read first on this thread,
     then the oracle work runs on a thread pool (numpy releases the interpreter lock in its
     array loops; the BLAS calls are serialised).  The first failing row raises, with its row
@@ -277,10 +278,17 @@ def check_group_rows(case: Case, caches, snaps, rows, workers: int = 8, **kw) ->
     from concurrent.futures import ThreadPoolExecutor
     rows = list(rows)
     data = {qi: gather_group_row(case, caches, snaps, qi, kw.get("window", 128)) for qi in rows}
+    shared = {}
+    if shared_index:   # few sequences, many rows each (a prefill chunk): one oracle cache each
+        for seq in sorted({int(case.wl.q_seq[qi]) for qi in rows}):
+            oc = oracle_index_cache(case.wl, seq, case.index_fmt)
+            oc.ik_deq(case.wl.seq_cap)   # dequantised once, before the threads read it
+            shared[seq] = oc
 
     def one(qi):
         try:
-            return check_group_query(case, None, snaps, qi, gpu=data[qi], **kw)
+            return check_group_query(case, None, snaps, qi, gpu=data[qi],
+                                     oracle_index=shared.get(int(case.wl.q_seq[qi])), **kw)
         except AssertionError as e:
             raise AssertionError(f"query row {qi}: {e}") from e
 
@@ -289,7 +297,8 @@ def check_group_rows(case: Case, caches, snaps, rows, workers: int = 8, **kw) ->
 
 
 def check_group_query(case: Case, caches, snaps, qi: int, k: int = 512, window: int = 128,
-                      block: int = 8, max_blocks: int = 2048, gpu: dict | None = None) -> dict:
+                      block: int = 8, max_blocks: int = 2048, gpu: dict | None = None,
+                      oracle_index: O.PackedCaches | None = None) -> dict:
     """Oracle parity of one query row through every layer of the group.  Index sets and the
     pool pass the oracle's acceptance rules; each layer's attention is compared with the
     oracle's over the set the GPU attended (so a legitimate near-tie swap upstream does not
@@ -300,6 +309,8 @@ def check_group_query(case: Case, caches, snaps, qi: int, k: int = 512, window: 
     if gpu is None:
         gpu = gather_group_row(case, caches, snaps, qi, window)
         oc = oracle_index_cache(wl, seq, case.index_fmt)
+    elif oracle_index is not None:   # shared read-only by check_group_rows' threads
+        oc = oracle_index
     else:   # a thread of check_group_rows: a cache of its own, nothing shared
         ik_c, ik_s = O.quantize_indexer(wl.index_k_latents(seq, 0, wl.seq_cap), case.index_fmt)
         oc = O.PackedCaches(None, None, ik_c, ik_s, index_fmt=case.index_fmt)

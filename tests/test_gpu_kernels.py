@@ -232,6 +232,92 @@ def test_index_score_grouped_matches_per_row(C, group):
         assert np.all(np.abs(got[qi, :nv] - r) <= 1e-5 * np.abs(r) + 1e-6 * np.abs(r).max())
 
 
+def _grouped_two_call(C, st, caches, w, q_seq_d, n_vis_d, group, k):
+    """Reference for the fused grouped selection: grouped scores, then csa2_topk."""
+    idx = torch.full((st.n_q, k), -5, dtype=torch.int32, device="cuda")
+    cnt = torch.full((st.n_q,), -5, dtype=torch.int32, device="cuda")
+    C.csa2_index_score_grouped(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq_d, n_vis_d,
+                               group, st.scores)
+    C.csa2_topk(st.scores, n_vis_d, st.seq_cap, k, idx, cnt)
+    return idx, cnt
+
+
+@pytest.mark.parametrize("group,k", [(8, 512), (3, 512), (8, 7), (8, 704), (1, 512)])
+def test_index_topk_grouped_matches_score_then_topk(C, group, k):
+    """Grouped rows scored and selected in one pass (no score array): exactly the index set
+    of grouped scoring followed by csa2_topk, over a cache of 70,000 entries (four ranges
+    whose survivors meet in the last level), ragged visible counts (a row of 1 entry, rows
+    ending inside a range, a row covering all) and rows of another sequence than their
+    group's first row (which get an empty set)."""
+    _say("index_topk_grouped", group, k)
+    q_seq = np.array([0, 0, 0, 1, 1, 1, 2, 2, 0, 1, 2, 2], np.int32)
+    n_vis = np.array([70000, 69990, 40097, 70000, 1, 64, 69999, 33000, 700, 31000, 65536, 65537], np.int64)
+    n_q = q_seq.size
+    wl = G.workloads.Workload(name="grouped_topk", seed=47, n_seq=3, seq_cap=70000, m=1, heads=16, idx_heads=16,
+                              q_seq=q_seq, q_pos=n_vis - 1, replay_start=np.zeros(n_q, np.int64),
+                              layers=("full",), new_entries=(0, 0))
+    case = G.Case(wl)
+    caches = case.gpu_caches()
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq_d, n_vis_d, _, _ = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(n_q, 16, 16, wl.seq_cap, k=k)
+    st.quantize_index_q(q_idx)
+    ref_idx, ref_cnt = _grouped_two_call(C, st, caches, w, q_seq_d, n_vis_d, group, k)
+    idx = torch.full((n_q, k), -5, dtype=torch.int32, device="cuda")
+    cnt = torch.full((n_q,), -5, dtype=torch.int32, device="cuda")
+    ws = torch.empty(C.csa2_index_topk_grouped_workspace_bytes(n_q, wl.seq_cap, k, group), dtype=torch.uint8, device="cuda")
+    for _ in range(2):   # a second call over the first one's workspace
+        C.csa2_index_topk_grouped(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq_d, n_vis_d,
+                                  group, k, idx, cnt, ws)
+        torch.cuda.synchronize()
+        gi, gc, ri, rc = idx.cpu().numpy(), cnt.cpu().numpy(), ref_idx.cpu().numpy(), ref_cnt.cpu().numpy()
+        for qi in range(n_q):
+            if q_seq[qi] == q_seq[(qi // group) * group]:
+                assert gc[qi] == rc[qi] == min(k, n_vis[qi]), qi
+                assert np.array_equal(gi[qi], ri[qi]), qi
+            else:
+                assert gc[qi] == 0 and np.all(gi[qi] == -1), qi
+    # and the oracle's rule on one row per sequence
+    for qi in (1, 3, 6):
+        if q_seq[qi] != q_seq[(qi // group) * group]:
+            continue
+        oc = case.oracle_caches(int(q_seq[qi]))
+        qc, qs, wq, _ = case.oracle_query(0, qi)
+        pos, sc = O.full_scores(qc, qs, wq, oc, int(n_vis[qi]))
+        G.topk_accept(gi[qi], int(gc[qi]), pos, sc, k)
+
+
+def test_index_topk_grouped_rising_scores(C):
+    """The worst order for a running selection: scores that rise with the position (and
+    plateau where neighbouring entries quantise alike), so almost every entry enters the
+    candidate lists and the lists are cut down after every step.  Same result as grouped
+    scores followed by csa2_topk, ties going to the lower position."""
+    _say("index_topk_grouped rising")
+    n = 40000
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal(128).astype(np.float32)
+    lat = ((np.arange(n, dtype=np.float32)[:, None] + 1.0) / n) * v[None, :]
+    from fp4_kv_cache_layer_amd.layer import Caches, Csa2Step
+    caches = Caches.empty(1, n, (0,), 128)
+    C.csa2_quantize_kv(torch.from_numpy(lat).cuda(), C.FMT_MXFP4, caches.ik_codes[0], caches.ik_scales[0])
+    n_q = 8
+    st = Csa2Step(n_q, 16, 16, n)
+    q = torch.from_numpy(np.tile(v, (n_q, 16, 1)) * (1.0 + 0.1 * np.arange(n_q)[:, None, None])).float().cuda()
+    st.quantize_index_q(q)
+    w = torch.ones(n_q, 16, dtype=torch.float32, device="cuda")
+    q_seq_d = torch.zeros(n_q, dtype=torch.int32, device="cuda")
+    n_vis_d = torch.tensor([n - 13 * i for i in range(n_q)], dtype=torch.int64, device="cuda")
+    ref_idx, ref_cnt = _grouped_two_call(C, st, caches, w, q_seq_d, n_vis_d, 8, 512)
+    idx = torch.full((n_q, 512), -5, dtype=torch.int32, device="cuda")
+    cnt = torch.full((n_q,), -5, dtype=torch.int32, device="cuda")
+    C.csa2_index_topk_grouped(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq_d, n_vis_d, 8,
+                              512, idx, cnt)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt, ref_cnt) and torch.equal(idx, ref_idx)
+    assert int(idx[0, 0].item()) > n // 2        # the set really sits at the rising end
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 def test_index_score_pool_slots(C, fmt):
     _say("index_score pool", fmt)

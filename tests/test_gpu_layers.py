@@ -157,9 +157,10 @@ def test_prefill_chunk_full_size(C, group):
     case = G.Case(wl, swa_layers=(0,))
     caches = case.gpu_caches()
     step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group)
+    assert step.group_select == (group > 1)          # grouped rows: scored and selected in one pass
     snaps = G.run_group_snapshots(case, step, caches)
-    for qi in (0, 63, 127, 128, 2100, wl.n_q - 1):
-        _say("  oracle query", qi, "t", int(wl.q_pos[qi]), "n_vis", int(wl.n_vis[qi]))
-        G.check_group_query(case, caches, snaps, qi)
+    rows = sorted({0, 1, 63, 126, 127, 128, 129, wl.n_q - 1} | set(range(128, wl.n_q, 61)))
+    _say("  oracle rows", len(rows))
+    G.check_group_rows(case, caches, snaps, rows, workers=16, shared_index=True)
     del caches, step
     torch.cuda.empty_cache()

@@ -53,8 +53,8 @@ def test_decoder_step_is_the_model_decoder():
 
 def test_grouped_plan_scores_then_selects():
     plan = plan_group(["full", "reuse", "reindex", "full_pool", "reindex_pool"], group=4)
-    assert plan[0] == ["quantize_index_q", "score_grouped", "select", "attend"]
-    assert plan[2] == ["quantize_index_q", "score_grouped", "select", "attend"]
+    assert plan[0] == ["quantize_index_q", "index_topk_grouped", "attend"]   # no score array
+    assert plan[2] == ["quantize_index_q", "index_topk_grouped", "attend"]
     assert plan[3] == ["quantize_index_q", "index_topk_pool", "attend"]      # pool layers keep their path
     assert plan[4] == ["quantize_index_q", "index_topk_in_pool", "attend"]
     assert plan_group(["full"], group=1)[0] == ["quantize_index_q", "index_topk", "attend"]
@@ -92,6 +92,5 @@ def test_plan_select_in_attention():
     assert plan[2] == ["quantize_index_q", "score_pool", "attend_pool_topk"]
     plan = plan_group(["full_pool", "reuse", "reindex_pool"], attn_select=True, pool_select=False)
     assert plan[2] == ["quantize_index_q", "index_topk_in_pool", "attend"]
-    assert plan_group(["full"], group=4, attn_select=True)[0] == ["quantize_index_q", "score_grouped", "select",
-                                                                   "attend"]
+    assert plan_group(["full"], group=4, attn_select=True)[0] == ["quantize_index_q", "index_topk_grouped", "attend"]
     assert plan_group(["full"], fused=False, attn_select=True)[0] == ["quantize_index_q", "score", "select", "attend"]
