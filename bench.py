@@ -606,7 +606,7 @@ def main():
         modes["full_128k_nvfp4_indexer"] = {
             "index_format": "E2M1 + E4M3 per 16 (72 B per indexer-K entry), fp16 MFMA scoring",
             "us_per_layer_step": round(msn * 1e3, 2), "query_tokens_per_s": round(wln.n_q / (msn / 1e3), 1),
-            "scoring_call": f"csa2_{scn}_nvfp4", "scoring_us": round(gcn[scn] * 1e3, 2),
+            "scoring_call": f"csa2_{scn} (fmt CSA2_FMT_NVFP4)", "scoring_us": round(gcn[scn] * 1e3, 2),
             "scoring_gb_per_s": round(gbs, 1),
             "scoring_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "scoring_bytes": bn,
             "scoring_kernel_us": round(gcn["scoring_kernel"] * 1e3, 2) if "scoring_kernel" in gcn else None,

@@ -53,43 +53,41 @@ def lib() -> ctypes.CDLL:
         "csa2_debug_set_wait_limit": ([i32], i32),
         "csa2_status_string": ([i32], ctypes.c_char_p),
         "csa2_last_error": ([], ctypes.c_char_p),
-        "csa2_quantize_kv": ([vp, i32, i64, i32, i32, vp, i64, vp, vp, vp], i32),
+        "csa2_quantize_kv": ([vp, i32, i64, i32, i32, vp, i64, vp, i64, vp, i64, vp], i32),
         "csa2_quantize_kv_multi": ([vp, i32, vp], i32),
-        "csa2_index_score_grouped": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp], i32),
-        "csa2_index_score": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64, vp],
-                             i32),
-        "csa2_index_score_q": ([vp, i32, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64, vp],
-                               i32),
-        "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp,
-                             sz, vp], i32),
+        "csa2_index_score_grouped": ([vp, vp, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp,
+                                      i32, vp, i64, vp], i32),
+        "csa2_index_score": ([vp, vp, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, vp, vp,
+                              i32, i32, vp, i64, vp], i32),
+        "csa2_index_score_q": ([vp, i32, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, vp, vp,
+                                i32, i32, vp, i64, vp], i32),
+        "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, vp, vp,
+                             i32, i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_index_topk_workspace_bytes": ([i32, i64, i32, i32], sz),
-        "csa2_index_topk_grouped": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, sz,
-                                     vp], i32),
+        "csa2_index_topk_grouped": ([vp, vp, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp,
+                                     i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_index_topk_grouped_workspace_bytes": ([i32, i64, i32, i32], sz),
-        "csa2_index_score_nvfp4": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, vp, i64,
-                                    vp], i32),
-        "csa2_index_topk_nvfp4": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp,
-                                   vp, sz, vp], i32),
-        "csa2_index_topk_pool": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp, i32, i32, vp, vp,
-                                  vp, sz, vp], i32),
+        "csa2_index_topk_pool": ([vp, vp, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, i32,
+                                  vp, vp, i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_index_topk_pool_workspace_bytes": ([i32, i64, i32, i32, i32], sz),
         "csa2_topk": ([vp, i64, i32, vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_topk_workspace_bytes": ([i32, i64, i32], sz),
         "csa2_build_pool": ([vp, i64, i32, vp, i64, i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_pool_workspace_bytes": ([i32, i64, i32, i32], sz),
-        "csa2_sparse_attn": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp, vp, vp, vp, i32, i32, f32,
-                              vp, i32, vp, vp, sz, vp], i32),
+        "csa2_sparse_attn": ([vp, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, i32, vp, i64, i64, i64,
+                              vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, sz, vp], i32),
         "csa2_attn_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
-        "csa2_sparse_attn_noalloc": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, i64, vp, vp, vp, vp, i32,
-                                      i32, f32, vp, i32, vp, vp], i32),
+        "csa2_sparse_attn_noalloc": ([vp, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, i32, vp, i64,
+                                      i64, i64, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp], i32),
         "csa2_sparse_attn_noalloc_max_bytes": ([], sz),
-        "csa2_index_segments": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp], i32),
-        "csa2_index_segments_nvfp4": ([vp, vp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, vp, vp], i32),
+        "csa2_index_segments": ([vp, vp, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, i32,
+                                 vp, vp], i32),
         "csa2_segment_keys": ([i64, i32], i64),
-        "csa2_sparse_attn_topk": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32, i32, vp, vp, vp, i64, vp, vp, vp,
-                                   vp, i32, i32, f32, vp, i32, vp, vp, sz, vp], i32),
-        "csa2_sparse_attn_pool_topk": ([vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i64, vp, vp, vp, i32, i32, i32, vp,
-                                        vp, vp, i64, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, sz, vp], i32),
+        "csa2_sparse_attn_topk": ([vp, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, i32, i32, vp, vp,
+                                   vp, i64, i64, i64, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, sz, vp], i32),
+        "csa2_sparse_attn_pool_topk": ([vp, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, i64, vp, vp,
+                                        vp, i32, i32, i32, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, i32, i32, f32,
+                                        vp, i32, vp, vp, sz, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -166,8 +164,17 @@ def _workspace(need: int, workspace, device, bind: bool, name: str):
     return workspace, (0 if workspace is None else workspace.numel())
 
 
+def _rows2(t, name):
+    """A [rows, row_bytes] uint8 device view whose rows may be strided (stride(1) == 1):
+    (pointer, row stride in bytes)."""
+    if t.dtype != torch.uint8 or t.dim() != 2 or not t.is_cuda or t.stride(1) != 1:
+        raise ValueError(f"{name}: expected a 2-D uint8 device tensor with unit inner stride")
+    return _p(t), t.stride(0)
+
+
 def _quant_args(src, fmt: int, codes, scales, dst_row, bind: bool):
-    """Checks one quantise job and returns its C arguments (src .. scales)."""
+    """Checks one quantise job and returns its C arguments (src .. scales_stride).  codes and
+    scales may be strided row views (e.g. the two parts of an interleaved cache record)."""
     if src.dtype not in (torch.float32, torch.bfloat16) or src.dim() != 2 or not src.is_cuda:
         raise TypeError("src must be a 2-D f32/bf16 device tensor")
     if not src.is_contiguous():
@@ -175,27 +182,28 @@ def _quant_args(src, fmt: int, codes, scales, dst_row, bind: bool):
             raise ValueError("src must be contiguous when binding a call")
         src = src.contiguous()
     rows, dim = src.shape
-    _need(codes, torch.uint8, 2, "codes")
+    cp, cst = _rows2(codes, "codes")
     per = dim if fmt == FMT_FP8 else dim // 2
     if codes.shape[1] != per:
         raise ValueError("codes row size does not match dim")
+    sp, sst = None, 0
     if fmt != FMT_FP8:
-        _need(scales, torch.uint8, 2, "scales")
+        sp, sst = _rows2(scales, "scales")
         g = 16 if fmt == FMT_NVFP4 else 32
-        if scales.shape != (codes.shape[0], dim // g):
+        if tuple(scales.shape) != (codes.shape[0], dim // g):
             raise ValueError("scales shape does not match codes / dim")
     if dst_row is not None:
         _need(dst_row, torch.int64, 1, "dst_row")
         if dst_row.shape[0] != rows:
             raise ValueError("dst_row length != rows")
     dt = DT_F32 if src.dtype == torch.float32 else DT_BF16
-    return (_p(src), dt, rows, dim, fmt, _p(dst_row), codes.shape[0], _p(codes),
-            _p(scales) if fmt != FMT_FP8 else None)
+    return (_p(src), dt, rows, dim, fmt, _p(dst_row), codes.shape[0], cp, cst, sp, sst)
 
 
 def csa2_quantize_kv(src, fmt: int, codes, scales=None, dst_row=None, _bind: bool = False):
     """src [rows, dim] f32/bf16; codes [dst_rows, dim/2] (FP4) or [dst_rows, dim] (FP8) u8;
-    scales [dst_rows, dim/16 | dim/32] u8; dst_row [rows] int64 or None."""
+    scales [dst_rows, dim/16 | dim/32] u8 (row views, possibly strided); dst_row [rows] int64
+    or None."""
     return _run("csa2_quantize_kv", _quant_args(src, fmt, codes, scales, dst_row, _bind) + (_stream(),), _bind)
 
 
@@ -203,7 +211,8 @@ class QuantJob(ctypes.Structure):
     """csa2_quant_job of include/csa2.h."""
     _fields_ = [("src", ctypes.c_void_p), ("src_dtype", ctypes.c_int), ("rows", ctypes.c_int64),
                 ("dim", ctypes.c_int), ("fmt", ctypes.c_int), ("dst_row", ctypes.c_void_p),
-                ("dst_rows", ctypes.c_int64), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+                ("dst_rows", ctypes.c_int64), ("codes", ctypes.c_void_p), ("codes_stride", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("scales_stride", ctypes.c_int64)]
 
 
 def csa2_quantize_kv_multi(jobs, _bind: bool = False):
@@ -216,23 +225,35 @@ def csa2_quantize_kv_multi(jobs, _bind: bool = False):
     return _run("csa2_quantize_kv_multi", (ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream()), _bind)
 
 
+def _cache3(t, name):
+    """A [n_seq, seq_cap, row_bytes] uint8 device view of a cache whose entries and sequences
+    may be strided (stride(2) == 1; e.g. the two parts of an interleaved record):
+    (pointer, entry stride, sequence stride) in bytes."""
+    if t.dtype != torch.uint8 or t.dim() != 3 or not t.is_cuda or t.stride(2) != 1:
+        raise ValueError(f"{name}: expected a 3-D uint8 device tensor with unit inner stride")
+    return _p(t), t.stride(1), t.stride(0)
+
+
 def _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block,
-                scale_group: int = 32):
-    """Checks the indexer operands shared by csa2_index_score and csa2_index_topk and returns
-    the C arguments from q_codes to max_cand_blocks, and n_slots.  scale_group: channels per
-    scale byte (32 for MXFP4, 16 for the NVFP4 variants)."""
+                fmt: int = FMT_MXFP4):
+    """Checks the indexer operands shared by the scoring calls and returns the C arguments
+    from q_codes to max_cand_blocks, and n_slots.  fmt: the indexer format (MXFP4: one scale
+    byte per 32 channels; NVFP4: one per 16)."""
+    if fmt not in (FMT_MXFP4, FMT_NVFP4):
+        raise ValueError("indexer format must be FMT_MXFP4 or FMT_NVFP4")
+    scale_group = 32 if fmt == FMT_MXFP4 else 16
     _need(q_codes, torch.uint8, 3, "q_codes")
     _need(q_scales, torch.uint8, 3, "q_scales")
     _need(w, torch.float32, 2, "w")
-    _need(k_codes, torch.uint8, 3, "k_codes")
-    _need(k_scales, torch.uint8, 3, "k_scales")
+    kc, kce, kcs = _cache3(k_codes, "k_codes")
+    ks, kse, kss = _cache3(k_scales, "k_scales")
     _need(q_seq, torch.int32, 1, "q_seq")
     _need(n_vis, torch.int64, 1, "n_vis")
     n_q, h, half = q_codes.shape
     n_seq, seq_cap, kh = k_codes.shape
     n_sc = 2 * half // scale_group
     if q_scales.shape != (n_q, h, n_sc) or w.shape != (n_q, h) or kh != half or \
-            k_scales.shape != (n_seq, seq_cap, n_sc) or q_seq.shape[0] != n_q or n_vis.shape[0] != n_q:
+            tuple(k_scales.shape) != (n_seq, seq_cap, n_sc) or q_seq.shape[0] != n_q or n_vis.shape[0] != n_q:
         raise ValueError("index: inconsistent shapes")
     max_blocks = 0
     if cand_blocks is not None:
@@ -242,43 +263,38 @@ def _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_bloc
         if cand_blocks.shape[0] != n_q or n_cand_blocks.shape[0] != n_q:
             raise ValueError("index: inconsistent pool shapes")
     n_slots = max_blocks * block if cand_blocks is not None else seq_cap
-    return (_p(q_codes), _p(q_scales), _p(w), n_q, h, 2 * half, _p(k_codes), _p(k_scales), seq_cap, n_seq,
+    return (_p(q_codes), _p(q_scales), _p(w), n_q, h, 2 * half, fmt, kc, kce, kcs, ks, kse, kss, seq_cap, n_seq,
             _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks), block, max_blocks), n_slots
 
 
-def _index_score(name, scale_group, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores, cand_blocks,
-                 n_cand_blocks, block, bind):
+def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
+                     cand_blocks=None, n_cand_blocks=None, block: int = 8, fmt: int = FMT_MXFP4, _bind: bool = False):
+    """q_codes [n_q, H_I, 64], q_scales [n_q, H_I, 4 (MXFP4) | 8 (NVFP4)], w [n_q, H_I] f32;
+    k_codes [n_seq, seq_cap, 64], k_scales [n_seq, seq_cap, 4 | 8] (views, entries and
+    sequences possibly strided); q_seq [n_q] int32, n_vis [n_q] int64; scores [n_q, stride]
+    f32; cand_blocks [n_q, max_blocks] int32; fmt FMT_MXFP4 or FMT_NVFP4."""
     args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block,
-                          scale_group)
+                          fmt)
     _need(scores, torch.float32, 2, "scores")
     if scores.shape[0] != q_codes.shape[0]:
         raise ValueError("index_score: scores rows != n_q")
-    return _run(name, args + (_p(scores), scores.stride(0), _stream()), bind)
-
-
-def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
-                     cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
-    """q_codes [n_q, H_I, 64], q_scales [n_q, H_I, 4], w [n_q, H_I] f32;
-    k_codes [n_seq, seq_cap, 64], k_scales [n_seq, seq_cap, 4]; q_seq [n_q] int32,
-    n_vis [n_q] int64; scores [n_q, stride] f32; cand_blocks [n_q, max_blocks] int32."""
-    return _index_score("csa2_index_score", 32, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
-                        cand_blocks, n_cand_blocks, block, _bind)
+    return _run("csa2_index_score", args + (_p(scores), scores.stride(0), _stream()), _bind)
 
 
 def csa2_index_score_q(q, w, k_codes, k_scales, q_seq, n_vis, scores, cand_blocks=None, n_cand_blocks=None,
                        block: int = 8, _bind: bool = False):
     """csa2_index_score with the indexer Q unquantised: q [n_q, H_I, 128] f32 or bf16, quantised
-    to MXFP4 inside the scoring kernel; the other operands as csa2_index_score."""
+    to MXFP4 inside the scoring kernel; the other operands as csa2_index_score (MXFP4)."""
     if q.dtype not in (torch.float32, torch.bfloat16) or q.dim() != 3 or not q.is_cuda or not q.is_contiguous():
         raise ValueError("q must be a contiguous CUDA [n_q, H_I, 128] f32/bf16 tensor")
     n_q, h, d = q.shape
     _need(w, torch.float32, 2, "w")
-    _need(k_codes, torch.uint8, 3, "k_codes")
-    _need(k_scales, torch.uint8, 3, "k_scales")
+    kc, kce, kcs = _cache3(k_codes, "k_codes")
+    ks, kse, kss = _cache3(k_scales, "k_scales")
     _need(q_seq, torch.int32, 1, "q_seq")
     _need(n_vis, torch.int64, 1, "n_vis")
     n_seq, seq_cap, kh = k_codes.shape
-    if w.shape != (n_q, h) or kh != d // 2 or k_scales.shape != (n_seq, seq_cap, d // 32) or \
+    if w.shape != (n_q, h) or kh != d // 2 or tuple(k_scales.shape) != (n_seq, seq_cap, d // 32) or \
             q_seq.shape[0] != n_q or n_vis.shape[0] != n_q:
         raise ValueError("index_score_q: inconsistent shapes")
     max_blocks = 0
@@ -292,28 +308,20 @@ def csa2_index_score_q(q, w, k_codes, k_scales, q_seq, n_vis, scores, cand_block
     if scores.shape[0] != n_q:
         raise ValueError("index_score_q: scores rows != n_q")
     qdt = DT_F32 if q.dtype == torch.float32 else DT_BF16
-    return _run("csa2_index_score_q", (_p(q), qdt, _p(w), n_q, h, d, _p(k_codes), _p(k_scales), seq_cap, n_seq,
-                                       _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks), block, max_blocks,
-                                       _p(scores), scores.stride(0), _stream()), _bind)
-
-
-def csa2_index_score_nvfp4(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
-                           cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
-    """csa2_index_score for NVFP4 indexer Q/K: q_scales [n_q, H_I, 8] and k_scales
-    [n_seq, seq_cap, 8] hold one E4M3 scale per 16 channels."""
-    return _index_score("csa2_index_score_nvfp4", 16, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
-                        cand_blocks, n_cand_blocks, block, _bind)
+    return _run("csa2_index_score_q", (_p(q), qdt, _p(w), n_q, h, d, FMT_MXFP4, kc, kce, kcs, ks, kse, kss, seq_cap,
+                                       n_seq, _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks), block,
+                                       max_blocks, _p(scores), scores.stride(0), _stream()), _bind)
 
 
 def csa2_index_score_grouped(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, group: int, scores,
                              _bind: bool = False):
     """csa2_index_score without a pool for rows in groups of `group` consecutive rows that
-    share a sequence (each group's indexer K is read once); operands as csa2_index_score."""
+    share a sequence (each group's indexer K is read once); operands as csa2_index_score (MXFP4)."""
     args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8)
     _need(scores, torch.float32, 2, "scores")
     if scores.shape[0] != q_codes.shape[0]:
         raise ValueError("index_score_grouped: scores rows != n_q")
-    return _run("csa2_index_score_grouped", args[:12] + (int(group), _p(scores), scores.stride(0), _stream()), _bind)
+    return _run("csa2_index_score_grouped", args[:17] + (int(group), _p(scores), scores.stride(0), _stream()), _bind)
 
 
 def csa2_index_topk_grouped_workspace_bytes(n_q: int, seq_cap: int, k: int, group: int) -> int:
@@ -333,7 +341,7 @@ def csa2_index_topk_grouped(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vi
         raise ValueError("index_topk_grouped: inconsistent output shapes")
     need = csa2_index_topk_grouped_workspace_bytes(n_q, k_codes.shape[1], k, int(group))
     workspace, ws_bytes = _workspace(need, workspace, q_codes.device, _bind, "index_topk_grouped")
-    return _run("csa2_index_topk_grouped", args[:12] + (int(group), k, _p(idx_out), _p(count_out), _p(workspace),
+    return _run("csa2_index_topk_grouped", args[:17] + (int(group), k, _p(idx_out), _p(count_out), _p(workspace),
                                                         ws_bytes, _stream()), _bind)
 
 
@@ -342,61 +350,37 @@ def csa2_index_topk_workspace_bytes(n_q: int, n_slots: int, k: int, in_pool: boo
 
 
 def csa2_index_topk(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, idx_out, count_out,
-                    workspace=None, cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
+                    workspace=None, cand_blocks=None, n_cand_blocks=None, block: int = 8, fmt: int = FMT_MXFP4,
+                    _bind: bool = False):
     """Scores and Top-K in one pass: the operands of csa2_index_score (without scores) ->
     idx_out [n_q, k] int32, count_out [n_q] int32, as csa2_topk returns them."""
-    return _index_topk("csa2_index_topk", 32, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k, idx_out,
-                       count_out, workspace, cand_blocks, n_cand_blocks, block, _bind)
-
-
-def csa2_index_topk_nvfp4(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, idx_out, count_out,
-                          workspace=None, cand_blocks=None, n_cand_blocks=None, block: int = 8, _bind: bool = False):
-    """csa2_index_topk for NVFP4 indexer Q/K (scales [.., 8]: one E4M3 per 16 channels)."""
-    return _index_topk("csa2_index_topk_nvfp4", 16, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k,
-                       idx_out, count_out, workspace, cand_blocks, n_cand_blocks, block, _bind)
-
-
-def _index_topk(name, scale_group, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k, idx_out, count_out,
-                workspace, cand_blocks, n_cand_blocks, block, _bind):
     args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks,
-                                block, scale_group)
+                                block, fmt)
     _need(idx_out, torch.int32, 2, "idx_out")
     _need(count_out, torch.int32, 1, "count_out")
     n_q = q_codes.shape[0]
     if idx_out.shape != (n_q, k) or count_out.shape[0] != n_q:
         raise ValueError("index_topk: inconsistent output shapes")
     need = csa2_index_topk_workspace_bytes(n_q, max(n_slots, 1), k, cand_blocks is not None)
-    workspace, ws_bytes = _workspace(need, workspace, q_codes.device, _bind, "workspace")
-    return _run(name, args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, _stream()), _bind)
+    workspace, ws_bytes = _workspace(need, workspace, q_codes.device, _bind, "index_topk")
+    return _run("csa2_index_topk", args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, _stream()), _bind)
 
 
 def csa2_segment_keys(n_slots: int, k: int) -> int:
     return int(lib().csa2_segment_keys(n_slots, k))
 
 
-def _index_segments(name, scale_group, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k, cand_keys, _bind):
-    args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8, scale_group)
+def csa2_index_segments(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, cand_keys,
+                        fmt: int = FMT_MXFP4, _bind: bool = False):
+    """The fused first Top-K level alone: the operands of csa2_index_score (no pool) ->
+    cand_keys [n_q, csa2_segment_keys(seq_cap, k)] (opaque 64-bit keys, held in an int64
+    tensor) for csa2_sparse_attn_topk."""
+    args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8, fmt)
     _need(cand_keys, torch.int64, 2, "cand_keys")
     n_q = q_codes.shape[0]
     if tuple(cand_keys.shape) != (n_q, csa2_segment_keys(n_slots, k)):
         raise ValueError("index_segments: cand_keys must be [n_q, csa2_segment_keys(seq_cap, k)]")
-    return _run(name, args[:12] + (k, _p(cand_keys), _stream()), _bind)
-
-
-def csa2_index_segments(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, cand_keys,
-                        _bind: bool = False):
-    """The fused first Top-K level alone: the operands of csa2_index_score (no pool) ->
-    cand_keys [n_q, csa2_segment_keys(seq_cap, k)] (opaque 64-bit keys, held in an int64
-    tensor) for csa2_sparse_attn_topk."""
-    return _index_segments("csa2_index_segments", 32, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k,
-                           cand_keys, _bind)
-
-
-def csa2_index_segments_nvfp4(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, cand_keys,
-                              _bind: bool = False):
-    """csa2_index_segments for an NVFP4-style indexer (E4M3 scale per 16 channels)."""
-    return _index_segments("csa2_index_segments_nvfp4", 16, q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k,
-                           cand_keys, _bind)
+    return _run("csa2_index_segments", args[:17] + (k, _p(cand_keys), _stream()), _bind)
 
 
 def csa2_index_topk_pool_workspace_bytes(n_q: int, n_slots: int, k: int, block: int, max_blocks: int) -> int:
@@ -406,8 +390,8 @@ def csa2_index_topk_pool_workspace_bytes(n_q: int, n_slots: int, k: int, block: 
 def csa2_index_topk_pool(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, idx_out, count_out,
                          blocks_out, blocks_count, block: int = 8, workspace=None, _bind: bool = False):
     """Top-K and candidate pool in one scoring pass: the operands of csa2_index_score (no
-    pool) -> idx_out [n_q, k], count_out [n_q] (as csa2_topk) and blocks_out [n_q, max_blocks],
-    blocks_count [n_q] (as csa2_build_pool)."""
+    pool, MXFP4) -> idx_out [n_q, k], count_out [n_q] (as csa2_topk) and blocks_out
+    [n_q, max_blocks], blocks_count [n_q] (as csa2_build_pool)."""
     args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, block)
     for t, name in ((idx_out, "idx_out"), (blocks_out, "blocks_out")):
         _need(t, torch.int32, 2, name)
@@ -420,9 +404,8 @@ def csa2_index_topk_pool(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, 
         raise ValueError("index_topk_pool: inconsistent output shapes")
     need = csa2_index_topk_pool_workspace_bytes(n_q, max(n_slots, 1), k, block, max_blocks)
     workspace, ws_bytes = _workspace(max(need, 1), workspace, q_codes.device, _bind, "index_topk_pool")
-    return _run("csa2_index_topk_pool", args[:12] + (k, _p(idx_out), _p(count_out), block, max_blocks, _p(blocks_out),
-                                                     _p(blocks_count), _p(workspace), ws_bytes, _stream()),
-                _bind)
+    return _run("csa2_index_topk_pool", args[:17] + (k, _p(idx_out), _p(count_out), block, max_blocks, _p(blocks_out),
+                                                     _p(blocks_count), _p(workspace), ws_bytes, _stream()), _bind)
 
 
 def csa2_topk_workspace_bytes(n_q: int, n_slots: int, k: int) -> int:
@@ -475,11 +458,15 @@ def csa2_attn_workspace_bytes(n_q: int, n_heads: int, dim: int, k: int, window: 
 
 
 def _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, n_q_rows):
+    """Checks the operands every attention call shares; returns the C arguments of the
+    main-KV cache (codes, their strides, scales, their strides, seq_cap, n_seq) and of the
+    window ring (pointer, row stride, sequence stride, swa_cap).  The caches may be strided
+    views (e.g. the two parts of an interleaved 288-byte main-KV record)."""
     _need(q, torch.bfloat16, 3, "q")
-    _need(kv_codes, torch.uint8, 3, "kv_codes")
-    _need(kv_scales, torch.uint8, 3, "kv_scales")
+    kc, kce, kcs = _cache3(kv_codes, "kv_codes")
+    ks, kse, kss = _cache3(kv_scales, "kv_scales")
+    sw, swr, sws = _cache3(swa, "swa")
     _need(q_seq, torch.int32, 1, "q_seq")
-    _need(swa, torch.uint8, 3, "swa")
     _need(swa_base, torch.int64, 1, "swa_base")
     _need(q_pos, torch.int64, 1, "q_pos")
     _need(replay_start, torch.int64, 1, "replay_start")
@@ -487,28 +474,44 @@ def _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start
     n_seq, seq_cap, _ = kv_codes.shape
     if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (n_q, H, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [n_q, H, D] f32/bf16 tensor")
-    if kv_codes.shape[2] != D // 2 or kv_scales.shape != (n_seq, seq_cap, D // 16) or swa.shape[0] != n_seq or \
+    if kv_codes.shape[2] != D // 2 or tuple(kv_scales.shape) != (n_seq, seq_cap, D // 16) or swa.shape[0] != n_seq or \
             swa.shape[2] != D or swa_base.shape[0] != n_seq or n_q_rows != n_q:
         raise ValueError("sparse_attn: inconsistent shapes")
     if lse is not None:
         _need(lse, torch.float32, 2, "lse")
         if tuple(lse.shape) != (n_q, H):
             raise ValueError("lse shape")
+    return (kc, kce, kcs, ks, kse, kss, seq_cap, n_seq), (sw, swr, sws, swa.shape[1])
 
 
 def _new_win(new_win, n_q, D, q_seq=None):
     """(pointer, dtype) of the optional window append: [n_q, D] f32 / bf16 latents.  The
     append needs every row of the call in a sequence of its own (otherwise one row's
     workgroups would write a ring row that another row's workgroups read): checked here,
-    once per call or per bound callable, with one read of q_seq."""
+    once per call or per bound callable, with one read of q_seq -- except while the stream
+    is being captured into a graph, where no such read may run (calls recorded there are
+    bound and checked before the capture, as the layer driver and the benchmark do)."""
     if new_win is None:
         return None, DT_F32
     if new_win.dtype not in (torch.float32, torch.bfloat16) or tuple(new_win.shape) != (n_q, D) or \
             not new_win.is_contiguous() or not new_win.is_cuda:
         raise ValueError("new_win must be a contiguous [n_q, D] f32/bf16 device tensor")
-    if q_seq is not None and n_q > 1 and torch.unique(q_seq).numel() != n_q:
+    if q_seq is not None and n_q > 1 and not torch.cuda.is_current_stream_capturing() and \
+            torch.unique(q_seq).numel() != n_q:
         raise ValueError("new_win: two rows of the call share a sequence (the append needs distinct sequences)")
     return _p(new_win), DT_F32 if new_win.dtype == torch.float32 else DT_BF16
+
+
+def _attn_tail(q, k, window, sm_scale, out, lse, workspace, new_win, q_seq, bind, name, with_workspace=True):
+    """The arguments every attention call ends with: window append .. stream."""
+    n_q, H, D = q.shape
+    odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
+    nw, nwt = _new_win(new_win, n_q, D, q_seq)
+    if not with_workspace:
+        return (nw, nwt, window, ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _stream())
+    need = csa2_attn_workspace_bytes(n_q, H, D, k, window)
+    workspace, ws_bytes = _workspace(need, workspace, q.device, bind, name)
+    return (nw, nwt, window, ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes, _stream())
 
 
 def csa2_sparse_attn_topk(q, kv_codes, kv_scales, q_seq, cand_keys, k: int, idx_out, count_out, swa, swa_base, q_pos,
@@ -519,20 +522,14 @@ def csa2_sparse_attn_topk(q, kv_codes, kv_scales, q_seq, cand_keys, k: int, idx_
     _need(cand_keys, torch.int64, 2, "cand_keys")
     _need(idx_out, torch.int32, 2, "idx_out")
     _need(count_out, torch.int32, 1, "count_out")
-    _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, cand_keys.shape[0])
+    kv, sw = _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, cand_keys.shape[0])
     n_q, H, D = q.shape
-    n_seq, seq_cap, _ = kv_codes.shape
     if tuple(idx_out.shape) != (n_q, k) or count_out.shape[0] != n_q:
         raise ValueError("sparse_attn_topk: inconsistent index output shapes")
-    need = csa2_attn_workspace_bytes(n_q, H, D, k, window)
-    workspace, ws_bytes = _workspace(need, workspace, q.device, _bind, "workspace")
-    odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
-    nw, nwt = _new_win(new_win, n_q, D, q_seq)
-    return _run("csa2_sparse_attn_topk", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq),
-                                          _p(cand_keys), cand_keys.shape[1], k, _p(idx_out), _p(count_out), _p(swa),
-                                          swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), nw, nwt, window,
-                                          ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes,
-                                          _stream()), _bind)
+    tail = _attn_tail(q, k, window, sm_scale, out, lse, workspace, new_win, q_seq, _bind, "sparse_attn_topk")
+    return _run("csa2_sparse_attn_topk", (_p(q), n_q, H, D) + kv + (_p(q_seq), _p(cand_keys), cand_keys.shape[1], k,
+                                                                   _p(idx_out), _p(count_out)) + sw +
+                (_p(swa_base), _p(q_pos), _p(replay_start)) + tail, _bind)
 
 
 def csa2_sparse_attn_pool_topk(q, kv_codes, kv_scales, q_seq, scores, n_vis, cand_blocks, n_cand_blocks, block: int,
@@ -547,58 +544,33 @@ def csa2_sparse_attn_pool_topk(q, kv_codes, kv_scales, q_seq, scores, n_vis, can
     _need(n_cand_blocks, torch.int32, 1, "n_cand_blocks")
     _need(idx_out, torch.int32, 2, "idx_out")
     _need(count_out, torch.int32, 1, "count_out")
-    _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, scores.shape[0])
+    kv, sw = _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, scores.shape[0])
     n_q, H, D = q.shape
-    n_seq, seq_cap, _ = kv_codes.shape
     if tuple(idx_out.shape) != (n_q, k) or count_out.shape[0] != n_q or cand_blocks.shape[0] != n_q or \
             n_cand_blocks.shape[0] != n_q or n_vis.shape[0] != n_q:
         raise ValueError("sparse_attn_pool_topk: inconsistent shapes")
-    need = csa2_attn_workspace_bytes(n_q, H, D, k, window)
-    workspace, ws_bytes = _workspace(need, workspace, q.device, _bind, "workspace")
-    odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
-    nw, nwt = _new_win(new_win, n_q, D, q_seq)
-    return _run("csa2_sparse_attn_pool_topk", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq,
-                                               _p(q_seq), _p(scores), scores.shape[1], _p(n_vis), _p(cand_blocks),
-                                               _p(n_cand_blocks), block, cand_blocks.shape[1], k, _p(idx_out),
-                                               _p(count_out), _p(swa), swa.shape[1], _p(swa_base), _p(q_pos),
-                                               _p(replay_start), nw, nwt, window, ctypes.c_float(sm_scale), _p(out),
-                                               odt, _p(lse), _p(workspace), ws_bytes, _stream()), _bind)
+    tail = _attn_tail(q, k, window, sm_scale, out, lse, workspace, new_win, q_seq, _bind, "sparse_attn_pool_topk")
+    return _run("csa2_sparse_attn_pool_topk",
+                (_p(q), n_q, H, D) + kv + (_p(q_seq), _p(scores), scores.shape[1], _p(n_vis), _p(cand_blocks),
+                                           _p(n_cand_blocks), block, cand_blocks.shape[1], k, _p(idx_out),
+                                           _p(count_out)) + sw + (_p(swa_base), _p(q_pos), _p(replay_start)) + tail,
+                _bind)
 
 
 def csa2_sparse_attn(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, q_pos, replay_start, window: int,
                      sm_scale: float, out, lse=None, workspace=None, new_win=None, _bind: bool = False):
-    """q [n_q, H, 512] bf16; kv_codes [n_seq, seq_cap, 256], kv_scales [n_seq, seq_cap, 32];
-    idx [n_q, k] int32; swa [n_seq, swa_cap, 512] u8; swa_base [n_seq] int64;
-    q_pos, replay_start [n_q] int64; out [n_q, H, 512] f32/bf16; lse [n_q, H] f32."""
-    _need(q, torch.bfloat16, 3, "q")
-    _need(kv_codes, torch.uint8, 3, "kv_codes")
-    _need(kv_scales, torch.uint8, 3, "kv_scales")
-    _need(q_seq, torch.int32, 1, "q_seq")
+    """q [n_q, H, 512] bf16; kv_codes [n_seq, seq_cap, 256], kv_scales [n_seq, seq_cap, 32]
+    (views, possibly strided: e.g. rec[..., :256] and rec[..., 256:] of one interleaved
+    [n_seq, seq_cap, 288] record); idx [n_q, k] int32; swa [n_seq, swa_cap, 512] u8 (view);
+    swa_base [n_seq] int64; q_pos, replay_start [n_q] int64; out [n_q, H, 512] f32/bf16; lse
+    [n_q, H] f32."""
     _need(idx, torch.int32, 2, "idx")
-    _need(swa, torch.uint8, 3, "swa")
-    _need(swa_base, torch.int64, 1, "swa_base")
-    _need(q_pos, torch.int64, 1, "q_pos")
-    _need(replay_start, torch.int64, 1, "replay_start")
+    kv, sw = _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, idx.shape[0])
     n_q, H, D = q.shape
-    n_seq, seq_cap, _ = kv_codes.shape
     k = idx.shape[1]
-    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (n_q, H, D) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [n_q, H, D] f32/bf16 tensor")
-    if kv_codes.shape[2] != D // 2 or kv_scales.shape != (n_seq, seq_cap, D // 16) or swa.shape[0] != n_seq or \
-            swa.shape[2] != D or swa_base.shape[0] != n_seq or idx.shape[0] != n_q:
-        raise ValueError("sparse_attn: inconsistent shapes")
-    if lse is not None:
-        _need(lse, torch.float32, 2, "lse")
-        if tuple(lse.shape) != (n_q, H):
-            raise ValueError("lse shape")
-    need = csa2_attn_workspace_bytes(n_q, H, D, k, window)
-    workspace, ws_bytes = _workspace(need, workspace, q.device, _bind, "workspace")
-    odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
-    nw, nwt = _new_win(new_win, n_q, D, q_seq)
-    return _run("csa2_sparse_attn", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq), _p(idx),
-                                     k, _p(swa), swa.shape[1], _p(swa_base), _p(q_pos), _p(replay_start), nw, nwt, window,
-                                     ctypes.c_float(sm_scale), _p(out), odt, _p(lse), _p(workspace), ws_bytes,
-                                     _stream()), _bind)
+    tail = _attn_tail(q, k, window, sm_scale, out, lse, workspace, new_win, q_seq, _bind, "sparse_attn")
+    return _run("csa2_sparse_attn", (_p(q), n_q, H, D) + kv + (_p(q_seq), _p(idx), k) + sw +
+                (_p(swa_base), _p(q_pos), _p(replay_start)) + tail, _bind)
 
 
 def csa2_sparse_attn_noalloc_max_bytes() -> int:
@@ -610,12 +582,9 @@ def csa2_sparse_attn_noalloc(q, kv_codes, kv_scales, q_seq, idx, swa, swa_base, 
     """csa2_sparse_attn without a workspace: a split key list's partials go to the library's
     static per-GPU scratch (calls that overlap on one GPU race).  Arguments as csa2_sparse_attn."""
     _need(idx, torch.int32, 2, "idx")
-    _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, idx.shape[0])
+    kv, sw = _attn_args(q, kv_codes, kv_scales, q_seq, swa, swa_base, q_pos, replay_start, out, lse, idx.shape[0])
     n_q, H, D = q.shape
-    n_seq, seq_cap, _ = kv_codes.shape
-    odt = DT_F32 if out.dtype == torch.float32 else DT_BF16
-    nw, nwt = _new_win(new_win, n_q, D, q_seq)
-    return _run("csa2_sparse_attn_noalloc", (_p(q), n_q, H, D, _p(kv_codes), _p(kv_scales), seq_cap, n_seq, _p(q_seq),
-                                             _p(idx), idx.shape[1], _p(swa), swa.shape[1], _p(swa_base), _p(q_pos),
-                                             _p(replay_start), nw, nwt, window, ctypes.c_float(sm_scale), _p(out),
-                                             odt, _p(lse), _stream()), _bind)
+    tail = _attn_tail(q, idx.shape[1], window, sm_scale, out, lse, None, new_win, q_seq, _bind,
+                      "sparse_attn_noalloc", with_workspace=False)
+    return _run("csa2_sparse_attn_noalloc", (_p(q), n_q, H, D) + kv + (_p(q_seq), _p(idx), idx.shape[1]) + sw +
+                (_p(swa_base), _p(q_pos), _p(replay_start)) + tail, _bind)

@@ -77,6 +77,7 @@ struct AttnArgs {
   int n_q, n_heads;
   const uint8_t* kv_codes;
   const uint8_t* kv_scales;
+  int64_t kv_ce, kv_cs, kv_se, kv_ss;   // byte strides: code entry / sequence, scale entry / sequence
   int64_t seq_cap;
   int n_seq;
   const int32_t* q_seq;
@@ -84,6 +85,7 @@ struct AttnArgs {
   int k;
   const uint8_t* swa;
   uint8_t* swa_w;     // the same ring, written only by the window append
+  int64_t swa_re, swa_rs;   // byte strides of the ring: row, sequence
   int64_t swa_cap;
   const int64_t* swa_base;
   const int64_t* q_pos;
@@ -325,11 +327,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     // ring row of token t: the window keys [lo, t] are consecutive rows from win_row0
     int64_t rt = (t - swa_b) % a.swa_cap;
     rt = rt < 0 ? rt + a.swa_cap : rt;
-    a.swa_w[((int64_t)seq * a.swa_cap + rt) * kD + tid] = (uint8_t)new_code;
+    a.swa_w[(int64_t)seq * a.swa_rs + rt * a.swa_re + tid] = (uint8_t)new_code;
   }
-  const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 2);
-  const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.seq_cap * (kD / 16);
-  const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_cap * kD;
+  const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.kv_cs;
+  const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.kv_ss;
+  const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_rs;
   // ---- this pair's tiles: window tiles first (their rows need no index), then main tiles;
   // pair p takes positions p, p+4, ... of that order.  Every wave runs the same number of
   // steps (one exchange with its partner each) and masks the steps past its pair's end ----
@@ -362,15 +364,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     g.is_new = a.new_win != nullptr && ok_win && j == n_swa - 1;   // window key j is token lo + j
     uint32_t row = win_row0 + (uint32_t)j;
     row = ok_win ? (row >= swa_cap32 ? row - swa_cap32 : row) : 0u;
-    // byte offsets fit 32 bits: seq_cap <= 2^24 rows of 256 B, swa_cap <= 2^23 rows of 512 B
-    const uint4* c = is_main ? reinterpret_cast<const uint4*>(kvc + (pm * (kD / 2) + 128 * half + 32 * grp))
-                             : reinterpret_cast<const uint4*>(swq + (row * kD + kHalf * half + 64 * grp));
+    // rows and positions are 32-bit (seq_cap <= 2^24, swa_cap <= 2^23), byte offsets 64-bit
+    const uint4* c = is_main
+        ? reinterpret_cast<const uint4*>(kvc + ((uint64_t)pm * (uint64_t)a.kv_ce + 128 * half + 32 * grp))
+        : reinterpret_cast<const uint4*>(swq + ((uint64_t)row * (uint64_t)a.swa_re + kHalf * half + 64 * grp));
     const uint4* c2 = is_main ? c : c + 2;  // main needs 32 B: the second pair re-reads them
     g.r[0] = c[0];
     g.r[1] = c[1];
     g.r[2] = c2[0];
     g.r[3] = c2[1];
-    g.sc = *reinterpret_cast<const uint32_t*>(kvs + (pm * (kD / 16) + 16 * half + 4 * grp));
+    g.sc = *reinterpret_cast<const uint32_t*>(kvs + ((uint64_t)pm * (uint64_t)a.kv_se + 16 * half + 4 * grp));
     g.ok = is_main ? ok_main : ok_win;
   };
 
@@ -815,14 +818,14 @@ struct AttnSel {
   int block, max_cand_blocks;
 };
 
-static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes, const uint8_t* kv_scales,
+static int sparse_attn(const void* q, int n_q, int n_heads, int dim, CacheRef kv,
                        int64_t seq_cap, int n_seq, const int32_t* q_seq, const int32_t* idx, const AttnSel& sel,
-                       int32_t* idx_out, int32_t* count_out, int k, uint8_t* swa, int64_t swa_cap,
+                       int32_t* idx_out, int32_t* count_out, int k, uint8_t* swa, int64_t swa_re, int64_t swa_rs, int64_t swa_cap,
                        const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
                        const void* new_win, int new_win_dtype, int window, float sm_scale, void* out, int out_dtype,
                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (int rc = csa2_take_device_status()) return rc;
-  if (!q || !kv_codes || !kv_scales || !q_seq || !swa || !swa_base || !q_pos || !replay_start || !out)
+  if (!q || !kv.codes || !kv.scales || !q_seq || !swa || !swa_base || !q_pos || !replay_start || !out)
     return CSA2_ERR_NULL;
   const bool select = sel.mode != 0;
   if (!select && k > 0 && !idx) return CSA2_ERR_NULL;
@@ -837,8 +840,14 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
     return CSA2_ERR_SHAPE;
   if (out_dtype != CSA2_DT_F32 && out_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
   if (new_win && new_win_dtype != CSA2_DT_F32 && new_win_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(kv_codes) || !aligned16(swa) || !aligned16(out) || ((uintptr_t)kv_scales & 7))
+  if (!aligned16(q) || !aligned16(kv.codes) || !aligned16(swa) || !aligned16(out) || ((uintptr_t)kv.scales & 3))
     return CSA2_ERR_SHAPE;
+  // the main-KV cache (D/2 code bytes, D/16 scale bytes per entry; 4-byte scale loads) and
+  // the window ring (D bytes per row, 16-byte loads)
+  if (resolve_cache(kv, seq_cap, kD / 2, kD / 16, 4) != CSA2_OK) return CSA2_ERR_SHAPE;
+  if (swa_re == 0) swa_re = kD;
+  if (swa_rs == 0) swa_rs = swa_cap * swa_re;
+  if (swa_re < kD || swa_rs < 0 || swa_re % 16 || swa_rs % 16) return CSA2_ERR_SHAPE;
   if (n_q == 0) return CSA2_OK;
   AttnPlan p = plan(n_q, n_heads, k, window);
   if (p.grid > 0x7fffffffLL || p.nsplit > kCombThreads) return CSA2_ERR_SHAPE;
@@ -846,8 +855,12 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
   a.q = (const uint16_t*)q;
   a.n_q = n_q;
   a.n_heads = n_heads;
-  a.kv_codes = kv_codes;
-  a.kv_scales = kv_scales;
+  a.kv_codes = kv.codes;
+  a.kv_scales = kv.scales;
+  a.kv_ce = kv.ce;
+  a.kv_cs = kv.cs;
+  a.kv_se = kv.se;
+  a.kv_ss = kv.ss;
   a.seq_cap = seq_cap;
   a.n_seq = n_seq;
   a.q_seq = q_seq;
@@ -855,6 +868,8 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
   a.k = k;
   a.swa = swa;
   a.swa_w = swa;
+  a.swa_re = swa_re;
+  a.swa_rs = swa_rs;
   a.swa_cap = swa_cap;
   a.swa_base = swa_base;
   a.q_pos = q_pos;
@@ -907,15 +922,16 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8
   return csa2_check_launch();
 }
 
-extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
-                                const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
-                                const int32_t* idx, int k, uint8_t* swa, int64_t swa_cap, const int64_t* swa_base,
+extern "C" int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes, int64_t kv_codes_stride, int64_t kv_codes_seq_stride, const uint8_t* kv_scales, int64_t kv_scales_stride, int64_t kv_scales_seq_stride, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                                const int32_t* idx, int k, uint8_t* swa, int64_t swa_row_stride, int64_t swa_seq_stride, int64_t swa_cap, const int64_t* swa_base,
                                 const int64_t* q_pos, const int64_t* replay_start, const void* new_win,
                                 int new_win_dtype, int window, float sm_scale, void* out, int out_dtype, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream) {
   AttnSel sel = {};
-  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, idx, sel, nullptr, nullptr, k,
-                     swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window, sm_scale, out,
+  return sparse_attn(q, n_q, n_heads, dim,
+                     CacheRef{kv_codes, kv_scales, kv_codes_stride, kv_codes_seq_stride, kv_scales_stride,
+                              kv_scales_seq_stride}, seq_cap, n_seq, q_seq, idx, sel, nullptr, nullptr, k,
+                     swa, swa_row_stride, swa_seq_stride, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window, sm_scale, out,
                      out_dtype, lse, workspace, workspace_bytes, stream);
 }
 
@@ -954,9 +970,8 @@ void* csa2_attn_scratch(int* rc_out) {
 
 extern "C" size_t csa2_sparse_attn_noalloc_max_bytes(void) { return kScratchBytes; }
 
-extern "C" int csa2_sparse_attn_noalloc(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
-                                        const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
-                                        const int32_t* idx, int k, uint8_t* swa, int64_t swa_cap,
+extern "C" int csa2_sparse_attn_noalloc(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes, int64_t kv_codes_stride, int64_t kv_codes_seq_stride, const uint8_t* kv_scales, int64_t kv_scales_stride, int64_t kv_scales_seq_stride, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                                        const int32_t* idx, int k, uint8_t* swa, int64_t swa_row_stride, int64_t swa_seq_stride, int64_t swa_cap,
                                         const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
                                         const void* new_win, int new_win_dtype, int window, float sm_scale,
                                         void* out, int out_dtype, float* lse, void* stream) {
@@ -969,15 +984,16 @@ extern "C" int csa2_sparse_attn_noalloc(const void* q, int n_q, int n_heads, int
     if (!ws) return rc != CSA2_OK ? rc : CSA2_ERR_HIP;
   }
   AttnSel sel = {};
-  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, idx, sel, nullptr, nullptr, k,
-                     swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window, sm_scale, out,
+  return sparse_attn(q, n_q, n_heads, dim,
+                     CacheRef{kv_codes, kv_scales, kv_codes_stride, kv_codes_seq_stride, kv_scales_stride,
+                              kv_scales_seq_stride}, seq_cap, n_seq, q_seq, idx, sel, nullptr, nullptr, k,
+                     swa, swa_row_stride, swa_seq_stride, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window, sm_scale, out,
                      out_dtype, lse, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
-extern "C" int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
-                                     const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+extern "C" int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes, int64_t kv_codes_stride, int64_t kv_codes_seq_stride, const uint8_t* kv_scales, int64_t kv_scales_stride, int64_t kv_scales_seq_stride, int64_t seq_cap, int n_seq, const int32_t* q_seq,
                                      const uint64_t* cand_keys, int cand_per_q, int k, int32_t* idx_out,
-                                     int32_t* count_out, uint8_t* swa, int64_t swa_cap, const int64_t* swa_base,
+                                     int32_t* count_out, uint8_t* swa, int64_t swa_row_stride, int64_t swa_seq_stride, int64_t swa_cap, const int64_t* swa_base,
                                      const int64_t* q_pos, const int64_t* replay_start, const void* new_win,
                                      int new_win_dtype, int window, float sm_scale, void* out, int out_dtype,
                                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
@@ -986,17 +1002,18 @@ extern "C" int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int di
   sel.mode = 1;
   sel.cand_keys = cand_keys;
   sel.cand_per_q = cand_per_q;
-  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, nullptr, sel, idx_out,
-                     count_out, k, swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window,
+  return sparse_attn(q, n_q, n_heads, dim,
+                     CacheRef{kv_codes, kv_scales, kv_codes_stride, kv_codes_seq_stride, kv_scales_stride,
+                              kv_scales_seq_stride}, seq_cap, n_seq, q_seq, nullptr, sel, idx_out,
+                     count_out, k, swa, swa_row_stride, swa_seq_stride, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window,
                      sm_scale, out, out_dtype, lse, workspace, workspace_bytes, stream);
 }
 
-extern "C" int csa2_sparse_attn_pool_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
-                                          const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+extern "C" int csa2_sparse_attn_pool_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes, int64_t kv_codes_stride, int64_t kv_codes_seq_stride, const uint8_t* kv_scales, int64_t kv_scales_stride, int64_t kv_scales_seq_stride, int64_t seq_cap, int n_seq, const int32_t* q_seq,
                                           const float* scores, int64_t scores_stride, const int64_t* n_vis,
                                           const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
                                           int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
-                                          uint8_t* swa, int64_t swa_cap, const int64_t* swa_base,
+                                          uint8_t* swa, int64_t swa_row_stride, int64_t swa_seq_stride, int64_t swa_cap, const int64_t* swa_base,
                                           const int64_t* q_pos, const int64_t* replay_start, const void* new_win,
                                           int new_win_dtype, int window, float sm_scale, void* out, int out_dtype,
                                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
@@ -1010,7 +1027,9 @@ extern "C" int csa2_sparse_attn_pool_topk(const void* q, int n_q, int n_heads, i
   sel.n_vis = n_vis;
   sel.block = block;
   sel.max_cand_blocks = max_cand_blocks;
-  return sparse_attn(q, n_q, n_heads, dim, kv_codes, kv_scales, seq_cap, n_seq, q_seq, nullptr, sel, idx_out,
-                     count_out, k, swa, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window,
+  return sparse_attn(q, n_q, n_heads, dim,
+                     CacheRef{kv_codes, kv_scales, kv_codes_stride, kv_codes_seq_stride, kv_scales_stride,
+                              kv_scales_seq_stride}, seq_cap, n_seq, q_seq, nullptr, sel, idx_out,
+                     count_out, k, swa, swa_row_stride, swa_seq_stride, swa_cap, swa_base, q_pos, replay_start, new_win, new_win_dtype, window,
                      sm_scale, out, out_dtype, lse, workspace, workspace_bytes, stream);
 }

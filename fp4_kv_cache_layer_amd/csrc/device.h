@@ -114,6 +114,27 @@ __device__ __forceinline__ int mxfp4_group(const uint32_t (&bits)[32], uint32_t 
   return code;
 }
 
+// A cache's addressing (see the header's cache layouts): entry e of sequence b has its
+// codes at codes + b*cs + e*ce and its scales at scales + b*ss + e*se (bytes).
+struct CacheRef {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int64_t ce, cs, se, ss;
+};
+
+// Fills the dense default for every stride given as 0 and checks the rest: entry strides at
+// least the row size, every stride non-negative, code strides multiples of 16 (16-byte code
+// loads), scale strides multiples of scale_align.  Returns a csa2 status.
+inline int resolve_cache(CacheRef& c, int64_t seq_cap, int64_t code_row, int64_t scale_row, int scale_align) {
+  if (c.ce == 0) c.ce = code_row;
+  if (c.se == 0) c.se = scale_row;
+  if (c.cs == 0) c.cs = seq_cap * c.ce;
+  if (c.ss == 0) c.ss = seq_cap * c.se;
+  if (c.ce < code_row || c.se < scale_row || c.cs < 0 || c.ss < 0) return CSA2_ERR_SHAPE;
+  if (c.ce % 16 || c.cs % 16 || c.se % scale_align || c.ss % scale_align) return CSA2_ERR_SHAPE;
+  return CSA2_OK;
+}
+
 }  // namespace csa2
 
 // Launch-error bookkeeping used by every entry point (defined in abi.hip).

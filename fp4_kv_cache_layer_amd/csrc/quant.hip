@@ -57,8 +57,8 @@ __device__ __forceinline__ uint32_t load_bits<uint16_t>(const uint16_t* p, int64
 template <bool kMap, typename T>
 __device__ __forceinline__ void quant_group_nvfp4(const T* __restrict__ src, int64_t rows, int dim,
                                                   const int64_t* __restrict__ dst_row, int64_t dst_rows,
-                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                  int64_t gid) {
+                                                  uint8_t* __restrict__ codes, int64_t cst,
+                                                  uint8_t* __restrict__ scales, int64_t sst, int64_t gid) {
   const int gpr = dim / 16;
   if (gid >= rows * gpr) return;
   int64_t r = gid / gpr;
@@ -86,17 +86,17 @@ __device__ __forceinline__ void quant_group_nvfp4(const T* __restrict__ src, int
   }
   keep_before_branch(lo, hi, (uint32_t)sc);
   if (d < 0 || d >= dst_rows) return;
-  uint2* out = reinterpret_cast<uint2*>(codes + d * (dim / 2) + g * 8);
+  uint2* out = reinterpret_cast<uint2*>(codes + d * cst + g * 8);
   *out = make_uint2(lo, hi);
-  scales[d * gpr + g] = (uint8_t)sc;
+  scales[d * sst + g] = (uint8_t)sc;
 }
 
 // ---- MXFP4: one thread per 32-channel group ----
 template <bool kMap, typename T>
 __device__ __forceinline__ void quant_group_mxfp4(const T* __restrict__ src, int64_t rows, int dim,
                                                   const int64_t* __restrict__ dst_row, int64_t dst_rows,
-                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                  int64_t gid) {
+                                                  uint8_t* __restrict__ codes, int64_t cst,
+                                                  uint8_t* __restrict__ scales, int64_t sst, int64_t gid) {
   const int gpr = dim / 32;
   if (gid >= rows * gpr) return;
   int64_t r = gid / gpr;
@@ -109,16 +109,16 @@ __device__ __forceinline__ void quant_group_mxfp4(const T* __restrict__ src, int
   const int code = mxfp4_group(bits, w);
   keep_before_branch(w[0] ^ w[1], w[2] ^ w[3], (uint32_t)code);
   if (d < 0 || d >= dst_rows) return;
-  uint4* out = reinterpret_cast<uint4*>(codes + d * (dim / 2) + g * 16);
+  uint4* out = reinterpret_cast<uint4*>(codes + d * cst + g * 16);
   *out = make_uint4(w[0], w[1], w[2], w[3]);
-  scales[d * gpr + g] = (uint8_t)code;
+  scales[d * sst + g] = (uint8_t)code;
 }
 
 // ---- FP8 (E4M3, unscaled): one thread per 8 channels ----
 template <bool kMap, typename T>
 __device__ __forceinline__ void quant_group_fp8(const T* __restrict__ src, int64_t rows, int dim,
                                                 const int64_t* __restrict__ dst_row, int64_t dst_rows,
-                                                uint8_t* __restrict__ codes, int64_t gid) {
+                                                uint8_t* __restrict__ codes, int64_t cst, int64_t gid) {
   const int gpr = dim / 8;
   if (gid >= rows * gpr) return;
   int64_t r = gid / gpr;
@@ -137,7 +137,7 @@ __device__ __forceinline__ void quant_group_fp8(const T* __restrict__ src, int64
   }
   keep_before_branch(lo, hi, 0u);
   if (d < 0 || d >= dst_rows) return;
-  *reinterpret_cast<uint2*>(codes + d * dim + g * 8) = make_uint2(lo, hi);
+  *reinterpret_cast<uint2*>(codes + d * cst + g * 8) = make_uint2(lo, hi);
 }
 
 // one job of a (multi-)quantise launch
@@ -148,6 +148,7 @@ struct QuantJob {
   int64_t dst_rows;
   uint8_t* codes;
   uint8_t* scales;
+  int64_t codes_stride, scales_stride;   // bytes between destination rows
   int dim, fmt, bf16;
   int64_t block0;   // first workgroup of this job
 };
@@ -160,14 +161,24 @@ struct QuantJobs {
 template <bool kMap>
 __device__ __forceinline__ void quant_dispatch_map(const QuantJob& j, int64_t gid) {
   if (j.fmt == CSA2_FMT_NVFP4) {
-    if (j.bf16) quant_group_nvfp4<kMap>((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
-    else quant_group_nvfp4<kMap>((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
+    if (j.bf16)
+      quant_group_nvfp4<kMap>((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.codes_stride,
+                              j.scales, j.scales_stride, gid);
+    else
+      quant_group_nvfp4<kMap>((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.codes_stride,
+                              j.scales, j.scales_stride, gid);
   } else if (j.fmt == CSA2_FMT_MXFP4) {
-    if (j.bf16) quant_group_mxfp4<kMap>((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
-    else quant_group_mxfp4<kMap>((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.scales, gid);
+    if (j.bf16)
+      quant_group_mxfp4<kMap>((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.codes_stride,
+                              j.scales, j.scales_stride, gid);
+    else
+      quant_group_mxfp4<kMap>((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.codes_stride,
+                              j.scales, j.scales_stride, gid);
   } else {
-    if (j.bf16) quant_group_fp8<kMap>((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, gid);
-    else quant_group_fp8<kMap>((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, gid);
+    if (j.bf16)
+      quant_group_fp8<kMap>((const uint16_t*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.codes_stride, gid);
+    else
+      quant_group_fp8<kMap>((const float*)j.src, j.rows, j.dim, j.dst_row, j.dst_rows, j.codes, j.codes_stride, gid);
   }
 }
 
@@ -189,13 +200,21 @@ __global__ __launch_bounds__(256) void k_quant(QuantJobs jobs) {
 }
 
 static int make_job(const void* src, int src_dtype, int64_t rows, int dim, int fmt, const int64_t* dst_row,
-                    int64_t dst_rows, uint8_t* codes, uint8_t* scales, QuantJob* out, int64_t* blocks) {
+                    int64_t dst_rows, uint8_t* codes, int64_t codes_stride, uint8_t* scales, int64_t scales_stride,
+                    QuantJob* out, int64_t* blocks) {
   if (fmt != CSA2_FMT_NVFP4 && fmt != CSA2_FMT_MXFP4 && fmt != CSA2_FMT_FP8) return CSA2_ERR_UNSUPPORTED;
   if (src_dtype != CSA2_DT_F32 && src_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
   if (rows != 0 && (!src || !codes || (fmt != CSA2_FMT_FP8 && !scales))) return CSA2_ERR_NULL;
   const int group = fmt == CSA2_FMT_NVFP4 ? 16 : (fmt == CSA2_FMT_MXFP4 ? 32 : 8);
   if (rows < 0 || dim <= 0 || dim > 8192 || dim % group || dst_rows < 0) return CSA2_ERR_SHAPE;
   if (rows != 0 && !aligned16(codes)) return CSA2_ERR_SHAPE;
+  // destination rows: dense by default; an explicit stride holds the row and keeps the code
+  // stores aligned (16-byte stores for MXFP4, 8-byte ones otherwise)
+  const int64_t code_row = fmt == CSA2_FMT_FP8 ? dim : dim / 2, scale_row = fmt == CSA2_FMT_FP8 ? 0 : dim / group;
+  if (codes_stride == 0) codes_stride = code_row;
+  if (scales_stride == 0) scales_stride = scale_row;
+  if (codes_stride < code_row || scales_stride < scale_row || codes_stride % (fmt == CSA2_FMT_MXFP4 ? 16 : 8))
+    return CSA2_ERR_SHAPE;
   const int64_t work = rows * (dim / group);
   *blocks = (work + 255) / 256;
   if (*blocks > 0x7fffffff) return CSA2_ERR_SHAPE;
@@ -205,6 +224,8 @@ static int make_job(const void* src, int src_dtype, int64_t rows, int dim, int f
   out->dst_rows = dst_rows;
   out->codes = codes;
   out->scales = scales;
+  out->codes_stride = codes_stride;
+  out->scales_stride = scales_stride;
   out->dim = dim;
   out->fmt = fmt;
   out->bf16 = src_dtype == CSA2_DT_BF16;
@@ -223,12 +244,13 @@ static int launch_jobs(QuantJobs& jobs, int64_t total_blocks, hipStream_t st) {
 using namespace csa2;
 
 extern "C" int csa2_quantize_kv(const void* src, int src_dtype, int64_t rows, int dim, int fmt,
-                                const int64_t* dst_row, int64_t dst_rows, uint8_t* codes,
-                                uint8_t* scales, void* stream) {
+                                const int64_t* dst_row, int64_t dst_rows, uint8_t* codes, int64_t codes_stride,
+                                uint8_t* scales, int64_t scales_stride, void* stream) {
   if (int rc_status = csa2_take_device_status()) return rc_status;
   QuantJobs jobs = {};
   int64_t blocks = 0;
-  const int rc = make_job(src, src_dtype, rows, dim, fmt, dst_row, dst_rows, codes, scales, &jobs.job[0], &blocks);
+  const int rc = make_job(src, src_dtype, rows, dim, fmt, dst_row, dst_rows, codes, codes_stride, scales,
+                          scales_stride, &jobs.job[0], &blocks);
   if (rc != CSA2_OK) return rc;
   jobs.n = 1;
   return launch_jobs(jobs, blocks, (hipStream_t)stream);
@@ -244,8 +266,8 @@ extern "C" int csa2_quantize_kv_multi(const csa2_quant_job* jobs, int n_jobs, vo
     const csa2_quant_job& j = jobs[i];
     int64_t blocks = 0;
     QuantJob q;
-    const int rc = make_job(j.src, j.src_dtype, j.rows, j.dim, j.fmt, j.dst_row, j.dst_rows, j.codes, j.scales, &q,
-                            &blocks);
+    const int rc = make_job(j.src, j.src_dtype, j.rows, j.dim, j.fmt, j.dst_row, j.dst_rows, j.codes,
+                            j.codes_stride, j.scales, j.scales_stride, &q, &blocks);
     if (rc != CSA2_OK) return rc;
     if (blocks == 0) continue;
     q.block0 = total;

@@ -48,6 +48,7 @@ struct ScoreArgs {
   int n_heads;
   const uint8_t* k_codes;
   const uint8_t* k_scales;
+  int64_t k_ce, k_cs, k_se, k_ss;   // byte strides: code entry / sequence, scale entry / sequence
   int64_t seq_cap;
   int n_seq;
   const int32_t* q_seq;
@@ -158,9 +159,8 @@ __device__ __forceinline__ float score_tiles_nv(const v8h (&a)[4], const float (
 }
 
 // One query's view of the cache: MFMA operands, slot -> row mapping, one scoring step.
-// Slots and rows are 32-bit (seq_cap <= 2^26, so byte offsets within a sequence fit in 32
-// bits) and the sequence's base pointers are workgroup-uniform, so each load is a scalar
-// base plus one 32-bit vector offset.
+// Slots and rows are 32-bit (seq_cap <= 2^26) and the sequence's base pointers are
+// workgroup-uniform, so each load is a scalar base plus the row times the entry stride.
 template <bool kPool, bool kNv, bool kQLat = false>
 struct QueryScorer {
   // scale bytes per entry (and per query head row): one per 32 channels (MXFP4) or per 16
@@ -195,8 +195,8 @@ struct QueryScorer {
       n_valid = nv;
       cb = nullptr;
     }
-    kc = s.k_codes + (int64_t)seq * s.seq_cap * 64;
-    ks = s.k_scales + (int64_t)seq * s.seq_cap * kScalesPerRow;
+    kc = s.k_codes + (int64_t)seq * s.k_cs;
+    ks = s.k_scales + (int64_t)seq * s.k_ss;
     a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     a_scale = 127;
 #pragma unroll
@@ -280,11 +280,13 @@ struct QueryScorer {
     for (int t = 0; t < 4; ++t) {
       uint32_t pos;
       slot_pos(s, base + 16 * t + row, pos);
-      const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(kc + (pos * 64u + kb * 16u)));
+      const v4u v = __builtin_nontemporal_load(
+          reinterpret_cast<const v4u*>(kc + ((uint64_t)pos * (uint64_t)s.k_ce + kb * 16u)));
       bc[t] = make_uint4(v.x, v.y, v.z, v.w);
       // NVFP4: the two scale bytes of this lane's 32 channels, one 16-bit load
-      bs[t] = kNv ? (int)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(ks + (pos * 8u + kb * 2u)))
-                  : (int)__builtin_nontemporal_load(ks + (pos * 4u + kb));
+      const uint8_t* sp = ks + (uint64_t)pos * (uint64_t)s.k_se;
+      bs[t] = kNv ? (int)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sp + kb * 2u))
+                  : (int)__builtin_nontemporal_load(sp + kb);
     }
   }
 
@@ -345,17 +347,18 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_grouped(ScoreArgs s, in
   const int chunk_lo = chunk * s.chunk_len;
   if (chunk_lo >= nv_max) return;
   const int hi = chunk_lo + s.chunk_len < nv_max ? chunk_lo + s.chunk_len : nv_max;
-  const uint8_t* kc = s.k_codes + (int64_t)seq * s.seq_cap * 64;
-  const uint8_t* ks = s.k_scales + (int64_t)seq * s.seq_cap * 4;
+  const uint8_t* kc = s.k_codes + (int64_t)seq * s.k_cs;
+  const uint8_t* ks = s.k_scales + (int64_t)seq * s.k_ss;
   // entries past the group's visible range read entry 0 and their results are discarded
   auto load_step = [&](int base, uint4 (&bc)[4], int (&bs)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int e = base + 16 * t + row;
       const uint32_t pos = e < nv_max ? (uint32_t)e : 0u;
-      const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(kc + (pos * 64u + kb * 16u)));
+      const v4u v = __builtin_nontemporal_load(
+          reinterpret_cast<const v4u*>(kc + ((uint64_t)pos * (uint64_t)s.k_ce + kb * 16u)));
       bc[t] = make_uint4(v.x, v.y, v.z, v.w);
-      bs[t] = __builtin_nontemporal_load(ks + (pos * 4u + kb));
+      bs[t] = __builtin_nontemporal_load(ks + ((uint64_t)pos * (uint64_t)s.k_se + kb));
     }
   };
   int base = chunk_lo + wave * kScoreStep;
@@ -449,16 +452,16 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topk_grouped(ScoreArgs 
   }
   const int lo = range * range_len;
   const int hi = lo + range_len < nv_max ? lo + range_len : nv_max;   // uniform over the wave
-  const uint8_t* kc = s.k_codes + (int64_t)(seq_ok ? seq : 0) * s.seq_cap * 64;
-  const uint8_t* ks = s.k_scales + (int64_t)(seq_ok ? seq : 0) * s.seq_cap * 4;
+  const uint8_t* kc = s.k_codes + (int64_t)(seq_ok ? seq : 0) * s.k_cs;
+  const uint8_t* ks = s.k_scales + (int64_t)(seq_ok ? seq : 0) * s.k_ss;
   auto load_step = [&](int base, uint4 (&bc)[4], int (&bs)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int e = base + 16 * t + row;
       const uint32_t pos = e < hi ? (uint32_t)e : 0u;
-      const v4u v = *reinterpret_cast<const v4u*>(kc + (pos * 64u + kb * 16u));
+      const v4u v = *reinterpret_cast<const v4u*>(kc + ((uint64_t)pos * (uint64_t)s.k_ce + kb * 16u));
       bc[t] = make_uint4(v.x, v.y, v.z, v.w);
-      bs[t] = ks[pos * 4u + kb];
+      bs[t] = ks[(uint64_t)pos * (uint64_t)s.k_se + kb];
     }
   };
   int cnt[kGtRowsPerWave];
@@ -646,15 +649,29 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
                          s.count_out);
 }
 
+// The indexer-K cache of a call: fmt (CSA2_FMT_MXFP4 or CSA2_FMT_NVFP4) fixes its scale row
+// (4 bytes of E8M0 or 8 of E4M3 per 128 channels; NVFP4 scales are read two bytes at a time).
+static int resolve_index_cache(int fmt, CacheRef& kr, int64_t seq_cap) {
+  if (fmt != CSA2_FMT_MXFP4 && fmt != CSA2_FMT_NVFP4) return CSA2_ERR_UNSUPPORTED;
+  if (!kr.codes || !kr.scales) return CSA2_ERR_NULL;
+  if (!aligned16(kr.codes)) return CSA2_ERR_SHAPE;
+  const bool nv = fmt == CSA2_FMT_NVFP4;
+  if (nv && ((uintptr_t)kr.scales & 1u)) return CSA2_ERR_SHAPE;
+  return resolve_cache(kr, seq_cap, CSA2_INDEX_DIM / 2, nv ? CSA2_INDEX_DIM / 16 : CSA2_INDEX_DIM / 32, nv ? 2 : 1);
+}
+
 static int check_score_args(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q, int n_heads,
-                            int dim, const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
-                            const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
-                            const int32_t* n_cand_blocks, int block, int max_cand_blocks, int64_t* n_slots) {
-  if (!q_codes || !q_scales || !w || !k_codes || !k_scales || !q_seq || !n_vis) return CSA2_ERR_NULL;
+                            int dim, int fmt, CacheRef& kr, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                            const int64_t* n_vis, const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                            int max_cand_blocks, int64_t* n_slots) {
+  if (!q_codes || !q_scales || !w || !q_seq || !n_vis) return CSA2_ERR_NULL;
   if (n_q < 0 || n_heads < 1 || n_heads > CSA2_MAX_INDEX_HEADS || dim != CSA2_INDEX_DIM || seq_cap < 0 ||
       seq_cap > CSA2_MAX_INDEX_ENTRIES || n_seq < 1)
     return CSA2_ERR_SHAPE;
-  if (!aligned16(q_codes) || !aligned16(k_codes)) return CSA2_ERR_SHAPE;
+  if (!aligned16(q_codes)) return CSA2_ERR_SHAPE;
+  if (fmt == CSA2_FMT_NVFP4 && ((uintptr_t)q_scales & 1u)) return CSA2_ERR_SHAPE;
+  const int rc = resolve_index_cache(fmt, kr, seq_cap);
+  if (rc != CSA2_OK) return rc;
   if (cand_blocks) {
     if (!n_cand_blocks) return CSA2_ERR_NULL;
     if (block < 1 || block > 64 || max_cand_blocks < 1 || max_cand_blocks > (1 << 20)) return CSA2_ERR_SHAPE;
@@ -666,16 +683,20 @@ static int check_score_args(const uint8_t* q_codes, const uint8_t* q_scales, con
 }
 
 static ScoreArgs make_args(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_heads,
-                           const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
-                           const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
-                           const int32_t* n_cand_blocks, int block, int max_cand_blocks, int64_t n_slots) {
+                           const CacheRef& kr, int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
+                           const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block, int max_cand_blocks,
+                           int64_t n_slots) {
   ScoreArgs a = {};
   a.q_codes = q_codes;
   a.q_scales = q_scales;
   a.w = w;
   a.n_heads = n_heads;
-  a.k_codes = k_codes;
-  a.k_scales = k_scales;
+  a.k_codes = kr.codes;
+  a.k_scales = kr.scales;
+  a.k_ce = kr.ce;
+  a.k_cs = kr.cs;
+  a.k_se = kr.se;
+  a.k_ss = kr.ss;
   a.seq_cap = seq_cap;
   a.n_seq = n_seq;
   a.q_seq = q_seq;
@@ -722,89 +743,95 @@ static size_t index_topk_ws(int n_q, int64_t n_slots, int k, bool pool) {
   return (((size_t)n_q * n_slots * sizeof(float) + 255) & ~(size_t)255) + sel + 256;
 }
 
+static size_t index_topk_pool_ws(int n_q, int64_t n_slots, int k, int block, int max_blocks, size_t* bmax_bytes,
+                                 size_t* sel_bytes) {
+  const int64_t nblk = (n_slots + block - 1) / block;
+  *bmax_bytes = (((size_t)n_q * nblk * sizeof(float)) + 255) & ~(size_t)255;
+  *sel_bytes = (ws_bytes(n_q, n_slots, k) + 255) & ~(size_t)255;
+  return 256 + *bmax_bytes + *sel_bytes + ws_bytes(n_q, nblk, max_blocks) + 256;
+}
+
+// Ranges per row of csa2_index_topk_grouped: a power of two (so that, with consecutive
+// workgroups on consecutive XCDs, one range's workgroups share an XCD and its L2 holds the
+// range's indexer K), with all ranges' survivors within one last selection level (n_ranges *
+// k <= 8,192) and ranges of at least 8,192 entries; as many as that allows while the grid is
+// below 3 workgroups per CU (the LDS of the candidate lists fits three), and at least 16,384
+// entries per range beyond.
+static int grouped_ranges(int64_t seq_cap, int k, int64_t n_groups) {
+  int n = 1;
+  auto ok = [&](int m) { return m <= 16 && (int64_t)m * k <= kTkSeg && seq_cap >= (int64_t)m * 8192; };
+  while (ok(2 * n) && (n_groups * n < 3 * 256 || seq_cap >= (int64_t)2 * n * 16384)) n *= 2;
+  return n;
+}
+
 }  // namespace csa2
 
 using namespace csa2;
 
-// the NVFP4 scale arrays are read two bytes at a time
-static int check_nv_scales(const uint8_t* q_scales, const uint8_t* k_scales) {
-  return (((uintptr_t)q_scales | (uintptr_t)k_scales) & 1u) ? CSA2_ERR_SHAPE : CSA2_OK;
-}
+#define CSA2_INDEX_CACHE_ARGS                                                                          \
+  int fmt, const uint8_t *k_codes, int64_t k_codes_stride, int64_t k_codes_seq_stride,                 \
+      const uint8_t *k_scales, int64_t k_scales_stride, int64_t k_scales_seq_stride
+#define CSA2_INDEX_CACHE_REF \
+  CacheRef { k_codes, k_scales, k_codes_stride, k_codes_seq_stride, k_scales_stride, k_scales_seq_stride }
 
-static int index_score(bool nv, const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q, int n_heads,
-                       int dim, const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
-                       const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
-                       const int32_t* n_cand_blocks, int block, int max_cand_blocks, float* scores,
-                       int64_t scores_stride, void* stream) {
+extern "C" int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                                int n_heads, int dim, CSA2_INDEX_CACHE_ARGS, int64_t seq_cap, int n_seq,
+                                const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
+                                const int32_t* n_cand_blocks, int block, int max_cand_blocks, float* scores,
+                                int64_t scores_stride, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
+  CacheRef kr = CSA2_INDEX_CACHE_REF;
   int64_t n_slots = 0;
-  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, fmt, kr, seq_cap, n_seq, q_seq, n_vis,
                             cand_blocks, n_cand_blocks, block, max_cand_blocks, &n_slots);
-  if (rc == CSA2_OK && nv) rc = check_nv_scales(q_scales, k_scales);
   if (rc != CSA2_OK) return rc;
   if (!scores) return CSA2_ERR_NULL;
   if (scores_stride < n_slots) return CSA2_ERR_SHAPE;
   if (n_q == 0 || n_slots == 0) return CSA2_OK;
-  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
-                          n_cand_blocks, block, max_cand_blocks, n_slots);
-  return launch_score(a, n_q, scores, scores_stride, nv, (hipStream_t)stream);
-}
-
-extern "C" int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                                int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                                int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                                const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
-                                int max_cand_blocks, float* scores, int64_t scores_stride, void* stream) {
-  if (int rc_status = csa2_take_device_status()) return rc_status;
-  return index_score(false, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
-                     cand_blocks, n_cand_blocks, block, max_cand_blocks, scores, scores_stride, stream);
-}
-
-extern "C" int csa2_index_score_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                                      int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                                      int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                                      const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
-                                      int max_cand_blocks, float* scores, int64_t scores_stride, void* stream) {
-  if (int rc_status = csa2_take_device_status()) return rc_status;
-  return index_score(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
-                     cand_blocks, n_cand_blocks, block, max_cand_blocks, scores, scores_stride, stream);
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, cand_blocks, n_cand_blocks,
+                          block, max_cand_blocks, n_slots);
+  return launch_score(a, n_q, scores, scores_stride, fmt == CSA2_FMT_NVFP4, (hipStream_t)stream);
 }
 
 extern "C" int csa2_index_score_q(const void* q, int q_dtype, const float* w, int n_q, int n_heads, int dim,
-                                  const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
-                                  const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
-                                  const int32_t* n_cand_blocks, int block, int max_cand_blocks, float* scores,
-                                  int64_t scores_stride, void* stream) {
+                                  CSA2_INDEX_CACHE_ARGS, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                                  const int64_t* n_vis, const int32_t* cand_blocks, const int32_t* n_cand_blocks,
+                                  int block, int max_cand_blocks, float* scores, int64_t scores_stride, void* stream) {
   if (int rc_status = csa2_take_device_status()) return rc_status;
   if (q_dtype != CSA2_DT_F32 && q_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
+  if (fmt != CSA2_FMT_MXFP4) return CSA2_ERR_UNSUPPORTED;
+  CacheRef kr = CSA2_INDEX_CACHE_REF;
   const uint8_t* qb = static_cast<const uint8_t*>(q);   // checked as the Q array: non-null, 16-byte aligned
   int64_t n_slots = 0;
-  int rc = check_score_args(qb, qb, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
-                            cand_blocks, n_cand_blocks, block, max_cand_blocks, &n_slots);
+  int rc = check_score_args(qb, qb, w, n_q, n_heads, dim, fmt, kr, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
+                            n_cand_blocks, block, max_cand_blocks, &n_slots);
   if (rc != CSA2_OK) return rc;
   if (!scores) return CSA2_ERR_NULL;
   if (scores_stride < n_slots) return CSA2_ERR_SHAPE;
   if (n_q == 0 || n_slots == 0) return CSA2_OK;
-  ScoreArgs a = make_args(nullptr, nullptr, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
-                          n_cand_blocks, block, max_cand_blocks, n_slots);
+  ScoreArgs a = make_args(nullptr, nullptr, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, cand_blocks, n_cand_blocks,
+                          block, max_cand_blocks, n_slots);
   a.q_lat = q;
   a.q_bf16 = q_dtype == CSA2_DT_BF16;
   return launch_score(a, n_q, scores, scores_stride, false, (hipStream_t)stream, true);
 }
 
 extern "C" int csa2_index_score_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                                        int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                                        int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                                        int group, float* scores, int64_t scores_stride, void* stream) {
+                                        int n_heads, int dim, CSA2_INDEX_CACHE_ARGS, int64_t seq_cap, int n_seq,
+                                        const int32_t* q_seq, const int64_t* n_vis, int group, float* scores,
+                                        int64_t scores_stride, void* stream) {
   if (int rc_status = csa2_take_device_status()) return rc_status;
+  if (fmt != CSA2_FMT_MXFP4) return CSA2_ERR_UNSUPPORTED;
+  CacheRef kr = CSA2_INDEX_CACHE_REF;
   int64_t n_slots = 0;
-  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
-                            nullptr, nullptr, 0, 0, &n_slots);
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, fmt, kr, seq_cap, n_seq, q_seq, n_vis, nullptr,
+                            nullptr, 0, 0, &n_slots);
   if (rc != CSA2_OK) return rc;
   if (!scores) return CSA2_ERR_NULL;
   if (group < 1 || group > kGroupMax || scores_stride < n_slots) return CSA2_ERR_SHAPE;
   if (n_q == 0 || n_slots == 0) return CSA2_OK;
-  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, nullptr,
-                          nullptr, 0, 0, n_slots);
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, nullptr, nullptr, 0, 0,
+                          n_slots);
   const int64_t groups = ((int64_t)n_q + group - 1) / group;
   // chunks of 4,096 entries, halved (down to 1,024) while that leaves fewer than four
   // workgroups per CU
@@ -826,16 +853,18 @@ extern "C" size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int 
   return index_topk_ws(n_q, n_slots, k, in_pool != 0);
 }
 
-static int index_topk(bool nv, const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q, int n_heads,
-                      int dim, const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
-                      const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
-                      const int32_t* n_cand_blocks, int block, int max_cand_blocks, int k, int32_t* idx_out,
-                      int32_t* count_out, void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q, int n_heads,
+                               int dim, CSA2_INDEX_CACHE_ARGS, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                               const int64_t* n_vis, const int32_t* cand_blocks, const int32_t* n_cand_blocks,
+                               int block, int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
+  CacheRef kr = CSA2_INDEX_CACHE_REF;
   int64_t n_slots = 0;
-  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, fmt, kr, seq_cap, n_seq, q_seq, n_vis,
                             cand_blocks, n_cand_blocks, block, max_cand_blocks, &n_slots);
-  if (rc == CSA2_OK && nv) rc = check_nv_scales(q_scales, k_scales);
   if (rc != CSA2_OK) return rc;
+  const bool nv = fmt == CSA2_FMT_NVFP4;
   if (!idx_out || !count_out) return CSA2_ERR_NULL;
   if (n_q > 65535 || k < 1 || k > CSA2_MAX_TOPK || n_slots > 0x7fffffffLL) return CSA2_ERR_SHAPE;
   if (n_q == 0) return CSA2_OK;
@@ -849,8 +878,8 @@ static int index_topk(bool nv, const uint8_t* q_codes, const uint8_t* q_scales, 
   if (cand_blocks) {  // inside a pool: scores into the workspace, then the selection levels
     float* sc = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
     const size_t sc_bytes = ((size_t)n_q * n0 * sizeof(float) + 255) & ~(size_t)255;
-    ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
-                            cand_blocks, n_cand_blocks, block, max_cand_blocks, n_slots);
+    ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
+                            n_cand_blocks, block, max_cand_blocks, n_slots);
     rc = launch_score(a, n_q, sc, n0, nv, st);
     if (rc != CSA2_OK) return rc;
     TkArgs t = {};
@@ -866,12 +895,13 @@ static int index_topk(bool nv, const uint8_t* q_codes, const uint8_t* q_scales, 
     t.count_out = count_out;
     t.k = k;
     t.n_slots = n0;
-    return select_from_scores(t, n_q, n0, (uint8_t*)sc + sc_bytes, workspace_bytes - (size_t)((uint8_t*)sc + sc_bytes - (uint8_t*)workspace), st);
+    uint8_t* rest = (uint8_t*)sc + sc_bytes;
+    return select_from_scores(t, n_q, n0, rest, workspace_bytes - (size_t)(rest - (uint8_t*)workspace), st);
   }
   uint64_t* bufA = (uint64_t*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   uint64_t* bufB = bufA + (size_t)k * n_q * segs[0];
-  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
-                          n_cand_blocks, block, max_cand_blocks, n_slots);
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, cand_blocks, n_cand_blocks,
+                          block, max_cand_blocks, n_slots);
   a.k = k;
   a.keys_out = bufA;
   a.idx_out = idx_out;
@@ -895,38 +925,6 @@ static int index_topk(bool nv, const uint8_t* q_codes, const uint8_t* q_scales, 
   return select_levels_after0(segs, L, t, n_q, bufA, bufB, st);
 }
 
-extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                               int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                               int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                               const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
-                               int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out, void* workspace,
-                               size_t workspace_bytes, void* stream) {
-  if (int rc_status = csa2_take_device_status()) return rc_status;
-  return index_topk(false, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
-                    cand_blocks, n_cand_blocks, block, max_cand_blocks, k, idx_out, count_out, workspace,
-                    workspace_bytes, stream);
-}
-
-extern "C" int csa2_index_topk_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                                     int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                                     int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                                     const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
-                                     int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (int rc_status = csa2_take_device_status()) return rc_status;
-  return index_topk(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
-                    cand_blocks, n_cand_blocks, block, max_cand_blocks, k, idx_out, count_out, workspace,
-                    workspace_bytes, stream);
-}
-
-static size_t index_topk_pool_ws(int n_q, int64_t n_slots, int k, int block, int max_blocks, size_t* bmax_bytes,
-                                 size_t* sel_bytes) {
-  const int64_t nblk = (n_slots + block - 1) / block;
-  *bmax_bytes = (((size_t)n_q * nblk * sizeof(float)) + 255) & ~(size_t)255;
-  *sel_bytes = (ws_bytes(n_q, n_slots, k) + 255) & ~(size_t)255;
-  return 256 + *bmax_bytes + *sel_bytes + ws_bytes(n_q, nblk, max_blocks) + 256;
-}
-
 // ---- csa2_index_segments: the fused first level alone; the last one runs in the
 // attention kernel (csa2_sparse_attn_topk) ----
 extern "C" int64_t csa2_segment_keys(int64_t n_slots, int k) {
@@ -935,75 +933,48 @@ extern "C" int64_t csa2_segment_keys(int64_t n_slots, int k) {
   return n_seg * k;
 }
 
-static int index_segments(bool nv, const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                          int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap,
-                          int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k, uint64_t* cand_keys,
-                          void* stream) {
+extern "C" int csa2_index_segments(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
+                                   int n_heads, int dim, CSA2_INDEX_CACHE_ARGS, int64_t seq_cap, int n_seq,
+                                   const int32_t* q_seq, const int64_t* n_vis, int k, uint64_t* cand_keys,
+                                   void* stream) {
+  if (int rc_status = csa2_take_device_status()) return rc_status;
+  CacheRef kr = CSA2_INDEX_CACHE_REF;
   int64_t n_slots = 0;
-  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
-                            nullptr, nullptr, 8, 1, &n_slots);
-  if (rc == CSA2_OK && nv) rc = check_nv_scales(q_scales, k_scales);
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, fmt, kr, seq_cap, n_seq, q_seq, n_vis, nullptr,
+                            nullptr, 8, 1, &n_slots);
   if (rc != CSA2_OK) return rc;
   if (!cand_keys) return CSA2_ERR_NULL;
   if (n_q > 65535 || k < 1 || k > CSA2_MAX_TOPK || n_slots > 0x7fffffffLL) return CSA2_ERR_SHAPE;
   if (n_q == 0) return CSA2_OK;
   const int64_t n_seg = csa2_segment_keys(n_slots, k) / k;
-  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, nullptr,
-                          nullptr, 8, 1, n_slots);
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, nullptr, nullptr, 8, 1,
+                          n_slots);
   a.k = k;
   a.keys_out = cand_keys;
   dim3 grid((unsigned)n_seg, (unsigned)n_q), blk(kScoreThreads);
   hipStream_t st = (hipStream_t)stream;
-  if (nv) hipLaunchKernelGGL((k_score_select<false, false, false, true>), grid, blk, 0, st, a);
+  if (fmt == CSA2_FMT_NVFP4) hipLaunchKernelGGL((k_score_select<false, false, false, true>), grid, blk, 0, st, a);
   else hipLaunchKernelGGL((k_score_select<false, false, false, false>), grid, blk, 0, st, a);
   return csa2_check_launch();
 }
 
-extern "C" int csa2_index_segments(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                                   int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                                   int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k,
-                                   uint64_t* cand_keys, void* stream) {
-  if (int rc_status = csa2_take_device_status()) return rc_status;
-  return index_segments(false, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq,
-                        n_vis, k, cand_keys, stream);
-}
-
-extern "C" int csa2_index_segments_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                                         int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                                         int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                                         int k, uint64_t* cand_keys, void* stream) {
-  if (int rc_status = csa2_take_device_status()) return rc_status;
-  return index_segments(true, q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq,
-                        n_vis, k, cand_keys, stream);
-}
-
 // ---- csa2_index_topk_grouped: grouped rows, scored and selected without a score array ----
-// Ranges per row: a power of two (so that, with consecutive workgroups on consecutive XCDs,
-// one range's workgroups share an XCD and its L2 holds the range's indexer K), with all
-// ranges' survivors within one last selection level (n_ranges * k <= 8,192) and ranges of at
-// least 8,192 entries; as many as that allows while the grid is below 3 workgroups per CU
-// (the LDS of the candidate lists fits three), and at least 16,384 entries per range beyond.
-static int grouped_ranges(int64_t seq_cap, int k, int64_t n_groups) {
-  int n = 1;
-  auto ok = [&](int m) { return m <= 16 && (int64_t)m * k <= kTkSeg && seq_cap >= (int64_t)m * 8192; };
-  while (ok(2 * n) && (n_groups * n < 3 * 256 || seq_cap >= (int64_t)2 * n * 16384)) n *= 2;
-  return n;
-}
-
 extern "C" size_t csa2_index_topk_grouped_workspace_bytes(int n_q, int64_t seq_cap, int k, int group) {
   if (n_q <= 0 || seq_cap < 0 || k < 1 || k > CSA2_MAX_GROUPED_TOPK || group < 1 || group > kGroupMax) return 0;
   return (size_t)n_q * grouped_ranges(seq_cap, k, (n_q + group - 1) / group) * k * sizeof(uint64_t) + 256;
 }
 
 extern "C" int csa2_index_topk_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                                       int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                                       int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                                       int group, int k, int32_t* idx_out, int32_t* count_out, void* workspace,
+                                       int n_heads, int dim, CSA2_INDEX_CACHE_ARGS, int64_t seq_cap, int n_seq,
+                                       const int32_t* q_seq, const int64_t* n_vis, int group, int k,
+                                       int32_t* idx_out, int32_t* count_out, void* workspace,
                                        size_t workspace_bytes, void* stream) {
   if (int rc_status = csa2_take_device_status()) return rc_status;
+  if (fmt != CSA2_FMT_MXFP4) return CSA2_ERR_UNSUPPORTED;
+  CacheRef kr = CSA2_INDEX_CACHE_REF;
   int64_t n_slots = 0;
-  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
-                            nullptr, nullptr, 8, 1, &n_slots);
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, fmt, kr, seq_cap, n_seq, q_seq, n_vis, nullptr,
+                            nullptr, 8, 1, &n_slots);
   if (rc != CSA2_OK) return rc;
   if (!idx_out || !count_out) return CSA2_ERR_NULL;
   if (group < 1 || group > kGroupMax || k < 1 || k > CSA2_MAX_GROUPED_TOPK || n_q > 65535 * group)
@@ -1016,8 +987,8 @@ extern "C" int csa2_index_topk_grouped(const uint8_t* q_codes, const uint8_t* q_
   int64_t range_len = (seq_cap + n_ranges - 1) / n_ranges;
   range_len = (range_len + 63) / 64 * 64;
   if (range_len < 64) range_len = 64;
-  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, nullptr,
-                          nullptr, 8, 1, n_slots);
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, nullptr, nullptr, 8, 1,
+                          n_slots);
   a.k = k;
   a.keys_out = (uint64_t*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   hipStream_t st = (hipStream_t)stream;
@@ -1044,15 +1015,16 @@ extern "C" size_t csa2_index_topk_pool_workspace_bytes(int n_q, int64_t n_slots,
 }
 
 extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                                    int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                                    int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k,
-                                    int32_t* idx_out, int32_t* count_out, int block, int max_blocks,
-                                    int32_t* blocks_out, int32_t* blocks_count, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+                                    int n_heads, int dim, CSA2_INDEX_CACHE_ARGS, int64_t seq_cap, int n_seq,
+                                    const int32_t* q_seq, const int64_t* n_vis, int k, int32_t* idx_out,
+                                    int32_t* count_out, int block, int max_blocks, int32_t* blocks_out,
+                                    int32_t* blocks_count, void* workspace, size_t workspace_bytes, void* stream) {
   if (int rc_status = csa2_take_device_status()) return rc_status;
+  if (fmt != CSA2_FMT_MXFP4) return CSA2_ERR_UNSUPPORTED;
+  CacheRef kr = CSA2_INDEX_CACHE_REF;
   int64_t n_slots = 0;
-  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis,
-                            nullptr, nullptr, 0, 0, &n_slots);
+  int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, fmt, kr, seq_cap, n_seq, q_seq, n_vis, nullptr,
+                            nullptr, 0, 0, &n_slots);
   if (rc != CSA2_OK) return rc;
   if (!idx_out || !count_out || !blocks_out || !blocks_count) return CSA2_ERR_NULL;
   if (n_q > 65535 || k < 1 || k > CSA2_MAX_TOPK || block < 1 || block > 64 || (block & (block - 1)) ||
@@ -1074,8 +1046,8 @@ extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_sca
   const size_t pool_ws_bytes = workspace_bytes - (size_t)(pool_ws - (uint8_t*)workspace);
   const int64_t nblk = (n0 + block - 1) / block;
 
-  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, k_codes, k_scales, seq_cap, n_seq, q_seq, n_vis, nullptr,
-                          nullptr, block, 0, n_slots);
+  ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, nullptr, nullptr, block, 0,
+                          n_slots);
   a.k = k;
   a.keys_out = bufA;
   a.idx_out = idx_out;

@@ -106,10 +106,18 @@ class Caches:
 
     @staticmethod
     def empty(n_seq: int, seq_cap: int, swa_layers, swa_cap: int, dim: int = 512, idx_dim: int = 128,
-              device="cuda", index_fmt: str = "mxfp4"):
+              device="cuda", index_fmt: str = "mxfp4", interleaved: bool = False):
+        """interleaved: the main KV as one record per entry, its dim/2 code bytes followed by
+        its dim/16 scale bytes (288 bytes at dim 512, [W] "FP4 与 SWA Bounded Replay"); codes and
+        scales are then two strided views of it."""
         u8 = dict(dtype=torch.uint8, device=device)
         per = INDEX_FORMATS[index_fmt][1]
-        return Caches(torch.zeros(n_seq, seq_cap, dim // 2, **u8), torch.zeros(n_seq, seq_cap, dim // 16, **u8),
+        if interleaved:
+            rec = torch.zeros(n_seq, seq_cap, dim // 2 + dim // 16, **u8)
+            kv_codes, kv_scales = rec[..., :dim // 2], rec[..., dim // 2:]
+        else:
+            kv_codes, kv_scales = torch.zeros(n_seq, seq_cap, dim // 2, **u8), torch.zeros(n_seq, seq_cap, dim // 16, **u8)
+        return Caches(kv_codes, kv_scales,
                       torch.zeros(n_seq, seq_cap, idx_dim // 2, **u8), torch.zeros(n_seq, seq_cap, idx_dim // per, **u8),
                       {L: torch.zeros(n_seq, swa_cap, dim, **u8) for L in swa_layers},
                       torch.zeros(n_seq, dtype=torch.int64, device=device))
@@ -184,12 +192,12 @@ class Csa2Step:
                                   self.qi_scales.view(n_q * h, d // self.idx_group), _bind=bind)
 
     def score(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False):
-        fn = C.csa2_index_score_nvfp4 if self.index_fmt == "nvfp4" else C.csa2_index_score
         if in_pool:
-            return fn(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.scores,
-                      self.pool, self.pool_count, self.block, _bind=bind)
-        return fn(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.scores,
-                  _bind=bind)
+            return C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
+                                      self.scores, self.pool, self.pool_count, self.block, fmt=self.idx_qfmt,
+                                      _bind=bind)
+        return C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
+                                  self.scores, fmt=self.idx_qfmt, _bind=bind)
 
     def score_q(self, caches: Caches, q_index_f32, w, q_seq, n_vis, in_pool: bool = False, bind=False):
         """Slot scores from the unquantised indexer Q (MXFP4, quantised inside the call)."""
@@ -224,9 +232,9 @@ class Csa2Step:
     def index_topk(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False):
         """score + select in one pass, without the score array."""
         pool = (self.pool, self.pool_count) if in_pool else (None, None)
-        fn = C.csa2_index_topk_nvfp4 if self.index_fmt == "nvfp4" else C.csa2_index_topk
-        return fn(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.k, self.idx,
-                  self.count, self.ws_index_topk, pool[0], pool[1], self.block, _bind=bind)
+        return C.csa2_index_topk(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
+                                 self.k, self.idx, self.count, self.ws_index_topk, pool[0], pool[1], self.block,
+                                 fmt=self.idx_qfmt, _bind=bind)
 
     def index_topk_build_pool(self, caches: Caches, w, q_seq, n_vis, bind=False):
         """score + select + pool in one pass (the decoder's first Full layer)."""
@@ -237,9 +245,8 @@ class Csa2Step:
 
     def index_segments(self, caches: Caches, w, q_seq, n_vis, bind=False):
         """the first Top-K level alone (its survivors feed attend_topk)."""
-        fn = C.csa2_index_segments_nvfp4 if self.index_fmt == "nvfp4" else C.csa2_index_segments
-        return fn(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, self.k,
-                  self.cand_keys, _bind=bind)
+        return C.csa2_index_segments(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
+                                     self.k, self.cand_keys, fmt=self.idx_qfmt, _bind=bind)
 
     def attend_topk(self, caches: Caches, layer: int, q_attn, q_seq, q_pos, replay_start, out=None, lse=None,
                     bind=False, new_win=None):

@@ -39,16 +39,26 @@
  *     16-byte boundary and kv_scales on an 8-byte one (CSA2_ERR_SHAPE otherwise); row
  *     sizes keep every row aligned.
  *
- * Layouts (row-major, contiguous):
- *   main-KV cache   kv_codes  [n_seq, seq_cap, D/2]  E2M1 pairs, channel 2i in the low
- *                                                     nibble of byte i
- *                   kv_scales [n_seq, seq_cap, D/16] E4M3, one per 16 channels
- *   indexer-K cache k_codes   [n_seq, seq_cap, d/2]  E2M1 pairs
- *                   k_scales  [n_seq, seq_cap, d/32] E8M0, one per 32 channels
- *   indexer Q       q_codes   [n_q, H_I, d/2], q_scales [n_q, H_I, d/32] (MXFP4)
- *   SWA cache       swa       [n_seq, swa_cap, D]    E4M3; the row of token p of sequence
- *                                                     b is (p - swa_base[b]) mod swa_cap
- *   index sets      idx       [n_q, k] int32 positions, ascending, -1 padded
+ * Cache layouts.  Every cache is addressed through its base pointers and byte strides, so
+ * the codes and scales of a cache may be separate arrays or one interleaved record (the main
+ * KV's 288-byte entry: scales = codes + 256, both entry strides 288):
+ *   entry e of sequence b   codes  + b*codes_seq_stride  + e*codes_stride
+ *                           scales + b*scales_seq_stride + e*scales_stride
+ * A stride of 0 means dense: an entry stride of the row's own size and a sequence stride of
+ * seq_cap entries.  Entry strides are at least the row size; code strides are multiples of
+ * 16, main-KV scale strides multiples of 4 and NVFP4 indexer scale strides multiples of 2
+ * (CSA2_ERR_SHAPE otherwise).  Distinct (sequence, entry) pairs must address disjoint bytes.
+ *   main-KV cache   codes  D/2 bytes per entry: E2M1 pairs, channel 2i in the low nibble
+ *                          of byte i
+ *                   scales D/16 bytes per entry: E4M3, one per 16 channels
+ *   indexer-K cache codes  d/2 bytes per entry: E2M1 pairs
+ *                   scales d/32 bytes per entry (MXFP4: E8M0 per 32 channels) or d/16
+ *                          (CSA2_FMT_NVFP4: E4M3 per 16 channels)
+ *   indexer Q       q_codes [n_q, H_I, d/2], q_scales [n_q, H_I, d/32 or d/16] (dense)
+ *   SWA cache       row r of sequence b: D bytes of E4M3 at swa + b*swa_seq_stride +
+ *                   r*swa_row_stride (0: dense, D and swa_cap*D); token p of sequence b sits
+ *                   in row (p - swa_base[b]) mod swa_cap
+ *   index sets      idx [n_q, k] int32 positions, ascending, -1 padded
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -141,16 +151,19 @@ const char* csa2_last_error(void);
  *              Nearest = round to nearest, ties to the even code (bit-exact).
  *   dst_row    [rows] int64 destination row of each source row (NULL: row r -> r);
  *              rows whose destination is outside [0, dst_rows) are skipped
- *   codes      [dst_rows, dim/2] (FP4) or [dst_rows, dim] (FP8) bytes
- *   scales     [dst_rows, dim/16] (NVFP4) or [dst_rows, dim/32] (MXFP4); unused for FP8
+ *   codes      destination row d at codes + d*codes_stride: dim/2 bytes (FP4) or dim (FP8);
+ *              codes_stride 0 = dense (dim/2 or dim), else >= that and a multiple of 16
+ *   scales     destination row d at scales + d*scales_stride: dim/16 bytes (NVFP4) or dim/32
+ *              (MXFP4); scales_stride 0 = dense; unused for FP8
+ *              (an interleaved main-KV record: codes = rec, scales = rec + 256, both strides 288)
  * Errors: NULL src/codes (or scales for FP4) -> CSA2_ERR_NULL; rows < 0, dim <= 0, dim not
- * a multiple of the group (16 / 32 / 8 for FP8) or dim > 8192 -> CSA2_ERR_SHAPE; unknown
- * fmt or src_dtype -> CSA2_ERR_UNSUPPORTED.  rows == 0 launches nothing (src, codes and
- * scales may then be NULL).
+ * a multiple of the group (16 / 32 / 8 for FP8), dim > 8192, or a stride below the row size
+ * or (codes) not a multiple of 16 -> CSA2_ERR_SHAPE; unknown fmt or src_dtype ->
+ * CSA2_ERR_UNSUPPORTED.  rows == 0 launches nothing (src, codes and scales may then be NULL).
  */
 int csa2_quantize_kv(const void* src, int src_dtype, int64_t rows, int dim, int fmt,
-                     const int64_t* dst_row, int64_t dst_rows, uint8_t* codes, uint8_t* scales,
-                     void* stream);
+                     const int64_t* dst_row, int64_t dst_rows, uint8_t* codes, int64_t codes_stride,
+                     uint8_t* scales, int64_t scales_stride, void* stream);
 
 /*
  * csa2_quantize_kv_multi -- several csa2_quantize_kv jobs in one launch (a decode step's
@@ -170,7 +183,9 @@ typedef struct {
   const int64_t* dst_row;
   int64_t dst_rows;
   uint8_t* codes;
+  int64_t codes_stride;
   uint8_t* scales;
+  int64_t scales_stride;
 } csa2_quant_job;
 int csa2_quantize_kv_multi(const csa2_quant_job* jobs, int n_jobs, void* stream);
 
@@ -178,15 +193,19 @@ int csa2_quantize_kv_multi(const csa2_quant_job* jobs, int n_jobs, void* stream)
  * csa2_index_score -- indexer scores of each query over its sequence's entries.
  * [W] "CSA2：跨层复用，能借就不自己算" (a lightweight indexer scores the global main KV with
  * indexer Q/K), "分层稀疏索引器" (later layers score only inside the pool);
- * [W] "FP4 与 SWA Bounded Replay" (indexer Q/K in FP4).
+ * [W] "FP4 与 SWA Bounded Replay" (indexer Q/K in FP4; the page does not fix the indexer's
+ * scale format, so both readings are served).
  *
  *   score(q, j) = sum_h w[q,h] * max(0, sum_c Q[q,h,c] K[seq(q), j, c])
- * with Q and K the exact MXFP4 values; products are exact, sums are fp32.
+ * with Q and K the exact FP4 values; products are exact, sums are fp32.
  *
- *   q_codes/q_scales  [n_q, n_heads, dim/2] / [n_q, n_heads, dim/32], MXFP4
+ *   fmt               the indexer format of Q and K: CSA2_FMT_MXFP4 (E8M0 per 32 channels,
+ *                     the scaled FP4 matrix-core path) or CSA2_FMT_NVFP4 (E4M3 per 16
+ *                     channels, as the main KV; dequantised exactly to fp16 matrix cores)
+ *   q_codes/q_scales  [n_q, n_heads, dim/2] / [n_q, n_heads, dim/32 (MXFP4) or dim/16]
  *   w                 [n_q, n_heads] f32
  *   n_heads           1..16;  dim == 128
- *   k_codes/k_scales  indexer-K cache, [n_seq, seq_cap, dim/2] / [.., dim/32]
+ *   k_codes, k_scales and their strides   the indexer-K cache (see Cache layouts)
  *   q_seq             [n_q] int32 sequence of each query (queries with q_seq outside
  *                     [0, n_seq) get no scores)
  *   n_vis             [n_q] int64 visible entries of each query (clamped to seq_cap)
@@ -204,10 +223,12 @@ int csa2_quantize_kv_multi(const csa2_quant_job* jobs, int n_jobs, void* stream)
  * seq_cap or max_cand_blocks*block).
  */
 int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                     int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                     int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                     const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
-                     int max_cand_blocks, float* scores, int64_t scores_stride, void* stream);
+                     int n_heads, int dim, int fmt, const uint8_t* k_codes, int64_t k_codes_stride,
+                     int64_t k_codes_seq_stride, const uint8_t* k_scales, int64_t k_scales_stride,
+                     int64_t k_scales_seq_stride, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                     const int64_t* n_vis, const int32_t* cand_blocks, const int32_t* n_cand_blocks,
+                     int block, int max_cand_blocks, float* scores, int64_t scores_stride,
+                     void* stream);
 
 /*
  * csa2_index_score_q -- csa2_index_score with the indexer Q given unquantised: every
@@ -220,11 +241,13 @@ int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales, const floa
  *            16-byte aligned, finite; read only
  *   others   as csa2_index_score
  * The scores equal those of csa2_quantize_kv (CSA2_FMT_MXFP4) followed by
- * csa2_index_score on its codes.  Errors: as csa2_index_score; CSA2_ERR_UNSUPPORTED for
- * another q_dtype.
+ * csa2_index_score on its codes.  fmt must be CSA2_FMT_MXFP4.  Errors: as csa2_index_score;
+ * CSA2_ERR_UNSUPPORTED for another q_dtype or fmt.
  */
 int csa2_index_score_q(const void* q, int q_dtype, const float* w, int n_q, int n_heads, int dim,
-                       const uint8_t* k_codes, const uint8_t* k_scales, int64_t seq_cap, int n_seq,
+                       int fmt, const uint8_t* k_codes, int64_t k_codes_stride,
+                       int64_t k_codes_seq_stride, const uint8_t* k_scales, int64_t k_scales_stride,
+                       int64_t k_scales_seq_stride, int64_t seq_cap, int n_seq,
                        const int32_t* q_seq, const int64_t* n_vis, const int32_t* cand_blocks,
                        const int32_t* n_cand_blocks, int block, int max_cand_blocks, float* scores,
                        int64_t scores_stride, void* stream);
@@ -242,12 +265,16 @@ int csa2_index_score_q(const void* q, int q_dtype, const float* w, int n_q, int 
  * Every row's scores are written exactly as csa2_index_score writes them (bit-identical:
  * the same arithmetic per row and entry); positions past a row's n_vis are not written.  A
  * row whose q_seq differs from its group's first row, or lies outside [0, n_seq), gets no
- * scores.  Errors: those of csa2_index_score, CSA2_ERR_SHAPE for group out of range.
+ * scores.  fmt must be CSA2_FMT_MXFP4.  Errors: those of csa2_index_score, CSA2_ERR_SHAPE for
+ * group out of range, CSA2_ERR_UNSUPPORTED for another fmt.
  */
-int csa2_index_score_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                             int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                             int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                             int group, float* scores, int64_t scores_stride, void* stream);
+int csa2_index_score_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                             int n_q, int n_heads, int dim, int fmt, const uint8_t* k_codes,
+                             int64_t k_codes_stride, int64_t k_codes_seq_stride,
+                             const uint8_t* k_scales, int64_t k_scales_stride,
+                             int64_t k_scales_seq_stride, int64_t seq_cap, int n_seq,
+                             const int32_t* q_seq, const int64_t* n_vis, int group, float* scores,
+                             int64_t scores_stride, void* stream);
 
 /*
  * csa2_index_topk_grouped -- csa2_index_score_grouped followed by csa2_topk, without the
@@ -266,14 +293,18 @@ int csa2_index_score_grouped(const uint8_t* q_codes, const uint8_t* q_scales, co
  *   k in 1..CSA2_MAX_GROUPED_TOPK; n_q <= 65535 * group.
  *   Workspace: csa2_index_topk_grouped_workspace_bytes(n_q, seq_cap, k, group) bytes (each
  *   row's best k of every range of its entries: at most 8,192 keys per row).
- * Errors: those of csa2_index_score_grouped; CSA2_ERR_NULL (idx_out, count_out);
+ * fmt must be CSA2_FMT_MXFP4.  Errors: those of csa2_index_score_grouped; CSA2_ERR_NULL
+ * (idx_out, count_out);
  * CSA2_ERR_SHAPE (k, n_q); CSA2_ERR_WORKSPACE.
  */
 #define CSA2_MAX_GROUPED_TOPK 704
-int csa2_index_topk_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                            int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                            int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis, int group,
-                            int k, int32_t* idx_out, int32_t* count_out, void* workspace,
+int csa2_index_topk_grouped(const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                            int n_q, int n_heads, int dim, int fmt, const uint8_t* k_codes,
+                            int64_t k_codes_stride, int64_t k_codes_seq_stride,
+                            const uint8_t* k_scales, int64_t k_scales_stride,
+                            int64_t k_scales_seq_stride, int64_t seq_cap, int n_seq,
+                            const int32_t* q_seq, const int64_t* n_vis, int group, int k,
+                            int32_t* idx_out, int32_t* count_out, void* workspace,
                             size_t workspace_bytes, void* stream);
 size_t csa2_index_topk_grouped_workspace_bytes(int n_q, int64_t seq_cap, int k, int group);
 
@@ -297,10 +328,11 @@ size_t csa2_index_topk_grouped_workspace_bytes(int n_q, int64_t seq_cap, int k, 
  * count_out), CSA2_ERR_SHAPE (k, n_q), CSA2_ERR_WORKSPACE.
  */
 int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                    int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                    int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                    const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
-                    int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
+                    int n_heads, int dim, int fmt, const uint8_t* k_codes, int64_t k_codes_stride,
+                    int64_t k_codes_seq_stride, const uint8_t* k_scales, int64_t k_scales_stride,
+                    int64_t k_scales_seq_stride, int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                    const int64_t* n_vis, const int32_t* cand_blocks, const int32_t* n_cand_blocks,
+                    int block, int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
                     void* workspace, size_t workspace_bytes, void* stream);
 size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_pool);
 
@@ -321,44 +353,12 @@ size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_p
  * CSA2_ERR_SHAPE (k, n_q).
  */
 int csa2_index_segments(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                        int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                        int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                        int k, uint64_t* cand_keys, void* stream);
+                        int n_heads, int dim, int fmt, const uint8_t* k_codes,
+                        int64_t k_codes_stride, int64_t k_codes_seq_stride, const uint8_t* k_scales,
+                        int64_t k_scales_stride, int64_t k_scales_seq_stride, int64_t seq_cap,
+                        int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k,
+                        uint64_t* cand_keys, void* stream);
 int64_t csa2_segment_keys(int64_t n_slots, int k);
-
-/*
- * csa2_index_score_nvfp4 / csa2_index_topk_nvfp4 / csa2_index_segments_nvfp4 --
- * csa2_index_score / csa2_index_topk / csa2_index_segments for
- * an indexer kept in the main KV's NVFP4-style format instead of MXFP4: E2M1 codes with one
- * E4M3 scale per 16 channels, as CSA2_FMT_NVFP4 of csa2_quantize_kv writes them.
- * [W] "FP4 与 SWA Bounded Replay" (indexer Q/K in FP4, main KV in E2M1 + E4M3 per 16; the
- * page does not fix the indexer's scale format, so both readings are served).
- *
- *   score(q, j) = sum_h w[q,h] * max(0, sum_c Q[q,h,c] K[seq(q), j, c])
- * with Q and K the exact NVFP4 values; products are exact, sums are fp32.
- *
- * Arguments, layouts, outputs, workspace and errors are those of csa2_index_score,
- * csa2_index_topk and csa2_index_segments, except:
- *   q_scales   [n_q, n_heads, dim/16] E4M3 (8 per head row)
- *   k_scales   [n_seq, seq_cap, dim/16] E4M3 (8 per entry); both scale arrays 2-byte
- *              aligned (CSA2_ERR_SHAPE otherwise)
- * A cache entry is 72 bytes (64 code + 8 scale bytes) against MXFP4's 68.
- */
-int csa2_index_score_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                           int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                           int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                           const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
-                           int max_cand_blocks, float* scores, int64_t scores_stride, void* stream);
-int csa2_index_topk_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                          int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                          int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                          const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
-                          int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
-                          void* workspace, size_t workspace_bytes, void* stream);
-int csa2_index_segments_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                              int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                              int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
-                              int k, uint64_t* cand_keys, void* stream);
 
 /*
  * csa2_index_topk_pool -- the decoder's first Full layer in one pass over the indexer-K
@@ -374,15 +374,20 @@ int csa2_index_segments_nvfp4(const uint8_t* q_codes, const uint8_t* q_scales, c
  * Top-K survivors.  A query whose q_seq is outside [0, n_seq) gets count 0 and a pool of
  * its lowest visible block ids (all their scores are -inf).
  *   Workspace: csa2_index_topk_pool_workspace_bytes(n_q, seq_cap, k, block, max_blocks).
- * Errors: as csa2_index_topk; CSA2_ERR_SHAPE for block or max_blocks out of range.
+ * fmt must be CSA2_FMT_MXFP4.  Errors: as csa2_index_topk; CSA2_ERR_SHAPE for block or
+ * max_blocks out of range; CSA2_ERR_UNSUPPORTED for another fmt.
  */
 int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
-                         int n_heads, int dim, const uint8_t* k_codes, const uint8_t* k_scales,
-                         int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k,
-                         int32_t* idx_out, int32_t* count_out, int block, int max_blocks,
-                         int32_t* blocks_out, int32_t* blocks_count, void* workspace,
-                         size_t workspace_bytes, void* stream);
-size_t csa2_index_topk_pool_workspace_bytes(int n_q, int64_t n_slots, int k, int block, int max_blocks);
+                         int n_heads, int dim, int fmt, const uint8_t* k_codes,
+                         int64_t k_codes_stride, int64_t k_codes_seq_stride,
+                         const uint8_t* k_scales, int64_t k_scales_stride,
+                         int64_t k_scales_seq_stride, int64_t seq_cap, int n_seq,
+                         const int32_t* q_seq, const int64_t* n_vis, int k, int32_t* idx_out,
+                         int32_t* count_out, int block, int max_blocks, int32_t* blocks_out,
+                         int32_t* blocks_count, void* workspace, size_t workspace_bytes,
+                         void* stream);
+size_t csa2_index_topk_pool_workspace_bytes(int n_q, int64_t n_slots, int k, int block,
+                                            int max_blocks);
 
 /*
  * csa2_topk -- the k highest-scoring candidates of each query.
@@ -441,12 +446,13 @@ size_t csa2_pool_workspace_bytes(int n_q, int64_t max_vis, int block, int max_bl
  * A query with no key (only possible when s > t) gets out = 0 and lse = -inf.
  *
  *   q         [n_q, n_heads, dim] bf16;  n_heads a multiple of 16 (<= 256); dim == 512
- *   kv_codes/kv_scales  main-KV cache (NVFP4), [n_seq, seq_cap, ...]
+ *   kv_codes, kv_scales and their strides   the main-KV cache (NVFP4; see Cache layouts)
  *   q_seq     [n_q] int32 (queries with q_seq outside [0, n_seq) get out = 0, lse = -inf)
  *   idx       [n_q, k] int32 positions, any order, -1 (or any value outside
  *             [0, seq_cap)) = empty;  k in 0..2048
- *   swa       [n_seq, swa_cap, dim] E4M3; swa_base [n_seq] int64; window in 1..1024 and
- *             window <= swa_cap <= CSA2_MAX_WINDOW_ROWS; seq_cap <= CSA2_MAX_ATTN_ENTRIES
+ *   swa, swa_row_stride, swa_seq_stride   the window ring (E4M3 rows of dim bytes; see Cache
+ *             layouts); swa_base [n_seq] int64; window in 1..1024 and window <= swa_cap <=
+ *             CSA2_MAX_WINDOW_ROWS; seq_cap <= CSA2_MAX_ATTN_ENTRIES
  *   new_win   NULL, or [n_q, dim] f32 / bf16 (new_win_dtype): the post-RoPE window latent of
  *             each row's own token t = q_pos[q].  The call appends it first: quantised to
  *             E4M3 exactly as csa2_quantize_kv with CSA2_FMT_FP8 writes it, stored at ring
@@ -467,11 +473,14 @@ size_t csa2_pool_workspace_bytes(int n_q, int64_t max_vis, int block, int max_bl
  * CSA2_ERR_WORKSPACE.
  */
 int csa2_sparse_attn(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
-                     const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
-                     const int32_t* idx, int k, uint8_t* swa, int64_t swa_cap,
+                     int64_t kv_codes_stride, int64_t kv_codes_seq_stride, const uint8_t* kv_scales,
+                     int64_t kv_scales_stride, int64_t kv_scales_seq_stride, int64_t seq_cap,
+                     int n_seq, const int32_t* q_seq, const int32_t* idx, int k, uint8_t* swa,
+                     int64_t swa_row_stride, int64_t swa_seq_stride, int64_t swa_cap,
                      const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
                      const void* new_win, int new_win_dtype, int window, float sm_scale, void* out,
-                     int out_dtype, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+                     int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream);
 size_t csa2_attn_workspace_bytes(int n_q, int n_heads, int dim, int k, int window);
 
 /*
@@ -492,11 +501,15 @@ size_t csa2_attn_workspace_bytes(int n_q, int n_heads, int dim, int k, int windo
  * shape within 16 MiB); CSA2_ERR_HIP if the array's address cannot be had.
  */
 int csa2_sparse_attn_noalloc(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
-                             const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
-                             const int32_t* idx, int k, uint8_t* swa, int64_t swa_cap,
-                             const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
-                             const void* new_win, int new_win_dtype, int window, float sm_scale, void* out,
-                             int out_dtype, float* lse, void* stream);
+                             int64_t kv_codes_stride, int64_t kv_codes_seq_stride,
+                             const uint8_t* kv_scales, int64_t kv_scales_stride,
+                             int64_t kv_scales_seq_stride, int64_t seq_cap, int n_seq,
+                             const int32_t* q_seq, const int32_t* idx, int k, uint8_t* swa,
+                             int64_t swa_row_stride, int64_t swa_seq_stride, int64_t swa_cap,
+                             const int64_t* swa_base, const int64_t* q_pos,
+                             const int64_t* replay_start, const void* new_win, int new_win_dtype,
+                             int window, float sm_scale, void* out, int out_dtype, float* lse,
+                             void* stream);
 size_t csa2_sparse_attn_noalloc_max_bytes(void);
 
 /*
@@ -518,13 +531,16 @@ size_t csa2_sparse_attn_noalloc_max_bytes(void);
  * CSA2_ERR_SHAPE (cand_per_q, k).
  */
 int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
-                          const uint8_t* kv_scales, int64_t seq_cap, int n_seq, const int32_t* q_seq,
-                          const uint64_t* cand_keys, int cand_per_q, int k, int32_t* idx_out,
-                          int32_t* count_out, uint8_t* swa, int64_t swa_cap,
-                          const int64_t* swa_base, const int64_t* q_pos, const int64_t* replay_start,
-                          const void* new_win, int new_win_dtype, int window, float sm_scale,
-                          void* out, int out_dtype, float* lse, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          int64_t kv_codes_stride, int64_t kv_codes_seq_stride,
+                          const uint8_t* kv_scales, int64_t kv_scales_stride,
+                          int64_t kv_scales_seq_stride, int64_t seq_cap, int n_seq,
+                          const int32_t* q_seq, const uint64_t* cand_keys, int cand_per_q, int k,
+                          int32_t* idx_out, int32_t* count_out, uint8_t* swa,
+                          int64_t swa_row_stride, int64_t swa_seq_stride, int64_t swa_cap,
+                          const int64_t* swa_base, const int64_t* q_pos,
+                          const int64_t* replay_start, const void* new_win, int new_win_dtype,
+                          int window, float sm_scale, void* out, int out_dtype, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * csa2_sparse_attn_pool_topk -- csa2_sparse_attn for a Reindex layer inside the pool, with
@@ -545,13 +561,16 @@ int csa2_sparse_attn_topk(const void* q, int n_q, int n_heads, int dim, const ui
  * Errors: those of csa2_sparse_attn; CSA2_ERR_NULL (scores, n_vis, cand_blocks,
  * n_cand_blocks, idx_out, count_out); CSA2_ERR_SHAPE (block, max_cand_blocks, k, stride).
  */
-int csa2_sparse_attn_pool_topk(const void* q, int n_q, int n_heads, int dim, const uint8_t* kv_codes,
-                               const uint8_t* kv_scales, int64_t seq_cap, int n_seq,
-                               const int32_t* q_seq, const float* scores, int64_t scores_stride,
-                               const int64_t* n_vis, const int32_t* cand_blocks,
-                               const int32_t* n_cand_blocks, int block, int max_cand_blocks, int k,
-                               int32_t* idx_out, int32_t* count_out, uint8_t* swa, int64_t swa_cap,
-                               const int64_t* swa_base, const int64_t* q_pos,
+int csa2_sparse_attn_pool_topk(const void* q, int n_q, int n_heads, int dim,
+                               const uint8_t* kv_codes, int64_t kv_codes_stride,
+                               int64_t kv_codes_seq_stride, const uint8_t* kv_scales,
+                               int64_t kv_scales_stride, int64_t kv_scales_seq_stride,
+                               int64_t seq_cap, int n_seq, const int32_t* q_seq,
+                               const float* scores, int64_t scores_stride, const int64_t* n_vis,
+                               const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
+                               int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
+                               uint8_t* swa, int64_t swa_row_stride, int64_t swa_seq_stride,
+                               int64_t swa_cap, const int64_t* swa_base, const int64_t* q_pos,
                                const int64_t* replay_start, const void* new_win, int new_win_dtype,
                                int window, float sm_scale, void* out, int out_dtype, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);

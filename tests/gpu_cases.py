@@ -43,10 +43,11 @@ def swa_ring_latents(wl: Workload, layer: int, seq: int) -> np.ndarray:
 class Case:
     """A workload's inputs on both sides."""
 
-    def __init__(self, wl: Workload, swa_layers=(0,), index_fmt: str = "mxfp4"):
+    def __init__(self, wl: Workload, swa_layers=(0,), index_fmt: str = "mxfp4", interleaved: bool = False):
         self.wl = wl
         self.swa_layers = tuple(swa_layers)
         self.index_fmt = index_fmt
+        self.interleaved = interleaved   # main KV as one 288-byte record per entry
 
     # ---------- HIP side ----------
     def gpu_caches(self, window_empty: bool = False):
@@ -55,7 +56,8 @@ class Case:
         write them)."""
         from fp4_kv_cache_layer_amd.layer import Caches
         wl, C_ = self.wl, C()
-        caches = Caches.empty(wl.n_seq, wl.seq_cap, self.swa_layers, wl.swa_cap, index_fmt=self.index_fmt)
+        caches = Caches.empty(wl.n_seq, wl.seq_cap, self.swa_layers, wl.swa_cap, index_fmt=self.index_fmt,
+                              interleaved=self.interleaved)
         ik_fmt = C_.FMT_NVFP4 if self.index_fmt == "nvfp4" else C_.FMT_MXFP4
         caches.swa_base.fill_(wl.swa_base)
         for b in range(wl.n_seq):

@@ -408,9 +408,8 @@ def _run_index_topk(C, st, caches, w, q_seq, n_vis, k, in_pool=False):
     idx_f = torch.full((st.n_q, k), 77, dtype=torch.int32, device="cuda")
     cnt_f = torch.full((st.n_q,), 77, dtype=torch.int32, device="cuda")
     pool = (st.pool, st.pool_count) if in_pool else (None, None)
-    fn = C.csa2_index_topk_nvfp4 if st.index_fmt == "nvfp4" else C.csa2_index_topk
-    fn(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, k, idx_f, cnt_f, None, pool[0],
-       pool[1], 8)
+    C.csa2_index_topk(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis, k, idx_f, cnt_f,
+                      None, pool[0], pool[1], 8, fmt=st.idx_qfmt)
     idx_u = torch.empty(st.n_q, k, dtype=torch.int32, device="cuda")
     cnt_u = torch.empty(st.n_q, dtype=torch.int32, device="cuda")
     st.score(caches, w, q_seq, n_vis, in_pool)
@@ -469,10 +468,10 @@ def test_segments_then_attention_topk(C, k, fmt):
     lse_a = torch.empty(wl.n_q, 16, dtype=torch.float32, device="cuda")
     C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, torch.from_numpy(gi).cuda(), caches.swa[0],
                        caches.swa_base, q_pos, rs, 128, sm, out_a, lse_a)
-    seg_fn = C.csa2_index_segments_nvfp4 if fmt == "nvfp4" else C.csa2_index_segments
     for rep in range(2):
         keys = torch.full((wl.n_q, C.csa2_segment_keys(wl.seq_cap, k)), 5, dtype=torch.int64, device="cuda")
-        seg_fn(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis_t, k, keys)
+        C.csa2_index_segments(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis_t, k,
+                              keys, fmt=st.idx_qfmt)
         idx_b = torch.full((wl.n_q, k), 77, dtype=torch.int32, device="cuda")
         cnt_b = torch.full((wl.n_q,), 77, dtype=torch.int32, device="cuda")
         out_b = torch.empty_like(out_a)

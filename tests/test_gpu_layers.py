@@ -30,27 +30,34 @@ ALL = None   # every query row of the workload
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,samples,fused,attn_select", [
-    ("c2", (0, 63), True, False), ("c2", ALL, True, True), ("c3", (0, 13, 31), True, False),
-    ("c3", (0, 13, 31), False, False), ("c3", ALL, True, True), ("c4", (0, 5), True, False),
-    ("c4", (0, 5), False, False), ("c4", ALL, True, True)])
-def test_layer_group_full_size(C, name, samples, fused, attn_select):
+@pytest.mark.parametrize("name,samples,fused,attn_select,interleaved", [
+    ("c2", (0, 63), True, False, False), ("c2", ALL, True, True, False), ("c3", (0, 13, 31), True, False, False),
+    ("c3", (0, 13, 31), False, False, False), ("c3", ALL, True, True, False), ("c4", (0, 5), True, False, False),
+    ("c4", (0, 5), False, False, False), ("c4", ALL, True, True, False),
+    ("c2", ALL, True, True, True), ("c3", ALL, True, True, True), ("c4", (0, 3, 7), True, True, True)])
+def test_layer_group_full_size(C, name, samples, fused, attn_select, interleaved):
     """Every layer of a group at full size against the oracle: fused scoring + selection,
     two calls, and the last Top-K level inside the attention call.  The cases with the
     selection inside attention run as the single-token decode step is benchmarked (each
     row's own window entry appended by the attention call, its ring row zeroed beforehand)
     and are checked on every query row: index set and pool by the acceptance rule, cache
     bytes, and attention.  The other variants attend over a prefilled ring and are checked
-    on sampled rows."""
-    _say("layer group", name, "fused" if fused else "two-call", "select in attention" if attn_select else "")
+    on sampled rows.  interleaved: the main KV as one 288-byte record per entry (codes, then
+    scales; both strides 288), written by the quantiser and read by every attention call
+    through the strides of the boundary."""
+    _say("layer group", name, "fused" if fused else "two-call", "select in attention" if attn_select else "",
+         "interleaved main KV" if interleaved else "")
     from fp4_kv_cache_layer_amd.layer import Csa2Step
     wl = workloads.config(name)
-    case = G.Case(wl, swa_layers=range(len(wl.layers)))
+    case = G.Case(wl, swa_layers=range(len(wl.layers)), interleaved=interleaved)
     caches = case.gpu_caches()
     step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, fused=fused, attn_select=attn_select)
     # at 1M the segment survivors exceed one selection, so only the pool's Top-K (Reindex
     # inside the pool) moves into the attention call
     assert (step.attn_select or step.pool_select) == attn_select
+    if interleaved:
+        assert caches.kv_codes.stride(1) == 288 and caches.kv_scales.stride(1) == 288
+        assert caches.kv_scales.data_ptr() == caches.kv_codes.data_ptr() + 256
     snaps = G.run_group_snapshots(case, step, caches, fused_window=attn_select)
     rows = range(wl.n_q) if samples is ALL else samples
     _say("  oracle rows", len(rows))
