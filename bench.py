@@ -117,6 +117,7 @@ class LayerBench:
         self.plan = plan_group(wl.layers, fused=fused, group=group, index_fmt=index_fmt,
                                attn_select=self.step.attn_select, pool_select=self.step.pool_select,
                                group_select=self.step.group_select)
+        torch.cuda.synchronize()   # the setup's copies and launches end here
 
     def calls(self, L: int):
         """Layer L's step as {phase: bound call} bound to the current stream, in order."""
@@ -312,6 +313,12 @@ def cpu_baseline(wl, n_sample: int, reps: int):
         threads = max(blas) if blas else 1
     except Exception:
         threads = 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), model)
+    except OSError:
+        pass
     sm = 1.0 / math.sqrt(512)
     prepared = []
     for qi in range(n_sample):
@@ -342,6 +349,7 @@ def cpu_baseline(wl, n_sample: int, reps: int):
                          n_vis=nv, sm_scale=sm)
     el = time.perf_counter() - t0
     return {"value": n_sample * reps / el, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{n_sample} of {wl.n_q} queries (their own {wl.seq_cap}-entry sequences), each Full layer "
                       f"step (dequantise indexer-K cache, score, Top-512, dequantise 512+window rows, attention) "
                       f"run {reps}x; {el:.1f}s; numpy fp64, BLAS threads = cores"}
@@ -355,7 +363,15 @@ def measure_layers(name, steps, warmup, torch, C, layers_to_time, group: int = 1
     from synth import workloads
     wl = workloads.config(name)
     log(f"workload {name}: {wl.description}")
-    lb = LayerBench(wl, torch, C, group, index_fmt, attn_select, fused)
+    label = f"workload {name}" + (f" group {group}" if group > 1 else "") + \
+        (f" index {index_fmt}" if index_fmt != "mxfp4" else "") + ("" if attn_select else " last level kernel")
+    with torch.cuda.nvtx.range(label):
+        return _measure_layers(wl, steps, warmup, torch, C, layers_to_time, group, index_fmt, attn_select, fused)
+
+
+def _measure_layers(wl, steps, warmup, torch, C, layers_to_time, group, index_fmt, attn_select, fused):
+    with torch.cuda.nvtx.range("setup"):
+        lb = LayerBench(wl, torch, C, group, index_fmt, attn_select, fused)
     res = {"wl": wl, "layers": {}}
     G = steps_per_graph(steps)
     res["per_graph"] = G
@@ -390,12 +406,14 @@ def measure_group(name, steps, warmup, torch, C, group: int = 1):
     from synth import workloads
     wl = workloads.config(name)
     log(f"workload {name}: {wl.description}")
-    lb = LayerBench(wl, torch, C, group)
-    g = lb.capture(list(range(len(wl.layers))))
-    ms, _ = time_graph(g, steps, warmup, torch)
-    del g, lb
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    with torch.cuda.nvtx.range(f"workload {name}"):
+        with torch.cuda.nvtx.range("setup"):
+            lb = LayerBench(wl, torch, C, group)
+        g = lb.capture(list(range(len(wl.layers))))
+        ms, _ = time_graph(g, steps, warmup, torch)
+        del g, lb
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     return wl, ms
 
 
@@ -439,9 +457,10 @@ def measured_traffic():
     return int(vals["traffic_bytes"].strip())
 
 
-def pmc_run(torch, C):
+def pmc_run(torch, C, name="c2"):
     """Workload of the counter runs: one plain 1 GiB device copy (the calibration of
-    FETCH_SIZE / WRITE_SIZE), then each call of the 64 x 128K Full step three times."""
+    FETCH_SIZE / WRITE_SIZE), then each call of the workload's Full layer three times (the
+    64 x 128K decode step, or the m = 2 prefill chunk scored in groups of 8 rows)."""
     from synth import workloads
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
@@ -449,7 +468,7 @@ def pmc_run(torch, C):
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    lb = LayerBench(workloads.config("c2"), torch, C)
+    lb = LayerBench(workloads.config(name), torch, C, group=PREFILL_GROUP if name == "c5" else 1)
     for name, fn in lb.calls(0).items():
         for _ in range(3):
             fn()
@@ -463,6 +482,151 @@ def mode_entry(wl, mode, ms):
             "hbm_frac": round(b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": b}
 
 
+MFMA_FP4_PEAK_TFLOPS = 10100.0   # dense FP4 matrix-core peak
+
+
+def score_flops(wl) -> int:
+    """Algorithmic FLOPs of one scoring pass over every visible entry: a 128-channel dot
+    product per indexer head (2 FLOP per multiply-add) for each query row and entry."""
+    return int(wl.n_vis.astype(np.int64).sum()) * wl.idx_heads * 128 * 2
+
+
+def mfma_entry(flops, ms, peak) -> dict:
+    tf = flops / (ms / 1e3) / 1e12
+    return {"us": round(ms * 1e3, 1), "flops": int(flops), "tflops": round(tf, 1), "mfma_peak_tflops": peak,
+            "mfma_frac": round(tf / peak, 4)}
+
+
+def run_group_128k(args, torch, C):
+    r3 = measure_layers("c3", args.steps, args.warmup, torch, C, [0, 1, 4])
+    out = {f"{v['mode']}_128k": mode_entry(r3["wl"], v["mode"], v["ms"]) for v in r3["layers"].values()}
+    n3 = len(r3["wl"].layers)
+    out["group_128k"] = {"layers": list(r3["wl"].layers), "us_per_group": round(r3["group_ms"] * 1e3, 2),
+                         "query_tokens_per_s_per_layer": round(r3["wl"].n_q * n3 / (r3["group_ms"] / 1e3), 1)}
+    return out
+
+
+def run_group_1m(args, torch, C):
+    r4 = measure_layers("c4", args.steps, args.warmup, torch, C, [0, 1])
+    out = {f"{v['mode']}_1m": mode_entry(r4["wl"], v["mode"], v["ms"]) for v in r4["layers"].values()}
+    n4 = len(r4["wl"].layers)
+    out["group_1m"] = {"layers": list(r4["wl"].layers), "us_per_group": round(r4["group_ms"] * 1e3, 2),
+                       "query_tokens_per_s_per_layer": round(r4["wl"].n_q * n4 / (r4["group_ms"] / 1e3), 1)}
+    return out
+
+
+def run_prefill_chunk(args, torch, C):
+    # the chunk's rows all belong to one sequence: scored and selected in groups of 8 over
+    # one pass of K
+    r5 = measure_layers("c5", max(args.steps // 5, 3), max(args.warmup // 5, 1), torch, C, [0], group=PREFILL_GROUP)
+    wl5, ms5, g5 = r5["wl"], r5["layers"][0]["ms"], r5["graph_call"]
+    rows = int(wl5.extra["counted_rows"])
+    return {"prefill_chunk_m2": {
+        "query_rows": wl5.n_q, "counted_new_tokens": rows, "scoring_group": PREFILL_GROUP,
+        "us_per_chunk": round(ms5 * 1e3, 1), "new_tokens_per_s": round(rows / (ms5 / 1e3), 1),
+        "graph_call_us": {k: round(v * 1e3, 1) for k, v in g5.items()},
+        "scoring": dict(kernel="k_score_topk_grouped (csa2_index_topk_grouped: FP4 scores and Top-512 of 8 rows "
+                               "per pass over the sequence's indexer K; no score array)",
+                        **mfma_entry(score_flops(wl5), g5["index_topk_grouped"], MFMA_FP4_PEAK_TFLOPS)),
+        "attention": dict(kernel="k_attn (csa2_sparse_attn, 512 entries + window per row)",
+                          **mfma_entry(attn_flops(wl5), g5["attn"], MFMA_F16_PEAK_TFLOPS)),
+        "isolated_launch_us": {k: round(v * 1000, 1) for k, v in r5["isolated"].items()}}}
+
+
+def run_encoder_group(args, torch, C):
+    re_ = measure_layers("enc_group", max(args.steps // 5, 3), max(args.warmup // 5, 1), torch, C, [0, 1],
+                         group=PREFILL_GROUP)
+    wle, mse, ge = re_["wl"], re_["group_ms"], re_["graph_call"]
+    rows = int(wle.extra["counted_rows"])
+    return {"encoder_group_prefill_m2": {
+        "layers": len(wle.layers), "structure": "Full + 5 Reuse, window state missed (replay rows rewrite it)",
+        "query_rows": wle.n_q, "counted_new_tokens": rows, "us_per_chunk": round(mse * 1e3, 1),
+        "us_per_layer": round(mse * 1e3 / len(wle.layers), 1), "new_tokens_per_s": round(rows / (mse / 1e3), 1),
+        "scoring_group": PREFILL_GROUP,
+        "us_full_layer": round(re_["layers"][0]["ms"] * 1e3, 1), "us_reuse_layer": round(re_["layers"][1]["ms"] * 1e3, 1),
+        "full_layer_graph_call_us": {k: round(v * 1e3, 1) for k, v in ge.items()},
+        "scoring": mfma_entry(score_flops(wle), ge["index_topk_grouped"], MFMA_FP4_PEAK_TFLOPS),
+        "attention": mfma_entry(attn_flops(wle), ge["attn"], MFMA_F16_PEAK_TFLOPS)}}
+
+
+def run_multi_token_decode(args, torch, C):
+    # 4 tokens of each of 16 sequences; the Full layer's scoring with each sequence's 4 rows
+    # in one pass over its K (group 4) and per row (group 1)
+    mt = {}
+    for g in (1, 4):
+        rm = measure_layers("mtd_128k", args.steps, args.warmup, torch, C, [0], group=g)
+        mt[g] = (rm["wl"], rm["layers"][0]["ms"], rm["isolated"])
+    wlm = mt[1][0]
+    return {"multi_token_decode_128k": {
+        "sequences": wlm.n_seq, "tokens_per_seq": int(wlm.extra["tokens_per_seq"]), "query_rows": wlm.n_q,
+        "us_per_layer_step": round(mt[1][1] * 1e3, 2), "query_tokens_per_s": round(wlm.n_q / (mt[1][1] / 1e3), 1),
+        "us_per_layer_step_grouped_scoring": round(mt[4][1] * 1e3, 2),
+        "isolated_launch_us": {k: round(v * 1e3, 1) for k, v in mt[1][2].items()},
+        "isolated_launch_us_grouped": {k: round(v * 1e3, 1) for k, v in mt[4][2].items()}}}
+
+
+def run_last_level_kernel(args, torch, C):
+    # the headline step with the last Top-K level as a launch of its own
+    rs_ = measure_layers("c2", args.steps, args.warmup, torch, C, [0], attn_select=False)
+    g_ = rs_["graph_call"]
+    return {"full_128k_last_level_kernel": {
+        "calls": "csa2_index_topk (k_score_select + the last Top-K level), then csa2_sparse_attn",
+        "us_per_layer_step": round(rs_["layers"][0]["ms"] * 1e3, 2),
+        "query_tokens_per_s": round(rs_["wl"].n_q / (rs_["layers"][0]["ms"] / 1e3), 1),
+        "graph_call_us": {k: round(v * 1e3, 2) for k, v in g_.items()},
+        "index_topk_gb_per_s": round(score_bytes(rs_["wl"], "full") / (g_["index_topk"] / 1e3) / 1e9, 1)}}
+
+
+def run_nvfp4_indexer(args, torch, C):
+    rn = measure_layers("c2", args.steps, args.warmup, torch, C, [0], index_fmt="nvfp4")
+    wln, msn, isn, gcn = rn["wl"], rn["layers"][0]["ms"], rn["isolated"], rn["graph_call"]
+    bn = score_bytes(wln, "full", "nvfp4")
+    scn = "index_segments" if "index_segments" in gcn else "index_topk"
+    gbs = bn / (gcn[scn] / 1e3) / 1e9
+    return {"full_128k_nvfp4_indexer": {
+        "index_format": "E2M1 + E4M3 per 16 (72 B per indexer-K entry), fp16 MFMA scoring",
+        "us_per_layer_step": round(msn * 1e3, 2), "query_tokens_per_s": round(wln.n_q / (msn / 1e3), 1),
+        "scoring_call": f"csa2_{scn} (fmt CSA2_FMT_NVFP4)", "scoring_us": round(gcn[scn] * 1e3, 2),
+        "scoring_gb_per_s": round(gbs, 1), "scoring_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "scoring_bytes": bn,
+        "scoring_kernel_us": round(gcn["scoring_kernel"] * 1e3, 2) if "scoring_kernel" in gcn else None,
+        "isolated_launch_us": {k: round(v * 1e3, 2) for k, v in isn.items()}}}
+
+
+def run_decoders(args, torch, C):
+    out = {}
+    for name, key in (("dec_128k", "decoder_128k"), ("dec_1m", "decoder_1m")):
+        wld, msd = measure_group(name, args.steps, args.warmup, torch, C)
+        out[key] = decoder_entry(wld, msd)
+    return out
+
+
+# the reported modes, each measured in its own runner (`--only NAME` runs one, for profiling)
+MODE_RUNNERS = {"group_128k": run_group_128k, "group_1m": run_group_1m, "prefill_chunk": run_prefill_chunk,
+                "encoder_group": run_encoder_group, "multi_token_decode": run_multi_token_decode,
+                "last_level_kernel": run_last_level_kernel, "nvfp4_indexer": run_nvfp4_indexer,
+                "decoders": run_decoders}
+
+
+def device_copy_gbs(torch, reps: int = 10) -> dict:
+    """A plain 1 GiB device-to-device copy (torch's copy kernel), timed with HIP events:
+    the HBM rate an ordinary streaming kernel reaches on this GPU, beside the 8 TB/s spec."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * COPY_BYTES * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gb_per_s": round(gbs, 1), "bytes_per_copy": 2 * COPY_BYTES, "frac_of_spec": round(gbs / HBM_PEAK_GBS, 4),
+            "timing": f"HIP events around {reps} back-to-back 1 GiB copies (read + write counted)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -472,8 +636,11 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4)
     ap.add_argument("--cpu-reps", type=int, default=48)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--pmc-run", action="store_true",
-                    help="only run the workload of the FETCH_SIZE / WRITE_SIZE counter runs and exit")
+    ap.add_argument("--pmc-run", nargs="?", const="c2", choices=("c2", "c5"),
+                    help="only run the workload of a counter run and exit: the calibration copy and the "
+                         "64 x 128K Full step's calls (c2, the default), or the m = 2 prefill chunk's calls (c5)")
+    ap.add_argument("--only", choices=tuple(MODE_RUNNERS),
+                    help="only measure this mode (no headline line: for per-workload kernel traces)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the CSA2 step is built and measured on a single MI355X "
@@ -485,7 +652,11 @@ def main():
     C.csa2_init()
     torch.cuda.set_device(0)
     if args.pmc_run:
-        pmc_run(torch, C)
+        pmc_run(torch, C, args.pmc_run)
+        return
+    if args.only:
+        modes = MODE_RUNNERS[args.only](args, torch, C)
+        print(json.dumps({"only": args.only, "modes": modes}), flush=True)
         return
 
     head = measure_layers("c2", args.steps, args.warmup, torch, C, [0])
@@ -508,6 +679,9 @@ def main():
         ", ".join(f"{k}={v * 1000:.1f}" for k, v in gcall.items()))
     log(f"k_score_select {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak); attention "
         f"{at_tflops:.1f} TFLOP/s ({at_tflops / MFMA_F16_PEAK_TFLOPS:.2%} of fp16 MFMA peak), {at_gbs:.0f} GB/s")
+    with torch.cuda.nvtx.range("device copy"):
+        copy = device_copy_gbs(torch)
+    log(f"device copy {copy['gb_per_s']:.0f} GB/s")
     result = {
         "metric": "CSA2 decode query-tokens/s per layer at 128K & 1M ctx; % HBM peak",
         "value": round(value, 1),
@@ -534,6 +708,7 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": sb,
                      "traffic": measured_traffic(),
+                     "frac_of_measured_copy": round(achieved / copy["gb_per_s"], 4),
                      "timing": "HIP events around graph replays of 8 back-to-back csa2_index_segments calls"},
         "attention": {"kernel": "csa2_sparse_attn_topk (k_attn: the last Top-K level, then attention)",
                       "us": round(at_ms * 1e3, 2),
@@ -543,77 +718,12 @@ def main():
                       "hbm_frac": round(at_gbs / HBM_PEAK_GBS, 4),
                       "timing": "HIP events around graph replays of 8 back-to-back csa2_sparse_attn_topk calls "
                                 "(the selection of the last Top-K level included)"},
+        "device_copy": copy,
     }
     if not args.no_modes:
         modes = {}
-        r3 = measure_layers("c3", args.steps, args.warmup, torch, C, [0, 1, 4])
-        for L, v in r3["layers"].items():
-            modes[f"{v['mode']}_128k"] = mode_entry(r3["wl"], v["mode"], v["ms"])
-        n3 = len(r3["wl"].layers)
-        modes["group_128k"] = {"layers": list(r3["wl"].layers), "us_per_group": round(r3["group_ms"] * 1e3, 2),
-                               "query_tokens_per_s_per_layer": round(r3["wl"].n_q * n3 / (r3["group_ms"] / 1e3), 1)}
-        r4 = measure_layers("c4", args.steps, args.warmup, torch, C, [0, 1])
-        for L, v in r4["layers"].items():
-            modes[f"{v['mode']}_1m"] = mode_entry(r4["wl"], v["mode"], v["ms"])
-        n4 = len(r4["wl"].layers)
-        modes["group_1m"] = {"layers": list(r4["wl"].layers), "us_per_group": round(r4["group_ms"] * 1e3, 2),
-                             "query_tokens_per_s_per_layer": round(r4["wl"].n_q * n4 / (r4["group_ms"] / 1e3), 1)}
-        # the chunk's rows all belong to one sequence: scored in groups of 8 over one pass of K
-        r5 = measure_layers("c5", max(args.steps // 5, 3), max(args.warmup // 5, 1), torch, C, [0], group=PREFILL_GROUP)
-        wl5, ms5 = r5["wl"], r5["layers"][0]["ms"]
-        rows = int(wl5.extra["counted_rows"])
-        modes["prefill_chunk_m2"] = {"query_rows": wl5.n_q, "counted_new_tokens": rows, "scoring_group": PREFILL_GROUP,
-                                     "us_per_chunk": round(ms5 * 1e3, 1),
-                                     "new_tokens_per_s": round(rows / (ms5 / 1e3), 1),
-                                     "isolated_launch_us": {k: round(v * 1000, 1) for k, v in r5["isolated"].items()}}
-        wle, mse = measure_group("enc_group", max(args.steps // 5, 3), max(args.warmup // 5, 1), torch, C,
-                                 PREFILL_GROUP)
-        rows = int(wle.extra["counted_rows"])
-        modes["encoder_group_prefill_m2"] = {
-            "layers": len(wle.layers), "structure": "Full + 5 Reuse, window state missed (replay rows rewrite it)",
-            "query_rows": wle.n_q, "counted_new_tokens": rows, "us_per_chunk": round(mse * 1e3, 1),
-            "us_per_layer": round(mse * 1e3 / len(wle.layers), 1), "new_tokens_per_s": round(rows / (mse / 1e3), 1),
-            "scoring_group": PREFILL_GROUP}
-        # multi-token decode: 4 tokens of each of 16 sequences; the Full layer's scoring with
-        # each sequence's 4 rows in one pass over its K (group 4) and per row (group 1)
-        mt = {}
-        for g in (1, 4):
-            rm = measure_layers("mtd_128k", args.steps, args.warmup, torch, C, [0], group=g)
-            mt[g] = (rm["wl"], rm["layers"][0]["ms"], rm["isolated"])
-        wlm = mt[1][0]
-        modes["multi_token_decode_128k"] = {
-            "sequences": wlm.n_seq, "tokens_per_seq": int(wlm.extra["tokens_per_seq"]), "query_rows": wlm.n_q,
-            "us_per_layer_step": round(mt[1][1] * 1e3, 2),
-            "query_tokens_per_s": round(wlm.n_q / (mt[1][1] / 1e3), 1),
-            "us_per_layer_step_grouped_scoring": round(mt[4][1] * 1e3, 2),
-            "isolated_launch_us": {k: round(v * 1e3, 1) for k, v in mt[1][2].items()},
-            "isolated_launch_us_grouped": {k: round(v * 1e3, 1) for k, v in mt[4][2].items()}}
-        # the headline step with the last Top-K level as a launch of its own
-        rs_ = measure_layers("c2", args.steps, args.warmup, torch, C, [0], attn_select=False)
-        g_ = rs_["graph_call"]
-        modes["full_128k_last_level_kernel"] = {
-            "calls": "csa2_index_topk (k_score_select + the last Top-K level), then csa2_sparse_attn",
-            "us_per_layer_step": round(rs_["layers"][0]["ms"] * 1e3, 2),
-            "query_tokens_per_s": round(rs_["wl"].n_q / (rs_["layers"][0]["ms"] / 1e3), 1),
-            "graph_call_us": {k: round(v * 1e3, 2) for k, v in g_.items()},
-            "index_topk_gb_per_s": round(score_bytes(rs_["wl"], "full") / (g_["index_topk"] / 1e3) / 1e9, 1)}
-        # the NVFP4-style indexer variant on the headline step
-        rn = measure_layers("c2", args.steps, args.warmup, torch, C, [0], index_fmt="nvfp4")
-        wln, msn, isn, gcn = rn["wl"], rn["layers"][0]["ms"], rn["isolated"], rn["graph_call"]
-        bn = score_bytes(wln, "full", "nvfp4")
-        scn = "index_segments" if "index_segments" in gcn else "index_topk"
-        gbs = bn / (gcn[scn] / 1e3) / 1e9
-        modes["full_128k_nvfp4_indexer"] = {
-            "index_format": "E2M1 + E4M3 per 16 (72 B per indexer-K entry), fp16 MFMA scoring",
-            "us_per_layer_step": round(msn * 1e3, 2), "query_tokens_per_s": round(wln.n_q / (msn / 1e3), 1),
-            "scoring_call": f"csa2_{scn} (fmt CSA2_FMT_NVFP4)", "scoring_us": round(gcn[scn] * 1e3, 2),
-            "scoring_gb_per_s": round(gbs, 1),
-            "scoring_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "scoring_bytes": bn,
-            "scoring_kernel_us": round(gcn["scoring_kernel"] * 1e3, 2) if "scoring_kernel" in gcn else None,
-            "isolated_launch_us": {k: round(v * 1e3, 2) for k, v in isn.items()}}
-        for name, key in (("dec_128k", "decoder_128k"), ("dec_1m", "decoder_1m")):
-            wld, msd = measure_group(name, args.steps, args.warmup, torch, C)
-            modes[key] = decoder_entry(wld, msd)
+        for name in MODE_RUNNERS:
+            modes.update(MODE_RUNNERS[name](args, torch, C))
         result["modes"] = modes
         for k, v in modes.items():
             log(f"  {k}: {v}")
