@@ -769,6 +769,335 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
   if (a.lse && tid == 0) a.lse[qh] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
 }
 
+// ---- many query rows: one workgroup per row, every head ----
+//
+// With thousands of rows (a prefill chunk, an encoder group) the grid is full without
+// cutting a row's heads into 16-head workgroups, so a row's keys can be dequantised once
+// for all of its heads instead of once per head group.  One workgroup = one row and 64
+// heads, 4 waves of 16 heads each.  Per tile of 32 keys all 256 threads gather the raw
+// bytes (thread = key x 64 channels, two tiles ahead) and dequantise them once into an
+// fp16 tile in LDS (three buffers, one barrier per tile); every wave then forms S^T =
+// K Q^T for its 16 heads over all 512 channels (K read from the tile, Q in registers),
+// runs the online softmax of its own heads (no exchange between waves: a wave holds whole
+// heads) and accumulates O^T += V^T P^T on V_MFMA_F32_16X16X32_F16 over the 32 keys, V^T
+// read from the same tile through DS_READ_B64_TR_B16.  The 32 keys of a P.V product are
+// taken in the order in which the two 16-key S^T blocks leave them in the lanes (keys
+// 4g..4g+3 and 16+4g..16+4g+3 for lane group g), and the V^T reads follow that order, so P
+// needs no shuffle.  Step i forms S of tile i and P.V of tile i-1 (independent matrix
+// work) beside the dequantisation of tile i+1 and the softmax of tile i.  Rows are dealt
+// to the XCDs in contiguous ranges, so neighbouring rows, whose windows overlap, share an
+// L2.  The arithmetic per (row, head) is that of k_attn: exact fp16 keys and values, Q
+// scaled by a power of two per head, P rounded to fp16, fp32 accumulation.
+constexpr int kRWaves = 4;                  // waves per workgroup, 16 heads each
+constexpr int kRThreads = kRWaves * 64;
+constexpr int kRHeads = kRWaves * kHG;      // heads per row
+constexpr int kRT = 32;                     // keys per tile
+// A key row of the fp16 tile (1,024 B) starts at r * kRRow + rpad(r): the per-row offsets
+// put the 16 rows of a K-operand read (16 B per lane) in 16 different bank slots, the 8 rows
+// of a transposed V read (32 B per 4 lanes) in 8 different 32-byte spans, and the rows of
+// one dequantisation store in different slots, so none of the three conflicts
+constexpr int kRRow = kD * 2 + 256;         // row pitch: the data plus room for the offset
+constexpr int kRBuf = kRT * kRRow;          // 40,960 B
+__device__ __forceinline__ int rpad(int r) { return 32 * (r & 7) + 16 * ((r >> 3) & 1); }
+constexpr int kRBufs = 3;
+constexpr int kRSteps = kD / 32;            // QK steps per tile and 16-key block: 16
+constexpr int kRDT = kD / 16;               // 16-channel blocks of O^T: 32
+constexpr int kRIdxPer = CSA2_MAX_TOPK / kRThreads;
+static_assert(kRT * 8 == kRThreads, "one thread per (key, 64 channels) of a tile");
+
+__global__ __launch_bounds__(kRThreads, 1) void k_attn_rows(AttnArgs a, const int32_t* __restrict__ q_seq,
+                                                            const int64_t* __restrict__ q_pos,
+                                                            const int64_t* __restrict__ replay_start,
+                                                            const int64_t* __restrict__ swa_base) {
+  const int rows_per_xcd = (a.n_q + 7) >> 3;
+  const int q = (blockIdx.x & 7) * rows_per_xcd + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= rows_per_xcd || q >= a.n_q) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;    // MFMA roles: key row / head column, lane group
+  const int kk = tid & 31, ck = tid >> 5;         // gather role: key of the tile, 64-channel chunk
+
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[kRBufs * kRBuf];
+  __shared__ int32_t s_idx[CSA2_MAX_TOPK];
+  __shared__ uint32_t s_mask[kRBufs];             // bit k: key k of the tile is present
+
+  const int seq = q_seq[q];
+  const int64_t t = q_pos[q], s = replay_start[q];
+  const bool seq_ok = seq >= 0 && seq < a.n_seq;
+  const int n_mt = (a.k + kRT - 1) / kRT;                 // main tiles
+  const int n_wt = (a.window + kRT - 1) / kRT;            // window tiles (processed first)
+  const int n_tiles = n_mt + n_wt;
+
+  // the row's index list (unconditional clamped loads), then Q
+  int32_t iv[kRIdxPer];
+  const int n_slots = n_mt * kRT;
+  if (a.k > 0) {  // uniform
+#pragma unroll
+    for (int r = 0; r < kRIdxPer; ++r) {
+      const int i = tid + r * kRThreads;
+      iv[r] = a.idx[(int64_t)q * a.k + (i < a.k ? i : a.k - 1)];
+    }
+  }
+  const int head = wave * kHG + col;
+  uint4 qraw[kRSteps];   // step st: channels 32*st + 8*grp .. +7 of the lane's head
+  {
+    const uint16_t* qp = a.q + ((int64_t)q * a.n_heads + head) * kD + 8 * grp;
+#pragma unroll
+    for (int st = 0; st < kRSteps; ++st) qraw[st] = *reinterpret_cast<const uint4*>(qp + 32 * st);
+  }
+
+  const int64_t lo = s > t - a.window + 1 ? s : t - a.window + 1;
+  const int64_t n_swa = seq_ok && t >= lo ? t - lo + 1 : 0;
+  const int64_t swa_b = seq_ok ? swa_base[seq] : 0;
+  const int64_t rel = lo - swa_b;
+  const uint32_t swa_cap32 = (uint32_t)a.swa_cap;
+  int64_t r_lo;
+  if (rel >= 0 && rel <= 0xffffffffLL) {
+    r_lo = (uint32_t)rel % swa_cap32;
+  } else {
+    r_lo = rel % a.swa_cap;
+    r_lo = r_lo < 0 ? r_lo + a.swa_cap : r_lo;
+  }
+  const uint32_t win_row0 = (uint32_t)r_lo;
+  const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.kv_cs;
+  const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.kv_ss;
+  const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_rs;
+
+  // Tile i < n_wt holds window keys 32i .. 32i+31, tile n_wt + m the list's slots 32m ..
+  // 32m+31.  Every load is unconditional, to an in-bounds address (an absent key reads
+  // row 0 and is flagged).  Tiles past the end load row 0 of both caches, flagged absent.
+  auto load_slot = [&](int i, GatherSlot& g) {
+    const bool is_win = i < n_wt;   // uniform
+    const int slot = (i - n_wt) * kRT + kk;
+    const int sc = slot < 0 ? 0 : (slot < n_slots ? slot : (n_slots > 0 ? n_slots - 1 : 0));
+    const int32_t p = (!is_win && i < n_tiles && slot < a.k && n_slots > 0) ? s_idx[sc] : -1;
+    const bool ok_main = !is_win && seq_ok && p >= 0 && p < a.seq_cap;
+    const uint32_t pm = ok_main ? (uint32_t)p : 0u;
+    const int j = i * kRT + kk;
+    const bool ok_win = is_win && seq_ok && j < n_swa;
+    uint32_t row = win_row0 + (uint32_t)j;
+    row = ok_win ? (row >= swa_cap32 ? row - swa_cap32 : row) : 0u;
+    const uint4* c = !is_win
+        ? reinterpret_cast<const uint4*>(kvc + ((uint64_t)pm * (uint64_t)a.kv_ce + 32 * ck))
+        : reinterpret_cast<const uint4*>(swq + ((uint64_t)row * (uint64_t)a.swa_re + 64 * ck));
+    const uint4* c2 = !is_win ? c : c + 2;
+    g.r[0] = c[0];
+    g.r[1] = c[1];
+    g.r[2] = c2[0];
+    g.r[3] = c2[1];
+    g.sc = *reinterpret_cast<const uint32_t*>(kvs + ((uint64_t)pm * (uint64_t)a.kv_se + 4 * ck));
+    g.ok = is_win ? ok_win : ok_main;
+  };
+
+  // dequantise this thread's 64 channels of its key into the tile (absent keys: zeros)
+  // and record which keys are present
+  auto dequant = [&](int i, const GatherSlot& g, int buf) {
+    const uint32_t keep = 0u - g.ok;
+    uint8_t* dst = tiles + buf * kRBuf + kk * kRRow + rpad(kk) + 128 * ck;
+    if (i >= n_wt) {   // uniform: main entries
+      const uint32_t cw[8] = {g.r[0].x, g.r[0].y, g.r[0].z, g.r[0].w, g.r[1].x, g.r[1].y, g.r[1].z, g.r[1].w};
+      const uint32_t sc = g.sc & keep;
+      const v2h s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+      const v2h s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true);
+      const v2h ss[4] = {__builtin_shufflevector(s01, s01, 0, 0), __builtin_shufflevector(s01, s01, 1, 1),
+                         __builtin_shufflevector(s23, s23, 0, 0), __builtin_shufflevector(s23, s23, 1, 1)};
+#pragma unroll
+      for (int d = 0; d < 8; ++d) *reinterpret_cast<v8h*>(dst + 16 * d) = fp4x8_to_f16(cw[d], ss[d >> 1]);
+    } else {
+      const uint32_t w[16] = {g.r[0].x, g.r[0].y, g.r[0].z, g.r[0].w, g.r[1].x, g.r[1].y, g.r[1].z, g.r[1].w,
+                              g.r[2].x, g.r[2].y, g.r[2].z, g.r[2].w, g.r[3].x, g.r[3].y, g.r[3].z, g.r[3].w};
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        *reinterpret_cast<v8h*>(dst + 16 * d) = fp8x8_to_f16(w[2 * d] & keep, w[2 * d + 1] & keep);
+    }
+    // lane k < 32 of every wave holds key k: wave 0 writes the tile's presence mask
+    const uint32_t m32 = (uint32_t)__ballot(g.ok != 0);
+    if (tid == 0) s_mask[buf] = m32;
+  };
+
+  const bool early = n_wt >= 2;   // the first two tiles are window tiles: no index needed
+  GatherSlot g0, g1;
+  if (early) {
+    load_slot(0, g0);
+    load_slot(1, g1);
+  }
+  if (a.k > 0) {
+#pragma unroll
+    for (int r = 0; r < kRIdxPer; ++r) {
+      const int i = tid + r * kRThreads;
+      if (i < n_slots) s_idx[i] = i < a.k ? iv[r] : -1;
+    }
+  }
+  // the head's largest |q| over its 512 channels (bf16 magnitude bits), over the 4 lanes of
+  // the head
+  uint32_t qm = 0;
+#pragma unroll
+  for (int st = 0; st < kRSteps; ++st) {
+    const uint32_t w4[4] = {qraw[st].x, qraw[st].y, qraw[st].z, qraw[st].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t l16 = w4[i] & 0x7fffu, h16 = (w4[i] >> 16) & 0x7fffu;
+      qm = l16 > qm ? l16 : qm;
+      qm = h16 > qm ? h16 : qm;
+    }
+  }
+  {
+    uint32_t o = (uint32_t)__shfl_xor((int)qm, 16);
+    qm = o > qm ? o : qm;
+    o = (uint32_t)__shfl_xor((int)qm, 32);
+    qm = o > qm ? o : qm;
+  }
+  const int qsh = q_shift(qm);
+  const float qsl = ldexpf(a.scale_log2, qsh);
+  v8h qf[kRSteps];
+#pragma unroll
+  for (int st = 0; st < kRSteps; ++st) {
+    const uint32_t w4[4] = {qraw[st].x, qraw[st].y, qraw[st].z, qraw[st].w};
+    v8h h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[2 * i] = bf16_to_f16(w4[i] & 0xffffu, qsh);
+      h[2 * i + 1] = bf16_to_f16(w4[i] >> 16, qsh);
+    }
+    qf[st] = h;
+  }
+  __syncthreads();   // s_idx
+  if (!early) {
+    load_slot(0, g0);
+    load_slot(1, g1);
+  }
+
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  v4f o[kRDT];
+#pragma unroll
+  for (int i = 0; i < kRDT; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // S^T of tile buf for this wave's heads: two 16-key blocks, each over the 512 channels
+  // (K rows read from the tile: lane = key col, channels 32*st + 8*grp .. +7)
+  auto qk = [&](int buf, v4f* s2) {
+    const uint8_t* tb = tiles + buf * kRBuf + col * kRRow + rpad(col) + 16 * grp;
+    v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0;
+#pragma unroll
+    for (int st = 0; st < kRSteps; st += 2) {
+      const v8h k00 = *reinterpret_cast<const v8h*>(tb + 64 * st);
+      const v8h k01 = *reinterpret_cast<const v8h*>(tb + 64 * (st + 1));
+      const v8h k10 = *reinterpret_cast<const v8h*>(tb + 16 * kRRow + 64 * st);
+      const v8h k11 = *reinterpret_cast<const v8h*>(tb + 16 * kRRow + 64 * (st + 1));
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k00, qf[st], a0, 0, 0, 0);
+      b0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k10, qf[st], b0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k01, qf[st + 1], a1, 0, 0, 0);
+      b1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k11, qf[st + 1], b1, 0, 0, 0);
+    }
+    s2[0] = a0 + a1;
+    s2[1] = b0 + b1;
+  };
+
+  // online softmax of one tile (lane: head col; keys 4*grp + r and 16 + 4*grp + r) with the
+  // lazy reference of k_attn; returns P^T in fp16 in the K order of the P.V product
+  auto softmax = [&](const v4f* s2, uint32_t valid, float* alpha_out) -> v8h {
+    float x[8];
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int key = (r < 4 ? 0 : 16) + 4 * grp + (r & 3);
+      const bool ok = (valid >> key) & 1u;
+      x[r] = ok ? s2[r >> 2][r & 3] * qsl : -__builtin_inff();
+      mt = fmaxf(mt, x[r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const bool first = m_run == -__builtin_inff();
+    const bool move = first ? mt != -__builtin_inff() : mt > m_run + kLazy;
+    const float m_new = move ? mt : m_run;
+    const float alpha = (move && !first) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    const bool none = m_new == -__builtin_inff();
+    v8h pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float pr = none ? 0.0f : __builtin_amdgcn_exp2f(x[r] - m_new);
+      psum += pr;
+      pb[r] = (_Float16)pr;
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    *alpha_out = alpha;
+    return pb;
+  };
+
+  // O^T += V^T P^T over the 32 keys of tile buf: A = V^T (16 channels x 32 keys in the K
+  // order above), two transposed reads of 4 keys each per lane
+  auto pv = [&](v8h pb, int buf) {
+    const __attribute__((address_space(3))) uint8_t* vb =
+        (const __attribute__((address_space(3))) uint8_t*)(tiles + buf * kRBuf) + (4 * grp + (col >> 2)) * kRRow +
+        rpad(4 * grp + (col >> 2)) +
+        8 * (col & 3);
+#pragma unroll
+    for (int dt = 0; dt < kRDT; ++dt) {
+      const v4h lo4 = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + 32 * dt)));
+      const v4h hi4 =
+          __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + 16 * kRRow + 32 * dt)));
+      const v8h av = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, o[dt], 0, 0, 0);
+    }
+  };
+
+  // ---- pipeline.  Tile i lives in buffer i % 3 and its raw bytes in slot g(i % 2).  Step i
+  // (after a barrier) dequantises tile i+1, refills its slot with tile i+3, then forms S of
+  // tile i, P.V of tile i-1 and the softmax of tile i.  The barrier of step i orders the
+  // dequantisation of tile i (step i-1) before the S of tile i, and the P.V of tile i-2
+  // (step i-1) before the dequantisation of tile i+1 into the same buffer ----
+  dequant(0, g0, 0);
+  load_slot(2, g0);
+  __syncthreads();
+  dequant(1, g1, 1);
+  load_slot(3, g1);
+  v4f s2[2];
+  float alpha;
+  qk(0, s2);
+  v8h pb = softmax(s2, s_mask[0], &alpha);
+  auto step = [&](int i, GatherSlot& g) {   // 1 <= i < n_tiles; g holds tile i+1
+    __syncthreads();
+    dequant(i + 1, g, (i + 1) % kRBufs);   // past the last tile: absent keys, never read
+    load_slot(i + 3, g);
+    qk(i % kRBufs, s2);
+    pv(pb, (i - 1) % kRBufs);
+    pb = softmax(s2, s_mask[i % kRBufs], &alpha);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < kRDT; ++dt) o[dt] *= alpha;
+    }
+  };
+  // whole rounds of the two slots inside the loop, the remainder after it
+  int i = 1;
+  for (; i + 1 < n_tiles; i += 2) {
+    step(i, g0);
+    step(i + 1, g1);
+  }
+  if (i < n_tiles) step(i, g0);   // uniform
+  pv(pb, (n_tiles - 1) % kRBufs);
+
+  // ---- output: lane (head col, grp) holds channels 16*dt + 4*grp .. +3 of its head ----
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot = l_tot + __shfl_xor(l_tot, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const int64_t ob = ((int64_t)q * a.n_heads + head) * kD + 4 * grp;
+#pragma unroll
+  for (int dt = 0; dt < kRDT; ++dt) {
+    const v4f v = o[dt] * inv;
+    if (a.out_dtype == CSA2_DT_F32) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + ob + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      uint2 pk;
+      pk.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+      pk.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + ob + 16 * dt) = pk;
+    }
+  }
+  if (grp == 0 && a.lse) a.lse[(int64_t)q * a.n_heads + head] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+}
+
 struct AttnPlan {
   int head_groups, n_tiles, main_tiles, tiles_per_split, nsplit;
   int64_t grid;
@@ -791,6 +1120,13 @@ static AttnPlan plan(int n_q, int n_heads, int k, int window) {
   const int64_t q_pad = ((int64_t)n_q + 7) / 8 * 8;
   p.grid = q_pad * p.head_groups * p.nsplit;
   return p;
+}
+
+// The row kernel serves batches of many rows with an index list given and 64 heads, where
+// one workgroup per row fills the GPU several times over (at least 4 rows per CU).
+constexpr int kRowsMinQ = 1024;
+static bool use_rows_kernel(int n_q, int n_heads, int sel_mode, bool new_win) {
+  return sel_mode == 0 && !new_win && n_heads == kRHeads && n_q >= kRowsMinQ;
 }
 
 }  // namespace csa2
@@ -907,6 +1243,12 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, CacheRef kv
     a.ws_ml = a.ws_o + (size_t)p.nsplit * n_q * n_heads * kD;
   }
   hipStream_t st = (hipStream_t)stream;
+  if (use_rows_kernel(n_q, n_heads, sel.mode, new_win != nullptr)) {
+    const int64_t grid = 8 * (((int64_t)n_q + 7) / 8);
+    hipLaunchKernelGGL(k_attn_rows, dim3((unsigned)grid), dim3(kRThreads), 0, st, a, a.q_seq, a.q_pos,
+                       a.replay_start, a.swa_base);
+    return csa2_check_launch();
+  }
   if (sel.mode == 2)
     hipLaunchKernelGGL(k_attn<2>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
                        a.replay_start, a.swa_base);

@@ -1077,6 +1077,67 @@ def test_binding_refuses_unsafe_calls(C):
                            rs, 128, 0.05, out, new_win=new)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("window,k,out_dt,peaked", [(128, 512, "f32", False), (128, 512, "bf16", True),
+                                                    (40, 100, "f32", False), (1, 512, "f32", False),
+                                                    (200, 512, "f32", True)])
+def test_sparse_attn_many_rows(C, window, k, out_dt, peaked):
+    """A batch of 1,100 rows with 64 heads and a given index list (the size of a prefill
+    chunk's batch: one workgroup per row, every head): every row against the oracle.  Rows
+    of 4 sequences with ragged index sets (empty ones included), invalid indices, replay
+    starts inside and at the end of the window, windows of 1, 40, 128 and 200 keys (ring of
+    256 rows), k not a multiple of the 32-key tile, and peaked logits (later tiles beat the
+    lazy softmax reference by far more than its headroom)."""
+    _say("sparse_attn many rows", window, k, out_dt, peaked)
+    n_q, n_seq, cap, heads = 1100, 4, 2400, 64
+    rng = np.random.default_rng(window * 7 + k)
+    t = [int(x) for x in rng.integers(0, cap, size=n_q)]
+    t[0] = cap - 1
+    s = [0 if i % 3 == 0 else (max(0, ti - window // 2) if i % 3 == 1 else ti) for i, ti in enumerate(t)]
+    case = _attn_case(50 + window, n_seq, cap, heads, t, s, swa_cap=256)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_seq, _, q_pos, rs = case.gpu_meta()
+    counts = [int(c) for c in rng.integers(0, k + 1, size=n_q)]
+    counts[0], counts[1], counts[2] = k, 0, k
+    idx = np.full((n_q, k), -1, np.int32)
+    for qi in range(n_q):
+        idx[qi, :counts[qi]] = np.sort(rng.choice(t[qi] + 1 if t[qi] + 1 >= counts[qi] else cap,
+                                                  size=counts[qi], replace=False))
+    idx[2, 5] = cap + 3          # out of range: skipped
+    idx[2, 9] = -4               # negative: skipped
+    sm_scale = 1.0 / math.sqrt(512)
+    if peaked:
+        q_np = _peaked_q(case, idx, counts, t, s, window, heads, rng)
+    else:
+        q_np = rng.standard_normal((n_q, heads, 512)).astype(np.float32)
+    qa = _bf16(q_np)
+    q_exact = qa.float().cpu().numpy()
+    dt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    out = torch.empty(n_q, heads, 512, dtype=dt, device="cuda")
+    lse = torch.empty(n_q, heads, dtype=torch.float32, device="cuda")
+    assert C.csa2_attn_workspace_bytes(n_q, heads, 512, k, window) == 0
+    C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, torch.from_numpy(idx).cuda(), caches.swa[0],
+                       caches.swa_base, q_pos, rs, window, sm_scale, out, lse)
+    torch.cuda.synchronize()
+    assert C.csa2_device_status() == 0
+    go, gl = out.float().cpu().numpy(), lse.cpu().numpy()
+    ocs = {b: case.oracle_caches(b) for b in range(n_seq)}
+    for qi in range(n_q):
+        oc = ocs[int(wl.q_seq[qi])]
+        sel = idx[qi, :counts[qi]]
+        sel = sel[(sel >= 0) & (sel < cap)]
+        ref, ref_lse = O.sparse_attention(q_exact[qi].astype(np.float64), oc.main_rows(sel),
+                                          oc.swa_rows(0, O.swa_positions(t[qi], s[qi], window)), sm_scale)
+        if out_dt == "f32":
+            G.attn_close(go[qi], ref, 2e-3)
+        else:
+            attn_close_bf16(go[qi], ref)
+        finite = np.isfinite(ref_lse)
+        assert np.array_equal(finite, np.isfinite(gl[qi])), qi
+        assert np.abs(gl[qi][finite] - ref_lse[finite]).max(initial=0.0) <= 1e-3, qi
+
+
 def test_sparse_attn_no_keys(C):
     """s > t leaves the window empty; with no main entries the output is 0 and lse -inf."""
     _say("sparse_attn no keys")
