@@ -77,19 +77,23 @@ struct ScoreArgs {
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // reduce-scatter of the four tiles' per-lane-group partial sums: lane group g ends with tile
-// g's full sum, so lane l holds the score of entry l of the step
-__device__ __forceinline__ float scatter_tiles(const float (&part)[4], int kb) {
-  const bool b1 = (kb & 2) != 0, b0 = (kb & 1) != 0;
-  const float s0 = b1 ? part[0] : part[2];
-  const float s1 = b1 ? part[1] : part[3];
-  const float r0 = __shfl_xor(s0, 32);
-  const float r1 = __shfl_xor(s1, 32);
-  const float k0 = (b1 ? part[2] : part[0]) + r0;
-  const float k1 = (b1 ? part[3] : part[1]) + r1;
-  const float send = b0 ? k0 : k1;
-  const float recv = __shfl_xor(send, 16);
-  return (b0 ? k1 : k0) + recv;
+// g's full sum, so lane l holds the score of entry l of the step.  V_PERMLANE32_SWAP of
+// (tile 0, tile 2) leaves in its two results, lane by lane, the two halves of the wave that
+// the lane's own half needs, so their sum is tiles 0 + 0' for the low half and 2 + 2' for
+// the high one (likewise tiles 1 and 3); V_PERMLANE16_SWAP does the same across the 16-lane
+// groups.  No LDS round trip; each sum adds the same two numbers as a lane exchange would.
+__device__ __forceinline__ float scatter_tiles(const float (&part)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+  const float k0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float k1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
+
+// ReLU on the bit pattern: a non-negative float is a non-negative int and a negative one
+// (or -0) a negative int, so one integer max gives max(x, +0)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Scores of the 64 entries of one step (four 16-entry MFMA tiles) for one query row: A =
 // the row's indexer Q (16 heads x 128 channels, this lane: head `lane % 16`, channels
@@ -105,10 +109,10 @@ __device__ __forceinline__ float score_tiles(const v8i& a, int a_scale, const fl
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 4, 0, a_scale, 0, bs[t]);
     float p = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p += wv[r] * fmaxf(acc[r], 0.0f);
+    for (int r = 0; r < 4; ++r) p += wv[r] * relu(acc[r]);
     part[t] = p;
   }
-  return scatter_tiles(part, kb);
+  return scatter_tiles(part);
 }
 
 // ---- NVFP4-style indexer operands (E2M1 + one E4M3 scale per 16 channels) ----
@@ -152,10 +156,10 @@ __device__ __forceinline__ float score_tiles_nv(const v8h (&a)[4], const float (
     for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u], b[u], acc, 0, 0, 0);
     float p = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p += wv[r] * fmaxf(acc[r], 0.0f);
+    for (int r = 0; r < 4; ++r) p += wv[r] * relu(acc[r]);
     part[t] = p;
   }
-  return scatter_tiles(part, kb);
+  return scatter_tiles(part);
 }
 
 // One query's view of the cache: MFMA operands, slot -> row mapping, one scoring step.
@@ -405,6 +409,10 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_grouped(ScoreArgs s, in
 constexpr int kGtRowsPerWave = kGroupMax / (kScoreThreads / 64);   // 2
 constexpr int kGtCap = 768;                                        // candidate keys per row in LDS
 
+// kOff32: every entry's code and scale offsets within its sequence fit 32 bits (the host
+// checks seq_cap * stride), so a load is the sequence's uniform base plus a 32-bit lane offset
+// that advances by a constant per step instead of a 64-bit multiply per tile.
+template <bool kOff32>
 __global__ __launch_bounds__(kScoreThreads) void k_score_topk_grouped(ScoreArgs s, int n_q, int group,
                                                                       int range_len, int n_ranges) {
   const int range = blockIdx.x;    // consecutive workgroups take consecutive ranges, so one
@@ -454,14 +462,36 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topk_grouped(ScoreArgs 
   const int hi = lo + range_len < nv_max ? lo + range_len : nv_max;   // uniform over the wave
   const uint8_t* kc = s.k_codes + (int64_t)(seq_ok ? seq : 0) * s.k_cs;
   const uint8_t* ks = s.k_scales + (int64_t)(seq_ok ? seq : 0) * s.k_ss;
+  // entries past hi (the next range's, or past the visible end) read entry hi - 1 and their
+  // results are discarded
+  const uint32_t ce = (uint32_t)s.k_ce, se = (uint32_t)s.k_se;
+  const uint32_t last = hi > 0 ? (uint32_t)(hi - 1) : 0u;
+  const uint32_t c_last = last * ce + kb * 16u, s_last = last * se + kb;
+  uint32_t c_off[4], s_off[4];   // kOff32: offsets of the next step's entries
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t e0 = (uint32_t)(lo + 16 * t + row);
+    c_off[t] = e0 * ce + kb * 16u;
+    s_off[t] = e0 * se + kb;
+  }
   auto load_step = [&](int base, uint4 (&bc)[4], int (&bs)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int e = base + 16 * t + row;
-      const uint32_t pos = e < hi ? (uint32_t)e : 0u;
-      const v4u v = *reinterpret_cast<const v4u*>(kc + ((uint64_t)pos * (uint64_t)s.k_ce + kb * 16u));
-      bc[t] = make_uint4(v.x, v.y, v.z, v.w);
-      bs[t] = ks[(uint64_t)pos * (uint64_t)s.k_se + kb];
+      if constexpr (kOff32) {
+        const uint32_t co = c_off[t] < c_last ? c_off[t] : c_last;
+        const uint32_t so = s_off[t] < s_last ? s_off[t] : s_last;
+        const v4u v = *reinterpret_cast<const v4u*>(kc + co);
+        bc[t] = make_uint4(v.x, v.y, v.z, v.w);
+        bs[t] = ks[so];
+        c_off[t] += 64u * ce;
+        s_off[t] += 64u * se;
+      } else {
+        const int e = base + 16 * t + row;
+        const uint32_t pos = e < hi ? (uint32_t)e : last;
+        const v4u v = *reinterpret_cast<const v4u*>(kc + ((uint64_t)pos * (uint64_t)s.k_ce + kb * 16u));
+        bc[t] = make_uint4(v.x, v.y, v.z, v.w);
+        bs[t] = ks[(uint64_t)pos * (uint64_t)s.k_se + kb];
+      }
     }
   };
   int cnt[kGtRowsPerWave];
@@ -494,14 +524,20 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topk_grouped(ScoreArgs 
     for (int base = lo; base < hi; base += 64) {
       uint4 bcn[4];
       int bsn[4];
-      load_step(base + 64 < hi ? base + 64 : base, bcn, bsn);
+      load_step(base + 64 < hi ? base + 64 : base, bcn, bsn);   // past the end: entry hi - 1
       const int e = base + lane;
+      // every row's matrix work first (a row whose visible range has ended is scored and
+      // discarded), so one row's reductions overlap the next row's MFMAs
+      float v[kGtRowsPerWave];
+#pragma unroll
+      for (int u = 0; u < kGtRowsPerWave; ++u) {
+        const v8i a = {(int)qa[u].x, (int)qa[u].y, (int)qa[u].z, (int)qa[u].w, 0, 0, 0, 0};
+        v[u] = score_tiles(a, asc[u], wv[u], kb, bc, bs);
+      }
 #pragma unroll
       for (int u = 0; u < kGtRowsPerWave; ++u) {
         if (nvr[u] > base) {   // uniform
-          const v8i a = {(int)qa[u].x, (int)qa[u].y, (int)qa[u].z, (int)qa[u].w, 0, 0, 0, 0};
-          const float v = score_tiles(a, asc[u], wv[u], kb, bc, bs);
-          const uint64_t key = make_key(v, (uint32_t)e);
+          const uint64_t key = make_key(v[u], (uint32_t)e);
           const bool in = e < hi && e < nvr[u] && key >= thr[u];   // past hi: the next range's entry
           const uint64_t m = __ballot(in);
           if (in) list[wave + (kScoreThreads / 64) * u][cnt[u] + (int)__popcll(m & lt_mask)] = key;
@@ -992,8 +1028,16 @@ extern "C" int csa2_index_topk_grouped(const uint8_t* q_codes, const uint8_t* q_
   a.k = k;
   a.keys_out = (uint64_t*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(k_score_topk_grouped, dim3((unsigned)n_ranges, (unsigned)n_groups), dim3(kScoreThreads), 0, st,
-                     a, n_q, group, (int)range_len, n_ranges);
+  // 32-bit offsets within a sequence: a lane's offsets run at most 128 entries past the last
+  // one before they are clamped, and must not wrap on the way
+  const bool off32 = (uint64_t)(seq_cap + 128) * (uint64_t)a.k_ce + 64 <= 0xffffffffull &&
+                     (uint64_t)(seq_cap + 128) * (uint64_t)a.k_se + 4 <= 0xffffffffull;
+  if (off32)
+    hipLaunchKernelGGL(k_score_topk_grouped<true>, dim3((unsigned)n_ranges, (unsigned)n_groups), dim3(kScoreThreads),
+                       0, st, a, n_q, group, (int)range_len, n_ranges);
+  else
+    hipLaunchKernelGGL(k_score_topk_grouped<false>, dim3((unsigned)n_ranges, (unsigned)n_groups), dim3(kScoreThreads),
+                       0, st, a, n_q, group, (int)range_len, n_ranges);
   rc = csa2_check_launch();
   if (rc != CSA2_OK) return rc;
   const int64_t segs[2] = {n_ranges, 1};
