@@ -1110,8 +1110,6 @@ extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_sca
   t.k = k;
   t.idx_out = idx_out;
   t.count_out = count_out;
-  rc = select_levels_after0(segs, L, t, n_q, bufA, bufB, st);
-  if (rc != CSA2_OK) return rc;
   // the pool: top max_blocks blocks by block maximum (ties to the lower block id)
   TkArgs pa = {};
   pa.scores = bmax;
@@ -1123,5 +1121,39 @@ extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_sca
   pa.idx_out = blocks_out;
   pa.count_out = blocks_count;
   pa.n_slots = nblk;
-  return select_from_scores(pa, n_q, nblk, pool_ws, pool_ws_bytes, st);
+  // Two selection chains: A, the Top-k over the segment survivors (levels 1 .. L-1), and B,
+  // the pool over the block maxima (levels 0 .. LB-1).  Launch j runs level j+1 of A and
+  // level j of B together (they are independent), so the chains share their launches.
+  int64_t segs_b[16];
+  const int LB = plan_levels(nblk < 1 ? 1 : nblk, max_blocks, segs_b, 16);
+  if (LB >= 16) return CSA2_ERR_SHAPE;
+  if (ws_bytes(n_q, nblk < 1 ? 1 : nblk, max_blocks) > pool_ws_bytes) return CSA2_ERR_WORKSPACE;
+  uint64_t* poolA = (uint64_t*)(((uintptr_t)pool_ws + 255) & ~(uintptr_t)255);
+  uint64_t* poolB = poolA + (size_t)max_blocks * n_q * segs_b[0];
+  const int LA = L - 1;
+  for (int j = 0; j < (LA > LB ? LA : LB); ++j) {
+    TkArgs ta = t, tb = pa;
+    int sa = 0, sb = 0;
+    bool fa = false, fb = false;
+    if (j < LA) {
+      const int l = j + 1;
+      ta.keys_in = (l % 2 == 1) ? bufA : bufB;
+      ta.keys_in_per_q = segs[l - 1] * k;
+      ta.keys_out = (l % 2 == 0) ? bufA : bufB;
+      sa = (int)segs[l];
+      fa = l == L - 1;
+    }
+    if (j < LB) {
+      if (j > 0) {
+        tb.keys_in = (j % 2 == 1) ? poolA : poolB;
+        tb.keys_in_per_q = segs_b[j - 1] * max_blocks;
+      }
+      tb.keys_out = (j % 2 == 0) ? poolA : poolB;
+      sb = (int)segs_b[j];
+      fb = j == LB - 1;
+    }
+    rc = launch_wide2(ta, sa, fa, tb, sb, fb, j == 0, n_q, st);
+    if (rc != CSA2_OK) return rc;
+  }
+  return CSA2_OK;
 }

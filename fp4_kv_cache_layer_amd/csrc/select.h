@@ -430,6 +430,12 @@ inline size_t ws_bytes(int n_q, int64_t n0, int k) {
 int select_levels_after0(const int64_t* segs, int L, TkArgs base, int n_q, uint64_t* bufA, uint64_t* bufB,
                          hipStream_t st);
 
+// One level of each of two selection chains in one launch of the 1,024-thread level kernel
+// (segments of kTkSeg candidates): chain a reads keys, chain b keys or (b_from_scores, its
+// first level) a score array without a slot map; segs 0 leaves a chain out.
+int launch_wide2(const TkArgs& a, int segs_a, bool final_a, const TkArgs& b, int segs_b, bool final_b,
+                 bool b_from_scores, int n_q, hipStream_t st);
+
 // The Top-K levels over a score array (the csa2_topk path; `base` as csa2_topk fills it);
 // `workspace` holds ws_bytes(n_q, n0, base.k) bytes.  Returns a csa2 status.
 int select_from_scores(TkArgs base, int n_q, int64_t n0, void* workspace, size_t workspace_bytes, hipStream_t st);

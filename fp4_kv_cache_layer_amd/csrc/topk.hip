@@ -137,35 +137,71 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(TkArgs a) {
   select_segment<kFinal>(key, q, seg, gridDim.x, K, hist, a.keys_out, a.idx_out, a.count_out);
 }
 
-// ---- the last level: one query's at most 8,192 survivors, 1,024 threads x 8 keys ----
-// Same selection and output as select_segment<true> (exact radix select on the 64-bit keys,
-// then a stable compaction in candidate order), laid out for 16 waves so that the serial
-// parts of the single workgroup per query are short: the count comes from ballots, the
-// range of the keys from DPP reductions of their high words, each wave counts into its own
-// 256-bin histogram and the sixteen are summed in two stages.
+// ---- the wide level: one segment of at most 8,192 candidates, 1,024 threads x 8 keys ----
+// Same selection and output as select_segment (exact radix select on the 64-bit keys, then a
+// stable compaction in candidate order), laid out for 16 waves so that the serial parts of
+// a workgroup are short: the count comes from ballots, the range of the keys from DPP
+// reductions of their high words, each wave counts into its own 256-bin histogram and the
+// sixteen are summed in two stages.  It serves the levels after the first (candidates are
+// the previous level's surviving keys) and the first level over a score array without a
+// slot map (the pool's block maxima).  kFinal: the query's Top-K positions; otherwise the
+// segment's best K keys for the next level.
 constexpr int kFinThreads = 1024;
 constexpr int kFinWaves = kFinThreads / 64;
 constexpr int kFinEpt = kTkSeg / kFinThreads;   // 8
 
-__global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
-  const int q = blockIdx.y;
+struct WideLds {
+  uint32_t hist[kFinWaves][256];
+  uint32_t part[4][256];
+  uint32_t red[3][kFinWaves];
+  uint32_t cnt[kFinWaves][kFinEpt];
+};
+
+template <int kMode, bool kFinal>
+__device__ __forceinline__ void wide_level(const TkArgs& a, int q, int seg, int n_seg, WideLds& L) {
+  static_assert(kMode == kFromKeys || kMode == kFromScores, "keys, or a score array without a slot map");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.k;
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kFinWaves][256];
-  __shared__ __attribute__((aligned(16))) uint32_t part[4][256];
-  __shared__ uint32_t red[3][kFinWaves];
-  __shared__ uint32_t cnt[kFinWaves][kFinEpt];
+  const int64_t c0 = (int64_t)seg * kTkSeg;
 
-  // ---- keys: candidate i*1024 + tid ----
+  // ---- keys: candidate c0 + i*1024 + tid; unconditional clamped loads, masked after ----
   uint64_t key[kFinEpt];
-  {
-    const uint64_t* kp = a.keys_in + q * a.keys_in_per_q;
-    const int lim = (int)(a.keys_in_per_q < kTkSeg ? a.keys_in_per_q : kTkSeg);
+  if constexpr (kMode == kFromKeys) {
+    const int64_t left = a.keys_in_per_q - c0;
+    const int lim = (int)(left < kTkSeg ? (left > 0 ? left : 0) : kTkSeg);
+    if (lim > 0) {  // uniform
+      const uint64_t* kp = a.keys_in + q * a.keys_in_per_q + c0;
 #pragma unroll
-    for (int i = 0; i < kFinEpt; ++i) {
-      const int o = i * kFinThreads + tid;
-      key[i] = o < lim ? kp[o] : 0ull;
+      for (int i = 0; i < kFinEpt; ++i) {
+        const int o = i * kFinThreads + tid;
+        key[i] = kp[o < lim ? o : lim - 1] & (0ull - (uint64_t)(o < lim));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kFinEpt; ++i) key[i] = 0ull;
+    }
+  } else {
+    int64_t nv = a.n_vis[q];
+    if (a.vis_div > 1) nv = nv > 0 ? (nv + a.vis_div - 1) / a.vis_div : 0;
+    nv = nv < 0 ? 0 : (nv > a.max_vis ? a.max_vis : nv);
+    const int lim = (int)(nv - c0 < kTkSeg ? (nv - c0 > 0 ? nv - c0 : 0) : kTkSeg);
+    if (lim > 0) {  // uniform
+      const float* sp = a.scores + q * a.scores_stride + c0;
+      float v[kFinEpt];
+#pragma unroll
+      for (int i = 0; i < kFinEpt; ++i) {
+        const int o = i * kFinThreads + tid;
+        v[i] = sp[o < lim ? o : lim - 1];
+      }
+#pragma unroll
+      for (int i = 0; i < kFinEpt; ++i) {
+        const int o = i * kFinThreads + tid;
+        key[i] = make_key(v[i], (uint32_t)(c0 + o)) & (0ull - (uint64_t)(o < lim));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kFinEpt; ++i) key[i] = 0ull;
     }
   }
 
@@ -181,9 +217,9 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
   hmax = dpp_max_u32(hmax);
   hmin = dpp_min_u32(hmin);
   if (lane == 0) {
-    red[0][wave] = nw;
-    red[1][wave] = hmax;
-    red[2][wave] = hmin;
+    L.red[0][wave] = nw;
+    L.red[1][wave] = hmax;
+    L.red[2][wave] = hmin;
   }
   __syncthreads();
   uint32_t n = 0;
@@ -191,9 +227,9 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
   hmin = ~0u;
 #pragma unroll
   for (int w = 0; w < kFinWaves; ++w) {
-    n += red[0][w];
-    hmax = max(hmax, red[1][w]);
-    hmin = min(hmin, red[2][w]);
+    n += L.red[0][w];
+    hmax = max(hmax, L.red[1][w]);
+    hmin = min(hmin, L.red[2][w]);
   }
 
   // ---- radix select: (prefix, mask) such that exactly K keys have (key & mask) >= prefix ----
@@ -215,16 +251,16 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
       lmin = dpp_min_u32(lmin);
       __syncthreads();  // red[] was read above
       if (lane == 0) {
-        red[1][wave] = lmax;
-        red[2][wave] = lmin;
+        L.red[1][wave] = lmax;
+        L.red[2][wave] = lmin;
       }
       __syncthreads();
       lmax = 0u;
       lmin = ~0u;
 #pragma unroll
       for (int w = 0; w < kFinWaves; ++w) {
-        lmax = max(lmax, red[1][w]);
-        lmin = min(lmin, red[2][w]);
+        lmax = max(lmax, L.red[1][w]);
+        lmin = min(lmin, L.red[2][w]);
       }
       hb = 31 - __clz(lmax ^ lmin);  // n >= 2 unique keys: lmax != lmin
       top = ((uint64_t)hmax << 32) | lmax;
@@ -234,23 +270,23 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
     int shift = hb - 7 > 0 ? hb - 7 : 0;
     uint32_t need = (uint32_t)K;
     for (;;) {
-      reinterpret_cast<uint4*>(hist[wave])[lane] = make_uint4(0u, 0u, 0u, 0u);
+      reinterpret_cast<uint4*>(L.hist[wave])[lane] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int i = 0; i < kFinEpt; ++i)
-        if (key[i] && (key[i] & mask) == prefix) atomicAdd(&hist[wave][(uint32_t)(key[i] >> shift) & 255u], 1u);
+        if (key[i] && (key[i] & mask) == prefix) atomicAdd(&L.hist[wave][(uint32_t)(key[i] >> shift) & 255u], 1u);
       __syncthreads();
       {  // stage 1: thread t sums bin t % 256 over waves 4*(t / 256) .. +3
         const int b = tid & 255, g4 = tid >> 8;
-        part[g4][b] = hist[4 * g4][b] + hist[4 * g4 + 1][b] + hist[4 * g4 + 2][b] + hist[4 * g4 + 3][b];
+        L.part[g4][b] = L.hist[4 * g4][b] + L.hist[4 * g4 + 1][b] + L.hist[4 * g4 + 2][b] + L.hist[4 * g4 + 3][b];
       }
       __syncthreads();
       // stage 2, in every wave: lane l owns bins 4l..4l+3
       uint32_t hs[4];
       {
-        const uint4 p0 = reinterpret_cast<const uint4*>(part[0])[lane];
-        const uint4 p1 = reinterpret_cast<const uint4*>(part[1])[lane];
-        const uint4 p2 = reinterpret_cast<const uint4*>(part[2])[lane];
-        const uint4 p3 = reinterpret_cast<const uint4*>(part[3])[lane];
+        const uint4 p0 = reinterpret_cast<const uint4*>(L.part[0])[lane];
+        const uint4 p1 = reinterpret_cast<const uint4*>(L.part[1])[lane];
+        const uint4 p2 = reinterpret_cast<const uint4*>(L.part[2])[lane];
+        const uint4 p3 = reinterpret_cast<const uint4*>(L.part[3])[lane];
         hs[0] = p0.x + p1.x + p2.x + p3.x;
         hs[1] = p0.y + p1.y + p2.y + p3.y;
         hs[2] = p0.z + p1.z + p2.z + p3.z;
@@ -292,7 +328,7 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
 #pragma unroll
   for (int i = 0; i < kFinEpt; ++i) {
     const uint64_t m = __ballot(key[i] && (key[i] & mask) >= prefix);
-    if (lane == 0) cnt[wave][i] = (uint32_t)__popcll(m);
+    if (lane == 0) L.cnt[wave][i] = (uint32_t)__popcll(m);
   }
   __syncthreads();
   // lane i < 8: off = (survivors of slots < i, all waves) + (survivors of slot i, waves < w)
@@ -300,7 +336,7 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
   if (lane < kFinEpt) {
 #pragma unroll
     for (int w = 0; w < kFinWaves; ++w) {
-      const uint32_t c = cnt[w][lane];
+      const uint32_t c = L.cnt[w][lane];
       tot_i += c;
       before_w += w < wave ? c : 0u;
     }
@@ -310,16 +346,62 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
   const uint32_t off = excl - tot_i + before_w;
   const uint32_t nsel = total < (uint32_t)K ? total : (uint32_t)K;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int32_t* out = a.idx_out + (int64_t)q * K;
+  if constexpr (kFinal) {
+    int32_t* out = a.idx_out + (int64_t)q * K;
 #pragma unroll
-  for (int i = 0; i < kFinEpt; ++i) {
-    const bool take = key[i] && (key[i] & mask) >= prefix;
-    const uint64_t m = __ballot(take);
-    const uint32_t slot = __builtin_amdgcn_readlane(off, i) + (uint32_t)__popcll(m & lt_mask);
-    if (take && slot < (uint32_t)K) out[slot] = key_pos(key[i]);
+    for (int i = 0; i < kFinEpt; ++i) {
+      const bool take = key[i] && (key[i] & mask) >= prefix;
+      const uint64_t m = __ballot(take);
+      const uint32_t slot = __builtin_amdgcn_readlane(off, i) + (uint32_t)__popcll(m & lt_mask);
+      if (take && slot < (uint32_t)K) out[slot] = key_pos(key[i]);
+    }
+    for (int i = (int)nsel + tid; i < K; i += kFinThreads) out[i] = -1;
+    if (tid == 0) a.count_out[q] = (int32_t)nsel;
+  } else {
+    uint64_t* out = a.keys_out + ((int64_t)q * n_seg + seg) * K;
+#pragma unroll
+    for (int i = 0; i < kFinEpt; ++i) {
+      const bool take = key[i] && (key[i] & mask) >= prefix;
+      const uint64_t m = __ballot(take);
+      const uint32_t slot = __builtin_amdgcn_readlane(off, i) + (uint32_t)__popcll(m & lt_mask);
+      if (take && slot < (uint32_t)K) out[slot] = key[i];
+    }
+    for (int i = (int)nsel + tid; i < K; i += kFinThreads) out[i] = 0ull;
   }
-  for (int i = (int)nsel + tid; i < K; i += kFinThreads) out[i] = -1;
-  if (tid == 0) a.count_out[q] = (int32_t)nsel;
+}
+
+// the last level of one query (at most 8,192 survivor keys): its Top-K positions
+__global__ __launch_bounds__(kFinThreads) void k_topk_final(TkArgs a) {
+  __shared__ __attribute__((aligned(16))) WideLds L;
+  wide_level<kFromKeys, true>(a, blockIdx.y, 0, 1, L);
+}
+
+// Two independent wide levels in one launch: segments [0, segs_a) of task a, then
+// [segs_a, segs_a + segs_b) of task b (each workgroup runs one task's segment; both tasks
+// cover every query, grid y).  Two selection chains then share their launches.
+template <int kModeA, bool kFinalA, int kModeB, bool kFinalB>
+__global__ __launch_bounds__(kFinThreads) void k_topk_wide2(TkArgs a, int segs_a, TkArgs b, int segs_b) {
+  __shared__ __attribute__((aligned(16))) WideLds L;
+  const int x = blockIdx.x, q = blockIdx.y;
+  if (x < segs_a) wide_level<kModeA, kFinalA>(a, q, x, segs_a, L);
+  else if (x - segs_a < segs_b) wide_level<kModeB, kFinalB>(b, q, x - segs_a, segs_b, L);
+}
+
+// Launches one wide level of each of two chains (a: keys; b: keys or the first level over a
+// score array); segs 0 leaves a chain out.  Returns a csa2 status.
+int launch_wide2(const TkArgs& a, int segs_a, bool final_a, const TkArgs& b, int segs_b, bool final_b,
+                 bool b_from_scores, int n_q, hipStream_t st) {
+  const dim3 grid((unsigned)(segs_a + segs_b), (unsigned)n_q), blk(kFinThreads);
+#define CSA2_WIDE2(FA, MB, FB) hipLaunchKernelGGL((k_topk_wide2<kFromKeys, FA, MB, FB>), grid, blk, 0, st, a, segs_a, b, segs_b)
+  if (b_from_scores) {
+    if (final_a) { if (final_b) CSA2_WIDE2(true, kFromScores, true); else CSA2_WIDE2(true, kFromScores, false); }
+    else { if (final_b) CSA2_WIDE2(false, kFromScores, true); else CSA2_WIDE2(false, kFromScores, false); }
+  } else {
+    if (final_a) { if (final_b) CSA2_WIDE2(true, kFromKeys, true); else CSA2_WIDE2(true, kFromKeys, false); }
+    else { if (final_b) CSA2_WIDE2(false, kFromKeys, true); else CSA2_WIDE2(false, kFromKeys, false); }
+  }
+#undef CSA2_WIDE2
+  return csa2_check_launch();
 }
 
 // Launch the key-merging levels 1..L-1 (level 0 has written bufA); returns a csa2 status.
@@ -331,10 +413,7 @@ int select_levels_after0(const int64_t* segs, int L, TkArgs base, int n_q, uint6
     a.keys_in = (l % 2 == 1) ? bufA : bufB;
     a.keys_in_per_q = segs[l - 1] * base.k;
     a.keys_out = (l % 2 == 0) ? bufA : bufB;
-    dim3 grid((unsigned)segs[l], (unsigned)n_q), blk(kTkThreads);
-    if (final) hipLaunchKernelGGL(k_topk_final, dim3(1u, (unsigned)n_q), dim3(kFinThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_topk<kFromKeys, false>), grid, blk, 0, st, a);
-    const int rc = csa2_check_launch();
+    const int rc = launch_wide2(a, (int)segs[l], final, TkArgs{}, 0, false, false, n_q, st);
     if (rc != CSA2_OK) return rc;
   }
   return CSA2_OK;
