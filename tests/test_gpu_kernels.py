@@ -318,6 +318,51 @@ def test_index_topk_grouped_rising_scores(C):
     assert int(idx[0, 0].item()) > n // 2        # the set really sits at the rising end
 
 
+@pytest.mark.timeout(300)
+def test_index_topk_grouped_wide_offsets(C):
+    """A cache whose entry offsets within a sequence do not fit 32 bits (1,048,579 entries at
+    an entry stride of 4,160 bytes: 4.36 GB of codes), so the grouped selection takes its
+    64-bit address path: the same index sets as grouped scores followed by csa2_topk."""
+    _say("index_topk_grouped wide offsets")
+    n, pitch = (1 << 20) + 3, 4160
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    store = torch.zeros(n, pitch, dtype=torch.uint8, device="cuda")
+    k_codes = store[:, :64]
+    k_scales = torch.zeros(1, n, 4, dtype=torch.uint8, device="cuda")
+    wl = G.workloads.Workload(name="wide", seed=53, n_seq=1, seq_cap=n, m=1, heads=16, idx_heads=16,
+                              q_seq=np.zeros(8, np.int32), q_pos=np.zeros(8, np.int64),
+                              replay_start=np.zeros(8, np.int64), layers=("full",), new_entries=(0, 0))
+    for r0 in range(0, n, 1 << 16):
+        rows = min(1 << 16, n - r0)
+        lat = torch.from_numpy(wl.index_k_latents(0, r0, rows)).cuda()
+        C.csa2_quantize_kv(lat, C.FMT_MXFP4, k_codes[r0:r0 + rows], k_scales[0, r0:r0 + rows])
+    n_q = 8
+    st = Csa2Step(n_q, 16, 16, n)
+    q = torch.from_numpy(np.random.default_rng(5).standard_normal((n_q, 16, 128)).astype(np.float32)).cuda()
+    st.quantize_index_q(q)
+    w = torch.from_numpy(np.random.default_rng(6).random((n_q, 16)).astype(np.float32)).cuda()
+    q_seq_d = torch.zeros(n_q, dtype=torch.int32, device="cuda")
+    n_vis_d = torch.tensor([n, n - 5, n - 70000, 4097, n - 1, 600000, 1, n - 64], dtype=torch.int64, device="cuda")
+    codes3 = k_codes.unsqueeze(0)
+    assert codes3.stride(1) == pitch
+    ref_idx, ref_cnt = _grouped_two_call(C, st, Caches3(codes3, k_scales), w, q_seq_d, n_vis_d, 8, 512)
+    idx = torch.full((n_q, 512), -5, dtype=torch.int32, device="cuda")
+    cnt = torch.full((n_q,), -5, dtype=torch.int32, device="cuda")
+    C.csa2_index_topk_grouped(st.qi_codes, st.qi_scales, w, codes3, k_scales, q_seq_d, n_vis_d, 8, 512, idx, cnt)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt, ref_cnt) and torch.equal(idx, ref_idx)
+    assert int(cnt[6].item()) == 1 and int(idx[6, 0].item()) == 0
+    del store, k_codes, codes3
+    torch.cuda.empty_cache()
+
+
+class Caches3:
+    """The indexer-K views _grouped_two_call reads (ik_codes, ik_scales)."""
+
+    def __init__(self, ik_codes, ik_scales):
+        self.ik_codes, self.ik_scales = ik_codes, ik_scales
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 def test_index_score_pool_slots(C, fmt):
     _say("index_score pool", fmt)
