@@ -116,7 +116,7 @@ class LayerBench:
                              attn_select=attn_select, fused=fused)
         self.plan = plan_group(wl.layers, fused=fused, group=group, index_fmt=index_fmt,
                                attn_select=self.step.attn_select, pool_select=self.step.pool_select,
-                               group_select=self.step.group_select)
+                               group_select=self.step.group_select, q_in_call=self.step.q_in_call)
         torch.cuda.synchronize()   # the setup's copies and launches end here
 
     def calls(self, L: int):
@@ -142,21 +142,23 @@ class LayerBench:
         if jobs:
             out["quantize"] = C.csa2_quantize_kv_multi(jobs, _bind=True)
         nw = self.new_swa[L] if self.fuse_window else None
+        # calls named "..._q" read the unquantised indexer Q and quantise it themselves
+        qq = q_idx if any(n.endswith("_q") and n != "quantize_index_q" for n in names) else None
         if mode == "full_pool":
-            out["index_topk_pool"] = st.index_topk_build_pool(c, w, self.q_seq, self.n_vis, bind=True)
+            out["index_topk_pool"] = st.index_topk_build_pool(c, w, self.q_seq, self.n_vis, bind=True, q=qq)
         elif "index_topk_grouped" in names:   # grouped rows scored and selected, no score array
             out["index_topk_grouped"] = st.index_topk_grouped(c, w, self.q_seq, self.n_vis, bind=True)
         elif "score_grouped" in names:
             out["score"] = st.score_grouped(c, w, self.q_seq, self.n_vis, bind=True)
             out["select"] = st.select(self.n_vis, bind=True)
-        elif "index_segments" in names:
-            out["index_segments"] = st.index_segments(c, w, self.q_seq, self.n_vis, bind=True)
+        elif "index_segments" in names or "index_segments_q" in names:
+            out["index_segments"] = st.index_segments(c, w, self.q_seq, self.n_vis, bind=True, q=qq)
         elif "score_pool_q" in names:   # pool slot scores from the unquantised Q; Top-K in attention
             out["score"] = st.score_q(c, q_idx, w, self.q_seq, self.n_vis, in_pool=True, bind=True)
         elif "attend_pool_topk" in names:   # pool slot scores; the Top-K is selected in attention
             out["score"] = st.score(c, w, self.q_seq, self.n_vis, in_pool=True, bind=True)
         elif mode != "reuse":
-            out["index_topk"] = st.index_topk(c, w, self.q_seq, self.n_vis, mode == "reindex_pool", bind=True)
+            out["index_topk"] = st.index_topk(c, w, self.q_seq, self.n_vis, mode == "reindex_pool", bind=True, q=qq)
         if "attend_topk" in names:   # the last Top-K level runs inside the attention call
             out["attn"] = st.attend_topk(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True, new_win=nw)
         elif "attend_pool_topk" in names:
@@ -173,7 +175,8 @@ class LayerBench:
         mode, st = self.wl.layers[L], self.step
         if mode not in ("full", "reindex") or not 1 <= self.C.csa2_segment_keys(self.wl.seq_cap, st.k) <= 8192:
             return None
-        return st.index_segments(self.caches, self.inputs[L][1], self.q_seq, self.n_vis, bind=True)
+        return st.index_segments(self.caches, self.inputs[L][1], self.q_seq, self.n_vis, bind=True,
+                                 q=self.inputs[L][0] if st.q_in_call else None)
 
     def record(self, layers):
         """Issues the steps of `layers` on the current stream.  (Forking the appends onto

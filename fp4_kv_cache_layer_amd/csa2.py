@@ -16,6 +16,7 @@ import torch  # imported before libcsa2.so so that the process holds a single HI
 from .build import LIB_PATH
 
 FMT_NVFP4, FMT_MXFP4, FMT_FP8 = 0, 1, 2
+FMT_MXFP4_Q_F32, FMT_MXFP4_Q_BF16 = 3, 4   # MXFP4 indexer, Q given unquantised (scoring calls)
 DT_F32, DT_BF16 = 0, 1
 MAX_TOPK = 2048
 
@@ -235,24 +236,37 @@ def _cache3(t, name):
 
 
 def _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block,
-                fmt: int = FMT_MXFP4):
+                fmt: int = FMT_MXFP4, q_lat_ok: bool = True):
     """Checks the indexer operands shared by the scoring calls and returns the C arguments
     from q_codes to max_cand_blocks, and n_slots.  fmt: the indexer format (MXFP4: one scale
-    byte per 32 channels; NVFP4: one per 16)."""
+    byte per 32 channels; NVFP4: one per 16).  q_scales None (MXFP4 only, calls with
+    q_lat_ok): q_codes is the unquantised indexer Q, [n_q, H_I, 128] f32 or bf16, which the
+    call quantises itself (fmt FMT_MXFP4_Q_F32 / _BF16 at the C boundary)."""
     if fmt not in (FMT_MXFP4, FMT_NVFP4):
         raise ValueError("indexer format must be FMT_MXFP4 or FMT_NVFP4")
     scale_group = 32 if fmt == FMT_MXFP4 else 16
-    _need(q_codes, torch.uint8, 3, "q_codes")
-    _need(q_scales, torch.uint8, 3, "q_scales")
+    q_lat = q_scales is None
+    if q_lat:
+        if fmt != FMT_MXFP4 or not q_lat_ok:
+            raise ValueError("an unquantised indexer Q is taken by the MXFP4 scoring calls only")
+        if q_codes.dtype not in (torch.float32, torch.bfloat16) or q_codes.dim() != 3 or not q_codes.is_cuda or \
+                not q_codes.is_contiguous():
+            raise ValueError("unquantised indexer Q: a contiguous CUDA [n_q, H_I, 128] f32/bf16 tensor")
+        fmt = FMT_MXFP4_Q_F32 if q_codes.dtype == torch.float32 else FMT_MXFP4_Q_BF16
+        n_q, h, d = q_codes.shape
+        half = d // 2
+    else:
+        _need(q_codes, torch.uint8, 3, "q_codes")
+        _need(q_scales, torch.uint8, 3, "q_scales")
+        n_q, h, half = q_codes.shape
     _need(w, torch.float32, 2, "w")
     kc, kce, kcs = _cache3(k_codes, "k_codes")
     ks, kse, kss = _cache3(k_scales, "k_scales")
     _need(q_seq, torch.int32, 1, "q_seq")
     _need(n_vis, torch.int64, 1, "n_vis")
-    n_q, h, half = q_codes.shape
     n_seq, seq_cap, kh = k_codes.shape
     n_sc = 2 * half // scale_group
-    if q_scales.shape != (n_q, h, n_sc) or w.shape != (n_q, h) or kh != half or \
+    if (not q_lat and q_scales.shape != (n_q, h, n_sc)) or w.shape != (n_q, h) or kh != half or \
             tuple(k_scales.shape) != (n_seq, seq_cap, n_sc) or q_seq.shape[0] != n_q or n_vis.shape[0] != n_q:
         raise ValueError("index: inconsistent shapes")
     max_blocks = 0
@@ -272,7 +286,9 @@ def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scor
     """q_codes [n_q, H_I, 64], q_scales [n_q, H_I, 4 (MXFP4) | 8 (NVFP4)], w [n_q, H_I] f32;
     k_codes [n_seq, seq_cap, 64], k_scales [n_seq, seq_cap, 4 | 8] (views, entries and
     sequences possibly strided); q_seq [n_q] int32, n_vis [n_q] int64; scores [n_q, stride]
-    f32; cand_blocks [n_q, max_blocks] int32; fmt FMT_MXFP4 or FMT_NVFP4."""
+    f32; cand_blocks [n_q, max_blocks] int32; fmt FMT_MXFP4 or FMT_NVFP4.  With MXFP4,
+    q_scales None and q_codes the unquantised [n_q, H_I, 128] f32/bf16 indexer Q, the call
+    quantises Q itself (the same for csa2_index_topk, _segments and _topk_pool)."""
     args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks, block,
                           fmt)
     _need(scores, torch.float32, 2, "scores")
@@ -317,7 +333,7 @@ def csa2_index_score_grouped(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_v
                              _bind: bool = False):
     """csa2_index_score without a pool for rows in groups of `group` consecutive rows that
     share a sequence (each group's indexer K is read once); operands as csa2_index_score (MXFP4)."""
-    args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8)
+    args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8, q_lat_ok=False)
     _need(scores, torch.float32, 2, "scores")
     if scores.shape[0] != q_codes.shape[0]:
         raise ValueError("index_score_grouped: scores rows != n_q")
@@ -333,7 +349,7 @@ def csa2_index_topk_grouped(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vi
     """Grouped rows scored and selected without a score array: the operands of
     csa2_index_score_grouped -> idx_out [n_q, k] int32, count_out [n_q] int32, as
     csa2_index_score_grouped followed by csa2_topk returns them."""
-    args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8)
+    args, _ = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8, q_lat_ok=False)
     _need(idx_out, torch.int32, 2, "idx_out")
     _need(count_out, torch.int32, 1, "count_out")
     n_q = q_codes.shape[0]

@@ -172,11 +172,12 @@ struct GatherSlot {
 // kernel writes can alias them, so their uniform loads go through the scalar cache.
 //
 // kSel != 0: the index list is not given but selected here, in every workgroup of the
-// query: from the survivors of the first Top-K level (kSel 1, csa2_index_segments, 16 keys
-// per thread) or from the scores of the pool's slots (kSel 2, at most 2,048 blocks x 8 =
-// 16,384 slots, 32 keys per thread), with the same exact radix select as the Top-K levels
-// (select.h), its histograms and scratch in the LDS of the V buffers (unused until the
-// first tile), straight into the staged index list.  Workgroup (head group 0, split 0) of
+// query: from the survivors of the first Top-K level (kSel 1, csa2_index_segments, 16
+// consecutive keys per thread) or from the scores of the pool's slots (kSel 2, at most 2,048
+// blocks x 8 = 16,384 slots, 32 consecutive slots per thread), with the same exact radix
+// select as the Top-K levels (select.h; its thread-major compaction keeps the candidate
+// order), its histograms and scratch in the LDS of the V buffers (unused until the first
+// tile), straight into the staged index list.  Workgroup (head group 0, split 0) of
 // the query also writes the list and its count out for the layers that reuse it.
 constexpr int kSelMax = kAttnThreads * 16;      // 8,192 survivor keys per query at most
 constexpr int kPoolMax = kAttnThreads * 32;     // 16,384 pool slots per query at most
@@ -235,46 +236,85 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   const int n_keys = n_main * kT;
   int32_t iv[kIdxPer];
   uint64_t key[kEpt];
-  if constexpr (kSel == 1) {  // candidate i*512 + tid of the query's survivors (cand_per_q >= 1)
+  if constexpr (kSel == 1) {
+    // survivors tid*16 .. tid*16+15 of the query (cand_per_q >= 1): runs of 16 B loads where
+    // the wave's whole range is inside the list (uniform), clamped single loads otherwise
     const uint64_t* kp = a.cand_keys + (int64_t)q * a.cand_per_q;
     const int lim = a.cand_per_q;
+    const int c0 = tid * kEpt;
+    if ((wave + 1) * 64 * kEpt <= lim) {
+      typedef uint64_t u64x2 __attribute__((ext_vector_type(2), aligned(8)));
 #pragma unroll
-    for (int i = 0; i < kEpt; ++i) {
-      const int o = i * kAttnThreads + tid;
-      key[i] = kp[o < lim ? o : lim - 1] & (0ull - (uint64_t)(o < lim));
+      for (int i = 0; i < kEpt; i += 2) {
+        const u64x2 v = *reinterpret_cast<const u64x2*>(kp + c0 + i);
+        key[i] = v.x;
+        key[i + 1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        const int o = c0 + i;
+        key[i] = kp[o < lim ? o : lim - 1] & (0ull - (uint64_t)(o < lim));
+      }
     }
   } else if constexpr (kSel == 2) {
-    // pool slot c = i*512 + tid: block cand_blocks[q][c / block], position block id * block
+    // pool slot c = tid*32 + i: block cand_blocks[q][c / block], position block id * block
     // + c % block; a candidate if c lies in the query's first n_cand_blocks blocks, the block
-    // id is valid and the position visible (as the first Top-K level inside a pool)
+    // id is valid and the position visible (as the first Top-K level inside a pool).  The
+    // loads are clamped to the row (max_cand_blocks * block slots, all inside the arrays),
+    // not to the query's slot count, so they go out without waiting for n_cand_blocks; the
+    // scores come in 16 B loads where the wave's whole range is inside the row (uniform),
+    // and the slot's block and offset advance by one slot per step (one division).
+    const uint32_t blk = (uint32_t)a.block;
+    const uint32_t row_slots = (uint32_t)a.max_cand_blocks * blk;   // <= 16,384
+    const float* sp = a.pool_scores + (int64_t)q * a.pool_stride;
+    const int32_t* cb = a.cand_blocks + (int64_t)q * a.max_cand_blocks;
+    const uint32_t c0 = (uint32_t)tid * kEpt;
+    uint32_t sb[kEpt], so[kEpt];
+    {
+      uint32_t b = c0 / blk, o = c0 % blk;
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        sb[i] = b;
+        so[i] = o;
+        const bool carry = o + 1u == blk;
+        o = carry ? 0u : o + 1u;
+        b += carry ? 1u : 0u;
+      }
+    }
+    int32_t bv[kEpt];
+    float v[kEpt];
+    const uint32_t last_blk = (uint32_t)a.max_cand_blocks - 1u;
+#pragma unroll
+    for (int i = 0; i < kEpt; ++i) bv[i] = cb[sb[i] < last_blk ? sb[i] : last_blk];
+    if ((uint32_t)(wave + 1) * 64u * kEpt <= row_slots) {
+      typedef float f32x4 __attribute__((ext_vector_type(4), aligned(4)));
+#pragma unroll
+      for (int i = 0; i < kEpt; i += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sp + c0 + i);
+        v[i] = x.x;
+        v[i + 1] = x.y;
+        v[i + 2] = x.z;
+        v[i + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        const uint32_t c = c0 + (uint32_t)i;
+        v[i] = sp[c < row_slots ? c : row_slots - 1u];
+      }
+    }
     int nc = a.n_cand_blocks[q];
     nc = nc < 0 ? 0 : (nc > a.max_cand_blocks ? a.max_cand_blocks : nc);
     int64_t nv = a.n_vis[q];
     nv = nv < 0 ? 0 : (nv > a.seq_cap ? a.seq_cap : nv);
-    const uint32_t blk = (uint32_t)a.block;
     const uint32_t nslot = (uint32_t)nc * blk;   // <= 16,384
-    if (nslot > 0) {  // uniform
-      const float* sp = a.pool_scores + (int64_t)q * a.pool_stride;
-      const int32_t* cb = a.cand_blocks + (int64_t)q * a.max_cand_blocks;
-      int32_t bv[kEpt];
-      float v[kEpt];
 #pragma unroll
-      for (int i = 0; i < kEpt; ++i) {
-        uint32_t c = (uint32_t)(i * kAttnThreads + tid);
-        c = c < nslot - 1 ? c : nslot - 1;
-        bv[i] = cb[c / blk];
-        v[i] = sp[c];
-      }
-#pragma unroll
-      for (int i = 0; i < kEpt; ++i) {
-        const uint32_t c = (uint32_t)(i * kAttnThreads + tid);
-        const int64_t pos = (int64_t)bv[i] * blk + c % blk;
-        const bool ok = c < nslot && bv[i] >= 0 && pos < nv;
-        key[i] = make_key(v[i], (uint32_t)pos) & (0ull - (uint64_t)ok);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kEpt; ++i) key[i] = 0ull;
+    for (int i = 0; i < kEpt; ++i) {
+      const uint32_t c = c0 + (uint32_t)i;
+      const int64_t pos = (int64_t)bv[i] * blk + so[i];
+      const bool ok = c < nslot && bv[i] >= 0 && pos < nv;
+      key[i] = make_key(v[i], (uint32_t)pos) & (0ull - (uint64_t)ok);
     }
   } else if (n_keys > 0) {  // uniform; idx may be absent when k == 0
 #pragma unroll
@@ -392,7 +432,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     // the whole index list, s_idx[0 .. k), ascending; the tiles index it from tile_lo * 16
     __shared__ int32_t s_count;
     uint32_t* hist = reinterpret_cast<uint32_t*>(lds);
-    select_block<kAttnThreads, kEpt, true>(key, a.k, hist, nullptr, s_idx, &s_count, hist + kSelHistWords);
+    select_block<kAttnThreads, kEpt, true, kTkCopies, true>(key, a.k, hist, nullptr, s_idx, &s_count,
+                                                            hist + kSelHistWords);
     __syncthreads();
     if (hg == 0 && split == 0) {
       for (int i = tid; i < a.k; i += kAttnThreads) a.idx_out[(int64_t)q * a.k + i] = s_idx[i];

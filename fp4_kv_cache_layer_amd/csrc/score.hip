@@ -181,7 +181,9 @@ struct QueryScorer {
   int blk_lim;       // nv / block: no visible position lies in a block past this one
   int row, kb;       // A row (head) / B column (entry within tile); K-block of 32
 
-  __device__ __forceinline__ bool init(const ScoreArgs& s, int q) {
+  // with_q false: everything but the A operand and the weights, which init_q then sets
+  // (so that a kernel can issue its first K loads before the Q loads and their quantisation)
+  __device__ __forceinline__ bool init(const ScoreArgs& s, int q, bool with_q = true) {
     const int lane = threadIdx.x & 63;
     row = lane & 15;
     kb = lane >> 4;
@@ -201,6 +203,11 @@ struct QueryScorer {
     }
     kc = s.k_codes + (int64_t)seq * s.k_cs;
     ks = s.k_scales + (int64_t)seq * s.k_ss;
+    if (with_q) init_q(s, q);
+    return true;
+  }
+
+  __device__ __forceinline__ void init_q(const ScoreArgs& s, int q) {
     a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     a_scale = 127;
 #pragma unroll
@@ -259,7 +266,6 @@ struct QueryScorer {
       const int h = 4 * kb + r;
       wv[r] = h < s.n_heads ? s.w[(int64_t)q * s.n_heads + h] : 0.0f;
     }
-    return true;
   }
 
   // slot -> (row to read, valid); invalid slots read row 0 and their results are discarded,
@@ -617,7 +623,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_decode(ScoreArgs s) {
 // kBlockMax: the segment also writes the maximum visible score of each of its blocks of
 // s.block positions (the pool's block scores), read from the parked scores before the
 // selection reuses that LDS.
-template <bool kPool, bool kFinal, bool kBlockMax, bool kNv>
+template <bool kPool, bool kFinal, bool kBlockMax, bool kNv, bool kQLat = false>
 __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
   static_assert(kTkSeg >= kTkHistWords, "the score array doubles as the selection histograms");
   __shared__ __attribute__((aligned(16))) float park[kTkSeg];
@@ -627,14 +633,15 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   uint64_t key[kTkEpt];
-  QueryScorer<kPool, kNv> sc;
+  QueryScorer<kPool, kNv, kQLat> sc;
   const int c0 = seg * kTkSeg;
-  const bool seq_ok = sc.init(s, q);
+  const bool seq_ok = sc.init(s, q, false);
   // workgroup-uniform condition: every thread reaches select_segment's barriers
   if (seq_ok && sc.nv > 0 && c0 < sc.n_valid) {
     uint4 bc[4];
     int bs[4];
     sc.load_step(s, c0 + wave * kScoreStep, bc, bs);
+    sc.init_q(s, q);   // the Q operand (and, unquantised, its quantisation) while those loads fly
 #pragma unroll 2
     for (int i = 0; i < kTkEpt; ++i) {
       const int base = c0 + i * kTkThreads + wave * kScoreStep;
@@ -685,9 +692,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
                          s.count_out);
 }
 
+// CSA2_FMT_MXFP4_Q_*: an MXFP4 indexer whose Q comes unquantised
+static bool q_latent(int fmt) { return fmt == CSA2_FMT_MXFP4_Q_F32 || fmt == CSA2_FMT_MXFP4_Q_BF16; }
+
 // The indexer-K cache of a call: fmt (CSA2_FMT_MXFP4 or CSA2_FMT_NVFP4) fixes its scale row
 // (4 bytes of E8M0 or 8 of E4M3 per 128 channels; NVFP4 scales are read two bytes at a time).
 static int resolve_index_cache(int fmt, CacheRef& kr, int64_t seq_cap) {
+  if (q_latent(fmt)) fmt = CSA2_FMT_MXFP4;
   if (fmt != CSA2_FMT_MXFP4 && fmt != CSA2_FMT_NVFP4) return CSA2_ERR_UNSUPPORTED;
   if (!kr.codes || !kr.scales) return CSA2_ERR_NULL;
   if (!aligned16(kr.codes)) return CSA2_ERR_SHAPE;
@@ -700,7 +711,7 @@ static int check_score_args(const uint8_t* q_codes, const uint8_t* q_scales, con
                             int dim, int fmt, CacheRef& kr, int64_t seq_cap, int n_seq, const int32_t* q_seq,
                             const int64_t* n_vis, const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block,
                             int max_cand_blocks, int64_t* n_slots) {
-  if (!q_codes || !q_scales || !w || !q_seq || !n_vis) return CSA2_ERR_NULL;
+  if (!q_codes || (!q_scales && !q_latent(fmt)) || !w || !q_seq || !n_vis) return CSA2_ERR_NULL;
   if (n_q < 0 || n_heads < 1 || n_heads > CSA2_MAX_INDEX_HEADS || dim != CSA2_INDEX_DIM || seq_cap < 0 ||
       seq_cap > CSA2_MAX_INDEX_ENTRIES || n_seq < 1)
     return CSA2_ERR_SHAPE;
@@ -721,10 +732,15 @@ static int check_score_args(const uint8_t* q_codes, const uint8_t* q_scales, con
 static ScoreArgs make_args(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_heads,
                            const CacheRef& kr, int64_t seq_cap, int n_seq, const int32_t* q_seq, const int64_t* n_vis,
                            const int32_t* cand_blocks, const int32_t* n_cand_blocks, int block, int max_cand_blocks,
-                           int64_t n_slots) {
+                           int64_t n_slots, int fmt = CSA2_FMT_MXFP4) {
   ScoreArgs a = {};
-  a.q_codes = q_codes;
-  a.q_scales = q_scales;
+  if (q_latent(fmt)) {   // q_codes is the unquantised Q
+    a.q_lat = q_codes;
+    a.q_bf16 = fmt == CSA2_FMT_MXFP4_Q_BF16;
+  } else {
+    a.q_codes = q_codes;
+    a.q_scales = q_scales;
+  }
   a.w = w;
   a.n_heads = n_heads;
   a.k_codes = kr.codes;
@@ -766,6 +782,22 @@ static int launch_score(ScoreArgs a, int n_q, float* scores, int64_t scores_stri
   } else {
     if (a.cand_blocks) hipLaunchKernelGGL((k_score_decode<true, false>), grid, blk, 0, st, a);
     else hipLaunchKernelGGL((k_score_decode<false, false>), grid, blk, 0, st, a);
+  }
+  return csa2_check_launch();
+}
+
+// k_score_select for the indexer format of a call (NVFP4; MXFP4 with quantised or
+// unquantised Q); the pool build (kBlockMax) exists for MXFP4 only
+template <bool kFinal, bool kBlockMax>
+static int launch_score_select(int fmt, dim3 grid, hipStream_t st, const ScoreArgs& a) {
+  const dim3 blk(kScoreThreads);
+  if (q_latent(fmt)) {
+    hipLaunchKernelGGL((k_score_select<false, kFinal, kBlockMax, false, true>), grid, blk, 0, st, a);
+  } else if (fmt == CSA2_FMT_NVFP4) {
+    if constexpr (kBlockMax) return CSA2_ERR_UNSUPPORTED;
+    else hipLaunchKernelGGL((k_score_select<false, kFinal, false, true>), grid, blk, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_score_select<false, kFinal, kBlockMax, false>), grid, blk, 0, st, a);
   }
   return csa2_check_launch();
 }
@@ -825,8 +857,8 @@ extern "C" int csa2_index_score(const uint8_t* q_codes, const uint8_t* q_scales,
   if (scores_stride < n_slots) return CSA2_ERR_SHAPE;
   if (n_q == 0 || n_slots == 0) return CSA2_OK;
   ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, cand_blocks, n_cand_blocks,
-                          block, max_cand_blocks, n_slots);
-  return launch_score(a, n_q, scores, scores_stride, fmt == CSA2_FMT_NVFP4, (hipStream_t)stream);
+                          block, max_cand_blocks, n_slots, fmt);
+  return launch_score(a, n_q, scores, scores_stride, fmt == CSA2_FMT_NVFP4, (hipStream_t)stream, q_latent(fmt));
 }
 
 extern "C" int csa2_index_score_q(const void* q, int q_dtype, const float* w, int n_q, int n_heads, int dim,
@@ -915,8 +947,8 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
     float* sc = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
     const size_t sc_bytes = ((size_t)n_q * n0 * sizeof(float) + 255) & ~(size_t)255;
     ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, cand_blocks,
-                            n_cand_blocks, block, max_cand_blocks, n_slots);
-    rc = launch_score(a, n_q, sc, n0, nv, st);
+                            n_cand_blocks, block, max_cand_blocks, n_slots, fmt);
+    rc = launch_score(a, n_q, sc, n0, nv, st, q_latent(fmt));
     if (rc != CSA2_OK) return rc;
     TkArgs t = {};
     t.scores = sc;
@@ -937,20 +969,13 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
   uint64_t* bufA = (uint64_t*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   uint64_t* bufB = bufA + (size_t)k * n_q * segs[0];
   ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, cand_blocks, n_cand_blocks,
-                          block, max_cand_blocks, n_slots);
+                          block, max_cand_blocks, n_slots, fmt);
   a.k = k;
   a.keys_out = bufA;
   a.idx_out = idx_out;
   a.count_out = count_out;
-  dim3 grid((unsigned)segs[0], (unsigned)n_q), blk(kScoreThreads);
-  if (nv) {
-    if (L == 1) hipLaunchKernelGGL((k_score_select<false, true, false, true>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((k_score_select<false, false, false, true>), grid, blk, 0, st, a);
-  } else {
-    if (L == 1) hipLaunchKernelGGL((k_score_select<false, true, false, false>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((k_score_select<false, false, false, false>), grid, blk, 0, st, a);
-  }
-  rc = csa2_check_launch();
+  const dim3 grid((unsigned)segs[0], (unsigned)n_q);
+  rc = L == 1 ? launch_score_select<true, false>(fmt, grid, st, a) : launch_score_select<false, false>(fmt, grid, st, a);
   if (rc != CSA2_OK) return rc;
   TkArgs t = {};
   t.n_vis = n_vis;
@@ -984,14 +1009,10 @@ extern "C" int csa2_index_segments(const uint8_t* q_codes, const uint8_t* q_scal
   if (n_q == 0) return CSA2_OK;
   const int64_t n_seg = csa2_segment_keys(n_slots, k) / k;
   ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, nullptr, nullptr, 8, 1,
-                          n_slots);
+                          n_slots, fmt);
   a.k = k;
   a.keys_out = cand_keys;
-  dim3 grid((unsigned)n_seg, (unsigned)n_q), blk(kScoreThreads);
-  hipStream_t st = (hipStream_t)stream;
-  if (fmt == CSA2_FMT_NVFP4) hipLaunchKernelGGL((k_score_select<false, false, false, true>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((k_score_select<false, false, false, false>), grid, blk, 0, st, a);
-  return csa2_check_launch();
+  return launch_score_select<false, false>(fmt, dim3((unsigned)n_seg, (unsigned)n_q), (hipStream_t)stream, a);
 }
 
 // ---- csa2_index_topk_grouped: grouped rows, scored and selected without a score array ----
@@ -1064,7 +1085,7 @@ extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_sca
                                     int32_t* count_out, int block, int max_blocks, int32_t* blocks_out,
                                     int32_t* blocks_count, void* workspace, size_t workspace_bytes, void* stream) {
   if (int rc_status = csa2_take_device_status()) return rc_status;
-  if (fmt != CSA2_FMT_MXFP4) return CSA2_ERR_UNSUPPORTED;
+  if (fmt != CSA2_FMT_MXFP4 && !q_latent(fmt)) return CSA2_ERR_UNSUPPORTED;
   CacheRef kr = CSA2_INDEX_CACHE_REF;
   int64_t n_slots = 0;
   int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, fmt, kr, seq_cap, n_seq, q_seq, n_vis, nullptr,
@@ -1091,7 +1112,7 @@ extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_sca
   const int64_t nblk = (n0 + block - 1) / block;
 
   ScoreArgs a = make_args(q_codes, q_scales, w, n_heads, kr, seq_cap, n_seq, q_seq, n_vis, nullptr, nullptr, block, 0,
-                          n_slots);
+                          n_slots, fmt);
   a.k = k;
   a.keys_out = bufA;
   a.idx_out = idx_out;
@@ -1099,10 +1120,8 @@ extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_sca
   a.bmax = bmax;
   a.bmax_stride = nblk;
   hipStream_t st = (hipStream_t)stream;
-  dim3 grid((unsigned)segs[0], (unsigned)n_q), blk(kScoreThreads);
-  if (L == 1) hipLaunchKernelGGL((k_score_select<false, true, true, false>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((k_score_select<false, false, true, false>), grid, blk, 0, st, a);
-  rc = csa2_check_launch();
+  const dim3 grid((unsigned)segs[0], (unsigned)n_q);
+  rc = L == 1 ? launch_score_select<true, true>(fmt, grid, st, a) : launch_score_select<false, true>(fmt, grid, st, a);
   if (rc != CSA2_OK) return rc;
   TkArgs t = {};
   t.n_vis = n_vis;

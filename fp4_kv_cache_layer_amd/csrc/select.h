@@ -70,6 +70,16 @@ __device__ __forceinline__ uint32_t dpp_prefix_sum(uint32_t v) {
 }
 
 
+// A lower bound of the high word of a block's K-th largest key from one thread's largest
+// (h1) and second largest (h2) high word of its keys (0 when it holds fewer than one or two
+// keys): if every one of kThreads threads holds a key whose high word is at least b, at
+// least kThreads keys are >= (b << 32), so the minimum of h1 over the block bounds the K-th
+// largest key's high word from below when kThreads >= K, and the minimum of h2 does when
+// 2 * kThreads >= K.  Returns this thread's share of that minimum (0: no bound).
+__device__ __forceinline__ uint32_t prune_bound(uint32_t h1, uint32_t h2, int K, int threads) {
+  return K <= threads ? h1 : (K <= 2 * threads ? h2 : 0u);
+}
+
 // Selects the K largest of the kEpt*kThreads keys held by a kThreads-thread workgroup (key[i]
 // of thread t is candidate i*kThreads + t of the block; 0 = no candidate) and writes them
 // in candidate order: non-final levels write the keys to keys_out[0 .. K), zero padded;
@@ -91,13 +101,16 @@ constexpr int kTkHistWords = 2 * kTkWaves * 256 * kTkCopies;
 // are exactly the keys >= T (T = 0 when at most K keys are present, all of them kept), and
 // any key < T ranks below all K of them.  kCopies (1 or kTkCopies) sets the histogram
 // copies per wave: `hist` then holds 2 * (kThreads / 64) * 256 * kCopies words.
-template <int kThreads, int kEpt, bool kFinal, int kCopies = kTkCopies>
+// kThreadMajor: key[i] of thread t is candidate t*kEpt + i instead (each thread holds a run
+// of consecutive candidates), and the output follows that candidate order.
+template <int kThreads, int kEpt, bool kFinal, int kCopies = kTkCopies, bool kThreadMajor = false>
 __device__ __forceinline__ uint64_t select_block(uint64_t (&key)[kEpt], int K, uint32_t* hist,
                                                  uint64_t* __restrict__ keys_out, int32_t* __restrict__ idx_out,
                                                  int32_t* __restrict__ count_out, uint32_t* scratch = nullptr) {
   static_assert(kCopies == 1 || kCopies == kTkCopies, "one or four histogram copies");
   constexpr int kWaves = kThreads / 64;
   static_assert(kEpt <= 64 && kThreads % 64 == 0, "one lane per slot in the compaction scan");
+  static_assert(!kThreadMajor || kEpt <= 32, "a thread's survivors as bits of one word");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   uint32_t (*cnt)[kEpt];
@@ -107,19 +120,22 @@ __device__ __forceinline__ uint64_t select_block(uint64_t (&key)[kEpt], int K, u
   } else {
     cnt = reinterpret_cast<uint32_t(*)[kEpt]>(scratch + (kWaves / 4) * 256);
   }
-  __shared__ uint32_t red[5][kWaves];
+  __shared__ uint32_t red[6][kWaves];
 
-  // ---- count (ballots) and the range of the high (score) words (DPP reductions) ----
-  uint32_t nw = 0, hmax = 0u, hmin = ~0u, lmax = 0u, lmin = ~0u;
+  // ---- count (ballots), the range of the high (score) words (DPP reductions) and a lower
+  // bound of the K-th largest key's high word (prune_bound) ----
+  uint32_t nw = 0, hmax = 0u, hmin = ~0u, lmax = 0u, lmin = ~0u, h2 = 0u;
 #pragma unroll
   for (int i = 0; i < kEpt; ++i) {
     nw += (uint32_t)__popcll(__ballot(key[i] != 0ull));
     const uint32_t h = (uint32_t)(key[i] >> 32), l = (uint32_t)key[i];
+    h2 = key[i] ? max(h2, min(hmax, h)) : h2;
     hmax = key[i] ? max(hmax, h) : hmax;
     hmin = key[i] ? min(hmin, h) : hmin;
     lmax = key[i] ? max(lmax, l) : lmax;
     lmin = key[i] ? min(lmin, l) : lmin;
   }
+  const uint32_t tb = dpp_min_u32(prune_bound(hmax, h2, K, kThreads));
   hmax = dpp_max_u32(hmax);
   hmin = dpp_min_u32(hmin);
   lmax = dpp_max_u32(lmax);
@@ -130,9 +146,10 @@ __device__ __forceinline__ uint64_t select_block(uint64_t (&key)[kEpt], int K, u
     red[2][wave] = hmin;
     red[3][wave] = lmax;
     red[4][wave] = lmin;
+    red[5][wave] = tb;
   }
   __syncthreads();
-  uint32_t n = 0;
+  uint32_t n = 0, tmin = ~0u;
   hmax = 0u;
   hmin = ~0u;
 #pragma unroll
@@ -140,18 +157,25 @@ __device__ __forceinline__ uint64_t select_block(uint64_t (&key)[kEpt], int K, u
     n += red[0][wv];
     hmax = max(hmax, red[1][wv]);
     hmin = min(hmin, red[2][wv]);
+    tmin = min(tmin, red[5][wv]);
   }
 
   // ---- radix select: find (prefix, mask) such that exactly K keys have (key&mask) >= prefix ----
   uint64_t prefix = 0, mask = 0;
   if (n > (uint32_t)K) {
+    // keys below the bound rank below the K-th: drop them before the first count
+    if (tmin > hmin) {
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) key[i] = (uint32_t)(key[i] >> 32) >= tmin ? key[i] : 0ull;
+      hmin = tmin;
+    }
     int hb;        // highest bit where the largest and smallest key differ
     uint64_t top;  // the largest key's bits above hb
     if (hmax != hmin) {
       hb = 32 + 31 - __clz(hmax ^ hmin);
       top = (uint64_t)hmax << 32;
-    } else {       // every score equal: the keys differ in their position words only
-      lmax = 0u;
+    } else {       // every remaining score equal: the keys differ in their position words
+      lmax = 0u;     // only (whose range over all keys covers those that remain)
       lmin = ~0u;
 #pragma unroll
       for (int wv = 0; wv < kWaves; ++wv) {
@@ -257,6 +281,48 @@ __device__ __forceinline__ uint64_t select_block(uint64_t (&key)[kEpt], int K, u
       if (inbin == need || shift == 0) break;
       shift = shift - 8 > 0 ? shift - 8 : 0;
     }
+  }
+
+  if constexpr (kThreadMajor) {
+    // ---- stable compaction in candidate order (thread-major): each thread's survivors
+    // after those of the threads before it (a DPP prefix sum in the wave, the waves' totals
+    // through LDS), written one after another ----
+    uint32_t takes = 0u;
+#pragma unroll
+    for (int i = 0; i < kEpt; ++i) takes |= (key[i] && (key[i] & mask) >= prefix) ? 1u << i : 0u;
+    const uint32_t mine = (uint32_t)__builtin_popcount(takes);
+    const uint32_t incl = dpp_prefix_sum(mine);
+    if (lane == 63) cnt[wave][0] = incl;
+    __syncthreads();
+    uint32_t slot = incl - mine, total = 0u;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) {
+      const uint32_t c = cnt[wv][0];
+      total += c;
+      slot += wv < wave ? c : 0u;
+    }
+    const uint32_t nsel = total < (uint32_t)K ? total : (uint32_t)K;
+    if constexpr (!kFinal) {
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        if ((takes >> i) & 1u) {
+          if (slot < (uint32_t)K) keys_out[slot] = key[i];
+          ++slot;
+        }
+      }
+      for (int i = (int)nsel + tid; i < K; i += kThreads) keys_out[i] = 0ull;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        if ((takes >> i) & 1u) {
+          if (slot < (uint32_t)K) idx_out[slot] = key_pos(key[i]);
+          ++slot;
+        }
+      }
+      for (int i = (int)nsel + tid; i < K; i += kThreads) idx_out[i] = -1;
+      if (tid == 0) *count_out = (int32_t)nsel;
+    }
+    return prefix;
   }
 
   // ---- stable compaction in candidate order (i-major, then thread) ----

@@ -153,7 +153,7 @@ constexpr int kFinEpt = kTkSeg / kFinThreads;   // 8
 struct WideLds {
   uint32_t hist[kFinWaves][256];
   uint32_t part[4][256];
-  uint32_t red[3][kFinWaves];
+  uint32_t red[4][kFinWaves];
   uint32_t cnt[kFinWaves][kFinEpt];
 };
 
@@ -205,24 +205,28 @@ __device__ __forceinline__ void wide_level(const TkArgs& a, int q, int seg, int 
     }
   }
 
-  // ---- count and the range of the high (score) words ----
-  uint32_t nw = 0, hmax = 0u, hmin = ~0u;
+  // ---- count, the range of the high (score) words and a lower bound of the K-th largest
+  // key's high word (prune_bound) ----
+  uint32_t nw = 0, hmax = 0u, hmin = ~0u, h2 = 0u;
 #pragma unroll
   for (int i = 0; i < kFinEpt; ++i) {
     nw += (uint32_t)__popcll(__ballot(key[i] != 0ull));
     const uint32_t h = (uint32_t)(key[i] >> 32);
+    h2 = key[i] ? max(h2, min(hmax, h)) : h2;
     hmax = key[i] ? max(hmax, h) : hmax;
     hmin = key[i] ? min(hmin, h) : hmin;
   }
+  const uint32_t tb = dpp_min_u32(prune_bound(hmax, h2, K, kFinThreads));
   hmax = dpp_max_u32(hmax);
   hmin = dpp_min_u32(hmin);
   if (lane == 0) {
     L.red[0][wave] = nw;
     L.red[1][wave] = hmax;
     L.red[2][wave] = hmin;
+    L.red[3][wave] = tb;
   }
   __syncthreads();
-  uint32_t n = 0;
+  uint32_t n = 0, tmin = ~0u;
   hmax = 0u;
   hmin = ~0u;
 #pragma unroll
@@ -230,17 +234,24 @@ __device__ __forceinline__ void wide_level(const TkArgs& a, int q, int seg, int 
     n += L.red[0][w];
     hmax = max(hmax, L.red[1][w]);
     hmin = min(hmin, L.red[2][w]);
+    tmin = min(tmin, L.red[3][w]);
   }
 
   // ---- radix select: (prefix, mask) such that exactly K keys have (key & mask) >= prefix ----
   uint64_t prefix = 0, mask = 0;
   if (n > (uint32_t)K) {
+    // keys below the bound rank below the K-th: drop them before the first count
+    if (tmin > hmin) {
+#pragma unroll
+      for (int i = 0; i < kFinEpt; ++i) key[i] = (uint32_t)(key[i] >> 32) >= tmin ? key[i] : 0ull;
+      hmin = tmin;
+    }
     int hb;        // highest bit where the largest and smallest key differ
     uint64_t top;  // the largest key's bits above hb
     if (hmax != hmin) {
       hb = 32 + 31 - __clz(hmax ^ hmin);
       top = (uint64_t)hmax << 32;
-    } else {       // every score equal: the keys differ in their position words only
+    } else {       // every remaining score equal: the keys differ in their position words only
       uint32_t lmax = 0u, lmin = ~0u;
 #pragma unroll
       for (int i = 0; i < kFinEpt; ++i) {

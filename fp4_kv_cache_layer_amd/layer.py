@@ -31,7 +31,7 @@ INDEX_FORMATS = {"mxfp4": (C.FMT_MXFP4, 32), "nvfp4": (C.FMT_NVFP4, 16)}
 
 
 def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp4",
-               attn_select: bool = False, pool_select=None, group_select: bool = True) -> list:
+               attn_select: bool = False, pool_select=None, group_select: bool = True, q_in_call=None) -> list:
     """Checks a layer group's mode sequence and returns the calls each layer makes.
 
     [W] "CSA2：跨层复用，能借就不自己算" and Figure 4: a Reindex layer re-scores the KV of the
@@ -52,11 +52,20 @@ def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp
     scores and select inside their attention call (csa2_sparse_attn_pool_topk).  With the
     MXFP4 indexer those slot scores come from csa2_index_score_q, which quantises the
     layer's indexer Q itself, so such a layer (which appends nothing) makes no quantise
-    call."""
+    call.  q_in_call (default: MXFP4 indexer, group 1): the scoring call of every Reindex
+    layer (which appends nothing) reads the unquantised indexer Q and quantises it itself
+    (the call names end in "_q"), so such a layer makes no quantise launch; a Full layer
+    keeps its quantise launch, which also carries the step's appends of new entries (one
+    launch either way, and a quantised Q keeps the scoring kernel's prologue short).
+    Grouped scoring takes quantised Q only."""
     if index_fmt not in INDEX_FORMATS:
         raise ValueError(f"unknown indexer format {index_fmt!r}")
     if index_fmt != "mxfp4" and group > 1:
         raise ValueError("grouped scoring reads an MXFP4 indexer only")
+    if q_in_call is None:
+        q_in_call = index_fmt == "mxfp4" and group == 1
+    if q_in_call and (index_fmt != "mxfp4" or group > 1):
+        raise ValueError("an unquantised indexer Q is read by the ungrouped MXFP4 scoring calls only")
     plan, have_kv, have_pool = [], False, False
     for i, m in enumerate(modes):
         if m not in MODES:
@@ -86,6 +95,8 @@ def plan_group(modes, fused: bool = True, group: int = 1, index_fmt: str = "mxfp
             pool = m == "reindex_pool"
             calls = ["quantize_index_q", "score_pool" if pool else "score", "select_pool" if pool else "select",
                      "attend"]
+        if q_in_call and m.startswith("reindex") and calls[0] == "quantize_index_q":
+            calls = [c + "_q" if c.startswith(("score", "index_")) and not c.endswith("_q") else c for c in calls[1:]]
         plan.append(calls)
     return plan
 
@@ -151,6 +162,8 @@ class Csa2Step:
         # the grouped scores and the Top-K levels
         self.group_select = fused and group > 1 and (n_q + group - 1) // group >= 128
         self.index_fmt = index_fmt
+        # Reindex layers' scoring calls quantise the indexer Q themselves (no quantise launch)
+        self.q_in_call = index_fmt == "mxfp4" and group == 1
         self.idx_qfmt, self.idx_group = INDEX_FORMATS[index_fmt]
         self.n_q, self.n_heads, self.idx_heads = n_q, n_heads, idx_heads
         self.fused, self.group = fused, group
@@ -191,6 +204,11 @@ class Csa2Step:
         return C.csa2_quantize_kv(q_f32.view(n_q * h, d), self.idx_qfmt, self.qi_codes.view(n_q * h, d // 2),
                                   self.qi_scales.view(n_q * h, d // self.idx_group), _bind=bind)
 
+    def _q(self, q):
+        """The indexer-Q operands of a scoring call: the step's quantised Q, or (q given)
+        the unquantised Q, which the call quantises itself."""
+        return (self.qi_codes, self.qi_scales) if q is None else (q, None)
+
     def score(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False):
         if in_pool:
             return C.csa2_index_score(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
@@ -229,23 +247,24 @@ class Csa2Step:
                                self.pool, self.pool_count, self.block, _bind=bind)
         return C.csa2_topk(self.scores, n_vis, self.seq_cap, self.k, self.idx, self.count, self.ws_topk, _bind=bind)
 
-    def index_topk(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False):
-        """score + select in one pass, without the score array."""
+    def index_topk(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False, q=None):
+        """score + select in one pass, without the score array.  q: the unquantised indexer Q
+        (MXFP4: the call quantises it), else the step's quantised Q (as for the calls below)."""
         pool = (self.pool, self.pool_count) if in_pool else (None, None)
-        return C.csa2_index_topk(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
+        return C.csa2_index_topk(*self._q(q), w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
                                  self.k, self.idx, self.count, self.ws_index_topk, pool[0], pool[1], self.block,
                                  fmt=self.idx_qfmt, _bind=bind)
 
-    def index_topk_build_pool(self, caches: Caches, w, q_seq, n_vis, bind=False):
+    def index_topk_build_pool(self, caches: Caches, w, q_seq, n_vis, bind=False, q=None):
         """score + select + pool in one pass (the decoder's first Full layer)."""
         self._mx_only("the fused pool build")
-        return C.csa2_index_topk_pool(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq,
+        return C.csa2_index_topk_pool(*self._q(q), w, caches.ik_codes, caches.ik_scales, q_seq,
                                       n_vis, self.k, self.idx, self.count, self.pool, self.pool_count, self.block,
                                       self.ws_index_topk_pool, _bind=bind)
 
-    def index_segments(self, caches: Caches, w, q_seq, n_vis, bind=False):
+    def index_segments(self, caches: Caches, w, q_seq, n_vis, bind=False, q=None):
         """the first Top-K level alone (its survivors feed attend_topk)."""
-        return C.csa2_index_segments(self.qi_codes, self.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
+        return C.csa2_index_segments(*self._q(q), w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
                                      self.k, self.cand_keys, fmt=self.idx_qfmt, _bind=bind)
 
     def attend_topk(self, caches: Caches, layer: int, q_attn, q_seq, q_pos, replay_start, out=None, lse=None,
@@ -268,9 +287,11 @@ class Csa2Step:
                                             self.lse if lse is None else lse, self.ws_attn, new_win=new_win,
                                             _bind=bind)
 
-    def _score_select(self, caches, w, q_seq, n_vis, in_pool, bind):
+    def _score_select(self, caches, w, q_seq, n_vis, in_pool, bind, q=None):
         if self.fused:
-            return [self.index_topk(caches, w, q_seq, n_vis, in_pool, bind)]
+            return [self.index_topk(caches, w, q_seq, n_vis, in_pool, bind, q)]
+        if q is not None:
+            return [self.score_q(caches, q, w, q_seq, n_vis, in_pool, bind), self.select(n_vis, in_pool, bind)]
         return [self.score(caches, w, q_seq, n_vis, in_pool, bind), self.select(n_vis, in_pool, bind)]
 
     def build_pool(self, n_vis, bind=False):
@@ -296,7 +317,7 @@ class Csa2Step:
         call (see attend).  With bind=True returns the group's calls as one flat list of
         callables."""
         plan = plan_group(modes, self.fused, self.group, self.index_fmt, self.attn_select,
-                          pool_select=self.pool_select, group_select=self.group_select)
+                          pool_select=self.pool_select, group_select=self.group_select, q_in_call=self.q_in_call)
         calls = []
         for i, (m, names) in enumerate(zip(modes, plan)):
             q_index, w, q_attn = inputs[i]
@@ -304,26 +325,29 @@ class Csa2Step:
             lse = None if lses is None else lses[i]
             nw = None if new_wins is None else new_wins[i]
             for name in names:
+                # "_q": the scoring call reads the unquantised indexer Q itself
+                qq = q_index if name.endswith("_q") else None
+                base = name[:-2] if qq is not None else name
                 if name == "quantize_index_q":
                     c = self.quantize_index_q(q_index, bind)
-                elif name == "index_topk_pool":
-                    c = self.index_topk_build_pool(caches, w, q_seq, n_vis, bind)
-                elif name in ("index_topk", "index_topk_in_pool"):
-                    c = self.index_topk(caches, w, q_seq, n_vis, name.endswith("in_pool"), bind)
+                elif base == "index_topk_pool":
+                    c = self.index_topk_build_pool(caches, w, q_seq, n_vis, bind, q=qq)
+                elif base in ("index_topk", "index_topk_in_pool"):
+                    c = self.index_topk(caches, w, q_seq, n_vis, base.endswith("in_pool"), bind, q=qq)
                 elif name == "score_grouped":
                     c = self.score_grouped(caches, w, q_seq, n_vis, bind)
                 elif name == "index_topk_grouped":
                     c = self.index_topk_grouped(caches, w, q_seq, n_vis, bind)
                 elif name in ("score", "score_pool"):
                     c = self.score(caches, w, q_seq, n_vis, name.endswith("pool"), bind)
-                elif name == "score_pool_q":
-                    c = self.score_q(caches, q_index, w, q_seq, n_vis, True, bind)
+                elif name in ("score_q", "score_pool_q"):
+                    c = self.score_q(caches, q_index, w, q_seq, n_vis, name == "score_pool_q", bind)
                 elif name in ("select", "select_pool"):
                     c = self.select(n_vis, name.endswith("pool"), bind)
                 elif name == "build_pool":
                     c = self.build_pool(n_vis, bind)
-                elif name == "index_segments":
-                    c = self.index_segments(caches, w, q_seq, n_vis, bind)
+                elif base == "index_segments":
+                    c = self.index_segments(caches, w, q_seq, n_vis, bind, q=qq)
                 elif name == "attend_topk":
                     c = self.attend_topk(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind, new_win=nw)
                 elif name == "attend_pool_topk":
@@ -341,26 +365,30 @@ class Csa2Step:
 
     def full(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, make_pool=False,
              out=None, lse=None, bind=False):
+        q = None   # a Full layer's quantise launch also carries the step's appends (plan_group)
         calls = [self.quantize_index_q(q_index_f32, bind)]
         if make_pool and self.fused and self.index_fmt == "mxfp4":
-            calls.append(self.index_topk_build_pool(caches, w, q_seq, n_vis, bind))
+            calls.append(self.index_topk_build_pool(caches, w, q_seq, n_vis, bind, q=q))
         elif make_pool:
-            calls += [self.score(caches, w, q_seq, n_vis, bind=bind), self.select(n_vis, bind=bind),
-                      self.build_pool(n_vis, bind)]
+            calls += [self.score(caches, w, q_seq, n_vis, bind=bind) if q is None else
+                      self.score_q(caches, q, w, q_seq, n_vis, bind=bind),
+                      self.select(n_vis, bind=bind), self.build_pool(n_vis, bind)]
         elif self.attn_select:
-            calls += [self.index_segments(caches, w, q_seq, n_vis, bind),
+            calls += [self.index_segments(caches, w, q_seq, n_vis, bind, q=q),
                       self.attend_topk(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
             return self._seq(calls, bind)
         else:
-            calls += self._score_select(caches, w, q_seq, n_vis, False, bind)
+            calls += self._score_select(caches, w, q_seq, n_vis, False, bind, q)
         calls.append(self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind))
         return self._seq(calls, bind)
 
     def reindex(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, in_pool=False,
                 out=None, lse=None, bind=False):
+        q = q_index_f32 if self.q_in_call else None
+        quant = [] if q is not None else [self.quantize_index_q(q_index_f32, bind)]
         if self.attn_select and not in_pool:
-            calls = [self.quantize_index_q(q_index_f32, bind), self.index_segments(caches, w, q_seq, n_vis, bind),
-                     self.attend_topk(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
+            calls = quant + [self.index_segments(caches, w, q_seq, n_vis, bind, q=q),
+                             self.attend_topk(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
             return self._seq(calls, bind)
         if self.pool_select and in_pool:
             if self.index_fmt == "mxfp4":
@@ -370,8 +398,8 @@ class Csa2Step:
             calls.append(self.attend_pool_topk(caches, layer, q_attn, q_seq, n_vis, q_pos, replay_start, out, lse,
                                                bind))
             return self._seq(calls, bind)
-        calls = [self.quantize_index_q(q_index_f32, bind), *self._score_select(caches, w, q_seq, n_vis, in_pool, bind),
-                 self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
+        calls = quant + [*self._score_select(caches, w, q_seq, n_vis, in_pool, bind, q),
+                         self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
         return self._seq(calls, bind)
 
     def reuse(self, caches, layer, q_attn, q_seq, q_pos, replay_start, out=None, lse=None, bind=False):

@@ -90,6 +90,15 @@ extern "C" {
 #define CSA2_FMT_MXFP4 1  /* indexer Q/K: E2M1 + one E8M0 scale per 32 channels ([MX];
                              [W] "FP4 与 SWA Bounded Replay": indexer Q/K in FP4) */
 #define CSA2_FMT_FP8 2    /* sliding-window KV: unscaled E4M3 ([J] "缓存压缩真的是越大越好吗") */
+/* fmt of the indexer scoring calls that take it (csa2_index_score, csa2_index_topk,
+   csa2_index_segments, csa2_index_topk_pool): the indexer K in MXFP4 and the indexer Q
+   given unquantised, [n_q, n_heads, 128] f32 or bf16 in q_codes (16-byte aligned, finite;
+   q_scales unused, may be NULL); every workgroup quantises its query's Q to MXFP4 itself by
+   the csa2_quantize_kv rule, so the results equal csa2_quantize_kv (CSA2_FMT_MXFP4) followed
+   by the same call with CSA2_FMT_MXFP4 on its codes, and a layer step needs no quantise
+   launch before scoring ([W] "FP4 与 SWA Bounded Replay": indexer Q in FP4) */
+#define CSA2_FMT_MXFP4_Q_F32 3
+#define CSA2_FMT_MXFP4_Q_BF16 4
 
 /* ---- element types of dense inputs / outputs ---- */
 #define CSA2_DT_F32 0
@@ -201,8 +210,11 @@ int csa2_quantize_kv_multi(const csa2_quant_job* jobs, int n_jobs, void* stream)
  *
  *   fmt               the indexer format of Q and K: CSA2_FMT_MXFP4 (E8M0 per 32 channels,
  *                     the scaled FP4 matrix-core path) or CSA2_FMT_NVFP4 (E4M3 per 16
- *                     channels, as the main KV; dequantised exactly to fp16 matrix cores)
+ *                     channels, as the main KV; dequantised exactly to fp16 matrix cores);
+ *                     CSA2_FMT_MXFP4_Q_F32 / _Q_BF16: MXFP4 with Q given unquantised
  *   q_codes/q_scales  [n_q, n_heads, dim/2] / [n_q, n_heads, dim/32 (MXFP4) or dim/16]
+ *                     (q_codes 16-byte aligned); with CSA2_FMT_MXFP4_Q_*: q_codes the
+ *                     [n_q, n_heads, dim] f32 / bf16 Q, q_scales unused
  *   w                 [n_q, n_heads] f32
  *   n_heads           1..16;  dim == 128
  *   k_codes, k_scales and their strides   the indexer-K cache (see Cache layouts)
@@ -374,8 +386,8 @@ int64_t csa2_segment_keys(int64_t n_slots, int k);
  * Top-K survivors.  A query whose q_seq is outside [0, n_seq) gets count 0 and a pool of
  * its lowest visible block ids (all their scores are -inf).
  *   Workspace: csa2_index_topk_pool_workspace_bytes(n_q, seq_cap, k, block, max_blocks).
- * fmt must be CSA2_FMT_MXFP4.  Errors: as csa2_index_topk; CSA2_ERR_SHAPE for block or
- * max_blocks out of range; CSA2_ERR_UNSUPPORTED for another fmt.
+ * fmt must be CSA2_FMT_MXFP4 or CSA2_FMT_MXFP4_Q_F32 / _Q_BF16.  Errors: as csa2_index_topk;
+ * CSA2_ERR_SHAPE for block or max_blocks out of range; CSA2_ERR_UNSUPPORTED for another fmt.
  */
 int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
                          int n_heads, int dim, int fmt, const uint8_t* k_codes,

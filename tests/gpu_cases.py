@@ -216,7 +216,7 @@ def run_group_snapshots(case: Case, step, caches, window_appends: bool = False, 
     snaps, at = [], 0
     # the calls of each layer as the step plans them (the flat list is cut by these counts)
     plan = plan_group(modes, step.fused, step.group, step.index_fmt, step.attn_select, pool_select=step.pool_select,
-                      group_select=step.group_select)
+                      group_select=step.group_select, q_in_call=step.q_in_call)
     assert sum(len(n) for n in plan) == len(calls)
     for L, names in enumerate(plan):
         if window_appends:

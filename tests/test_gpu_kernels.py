@@ -448,6 +448,68 @@ def test_index_score_q_matches_quantize_then_score(C, pool, q_dt, heads):
             assert torch.equal(st.scores[qi, :nv], ref[qi, :nv])
 
 
+@pytest.mark.parametrize("q_dt,heads", [("f32", 16), ("bf16", 16), ("f32", 5)])
+def test_scoring_calls_take_unquantised_q(C, q_dt, heads):
+    """The fused scoring calls with the indexer Q given unquantised (fmt CSA2_FMT_MXFP4_Q_F32
+    / _BF16 at the boundary: q_codes the f32 / bf16 Q, q_scales None) return exactly what
+    csa2_quantize_kv (MXFP4) followed by the same call on its codes returns: csa2_index_score,
+    csa2_index_topk (all visible entries and inside a pool), csa2_index_segments (its keys)
+    and csa2_index_topk_pool (Top-K and pool).  The quantised-Q calls are pinned to the oracle
+    by the tests above and below."""
+    _say("unquantised Q", q_dt, heads)
+    case = _score_case(41 + heads, 2, 20000, [20000, 17001, 333], heads)
+    wl = case.wl
+    caches = case.gpu_caches()
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq, n_vis, _, _ = case.gpu_meta()
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    k = 512
+    st = Csa2Step(wl.n_q, 16, heads, wl.seq_cap, max_blocks=300)
+    rng = np.random.default_rng(9)
+    blocks = np.full((wl.n_q, 300), -1, np.int32)
+    ncb = np.array([300, 250, 40], np.int32)
+    for qi in range(wl.n_q):
+        nb = -(-int(wl.n_vis[qi]) // 8)
+        blocks[qi, :ncb[qi]] = np.sort(rng.choice(nb, size=ncb[qi], replace=False))
+    st.pool.copy_(torch.from_numpy(blocks))
+    st.pool_count.copy_(torch.from_numpy(ncb))
+    q_in = (q_idx if q_dt == "f32" else q_idx.to(torch.bfloat16)).contiguous()
+    st.quantize_index_q(q_in.float().contiguous())      # exact widening of bf16 values
+    ik = (caches.ik_codes, caches.ik_scales)
+    n_q = wl.n_q
+
+    def outs():
+        return {"idx": torch.full((n_q, k), 77, dtype=torch.int32, device="cuda"),
+                "cnt": torch.full((n_q,), 77, dtype=torch.int32, device="cuda"),
+                "blk": torch.full((n_q, 64), 77, dtype=torch.int32, device="cuda"),
+                "bcnt": torch.full((n_q,), 77, dtype=torch.int32, device="cuda"),
+                "keys": torch.full((n_q, C.csa2_segment_keys(wl.seq_cap, k)), 77, dtype=torch.int64, device="cuda"),
+                "sc": torch.full((n_q, wl.seq_cap), 7.0, dtype=torch.float32, device="cuda")}
+
+    def run(qc, qs):
+        o = {"plain": outs(), "pool": outs(), "build": outs()}
+        C.csa2_index_score(qc, qs, w, *ik, q_seq, n_vis, o["plain"]["sc"])
+        C.csa2_index_topk(qc, qs, w, *ik, q_seq, n_vis, k, o["plain"]["idx"], o["plain"]["cnt"])
+        C.csa2_index_segments(qc, qs, w, *ik, q_seq, n_vis, k, o["plain"]["keys"])
+        C.csa2_index_topk(qc, qs, w, *ik, q_seq, n_vis, k, o["pool"]["idx"], o["pool"]["cnt"], None, st.pool,
+                          st.pool_count, 8)
+        C.csa2_index_topk_pool(qc, qs, w, *ik, q_seq, n_vis, k, o["build"]["idx"], o["build"]["cnt"],
+                               o["build"]["blk"], o["build"]["bcnt"], 8)
+        torch.cuda.synchronize()
+        return o
+
+    ref = run(st.qi_codes, st.qi_scales)
+    got = run(q_in, None)
+    for part in ("plain", "pool", "build"):
+        for name in ("idx", "cnt", "blk", "bcnt", "keys"):
+            assert torch.equal(got[part][name], ref[part][name]), (part, name)
+    for qi in range(n_q):
+        nv = int(wl.n_vis[qi])
+        assert torch.equal(got["plain"]["sc"][qi, :nv], ref["plain"]["sc"][qi, :nv])
+    with pytest.raises(ValueError):   # NVFP4 and grouped calls take quantised Q only
+        C.csa2_index_segments(q_in, None, w, *ik, q_seq, n_vis, k, ref["plain"]["keys"], fmt=C.FMT_NVFP4)
+
+
 def _run_index_topk(C, st, caches, w, q_seq, n_vis, k, in_pool=False):
     """(fused idx, count), (two-call idx, count) on the same inputs."""
     idx_f = torch.full((st.n_q, k), 77, dtype=torch.int32, device="cuda")

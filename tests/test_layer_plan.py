@@ -26,12 +26,18 @@ def test_model_schedule_groups_plan():
             assert calls[-1] == "attend"
             if mode == "reuse":
                 assert calls == ["attend"]          # borrows the index set: no scoring
+            elif mode == "full":
+                assert calls[0] == "quantize_index_q"   # its own indexer Q (and the step's appends)
             else:
-                assert calls[0] == "quantize_index_q"  # its own indexer Q
+                assert calls[0].endswith("_q")      # its own indexer Q, quantised by the scoring call
+                assert "quantize_index_q" not in calls
+        assert all(p[0] == "quantize_index_q" for m, p in zip(g, plan_group(g, q_in_call=False)) if m != "reuse")
     dec = _groups(O.layer_schedule())[-1]
     dec = ["full_pool"] + ["reindex_pool" if m == "reindex" else m for m in dec[1:]]
     plan = plan_group(dec)
     assert plan[0] == ["quantize_index_q", "index_topk_pool", "attend"]     # Top-K and pool in one pass
+    assert all(p == ["index_topk_in_pool_q", "attend"] for m, p in zip(dec, plan) if m == "reindex_pool")
+    plan = plan_group(dec, q_in_call=False)
     assert all(p == ["quantize_index_q", "index_topk_in_pool", "attend"] for m, p in zip(dec, plan)
                if m == "reindex_pool")
     plan = plan_group(dec, fused=False)
@@ -58,13 +64,20 @@ def test_grouped_plan_scores_then_selects():
     assert plan[3] == ["quantize_index_q", "index_topk_pool", "attend"]      # pool layers keep their path
     assert plan[4] == ["quantize_index_q", "index_topk_in_pool", "attend"]
     assert plan_group(["full"], group=1)[0] == ["quantize_index_q", "index_topk", "attend"]
+    assert plan_group(["full", "reindex"], group=1)[1] == ["index_topk_q", "attend"]
     assert plan_group(["full"], fused=False, group=4)[0] == ["quantize_index_q", "score_grouped", "select", "attend"]
+    with pytest.raises(ValueError):   # grouped scoring reads quantised Q only
+        plan_group(["full"], group=4, q_in_call=True)
 
 
 def test_unfused_plan_keeps_two_calls():
     plan = plan_group(["full", "reuse", "reindex", "reindex"], fused=False)
     assert plan[0] == ["quantize_index_q", "score", "select", "attend"]
-    assert plan[2] == ["quantize_index_q", "score", "select", "attend"]
+    assert plan[2] == ["score_q", "select", "attend"]
+    plan = plan_group(["full", "reuse", "reindex", "reindex"], fused=False, q_in_call=False)
+    assert plan[0] == ["quantize_index_q", "score", "select", "attend"]
+    plan = plan_group(["full", "reindex"], fused=False, index_fmt="nvfp4")   # NVFP4: quantised Q
+    assert plan[1] == ["quantize_index_q", "score", "select", "attend"]
 
 
 @pytest.mark.parametrize("modes", [["reuse"], ["reindex", "reuse"], ["full", "reindex_pool"], ["full_pool", "bogus"],
@@ -82,15 +95,17 @@ def test_plan_select_in_attention():
     plan = plan_group(["full", "reuse", "reindex"], attn_select=True)
     assert plan[0] == ["quantize_index_q", "index_segments", "attend_topk"]
     assert plan[1] == ["attend"]
+    assert plan[2] == ["index_segments_q", "attend_topk"]    # the scoring call quantises Q itself
+    plan = plan_group(["full", "reuse", "reindex"], attn_select=True, q_in_call=False)
     assert plan[2] == ["quantize_index_q", "index_segments", "attend_topk"]
     plan = plan_group(["full_pool", "reuse", "reindex_pool"], attn_select=True)
     assert plan[0] == ["quantize_index_q", "index_topk_pool", "attend"]
-    assert plan[2] == ["score_pool_q", "attend_pool_topk"]   # the scoring call quantises Q itself
+    assert plan[2] == ["score_pool_q", "attend_pool_topk"]
     plan = plan_group(["full_pool", "reuse", "reindex_pool"], attn_select=False, pool_select=True)
     assert plan[2] == ["score_pool_q", "attend_pool_topk"]
     plan = plan_group(["full_pool", "reuse", "reindex_pool"], index_fmt="nvfp4", pool_select=True)
     assert plan[2] == ["quantize_index_q", "score_pool", "attend_pool_topk"]
     plan = plan_group(["full_pool", "reuse", "reindex_pool"], attn_select=True, pool_select=False)
-    assert plan[2] == ["quantize_index_q", "index_topk_in_pool", "attend"]
+    assert plan[2] == ["index_topk_in_pool_q", "attend"]
     assert plan_group(["full"], group=4, attn_select=True)[0] == ["quantize_index_q", "index_topk_grouped", "attend"]
     assert plan_group(["full"], fused=False, attn_select=True)[0] == ["quantize_index_q", "score", "select", "attend"]
