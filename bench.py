@@ -111,6 +111,16 @@ class LayerBench:
         self.fuse_window = bool(np.unique(wl.q_seq).size == wl.n_q and new_tok.all()
                                 and not wl.extra.get("swa_miss"))
         self.dst_entry = torch.from_numpy(ent_seq * wl.seq_cap + ent_row).to(dev)
+        # single-token decode (each query its own sequence, one new entry each): a Full layer's
+        # scoring call writes the new main-KV and indexer-K rows itself and quantises the
+        # indexer Q itself, and the attention call appends the window entry, so the layer
+        # step makes no quantise launch
+        self.fold_append = bool(self.fuse_window and n_new == 1 and index_fmt == "mxfp4" and group == 1 and fused)
+        if self.fold_append:
+            self.app = (torch.full((wl.n_q,), first_new, dtype=torch.int64, device=dev),
+                        torch.from_numpy(np.stack([wl.main_latents(int(b), first_new, 1)[0] for b in wl.q_seq])).to(dev),
+                        torch.from_numpy(np.stack([wl.index_k_latents(int(b), first_new, 1)[0]
+                                                   for b in wl.q_seq])).to(dev))
         self.dst_swa = torch.from_numpy(tok_seq * wl.swa_cap + (tok_pos - wl.swa_base) % wl.swa_cap).to(dev)
         self.step = Csa2Step(wl.n_q, wl.heads, wl.idx_heads, wl.seq_cap, group=group, index_fmt=index_fmt,
                              attn_select=attn_select, fused=fused)
@@ -128,37 +138,42 @@ class LayerBench:
         # the step's quantisations in one launch: the new entries (Full layers: main KV and
         # indexer K; every layer: its window entry) and the layer's indexer Q
         jobs = []
-        if mode.startswith("full"):
+        fold = self.fold_append and mode.startswith("full")   # appends and Q inside the scoring call
+        app = self.app if fold else None
+        if mode.startswith("full") and not fold:
             jobs += [(self.new_main, C.FMT_NVFP4, flat(c.kv_codes), flat(c.kv_scales), self.dst_entry),
                      (self.new_ik, self.ik_fmt, flat(c.ik_codes), flat(c.ik_scales), self.dst_entry)]
         if not self.fuse_window:
             jobs.append((self.new_swa[L], C.FMT_FP8, flat(c.swa[L]), None, self.dst_swa))
         q_idx, w, qa = self.inputs[L]
         names = self.plan[L]
-        if "quantize_index_q" in names:
+        if "quantize_index_q" in names and not fold:
             n_q, h, d = q_idx.shape
             jobs.append((q_idx.view(n_q * h, d), self.ik_fmt, st.qi_codes.view(n_q * h, d // 2),
                          st.qi_scales.view(n_q * h, d // self.ik_group), None))
         if jobs:
             out["quantize"] = C.csa2_quantize_kv_multi(jobs, _bind=True)
         nw = self.new_swa[L] if self.fuse_window else None
-        # calls named "..._q" read the unquantised indexer Q and quantise it themselves
-        qq = q_idx if any(n.endswith("_q") and n != "quantize_index_q" for n in names) else None
+        # calls named "..._q" (and a Full layer's scoring call with the appends) read the
+        # unquantised indexer Q and quantise it themselves
+        qq = q_idx if fold or any(n.endswith("_q") and n != "quantize_index_q" for n in names) else None
         if mode == "full_pool":
-            out["index_topk_pool"] = st.index_topk_build_pool(c, w, self.q_seq, self.n_vis, bind=True, q=qq)
+            out["index_topk_pool"] = st.index_topk_build_pool(c, w, self.q_seq, self.n_vis, bind=True, q=qq,
+                                                              append=app)
         elif "index_topk_grouped" in names:   # grouped rows scored and selected, no score array
             out["index_topk_grouped"] = st.index_topk_grouped(c, w, self.q_seq, self.n_vis, bind=True)
         elif "score_grouped" in names:
             out["score"] = st.score_grouped(c, w, self.q_seq, self.n_vis, bind=True)
             out["select"] = st.select(self.n_vis, bind=True)
         elif "index_segments" in names or "index_segments_q" in names:
-            out["index_segments"] = st.index_segments(c, w, self.q_seq, self.n_vis, bind=True, q=qq)
+            out["index_segments"] = st.index_segments(c, w, self.q_seq, self.n_vis, bind=True, q=qq, append=app)
         elif "score_pool_q" in names:   # pool slot scores from the unquantised Q; Top-K in attention
             out["score"] = st.score_q(c, q_idx, w, self.q_seq, self.n_vis, in_pool=True, bind=True)
         elif "attend_pool_topk" in names:   # pool slot scores; the Top-K is selected in attention
             out["score"] = st.score(c, w, self.q_seq, self.n_vis, in_pool=True, bind=True)
         elif mode != "reuse":
-            out["index_topk"] = st.index_topk(c, w, self.q_seq, self.n_vis, mode == "reindex_pool", bind=True, q=qq)
+            out["index_topk"] = st.index_topk(c, w, self.q_seq, self.n_vis, mode == "reindex_pool", bind=True, q=qq,
+                                              append=app)
         if "attend_topk" in names:   # the last Top-K level runs inside the attention call
             out["attn"] = st.attend_topk(c, L, qa, self.q_seq, self.q_pos, self.rs, bind=True, new_win=nw)
         elif "attend_pool_topk" in names:

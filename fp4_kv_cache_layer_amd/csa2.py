@@ -63,13 +63,13 @@ def lib() -> ctypes.CDLL:
         "csa2_index_score_q": ([vp, i32, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, vp, vp,
                                 i32, i32, vp, i64, vp], i32),
         "csa2_index_topk": ([vp, vp, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, vp, vp,
-                             i32, i32, i32, vp, vp, vp, sz, vp], i32),
+                             i32, i32, i32, vp, vp, vp, sz, vp, vp], i32),
         "csa2_index_topk_workspace_bytes": ([i32, i64, i32, i32], sz),
         "csa2_index_topk_grouped": ([vp, vp, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp,
                                      i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_index_topk_grouped_workspace_bytes": ([i32, i64, i32, i32], sz),
         "csa2_index_topk_pool": ([vp, vp, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, i32,
-                                  vp, vp, i32, i32, vp, vp, vp, sz, vp], i32),
+                                  vp, vp, i32, i32, vp, vp, vp, sz, vp, vp], i32),
         "csa2_index_topk_pool_workspace_bytes": ([i32, i64, i32, i32, i32], sz),
         "csa2_topk": ([vp, i64, i32, vp, i64, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp], i32),
         "csa2_topk_workspace_bytes": ([i32, i64, i32], sz),
@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
                                       i64, i64, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp], i32),
         "csa2_sparse_attn_noalloc_max_bytes": ([], sz),
         "csa2_index_segments": ([vp, vp, vp, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, i32,
-                                 vp, vp], i32),
+                                 vp, vp, vp], i32),
         "csa2_segment_keys": ([i64, i32], i64),
         "csa2_sparse_attn_topk": ([vp, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, i32, vp, vp, i32, i32, vp, vp,
                                    vp, i64, i64, i64, vp, vp, vp, vp, i32, i32, f32, vp, i32, vp, vp, sz, vp], i32),
@@ -281,6 +281,47 @@ def _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_bloc
             _p(q_seq), _p(n_vis), _p(cand_blocks), _p(n_cand_blocks), block, max_blocks), n_slots
 
 
+class Append(ctypes.Structure):
+    """csa2_append: the new main-KV / indexer-K rows that a fused scoring call writes itself
+    before it scores (each query's new entry of its own sequence)."""
+    _fields_ = [("row", ctypes.c_void_p), ("main", ctypes.c_void_p), ("index", ctypes.c_void_p),
+                ("dtype", ctypes.c_int), ("kv_codes", ctypes.c_void_p), ("kv_codes_stride", ctypes.c_int64),
+                ("kv_codes_seq_stride", ctypes.c_int64), ("kv_scales", ctypes.c_void_p),
+                ("kv_scales_stride", ctypes.c_int64), ("kv_scales_seq_stride", ctypes.c_int64)]
+
+
+def _append_arg(append, n_q: int, seq_cap: int):
+    """append: None, or a dict with row ([n_q] int64: the new entry's row in the query's
+    sequence, negative for none), main ([n_q, 512] latents or None) with kv_codes / kv_scales
+    (the main-KV cache views, as for csa2_sparse_attn), and index ([n_q, 128] latents or
+    None; written into the call's indexer-K cache).  Latents f32 or bf16 (both the same),
+    contiguous.  Returns the C argument (a pointer to a csa2_append, or None)."""
+    if append is None:
+        return None
+    row, main, index = append["row"], append.get("main"), append.get("index")
+    _need(row, torch.int64, 1, "append row")
+    if row.shape[0] != n_q:
+        raise ValueError("append: row must have n_q entries")
+    dts = {t.dtype for t in (main, index) if t is not None}
+    if len(dts) != 1 or not dts <= {torch.float32, torch.bfloat16}:
+        raise ValueError("append: main / index latents f32 or bf16, the same for both, at least one")
+    a = Append(row=row.data_ptr(), dtype=DT_F32 if dts == {torch.float32} else DT_BF16)
+    for t, name, d in ((main, "main", 512), (index, "index", 128)):
+        if t is None:
+            continue
+        if t.dim() != 2 or tuple(t.shape) != (n_q, d) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"append: {name} must be a contiguous CUDA [n_q, {d}] tensor")
+        setattr(a, name, t.data_ptr())
+    if main is not None:
+        kc, kce, kcs = _cache3(append["kv_codes"], "append kv_codes")
+        ks, kse, kss = _cache3(append["kv_scales"], "append kv_scales")
+        if append["kv_codes"].shape[1] < seq_cap or append["kv_scales"].shape[1] < seq_cap:
+            raise ValueError("append: the main-KV cache holds fewer rows than the indexer cache")
+        a.kv_codes, a.kv_codes_stride, a.kv_codes_seq_stride = kc.value, kce, kcs
+        a.kv_scales, a.kv_scales_stride, a.kv_scales_seq_stride = ks.value, kse, kss
+    return ctypes.byref(a)
+
+
 def csa2_index_score(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, scores,
                      cand_blocks=None, n_cand_blocks=None, block: int = 8, fmt: int = FMT_MXFP4, _bind: bool = False):
     """q_codes [n_q, H_I, 64], q_scales [n_q, H_I, 4 (MXFP4) | 8 (NVFP4)], w [n_q, H_I] f32;
@@ -367,9 +408,10 @@ def csa2_index_topk_workspace_bytes(n_q: int, n_slots: int, k: int, in_pool: boo
 
 def csa2_index_topk(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, idx_out, count_out,
                     workspace=None, cand_blocks=None, n_cand_blocks=None, block: int = 8, fmt: int = FMT_MXFP4,
-                    _bind: bool = False):
+                    append=None, _bind: bool = False):
     """Scores and Top-K in one pass: the operands of csa2_index_score (without scores) ->
-    idx_out [n_q, k] int32, count_out [n_q] int32, as csa2_topk returns them."""
+    idx_out [n_q, k] int32, count_out [n_q] int32, as csa2_topk returns them.  append: the
+    new entries the call writes first (see _append_arg; not inside a pool)."""
     args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, cand_blocks, n_cand_blocks,
                                 block, fmt)
     _need(idx_out, torch.int32, 2, "idx_out")
@@ -379,7 +421,9 @@ def csa2_index_topk(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: in
         raise ValueError("index_topk: inconsistent output shapes")
     need = csa2_index_topk_workspace_bytes(n_q, max(n_slots, 1), k, cand_blocks is not None)
     workspace, ws_bytes = _workspace(need, workspace, q_codes.device, _bind, "index_topk")
-    return _run("csa2_index_topk", args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, _stream()), _bind)
+    app = _append_arg(append, n_q, k_codes.shape[1])
+    return _run("csa2_index_topk", args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, app, _stream()),
+                _bind)
 
 
 def csa2_segment_keys(n_slots: int, k: int) -> int:
@@ -387,16 +431,17 @@ def csa2_segment_keys(n_slots: int, k: int) -> int:
 
 
 def csa2_index_segments(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, cand_keys,
-                        fmt: int = FMT_MXFP4, _bind: bool = False):
+                        fmt: int = FMT_MXFP4, append=None, _bind: bool = False):
     """The fused first Top-K level alone: the operands of csa2_index_score (no pool) ->
     cand_keys [n_q, csa2_segment_keys(seq_cap, k)] (opaque 64-bit keys, held in an int64
-    tensor) for csa2_sparse_attn_topk."""
+    tensor) for csa2_sparse_attn_topk.  append: the new entries the call writes first."""
     args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, 8, fmt)
     _need(cand_keys, torch.int64, 2, "cand_keys")
     n_q = q_codes.shape[0]
     if tuple(cand_keys.shape) != (n_q, csa2_segment_keys(n_slots, k)):
         raise ValueError("index_segments: cand_keys must be [n_q, csa2_segment_keys(seq_cap, k)]")
-    return _run("csa2_index_segments", args[:17] + (k, _p(cand_keys), _stream()), _bind)
+    app = _append_arg(append, n_q, k_codes.shape[1])
+    return _run("csa2_index_segments", args[:17] + (k, _p(cand_keys), app, _stream()), _bind)
 
 
 def csa2_index_topk_pool_workspace_bytes(n_q: int, n_slots: int, k: int, block: int, max_blocks: int) -> int:
@@ -404,10 +449,11 @@ def csa2_index_topk_pool_workspace_bytes(n_q: int, n_slots: int, k: int, block: 
 
 
 def csa2_index_topk_pool(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: int, idx_out, count_out,
-                         blocks_out, blocks_count, block: int = 8, workspace=None, _bind: bool = False):
+                         blocks_out, blocks_count, block: int = 8, workspace=None, append=None, _bind: bool = False):
     """Top-K and candidate pool in one scoring pass: the operands of csa2_index_score (no
     pool, MXFP4) -> idx_out [n_q, k], count_out [n_q] (as csa2_topk) and blocks_out
-    [n_q, max_blocks], blocks_count [n_q] (as csa2_build_pool)."""
+    [n_q, max_blocks], blocks_count [n_q] (as csa2_build_pool).  append: the new entries the
+    call writes first."""
     args, n_slots = _index_args(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, None, None, block)
     for t, name in ((idx_out, "idx_out"), (blocks_out, "blocks_out")):
         _need(t, torch.int32, 2, name)
@@ -420,8 +466,10 @@ def csa2_index_topk_pool(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, 
         raise ValueError("index_topk_pool: inconsistent output shapes")
     need = csa2_index_topk_pool_workspace_bytes(n_q, max(n_slots, 1), k, block, max_blocks)
     workspace, ws_bytes = _workspace(max(need, 1), workspace, q_codes.device, _bind, "index_topk_pool")
+    app = _append_arg(append, n_q, k_codes.shape[1])
     return _run("csa2_index_topk_pool", args[:17] + (k, _p(idx_out), _p(count_out), block, max_blocks, _p(blocks_out),
-                                                     _p(blocks_count), _p(workspace), ws_bytes, _stream()), _bind)
+                                                     _p(blocks_count), _p(workspace), ws_bytes, app, _stream()),
+                _bind)
 
 
 def csa2_topk_workspace_bytes(n_q: int, n_slots: int, k: int) -> int:

@@ -83,6 +83,46 @@ __device__ __forceinline__ uint32_t e2m1_code(float a, float s) {
   return c;
 }
 
+// "a/6 rounds to an E4M3 code >= c" for c >= 1: a/6 lies above the midpoint of codes c-1
+// and c, or on it with c even.  6 * midpoint = 3 * (v(c-1) + v(c)) is exact in fp32.
+__device__ __forceinline__ bool scale_at_least(float a, int c) {
+  const float t = 3.0f * (e4m3_mag(c - 1) + e4m3_mag(c));
+  return a > t || (a == t && !(c & 1));
+}
+
+// E4M3 code nearest to the exact quotient a/6 (a >= 0), ties to even, saturating at 448.
+// The correctly rounded fp32 quotient lands on the right code or, when a/6 sits within
+// an fp32 ulp of a midpoint, on its neighbour; the exact midpoint tests settle which.
+__device__ __forceinline__ int nvfp4_scale_code(float a) {
+  int c = fp8_mag_code(a / 6.0f);
+  if (c < 126 && scale_at_least(a, c + 1)) ++c;
+  else if (c > 0 && !scale_at_least(a, c)) --c;
+  return c;
+}
+
+// One NVFP4 group: 16 finite fp32 values (as bits; bf16 inputs widened by a shift) -> E4M3
+// scale code (returned; nearest to amax/6) and 16 E2M1 codes of x / scale packed as two
+// words, channel 2i in the low nibble of byte i (lo: channels 0-7, hi: 8-15).
+__device__ __forceinline__ int nvfp4_group(const uint32_t (&bits)[16], uint32_t& lo, uint32_t& hi) {
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t ab = bits[i] & 0x7fffffffu;  // |x|; integer order == float order for x >= 0
+    amax_bits = ab > amax_bits ? ab : amax_bits;
+  }
+  const int sc = nvfp4_scale_code(__uint_as_float(amax_bits));
+  const float s = e4m3_mag(sc);
+  lo = hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t mag = s > 0.0f ? e2m1_code(__uint_as_float(bits[i] & 0x7fffffffu), s) : 0u;
+    const uint32_t c = mag | ((bits[i] >> 28) & 8u);
+    if (i < 8) lo |= c << (4 * i);
+    else hi |= c << (4 * (i - 8));
+  }
+  return sc;
+}
+
 // One MXFP4 group: 32 finite fp32 values (as bits; bf16 inputs widened by a shift) ->
 // E8M0 scale code (returned) and 32 E2M1 codes packed as four words, channel 2i in the low
 // nibble of byte i.  E = floor(log2 amax) - 2 clamped to [-127, 127] (an all-zero group or

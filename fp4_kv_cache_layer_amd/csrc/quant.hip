@@ -16,23 +16,6 @@
 
 namespace csa2 {
 
-// "a/6 rounds to an E4M3 code >= c" for c >= 1: a/6 lies above the midpoint of codes c-1
-// and c, or on it with c even.  6 * midpoint = 3 * (v(c-1) + v(c)) is exact in fp32.
-__device__ __forceinline__ bool scale_at_least(float a, int c) {
-  const float t = 3.0f * (e4m3_mag(c - 1) + e4m3_mag(c));
-  return a > t || (a == t && !(c & 1));
-}
-
-// E4M3 code nearest to the exact quotient a/6 (a >= 0), ties to even, saturating at 448.
-// The correctly rounded fp32 quotient lands on the right code or, when a/6 sits within
-// an fp32 ulp of a midpoint, on its neighbour; the exact midpoint tests settle which.
-__device__ __forceinline__ int nvfp4_scale_code(float a) {
-  int c = fp8_mag_code(a / 6.0f);
-  if (c < 126 && scale_at_least(a, c + 1)) ++c;
-  else if (c > 0 && !scale_at_least(a, c)) --c;
-  return c;
-}
-
 // An empty asm that takes a group's results as inputs: the arithmetic (and the loads it
 // depends on) must then run before the destination check that follows, instead of being
 // moved behind it, where the loads would only be issued once the destination row has
@@ -67,23 +50,10 @@ __device__ __forceinline__ void quant_group_nvfp4(const T* __restrict__ src, int
   // stores, so that both loads are one memory round trip
   const int64_t d = kMap ? dst_row[r] : r;
   uint32_t bits[16];
-  uint32_t amax_bits = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    bits[i] = load_bits(src, r * dim + g * 16 + i);
-    uint32_t ab = bits[i] & 0x7fffffffu;  // |x|; integer order == float order for x >= 0
-    amax_bits = ab > amax_bits ? ab : amax_bits;
-  }
-  int sc = nvfp4_scale_code(__uint_as_float(amax_bits));
-  float s = e4m3_mag(sc);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint32_t mag = s > 0.0f ? e2m1_code(__uint_as_float(bits[i] & 0x7fffffffu), s) : 0u;
-    uint32_t c = mag | ((bits[i] >> 28) & 8u);
-    if (i < 8) lo |= c << (4 * i);
-    else hi |= c << (4 * (i - 8));
-  }
+  for (int i = 0; i < 16; ++i) bits[i] = load_bits(src, r * dim + g * 16 + i);
+  uint32_t lo, hi;
+  const int sc = nvfp4_group(bits, lo, hi);
   keep_before_branch(lo, hi, (uint32_t)sc);
   if (d < 0 || d >= dst_rows) return;
   uint2* out = reinterpret_cast<uint2*>(codes + d * cst + g * 8);

@@ -72,7 +72,71 @@ struct ScoreArgs {
   int64_t bmax_stride;
   int32_t* idx_out;
   int32_t* count_out;
+  // csa2_append: each query's new main-KV / indexer-K row (app_row[q]), written by the
+  // workgroup whose segment holds it (k_score_select)
+  const int64_t* app_row;
+  const void* app_main;
+  const void* app_index;
+  int app_bf16;
+  uint8_t* app_kv_codes;
+  uint8_t* app_kv_scales;
+  int64_t app_kv_ce, app_kv_cs, app_kv_se, app_kv_ss;
 };
+
+// n consecutive latent values from p (f32, or bf16 widened by a shift) as fp32 bit patterns,
+// in 16-byte loads (p 16-byte aligned)
+template <int n>
+__device__ __forceinline__ void load_latent_bits(const void* p, bool bf16, uint32_t (&bits)[n]) {
+  if (bf16) {
+    const uint4* src = static_cast<const uint4*>(p);
+#pragma unroll
+    for (int u = 0; u < n / 8; ++u) {
+      const uint4 v = src[u];
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bits[8 * u + 2 * j] = wd[j] << 16;
+        bits[8 * u + 2 * j + 1] = wd[j] & 0xffff0000u;
+      }
+    }
+  } else {
+    const uint4* src = static_cast<const uint4*>(p);
+#pragma unroll
+    for (int u = 0; u < n / 4; ++u) {
+      const uint4 v = src[u];
+      bits[4 * u] = v.x;
+      bits[4 * u + 1] = v.y;
+      bits[4 * u + 2] = v.z;
+      bits[4 * u + 3] = v.w;
+    }
+  }
+}
+
+// The new entry of query q at row r of sequence seq (csa2_append), by one wave: lanes 0-31
+// quantise the 32 NVFP4 groups of the main-KV row, lanes 32-35 the four MXFP4 groups of the
+// indexer-K row, with the quantiser's rules (nvfp4_group, mxfp4_group), and store them.
+__device__ __forceinline__ void append_entry(const ScoreArgs& s, int q, int seq, int64_t r, int lane) {
+  if (lane < 32 && s.app_main) {
+    uint32_t bits[16];
+    load_latent_bits<16>(static_cast<const uint8_t*>(s.app_main) + ((int64_t)q * 512 + 16 * lane) * (s.app_bf16 ? 2 : 4),
+                         s.app_bf16, bits);
+    uint32_t lo, hi;
+    const int sc = nvfp4_group(bits, lo, hi);
+    *reinterpret_cast<uint2*>(s.app_kv_codes + (int64_t)seq * s.app_kv_cs + r * s.app_kv_ce + 8 * lane) =
+        make_uint2(lo, hi);
+    s.app_kv_scales[(int64_t)seq * s.app_kv_ss + r * s.app_kv_se + lane] = (uint8_t)sc;
+  } else if (lane >= 32 && lane < 36 && s.app_index) {
+    const int g = lane - 32;
+    uint32_t bits[32];
+    load_latent_bits<32>(static_cast<const uint8_t*>(s.app_index) + ((int64_t)q * 128 + 32 * g) * (s.app_bf16 ? 2 : 4),
+                         s.app_bf16, bits);
+    uint32_t w[4];
+    const int code = mxfp4_group(bits, w);
+    uint8_t* kc = const_cast<uint8_t*>(s.k_codes) + (int64_t)seq * s.k_cs + r * s.k_ce + 16 * g;
+    *reinterpret_cast<uint4*>(kc) = make_uint4(w[0], w[1], w[2], w[3]);
+    const_cast<uint8_t*>(s.k_scales)[(int64_t)seq * s.k_ss + r * s.k_se + g] = (uint8_t)code;
+  }
+}
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
@@ -218,29 +282,8 @@ struct QueryScorer {
         // this lane's A operand is one whole MXFP4 group (head `row`, channels 32*kb ..
         // +31): quantise it here, with the same rule as csa2_quantize_kv
         uint32_t bits[32];
-        if (s.q_bf16) {
-          const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(s.q_lat) + r * 128 + kb * 32);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint4 v = src[u];
-            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              bits[8 * u + 2 * j] = wd[j] << 16;
-              bits[8 * u + 2 * j + 1] = wd[j] & 0xffff0000u;
-            }
-          }
-        } else {
-          const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(s.q_lat) + r * 128 + kb * 32);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const uint4 v = src[u];
-            bits[4 * u] = v.x;
-            bits[4 * u + 1] = v.y;
-            bits[4 * u + 2] = v.z;
-            bits[4 * u + 3] = v.w;
-          }
-        }
+        load_latent_bits<32>(static_cast<const uint8_t*>(s.q_lat) + (r * 128 + kb * 32) * (s.q_bf16 ? 2 : 4), s.q_bf16,
+                             bits);
         uint32_t wq[4];
         a_scale = mxfp4_group(bits, wq);
         a[0] = (int)wq[0];
@@ -635,6 +678,17 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_select(ScoreArgs s) {
   uint64_t key[kTkEpt];
   QueryScorer<kPool, kNv, kQLat> sc;
   const int c0 = seg * kTkSeg;
+  if (!kNv && s.app_row) {   // uniform (a kernel argument): a csa2_append (MXFP4 indexer)
+    const int seq = s.q_seq[q];
+    const int64_t r = s.app_row[q];
+    if (seq >= 0 && seq < s.n_seq && r >= 0 && r < s.seq_cap && r / kTkSeg == seg) {   // uniform
+      // this segment holds the query's new row: write it, and let the stores complete
+      // before any wave of the workgroup reads the indexer K
+      if (wave == 0) append_entry(s, q, seq, r, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
   const bool seq_ok = sc.init(s, q, false);
   // workgroup-uniform condition: every thread reaches select_segment's barriers
   if (seq_ok && sc.nv > 0 && c0 < sc.n_valid) {
@@ -786,6 +840,34 @@ static int launch_score(ScoreArgs a, int n_q, float* scores, int64_t scores_stri
   return csa2_check_launch();
 }
 
+// A fused scoring call's csa2_append -> the ScoreArgs fields (nothing when app is null).
+// Returns a csa2 status.
+static int set_append(ScoreArgs& a, const csa2_append* app, int64_t seq_cap, int fmt) {
+  if (!app) return CSA2_OK;
+  if (fmt == CSA2_FMT_NVFP4) return CSA2_ERR_UNSUPPORTED;   // the appended indexer-K row is MXFP4
+  if (!app->row) return CSA2_ERR_NULL;
+  if (app->dtype != CSA2_DT_F32 && app->dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
+  if (app->main) {
+    if (!app->kv_codes || !app->kv_scales) return CSA2_ERR_NULL;
+    if (!aligned16(app->main) || !aligned16(app->kv_codes)) return CSA2_ERR_SHAPE;
+    CacheRef kv{app->kv_codes, app->kv_scales, app->kv_codes_stride, app->kv_codes_seq_stride,
+                app->kv_scales_stride, app->kv_scales_seq_stride};
+    if (resolve_cache(kv, seq_cap, 256, 32, 1) != CSA2_OK) return CSA2_ERR_SHAPE;
+    a.app_kv_codes = app->kv_codes;
+    a.app_kv_scales = app->kv_scales;
+    a.app_kv_ce = kv.ce;
+    a.app_kv_cs = kv.cs;
+    a.app_kv_se = kv.se;
+    a.app_kv_ss = kv.ss;
+  }
+  if (app->index && !aligned16(app->index)) return CSA2_ERR_SHAPE;
+  a.app_row = app->row;
+  a.app_main = app->main;
+  a.app_index = app->index;
+  a.app_bf16 = app->dtype == CSA2_DT_BF16;
+  return CSA2_OK;
+}
+
 // k_score_select for the indexer format of a call (NVFP4; MXFP4 with quantised or
 // unquantised Q); the pool build (kBlockMax) exists for MXFP4 only
 template <bool kFinal, bool kBlockMax>
@@ -925,8 +1007,10 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
                                int dim, CSA2_INDEX_CACHE_ARGS, int64_t seq_cap, int n_seq, const int32_t* q_seq,
                                const int64_t* n_vis, const int32_t* cand_blocks, const int32_t* n_cand_blocks,
                                int block, int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               void* workspace, size_t workspace_bytes, const csa2_append* append,
+                               void* stream) {
   if (int rc_status = csa2_take_device_status()) return rc_status;
+  if (append && cand_blocks) return CSA2_ERR_UNSUPPORTED;
   CacheRef kr = CSA2_INDEX_CACHE_REF;
   int64_t n_slots = 0;
   int rc = check_score_args(q_codes, q_scales, w, n_q, n_heads, dim, fmt, kr, seq_cap, n_seq, q_seq, n_vis,
@@ -974,6 +1058,8 @@ extern "C" int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, 
   a.keys_out = bufA;
   a.idx_out = idx_out;
   a.count_out = count_out;
+  rc = set_append(a, append, seq_cap, fmt);
+  if (rc != CSA2_OK) return rc;
   const dim3 grid((unsigned)segs[0], (unsigned)n_q);
   rc = L == 1 ? launch_score_select<true, false>(fmt, grid, st, a) : launch_score_select<false, false>(fmt, grid, st, a);
   if (rc != CSA2_OK) return rc;
@@ -997,7 +1083,7 @@ extern "C" int64_t csa2_segment_keys(int64_t n_slots, int k) {
 extern "C" int csa2_index_segments(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
                                    int n_heads, int dim, CSA2_INDEX_CACHE_ARGS, int64_t seq_cap, int n_seq,
                                    const int32_t* q_seq, const int64_t* n_vis, int k, uint64_t* cand_keys,
-                                   void* stream) {
+                                   const csa2_append* append, void* stream) {
   if (int rc_status = csa2_take_device_status()) return rc_status;
   CacheRef kr = CSA2_INDEX_CACHE_REF;
   int64_t n_slots = 0;
@@ -1012,6 +1098,8 @@ extern "C" int csa2_index_segments(const uint8_t* q_codes, const uint8_t* q_scal
                           n_slots, fmt);
   a.k = k;
   a.keys_out = cand_keys;
+  rc = set_append(a, append, seq_cap, fmt);
+  if (rc != CSA2_OK) return rc;
   return launch_score_select<false, false>(fmt, dim3((unsigned)n_seg, (unsigned)n_q), (hipStream_t)stream, a);
 }
 
@@ -1083,7 +1171,8 @@ extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_sca
                                     int n_heads, int dim, CSA2_INDEX_CACHE_ARGS, int64_t seq_cap, int n_seq,
                                     const int32_t* q_seq, const int64_t* n_vis, int k, int32_t* idx_out,
                                     int32_t* count_out, int block, int max_blocks, int32_t* blocks_out,
-                                    int32_t* blocks_count, void* workspace, size_t workspace_bytes, void* stream) {
+                                    int32_t* blocks_count, void* workspace, size_t workspace_bytes,
+                                    const csa2_append* append, void* stream) {
   if (int rc_status = csa2_take_device_status()) return rc_status;
   if (fmt != CSA2_FMT_MXFP4 && !q_latent(fmt)) return CSA2_ERR_UNSUPPORTED;
   CacheRef kr = CSA2_INDEX_CACHE_REF;
@@ -1119,6 +1208,8 @@ extern "C" int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_sca
   a.count_out = count_out;
   a.bmax = bmax;
   a.bmax_stride = nblk;
+  rc = set_append(a, append, seq_cap, fmt);
+  if (rc != CSA2_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid((unsigned)segs[0], (unsigned)n_q);
   rc = L == 1 ? launch_score_select<true, true>(fmt, grid, st, a) : launch_score_select<false, true>(fmt, grid, st, a);

@@ -247,25 +247,36 @@ class Csa2Step:
                                self.pool, self.pool_count, self.block, _bind=bind)
         return C.csa2_topk(self.scores, n_vis, self.seq_cap, self.k, self.idx, self.count, self.ws_topk, _bind=bind)
 
-    def index_topk(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False, q=None):
+    def index_topk(self, caches: Caches, w, q_seq, n_vis, in_pool: bool = False, bind=False, q=None, append=None):
         """score + select in one pass, without the score array.  q: the unquantised indexer Q
-        (MXFP4: the call quantises it), else the step's quantised Q (as for the calls below)."""
+        (MXFP4: the call quantises it), else the step's quantised Q (as for the calls below).
+        append: the step's new entries, written by the call itself (see Csa2Step.appends)."""
         pool = (self.pool, self.pool_count) if in_pool else (None, None)
         return C.csa2_index_topk(*self._q(q), w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
                                  self.k, self.idx, self.count, self.ws_index_topk, pool[0], pool[1], self.block,
-                                 fmt=self.idx_qfmt, _bind=bind)
+                                 fmt=self.idx_qfmt, append=self._app(caches, append), _bind=bind)
 
-    def index_topk_build_pool(self, caches: Caches, w, q_seq, n_vis, bind=False, q=None):
+    def index_topk_build_pool(self, caches: Caches, w, q_seq, n_vis, bind=False, q=None, append=None):
         """score + select + pool in one pass (the decoder's first Full layer)."""
         self._mx_only("the fused pool build")
         return C.csa2_index_topk_pool(*self._q(q), w, caches.ik_codes, caches.ik_scales, q_seq,
                                       n_vis, self.k, self.idx, self.count, self.pool, self.pool_count, self.block,
-                                      self.ws_index_topk_pool, _bind=bind)
+                                      self.ws_index_topk_pool, append=self._app(caches, append), _bind=bind)
 
-    def index_segments(self, caches: Caches, w, q_seq, n_vis, bind=False, q=None):
+    def index_segments(self, caches: Caches, w, q_seq, n_vis, bind=False, q=None, append=None):
         """the first Top-K level alone (its survivors feed attend_topk)."""
         return C.csa2_index_segments(*self._q(q), w, caches.ik_codes, caches.ik_scales, q_seq, n_vis,
-                                     self.k, self.cand_keys, fmt=self.idx_qfmt, _bind=bind)
+                                     self.k, self.cand_keys, fmt=self.idx_qfmt, append=self._app(caches, append),
+                                     _bind=bind)
+
+    @staticmethod
+    def _app(caches: Caches, append):
+        """(row, main latents, indexer-K latents) -> the binding's csa2_append, main-KV rows into
+        `caches`."""
+        if append is None:
+            return None
+        row, main, index = append
+        return {"row": row, "main": main, "index": index, "kv_codes": caches.kv_codes, "kv_scales": caches.kv_scales}
 
     def attend_topk(self, caches: Caches, layer: int, q_attn, q_seq, q_pos, replay_start, out=None, lse=None,
                     bind=False, new_win=None):
@@ -308,32 +319,33 @@ class Csa2Step:
                                   new_win=new_win, _bind=bind)
 
     def run_group(self, caches: Caches, modes, inputs, q_seq, n_vis, q_pos, replay_start, outs=None, lses=None,
-                  bind=False, new_wins=None):
+                  bind=False, new_wins=None, appends=None):
         """Runs the layers of a group in order.  inputs[i] = (indexer Q f32 [n_q, H_I, d] or
         None for Reuse, w [n_q, H_I] or None, attention Q bf16 [n_q, H, D]); layer i attends
         with its own window cache caches.swa[i].  outs/lses: optional per-layer outputs
         (default: the step's own buffers, overwritten by each layer).  new_wins: optional
         per-layer window latents of each row's own token, appended by the layer's attention
-        call (see attend).  With bind=True returns the group's calls as one flat list of
-        callables."""
-        plan = plan_group(modes, self.fused, self.group, self.index_fmt, self.attn_select,
-                          pool_select=self.pool_select, group_select=self.group_select, q_in_call=self.q_in_call)
+        call (see attend).  appends: optional per-layer new entries of Full layers, written
+        by their scoring call (see full; the layer then makes no quantise call).  With
+        bind=True returns the group's calls as one flat list of callables."""
+        plan = self.plan(modes, appends)
         calls = []
         for i, (m, names) in enumerate(zip(modes, plan)):
             q_index, w, q_attn = inputs[i]
             out = None if outs is None else outs[i]
             lse = None if lses is None else lses[i]
             nw = None if new_wins is None else new_wins[i]
+            app = None if appends is None else appends[i]
             for name in names:
-                # "_q": the scoring call reads the unquantised indexer Q itself
-                qq = q_index if name.endswith("_q") else None
-                base = name[:-2] if qq is not None else name
+                # "_q" (or a scoring call with appends): it reads the unquantised indexer Q itself
+                qq = q_index if name.endswith("_q") or app is not None else None
+                base = name[:-2] if name.endswith("_q") else name
                 if name == "quantize_index_q":
                     c = self.quantize_index_q(q_index, bind)
                 elif base == "index_topk_pool":
-                    c = self.index_topk_build_pool(caches, w, q_seq, n_vis, bind, q=qq)
+                    c = self.index_topk_build_pool(caches, w, q_seq, n_vis, bind, q=qq, append=app)
                 elif base in ("index_topk", "index_topk_in_pool"):
-                    c = self.index_topk(caches, w, q_seq, n_vis, base.endswith("in_pool"), bind, q=qq)
+                    c = self.index_topk(caches, w, q_seq, n_vis, base.endswith("in_pool"), bind, q=qq, append=app)
                 elif name == "score_grouped":
                     c = self.score_grouped(caches, w, q_seq, n_vis, bind)
                 elif name == "index_topk_grouped":
@@ -347,7 +359,7 @@ class Csa2Step:
                 elif name == "build_pool":
                     c = self.build_pool(n_vis, bind)
                 elif base == "index_segments":
-                    c = self.index_segments(caches, w, q_seq, n_vis, bind, q=qq)
+                    c = self.index_segments(caches, w, q_seq, n_vis, bind, q=qq, append=app)
                 elif name == "attend_topk":
                     c = self.attend_topk(caches, i, q_attn, q_seq, q_pos, replay_start, out, lse, bind, new_win=nw)
                 elif name == "attend_pool_topk":
@@ -358,28 +370,57 @@ class Csa2Step:
                 calls.append(c)
         return calls if bind else None
 
+    def plan(self, modes, appends=None) -> list:
+        """The calls of each layer as run_group makes them (plan_group with this step's
+        options; a Full layer with appends drops its quantise call)."""
+        plan = plan_group(modes, self.fused, self.group, self.index_fmt, self.attn_select,
+                          pool_select=self.pool_select, group_select=self.group_select, q_in_call=self.q_in_call)
+        if appends is None:
+            return plan
+        for i, m in enumerate(modes):
+            if appends[i] is None:
+                continue
+            if not m.startswith("full") or not self.appends_in_call():
+                raise ValueError(f"layer {i}: appends go to a Full layer's fused MXFP4 scoring call")
+            plan[i] = [n for n in plan[i] if n != "quantize_index_q"]
+        return plan
+
     # ---- layer modes ----
     @staticmethod
     def _seq(calls, bind):
         return calls if bind else None
 
+    def appends_in_call(self) -> bool:
+        """Whether a Full layer's scoring call can write the step's new entries itself
+        (csa2_append: the fused MXFP4 scoring calls, one row per query)."""
+        return self.fused and self.index_fmt == "mxfp4" and self.group == 1
+
     def full(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, make_pool=False,
-             out=None, lse=None, bind=False):
-        q = None   # a Full layer's quantise launch also carries the step's appends (plan_group)
-        calls = [self.quantize_index_q(q_index_f32, bind)]
+             out=None, lse=None, bind=False, append=None, new_win=None):
+        """append: None, or (row [n_q] int64, main latents [n_q, 512], indexer-K latents
+        [n_q, 128]) of each query's new entry (queries of distinct sequences; row < 0: none),
+        written by the scoring call, which then also quantises the indexer Q itself: with
+        new_win (the window entries, appended by the attention call) the layer step makes no
+        quantise launch.  Without append the step quantises its indexer Q in a launch of its
+        own, which a caller may extend with its appends (csa2_quantize_kv_multi)."""
+        if append is not None and not self.appends_in_call():
+            raise ValueError("appends inside the scoring call need the fused MXFP4 path with group 1")
+        q = q_index_f32 if append is not None else None
+        calls = [] if q is not None else [self.quantize_index_q(q_index_f32, bind)]
         if make_pool and self.fused and self.index_fmt == "mxfp4":
-            calls.append(self.index_topk_build_pool(caches, w, q_seq, n_vis, bind, q=q))
+            calls.append(self.index_topk_build_pool(caches, w, q_seq, n_vis, bind, q=q, append=append))
         elif make_pool:
-            calls += [self.score(caches, w, q_seq, n_vis, bind=bind) if q is None else
-                      self.score_q(caches, q, w, q_seq, n_vis, bind=bind),
-                      self.select(n_vis, bind=bind), self.build_pool(n_vis, bind)]
+            calls += [self.score(caches, w, q_seq, n_vis, bind=bind), self.select(n_vis, bind=bind),
+                      self.build_pool(n_vis, bind)]
         elif self.attn_select:
-            calls += [self.index_segments(caches, w, q_seq, n_vis, bind, q=q),
-                      self.attend_topk(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind)]
+            calls += [self.index_segments(caches, w, q_seq, n_vis, bind, q=q, append=append),
+                      self.attend_topk(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind,
+                                       new_win=new_win)]
             return self._seq(calls, bind)
         else:
-            calls += self._score_select(caches, w, q_seq, n_vis, False, bind, q)
-        calls.append(self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind))
+            calls += ([self.index_topk(caches, w, q_seq, n_vis, False, bind, q, append)] if append is not None else
+                      self._score_select(caches, w, q_seq, n_vis, False, bind))
+        calls.append(self.attend(caches, layer, q_attn, q_seq, q_pos, replay_start, out, lse, bind, new_win=new_win))
         return self._seq(calls, bind)
 
     def reindex(self, caches, layer, q_index_f32, w, q_attn, q_seq, n_vis, q_pos, replay_start, in_pool=False,

@@ -321,6 +321,40 @@ int csa2_index_topk_grouped(const uint8_t* q_codes, const uint8_t* q_scales, con
 size_t csa2_index_topk_grouped_workspace_bytes(int n_q, int64_t seq_cap, int k, int group);
 
 /*
+ * csa2_append -- new cache entries that a fused scoring call (csa2_index_topk without a pool,
+ * csa2_index_segments, csa2_index_topk_pool) writes itself, for decode steps whose Full
+ * layer would otherwise make a quantise launch first: each query's new entry of its own
+ * sequence, its main-KV row in NVFP4 and its indexer-K row in MXFP4 (the csa2_quantize_kv
+ * rules, bit for bit).  [W] "FP4 与 SWA Bounded Replay" (new entries in FP4 after RoPE).
+ * The call's scores see the new indexer-K entry, so the results (and the caches afterwards)
+ * equal csa2_quantize_kv of the two rows followed by the same call without an append.
+ *   row        [n_q] int64: the row of query q's new entry in sequence q_seq[q]; no append
+ *              for q when row[q] is outside [0, seq_cap) or q_seq[q] outside [0, n_seq).
+ *              Queries with an append must be of distinct sequences (no other query of the
+ *              call may read that sequence: its row is written while the call runs).
+ *   main       [n_q, 512] latents of the new main-KV rows (f32 or bf16, 16-byte aligned),
+ *              or NULL: no main-KV append
+ *   index      [n_q, 128] latents of the new indexer-K rows, or NULL: no indexer-K append;
+ *              written into the call's own indexer-K cache (k_codes / k_scales)
+ *   dtype      CSA2_DT_F32 or CSA2_DT_BF16, of both latents
+ *   kv_*       the main-KV cache and its strides (see Cache layouts; 0 = dense), written;
+ *              unused without `main`
+ * A NULL csa2_append pointer: nothing is appended.  Errors of the calls that take it:
+ * CSA2_ERR_NULL (row, or the main-KV cache with `main`), CSA2_ERR_SHAPE (alignment, strides),
+ * CSA2_ERR_UNSUPPORTED (dtype; an NVFP4 indexer; an append to csa2_index_topk inside a pool).
+ */
+typedef struct csa2_append {
+  const int64_t* row;
+  const void* main;
+  const void* index;
+  int dtype;
+  uint8_t* kv_codes;
+  int64_t kv_codes_stride, kv_codes_seq_stride;
+  uint8_t* kv_scales;
+  int64_t kv_scales_stride, kv_scales_seq_stride;
+} csa2_append;
+
+/*
  * csa2_index_topk -- csa2_index_score followed by csa2_topk in one pass, without the score
  * array.  [W] "CSA2：跨层复用，能借就不自己算" (indexer scores, then Top-K, K = 512),
  * "分层稀疏索引器" (inside the pool).
@@ -336,8 +370,9 @@ size_t csa2_index_topk_grouped_workspace_bytes(int n_q, int64_t seq_cap, int k, 
  *   and keeps its best k in registers.  Inside a pool (at most a few thousand blocks) the
  *   scores go through the workspace, which lets the block-id gather spread over many
  *   workgroups.
+ *   append     NULL, or the new entries the call writes first (csa2_append; not inside a pool)
  * Errors: those of csa2_index_score (except the score array's), CSA2_ERR_NULL (idx_out,
- * count_out), CSA2_ERR_SHAPE (k, n_q), CSA2_ERR_WORKSPACE.
+ * count_out), CSA2_ERR_SHAPE (k, n_q), CSA2_ERR_WORKSPACE; those of csa2_append.
  */
 int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
                     int n_heads, int dim, int fmt, const uint8_t* k_codes, int64_t k_codes_stride,
@@ -345,7 +380,8 @@ int csa2_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, const float
                     int64_t k_scales_seq_stride, int64_t seq_cap, int n_seq, const int32_t* q_seq,
                     const int64_t* n_vis, const int32_t* cand_blocks, const int32_t* n_cand_blocks,
                     int block, int max_cand_blocks, int k, int32_t* idx_out, int32_t* count_out,
-                    void* workspace, size_t workspace_bytes, void* stream);
+                    void* workspace, size_t workspace_bytes, const csa2_append* append,
+                    void* stream);
 size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_pool);
 
 /*
@@ -361,15 +397,16 @@ size_t csa2_index_topk_workspace_bytes(int n_q, int64_t n_slots, int k, int in_p
  *              fully overwritten: per run its k keys in position order, then zeros.  The
  *              keys are opaque (0 = no candidate): only csa2_sparse_attn_topk reads them.
  * csa2_segment_keys(n_slots, k) = ceil(n_slots / 8192) * k (at least k; 0 for a bad k).
+ *   append     NULL, or the new entries the call writes first (csa2_append)
  * Errors: those of csa2_index_score (except the score array's), CSA2_ERR_NULL (cand_keys),
- * CSA2_ERR_SHAPE (k, n_q).
+ * CSA2_ERR_SHAPE (k, n_q); those of csa2_append.
  */
 int csa2_index_segments(const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int n_q,
                         int n_heads, int dim, int fmt, const uint8_t* k_codes,
                         int64_t k_codes_stride, int64_t k_codes_seq_stride, const uint8_t* k_scales,
                         int64_t k_scales_stride, int64_t k_scales_seq_stride, int64_t seq_cap,
                         int n_seq, const int32_t* q_seq, const int64_t* n_vis, int k,
-                        uint64_t* cand_keys, void* stream);
+                        uint64_t* cand_keys, const csa2_append* append, void* stream);
 int64_t csa2_segment_keys(int64_t n_slots, int k);
 
 /*
@@ -386,6 +423,7 @@ int64_t csa2_segment_keys(int64_t n_slots, int k);
  * Top-K survivors.  A query whose q_seq is outside [0, n_seq) gets count 0 and a pool of
  * its lowest visible block ids (all their scores are -inf).
  *   Workspace: csa2_index_topk_pool_workspace_bytes(n_q, seq_cap, k, block, max_blocks).
+ * append: NULL, or the new entries the call writes first (csa2_append).
  * fmt must be CSA2_FMT_MXFP4 or CSA2_FMT_MXFP4_Q_F32 / _Q_BF16.  Errors: as csa2_index_topk;
  * CSA2_ERR_SHAPE for block or max_blocks out of range; CSA2_ERR_UNSUPPORTED for another fmt.
  */
@@ -397,7 +435,7 @@ int csa2_index_topk_pool(const uint8_t* q_codes, const uint8_t* q_scales, const 
                          const int32_t* q_seq, const int64_t* n_vis, int k, int32_t* idx_out,
                          int32_t* count_out, int block, int max_blocks, int32_t* blocks_out,
                          int32_t* blocks_count, void* workspace, size_t workspace_bytes,
-                         void* stream);
+                         const csa2_append* append, void* stream);
 size_t csa2_index_topk_pool_workspace_bytes(int n_q, int64_t n_slots, int k, int block,
                                             int max_blocks);
 

@@ -195,8 +195,9 @@ def run_group_snapshots(case: Case, step, caches, window_appends: bool = False, 
     window_appends: before its calls, each layer writes the FP8 window entry of every query
     row into its own ring (what a layer step does when the window state is not cached).
     fused_window: each row's own window entry is first zeroed in every layer's ring, and the
-    layer's attention call appends it (new_win), as the single-token decode step runs."""
-    from fp4_kv_cache_layer_amd.layer import plan_group
+    layer's attention call appends it (new_win), as the single-token decode step runs; with
+    one new entry per row, its main-KV and indexer-K rows are zeroed too and the Full layer's
+    scoring call writes them (csa2_append), so that step makes no quantise call either."""
     wl = case.wl
     q_seq, n_vis, q_pos, rs = case.gpu_meta()
     modes = list(wl.layers)
@@ -212,11 +213,25 @@ def run_group_snapshots(case: Case, step, caches, window_appends: bool = False, 
             lat = np.stack([wl.swa_latents(L, int(b), int(t), 1)[0] for b, t in zip(wl.q_seq, wl.q_pos)])
             new_wins.append(torch.from_numpy(lat.astype(np.float32)).cuda())
         torch.cuda.synchronize()
-    calls = step.run_group(caches, modes, inputs, q_seq, n_vis, q_pos, rs, bind=True, new_wins=new_wins)
+    appends = None
+    if fused_window and step.appends_in_call():
+        # as the decode step is benchmarked: each Full layer's scoring call writes the rows'
+        # new main-KV and indexer-K entries (blanked here first) and quantises the indexer Q
+        first_new, n_new = int(wl.new_entries[0]), int(wl.new_entries[1])
+        if n_new == 1:
+            seqs = torch.from_numpy(wl.q_seq.astype(np.int64)).cuda()
+            for t in (caches.kv_codes, caches.kv_scales, caches.ik_codes, caches.ik_scales):
+                t[seqs, first_new] = 0
+            app = (torch.full((wl.n_q,), first_new, dtype=torch.int64, device="cuda"),
+                   torch.from_numpy(np.stack([wl.main_latents(int(b), first_new, 1)[0] for b in wl.q_seq])).cuda(),
+                   torch.from_numpy(np.stack([wl.index_k_latents(int(b), first_new, 1)[0] for b in wl.q_seq])).cuda())
+            appends = [app if m.startswith("full") else None for m in modes]
+            torch.cuda.synchronize()
+    calls = step.run_group(caches, modes, inputs, q_seq, n_vis, q_pos, rs, bind=True, new_wins=new_wins,
+                           appends=appends)
     snaps, at = [], 0
     # the calls of each layer as the step plans them (the flat list is cut by these counts)
-    plan = plan_group(modes, step.fused, step.group, step.index_fmt, step.attn_select, pool_select=step.pool_select,
-                      group_select=step.group_select, q_in_call=step.q_in_call)
+    plan = step.plan(modes, appends)
     assert sum(len(n) for n in plan) == len(calls)
     for L, names in enumerate(plan):
         if window_appends:

@@ -115,7 +115,7 @@ def _index(**over):
 
 
 def test_index_validation(L):
-    seg = dict(k=512, cand_keys=FAKE, stream=None)
+    seg = dict(k=512, cand_keys=FAKE, append=None, stream=None)
     assert L.csa2_segment_keys(131072, 512) == 8192
     assert L.csa2_segment_keys(131073, 512) == 8704
     assert L.csa2_segment_keys(0, 512) == 512
@@ -130,6 +130,24 @@ def test_index_validation(L):
     assert _call(L, "csa2_index_segments", **_index(fmt=0, k_scales_stride=9), **seg) == -2  # NVFP4: even stride
     assert _call(L, "csa2_index_segments", **_index(fmt=0, k_scales=ctypes.c_void_p(0x1001)), **seg) == -2
     assert _call(L, "csa2_index_segments", **_index(n_q=0), **seg) == 0                    # no rows: no launch
+    # unquantised indexer Q (fmt 3 / 4): q_scales unused; 5 is no format
+    assert _call(L, "csa2_index_segments", **_index(fmt=3, q_scales=None), **dict(seg, cand_keys=None)) == -1
+    assert _call(L, "csa2_index_segments", **_index(fmt=5), **seg) == -3
+    assert _call(L, "csa2_index_segments", **_index(fmt=1, q_scales=None), **seg) == -1   # quantised Q needs scales
+    # csa2_append
+    from fp4_kv_cache_layer_amd.csa2 import Append
+    ok = Append(row=0x2000, main=0x3000, index=0x4000, dtype=0, kv_codes=0x5000, kv_scales=0x6000)
+    app = lambda **f: ctypes.byref(Append(**{**{k: getattr(ok, k) for k, _ in Append._fields_}, **f}))
+    assert _call(L, "csa2_index_segments", **_index(), **dict(seg, append=app(row=None))) == -1
+    assert _call(L, "csa2_index_segments", **_index(), **dict(seg, append=app(kv_codes=None))) == -1
+    assert _call(L, "csa2_index_segments", **_index(), **dict(seg, append=app(dtype=7))) == -3
+    assert _call(L, "csa2_index_segments", **_index(), **dict(seg, append=app(main=0x3004))) == -2    # misaligned
+    assert _call(L, "csa2_index_segments", **_index(), **dict(seg, append=app(index=0x4008))) == -2
+    assert _call(L, "csa2_index_segments", **_index(), **dict(seg, append=app(kv_codes_stride=200))) == -2
+    assert _call(L, "csa2_index_segments", **_index(fmt=0), **dict(seg, append=app())) == -3   # NVFP4 indexer
+    topk = dict(cand_blocks=FAKE, n_cand_blocks=FAKE, block=8, max_cand_blocks=16, k=512, idx_out=FAKE,
+                count_out=FAKE, workspace=None, workspace_bytes=0, append=app(), stream=None)
+    assert _call(L, "csa2_index_topk", **_index(), **topk) == -3                           # no append inside a pool
     grp = dict(group=8, k=512, idx_out=FAKE, count_out=FAKE, workspace=None, workspace_bytes=0, stream=None)
     assert _call(L, "csa2_index_topk_grouped", **_index(fmt=0), **grp) == -3               # MXFP4 only
     assert _call(L, "csa2_index_topk_grouped", **_index(), **dict(grp, group=9)) == -2

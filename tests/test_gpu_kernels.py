@@ -510,6 +510,84 @@ def test_scoring_calls_take_unquantised_q(C, q_dt, heads):
         C.csa2_index_segments(q_in, None, w, *ik, q_seq, n_vis, k, ref["plain"]["keys"], fmt=C.FMT_NVFP4)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_scoring_calls_append_new_entries(C, dt):
+    """A fused scoring call given a csa2_append writes each query's new main-KV row (NVFP4)
+    and indexer-K row (MXFP4) itself and scores with the new indexer-K row: the caches and
+    the results equal csa2_quantize_kv of the two rows followed by the call without an
+    append (csa2_index_segments, csa2_index_topk, csa2_index_topk_pool; rows at the first and
+    last entry of a segment, the last visible entry, one past the visible range, and none;
+    the quantiser is pinned to the oracle by test_quantize_bitexact).  With the unquantised
+    indexer Q as well, the step's quantise launch has nothing left to do."""
+    _say("append", dt)
+    n_vis = [20000, 17001, 8193, 333, 100]
+    rows = [19999, 17000, 8192, 5000, -1]
+    case = _score_case(61, 5, 20000, n_vis, 16)      # one sequence per query
+    wl = case.wl
+    q_idx, w, _ = case.gpu_query_inputs(0)
+    q_seq, n_vis_t, _, _ = case.gpu_meta()
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    gen = torch.Generator().manual_seed(7)
+    main = torch.randn(wl.n_q, 512, generator=gen).to(tdt).cuda()
+    index = torch.randn(wl.n_q, 128, generator=gen).to(tdt).cuda()
+    main[1, :16] = 0.0                                 # an all-zero NVFP4 group
+    row_t = torch.tensor(rows, dtype=torch.int64, device="cuda")
+    from fp4_kv_cache_layer_amd.layer import Csa2Step
+    st = Csa2Step(wl.n_q, 16, 16, wl.seq_cap)
+    k = 512
+    st.quantize_index_q(q_idx)
+
+    def run(caches, append):
+        ik = (caches.ik_codes, caches.ik_scales)
+        o = {"keys": torch.full((wl.n_q, C.csa2_segment_keys(wl.seq_cap, k)), 77, dtype=torch.int64, device="cuda"),
+             "idx": torch.full((wl.n_q, k), 77, dtype=torch.int32, device="cuda"),
+             "cnt": torch.full((wl.n_q,), 77, dtype=torch.int32, device="cuda"),
+             "pidx": torch.full((wl.n_q, k), 77, dtype=torch.int32, device="cuda"),
+             "pcnt": torch.full((wl.n_q,), 77, dtype=torch.int32, device="cuda"),
+             "blk": torch.full((wl.n_q, 64), 77, dtype=torch.int32, device="cuda"),
+             "bcnt": torch.full((wl.n_q,), 77, dtype=torch.int32, device="cuda")}
+        C.csa2_index_segments(st.qi_codes, st.qi_scales, w, *ik, q_seq, n_vis_t, k, o["keys"], append=append)
+        C.csa2_index_topk(st.qi_codes, st.qi_scales, w, *ik, q_seq, n_vis_t, k, o["idx"], o["cnt"], append=append)
+        C.csa2_index_topk_pool(st.qi_codes, st.qi_scales, w, *ik, q_seq, n_vis_t, k, o["pidx"], o["pcnt"], o["blk"],
+                               o["bcnt"], 8, append=append)
+        torch.cuda.synchronize()
+        return o
+
+    ref_c = case.gpu_caches()
+    for qi, r in enumerate(rows):
+        if r < 0:
+            continue
+        b = int(wl.q_seq[qi])
+        C.csa2_quantize_kv(main[qi:qi + 1], C.FMT_NVFP4, ref_c.kv_codes[b, r:r + 1], ref_c.kv_scales[b, r:r + 1])
+        C.csa2_quantize_kv(index[qi:qi + 1], C.FMT_MXFP4, ref_c.ik_codes[b, r:r + 1], ref_c.ik_scales[b, r:r + 1])
+    ref = run(ref_c, None)
+    got_c = case.gpu_caches()
+    app = {"row": row_t, "main": main, "index": index, "kv_codes": got_c.kv_codes, "kv_scales": got_c.kv_scales}
+    got = run(got_c, app)
+    for name in ref:
+        assert torch.equal(got[name], ref[name]), name
+    for name in ("kv_codes", "kv_scales", "ik_codes", "ik_scales"):
+        assert torch.equal(getattr(got_c, name), getattr(ref_c, name)), name
+    # the appended rows differ from what the caches held before (the check is not vacuous)
+    before = case.gpu_caches()
+    for qi, r in enumerate(rows):
+        b = int(wl.q_seq[qi])
+        same = torch.equal(got_c.ik_codes[b, max(r, 0)], before.ik_codes[b, max(r, 0)])
+        assert same == (r < 0), (qi, r)
+    del before
+    # indexer-K only (no main latents), and an unquantised Q on top: still the same results
+    got2_c = case.gpu_caches()
+    got2 = run(got2_c, {"row": row_t, "index": index})
+    for name in ref:
+        assert torch.equal(got2[name], ref[name]), name
+    assert torch.equal(got2_c.ik_codes, ref_c.ik_codes) and torch.equal(got2_c.ik_scales, ref_c.ik_scales)
+    keys_q = torch.full_like(ref["keys"], 77)
+    C.csa2_index_segments(q_idx, None, w, got2_c.ik_codes, got2_c.ik_scales, q_seq, n_vis_t, k, keys_q,
+                          append={"row": row_t, "index": index})
+    torch.cuda.synchronize()
+    assert torch.equal(keys_q, ref["keys"])
+
+
 def _run_index_topk(C, st, caches, w, q_seq, n_vis, k, in_pool=False):
     """(fused idx, count), (two-call idx, count) on the same inputs."""
     idx_f = torch.full((st.n_q, k), 77, dtype=torch.int32, device="cuda")
