@@ -226,6 +226,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   const int main_hi = a.main_tiles < tile_hi ? a.main_tiles : tile_hi;
   const int n_main = main_hi > tile_lo ? main_hi - tile_lo : 0;
 
+  // ---- this pair's tiles: window tiles first (their rows need no index), then main tiles;
+  // pair p takes positions p, p+4, ... of that order.  Every wave runs the same number of
+  // steps (one exchange with its partner each) and masks the steps past its pair's end ----
+  const int span = tile_hi - tile_lo;
+  const int n_win = span - n_main;
+  const int n_steps = (span + kPairs - 1) / kPairs;
+  const int n_my = span > pair ? (span - pair + kPairs - 1) / kPairs : 0;
+  auto my_tile = [&](int i) {
+    const int j = pair + kPairs * (i < n_my ? i : (n_my > 0 ? n_my - 1 : 0));
+    return j < n_win ? tile_lo + n_main + j : tile_lo + (j - n_win);
+  };
+
   // ---- the query's sequence and positions head the memory queue (scalar loads), then this
   // split's slice of the index list (it does not depend on them), then Q ----
   const int seq = q_seq[q];
@@ -325,6 +337,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
       iv[r] = a.idx[(int64_t)q * a.k + (slot < a.k ? slot : a.k - 1)];
     }
   }
+  // A given index list: this lane's keys of its first three tiles are read straight from it
+  // (one load each, all issued before any is waited for), so their gathers need neither the
+  // list staged in LDS nor the prologue's barrier.  A window tile or a slot past k gets -1.
+  int32_t idx0[3] = {-1, -1, -1};
+  if constexpr (!kSelect) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int tile = my_tile(i);
+      if (tile < main_hi) {   // uniform over the wave: a main tile of this split
+        const int slot = tile * kT + col;
+        const int32_t v = a.idx[(int64_t)q * a.k + (slot < a.k ? slot : a.k - 1)];
+        idx0[i] = slot < a.k ? v : -1;
+      }
+    }
+  }
 
   // ---- Q of head (hg*16 + col): step st of this wave holds channels
   //      256*half + 64*grp + 8*st .. +7 (the same channel order as the K operand) ----
@@ -372,30 +399,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.kv_cs;
   const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.kv_ss;
   const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_rs;
-  // ---- this pair's tiles: window tiles first (their rows need no index), then main tiles;
-  // pair p takes positions p, p+4, ... of that order.  Every wave runs the same number of
-  // steps (one exchange with its partner each) and masks the steps past its pair's end ----
-  const int span = tile_hi - tile_lo;
-  const int n_win = span - n_main;
-  const int n_steps = (span + kPairs - 1) / kPairs;
-  const int n_my = span > pair ? (span - pair + kPairs - 1) / kPairs : 0;
-  auto my_tile = [&](int i) {
-    const int j = pair + kPairs * (i < n_my ? i : (n_my > 0 ? n_my - 1 : 0));
-    return j < n_win ? tile_lo + n_main + j : tile_lo + (j - n_win);
-  };
-
   // Every gather load is unconditional, to an in-bounds address (an absent key reads row 0
   // and is flagged), so no branch sits around the loads of the ring.  Lane (col, grp)
   // fetches key col of the tile, channels 256*half + 64*grp .. +63.
-  auto load_slot = [&](int tile, bool real, GatherSlot& g) {
+  auto load_slot = [&](int tile, bool real, GatherSlot& g, const int32_t* direct = nullptr) {
     const bool is_main = tile < a.main_tiles;  // wave-uniform
     int si = (tile - tile_lo) * kT + col;
     si = si < 0 ? 0 : (si >= n_main * kT ? (n_main > 0 ? n_main * kT - 1 : 0) : si);
     // with kSelect s_idx holds the whole list (k entries, -1 padded), and a main tile's
     // slots from k on (the last tile when k is not a multiple of 16) are empty; otherwise
-    // s_idx is this split's slice
+    // s_idx is this split's slice, or the key comes from `direct` (read from the list)
     const int slot = tile_lo * kT + si;
-    const int32_t pv = s_idx[kSelect ? (slot < a.k ? slot : a.k - 1) : si];
+    const int32_t pv = direct ? *direct : s_idx[kSelect ? (slot < a.k ? slot : a.k - 1) : si];
     const int32_t p = (kSelect && slot >= a.k) ? -1 : pv;
     const bool ok_main = real && is_main && seq_ok && p >= 0 && p < a.seq_cap;
     const uint32_t pm = ok_main ? (uint32_t)p : 0u;
@@ -417,13 +432,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     g.ok = is_main ? ok_main : ok_win;
   };
 
-  // The first two tiles of every key stream are window tiles when the slice holds at least
-  // 2 * kPairs of them (always without a key split); their rows need no index, so their
-  // gathers go out before the wait for the index list.  Either way the ring slots are filled
-  // in the order g0, g1, g2.
+  // With a given index list the first three gathers of every key stream go out here, their
+  // keys read directly (idx0).  When the list is selected in this kernel, the first two
+  // tiles of every key stream are window tiles when the slice holds at least 2 * kPairs of
+  // them (always without a key split); their rows need no index, so their gathers go out
+  // before the selection.  Either way the ring slots are filled in the order g0, g1, g2.
   const bool early = n_win >= 2 * kPairs;   // uniform over the workgroup
   GatherSlot g0, g1, g2;
-  if (early) {
+  if constexpr (!kSelect) {   // the given list: all three gathers now (keys read directly)
+    load_slot(my_tile(0), 0 < n_my, g0, &idx0[0]);
+    load_slot(my_tile(1), 1 < n_my, g1, &idx0[1]);
+    load_slot(my_tile(2), 2 < n_my, g2, &idx0[2]);
+  } else if (early) {
     load_slot(my_tile(0), 0 < n_my, g0);
     load_slot(my_tile(1), 1 < n_my, g1);
   }
@@ -470,7 +490,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   }
   if (lane == 0) s_flag[wave] = 0u;
   __syncthreads();  // s_idx, s_flag, s_qmax
-  if (!early) {
+  if (kSelect && !early) {
     load_slot(my_tile(0), 0 < n_my, g0);
     load_slot(my_tile(1), 1 < n_my, g1);
   }
@@ -639,7 +659,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   // cores and the vector units.  The raw bytes of tiles i+2 .. i+4 are in flight meanwhile:
   // ring slot (i+1) % 3 is refilled with tile i+4 as soon as tile i+1 has left it ----
   auto tile_is_main = [&](int i) { return my_tile(i) < a.main_tiles; };
-  load_slot(my_tile(2), 2 < n_my, g2);
+  if constexpr (kSelect) load_slot(my_tile(2), 2 < n_my, g2);
 #pragma unroll
   for (int st = 0; st < kQS; ++st) {
     const uint32_t w4[4] = {qraw[st].x, qraw[st].y, qraw[st].z, qraw[st].w};
