@@ -328,28 +328,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
       const bool ok = c < nslot && bv[i] >= 0 && pos < nv;
       key[i] = make_key(v[i], (uint32_t)pos) & (0ull - (uint64_t)ok);
     }
-  } else if (n_keys > 0) {  // uniform; idx may be absent when k == 0
+  }
+  // A given index list: this thread's slice of it (staged in LDS below), and this lane's keys
+  // of its first three tiles, read straight from it so that their gathers need neither the
+  // staged list nor the prologue's barrier (a slot past k gets -1).  All of
+  // these loads are unconditional, from clamped in-bounds addresses (q_seq stands in for an
+  // absent list when k == 0), and branch-free: a load inside a branch would be waited for
+  // at the branch's end, one memory round trip after another.
+  int32_t idx0[3] = {-1, -1, -1};
+  if constexpr (!kSelect) {
+    const bool have = a.k > 0;
+    const int32_t* ib = have ? a.idx + (int64_t)q * a.k : q_seq;
+    const int klast = have ? a.k - 1 : 0;
 #pragma unroll
     for (int r = 0; r < kIdxPer; ++r) {
       int i = tid + r * kAttnThreads;
-      i = i < n_keys ? i : n_keys - 1;              // in-bounds, unconditional loads
+      i = i < n_keys ? i : (n_keys > 0 ? n_keys - 1 : 0);
       const int slot = tile_lo * kT + i;
-      iv[r] = a.idx[(int64_t)q * a.k + (slot < a.k ? slot : a.k - 1)];
+      iv[r] = ib[slot < klast ? slot : klast];
     }
-  }
-  // A given index list: this lane's keys of its first three tiles are read straight from it
-  // (one load each, all issued before any is waited for), so their gathers need neither the
-  // list staged in LDS nor the prologue's barrier.  A window tile or a slot past k gets -1.
-  int32_t idx0[3] = {-1, -1, -1};
-  if constexpr (!kSelect) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int tile = my_tile(i);
-      if (tile < main_hi) {   // uniform over the wave: a main tile of this split
-        const int slot = tile * kT + col;
-        const int32_t v = a.idx[(int64_t)q * a.k + (slot < a.k ? slot : a.k - 1)];
-        idx0[i] = slot < a.k ? v : -1;
-      }
+      const int slot = tile * kT + col;
+      const int32_t v = ib[slot < klast ? slot : klast];
+      idx0[i] = slot < a.k ? v : -1;   // (load_slot ignores it for a window tile)
     }
   }
 
@@ -364,15 +367,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
 
   // Window append: thread c quantises channel c of the row's new window latent (the
   // quantiser's exact E4M3 rounding); the bytes are staged in LDS for this workgroup's own
-  // window tiles, and workgroup (head group 0, split 0) writes them to the ring.
+  // window tiles, and workgroup (head group 0, split 0) writes them to the ring.  The latent
+  // is loaded here and converted just before the prologue's barrier: a wait for it here
+  // would wait for every load issued before it and hold back the per-query scalars below.
   static_assert(kAttnThreads == kD, "one thread per channel of the appended window entry");
   __shared__ __attribute__((aligned(16))) uint8_t s_new[kD];
-  uint32_t new_code = 0;
-  if (a.new_win) {  // uniform
-    const uint32_t bits = a.new_win_bf16 ? (uint32_t)reinterpret_cast<const uint16_t*>(a.new_win)[(int64_t)q * kD + tid] << 16
-                                         : reinterpret_cast<const uint32_t*>(a.new_win)[(int64_t)q * kD + tid];
-    new_code = fp8_code_bits(bits);
-    s_new[tid] = (uint8_t)new_code;
+  // One unconditional 32-bit load (branch-free, see above): an f32 element, or the word
+  // holding this bf16 element (Q stands in when there is no latent)
+  uint32_t new_bits;
+  {
+    const int64_t e = (int64_t)q * kD + tid;
+    const uint32_t* nwp = reinterpret_cast<const uint32_t*>(a.new_win ? a.new_win : (const void*)a.q);
+    const uint32_t w = nwp[a.new_win_bf16 || !a.new_win ? e >> 1 : e];
+    new_bits = a.new_win_bf16 ? ((tid & 1) ? (w & 0xffff0000u) : (w << 16)) : w;
   }
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   const int64_t lo = s > t - a.window + 1 ? s : t - a.window + 1;
@@ -390,12 +397,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     r_lo = r_lo < 0 ? r_lo + a.swa_cap : r_lo;
   }
   const uint32_t win_row0 = (uint32_t)r_lo;
-  if (a.new_win && hg == 0 && split == 0 && seq_ok && t >= 0) {
-    // ring row of token t: the window keys [lo, t] are consecutive rows from win_row0
-    int64_t rt = (t - swa_b) % a.swa_cap;
-    rt = rt < 0 ? rt + a.swa_cap : rt;
-    a.swa_w[(int64_t)seq * a.swa_rs + rt * a.swa_re + tid] = (uint8_t)new_code;
-  }
   const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.kv_cs;
   const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.kv_ss;
   const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_rs;
@@ -488,8 +489,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     qm = o > qm ? o : qm;
     if (pair == 0 && grp == 0) s_qmax[half][col] = qm;
   }
+  if (a.new_win) {  // uniform: the window append (see above)
+    const uint32_t new_code = fp8_code_bits(new_bits);
+    s_new[tid] = (uint8_t)new_code;
+    if (hg == 0 && split == 0 && seq_ok && t >= 0) {
+      // ring row of token t: the window keys [lo, t] are consecutive rows from win_row0
+      int64_t rt = (t - swa_b) % a.swa_cap;
+      rt = rt < 0 ? rt + a.swa_cap : rt;
+      a.swa_w[(int64_t)seq * a.swa_rs + rt * a.swa_re + tid] = (uint8_t)new_code;
+    }
+  }
   if (lane == 0) s_flag[wave] = 0u;
-  __syncthreads();  // s_idx, s_flag, s_qmax
+  __syncthreads();  // s_idx, s_flag, s_qmax, s_new
   if (kSelect && !early) {
     load_slot(my_tile(0), 0 < n_my, g0);
     load_slot(my_tile(1), 1 < n_my, g1);
@@ -1237,6 +1248,7 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, CacheRef kv
     return CSA2_ERR_SHAPE;
   if (out_dtype != CSA2_DT_F32 && out_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
   if (new_win && new_win_dtype != CSA2_DT_F32 && new_win_dtype != CSA2_DT_BF16) return CSA2_ERR_UNSUPPORTED;
+  if ((uintptr_t)new_win & 3) return CSA2_ERR_SHAPE;   // read in 32-bit words
   if (!aligned16(q) || !aligned16(kv.codes) || !aligned16(swa) || !aligned16(out) || ((uintptr_t)kv.scales & 3))
     return CSA2_ERR_SHAPE;
   // the main-KV cache (D/2 code bytes, D/16 scale bytes per entry; 4-byte scale loads) and

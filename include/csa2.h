@@ -503,7 +503,7 @@ size_t csa2_pool_workspace_bytes(int n_q, int64_t max_vis, int block, int max_bl
  *   swa, swa_row_stride, swa_seq_stride   the window ring (E4M3 rows of dim bytes; see Cache
  *             layouts); swa_base [n_seq] int64; window in 1..1024 and window <= swa_cap <=
  *             CSA2_MAX_WINDOW_ROWS; seq_cap <= CSA2_MAX_ATTN_ENTRIES
- *   new_win   NULL, or [n_q, dim] f32 / bf16 (new_win_dtype): the post-RoPE window latent of
+ *   new_win   NULL, or [n_q, dim] f32 / bf16 (new_win_dtype; 4-byte aligned): the post-RoPE window latent of
  *             each row's own token t = q_pos[q].  The call appends it first: quantised to
  *             E4M3 exactly as csa2_quantize_kv with CSA2_FMT_FP8 writes it, stored at ring
  *             row (t - swa_base[seq]) mod swa_cap of sequence q_seq[q], and attended as
