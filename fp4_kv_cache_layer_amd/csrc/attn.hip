@@ -782,12 +782,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   }
 }
 
-// merge the per-split (O, m, l) of one (query, head): 128 threads x 4 channels.  Thread
-// sp < nsplit reads split sp's (m, l) into LDS; the partial outputs are read eight splits
-// at a time with unconditional (clamped) loads and weights that are zero past the last
-// split, so the merge costs a few memory round trips instead of two per split.  (Merging
-// inside the attention kernel, in the last split's workgroup to finish, was measured much
-// slower: the agent-scope release that publishes the partial results writes back the L2.)
+// merge the per-split (O, m, l) of one (query, head): 128 threads x 4 channels.  The first
+// eight splits' partial outputs are loaded first (they do not depend on (m, l)), while
+// thread sp < nsplit reads split sp's (m, l) into LDS, so up to eight splits cost one memory
+// round trip; further splits are read eight at a time.  Every load is unconditional (clamped
+// split index) and the weights past the last split are zero.  (Merging inside the attention
+// kernel, in the last split's workgroup to finish, was measured much slower: the agent-scope
+// release that publishes the partial results writes back the L2.)
 constexpr int kCombThreads = 128;   // also the most splits a merge takes
 
 __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
@@ -796,35 +797,40 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
   const int ns = a.nsplit;
   const int64_t stride = (int64_t)a.n_q * a.n_heads;
   __shared__ float s_m[kCombThreads], s_l[kCombThreads];
-  if (tid < ns) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (tid * stride + qh) * 2);
-    s_m[tid] = ml.x;
-    s_l[tid] = ml.y;
+  auto load8 = [&](int sp0, float4 (&v)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = sp0 + u < ns ? sp0 + u : ns - 1;
+      v[u] = *reinterpret_cast<const float4*>(a.ws_o + (sp * stride + qh) * kD + tid * 4);
+    }
+  };
+  float4 v[8];
+  load8(0, v);
+  {
+    const int sp = tid < ns ? tid : ns - 1;
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (sp * stride + qh) * 2);
+    if (tid < ns) {
+      s_m[tid] = ml.x;
+      s_l[tid] = ml.y;
+    }
   }
   __syncthreads();
   float M = -__builtin_inff();
   for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_m[sp]);
   float L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (M != -__builtin_inff()) {
-    for (int sp0 = 0; sp0 < ns; sp0 += 8) {
-      float4 v[8];
+  for (int sp0 = 0; sp0 < ns && M != -__builtin_inff(); sp0 += 8) {
+    if (sp0 > 0) load8(sp0, v);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int sp = sp0 + u < ns ? sp0 + u : ns - 1;
-        v[u] = *reinterpret_cast<const float4*>(a.ws_o + (sp * stride + qh) * kD + tid * 4);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int sp = sp0 + u < ns ? sp0 + u : ns - 1;
-        const float m = s_m[sp];
-        const float wgt = (sp0 + u < ns && m != -__builtin_inff()) ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
-        L += wgt * s_l[sp];
-        acc.x += wgt * v[u].x;
-        acc.y += wgt * v[u].y;
-        acc.z += wgt * v[u].z;
-        acc.w += wgt * v[u].w;
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int sp = sp0 + u < ns ? sp0 + u : ns - 1;
+      const float m = s_m[sp];
+      const float wgt = (sp0 + u < ns && m != -__builtin_inff()) ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+      L += wgt * s_l[sp];
+      acc.x += wgt * v[u].x;
+      acc.y += wgt * v[u].y;
+      acc.z += wgt * v[u].z;
+      acc.w += wgt * v[u].w;
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
