@@ -48,6 +48,7 @@
 // the pool's slot scores; see k_attn's kSel) and, in single-token decode, the append of the
 // row's own window entry (new_win).
 #include <mutex>
+#include <type_traits>
 
 #include "select.h"
 
@@ -282,52 +283,72 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
     const float* sp = a.pool_scores + (int64_t)q * a.pool_stride;
     const int32_t* cb = a.cand_blocks + (int64_t)q * a.max_cand_blocks;
     const uint32_t c0 = (uint32_t)tid * kEpt;
-    uint32_t sb[kEpt], so[kEpt];
-    {
-      uint32_t b = c0 / blk, o = c0 % blk;
-#pragma unroll
-      for (int i = 0; i < kEpt; ++i) {
-        sb[i] = b;
-        so[i] = o;
-        const bool carry = o + 1u == blk;
-        o = carry ? 0u : o + 1u;
-        b += carry ? 1u : 0u;
-      }
-    }
-    int32_t bv[kEpt];
-    float v[kEpt];
     const uint32_t last_blk = (uint32_t)a.max_cand_blocks - 1u;
-#pragma unroll
-    for (int i = 0; i < kEpt; ++i) bv[i] = cb[sb[i] < last_blk ? sb[i] : last_blk];
-    if ((uint32_t)(wave + 1) * 64u * kEpt <= row_slots) {
-      typedef float f32x4 __attribute__((ext_vector_type(4), aligned(4)));
-#pragma unroll
-      for (int i = 0; i < kEpt; i += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(sp + c0 + i);
-        v[i] = x.x;
-        v[i + 1] = x.y;
-        v[i + 2] = x.z;
-        v[i + 3] = x.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kEpt; ++i) {
-        const uint32_t c = c0 + (uint32_t)i;
-        v[i] = sp[c < row_slots ? c : row_slots - 1u];
-      }
-    }
     int nc = a.n_cand_blocks[q];
     nc = nc < 0 ? 0 : (nc > a.max_cand_blocks ? a.max_cand_blocks : nc);
     int64_t nv = a.n_vis[q];
     nv = nv < 0 ? 0 : (nv > a.seq_cap ? a.seq_cap : nv);
     const uint32_t nslot = (uint32_t)nc * blk;   // <= 16,384
+    // Each path issues all of its loads (block ids, then scores) and builds the keys itself:
+    // only finished keys meet after the branch, so no load is waited for before the rest are
+    // issued.  kBlk8: the pool's 8-position blocks, a thread's 32 slots being blocks c0/8 ..
+    // c0/8 + 3 (four loads, one per 8 slots); otherwise each slot's block id is loaded, its
+    // block and offset advanced by one slot per step.
+    auto build = [&](auto blk8) {
+      constexpr bool kBlk8 = decltype(blk8)::value;
+      int32_t bv[kEpt];
+      uint32_t so[kEpt];
+      float v[kEpt];
+      if constexpr (kBlk8) {
+        int32_t b4[kEpt / 8];
 #pragma unroll
-    for (int i = 0; i < kEpt; ++i) {
-      const uint32_t c = c0 + (uint32_t)i;
-      const int64_t pos = (int64_t)bv[i] * blk + so[i];
-      const bool ok = c < nslot && bv[i] >= 0 && pos < nv;
-      key[i] = make_key(v[i], (uint32_t)pos) & (0ull - (uint64_t)ok);
-    }
+        for (int j = 0; j < kEpt / 8; ++j) {
+          const uint32_t bj = c0 / 8u + (uint32_t)j;
+          b4[j] = cb[bj < last_blk ? bj : last_blk];
+        }
+#pragma unroll
+        for (int i = 0; i < kEpt; ++i) {
+          bv[i] = b4[i / 8];
+          so[i] = (uint32_t)(i % 8);
+        }
+      } else {
+        uint32_t b = c0 / blk, o = c0 % blk;
+#pragma unroll
+        for (int i = 0; i < kEpt; ++i) {
+          bv[i] = cb[b < last_blk ? b : last_blk];
+          so[i] = o;
+          const bool carry = o + 1u == blk;
+          o = carry ? 0u : o + 1u;
+          b += carry ? 1u : 0u;
+        }
+      }
+      if ((uint32_t)(wave + 1) * 64u * kEpt <= row_slots) {   // uniform: 16 B score loads
+        typedef float f32x4 __attribute__((ext_vector_type(4), aligned(4)));
+#pragma unroll
+        for (int i = 0; i < kEpt; i += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(sp + c0 + i);
+          v[i] = x.x;
+          v[i + 1] = x.y;
+          v[i + 2] = x.z;
+          v[i + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kEpt; ++i) {
+          const uint32_t c = c0 + (uint32_t)i;
+          v[i] = sp[c < row_slots ? c : row_slots - 1u];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        const uint32_t c = c0 + (uint32_t)i;
+        const int64_t pos = (int64_t)bv[i] * blk + so[i];
+        const bool ok = c < nslot && bv[i] >= 0 && pos < nv;
+        key[i] = make_key(v[i], (uint32_t)pos) & (0ull - (uint64_t)ok);
+      }
+    };
+    if (blk == 8u) build(std::true_type{});   // uniform
+    else build(std::false_type{});
   }
   // A given index list: this thread's slice of it (staged in LDS below), and this lane's keys
   // of its first three tiles, read straight from it so that their gathers need neither the
