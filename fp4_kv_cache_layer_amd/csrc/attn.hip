@@ -36,8 +36,9 @@
 //     keys 4(l/16)..+3) is exactly the B-operand layout of V_MFMA_F32_16X16X16_F16, so P
 //     needs no shuffle; and accumulates O^T += V^T P^T over its 256 channels, V^T read from
 //     its V half-tile through DS_READ_B64_TR_B16 (each lane receives one channel of 4 keys).
-// Steps are software-pipelined: after the exchange of step i, P.V of tile i and the softmax
-// of tile i+1 are independent work.  At the end the four pairs merge (O, m, l) with the
+// Steps are software-pipelined: a wave posts its partial S of tile i+1, runs P.V of tile i
+// while its partner finishes, then collects the partner's half and runs the softmax of tile
+// i+1.  At the end the four pairs merge (O, m, l) with the
 // log-sum-exp rule through LDS.  The workgroups of one query are numbered so that they land
 // on the same XCD (dispatch is round-robin over the 8 XCDs) and share its L2 for the
 // gathered rows.  When a batch has too few queries to fill the GPU, the key list is split
@@ -120,6 +121,31 @@ struct AttnArgs {
   int wait_limit;
   uint32_t* status;
 };
+
+// Reductions over the lanes l, l^16, l^32, l^48 (the four lane groups of one MFMA column) in
+// the VALU, without an LDS round trip.  V_PERMLANE16_SWAP of a register with itself returns
+// the even 16-lane rows in its first result and the odd ones in its second, each row next to
+// its neighbour, so combining the two results pairs every lane with lane l^16;
+// V_PERMLANE32_SWAP does the same for the two halves of the wave (l^32).  The sum adds
+// (l + l^16) + (l^32 + l^48) in that grouping at every lane.
+__device__ __forceinline__ float lanes4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lanes4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ uint32_t lanes4_umax(uint32_t x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = a[0] > a[1] ? a[0] : a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return b[0] > b[1] ? b[0] : b[1];
+}
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -504,10 +530,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
         qm = hi > qm ? hi : qm;
       }
     }
-    uint32_t o = (uint32_t)__shfl_xor((int)qm, 16);
-    qm = o > qm ? o : qm;
-    o = (uint32_t)__shfl_xor((int)qm, 32);
-    qm = o > qm ? o : qm;
+    qm = lanes4_umax(qm);
     if (pair == 0 && grp == 0) s_qmax[half][col] = qm;
   }
   if (a.new_win) {  // uniform: the window append (see above)
@@ -606,8 +629,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
       x[r] = ok ? sv[r] * qsl : -__builtin_inff();
       mt = fmaxf(mt, x[r]);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = lanes4_max(mt);
     // Lazy rescaling: m_run is a reference, not necessarily the running maximum.  It moves
     // only when a logit exceeds it by more than 2^kLazy (or on the first key), so
     // p = 2^(x - m_run) <= 2^kLazy stays far inside fp16 and the accumulators are rescaled
@@ -652,20 +674,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   };
 
   // Combine this wave's partial S^T with its partner's.  Exchange number `id` goes through
-  // slot id % 2: the wave writes its slot, then its flag (id + 1), then waits for the
-  // partner's flag to reach id + 1 and reads the partner's slot.  Only the two waves of a
-  // stream synchronise, so the four streams drift freely.  Both waves make the same
-  // sequence of exchanges, so every wait is met; a slot is rewritten two exchanges later,
-  // which the writer can only reach after the partner's flag shows the read was done.  The
+  // slot id % 2: the wave writes its slot, then its flag (id + 1) (post); later it waits for
+  // the partner's flag to reach id + 1 and reads the partner's slot (collect).  Between the
+  // two a wave does work that does not need the partner (the previous tile's P.V).  Only the
+  // two waves of a stream synchronise, so the four streams drift freely.  Both waves make
+  // the same sequence of exchanges, each posting before it collects, so every wait is met; a
+  // slot is rewritten two exchanges later, which the writer can only reach after the
+  // partner's flag shows the read was done (a wave posts only after its last collect).  The
   // wait is bounded so that it always ends; a wait that gives up stores a nonzero code
   // into the library's status word, which the host reports at its next call (the output
   // of this call is then not to be trusted).  Both waves add in the same order up to
   // commutation, so the pair holds bit-identical S^T, softmax state and P.
-  auto exchange = [&](v4f own, int id) -> v4f {
-    const int sl = id & 1;
-    sx[(wave * 2 + sl) * 64 + lane] = make_float4(own[0], own[1], own[2], own[3]);
+  auto post = [&](v4f own, int id) {
+    sx[(wave * 2 + (id & 1)) * 64 + lane] = make_float4(own[0], own[1], own[2], own[3]);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) __hip_atomic_store(&s_flag[wave], (uint32_t)(id + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  auto collect = [&](v4f own, int id) -> v4f {
+    const int sl = id & 1;
     bool seen = false;
     for (int spin = 0; spin < a.wait_limit; ++spin) {
       if (__hip_atomic_load(&s_flag[partner], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= (uint32_t)(id + 1)) {
@@ -686,9 +712,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   auto lds_order = [] { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); };
 
   // ---- software pipeline.  Step i dequantises tile i+1 into V buffer (i+1) % 2, forms its
-  // partial S and exchanges it with its partner (the step's one wait); after that P.V of
-  // tile i (buffer i % 2) and the softmax of tile i+1 are independent work for the matrix
-  // cores and the vector units.  The raw bytes of tiles i+2 .. i+4 are in flight meanwhile:
+  // partial S and posts it to its partner; P.V of tile i (buffer i % 2) then keeps the
+  // matrix cores busy until the partner's half is collected (the step's one wait), and the
+  // softmax of tile i+1 follows.  The raw bytes of tiles i+2 .. i+4 are in flight meanwhile:
   // ring slot (i+1) % 3 is refilled with tile i+4 as soon as tile i+1 has left it ----
   auto tile_is_main = [&](int i) { return my_tile(i) < a.main_tiles; };
   if constexpr (kSelect) load_slot(my_tile(2), 2 < n_my, g2);
@@ -707,15 +733,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   float alpha;
   v4f sp = qk_tile(g0, tile_is_main(0), vbuf, &vmask);
   load_slot(my_tile(3), 3 < n_my, g0);
-  v4h pb = softmax_tile(exchange(sp, 0), vmask, &alpha);
+  post(sp, 0);
+  v4h pb = softmax_tile(collect(sp, 0), vmask, &alpha);
 
   auto step = [&](int i, GatherSlot& g) {
     const int nb = (i + 1) & 1;
     lds_order();
     sp = qk_tile(g, tile_is_main(i + 1), vbuf + nb * kVBuf, &vmask);
     load_slot(my_tile(i + 4), i + 4 < n_my, g);
-    const v4f sv = exchange(sp, i + 1);
-    pv_tile(pb, vbuf + (nb ^ 1) * kVBuf);   // tile i
+    post(sp, i + 1);
+    pv_tile(pb, vbuf + (nb ^ 1) * kVBuf);   // tile i, while the partner finishes tile i+1
+    const v4f sv = collect(sp, i + 1);
     pb = softmax_tile(sv, vmask, &alpha);   // tile i+1
     rescale(alpha);
   };
@@ -735,8 +763,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   if (n_steps > 0) pv_tile(pb, vbuf + (n_full & 1) * kVBuf);   // tile n_steps-1
 
   // ---- merge the four pairs' (O, m, l); the two waves of a pair hold the same (m, l) ----
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot = l_tot + __shfl_xor(l_tot, 32);
+  float l_tot = lanes4_sum(l_run);
   if (half == 0 && lane < kHG) {
     s_ml[pair][lane][0] = m_run;
     s_ml[pair][lane][1] = l_tot;
@@ -1042,10 +1069,7 @@ __global__ __launch_bounds__(kRThreads, 1) void k_attn_rows(AttnArgs a, const in
     }
   }
   {
-    uint32_t o = (uint32_t)__shfl_xor((int)qm, 16);
-    qm = o > qm ? o : qm;
-    o = (uint32_t)__shfl_xor((int)qm, 32);
-    qm = o > qm ? o : qm;
+    qm = lanes4_umax(qm);
   }
   const int qsh = q_shift(qm);
   const float qsl = ldexpf(a.scale_log2, qsh);
@@ -1104,8 +1128,7 @@ __global__ __launch_bounds__(kRThreads, 1) void k_attn_rows(AttnArgs a, const in
       x[r] = ok ? s2[r >> 2][r & 3] * qsl : -__builtin_inff();
       mt = fmaxf(mt, x[r]);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = lanes4_max(mt);
     const bool first = m_run == -__builtin_inff();
     const bool move = first ? mt != -__builtin_inff() : mt > m_run + kLazy;
     const float m_new = move ? mt : m_run;
@@ -1178,8 +1201,7 @@ __global__ __launch_bounds__(kRThreads, 1) void k_attn_rows(AttnArgs a, const in
   pv(pb, (n_tiles - 1) % kRBufs);
 
   // ---- output: lane (head col, grp) holds channels 16*dt + 4*grp .. +3 of its head ----
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot = l_tot + __shfl_xor(l_tot, 32);
+  float l_tot = lanes4_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const int64_t ob = ((int64_t)q * a.n_heads + head) * kD + 4 * grp;
 #pragma unroll
