@@ -290,18 +290,34 @@ class Append(ctypes.Structure):
                 ("kv_scales_stride", ctypes.c_int64), ("kv_scales_seq_stride", ctypes.c_int64)]
 
 
-def _append_arg(append, n_q: int, seq_cap: int):
+def _check_append_sequences(row, q_seq, seq_cap: int) -> None:
+    """Raises ValueError when a query of the call shares its sequence with a query that
+    appends (row in [0, seq_cap)): that query's row is written while the call runs."""
+    seqs = q_seq[(row >= 0) & (row < seq_cap)]
+    if seqs.numel():
+        vals, counts = torch.unique(q_seq, return_counts=True)
+        if bool((counts[torch.searchsorted(vals, seqs)] != 1).any()):
+            raise ValueError("append: another query of the call reads the sequence of an appending query")
+
+
+def _append_arg(append, n_q: int, seq_cap: int, q_seq):
     """append: None, or a dict with row ([n_q] int64: the new entry's row in the query's
     sequence, negative for none), main ([n_q, 512] latents or None) with kv_codes / kv_scales
     (the main-KV cache views, as for csa2_sparse_attn), and index ([n_q, 128] latents or
     None; written into the call's indexer-K cache).  Latents f32 or bf16 (both the same),
-    contiguous.  Returns the C argument (a pointer to a csa2_append, or None)."""
+    contiguous.  No other query of the call may read the sequence of a query that appends
+    (row in [0, seq_cap)); that is checked once per call or per bound callable, with one
+    read of row and q_seq (not while the stream is being captured into a graph: calls
+    recorded there are bound and checked before the capture).  Returns the C argument (a
+    pointer to a csa2_append, or None)."""
     if append is None:
         return None
     row, main, index = append["row"], append.get("main"), append.get("index")
     _need(row, torch.int64, 1, "append row")
     if row.shape[0] != n_q:
         raise ValueError("append: row must have n_q entries")
+    if n_q > 1 and not torch.cuda.is_current_stream_capturing():
+        _check_append_sequences(row, q_seq, seq_cap)
     dts = {t.dtype for t in (main, index) if t is not None}
     if len(dts) != 1 or not dts <= {torch.float32, torch.bfloat16}:
         raise ValueError("append: main / index latents f32 or bf16, the same for both, at least one")
@@ -421,7 +437,7 @@ def csa2_index_topk(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k: in
         raise ValueError("index_topk: inconsistent output shapes")
     need = csa2_index_topk_workspace_bytes(n_q, max(n_slots, 1), k, cand_blocks is not None)
     workspace, ws_bytes = _workspace(need, workspace, q_codes.device, _bind, "index_topk")
-    app = _append_arg(append, n_q, k_codes.shape[1])
+    app = _append_arg(append, n_q, k_codes.shape[1], q_seq)
     return _run("csa2_index_topk", args + (k, _p(idx_out), _p(count_out), _p(workspace), ws_bytes, app, _stream()),
                 _bind)
 
@@ -440,7 +456,7 @@ def csa2_index_segments(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, k
     n_q = q_codes.shape[0]
     if tuple(cand_keys.shape) != (n_q, csa2_segment_keys(n_slots, k)):
         raise ValueError("index_segments: cand_keys must be [n_q, csa2_segment_keys(seq_cap, k)]")
-    app = _append_arg(append, n_q, k_codes.shape[1])
+    app = _append_arg(append, n_q, k_codes.shape[1], q_seq)
     return _run("csa2_index_segments", args[:17] + (k, _p(cand_keys), app, _stream()), _bind)
 
 
@@ -466,7 +482,7 @@ def csa2_index_topk_pool(q_codes, q_scales, w, k_codes, k_scales, q_seq, n_vis, 
         raise ValueError("index_topk_pool: inconsistent output shapes")
     need = csa2_index_topk_pool_workspace_bytes(n_q, max(n_slots, 1), k, block, max_blocks)
     workspace, ws_bytes = _workspace(max(need, 1), workspace, q_codes.device, _bind, "index_topk_pool")
-    app = _append_arg(append, n_q, k_codes.shape[1])
+    app = _append_arg(append, n_q, k_codes.shape[1], q_seq)
     return _run("csa2_index_topk_pool", args[:17] + (k, _p(idx_out), _p(count_out), block, max_blocks, _p(blocks_out),
                                                      _p(blocks_count), _p(workspace), ws_bytes, app, _stream()),
                 _bind)

@@ -220,3 +220,17 @@ def test_select_in_attention_validation(L):
     assert _call(L, "csa2_sparse_attn_pool_topk", **dict(pool, scores_stride=1000)) == -2
     assert _call(L, "csa2_sparse_attn_pool_topk", **dict(pool, block=0)) == -2
     assert _call(L, "csa2_sparse_attn_pool_topk", **pool) == -5
+
+
+def test_append_needs_its_sequence_alone():
+    """A query that appends a row writes it while the call runs, so no other query of the
+    call may read that sequence; the binding checks it before anything is launched."""
+    import torch
+    from fp4_kv_cache_layer_amd import csa2 as C
+    row = torch.tensor([5, 7, -1, 9], dtype=torch.int64)      # queries 0, 1 and 3 append
+    ok = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
+    C._check_append_sequences(row, ok, 100)
+    C._check_append_sequences(row, torch.tensor([0, 1, 2, 2], dtype=torch.int32), 8)   # row 9 is past seq_cap
+    for bad in ([0, 0, 2, 3], [0, 1, 1, 3], [3, 1, 2, 3]):    # two appenders, or an appender and a reader
+        with pytest.raises(ValueError):
+            C._check_append_sequences(row, torch.tensor(bad, dtype=torch.int32), 100)
