@@ -65,9 +65,10 @@ class LayerBench:
         for b in range(wl.n_seq):
             for r0 in range(0, wl.seq_cap, chunk):
                 n = min(chunk, wl.seq_cap - r0)
-                lat = torch.from_numpy(wl.main_latents(b, r0, n)).to(dev)
+                main = wl.main_latents(b, r0, n)
+                lat = torch.from_numpy(main).to(dev)
                 C.csa2_quantize_kv(lat, C.FMT_NVFP4, caches.kv_codes[b, r0:r0 + n], caches.kv_scales[b, r0:r0 + n])
-                ik = torch.from_numpy(wl.index_k_latents(b, r0, n)).to(dev)
+                ik = torch.from_numpy(wl.index_k_latents(b, r0, n, main=main)).to(dev)
                 C.csa2_quantize_kv(ik, self.ik_fmt, caches.ik_codes[b, r0:r0 + n], caches.ik_scales[b, r0:r0 + n])
             t = int(wl.q_pos[wl.q_seq == b].max())
             p0 = max(0, t - wl.swa_cap + 1)

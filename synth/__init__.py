@@ -51,7 +51,7 @@ def _load():
 
 
 # tensor kinds: each (kind, layer, sequence) triple is an independent stream
-MAIN_LATENT, INDEX_K_LATENT, INDEX_Q, INDEX_W, ATTN_Q, SWA_LATENT = 1, 2, 3, 4, 5, 6
+MAIN_LATENT, INDEX_Q, INDEX_W, ATTN_Q, SWA_LATENT, INDEX_PROJ = 1, 3, 4, 5, 6, 7   # tensor kinds
 
 
 def tensor_id(kind: int, layer: int = 0, seq: int = 0) -> int:

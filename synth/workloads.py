@@ -8,9 +8,11 @@ same entries, a per-layer FP8 sliding-window cache, and a set of query rows
 Value recipe (all seeded, see ``synth.c``):
   main-KV latent   N(0,1)^512 -> RMS norm (unit weight) -> rotary embedding on
                    the last 64 channels at position entry*m, fp32
-  indexer-K latent N(0,1)^128, fp32 (a stand-in for the learned projection of
-                   the main latent; such a projection of an isotropic Gaussian
-                   is again a Gaussian of about unit variance per channel)
+  indexer-K latent a fixed seeded projection of the main-KV latent of the same
+                   entry: channel c = (+-x[c] +- x[c+128] +- x[c+256] +- x[c+384]) / 2
+                   with seeded signs (a stand-in for the learned projection: about
+                   unit variance per channel, and the indexer ranks the same token
+                   states the attention reads), fp32
   SWA latent       as the main latent, one row per token position, per layer
   indexer Q        N(0,1)^(H_I*128), fp32, per layer and query row
   indexer weight   U(0,1)^H_I, fp32, per layer and query row
@@ -20,9 +22,12 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
+import functools
+import math
+
 import numpy as np
 
-from . import (ATTN_Q, INDEX_K_LATENT, INDEX_Q, INDEX_W, MAIN_LATENT, SWA_LATENT,
+from . import (ATTN_Q, INDEX_PROJ, INDEX_Q, INDEX_W, MAIN_LATENT, SWA_LATENT,
                latent_rows, normal_bf16_bits, normal_f32, tensor_id, uniform_f32)
 
 DIM = 512          # main-KV latent channels
@@ -31,6 +36,16 @@ TOPK = 512         # entries kept per query
 WINDOW = 128       # sliding-window length
 BLOCK = 8          # pool block size (positions)
 MAX_BLOCKS = 2048  # pool capacity in blocks
+
+
+
+@functools.lru_cache(maxsize=4)
+def index_projection(seed: int) -> np.ndarray:
+    """The fixed projection from the main-KV latent to the indexer-K latent: indexer channel
+    c is (s0*x[c] + s1*x[c+128] + s2*x[c+256] + s3*x[c+384]) / 2 with seeded signs s
+    (every main channel feeds one indexer channel).  Returns the signs, [4, 128] f32."""
+    u = uniform_f32(seed, tensor_id(INDEX_PROJ), 0, DIM)
+    return np.where(u < 0.5, -1.0, 1.0).astype(np.float32).reshape(4, IDX_DIM)
 
 
 @dataclass
@@ -65,9 +80,17 @@ class Workload:
     def main_latents(self, seq: int, row0: int, rows: int) -> np.ndarray:
         return latent_rows(self.seed, tensor_id(MAIN_LATENT, 0, seq), row0, rows, DIM, 64, self.m)
 
-    def index_k_latents(self, seq: int, row0: int, rows: int) -> np.ndarray:
-        t = tensor_id(INDEX_K_LATENT, 0, seq)
-        return normal_f32(self.seed, t, row0 * IDX_DIM, rows * IDX_DIM).reshape(rows, IDX_DIM)
+    def index_k_latents(self, seq: int, row0: int, rows: int, main: np.ndarray | None = None) -> np.ndarray:
+        """Rows [row0, row0+rows) of the indexer-K latent: the main-KV latent of the same
+        entries (`main`, when the caller already holds those rows) through the fixed seeded
+        projection of index_projection, so each channel keeps unit variance and the indexer
+        ranks the same token states the attention reads.  f32 sums in a fixed order (exactly
+        reproducible)."""
+        s = index_projection(self.seed)
+        if main is None:
+            main = self.main_latents(seq, row0, rows)
+        x = [main[:, IDX_DIM * j:IDX_DIM * (j + 1)] * s[j] for j in range(4)]
+        return ((x[0] + x[1]) + (x[2] + x[3])) * np.float32(0.5)
 
     def swa_latents(self, layer: int, seq: int, pos0: int, count: int) -> np.ndarray:
         return latent_rows(self.seed, tensor_id(SWA_LATENT, layer, seq), pos0, count, DIM, 64, 1)

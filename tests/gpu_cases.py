@@ -63,9 +63,10 @@ class Case:
         for b in range(wl.n_seq):
             for r0 in range(0, wl.seq_cap, ROWS_PER_UPLOAD):
                 n = min(ROWS_PER_UPLOAD, wl.seq_cap - r0)
-                lat = torch.from_numpy(wl.main_latents(b, r0, n)).cuda()
+                main = wl.main_latents(b, r0, n)
+                lat = torch.from_numpy(main).cuda()
                 C_.csa2_quantize_kv(lat, C_.FMT_NVFP4, caches.kv_codes[b, r0:r0 + n], caches.kv_scales[b, r0:r0 + n])
-                ik = torch.from_numpy(wl.index_k_latents(b, r0, n)).cuda()
+                ik = torch.from_numpy(wl.index_k_latents(b, r0, n, main=main)).cuda()
                 C_.csa2_quantize_kv(ik, ik_fmt, caches.ik_codes[b, r0:r0 + n], caches.ik_scales[b, r0:r0 + n])
             for L in self.swa_layers if not window_empty else ():
                 ring = torch.from_numpy(swa_ring_latents(wl, L, b)).cuda()
