@@ -547,7 +547,7 @@ def run_prefill_chunk(args, torch, C):
         "scoring": dict(kernel="k_score_topk_grouped (csa2_index_topk_grouped: FP4 scores and Top-512 of 8 rows "
                                "per pass over the sequence's indexer K; no score array)",
                         **mfma_entry(score_flops(wl5), g5["index_topk_grouped"], MFMA_FP4_PEAK_TFLOPS)),
-        "attention": dict(kernel="k_attn (csa2_sparse_attn, 512 entries + window per row)",
+        "attention": dict(kernel="k_attn_fc (csa2_sparse_attn, 512 entries + window per row)",
                           **mfma_entry(attn_flops(wl5), g5["attn"], MFMA_F16_PEAK_TFLOPS)),
         "isolated_launch_us": {k: round(v * 1000, 1) for k, v in r5["isolated"].items()}}}
 
@@ -742,7 +742,7 @@ def main():
                      "frac_of_measured_copy": round(achieved / copy["gb_per_s"], 4),
                      "frac_of_measured_read": round(achieved / copy["read_gb_per_s"], 4),
                      "timing": "HIP events around graph replays of 8 back-to-back csa2_index_segments calls"},
-        "attention": {"kernel": "csa2_sparse_attn_topk (k_attn: the last Top-K level, then attention)",
+        "attention": {"kernel": "csa2_sparse_attn_topk (k_attn_fc: the last Top-K level, then attention)",
                       "us": round(at_ms * 1e3, 2),
                       "flops_per_launch": attn_flops(wl), "tflops": round(at_tflops, 2),
                       "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS, "mfma_frac": round(at_tflops / MFMA_F16_PEAK_TFLOPS, 4),

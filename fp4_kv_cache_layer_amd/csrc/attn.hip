@@ -16,7 +16,14 @@
 // with the fp32 rounding of the sums).  P = exp2(logit - max) is rounded to fp16 (11
 // significant bits) for the P.V product.
 //
-// Decomposition: one workgroup = (query, 16 heads, slice of the key list), 8 waves in four
+// Two decompositions share one workgroup shape, (query, 16 heads, slice of the key list) with
+// 8 waves, and everything outside the tile loop.  The full-channel kernel (k_attn_fc), taken
+// whenever the window is at most 128 keys (the decode configurations), makes each wave a key
+// stream of its own over all 512 channels: no partial S crosses waves, Q is staged once in
+// LDS, and the eight streams merge at the end (its own header comment has the details).
+// The split-channel kernel (k_attn) below takes any window up to the maximum:
+//
+// Split-channel decomposition: 8 waves in four
 // pairs.  The key list is cut into tiles of 16 keys; pair p takes every fourth tile of the
 // slice (window tiles first, since their rows need no index), and the two waves of a pair
 // split the 512 channels into halves.  Per tile a wave
@@ -830,6 +837,653 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
   }
 }
 
+// ---- the full-channel variant: each wave is a key stream of its own over all 512 channels ----
+//
+// One workgroup = (query, 16 heads, slice of the key list), as k_attn, but its 8 waves are 8
+// key streams: stream p takes tiles p, p+8, ... of the slice (window tiles first).  A wave
+// forms S^T = K Q^T over all 512 channels itself, so no partial S is exchanged and each
+// stream runs its own online softmax; Q is staged once per workgroup in LDS (scaled to fp16
+// by a power of two per head, as in k_attn) and each 32-channel MFMA step reads its slice.
+// Lane (key col, group grp) gathers channels 128*grp .. +127 of its key: 64 B of E2M1 codes
+// and 8 scale bytes, or 128 B of window E4M3.  V is single-buffered per wave: in step i the
+// P.V of tile i reads channel blocks m, m+8, m+16, m+24 of the V tile just before the
+// dequantisation of tile i+1 overwrites exactly those blocks (LDS executes one wave's
+// accesses in order), interleaved over m = 0..7 with tile i+1's QK steps 2m, 2m+1.  O^T of
+// all 512 channels stays in 32 accumulator blocks; at the end the eight streams merge
+// (O, m, l) with the log-sum-exp rule in two rounds through LDS.  Same arithmetic per (key,
+// head, channel) as k_attn: exact fp16 keys and values, P rounded to fp16, fp32 sums.
+constexpr int kStreams = 8;
+constexpr int kFcRow = kD * 2 + 16;   // bytes per V / Q row in LDS (padding against bank conflicts)
+constexpr int kFcVBuf = kT * kFcRow;  // one wave's V tile: 16,640 B
+constexpr int kFcDT = kD / 16;        // 16-channel blocks of O^T: 32
+static_assert(kStreams * 64 == kAttnThreads, "one wave per key stream");
+
+// raw bytes of one gather slot: main = 64 B of codes (r[0..3]; r[4..7] re-read them) and 8
+// scale bytes (sc0, sc1); window = 128 B of E4M3 (r[0..7])
+struct FcSlot {
+  uint4 r[8];
+  uint32_t sc0, sc1;
+  uint32_t ok;
+  uint32_t is_new;
+};
+// a main-tile slot: 64 B of codes and 8 scale bytes (every tile of a stream after its first
+// is a main tile: the window has at most kStreams tiles, and they come first)
+struct FcMainSlot {
+  uint4 r[4];
+  uint32_t sc0, sc1;
+  uint32_t ok;
+};
+
+template <int kSel>
+__global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fc(AttnArgs a, const int32_t* __restrict__ q_seq,
+                                                              const int64_t* __restrict__ q_pos,
+                                                              const int64_t* __restrict__ replay_start,
+                                                              const int64_t* __restrict__ swa_base) {
+  // ---- which (query, head group, split) this workgroup is; same query -> same XCD ----
+  const int G = a.head_groups * a.nsplit;
+  const int L = blockIdx.x;
+  const int xcd = L & 7, jj = L >> 3;
+  const int q = 8 * (jj / G) + xcd;
+  if (q >= a.n_q) return;
+  const int rem = jj % G;
+  const int hg = rem % a.head_groups;
+  const int split = rem / a.head_groups;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index (the key stream) is uniform over the wave; saying so keeps tile-level
+  // decisions scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // MFMA lane roles: col = key row of K / head column of Q^T and S^T, grp = lane group
+  const int col = lane & 15, grp = lane >> 4;
+
+  // LDS: one V tile per wave, Q of the 16 heads, the staged index list; after the loop the
+  // first 128 KB hold the partial outputs of the merge
+  constexpr int kVBytes = kStreams * kFcVBuf;                       // 133,120
+  constexpr int kQBytes = kHG * kFcRow;                             // 16,640
+  constexpr int kLdsBytes = kVBytes + kQBytes + CSA2_MAX_TOPK * 4;  // 157,952
+  static_assert(4 * kFcDT * 64 * 16 <= kVBytes, "merge area");
+  static_assert((kSelHistWords + 2 * 256 + 8 * 32) * 4 <= kVBytes, "selection LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  __shared__ float s_ml[kStreams][kHG][2];
+  __shared__ int s_qsh[kHG];
+  uint8_t* vbuf = lds + wave * kFcVBuf;                             // [16 rows][kFcRow]
+  uint8_t* qst = lds + kVBytes;                                     // [16 heads][kFcRow]
+  int32_t* s_idx = reinterpret_cast<int32_t*>(lds + kVBytes + kQBytes);
+
+  // ---- this split's tiles: main tiles [tile_lo, main_hi), window tiles after them ----
+  const int tile_lo = split * a.tiles_per_split;
+  const int tile_hi = tile_lo + a.tiles_per_split < a.n_tiles ? tile_lo + a.tiles_per_split : a.n_tiles;
+  const int main_hi = a.main_tiles < tile_hi ? a.main_tiles : tile_hi;
+  const int n_main = main_hi > tile_lo ? main_hi - tile_lo : 0;
+
+  // ---- this stream's tiles: window tiles first (their rows need no index), then main
+  // tiles; stream p takes positions p, p+8, ... of that order.  The streams never wait for
+  // one another inside the loop, so each runs its own number of steps ----
+  const int span = tile_hi - tile_lo;
+  const int n_win = span - n_main;
+  const int n_my = span > wave ? (span - wave + kStreams - 1) / kStreams : 0;
+  auto my_tile = [&](int i) {
+    const int j = wave + kStreams * (i < n_my ? i : (n_my > 0 ? n_my - 1 : 0));
+    return j < n_win ? tile_lo + n_main + j : tile_lo + (j - n_win);
+  };
+
+  // ---- the query's sequence and positions head the memory queue (scalar loads), then this
+  // split's slice of the index list (it does not depend on them), then Q ----
+  const int seq = q_seq[q];
+  const int64_t t = q_pos[q], s = replay_start[q];
+  constexpr bool kSelect = kSel != 0;
+  constexpr int kEpt = kSel == 2 ? 32 : 16;
+  constexpr int kIdxPer = CSA2_MAX_TOPK / kAttnThreads;
+  const int n_keys = n_main * kT;
+  int32_t iv[kIdxPer];
+  uint64_t key[kEpt];
+  if constexpr (kSel == 1) {
+    // survivors tid*16 .. tid*16+15 of the query (cand_per_q >= 1): runs of 16 B loads where
+    // the wave's whole range is inside the list (uniform), clamped single loads otherwise
+    const uint64_t* kp = a.cand_keys + (int64_t)q * a.cand_per_q;
+    const int lim = a.cand_per_q;
+    const int c0 = tid * kEpt;
+    if ((wave + 1) * 64 * kEpt <= lim) {
+      typedef uint64_t u64x2 __attribute__((ext_vector_type(2), aligned(8)));
+#pragma unroll
+      for (int i = 0; i < kEpt; i += 2) {
+        const u64x2 v = *reinterpret_cast<const u64x2*>(kp + c0 + i);
+        key[i] = v.x;
+        key[i + 1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        const int o = c0 + i;
+        key[i] = kp[o < lim ? o : lim - 1] & (0ull - (uint64_t)(o < lim));
+      }
+    }
+  } else if constexpr (kSel == 2) {
+    // pool slot c = tid*32 + i: block cand_blocks[q][c / block], position block id * block
+    // + c % block; a candidate if c lies in the query's first n_cand_blocks blocks, the block
+    // id is valid and the position visible (as the first Top-K level inside a pool).  The
+    // loads are clamped to the row (max_cand_blocks * block slots, all inside the arrays),
+    // not to the query's slot count, so they go out without waiting for n_cand_blocks; the
+    // scores come in 16 B loads where the wave's whole range is inside the row (uniform),
+    // and the slot's block and offset advance by one slot per step (one division).
+    const uint32_t blk = (uint32_t)a.block;
+    const uint32_t row_slots = (uint32_t)a.max_cand_blocks * blk;   // <= 16,384
+    const float* sp = a.pool_scores + (int64_t)q * a.pool_stride;
+    const int32_t* cb = a.cand_blocks + (int64_t)q * a.max_cand_blocks;
+    const uint32_t c0 = (uint32_t)tid * kEpt;
+    const uint32_t last_blk = (uint32_t)a.max_cand_blocks - 1u;
+    int nc = a.n_cand_blocks[q];
+    nc = nc < 0 ? 0 : (nc > a.max_cand_blocks ? a.max_cand_blocks : nc);
+    int64_t nv = a.n_vis[q];
+    nv = nv < 0 ? 0 : (nv > a.seq_cap ? a.seq_cap : nv);
+    const uint32_t nslot = (uint32_t)nc * blk;   // <= 16,384
+    // Each path issues all of its loads (block ids, then scores) and builds the keys itself:
+    // only finished keys meet after the branch, so no load is waited for before the rest are
+    // issued.  kBlk8: the pool's 8-position blocks, a thread's 32 slots being blocks c0/8 ..
+    // c0/8 + 3 (four loads, one per 8 slots); otherwise each slot's block id is loaded, its
+    // block and offset advanced by one slot per step.
+    auto build = [&](auto blk8) {
+      constexpr bool kBlk8 = decltype(blk8)::value;
+      int32_t bv[kEpt];
+      uint32_t so[kEpt];
+      float v[kEpt];
+      if constexpr (kBlk8) {
+        int32_t b4[kEpt / 8];
+#pragma unroll
+        for (int j = 0; j < kEpt / 8; ++j) {
+          const uint32_t bj = c0 / 8u + (uint32_t)j;
+          b4[j] = cb[bj < last_blk ? bj : last_blk];
+        }
+#pragma unroll
+        for (int i = 0; i < kEpt; ++i) {
+          bv[i] = b4[i / 8];
+          so[i] = (uint32_t)(i % 8);
+        }
+      } else {
+        uint32_t b = c0 / blk, o = c0 % blk;
+#pragma unroll
+        for (int i = 0; i < kEpt; ++i) {
+          bv[i] = cb[b < last_blk ? b : last_blk];
+          so[i] = o;
+          const bool carry = o + 1u == blk;
+          o = carry ? 0u : o + 1u;
+          b += carry ? 1u : 0u;
+        }
+      }
+      if ((uint32_t)(wave + 1) * 64u * kEpt <= row_slots) {   // uniform: 16 B score loads
+        typedef float f32x4 __attribute__((ext_vector_type(4), aligned(4)));
+#pragma unroll
+        for (int i = 0; i < kEpt; i += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(sp + c0 + i);
+          v[i] = x.x;
+          v[i + 1] = x.y;
+          v[i + 2] = x.z;
+          v[i + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kEpt; ++i) {
+          const uint32_t c = c0 + (uint32_t)i;
+          v[i] = sp[c < row_slots ? c : row_slots - 1u];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kEpt; ++i) {
+        const uint32_t c = c0 + (uint32_t)i;
+        const int64_t pos = (int64_t)bv[i] * blk + so[i];
+        const bool ok = c < nslot && bv[i] >= 0 && pos < nv;
+        key[i] = make_key(v[i], (uint32_t)pos) & (0ull - (uint64_t)ok);
+      }
+    };
+    if (blk == 8u) build(std::true_type{});   // uniform
+    else build(std::false_type{});
+  }
+  // A given index list: this thread's slice of it (staged in LDS below), and this lane's keys
+  // of its first three tiles, read straight from it so that their gathers need neither the
+  // staged list nor the prologue's barrier (a slot past k gets -1).  All of
+  // these loads are unconditional, from clamped in-bounds addresses (q_seq stands in for an
+  // absent list when k == 0), and branch-free: a load inside a branch would be waited for
+  // at the branch's end, one memory round trip after another.
+  int32_t idx0[3] = {-1, -1, -1};
+  if constexpr (!kSelect) {
+    const bool have = a.k > 0;
+    const int32_t* ib = have ? a.idx + (int64_t)q * a.k : q_seq;
+    const int klast = have ? a.k - 1 : 0;
+#pragma unroll
+    for (int r = 0; r < kIdxPer; ++r) {
+      int i = tid + r * kAttnThreads;
+      i = i < n_keys ? i : (n_keys > 0 ? n_keys - 1 : 0);
+      const int slot = tile_lo * kT + i;
+      iv[r] = ib[slot < klast ? slot : klast];
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int tile = my_tile(i);
+      const int slot = tile * kT + col;
+      const int32_t v = ib[slot < klast ? slot : klast];
+      idx0[i] = slot < a.k ? v : -1;   // (load_slot ignores it for a window tile)
+    }
+  }
+
+  // ---- Q of the 16 heads, once for the workgroup: thread t loads head t / 32, channels
+  //      16 * (t % 32) .. +15 (scaled and staged in LDS before the prologue's barrier) ----
+  const int qh = tid >> 5, qc = (tid & 31) * 16;
+  uint4 qr[2];
+  {
+    const uint16_t* qp = a.q + ((int64_t)q * a.n_heads + hg * kHG + qh) * kD + qc;
+    qr[0] = reinterpret_cast<const uint4*>(qp)[0];
+    qr[1] = reinterpret_cast<const uint4*>(qp)[1];
+  }
+
+  // Window append: thread c quantises channel c of the row's new window latent (the
+  // quantiser's exact E4M3 rounding); the bytes are staged in LDS for this workgroup's own
+  // window tiles, and workgroup (head group 0, split 0) writes them to the ring.  The latent
+  // is loaded here and converted just before the prologue's barrier: a wait for it here
+  // would wait for every load issued before it and hold back the per-query scalars below.
+  static_assert(kAttnThreads == kD, "one thread per channel of the appended window entry");
+  __shared__ __attribute__((aligned(16))) uint8_t s_new[kD];
+  // One unconditional 32-bit load (branch-free, see above): an f32 element, or the word
+  // holding this bf16 element (Q stands in when there is no latent)
+  uint32_t new_bits;
+  {
+    const int64_t e = (int64_t)q * kD + tid;
+    const uint32_t* nwp = reinterpret_cast<const uint32_t*>(a.new_win ? a.new_win : (const void*)a.q);
+    const uint32_t w = nwp[a.new_win_bf16 || !a.new_win ? e >> 1 : e];
+    new_bits = a.new_win_bf16 ? ((tid & 1) ? (w & 0xffff0000u) : (w << 16)) : w;
+  }
+  const bool seq_ok = seq >= 0 && seq < a.n_seq;
+  const int64_t lo = s > t - a.window + 1 ? s : t - a.window + 1;
+  const int64_t n_swa = seq_ok && t >= lo ? t - lo + 1 : 0;
+  const int64_t swa_b = seq_ok ? swa_base[seq] : 0;
+  // ring row of the first window key; later keys wrap at most once (window <= swa_cap).
+  // The offset from the ring base nearly always fits 32 bits: then a 32-bit remainder
+  const int64_t rel = lo - swa_b;
+  const uint32_t swa_cap32 = (uint32_t)a.swa_cap;
+  int64_t r_lo;
+  if (rel >= 0 && rel <= 0xffffffffLL) {
+    r_lo = (uint32_t)rel % swa_cap32;
+  } else {
+    r_lo = rel % a.swa_cap;
+    r_lo = r_lo < 0 ? r_lo + a.swa_cap : r_lo;
+  }
+  const uint32_t win_row0 = (uint32_t)r_lo;
+  const uint8_t* kvc = a.kv_codes + (int64_t)(seq_ok ? seq : 0) * a.kv_cs;
+  const uint8_t* kvs = a.kv_scales + (int64_t)(seq_ok ? seq : 0) * a.kv_ss;
+  const uint8_t* swq = a.swa + (int64_t)(seq_ok ? seq : 0) * a.swa_rs;
+  // Every gather load is unconditional, to an in-bounds address (an absent key reads row 0
+  // and is flagged), so no branch sits around the loads of the ring.  Lane (col, grp)
+  // fetches key col of the tile, channels 128*grp .. +127.
+  auto load_slot = [&](int tile, bool real, FcSlot& g, const int32_t* direct = nullptr) {
+    const bool is_main = tile < a.main_tiles;  // wave-uniform
+    int si = (tile - tile_lo) * kT + col;
+    si = si < 0 ? 0 : (si >= n_main * kT ? (n_main > 0 ? n_main * kT - 1 : 0) : si);
+    const int slot = tile_lo * kT + si;
+    const int32_t pv = direct ? *direct : s_idx[kSelect ? (slot < a.k ? slot : a.k - 1) : si];
+    const int32_t p = (kSelect && slot >= a.k) ? -1 : pv;
+    const bool ok_main = real && is_main && seq_ok && p >= 0 && p < a.seq_cap;
+    const uint32_t pm = ok_main ? (uint32_t)p : 0u;
+    const int j = (tile - a.main_tiles) * kT + col;
+    const bool ok_win = real && !is_main && seq_ok && j >= 0 && j < n_swa;
+    g.is_new = a.new_win != nullptr && ok_win && j == n_swa - 1;   // window key j is token lo + j
+    uint32_t row = win_row0 + (uint32_t)j;
+    row = ok_win ? (row >= swa_cap32 ? row - swa_cap32 : row) : 0u;
+    const uint4* c = is_main
+        ? reinterpret_cast<const uint4*>(kvc + ((uint64_t)pm * (uint64_t)a.kv_ce + 64 * grp))
+        : reinterpret_cast<const uint4*>(swq + ((uint64_t)row * (uint64_t)a.swa_re + 128 * grp));
+    const uint4* c2 = is_main ? c : c + 4;  // main needs 64 B: the second four re-read them
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      g.r[u] = c[u];
+      g.r[4 + u] = c2[u];
+    }
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(kvs + ((uint64_t)pm * (uint64_t)a.kv_se + 8 * grp));
+    g.sc0 = sp[0];
+    g.sc1 = sp[1];
+    g.ok = is_main ? ok_main : ok_win;
+  };
+
+  // the main-tile gather of a stream's later tiles (always main tiles)
+  auto load_main = [&](int tile, bool real, FcMainSlot& g, const int32_t* direct = nullptr) {
+    int si = (tile - tile_lo) * kT + col;
+    si = si < 0 ? 0 : (si >= n_main * kT ? (n_main > 0 ? n_main * kT - 1 : 0) : si);
+    const int slot = tile_lo * kT + si;
+    const int32_t pv = direct ? *direct : s_idx[kSelect ? (slot < a.k ? slot : a.k - 1) : si];
+    const int32_t p = (kSelect && slot >= a.k) ? -1 : pv;
+    const bool ok_main = real && tile < a.main_tiles && seq_ok && p >= 0 && p < a.seq_cap;
+    const uint32_t pm = ok_main ? (uint32_t)p : 0u;
+    const uint4* c = reinterpret_cast<const uint4*>(kvc + ((uint64_t)pm * (uint64_t)a.kv_ce + 64 * grp));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) g.r[u] = c[u];
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(kvs + ((uint64_t)pm * (uint64_t)a.kv_se + 8 * grp));
+    g.sc0 = sp[0];
+    g.sc1 = sp[1];
+    g.ok = ok_main;
+  };
+
+  // With a given index list the first three gathers of every key stream go out here, their
+  // keys read directly (idx0).  When the list is selected in this kernel, the first tile of
+  // every stream is a window tile when the slice holds at least kStreams of them (always
+  // without a key split); its rows need no index, so its gather goes out before the
+  // selection.  Slot g0 holds the first tile (main or window); the main slots gA, gB ring
+  // through the later ones.
+  const bool early = n_win >= kStreams;   // uniform over the workgroup
+  FcSlot g0;
+  FcMainSlot gA, gB;
+  if constexpr (!kSelect) {   // the given list: all three gathers now (keys read directly)
+    load_slot(my_tile(0), 0 < n_my, g0, &idx0[0]);
+    load_main(my_tile(1), 1 < n_my, gA, &idx0[1]);
+    load_main(my_tile(2), 2 < n_my, gB, &idx0[2]);
+  } else if (early) {
+    load_slot(my_tile(0), 0 < n_my, g0);
+  }
+
+  if constexpr (kSelect) {
+    // the whole index list, s_idx[0 .. k), ascending; the tiles index it from tile_lo * 16
+    __shared__ int32_t s_count;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(lds);
+    select_block<kAttnThreads, kEpt, true, kTkCopies, true>(key, a.k, hist, nullptr, s_idx, &s_count,
+                                                            hist + kSelHistWords);
+    __syncthreads();
+    if (hg == 0 && split == 0) {
+      for (int i = tid; i < a.k; i += kAttnThreads) a.idx_out[(int64_t)q * a.k + i] = s_idx[i];
+      if (tid == 0) a.count_out[q] = s_count;
+    }
+  } else if (n_keys > 0) {
+#pragma unroll
+    for (int r = 0; r < kIdxPer; ++r) {
+      const int i = tid + r * kAttnThreads;
+      if (i < n_keys) s_idx[i] = tile_lo * kT + i < a.k ? iv[r] : -1;
+    }
+  }
+  // Q scaled per head: the largest |q| of head qh over its 512 channels (bf16 magnitude bits;
+  // the order of finite bf16 magnitudes is that of their bit patterns), over the 32 threads
+  // of the head, gives the power-of-two shift of k_attn; the scaled fp16 Q goes to LDS
+  {
+    const uint32_t w8[8] = {qr[0].x, qr[0].y, qr[0].z, qr[0].w, qr[1].x, qr[1].y, qr[1].z, qr[1].w};
+    uint32_t qm = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo16 = w8[i] & 0x7fffu, hi16 = (w8[i] >> 16) & 0x7fffu;
+      qm = lo16 > qm ? lo16 : qm;
+      qm = hi16 > qm ? hi16 : qm;
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      const uint32_t v = (uint32_t)__shfl_xor((int)qm, o);
+      qm = v > qm ? v : qm;
+    }
+    const int sh = q_shift(qm);
+    v8h h0, h1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h0[2 * i] = bf16_to_f16(w8[i] & 0xffffu, sh);
+      h0[2 * i + 1] = bf16_to_f16(w8[i] >> 16, sh);
+      h1[2 * i] = bf16_to_f16(w8[4 + i] & 0xffffu, sh);
+      h1[2 * i + 1] = bf16_to_f16(w8[4 + i] >> 16, sh);
+    }
+    *reinterpret_cast<v8h*>(qst + qh * kFcRow + qc * 2) = h0;
+    *reinterpret_cast<v8h*>(qst + qh * kFcRow + qc * 2 + 16) = h1;
+    if ((tid & 31) == 0) s_qsh[qh] = sh;
+  }
+  if (a.new_win) {  // uniform: the window append (see above)
+    const uint32_t new_code = fp8_code_bits(new_bits);
+    s_new[tid] = (uint8_t)new_code;
+    if (hg == 0 && split == 0 && seq_ok && t >= 0) {
+      // ring row of token t: the window keys [lo, t] are consecutive rows from win_row0
+      int64_t rt = (t - swa_b) % a.swa_cap;
+      rt = rt < 0 ? rt + a.swa_cap : rt;
+      a.swa_w[(int64_t)seq * a.swa_rs + rt * a.swa_re + tid] = (uint8_t)new_code;
+    }
+  }
+  __syncthreads();  // s_idx, Q, s_qsh, s_new
+  if (kSelect && !early) load_slot(my_tile(0), 0 < n_my, g0);
+  if constexpr (kSelect) {
+    load_main(my_tile(1), 1 < n_my, gA);
+    load_main(my_tile(2), 2 < n_my, gB);
+  }
+
+  const float qsl = ldexpf(a.scale_log2, s_qsh[col]);   // log2-domain scale of head col
+  const uint8_t* qrow = qst + col * kFcRow + 256 * grp;   // head col, channels 128*grp ..
+  uint8_t* vrow = vbuf + col * kFcRow + 256 * grp;        // key col, channels 128*grp ..
+  // P.V reads: A = V^T (16 channels x 16 keys) through DS_READ_B64_TR_B16: in each 16-lane
+  // group (keys 4grp..4grp+3), lane 4a+b receives element b of the 8-byte reads of lanes a,
+  // a+4, a+8, a+12, so lane r of the group points at channels 4*(r & 3).. of key
+  // 4*grp + (r >> 2); block b adds 32 b bytes
+  const __attribute__((address_space(3))) uint8_t* vtr =
+      (const __attribute__((address_space(3))) uint8_t*)vbuf + (4 * grp + (col >> 2)) * kFcRow + 8 * (col & 3);
+
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  v4f o[kFcDT];
+#pragma unroll
+  for (int i = 0; i < kFcDT; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // the V reads of tile i must stay before the V writes of tile i+1 (LDS executes one wave's
+  // accesses in order; this keeps the compiler from reordering them)
+  auto lds_order = [] { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); };
+
+  // One tile's QK over all 512 channels (16 steps of 32: lane group grp supplies channels
+  // 128*grp + 8*j .. +7 in step j, for K and Q alike), its V written in place, and, when
+  // with_pv, the P.V of the previous tile from the same buffer, block by block just before
+  // it is overwritten.  Returns S^T (lane: head col, keys 4*grp..+3); *valid receives bit k
+  // for each present key k.
+  auto tile_step = [&](const auto& g, bool is_main, bool with_pv, v4h pb_prev, uint32_t* valid) -> v4f {
+    constexpr bool kFirst = std::is_same<std::decay_t<decltype(g)>, FcSlot>::value;
+    const uint32_t keep = 0u - g.ok;
+    v4f sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    auto word = [&](int d) -> uint32_t {   // raw dword d of the lane's slot
+      const uint4 v = g.r[d >> 2];
+      return (d & 3) == 0 ? v.x : ((d & 3) == 1 ? v.y : ((d & 3) == 2 ? v.z : v.w));
+    };
+    v2h ss[8];
+    {  // the eight E4M3 group scales to fp16 (exact); an absent key's scale is 0
+      const uint32_t s0 = g.sc0 & keep, s1 = g.sc1 & keep;
+      const v2h a01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s0, 1.0f, false);
+      const v2h a23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s0, 1.0f, true);
+      const v2h b01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s1, 1.0f, false);
+      const v2h b23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s1, 1.0f, true);
+      ss[0] = __builtin_shufflevector(a01, a01, 0, 0);
+      ss[1] = __builtin_shufflevector(a01, a01, 1, 1);
+      ss[2] = __builtin_shufflevector(a23, a23, 0, 0);
+      ss[3] = __builtin_shufflevector(a23, a23, 1, 1);
+      ss[4] = __builtin_shufflevector(b01, b01, 0, 0);
+      ss[5] = __builtin_shufflevector(b01, b01, 1, 1);
+      ss[6] = __builtin_shufflevector(b23, b23, 0, 0);
+      ss[7] = __builtin_shufflevector(b23, b23, 1, 1);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (with_pv) {   // uniform: blocks m, m+8, m+16, m+24 of the previous tile
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int b = m + 8 * gq;
+          const v4h av = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vtr + 32 * b)));
+          o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb_prev, o[b], 0, 0, 0);
+        }
+        lds_order();
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = 2 * m + h;
+        v8h k;
+        if constexpr (kFirst) {
+          if (is_main) {
+            k = fp4x8_to_f16(word(j), ss[j >> 1]);
+          } else {
+            uint32_t d0 = word(2 * j), d1 = word(2 * j + 1);
+            if (a.new_win) {  // uniform: the row's own token comes from the LDS copy, not the ring
+              const uint2 n = *reinterpret_cast<const uint2*>(s_new + 128 * grp + 8 * j);
+              d0 = g.is_new ? n.x : d0;
+              d1 = g.is_new ? n.y : d1;
+            }
+            k = fp8x8_to_f16(d0 & keep, d1 & keep);
+          }
+        } else {
+          k = fp4x8_to_f16(word(j), ss[j >> 1]);
+        }
+        *reinterpret_cast<v8h*>(vrow + 16 * j) = k;
+        const v8h qv = *reinterpret_cast<const v8h*>(qrow + 16 * j);
+        if (h == 0) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qv, sa, 0, 0, 0);
+        else sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qv, sb, 0, 0, 0);
+      }
+    }
+    *valid = (uint32_t)__ballot(g.ok != 0) & 0xffffu;  // lanes 0..15 hold keys 0..15
+    return sa + sb;
+  };
+
+  // online softmax over one tile's S^T (lane: head col, keys 4*grp + r), with k_attn's lazy
+  // reference; returns P^T in fp16 and in *alpha the factor for the accumulators
+  auto softmax_tile = [&](v4f sv, uint32_t valid, float* alpha_out) -> v4h {
+    float x[4];
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = (valid >> (4 * grp + r)) & 1u;
+      x[r] = ok ? sv[r] * qsl : -__builtin_inff();
+      mt = fmaxf(mt, x[r]);
+    }
+    mt = lanes4_max(mt);
+    const bool first = m_run == -__builtin_inff();
+    const bool move = first ? mt != -__builtin_inff() : mt > m_run + kLazy;
+    const float m_new = move ? mt : m_run;
+    const float alpha = (move && !first) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    const bool none = m_new == -__builtin_inff();
+    v4h pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pr = none ? 0.0f : __builtin_amdgcn_exp2f(x[r] - m_new);
+      psum += pr;
+      pb[r] = (_Float16)pr;
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    *alpha_out = alpha;
+    return pb;
+  };
+  auto rescale = [&](float alpha) {
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < kFcDT; ++dt) o[dt] *= alpha;
+    }
+  };
+
+  // ---- software pipeline.  Step i forms S of tile i+1 (main slot gA or gB) with the P.V of
+  // tile i interleaved, refills that slot with tile i+3, then runs the softmax of tile i+1.
+  // Each load has two steps to arrive ----
+  auto tile_is_main = [&](int i) { return my_tile(i) < a.main_tiles; };
+  uint32_t vmask = 0u;
+  float alpha = 1.0f;
+  v4h pb = {};
+  if (n_my > 0) {   // uniform over the wave
+    const v4f sp = tile_step(g0, tile_is_main(0), false, pb, &vmask);
+    pb = softmax_tile(sp, vmask, &alpha);
+  }
+  auto step = [&](int i, FcMainSlot& g) {
+    lds_order();
+    const v4f sp = tile_step(g, true, true, pb, &vmask);   // tile i+1, the P.V of tile i inside
+    load_main(my_tile(i + 3), i + 3 < n_my, g);
+    pb = softmax_tile(sp, vmask, &alpha);   // tile i+1
+    rescale(alpha);
+  };
+  // Steps 0 .. n_my-2 form S of tiles 1 .. n_my-1; then the last tile's P.V.  Whole rounds
+  // of the ring inside the loop and the remainder after it.
+  const int n_full = n_my - 1;
+  int i = 0;
+  for (; i + 2 <= n_full; i += 2) {
+    step(i, gA);
+    step(i + 1, gB);
+  }
+  if (i < n_full) step(i, gA);   // uniform over the wave
+  if (n_my > 0) {
+    lds_order();
+#pragma unroll
+    for (int b = 0; b < kFcDT; ++b) {
+      const v4h av = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vtr + 32 * b)));
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, o[b], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the eight streams' (O, m, l) ----
+  const float l_tot = lanes4_sum(l_run);
+  if (lane < kHG) {
+    s_ml[wave][lane][0] = m_run;
+    s_ml[wave][lane][1] = l_tot;
+  }
+  __syncthreads();  // every wave is past its loop: the V buffers are free
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int w = 0; w < kStreams; ++w) M = fmaxf(M, s_ml[w][col][0]);
+  float Ltot = 0.0f, mine = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kStreams; ++w) {
+    const float mw = s_ml[w][col][0];
+    const float sw = mw == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+    Ltot += sw * s_ml[w][col][1];
+    mine = w == wave ? sw : mine;
+  }
+  const int head = hg * kHG + col;
+  const float inv = Ltot > 0.0f ? 1.0f / Ltot : 0.0f;
+  float4* part = reinterpret_cast<float4*>(lds);   // [4 slots][32 blocks][64 lanes]: 128 KB
+  // round 1: streams 4..7 store their weighted O^T in slot wave - 4; streams 0..3 add it
+  if (wave >= 4) {
+#pragma unroll
+    for (int b = 0; b < kFcDT; ++b) {
+      const v4f v = o[b] * mine;
+      part[((wave - 4) * kFcDT + b) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int b = 0; b < kFcDT; ++b) {
+      const float4 p4 = part[(wave * kFcDT + b) * 64 + lane];
+      const v4f v = o[b] * mine + v4f{p4.x, p4.y, p4.z, p4.w};
+      part[(wave * kFcDT + b) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  __syncthreads();
+  // round 2: wave w sums blocks 4w .. 4w+3 over the four slots
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    const int b = 4 * wave + bb;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const float4 v = part[(sl * kFcDT + b) * 64 + lane];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const int ch = 16 * b + 4 * grp;   // channels ch..ch+3 of head col
+    if (a.nsplit == 1) {
+      const int64_t ob = ((int64_t)q * a.n_heads + head) * kD + ch;
+      if (a.out_dtype == CSA2_DT_F32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + ob) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      } else {
+        uint2 pk;
+        pk.x = f32_to_bf16_rne(acc.x * inv) | (f32_to_bf16_rne(acc.y * inv) << 16);
+        pk.y = f32_to_bf16_rne(acc.z * inv) | (f32_to_bf16_rne(acc.w * inv) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + ob) = pk;
+      }
+    } else {
+      const int64_t pbx = ((int64_t)split * a.n_q + q) * a.n_heads + head;
+      *reinterpret_cast<float4*>(a.ws_o + pbx * kD + ch) = acc;
+    }
+  }
+  if (wave == 0 && lane < kHG) {
+    if (a.nsplit == 1) {
+      if (a.lse) a.lse[(int64_t)q * a.n_heads + head] = Ltot > 0.0f ? (M + __log2f(Ltot)) * kLn2 : -__builtin_inff();
+    } else {
+      const int64_t pbx = ((int64_t)split * a.n_q + q) * a.n_heads + head;
+      a.ws_ml[pbx * 2] = M;
+      a.ws_ml[pbx * 2 + 1] = Ltot;
+    }
+  }
+}
+
+
 // merge the per-split (O, m, l) of one (query, head): 128 threads x 4 channels.  The first
 // eight splits' partial outputs are loaded first (they do not depend on (m, l)), while
 // thread sp < nsplit reads split sp's (m, l) into LDS, so up to eight splits cost one memory
@@ -1371,15 +2025,16 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, CacheRef kv
                        a.replay_start, a.swa_base);
     return csa2_check_launch();
   }
-  if (sel.mode == 2)
-    hipLaunchKernelGGL(k_attn<2>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
+  // The full-channel kernel takes a window of at most one tile per key stream (128 keys);
+  // a wider window goes to the split-channel kernel, whose streams take any mix of tiles
+  const bool full_channel = p.n_tiles - p.main_tiles <= kStreams;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
                        a.replay_start, a.swa_base);
-  else if (sel.mode == 1)
-    hipLaunchKernelGGL(k_attn<1>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
-                       a.replay_start, a.swa_base);
-  else
-    hipLaunchKernelGGL(k_attn<0>, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
-                       a.replay_start, a.swa_base);
+  };
+  if (sel.mode == 2) full_channel ? go(k_attn_fc<2>) : go(k_attn<2>);
+  else if (sel.mode == 1) full_channel ? go(k_attn_fc<1>) : go(k_attn<1>);
+  else full_channel ? go(k_attn_fc<0>) : go(k_attn<0>);
   int rc = csa2_check_launch();
   if (rc != CSA2_OK || p.nsplit == 1) return rc;
   hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(n_q * n_heads)), dim3(kCombThreads), 0, st, a);

@@ -147,12 +147,12 @@ def test_quantize_multi_matches_single_calls(C):
         assert (sa is None) == (sb is None) and (sa is None or torch.equal(sa, sb))
 
 
-def _score_case(seed, n_seq, seq_cap, n_vis, idx_heads, index_fmt="mxfp4"):
+def _score_case(seed, n_seq, seq_cap, n_vis, idx_heads, index_fmt="mxfp4", swa_cap=128):
     wl = G.workloads.Workload(
         name="small", seed=seed, n_seq=n_seq, seq_cap=seq_cap, m=1, heads=16, idx_heads=idx_heads,
         q_seq=np.array([i % n_seq for i in range(len(n_vis))], np.int32),
         q_pos=np.array(n_vis, np.int64) - 1, replay_start=np.zeros(len(n_vis), np.int64), layers=("full",),
-        new_entries=(0, 0))
+        new_entries=(0, 0), swa_cap=swa_cap)
     return G.Case(wl, index_fmt=index_fmt)
 
 
@@ -630,15 +630,17 @@ def test_index_topk_fused(C, k, fmt):
         G.topk_accept(gi[qi], int(gc[qi]), pos, ref, k)
 
 
-@pytest.mark.parametrize("k,fmt", [(512, "mxfp4"), (7, "mxfp4"), (1500, "mxfp4"), (512, "nvfp4")])
-def test_segments_then_attention_topk(C, k, fmt):
+@pytest.mark.parametrize("k,fmt,window", [(512, "mxfp4", 128), (7, "mxfp4", 128), (1500, "mxfp4", 128),
+                                          (512, "nvfp4", 128), (512, "mxfp4", 256)])
+def test_segments_then_attention_topk(C, k, fmt, window):
     """csa2_index_segments + csa2_sparse_attn_topk (the last Top-K level inside the attention
     call) give the index set of csa2_index_topk bit for bit, and attention outputs identical
     to csa2_sparse_attn over that set; repeated calls change nothing.  7 queries of 16 heads
-    split their key lists over 10 workgroups, each of which selects."""
-    _say("segments + attention topk", k, fmt)
+    split their key lists over 10 workgroups, each of which selects.  A 256-key window runs
+    the split-channel attention kernel, 128 keys the full-channel one."""
+    _say("segments + attention topk", k, fmt, window)
     n_vis = [40000, 8193, 1, 0, 511, 20001, 16384]
-    case = _score_case(50 + k, 3, 40000, n_vis, 16, fmt)
+    case = _score_case(50 + k, 3, 40000, n_vis, 16, fmt, swa_cap=window)
     wl = case.wl
     caches = case.gpu_caches()
     q_idx, w, qa = case.gpu_query_inputs(0)
@@ -652,7 +654,7 @@ def test_segments_then_attention_topk(C, k, fmt):
     out_a = torch.empty(wl.n_q, 16, 512, dtype=torch.float32, device="cuda")
     lse_a = torch.empty(wl.n_q, 16, dtype=torch.float32, device="cuda")
     C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, torch.from_numpy(gi).cuda(), caches.swa[0],
-                       caches.swa_base, q_pos, rs, 128, sm, out_a, lse_a)
+                       caches.swa_base, q_pos, rs, window, sm, out_a, lse_a)
     for rep in range(2):
         keys = torch.full((wl.n_q, C.csa2_segment_keys(wl.seq_cap, k)), 5, dtype=torch.int64, device="cuda")
         C.csa2_index_segments(st.qi_codes, st.qi_scales, w, caches.ik_codes, caches.ik_scales, q_seq, n_vis_t, k,
@@ -662,7 +664,7 @@ def test_segments_then_attention_topk(C, k, fmt):
         out_b = torch.empty_like(out_a)
         lse_b = torch.empty_like(lse_a)
         C.csa2_sparse_attn_topk(qa, caches.kv_codes, caches.kv_scales, q_seq, keys, k, idx_b, cnt_b, caches.swa[0],
-                                caches.swa_base, q_pos, rs, 128, sm, out_b, lse_b)
+                                caches.swa_base, q_pos, rs, window, sm, out_b, lse_b)
         torch.cuda.synchronize()
         assert np.array_equal(idx_b.cpu().numpy(), gi) and np.array_equal(cnt_b.cpu().numpy(), gc), rep
         assert torch.equal(out_b, out_a) and torch.equal(lse_b, lse_a), rep
@@ -767,14 +769,15 @@ def test_index_topk_fused_pool(C, fmt):
         G.topk_accept(gi[qi], int(gc[qi]), pos, ref, 512)
 
 
-@pytest.mark.parametrize("k,mb", [(512, 2048), (7, 2048), (512, 300)])
-def test_pool_select_in_attention(C, k, mb):
+@pytest.mark.parametrize("k,mb,window", [(512, 2048, 128), (7, 2048, 128), (512, 300, 128), (512, 2048, 256)])
+def test_pool_select_in_attention(C, k, mb, window):
     """csa2_sparse_attn_pool_topk (the Top-K selected inside the attention call from the
     pool's slot scores) returns csa2_topk's index set over the same scores and pool bit for
     bit, and attention outputs identical to csa2_sparse_attn over it; full pools, partial
-    ones, invalid block ids, blocks past n_vis and an empty pool."""
-    _say("pool select in attention", k, mb)
-    case = _score_case(71 + k, 4, 30000, [30000, 12000, 333, 5000], 16)
+    ones, invalid block ids, blocks past n_vis and an empty pool.  A 256-key window runs the
+    split-channel attention kernel, 128 keys the full-channel one."""
+    _say("pool select in attention", k, mb, window)
+    case = _score_case(71 + k, 4, 30000, [30000, 12000, 333, 5000], 16, swa_cap=window)
     wl = case.wl
     caches = case.gpu_caches()
     q_idx, w, qa = case.gpu_query_inputs(0)
@@ -801,7 +804,7 @@ def test_pool_select_in_attention(C, k, mb):
     out_a = torch.empty(wl.n_q, 16, 512, dtype=torch.float32, device="cuda")
     lse_a = torch.empty(wl.n_q, 16, dtype=torch.float32, device="cuda")
     C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, idx_a, caches.swa[0], caches.swa_base, q_pos, rs,
-                       128, sm, out_a, lse_a)
+                       window, sm, out_a, lse_a)
     for rep in range(2):
         idx_b = torch.full((wl.n_q, k), 77, dtype=torch.int32, device="cuda")
         cnt_b = torch.full((wl.n_q,), 77, dtype=torch.int32, device="cuda")
@@ -809,7 +812,7 @@ def test_pool_select_in_attention(C, k, mb):
         lse_b = torch.empty_like(lse_a)
         C.csa2_sparse_attn_pool_topk(qa, caches.kv_codes, caches.kv_scales, q_seq, st.scores, n_vis_t, st.pool,
                                      st.pool_count, 8, k, idx_b, cnt_b, caches.swa[0], caches.swa_base, q_pos, rs,
-                                     128, sm, out_b, lse_b)
+                                     window, sm, out_b, lse_b)
         torch.cuda.synchronize()
         assert torch.equal(idx_b, idx_a) and torch.equal(cnt_b, cnt_a), rep
         assert torch.equal(out_b, out_a) and torch.equal(lse_b, lse_a), rep
@@ -1202,10 +1205,11 @@ def test_device_status_reports_an_expired_wait(C):
     a wait bound of 0 polls every exchange gives up at once (the kernel still completes, with
     a wrong output); the kernel stores its code into the device status word, the next call
     returns CSA2_ERR_DEVICE without launching and names the cause, and once the bound is
-    restored the same call is correct again."""
+    restored the same call is correct again.  The window is 256 keys: only the split-channel
+    kernel, which a window wider than 128 keys selects, has such a wait."""
     _say("device status")
     t, s = [1500, 1400], [0, 0]
-    case = _attn_case(5, 2, 1501, 16, t, s)
+    case = _attn_case(5, 2, 1501, 16, t, s, swa_cap=256)
     caches = case.gpu_caches()
     _, _, qa = case.gpu_query_inputs(0)
     q_seq, _, q_pos, rs = case.gpu_meta()
@@ -1214,11 +1218,11 @@ def test_device_status_reports_an_expired_wait(C):
     idx_t = torch.from_numpy(idx).cuda()
     out = torch.empty(2, 16, 512, dtype=torch.float32, device="cuda")
     lse = torch.empty(2, 16, dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(C.csa2_attn_workspace_bytes(2, 16, 512, 512, 128), 1), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(C.csa2_attn_workspace_bytes(2, 16, 512, 512, 256), 1), dtype=torch.uint8, device="cuda")
 
     def attend():
         C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, idx_t, caches.swa[0], caches.swa_base, q_pos,
-                           rs, 128, 1.0 / math.sqrt(512), out, lse, workspace=ws)
+                           rs, 256, 1.0 / math.sqrt(512), out, lse, workspace=ws)
         torch.cuda.synchronize()
 
     C.csa2_device_status(clear=True)
@@ -1235,7 +1239,7 @@ def test_device_status_reports_an_expired_wait(C):
     assert C.csa2_device_status() == 0
     for qi in range(2):
         _, _, _, qa_np = case.oracle_query(0, qi)
-        ref, ref_lse = _attn_ref(case, qi, qa_np, idx[qi], t[qi], s[qi], 128, 1.0 / math.sqrt(512))
+        ref, ref_lse = _attn_ref(case, qi, qa_np, idx[qi], t[qi], s[qi], 256, 1.0 / math.sqrt(512))
         G.attn_close(out[qi].cpu().numpy(), ref, 2e-3)
 
 
