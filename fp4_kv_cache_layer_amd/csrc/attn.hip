@@ -1875,12 +1875,15 @@ __global__ __launch_bounds__(kRThreads, 1) void k_attn_rows(AttnArgs a, const in
 
 struct AttnPlan {
   int head_groups, n_tiles, main_tiles, tiles_per_split, nsplit;
+  bool full_channel;   // k_attn_fc: a window of at most one tile per key stream (128 keys)
   int64_t grid;
 };
 
 // One workgroup per CU (its eight waves, two per SIMD, and its 160 KB of LDS): split the
 // key list only when (query, head group) pairs alone cannot fill the 256 CUs, keeping at
-// least one tile per key stream in every split.
+// least one tile per key stream in every split (8 streams in the full-channel kernel, 4 in
+// the split-channel one).  Fewer, fuller splits also mean fewer repeats of the per-workgroup
+// prologue (a selection in the Top-K modes) and fewer partials for the combine kernel.
 static AttnPlan plan(int n_q, int n_heads, int k, int window) {
   AttnPlan p;
   p.head_groups = n_heads / kHG;
@@ -1888,7 +1891,9 @@ static AttnPlan plan(int n_q, int n_heads, int k, int window) {
   p.n_tiles = p.main_tiles + (window + kT - 1) / kT;
   const int64_t base = (int64_t)n_q * p.head_groups;
   int want = (int)((256 + base - 1) / (base > 0 ? base : 1));
-  const int max_split = (p.n_tiles + kPairs - 1) / kPairs;
+  p.full_channel = p.n_tiles - p.main_tiles <= kStreams;
+  const int streams = p.full_channel ? kStreams : kPairs;
+  const int max_split = (p.n_tiles + streams - 1) / streams;
   want = want < 1 ? 1 : (want > max_split ? max_split : want);
   p.tiles_per_split = (p.n_tiles + want - 1) / want;
   p.nsplit = (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
@@ -2027,7 +2032,7 @@ static int sparse_attn(const void* q, int n_q, int n_heads, int dim, CacheRef kv
   }
   // The full-channel kernel takes a window of at most one tile per key stream (128 keys);
   // a wider window goes to the split-channel kernel, whose streams take any mix of tiles
-  const bool full_channel = p.n_tiles - p.main_tiles <= kStreams;
+  const bool full_channel = p.full_channel;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)p.grid), dim3(kAttnThreads), 0, st, a, a.q_seq, a.q_pos,
                        a.replay_start, a.swa_base);
