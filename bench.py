@@ -547,7 +547,7 @@ def run_prefill_chunk(args, torch, C):
         "scoring": dict(kernel="k_score_topk_grouped (csa2_index_topk_grouped: FP4 scores and Top-512 of 8 rows "
                                "per pass over the sequence's indexer K; no score array)",
                         **mfma_entry(score_flops(wl5), g5["index_topk_grouped"], MFMA_FP4_PEAK_TFLOPS)),
-        "attention": dict(kernel="k_attn_fc (csa2_sparse_attn, 512 entries + window per row)",
+        "attention": dict(kernel="k_attn_rows (csa2_sparse_attn, 512 entries + window per row, one workgroup per row)",
                           **mfma_entry(attn_flops(wl5), g5["attn"], MFMA_F16_PEAK_TFLOPS)),
         "isolated_launch_us": {k: round(v * 1000, 1) for k, v in r5["isolated"].items()}}}
 
