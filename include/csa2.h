@@ -134,7 +134,9 @@ uint32_t csa2_device_status(int clear);
 /* Testing aid for the status path: sets how many times the attention kernel polls its
  * partner's flag before giving up (default 2^22; a negative value restores it) and returns
  * the previous bound.  With 0 every exchange gives up at once: the kernel still completes,
- * its output is wrong, and the status word is set. */
+ * its output is wrong, and the status word is set.  Only the split-channel attention kernel,
+ * which csa2_sparse_attn* run for a window wider than 128 keys, has such an exchange; with a
+ * window of at most 128 keys no wave waits for another and the bound has no effect. */
 int csa2_debug_set_wait_limit(int polls);
 
 /* Static text for a status code; never NULL. */
