@@ -1880,18 +1880,22 @@ struct AttnPlan {
 };
 
 // One workgroup per CU (its eight waves, two per SIMD, and its 160 KB of LDS): split the
-// key list only when (query, head group) pairs alone cannot fill the 256 CUs, keeping at
-// least one tile per key stream in every split (8 streams in the full-channel kernel, 4 in
-// the split-channel one).  Fewer, fuller splits also mean fewer repeats of the per-workgroup
-// prologue (a selection in the Top-K modes) and fewer partials for the combine kernel.
+// key list only while the (query, head group) pairs are too few, keeping at least one tile
+// per key stream in every split (8 streams in the full-channel kernel, 4 in the
+// split-channel one).  The split-channel kernel splits up to 256 workgroups (every CU); the
+// full-channel kernel up to 128: its streams are independent, so a longer key slice costs
+// little, while each split repeats the prologue (a selection in the Top-K modes) and adds a
+// combine launch (at 32 queries x 64 heads one slice per pair beats two by ~2 us a call;
+// at 8 queries four or five slices beat one or two).
 static AttnPlan plan(int n_q, int n_heads, int k, int window) {
   AttnPlan p;
   p.head_groups = n_heads / kHG;
   p.main_tiles = (k + kT - 1) / kT;
   p.n_tiles = p.main_tiles + (window + kT - 1) / kT;
   const int64_t base = (int64_t)n_q * p.head_groups;
-  int want = (int)((256 + base - 1) / (base > 0 ? base : 1));
   p.full_channel = p.n_tiles - p.main_tiles <= kStreams;
+  const int fill = p.full_channel ? 128 : 256;
+  int want = (int)((fill + base - 1) / (base > 0 ? base : 1));
   const int streams = p.full_channel ? kStreams : kPairs;
   const int max_split = (p.n_tiles + streams - 1) / streams;
   want = want < 1 ? 1 : (want > max_split ? max_split : want);

@@ -518,9 +518,11 @@ size_t csa2_pool_workspace_bytes(int n_q, int64_t max_vis, int block, int max_bl
  * (E2M1 x E4M3, or E4M3) is exact in fp16.  Q enters as fp16 after a power-of-two scale per
  * (query, head) that brings the head's largest |q| into [2^14, 2^15): every bf16 value
  * within a factor 2^32 of that maximum is then exact, over the whole bf16 range, and the
- * logits take the scale back exactly.  Softmax in fp32; P rounded to fp16.  The kernel's
- * one wait (between the two waves that share a key stream) is bounded; if it gives up, the
- * call's out and lse are invalid and the next call returns CSA2_ERR_DEVICE.  Batches of at
+ * logits take the scale back exactly.  Softmax in fp32; P rounded to fp16.  With a window
+ * of at most 128 keys every wave runs its own key stream over all channels and no wave
+ * waits for another; with a wider window the two waves that share a key stream exchange
+ * partial logits through one bounded wait, and if it gives up, the call's out and lse are
+ * invalid and the next call returns CSA2_ERR_DEVICE.  Batches of at
  * least 1,024 rows with 64 heads, without new_win, run one workgroup per row over all of
  * its heads (each key dequantised once per row; same arithmetic, no wait, no workspace).
  * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED (out_dtype, new_win_dtype),

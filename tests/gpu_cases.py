@@ -134,6 +134,17 @@ def attn_close(out_gpu: np.ndarray, out_ref: np.ndarray, tol: float = 2e-3) -> f
     return float(err)
 
 
+def attn_close_bf16(out_bf16: np.ndarray, ref: np.ndarray, tol: float = 2e-3):
+    """The bf16 output bar: every element within the fp32 bar (tol x max|ref|) plus one bf16
+    ulp of the reference element."""
+    ref = np.asarray(ref, np.float64)
+    mag = np.abs(ref)
+    ulp = np.where(mag > 0, np.ldexp(1.0, np.floor(np.log2(np.where(mag > 0, mag, 1.0))).astype(np.int64) - 7), 0.0)
+    err = np.abs(out_bf16.astype(np.float64) - ref)
+    bound = tol * mag.max() + ulp
+    assert np.all(err <= bound), f"bf16 output: {(err > bound).sum()} elements beyond fp32 bar + 1 ulp"
+
+
 def smoke_check() -> dict:
     """One Full-mode step of the tiny decode workload on cuda:0 against the oracle."""
     from fp4_kv_cache_layer_amd.layer import Csa2Step

@@ -973,9 +973,9 @@ def test_sparse_attn_window_sizes(C, window, n_q, heads):
         assert np.abs(gl[qi] - ref_lse).max() <= 1e-3
 
 
-@pytest.mark.parametrize("n_q", [6, 32])
+@pytest.mark.parametrize("n_q", [6, 24])
 def test_sparse_attn_split_workspace_reuse(C, n_q):
-    """Split key lists (10 splits at 6 queries, 2 at 32): consecutive calls on one
+    """Split key lists (5 splits at 6 queries, 2 at 24): consecutive calls on one
     workspace give bit-identical outputs and match the oracle."""
     _say("sparse_attn split reuse", n_q)
     heads = 64
@@ -1098,15 +1098,7 @@ def _attn_ref(case, qi, q_np, sel, t, s, window, sm_scale):
                               oc.swa_rows(0, O.swa_positions(t, s, window)), sm_scale)
 
 
-def attn_close_bf16(out_bf16: np.ndarray, ref: np.ndarray, tol: float = 2e-3):
-    """The bf16 output bar: every element within the fp32 bar (tol x max|ref|) plus one bf16
-    ulp of the reference element."""
-    ref = np.asarray(ref, np.float64)
-    mag = np.abs(ref)
-    ulp = np.where(mag > 0, np.ldexp(1.0, np.floor(np.log2(np.where(mag > 0, mag, 1.0))).astype(np.int64) - 7), 0.0)
-    err = np.abs(out_bf16.astype(np.float64) - ref)
-    bound = tol * mag.max() + ulp
-    assert np.all(err <= bound), f"bf16 output: {(err > bound).sum()} elements beyond fp32 bar + 1 ulp"
+attn_close_bf16 = G.attn_close_bf16
 
 
 @pytest.mark.parametrize("n_q,heads,sm", [(64, 64, None), (6, 16, None), (64, 64, 0.5), (6, 16, 0.5)])

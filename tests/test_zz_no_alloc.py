@@ -39,7 +39,7 @@ def _case(n_q, heads, seed):
 def test_noalloc_matches_workspace_call(C):
     assert C.csa2_sparse_attn_noalloc_max_bytes() == 16 << 20
     results = []
-    for n_q, heads, out_dt in ((32, 64, torch.float32), (6, 16, torch.bfloat16)):
+    for n_q, heads, out_dt in ((24, 64, torch.float32), (6, 16, torch.bfloat16)):
         _say("noalloc", n_q, heads, out_dt)
         case, t = _case(n_q, heads, 40 + n_q)
         caches = case.gpu_caches()
@@ -72,8 +72,11 @@ def test_noalloc_matches_workspace_call(C):
             ref, ref_lse = G.O.sparse_attention(qa_np, oc.main_rows(idx[qi][idx[qi] >= 0]),
                                                 oc.swa_rows(0, G.O.swa_positions(t[qi], int(case.wl.replay_start[qi]),
                                                                                  128)), sm)
-            G.attn_close(out_b[qi].float().cpu().numpy(), ref, 2e-3 if out_dt == torch.float32 else 6e-3)
+            if out_dt == torch.float32:
+                G.attn_close(out_b[qi].cpu().numpy(), ref, 2e-3)
+            else:
+                G.attn_close_bf16(out_b[qi].float().cpu().numpy(), ref)
             assert np.abs(lse_b[qi].cpu().numpy() - ref_lse).max() <= 1e-3
         results.append(n_q)
         del caches
-    assert results == [32, 6]
+    assert results == [24, 6]
