@@ -935,6 +935,46 @@ def test_sparse_attn_parity(C, heads, out_dt):
         assert np.abs(gl[qi] - ref_lse).max() <= 1e-3
 
 
+@pytest.mark.parametrize("k,window,n_q,heads", [(2048, 128, 8, 64), (2048, 128, 64, 16), (1500, 40, 64, 64),
+                                                (777, 1, 3, 16), (2048, 256, 6, 16)])
+def test_sparse_attn_large_k(C, k, window, n_q, heads):
+    """Index lists longer than the decode's 512, up to the maximum k = 2048: long key streams
+    (up to 17 tiles per stream without a split), key lists split into slices of many tiles,
+    a k that is not a multiple of the 16-key tile, and the split-channel kernel (256-key
+    window) at the maximum k; every row against the oracle."""
+    _say("sparse_attn large k", k, window, n_q, heads)
+    rng = np.random.default_rng(k + window + n_q)
+    cap = 3001
+    t = [int(x) for x in rng.integers(k, cap, size=n_q)]
+    t[0] = cap - 1
+    s = [0 if i % 2 == 0 else max(0, ti - window // 3) for i, ti in enumerate(t)]
+    case = _attn_case(5 + k + n_q, n_q, cap, heads, t, s, swa_cap=256)   # one sequence per query
+    wl = case.wl
+    caches = case.gpu_caches()
+    _, _, qa = case.gpu_query_inputs(0)
+    q_seq, _, q_pos, rs = case.gpu_meta()
+    idx = np.full((n_q, k), -1, np.int32)
+    counts = [k if i % 3 == 0 else int(rng.integers(1, k + 1)) for i in range(n_q)]
+    for qi in range(n_q):
+        idx[qi, :counts[qi]] = np.sort(rng.choice(t[qi] + 1, size=counts[qi], replace=False))
+    need = C.csa2_attn_workspace_bytes(n_q, heads, 512, k, window)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty(n_q, heads, 512, dtype=torch.float32, device="cuda")
+    lse = torch.empty(n_q, heads, dtype=torch.float32, device="cuda")
+    C.csa2_sparse_attn(qa, caches.kv_codes, caches.kv_scales, q_seq, torch.from_numpy(idx).cuda(), caches.swa[0],
+                       caches.swa_base, q_pos, rs, window, 1.0 / math.sqrt(512), out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    assert C.csa2_device_status() == 0
+    go, gl = out.cpu().numpy(), lse.cpu().numpy()
+    for qi in range(n_q):
+        oc = case.oracle_caches(int(wl.q_seq[qi]))
+        _, _, _, qa_np = case.oracle_query(0, qi)
+        ref, ref_lse = O.sparse_attention(qa_np, oc.main_rows(idx[qi, :counts[qi]]),
+                                          oc.swa_rows(0, O.swa_positions(t[qi], s[qi], window)), 1 / math.sqrt(512))
+        G.attn_close(go[qi], ref, 2e-3)
+        assert np.abs(gl[qi] - ref_lse).max() <= 1e-3
+
+
 @pytest.mark.parametrize("window,n_q,heads", [(1, 64, 64), (40, 64, 64), (200, 64, 64), (40, 6, 16), (200, 6, 16)])
 def test_sparse_attn_window_sizes(C, window, n_q, heads):
     """Windows other than 128 keys: a single key, a ragged number of tiles too few for the
