@@ -204,6 +204,25 @@ def test_attention_validation(L):
     assert L.csa2_sparse_attn_noalloc_max_bytes() == 16 << 20
 
 
+def test_attention_split_plan(L):
+    """The key-list split behind csa2_attn_workspace_bytes: a window of at most 128 keys (the
+    full-channel kernel) splits only while fewer than 128 (query, 16-head group) workgroups
+    exist, into slices of at least 8 tiles of 16 keys; a wider window (the split-channel
+    kernel) while fewer than 256, into slices of at least 4 tiles.  The workspace holds each
+    split's fp32 output and (m, l) per (query, head), plus 256 bytes of alignment."""
+    def ws(n_q, heads, k, window, nsplit):
+        return nsplit * n_q * heads * (512 + 2) * 4 + 256
+    assert L.csa2_attn_workspace_bytes(64, 64, 512, 512, 128) == 0          # 256 workgroups
+    assert L.csa2_attn_workspace_bytes(32, 64, 512, 512, 128) == 0          # 128: no split
+    assert L.csa2_attn_workspace_bytes(24, 64, 512, 512, 128) == ws(24, 64, 512, 128, 2)
+    assert L.csa2_attn_workspace_bytes(8, 64, 512, 512, 128) == ws(8, 64, 512, 128, 4)    # 40 tiles, 10 per slice
+    assert L.csa2_attn_workspace_bytes(1, 16, 512, 512, 128) == ws(1, 16, 512, 128, 5)    # at most 40 / 8 slices
+    assert L.csa2_attn_workspace_bytes(32, 64, 512, 512, 256) == ws(32, 64, 512, 256, 2)  # split-channel: up to 256
+    assert L.csa2_attn_workspace_bytes(6, 16, 512, 2048, 256) == ws(6, 16, 2048, 256, 36)  # 144 tiles, 4 per slice
+    assert L.csa2_attn_workspace_bytes(64, 64, 512, 512, 256) == 0
+    assert L.csa2_attn_workspace_bytes(8, 40, 512, 512, 128) == 0            # heads not a multiple of 16
+
+
 def test_select_in_attention_validation(L):
     """csa2_sparse_attn_topk and csa2_sparse_attn_pool_topk reject bad calls on the host."""
     att = _attn(cand_keys=FAKE, cand_per_q=8192, k=512, idx_out=FAKE, count_out=FAKE, workspace=None,
