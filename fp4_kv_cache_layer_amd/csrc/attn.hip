@@ -1290,8 +1290,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fc(AttnArgs a, const i
       ss[6] = __builtin_shufflevector(b23, b23, 0, 0);
       ss[7] = __builtin_shufflevector(b23, b23, 1, 1);
     }
+    // Q of the next two QK steps is read one iteration ahead, so its LDS latency is not
+    // waited for just before the MFMA that takes it
+    v8h qa0 = *reinterpret_cast<const v8h*>(qrow);
+    v8h qa1 = *reinterpret_cast<const v8h*>(qrow + 16);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
+      const v8h qc0 = qa0, qc1 = qa1;
+      if (m < 7) {
+        qa0 = *reinterpret_cast<const v8h*>(qrow + 16 * (2 * m + 2));
+        qa1 = *reinterpret_cast<const v8h*>(qrow + 16 * (2 * m + 3));
+      }
       if (with_pv) {   // uniform: blocks m, m+8, m+16, m+24 of the previous tile
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
@@ -1321,9 +1330,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fc(AttnArgs a, const i
           k = fp4x8_to_f16(word(j), ss[j >> 1]);
         }
         *reinterpret_cast<v8h*>(vrow + 16 * j) = k;
-        const v8h qv = *reinterpret_cast<const v8h*>(qrow + 16 * j);
-        if (h == 0) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qv, sa, 0, 0, 0);
-        else sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qv, sb, 0, 0, 0);
+        if (h == 0) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qc0, sa, 0, 0, 0);
+        else sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(k, qc1, sb, 0, 0, 0);
       }
     }
     *valid = (uint32_t)__ballot(g.ok != 0) & 0xffffu;  // lanes 0..15 hold keys 0..15
