@@ -845,7 +845,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn(AttnArgs a, const int3
 // stream runs its own online softmax; Q is staged once per workgroup in LDS (scaled to fp16
 // by a power of two per head, as in k_attn) and each 32-channel MFMA step reads its slice.
 // Lane (key col, group grp) gathers channels 128*grp .. +127 of its key: 64 B of E2M1 codes
-// and 8 scale bytes, or 128 B of window E4M3.  V is single-buffered per wave: in step i the
+// and 8 scale bytes, or 128 B of window E4M3.  The host takes this kernel only for a window
+// of at most kStreams tiles, so only a stream's first tile can be a window tile: the
+// gathers of its later tiles use main-tile slots (18 registers instead of 36), which keeps
+// the kernel at two waves per SIMD without spills.  V is single-buffered per wave: in step i the
 // P.V of tile i reads channel blocks m, m+8, m+16, m+24 of the V tile just before the
 // dequantisation of tile i+1 overwrites exactly those blocks (LDS executes one wave's
 // accesses in order), interleaved over m = 0..7 with tile i+1's QK steps 2m, 2m+1.  O^T of
